@@ -1,0 +1,147 @@
+"""MI355X (gfx950) scaled-dot-product-attention backward.
+
+A thin ctypes binding of the C ABI declared in include/sdpa_bwd.h: argument marshalling only,
+every step of the backward runs in the HIP kernels of libsdpa_bwd.so.  PyTorch supplies device
+memory and streams.  The library is loaded on first use and the call fails loudly when it has not
+been built (``python -m attention_backward_sdpa_amd.build``).
+"""
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsdpa_bwd.so")
+
+OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, LAUNCH_FAILED = 0, 1, 2, 3, 4
+
+_lib = None
+
+
+class SdpaBwdError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m attention_backward_sdpa_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.sdpa_bwd_workspace_size.argtypes = [i] * 11
+    lib.sdpa_bwd_workspace_size.restype = sz
+    lib.sdpa_bwd.argtypes = [vp] * 9 + [i] * 7 + [f, i, i, i, vp, vp]
+    lib.sdpa_bwd.restype = i
+    ex = [vp] * 9 + [i] * 7 + [f, i, i, i, vp, vp, i, i, vp, sz, vp]
+    lib.sdpa_bwd_ex.argtypes = ex
+    lib.sdpa_bwd_ex.restype = i
+    lib.sdpa_bwd_ex_events.argtypes = ex + [vp]
+    lib.sdpa_bwd_ex_events.restype = i
+    lib.sdpa_bwd_preprocess.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.sdpa_bwd_preprocess.restype = i
+    lib.sdpa_bwd_status_string.argtypes = [i]
+    lib.sdpa_bwd_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes library (raises when it has not been built)."""
+    return _load()
+
+
+def status_string(status: int) -> str:
+    return _load().sdpa_bwd_status_string(int(status)).decode()
+
+
+def _check(status):
+    if status != OK:
+        raise SdpaBwdError(status, f"sdpa_bwd failed: {status_string(status)} (status {status})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def workspace_size(B, Hq, Hkv, Sq, Skv, Dqk, Dv, causal=False, window_left=-1,
+                   deterministic=False, has_seqlens=False) -> int:
+    """sdpa_bwd_workspace_size(): bytes of workspace a call with these arguments needs."""
+    return int(_load().sdpa_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, Dqk, Dv, int(causal),
+                                               int(window_left), int(deterministic),
+                                               int(has_seqlens)))
+
+
+def _dims(q, k, v):
+    B, Hq, Sq, Dqk = q.shape
+    _, Hkv, Skv, _ = k.shape
+    Dv = v.shape[-1]
+    return B, Hq, Hkv, Sq, Skv, Dqk, Dv
+
+
+def sdpa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, window_left=-1,
+             deterministic=False, workspace=None, stream=None):
+    """sdpa_bwd(): the spec entry point on torch tensors (bf16 BHSD, lse fp32 (B,Hq,Sq)).
+
+    Outputs dq, dk, dv are written in place.  `workspace` is a uint8 device tensor of at least
+    workspace_size(...) bytes.  Raises SdpaBwdError on a non-zero status.
+    """
+    dims = _dims(q, k, v)
+    _check(_load().sdpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                            _ptr(dk), _ptr(dv), *dims, -1.0 if scale is None else float(scale),
+                            int(causal), int(window_left), int(deterministic), _ptr(workspace),
+                            _stream_handle(stream)))
+
+
+def sdpa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, window_left=-1,
+                deterministic=False, seq_q_lens=None, seq_kv_lens=None,
+                causal_bottom_right=False, window_right=0, workspace=None, stream=None,
+                events=None):
+    """sdpa_bwd_ex() (or sdpa_bwd_ex_events() when `events` lists five torch.cuda.Event)."""
+    dims = _dims(q, k, v)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+            *dims, -1.0 if scale is None else float(scale), int(causal), int(window_left),
+            int(deterministic), _ptr(seq_q_lens), _ptr(seq_kv_lens), int(causal_bottom_right),
+            int(window_right), _ptr(workspace), ws_bytes, _stream_handle(stream)]
+    lib = _load()
+    if events is None:
+        _check(lib.sdpa_bwd_ex(*args))
+    else:
+        handles = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        _check(lib.sdpa_bwd_ex_events(*args, handles))
+
+
+def sdpa_bwd_preprocess(o, do, delta, dq_accum=None, seq_q_lens=None, Dqk=0, stream=None):
+    """sdpa_bwd_preprocess(): delta = rowsum(O * dO) (and zero dq_accum when given)."""
+    B, Hq, Sq, Dv = o.shape
+    _check(_load().sdpa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(delta), _ptr(dq_accum),
+                                       _ptr(seq_q_lens), B, Hq, Sq, Dv, int(Dqk),
+                                       _stream_handle(stream)))
+
+
+def attention_backward(q, k, v, o, do, lse, scale=None, causal=False, window_left=-1,
+                       deterministic=False, seq_q_lens=None, seq_kv_lens=None,
+                       causal_bottom_right=False, window_right=0, stream=None):
+    """Allocate dq/dk/dv and the workspace with torch, then run sdpa_bwd_ex; returns (dq, dk, dv)."""
+    import torch
+    B, Hq, Hkv, Sq, Skv, Dqk, Dv = _dims(q, k, v)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    n = workspace_size(B, Hq, Hkv, Sq, Skv, Dqk, Dv, causal, window_left, deterministic,
+                       seq_q_lens is not None)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+    sdpa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale, causal, window_left, deterministic,
+                seq_q_lens, seq_kv_lens, causal_bottom_right, window_right, ws, stream)
+    return dq, dk, dv

@@ -1,0 +1,108 @@
+// Shared device helpers for the gfx950 (CDNA4) attention-backward kernels: bf16 storage,
+// MFMA fragment types and the lane layouts of the two bf16 matrix-core instructions used.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern in memory
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_float(bf16_t x) {
+  return __uint_as_float(((uint32_t)x) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 using the hardware convert (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16_t float_to_bf16(float x) {
+  __bf16 h = (__bf16)x;
+  return __builtin_bit_cast(bf16_t, h);
+}
+
+// ---------------------------------------------------------------------------------------------
+// MFMA tiles.  MT = 32 selects v_mfma_f32_32x32x16_bf16, MT = 16 selects v_mfma_f32_16x16x32_bf16.
+// Lane layouts (verified on the device):
+//   A operand (bf16x8): lane l holds row (l % MT), k slots (l / MT) * 8 + 0..7
+//   B operand (bf16x8): lane l holds col (l % MT), k slots (l / MT) * 8 + 0..7
+//   C/D (MT*MT/64 floats): lane l holds col (l % MT); register r holds
+//        row = (r / 4) * (4 * NG) + (l / MT) * 4 + (r % 4),   NG = 64 / MT
+// Only a consistent k numbering between A and B matters for the product, which is what lets an
+// accumulator tile be fed back as an operand whose contraction index is the accumulator's row.
+template <int MT>
+struct Mfma;
+
+template <>
+struct Mfma<32> {
+  static constexpr int NG = 2;           // lane groups
+  static constexpr int KT = 16;          // contraction length per instruction
+  static constexpr int NACC = 16;        // accumulator floats per lane
+  typedef floatx16 acc_t;
+  __device__ __forceinline__ static acc_t mma(bf16x8 a, bf16x8 b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mfma<16> {
+  static constexpr int NG = 4;
+  static constexpr int KT = 32;
+  static constexpr int NACC = 4;
+  typedef floatx4 acc_t;
+  __device__ __forceinline__ static acc_t mma(bf16x8 a, bf16x8 b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Row (within the tile) of accumulator register r for lane group g.
+template <int MT>
+__device__ __forceinline__ constexpr int acc_row(int r, int g) {
+  return (r / 4) * (4 * (64 / MT)) + g * 4 + (r % 4);
+}
+
+// ---------------------------------------------------------------------------------------------
+// LDS tiles are stored row-major with 16-byte chunks XOR-swizzled per row, so that both the
+// 16-byte row reads (8 consecutive rows, same chunk) and the transpose reads (4 consecutive rows,
+// two adjacent chunks) land on distinct banks.
+__device__ __forceinline__ int swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+
+// Byte offset of element (row, col) in a swizzled bf16 tile with ROWB bytes per row.  The XOR
+// touches only the low 3 bits of the chunk index, so it stays inside the row as long as the row
+// holds a whole number of 8-chunk (128-byte) groups.
+template <int ROWB>
+__device__ __forceinline__ int lds_off(int row, int col) {
+  static_assert(ROWB % 128 == 0, "swizzled rows must be multiples of 128 bytes");
+  int byte = col * 2;
+  return row * ROWB + (((byte >> 4) ^ swz(row)) << 4) + (byte & 15);
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const char* base, int off) {
+  return *reinterpret_cast<const bf16x8*>(base + off);
+}
+
+// ds_read_b64_tr_b16: within each block of 16 lanes, lane i returns column i of the 4 x 16 block
+// whose row (r / 4), columns 4*(r % 4) .. +3 are addressed by lane r of the block.
+__device__ __forceinline__ bf16x4 lds_read_tr(const char* base, int off) {
+  shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4*)(base + off));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 concat(bf16x4 a, bf16x4 b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+}  // namespace sdpa

@@ -1,0 +1,390 @@
+// Host side of the attention-backward library: argument validation, workspace carving, route
+// choice and kernel launches on the caller's stream.  Implements include/sdpa_bwd.h.
+//
+// Chain ("SDPA Backward (SM120)", section "The kernel chain"):
+//   preprocess -> main -> [GQA reduce] -> dQ convert        (fp32-atomic dQ route)
+//   preprocess -> main(dS out) -> [GQA reduce] -> dq2k      (deterministic two-kernel route)
+// The pages overlap consecutive launches with programmatic dependent launch; CDNA has no such
+// feature, so the launches are simply ordered on the stream.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/sdpa_bwd.h"
+#include "bwd_main.h"
+#include "dq2k.h"
+#include "small_kernels.h"
+
+using namespace sdpa;
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Tile geometry per supported (Dqk, Dv): the MFMA tile MT (32 -> 32x32x16, 16 -> 16x16x32), the
+// key tile BC = 4 * MT and the q tile BR.
+struct Geometry {
+  int mt, bc, br;
+};
+
+bool geometry_for(int Dqk, int Dv, Geometry* g) {
+  if (Dqk == 64 && Dv == 64) *g = {32, 128, 64};
+  else if (Dqk == 128 && Dv == 128) *g = {32, 128, 64};
+  else if (Dqk == 192 && Dv == 128) *g = {32, 128, 64};
+  else if (Dqk == 256 && Dv == 256) *g = {16, 64, 64};
+  else return false;
+  return true;
+}
+
+struct Carve {
+  int64_t delta = 0, dq_accum = -1, ds = -1, dk_ws = -1, dv_ws = -1, total = 0;
+  int64_t sq_pad = 0, skv_pad = 0;
+};
+
+Carve carve(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv, int det, const Geometry& g) {
+  Carve c;
+  int64_t off = 0;
+  const int64_t rows = (int64_t)B * Hq * Sq;
+  c.delta = off;
+  off = align_up(off + rows * 4, kAlign);
+  if (!det) {
+    c.dq_accum = off;
+    off = align_up(off + rows * Dqk * 4, kAlign);
+  } else {
+    c.sq_pad = align_up(Sq, g.br);
+    c.skv_pad = align_up(Skv, g.bc);
+    c.ds = off;
+    off = align_up(off + (int64_t)B * Hq * c.skv_pad * c.sq_pad * 2, kAlign);
+  }
+  if (Hq != Hkv) {
+    c.dk_ws = off;
+    off = align_up(off + (int64_t)B * Hq * Skv * Dqk * 2, kAlign);
+    c.dv_ws = off;
+    off = align_up(off + (int64_t)B * Hq * Skv * Dv * 2, kAlign);
+  }
+  c.total = off;
+  return c;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int validate(const void* q, const void* k, const void* v, const void* o, const void* dO,
+             const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
+             int Skv, int Dqk, int Dv, int window_left, int window_right, Geometry* geo) {
+  if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0) return SDPA_BWD_INVALID_ARG;
+  if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return SDPA_BWD_INVALID_ARG;
+  if (window_left < -1 || window_right < 0) return SDPA_BWD_INVALID_ARG;
+  if (!geometry_for(Dqk, Dv, geo)) return SDPA_BWD_UNSUPPORTED;
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return SDPA_BWD_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return SDPA_BWD_UNSUPPORTED;
+  return SDPA_BWD_OK;
+}
+
+template <class C>
+hipError_t launch_main(const MainParams& mp, int grid, hipStream_t s) {
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute((const void*)bwd_main_kernel<C>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL(bwd_main_kernel<C>, dim3(grid), dim3(C::NT), C::LDS_BYTES, s, mp);
+  return hipGetLastError();
+}
+
+template <class C>
+hipError_t launch_dq2k(const Dq2kParams& dp, int grid, hipStream_t s) {
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute((const void*)dq2k_kernel<C>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL(dq2k_kernel<C>, dim3(grid), dim3(C::NT), C::LDS_BYTES, s, dp);
+  return hipGetLastError();
+}
+
+template <int DQK, int DV, int MT, int BR>
+hipError_t dispatch_main(const MainParams& mp, int det, int grid, hipStream_t s) {
+  if (det) return launch_main<MainCfg<DQK, DV, MT, BR, true>>(mp, grid, s);
+  return launch_main<MainCfg<DQK, DV, MT, BR, false>>(mp, grid, s);
+}
+
+hipError_t run_main(int Dqk, int Dv, const MainParams& mp, int det, int grid, hipStream_t s) {
+  if (Dqk == 64) return dispatch_main<64, 64, 32, 64>(mp, det, grid, s);
+  if (Dqk == 128) return dispatch_main<128, 128, 32, 64>(mp, det, grid, s);
+  if (Dqk == 192) return dispatch_main<192, 128, 32, 64>(mp, det, grid, s);
+  return dispatch_main<256, 256, 16, 64>(mp, det, grid, s);
+}
+
+hipError_t run_dq2k(int Dqk, const Dq2kParams& dp, int grid, hipStream_t s) {
+  if (Dqk == 64) return launch_dq2k<Dq2kCfg<64, 64, 128>>(dp, grid, s);
+  if (Dqk == 128) return launch_dq2k<Dq2kCfg<128, 64, 128>>(dp, grid, s);
+  if (Dqk == 192) return launch_dq2k<Dq2kCfg<192, 64, 128>>(dp, grid, s);
+  return launch_dq2k<Dq2kCfg<256, 64, 64>>(dp, grid, s);
+}
+
+hipError_t launch_preprocess(const PreParams& pp, int Dv, hipStream_t s) {
+  const int rpb = 256 / (Dv / 8);
+  const int64_t blocks = (pp.rows + rpb - 1) / rpb;
+  if (blocks == 0) return hipSuccess;
+  if (Dv == 64) hipLaunchKernelGGL(preprocess_kernel<64>, dim3(blocks), dim3(256), 0, s, pp);
+  else if (Dv == 128) hipLaunchKernelGGL(preprocess_kernel<128>, dim3(blocks), dim3(256), 0, s, pp);
+  else hipLaunchKernelGGL(preprocess_kernel<256>, dim3(blocks), dim3(256), 0, s, pp);
+  return hipGetLastError();
+}
+
+__global__ void fill_zero_kernel(uint32_t* p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += stride) p[x] = 0;
+}
+
+hipError_t zero_buffer(void* p, int64_t bytes, hipStream_t s) {
+  const int64_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, s, (uint32_t*)p, n);
+  return hipGetLastError();
+}
+
+int grid_stride_blocks(int64_t n) {
+  int64_t b = (n + 255) / 256;
+  if (b > 16384) b = 16384;
+  return (int)(b < 1 ? 1 : b);
+}
+
+int run(const void* q, const void* k, const void* v, const void* o, const void* dO,
+        const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Skv,
+        int Dqk, int Dv, float scale, int causal, int window_left, int deterministic,
+        const int* seq_q_lens, const int* seq_kv_lens, int bottom_right, int window_right,
+        void* workspace, size_t workspace_bytes, bool check_ws, hipStream_t stream,
+        void* const* events) {
+  Geometry geo;
+  int st = validate(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, window_left,
+                    window_right, &geo);
+  if (st != SDPA_BWD_OK) return st;
+  const int det = deterministic ? 1 : 0;
+  const Carve c = carve(B, Hq, Hkv, Sq, Skv, Dqk, Dv, det, geo);
+  if (c.total > 0 && workspace == nullptr) return SDPA_BWD_INVALID_ARG;
+  if (check_ws && (uint64_t)c.total > (uint64_t)workspace_bytes) return SDPA_BWD_WORKSPACE_TOO_SMALL;
+  if (c.total > 0 && ((uintptr_t)workspace % kAlign) != 0) return SDPA_BWD_UNSUPPORTED;
+  if (!(scale > 0.f) || !isfinite(scale)) scale = 1.0f / sqrtf((float)Dqk);
+  auto rec = [&](int n) {
+    if (events) hipEventRecord((hipEvent_t)events[n], stream);
+  };
+
+  hipError_t e = hipSuccess;
+  rec(0);
+  if (B == 0 || Hq == 0) {
+    for (int n = 1; n < 5; ++n) rec(n);
+    return SDPA_BWD_OK;
+  }
+  if (Sq == 0 || Skv == 0) {
+    // nothing attends: every gradient that exists is zero
+    e = zero_buffer(dq, (int64_t)B * Hq * Sq * Dqk * 2, stream);
+    if (e == hipSuccess) e = zero_buffer(dk, (int64_t)B * Hkv * Skv * Dqk * 2, stream);
+    if (e == hipSuccess) e = zero_buffer(dv, (int64_t)B * Hkv * Skv * Dv * 2, stream);
+    for (int n = 1; n < 5; ++n) rec(n);
+    return e == hipSuccess ? SDPA_BWD_OK : SDPA_BWD_LAUNCH_FAILED;
+  }
+
+  char* ws = (char*)workspace;
+  float* delta = (float*)(ws + c.delta);
+  float* dq_accum = det ? nullptr : (float*)(ws + c.dq_accum);
+  const bool gqa = Hq != Hkv;
+
+  PreParams pp;
+  pp.o = (const bf16_t*)o;
+  pp.dO = (const bf16_t*)dO;
+  pp.delta = delta;
+  pp.dq_accum = dq_accum;
+  pp.seq_q_lens = seq_q_lens;
+  pp.rows = (int64_t)B * Hq * Sq;
+  pp.Hq = Hq;
+  pp.Sq = Sq;
+  pp.Dv = Dv;
+  pp.Dqk = Dqk;
+  pp.zero_rows = det ? 0 : 1;
+  e = launch_preprocess(pp, Dv, stream);
+  if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
+  rec(1);
+
+  MainParams mp;
+  mp.q = (const bf16_t*)q;
+  mp.k = (const bf16_t*)k;
+  mp.v = (const bf16_t*)v;
+  mp.dO = (const bf16_t*)dO;
+  mp.lse = lse;
+  mp.delta = delta;
+  mp.dq_accum = dq_accum;
+  mp.ds_ws = det ? (bf16_t*)(ws + c.ds) : nullptr;
+  mp.dk_out = gqa ? (bf16_t*)(ws + c.dk_ws) : (bf16_t*)dk;
+  mp.dv_out = gqa ? (bf16_t*)(ws + c.dv_ws) : (bf16_t*)dv;
+  mp.seq_q_lens = seq_q_lens;
+  mp.seq_kv_lens = seq_kv_lens;
+  mp.B = B;
+  mp.Hq = Hq;
+  mp.Hkv = Hkv;
+  mp.Sq = Sq;
+  mp.Skv = Skv;
+  mp.group = Hq / Hkv;
+  mp.out_heads = gqa ? Hq : Hkv;
+  mp.causal = causal ? 1 : 0;
+  mp.window_left = window_left;
+  mp.window_right = causal ? window_right : 0;
+  mp.bottom_right = bottom_right ? 1 : 0;
+  mp.n_kv_tiles = (Skv + geo.bc - 1) / geo.bc;
+  mp.sq_pad = (int)c.sq_pad;
+  mp.skv_pad = (int)c.skv_pad;
+  mp.scale = scale;
+  mp.scale_log2 = scale * kLog2e;
+  const int64_t main_grid = (int64_t)mp.n_kv_tiles * B * Hq;
+  if (main_grid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
+  e = run_main(Dqk, Dv, mp, det, (int)main_grid, stream);
+  if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
+  rec(2);
+
+  if (gqa) {
+    ReduceParams rp;
+    rp.dk_ws = mp.dk_out;
+    rp.dv_ws = mp.dv_out;
+    rp.dk = (bf16_t*)dk;
+    rp.dv = (bf16_t*)dv;
+    rp.head_k8 = (int64_t)Skv * Dqk / 8;
+    rp.head_v8 = (int64_t)Skv * Dv / 8;
+    rp.nk8 = (int64_t)B * Hkv * rp.head_k8;
+    rp.nv8 = (int64_t)B * Hkv * rp.head_v8;
+    rp.group = Hq / Hkv;
+    hipLaunchKernelGGL(gqa_reduce_kernel, dim3(grid_stride_blocks(rp.nk8 + rp.nv8)), dim3(256), 0,
+                       stream, rp);
+    if (hipGetLastError() != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
+  }
+  rec(3);
+
+  if (!det) {
+    const int64_t n8 = (int64_t)B * Hq * Sq * Dqk / 8;
+    hipLaunchKernelGGL(dq_convert_kernel, dim3(grid_stride_blocks(n8)), dim3(256), 0, stream,
+                       dq_accum, (bf16_t*)dq, n8, scale);
+    if (hipGetLastError() != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
+  } else {
+    Dq2kParams dp;
+    dp.ds_ws = mp.ds_ws;
+    dp.k = (const bf16_t*)k;
+    dp.dq = (bf16_t*)dq;
+    dp.seq_q_lens = seq_q_lens;
+    dp.seq_kv_lens = seq_kv_lens;
+    dp.B = B;
+    dp.Hq = Hq;
+    dp.Hkv = Hkv;
+    dp.Sq = Sq;
+    dp.Skv = Skv;
+    dp.group = Hq / Hkv;
+    dp.causal = mp.causal;
+    dp.window_left = window_left;
+    dp.window_right = mp.window_right;
+    dp.bottom_right = mp.bottom_right;
+    dp.n_kv_tiles = mp.n_kv_tiles;
+    dp.n_q_tiles = (Sq + geo.br - 1) / geo.br;
+    dp.sq_pad = (int)c.sq_pad;
+    dp.skv_pad = (int)c.skv_pad;
+    dp.scale = scale;
+    const int64_t grid = (int64_t)dp.n_q_tiles * B * Hq;
+    if (grid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
+    e = run_dq2k(Dqk, dp, (int)grid, stream);
+    if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
+  }
+  rec(4);
+  return SDPA_BWD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sdpa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv,
+                               int causal, int window_left, int deterministic, int has_seqlens) {
+  (void)causal;
+  (void)window_left;
+  (void)has_seqlens;
+  Geometry geo;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || Hq % Hkv != 0) return 0;
+  if (!geometry_for(Dqk, Dv, &geo)) return 0;
+  if (B == 0 || Sq == 0 || Skv == 0) return 0;
+  return (size_t)carve(B, Hq, Hkv, Sq, Skv, Dqk, Dv, deterministic ? 1 : 0, geo).total;
+}
+
+int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+             const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
+             int Skv, int Dqk, int Dv, float scale, int causal, int window_left,
+             int deterministic, void* workspace, void* stream) {
+  return run(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, scale, causal,
+             window_left, deterministic, nullptr, nullptr, 0, 0, workspace, 0, false,
+             (hipStream_t)stream, nullptr);
+}
+
+int sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
+                int Skv, int Dqk, int Dv, float scale, int causal, int window_left,
+                int deterministic, const int* seq_q_lens, const int* seq_kv_lens,
+                int causal_bottom_right, int window_right, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return run(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, scale, causal,
+             window_left, deterministic, seq_q_lens, seq_kv_lens, causal_bottom_right,
+             window_right, workspace, workspace_bytes, true, (hipStream_t)stream, nullptr);
+}
+
+int sdpa_bwd_ex_events(const void* q, const void* k, const void* v, const void* o,
+                       const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
+                       int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv, float scale, int causal,
+                       int window_left, int deterministic, const int* seq_q_lens,
+                       const int* seq_kv_lens, int causal_bottom_right, int window_right,
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       void* const* events) {
+  return run(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, scale, causal,
+             window_left, deterministic, seq_q_lens, seq_kv_lens, causal_bottom_right,
+             window_right, workspace, workspace_bytes, true, (hipStream_t)stream, events);
+}
+
+int sdpa_bwd_preprocess(const void* o, const void* dO, float* delta, float* dq_accum,
+                        const int* seq_q_lens, int B, int Hq, int Sq, int Dv, int Dqk,
+                        void* stream) {
+  if (B < 0 || Hq < 0 || Sq < 0) return SDPA_BWD_INVALID_ARG;
+  if (Dv != 64 && Dv != 128 && Dv != 256) return SDPA_BWD_UNSUPPORTED;
+  if (dq_accum && (Dqk <= 0 || Dqk % 4 != 0)) return SDPA_BWD_INVALID_ARG;
+  if (!o || !dO || !delta) return SDPA_BWD_INVALID_ARG;
+  if (!aligned16(o) || !aligned16(dO) || !aligned16(delta) || (dq_accum && !aligned16(dq_accum)))
+    return SDPA_BWD_UNSUPPORTED;
+  PreParams pp;
+  pp.o = (const bf16_t*)o;
+  pp.dO = (const bf16_t*)dO;
+  pp.delta = delta;
+  pp.dq_accum = dq_accum;
+  pp.seq_q_lens = seq_q_lens;
+  pp.rows = (int64_t)B * Hq * Sq;
+  pp.Hq = Hq;
+  pp.Sq = Sq;
+  pp.Dv = Dv;
+  pp.Dqk = Dqk;
+  pp.zero_rows = dq_accum ? 1 : 0;
+  return launch_preprocess(pp, Dv, (hipStream_t)stream) == hipSuccess ? SDPA_BWD_OK
+                                                                      : SDPA_BWD_LAUNCH_FAILED;
+}
+
+const char* sdpa_bwd_status_string(int status) {
+  switch (status) {
+    case SDPA_BWD_OK: return "ok";
+    case SDPA_BWD_INVALID_ARG: return "invalid argument";
+    case SDPA_BWD_UNSUPPORTED: return "unsupported configuration";
+    case SDPA_BWD_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case SDPA_BWD_LAUNCH_FAILED: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Bandwidth-bound kernels of the attention-backward chain ("SDPA Backward (SM120)", section
+// "The kernel chain"): the row-dot preprocess (delta = rowsum(O * dO), fused with zeroing the fp32
+// dQ accumulator), the dQ convert (fp32 accumulator -> bf16, times the softmax scale) and the
+// fixed-order GQA dK/dV group reduction ("GQA/MQA group reduction").
+#pragma once
+#include "common.h"
+
+namespace sdpa {
+
+// ---- preprocess ---------------------------------------------------------------------------------
+// One row of Dv bf16 per (Dv / 8) lanes; each lane loads 16 bytes of O and dO, multiplies in fp32
+// and the row's lanes reduce with butterfly shuffles in a fixed order (deterministic).  Rows at or
+// past the batch entry's query length get delta = 0.  When zero_rows is set, the same rows of the
+// fp32 dQ accumulator (Dqk floats each) are cleared.
+struct PreParams {
+  const bf16_t* o;
+  const bf16_t* dO;
+  float* delta;
+  float* dq_accum;
+  const int* seq_q_lens;
+  int64_t rows;   // B * Hq * Sq
+  int Hq, Sq, Dv, Dqk;
+  int zero_rows;
+};
+
+template <int DV>
+__global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
+  constexpr int LPR = DV / 8;              // lanes per row
+  constexpr int RPB = 256 / LPR;           // rows per block
+  const int tid = threadIdx.x;
+  const int sub = tid % LPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;
+  float acc = 0.f;
+  if (row < p.rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p.o + row * DV + sub * 8);
+    const u32x4 c = *reinterpret_cast<const u32x4*>(p.dO + row * DV + sub * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc += __uint_as_float(a[e] << 16) * __uint_as_float(c[e] << 16);
+      acc += __uint_as_float(a[e] & 0xffff0000u) * __uint_as_float(c[e] & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+  if (row < p.rows && sub == 0) {
+    const int s = (int)(row % p.Sq);
+    const int b = (int)(row / ((int64_t)p.Sq * p.Hq));
+    const int Lq = p.seq_q_lens ? p.seq_q_lens[b] : p.Sq;
+    p.delta[row] = (s < Lq) ? acc : 0.f;
+  }
+  if (p.zero_rows) {
+    // RPB rows of Dqk floats = RPB * Dqk / 4 float4 stores spread over the block
+    const int64_t row0 = (int64_t)blockIdx.x * RPB;
+    const int64_t nrows = (p.rows - row0) < RPB ? (p.rows - row0) : RPB;
+    const int64_t n4 = nrows * p.Dqk / 4;
+    float4* dst = reinterpret_cast<float4*>(p.dq_accum + row0 * p.Dqk);
+    for (int64_t x = tid; x < n4; x += 256) dst[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// ---- dQ convert ---------------------------------------------------------------------------------
+// dQ = bf16(scale * dq_accum); 8 elements per thread (two 16-byte loads, one 16-byte store).
+__global__ void __launch_bounds__(256) dq_convert_kernel(const float* __restrict__ acc,
+                                                         bf16_t* __restrict__ dq, int64_t n8,
+                                                         float scale) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n8; x += stride) {
+    const floatx4 a = reinterpret_cast<const floatx4*>(acc)[2 * x];
+    const floatx4 c = reinterpret_cast<const floatx4*>(acc)[2 * x + 1];
+    reinterpret_cast<u32x4*>(dq)[x] =
+        u32x4{pack_bf16x2(a[0] * scale, a[1] * scale), pack_bf16x2(a[2] * scale, a[3] * scale),
+              pack_bf16x2(c[0] * scale, c[1] * scale), pack_bf16x2(c[2] * scale, c[3] * scale)};
+  }
+}
+
+// ---- GQA reduce ---------------------------------------------------------------------------------
+// out[b, kvh, s, :] = bf16( sum_{g = 0 .. group-1} ws[b, kvh*group + g, s, :] ), summed in fp32
+// in ascending g.  One thread per 16-byte output vector; dK and dV handled by one launch
+// (vectors [0, nk8) are dK, [nk8, nk8 + nv8) are dV).
+struct ReduceParams {
+  const bf16_t* dk_ws;
+  const bf16_t* dv_ws;
+  bf16_t* dk;
+  bf16_t* dv;
+  int64_t nk8, nv8;          // output 8-element vectors of dK and dV
+  int64_t head_k8, head_v8;  // 8-element vectors per head (Skv * D / 8)
+  int group;
+};
+
+__global__ void __launch_bounds__(256) gqa_reduce_kernel(ReduceParams p) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < p.nk8 + p.nv8; x += stride) {
+    const bool isk = x < p.nk8;
+    const int64_t y = isk ? x : x - p.nk8;
+    const int64_t per = isk ? p.head_k8 : p.head_v8;
+    const int64_t kvhead = y / per, within = y % per;  // kvhead = b * Hkv + kvh
+    const u32x4* src = reinterpret_cast<const u32x4*>(isk ? p.dk_ws : p.dv_ws) +
+                       (kvhead * p.group) * per + within;
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int gi = 0; gi < p.group; ++gi) {
+      const u32x4 v = src[(int64_t)gi * per];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[2 * e] += __uint_as_float(v[e] << 16);
+        s[2 * e + 1] += __uint_as_float(v[e] & 0xffff0000u);
+      }
+    }
+    reinterpret_cast<u32x4*>(isk ? p.dk : p.dv)[y] =
+        u32x4{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]), pack_bf16x2(s[4], s[5]),
+              pack_bf16x2(s[6], s[7])};
+  }
+}
+
+}  // namespace sdpa

@@ -1,0 +1,110 @@
+/*
+ * sdpa_bwd.h -- C ABI of the MI355X (gfx950) scaled-dot-product-attention backward library.
+ *
+ * The operation ("SDPA Backward (SM120)", sections "Overview" and "API Usage"): given the forward
+ * activations Q, K, V, O, the loss gradient dO and the forward's natural-log log-sum-exp LSE,
+ * produce dQ, dK, dV of softmax(scale * Q K^T + mask) V, with
+ *     P     = exp(scale * Q K^T - LSE)                (replayed from LSE; masked pairs give 0)
+ *     delta = rowsum(O * dO)                           ("The kernel chain")
+ *     dS    = P * (dO V^T - delta)                     (unscaled softmax VJP)
+ *     dV    = P^T dO,  dK = scale * dS^T Q,  dQ = scale * dS K
+ * (scale placement as printed in "NVFP4 Attention QAT Backward", section "Overview").
+ * GQA/MQA: H_kv divides H_q, query head h uses KV head h / (H_q / H_kv), and dK/dV of a KV head
+ * sum over its query-head group in a fixed order ("GQA/MQA group reduction").
+ *
+ * Layout and types.  Every tensor is contiguous (B, H, S, D) with the head dim innermost:
+ *   q, dq : (B, Hq,  Sq,  Dqk) bf16       k, dk : (B, Hkv, Skv, Dqk) bf16
+ *   v, dv : (B, Hkv, Skv, Dv)  bf16       o, dO : (B, Hq,  Sq,  Dv)  bf16
+ *   lse   : (B, Hq,  Sq)       fp32, natural log; -inf marks a row that saw no key
+ * bf16 values are passed as their 16-bit patterns.  All pointers are device pointers and must be
+ * 16-byte aligned.  Supported head dims (Dqk, Dv): (64,64), (128,128), (192,128), (256,256).
+ *
+ * Masks ("API Usage" and "Causal, sliding-window, and padding masks"): query q and key k are
+ * visible together when q < seq_q, k < seq_kv, causal => k <= q + diag + window_right, and
+ * window_left >= 0 => k >= q + diag - window_left; diag = 0 (top-left) or seq_kv - seq_q
+ * (bottom-right).  dq rows at or past seq_q and dk/dv rows at or past seq_kv are written as 0;
+ * every element of dq, dk and dv is overwritten.
+ *
+ * Ownership and streams.  The caller owns every buffer, including one workspace of at least
+ * sdpa_bwd_workspace_size() bytes; the library allocates nothing and keeps no state between calls.
+ * All work is enqueued on `stream` (a hipStream_t; 0 = the null stream) and the call returns
+ * without synchronising.  Calls that share a workspace must be ordered on one stream.
+ *
+ * Errors.  Functions return SDPA_BWD_OK (0) or a status code; validation happens before the first
+ * launch, so a rejected call leaves every output untouched.  Nothing aborts or throws.
+ *
+ * Determinism ("Determinism"): deterministic != 0 selects the two-kernel route (dS streamed to the
+ * workspace, dQ reduced by a separate kernel in ascending KV order) and makes dq, dk, dv bitwise
+ * reproducible; otherwise dQ is accumulated with fp32 atomics and its low bits may vary between
+ * runs.  dK and dV are reproducible in both modes.
+ */
+#ifndef SDPA_BWD_H
+#define SDPA_BWD_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SDPA_BWD_OK = 0,
+  SDPA_BWD_INVALID_ARG = 1,          /* null pointer, negative size, H_kv not dividing H_q, ... */
+  SDPA_BWD_UNSUPPORTED = 2,          /* head dims outside the supported set, misaligned pointer */
+  SDPA_BWD_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below sdpa_bwd_workspace_size()        */
+  SDPA_BWD_LAUNCH_FAILED = 4         /* the HIP runtime reported an error at launch             */
+};
+
+/* Bytes of workspace needed by a call with these arguments (0 when none is needed beyond the
+ * outputs; a 256-byte-aligned carve of delta, the fp32 dQ accumulator or the bf16 dS buffer, and
+ * the per-query-head dK/dV partials under GQA).  Returns 0 for arguments sdpa_bwd would reject. */
+size_t sdpa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv,
+                               int causal, int window_left, int deterministic, int has_seqlens);
+
+/* The backward pass with top-left causal masking, no padding and no right band.
+ * scale <= 0 selects 1/sqrt(Dqk) ("API Usage": None -> 1/sqrt(D)).  window_left = -1 disables the
+ * left window.  `workspace` must hold sdpa_bwd_workspace_size(...) bytes (not checked here; use
+ * sdpa_bwd_ex to have it checked).  `stream` is a hipStream_t. */
+int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+             const float* lse, void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv,
+             float scale, int causal, int window_left, int deterministic,
+             void* workspace, void* stream);
+
+/* Superset of sdpa_bwd: per-batch padding lengths seq_q_lens / seq_kv_lens (device int32 (B,)
+ * arrays or NULL = full length; values are clamped to [0, S]), bottom-right causal alignment,
+ * a right band window_right >= 0 widening the causal diagonal, and a checked workspace size. */
+int sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                const float* lse, void* dq, void* dk, void* dv,
+                int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv,
+                float scale, int causal, int window_left, int deterministic,
+                const int* seq_q_lens, const int* seq_kv_lens, int causal_bottom_right,
+                int window_right, void* workspace, size_t workspace_bytes, void* stream);
+
+/* sdpa_bwd_ex that also records five HIP events (hipEvent_t, created by the caller) on `stream`:
+ * before the preprocess, after the preprocess, after the main kernel, after the GQA reduce (same
+ * point as the previous one when there is none) and after the dQ convert / dq2k kernel.  For
+ * measuring each kernel's share of the chain; the arithmetic is identical to sdpa_bwd_ex. */
+int sdpa_bwd_ex_events(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                       const float* lse, void* dq, void* dk, void* dv,
+                       int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv,
+                       float scale, int causal, int window_left, int deterministic,
+                       const int* seq_q_lens, const int* seq_kv_lens, int causal_bottom_right,
+                       int window_right, void* workspace, size_t workspace_bytes, void* stream,
+                       void* const* events);
+
+/* Step 1 of the chain alone ("The kernel chain", dot): delta[r] = sum_d O[r,d] * dO[r,d] in fp32
+ * for the B*Hq*Sq rows of O/dO (rows at or past seq_q_lens[b] get 0), and, when dq_accum is not
+ * NULL, zero the B*Hq*Sq*Dqk floats of dq_accum.  Dv in {64, 128, 256}. */
+int sdpa_bwd_preprocess(const void* o, const void* dO, float* delta, float* dq_accum,
+                        const int* seq_q_lens, int B, int Hq, int Sq, int Dv, int Dqk,
+                        void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* sdpa_bwd_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_BWD_H */

@@ -1,0 +1,104 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports every function
+declared in include/sdpa_bwd.h, the workspace size follows its carve rules, and every rejected call
+returns its status before touching the GPU (validation precedes any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_backward_sdpa_amd as lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdpa_bwd.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdpa_bwd\w*)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def so():
+    if not os.path.exists(lib.LIB_PATH):
+        pytest.fail("libsdpa_bwd.so is not built: run __graft_entry__.build()")
+    return lib.library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("sdpa_bwd", "sdpa_bwd_ex", "sdpa_bwd_workspace_size", "sdpa_bwd_status_string",
+              "sdpa_bwd_ex_events", "sdpa_bwd_preprocess"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(so):
+    for name in _declared_functions():
+        assert hasattr(so, name), f"libsdpa_bwd.so does not export {name}"
+
+
+def test_status_strings(so):
+    assert lib.status_string(0) == "ok"
+    for s in range(1, 5):
+        assert lib.status_string(s) != "ok"
+    assert lib.status_string(99) == "unknown status"
+
+
+def _ws(**kw):
+    base = dict(B=1, Hq=4, Hkv=4, Sq=256, Skv=256, Dqk=128, Dv=128, causal=False,
+                window_left=-1, deterministic=False, has_seqlens=False)
+    base.update(kw)
+    return lib.workspace_size(**base)
+
+
+def _al(n):
+    return (n + 255) // 256 * 256
+
+
+def test_workspace_size_rules(so):
+    # non-deterministic MHA: delta + fp32 dQ accumulator
+    assert _ws() == _al(4 * 256 * 4) + _al(4 * 256 * 128 * 4)
+    # GQA adds per-query-head bf16 dK/dV partials
+    assert _ws(Hkv=1) == _ws() + 2 * _al(4 * 256 * 128 * 2)
+    # deterministic: delta + bf16 dS (S_kv padded to the key tile, S_q to the q tile), no fp32 dQ
+    assert _ws(deterministic=True, Sq=200, Skv=200) == _al(4 * 200 * 4) + _al(4 * 256 * 256 * 2)
+    # monotone in the sequence length
+    sizes = [_ws(Sq=s, Skv=s) for s in (64, 128, 300, 1000)]
+    assert sizes == sorted(sizes)
+    # rejected shapes need nothing
+    assert _ws(Hkv=3) == 0
+    assert _ws(Dqk=96, Dv=96) == 0
+    assert _ws(Sq=0) == 0
+
+
+def _call(so, **kw):
+    a = dict(B=1, Hq=4, Hkv=4, Sq=64, Skv=64, Dqk=128, Dv=128, scale=0.0, causal=0, wl=-1, det=0,
+             lens_q=None, lens_kv=None, br=0, wr=0, ws=None, ws_bytes=0)
+    a.update(kw)
+    p = ctypes.c_void_p(4096)  # aligned, never dereferenced: validation fails before any launch
+    ptrs = [kw.get(n, p) for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv")]
+    return so.sdpa_bwd_ex(*ptrs, a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Skv"], a["Dqk"], a["Dv"],
+                          a["scale"], a["causal"], a["wl"], a["det"], a["lens_q"], a["lens_kv"],
+                          a["br"], a["wr"], a["ws"], a["ws_bytes"], None)
+
+
+def test_rejections_before_launch(so):
+    assert _call(so, Hkv=3) == lib.INVALID_ARG                    # H_kv does not divide H_q
+    assert _call(so, Hq=-1) == lib.INVALID_ARG
+    assert _call(so, wl=-2) == lib.INVALID_ARG                    # window_left < -1
+    assert _call(so, wr=-1) == lib.INVALID_ARG
+    assert _call(so, Dqk=96, Dv=96) == lib.UNSUPPORTED            # head dims outside the set
+    assert _call(so, Dqk=128, Dv=192) == lib.UNSUPPORTED          # D_v > D_qk
+    assert _call(so, q=ctypes.c_void_p(4098)) == lib.UNSUPPORTED  # misaligned pointer
+    assert _call(so, dk=None) == lib.INVALID_ARG                  # null output
+    assert _call(so, ws=None, ws_bytes=0) == lib.INVALID_ARG      # workspace needed but absent
+    need = _ws(Sq=64, Skv=64)
+    assert _call(so, ws=ctypes.c_void_p(1 << 20), ws_bytes=need - 1) == lib.WORKSPACE_TOO_SMALL
+    assert _call(so, ws=ctypes.c_void_p((1 << 20) + 16), ws_bytes=need) == lib.UNSUPPORTED
+
+
+def test_preprocess_rejections(so):
+    p = ctypes.c_void_p(4096)
+    assert so.sdpa_bwd_preprocess(p, p, p, None, None, 1, 1, 8, 96, 0, None) == lib.UNSUPPORTED
+    assert so.sdpa_bwd_preprocess(None, p, p, None, None, 1, 1, 8, 128, 0, None) == lib.INVALID_ARG
