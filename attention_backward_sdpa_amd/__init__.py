@@ -41,7 +41,7 @@ def _load():
     lib.sdpa_bwd_ex.restype = i
     lib.sdpa_bwd_ex_events.argtypes = ex + [vp]
     lib.sdpa_bwd_ex_events.restype = i
-    lib.sdpa_bwd_preprocess.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.sdpa_bwd_preprocess.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.sdpa_bwd_preprocess.restype = i
     lib.sdpa_bwd_status_string.argtypes = [i]
     lib.sdpa_bwd_status_string.restype = ctypes.c_char_p
@@ -122,10 +122,10 @@ def sdpa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, windo
         _check(lib.sdpa_bwd_ex_events(*args, handles))
 
 
-def sdpa_bwd_preprocess(o, do, delta, dq_accum=None, seq_q_lens=None, Dqk=0, stream=None):
-    """sdpa_bwd_preprocess(): delta = rowsum(O * dO) (and zero dq_accum when given)."""
+def sdpa_bwd_preprocess(o, do, lse, stats, dq_accum=None, seq_q_lens=None, Dqk=0, stream=None):
+    """sdpa_bwd_preprocess(): stats rows [LSE * log2 e, rowsum(O * dO)] (and zero dq_accum)."""
     B, Hq, Sq, Dv = o.shape
-    _check(_load().sdpa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(delta), _ptr(dq_accum),
+    _check(_load().sdpa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(lse), _ptr(stats), _ptr(dq_accum),
                                        _ptr(seq_q_lens), B, Hq, Sq, Dv, int(Dqk),
                                        _stream_handle(stream)))
 

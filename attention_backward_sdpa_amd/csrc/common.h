@@ -74,20 +74,20 @@ __device__ __forceinline__ constexpr int acc_row(int r, int g) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// LDS tiles are stored row-major with 16-byte chunks XOR-swizzled per row, so that both the
-// 16-byte row reads (8 consecutive rows, same chunk) and the transpose reads (4 consecutive rows,
-// two adjacent chunks) land on distinct banks.
-__device__ __forceinline__ int swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
-
-// Byte offset of element (row, col) in a swizzled bf16 tile with ROWB bytes per row.  The XOR
-// touches only the low 3 bits of the chunk index, so it stays inside the row as long as the row
-// holds a whole number of 8-chunk (128-byte) groups.
+// LDS tiles are stored row-major with every row padded by 32 bytes and bit 0 of the 16-byte chunk
+// index flipped on rows whose bit 2 is set.  With 128-byte bank windows this keeps both access
+// patterns conflict-free: 16-byte row reads of 8 consecutive rows at one column land on 8
+// distinct 16-byte slots, and the transpose reads (4 consecutive rows x 32 bytes) on 4 distinct
+// 32-byte slots.  The chunk flip only touches bit 0, which every loop index leaves alone, so the
+// address of any operand is a per-lane base plus a compile-time constant.
 template <int ROWB>
-__device__ __forceinline__ int lds_off(int row, int col) {
-  static_assert(ROWB % 128 == 0, "swizzled rows must be multiples of 128 bytes");
-  int byte = col * 2;
-  return row * ROWB + (((byte >> 4) ^ swz(row)) << 4) + (byte & 15);
-}
+struct PadTile {
+  static constexpr int STRIDE = ROWB + 32;
+  __device__ __forceinline__ static constexpr int off(int row, int col) {
+    return row * STRIDE + ((((col >> 3) ^ ((row >> 2) & 1))) << 4) + (col & 7) * 2;
+  }
+  static constexpr int bytes(int rows) { return rows * STRIDE; }
+};
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const char* base, int off) {
   return *reinterpret_cast<const bf16x8*>(base + off);

@@ -1,20 +1,21 @@
 // Deterministic dQ kernel of the two-kernel route ("SDPA Backward (SM120)", sections
 // "Determinism" and "Deterministic vs. non-deterministic dQ"): dQ = scale * dS K, one workgroup per
-// q tile of one query head, accumulating in registers over an ascending walk of exactly the KV
-// tiles the main kernel stored for that q tile, then a single bf16 store.  No atomics, fixed
-// order, so the result is bitwise reproducible.
+// 32-row q tile of one query head, accumulating in registers over an ascending walk of exactly the
+// KV tiles the main kernel stored for that q tile, then a single bf16 store.  No atomics and a
+// fixed order, so the result is bitwise reproducible.
 //
-// The workspace holds each stored (q tile, KV tile) block as dS^T (keys x q, q contiguous), the
-// layout the main kernel produces it in; both tiles are staged row-major in LDS and read as MFMA
-// operands with the transpose instruction.
+// The workspace holds each stored (KV tile, q tile) block in the main kernel's register order
+// (see bwd_main.h); any 64 consecutive keys of a block are one contiguous 4 KiB piece.  Chunks of
+// 64 keys of dS and of K (gathered as the main kernel's K fragments) are copied straight into LDS
+// (global_load_lds, double-buffered) and read as MFMA operands with the transpose instruction.
+// Waves split the head dim in 32-column tiles.
 #pragma once
-#include "common.h"
-#include "masks.h"
+#include "bwd_main.h"
 
 namespace sdpa {
 
 struct Dq2kParams {
-  const bf16_t* ds_ws;        // (B, Hq, skv_pad, sq_pad)
+  const bf16_t* ds_ws;        // (B*Hq, n_kv_tiles, n_q_tiles) blocks of BC x 32 bf16
   const bf16_t* k;            // (B, Hkv, Skv, Dqk)
   bf16_t* dq;                 // (B, Hq, Sq, Dqk)
   const int* seq_q_lens;
@@ -22,47 +23,33 @@ struct Dq2kParams {
   int B, Hq, Hkv, Sq, Skv, group;
   int causal, window_left, window_right, bottom_right;
   int n_kv_tiles, n_q_tiles;
-  int sq_pad, skv_pad;
   float scale;
 };
 
-template <int DQK_, int BR_, int BC_>
+template <int DQK_, int BC_>
 struct Dq2kCfg {
-  static constexpr int DQK = DQK_, BR = BR_, BC = BC_;
-  static constexpr int NW = 4, NT = 256;
-  static constexpr int DW = DQK / NW;                 // d columns per wave
-  static constexpr int MT = (DW % 32 == 0) ? 32 : 16;
-  using M = Mfma<MT>;
-  static constexpr int KT = M::KT, NACC = M::NACC;
-  static constexpr int N_RT = BR / MT, N_DT = DW / MT, N_K = BC / KT;
-  static constexpr int STROWB = BR * 2, KROWB = DQK * 2;
-  static constexpr int OFF_ST = 0, OFF_K = BC * STROWB;
-  static constexpr int LDS_BYTES = OFF_K + BC * KROWB;
-  static constexpr int SCH = BC * BR / 8 / NT, KCH = BC * DQK / 8 / NT;
-  static_assert(SCH * NT * 8 == BC * BR && KCH * NT * 8 == BC * DQK, "tile/thread mismatch");
-  static_assert(DW % MT == 0 && BR % MT == 0 && BC % KT == 0, "tile shapes");
+  static constexpr int DQK = DQK_, BC = BC_;
+  static constexpr int BR = 32, NW = 4, NT = 256, KC = 64;   // KC: keys per LDS chunk
+  static constexpr int N_DT = DQK / 32;                      // 32-column d tiles
+  static constexpr int PER_W = (N_DT + NW - 1) / NW;         // d tiles per wave (at most)
+  static constexpr int ST_BYTES = KC * BR * 2;               // 4 KiB of dS
+  static constexpr int K_BYTES = KC * DQK * 2;               // K fragments of 64 keys
+  static constexpr int BUF_BYTES = ST_BYTES + K_BYTES;
+  static constexpr int LDS_BYTES = 2 * BUF_BYTES;
+  static_assert(BC % KC == 0, "whole chunks per KV tile");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int MT, int ROWB>
-__device__ __forceinline__ bf16x8 tr_operand2(const char* base, int n_base, int k0a, int k0b,
-                                              int lane) {
-  const int i = lane & 15;
-  const int col = n_base + ((lane % MT) & ~15) + 4 * (i & 3);
-  return concat(lds_read_tr(base, lds_off<ROWB>(k0a + (i >> 2), col)),
-                lds_read_tr(base, lds_off<ROWB>(k0b + (i >> 2), col)));
-}
-
 template <class C>
 __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
-  using M = typename C::M;
-  using acc_t = typename M::acc_t;
-  constexpr int MT = C::MT, BR = C::BR, BC = C::BC, DQK = C::DQK, NT = C::NT, KT = C::KT;
+  using M = Mfma<32>;
+  using acc_t = M::acc_t;
+  constexpr int BR = C::BR, BC = C::BC, DQK = C::DQK, KC = C::KC;
+  constexpr int CPT = BC / KC;  // chunks per KV tile
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* sST = smem + C::OFF_ST;
-  char* sK = smem + C::OFF_K;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = lane / MT, lc = lane % MT;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, lc = lane & 31;
 
   const int nbh = p.B * p.Hq;
   const int bh = blockIdx.x % nbh;
@@ -90,75 +77,70 @@ __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
       j_last = j;
     }
   }
+  // chunks in ascending key order; chunks that start past the keys hold only zeros and are skipped
+  const int c_first = j_first * CPT;
+  int c_end = (j_last + 1) * CPT;
+  const int c_keys = (p.Skv + KC - 1) / KC;
+  c_end = c_end < c_keys ? c_end : c_keys;
 
-  const bf16_t* wsb = p.ds_ws + (int64_t)(b * p.Hq + h) * p.skv_pad * p.sq_pad + q0;
+  const bf16_t* wsh = p.ds_ws + (int64_t)bh * p.n_kv_tiles * p.n_q_tiles * (BC * BR);
   const bf16_t* Kb = p.k + (int64_t)(b * p.Hkv + kvh) * p.Skv * DQK;
 
-  acc_t acc[C::N_RT * C::N_DT];
-#pragma unroll
-  for (int t = 0; t < C::N_RT * C::N_DT; ++t) acc[t] = acc_t{};
-
-  u32x4 ps[C::SCH], pk[C::KCH];
-  auto prefetch = [&](int j) {
-    const int k0 = j * BC;
-#pragma unroll
-    for (int n = 0; n < C::SCH; ++n) {
-      const int c = tid + n * NT, row = c / (BR / 8), col = (c % (BR / 8)) * 8;
-      ps[n] = *reinterpret_cast<const u32x4*>(wsb + (int64_t)(k0 + row) * p.sq_pad + col);
-    }
-#pragma unroll
-    for (int n = 0; n < C::KCH; ++n) {
-      const int c = tid + n * NT, row = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
-      pk[n] = (k0 + row < p.Skv) ? *reinterpret_cast<const u32x4*>(Kb + (int64_t)(k0 + row) * DQK + col)
-                                 : u32x4{0, 0, 0, 0};
-    }
+  auto load_chunk = [&](int c, int buf) {
+    char* base = smem + buf * C::BUF_BYTES;
+    const int j = c / CPT, part = c % CPT;
+    const bf16_t* blk = wsh + ((int64_t)j * p.n_q_tiles + i) * (BC * BR) + part * KC * BR;
+    copy_frags(blk, C::ST_BYTES / 1024, base, w, lane);
+    gather_frags<DQK>(Kb, c * KC, p.Skv, (KC / 32) * (DQK / 16), base + C::ST_BYTES, w, lane);
   };
 
-  if (j_first <= j_last) prefetch(j_first);
-  for (int j = j_first; j <= j_last; ++j) {  // ascending KV order
-    __syncthreads();
+  // per-lane parts of the transpose-read addresses (see gemm4_atomic in bwd_main.h)
+  const int i16 = lane & 15, jj = i16 >> 2, cc = i16 & 3;
+  const int q4 = ((lane & 16) >> 2) + cc;
+  const int a_base = (q4 >> 1) * 512 + (8 * g + jj + 32 * (q4 & 1)) * 8;
+  const int b_base = ((lane & 16) >> 4) * 1024 + (8 * g + jj + 32 * (cc >> 1)) * 16 + 8 * (cc & 1);
+
+  acc_t acc[C::PER_W];
 #pragma unroll
-    for (int n = 0; n < C::SCH; ++n) {
-      const int c = tid + n * NT, row = c / (BR / 8), col = (c % (BR / 8)) * 8;
-      *reinterpret_cast<u32x4*>(sST + lds_off<C::STROWB>(row, col)) = ps[n];
-    }
+  for (int t = 0; t < C::PER_W; ++t) acc[t] = acc_t{};
+
+  if (c_first < c_end) load_chunk(c_first, 0);
+  for (int c = c_first; c < c_end; ++c) {
+    const int buf = (c - c_first) & 1;
+    wait_vmem();
+    __syncthreads();  // chunk c landed; every wave is done with the other buffer
+    if (c + 1 < c_end) load_chunk(c + 1, buf ^ 1);
+    const char* sST = smem + buf * C::BUF_BYTES;
+    const char* sK = sST + C::ST_BYTES;
 #pragma unroll
-    for (int n = 0; n < C::KCH; ++n) {
-      const int c = tid + n * NT, row = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
-      *reinterpret_cast<u32x4*>(sK + lds_off<C::KROWB>(row, col)) = pk[n];
-    }
-    __syncthreads();
-    if (j < j_last) prefetch(j + 1);
+    for (int t = 0; t < KC / 16; ++t) {
+      const int ka = (t >> 1) * 2048 + (t & 1) * 128;
+      const bf16x8 a = concat(lds_read_tr(sST, a_base + ka), lds_read_tr(sST, a_base + ka + 32));
 #pragma unroll
-    for (int t = 0; t < C::N_K; ++t) {
-      const int ka = t * KT + 8 * g;
-      bf16x8 bk[C::N_DT];
-#pragma unroll
-      for (int dt = 0; dt < C::N_DT; ++dt)
-        bk[dt] = tr_operand2<MT, C::KROWB>(sK, w * C::DW + dt * MT, ka, ka + 4, lane);
-#pragma unroll
-      for (int rt = 0; rt < C::N_RT; ++rt) {
-        bf16x8 a = tr_operand2<MT, C::STROWB>(sST, rt * MT, ka, ka + 4, lane);
-#pragma unroll
-        for (int dt = 0; dt < C::N_DT; ++dt)
-          acc[rt * C::N_DT + dt] = M::mma(a, bk[dt], acc[rt * C::N_DT + dt]);
+      for (int x = 0; x < C::PER_W; ++x) {
+        const int dt = w + x * C::NW;
+        if (dt < C::N_DT) {
+          const int kb = ((t >> 1) * (DQK / 16) + 2 * dt) * 1024 + (t & 1) * 256;
+          const bf16x8 bk = concat(lds_read_tr(sK, b_base + kb), lds_read_tr(sK, b_base + kb + 64));
+          acc[x] = M::mma(a, bk, acc[x]);
+        }
       }
     }
   }
 
-  // dQ = scale * acc, rows past the buffer are not stored; rows past len_q are exactly zero
+  // dQ = scale * acc; rows past the buffer are not stored, rows past len_q come out exactly zero
   bf16_t* dqb = p.dq + (int64_t)(b * p.Hq + h) * p.Sq * DQK;
 #pragma unroll
-  for (int rt = 0; rt < C::N_RT; ++rt)
+  for (int x = 0; x < C::PER_W; ++x) {
+    const int dt = w + x * C::NW;
+    if (dt < C::N_DT) {
 #pragma unroll
-    for (int dt = 0; dt < C::N_DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < C::NACC; ++r) {
-        const int q = q0 + rt * MT + acc_row<MT>(r, g);
-        if (q < p.Sq)
-          dqb[(int64_t)q * DQK + w * C::DW + dt * MT + lc] =
-              float_to_bf16(acc[rt * C::N_DT + dt][r] * p.scale);
+      for (int r = 0; r < 16; ++r) {
+        const int q = q0 + acc_row<32>(r, g);
+        if (q < p.Sq) dqb[(int64_t)q * DQK + dt * 32 + lc] = float_to_bf16(acc[x][r] * p.scale);
       }
+    }
+  }
 }
 
 }  // namespace sdpa

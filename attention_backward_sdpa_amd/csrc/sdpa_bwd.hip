@@ -22,38 +22,42 @@ namespace {
 constexpr int64_t kAlign = 256;
 inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-// Tile geometry per supported (Dqk, Dv): the MFMA tile MT (32 -> 32x32x16, 16 -> 16x16x32), the
-// key tile BC = 4 * MT and the q tile BR.
+// Tile geometry per supported (Dqk, Dv): keys per wave KPW (the key tile is BC = 4 * KPW) and the
+// q tile BR = 32.  64 keys per wave where the dK^T/dV^T accumulators (KPW * (Dqk + Dv) floats per
+// wave) fit the 256 accumulation registers of a lane, 32 above that.
 struct Geometry {
-  int mt, bc, br;
+  int kpw, bc, br;
 };
 
 bool geometry_for(int Dqk, int Dv, Geometry* g) {
-  if (Dqk == 64 && Dv == 64) *g = {32, 128, 64};
-  else if (Dqk == 128 && Dv == 128) *g = {32, 128, 64};
-  else if (Dqk == 192 && Dv == 128) *g = {32, 128, 64};
-  else if (Dqk == 256 && Dv == 256) *g = {16, 64, 64};
+  if (Dqk == 64 && Dv == 64) *g = {64, 256, 32};
+  else if (Dqk == 128 && Dv == 128) *g = {64, 256, 32};
+  else if (Dqk == 192 && Dv == 128) *g = {32, 128, 32};
+  else if (Dqk == 256 && Dv == 256) *g = {32, 128, 32};
   else return false;
   return true;
 }
 
 struct Carve {
-  int64_t delta = 0, dq_accum = -1, ds = -1, dk_ws = -1, dv_ws = -1, total = 0;
+  int64_t stats = 0, qt = 0, dot = 0, dq_accum = -1, ds = -1, dk_ws = -1, dv_ws = -1, total = 0;
   int64_t sq_pad = 0, skv_pad = 0;
 };
 
 Carve carve(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv, int det, const Geometry& g) {
   Carve c;
   int64_t off = 0;
-  const int64_t rows = (int64_t)B * Hq * Sq;
-  c.delta = off;
-  off = align_up(off + rows * 4, kAlign);
+  c.sq_pad = align_up(Sq, g.br);
+  c.skv_pad = align_up(Skv, g.bc);
+  c.stats = off;  // [LSE * log2e, delta] per padded q row
+  off = align_up(off + (int64_t)B * Hq * c.sq_pad * 2 * 4, kAlign);
+  c.qt = off;     // Q^T fragments per 32-row q tile
+  off = align_up(off + (int64_t)B * Hq * c.sq_pad * Dqk * 2, kAlign);
+  c.dot = off;    // dO^T fragments per 32-row q tile
+  off = align_up(off + (int64_t)B * Hq * c.sq_pad * Dv * 2, kAlign);
   if (!det) {
     c.dq_accum = off;
-    off = align_up(off + rows * Dqk * 4, kAlign);
+    off = align_up(off + (int64_t)B * Hq * Sq * Dqk * 4, kAlign);
   } else {
-    c.sq_pad = align_up(Sq, g.br);
-    c.skv_pad = align_up(Skv, g.bc);
     c.ds = off;
     off = align_up(off + (int64_t)B * Hq * c.skv_pad * c.sq_pad * 2, kAlign);
   }
@@ -78,7 +82,7 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
   if (!geometry_for(Dqk, Dv, geo)) return SDPA_BWD_UNSUPPORTED;
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return SDPA_BWD_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
-      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+      ((uintptr_t)lse & 3) != 0 || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return SDPA_BWD_UNSUPPORTED;
   return SDPA_BWD_OK;
 }
@@ -109,33 +113,34 @@ hipError_t launch_dq2k(const Dq2kParams& dp, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DQK, int DV, int MT, int BR>
+template <int DQK, int DV, int KPW>
 hipError_t dispatch_main(const MainParams& mp, int det, int grid, hipStream_t s) {
-  if (det) return launch_main<MainCfg<DQK, DV, MT, BR, true>>(mp, grid, s);
-  return launch_main<MainCfg<DQK, DV, MT, BR, false>>(mp, grid, s);
+  if (det) return launch_main<MainCfg<DQK, DV, KPW, true>>(mp, grid, s);
+  return launch_main<MainCfg<DQK, DV, KPW, false>>(mp, grid, s);
 }
 
 hipError_t run_main(int Dqk, int Dv, const MainParams& mp, int det, int grid, hipStream_t s) {
-  if (Dqk == 64) return dispatch_main<64, 64, 32, 64>(mp, det, grid, s);
-  if (Dqk == 128) return dispatch_main<128, 128, 32, 64>(mp, det, grid, s);
-  if (Dqk == 192) return dispatch_main<192, 128, 32, 64>(mp, det, grid, s);
-  return dispatch_main<256, 256, 16, 64>(mp, det, grid, s);
+  if (Dqk == 64) return dispatch_main<64, 64, 64>(mp, det, grid, s);
+  if (Dqk == 128) return dispatch_main<128, 128, 64>(mp, det, grid, s);
+  if (Dqk == 192) return dispatch_main<192, 128, 32>(mp, det, grid, s);
+  return dispatch_main<256, 256, 32>(mp, det, grid, s);
 }
 
 hipError_t run_dq2k(int Dqk, const Dq2kParams& dp, int grid, hipStream_t s) {
-  if (Dqk == 64) return launch_dq2k<Dq2kCfg<64, 64, 128>>(dp, grid, s);
-  if (Dqk == 128) return launch_dq2k<Dq2kCfg<128, 64, 128>>(dp, grid, s);
-  if (Dqk == 192) return launch_dq2k<Dq2kCfg<192, 64, 128>>(dp, grid, s);
-  return launch_dq2k<Dq2kCfg<256, 64, 64>>(dp, grid, s);
+  if (Dqk == 64) return launch_dq2k<Dq2kCfg<64, 256>>(dp, grid, s);
+  if (Dqk == 128) return launch_dq2k<Dq2kCfg<128, 256>>(dp, grid, s);
+  if (Dqk == 192) return launch_dq2k<Dq2kCfg<192, 128>>(dp, grid, s);
+  return launch_dq2k<Dq2kCfg<256, 128>>(dp, grid, s);
 }
 
-hipError_t launch_preprocess(const PreParams& pp, int Dv, hipStream_t s) {
-  const int rpb = 256 / (Dv / 8);
-  const int64_t blocks = (pp.rows + rpb - 1) / rpb;
-  if (blocks == 0) return hipSuccess;
-  if (Dv == 64) hipLaunchKernelGGL(preprocess_kernel<64>, dim3(blocks), dim3(256), 0, s, pp);
-  else if (Dv == 128) hipLaunchKernelGGL(preprocess_kernel<128>, dim3(blocks), dim3(256), 0, s, pp);
-  else hipLaunchKernelGGL(preprocess_kernel<256>, dim3(blocks), dim3(256), 0, s, pp);
+hipError_t launch_preprocess(const PreParams& pp, int Dqk, int Dv, int64_t tiles, hipStream_t s) {
+  if (tiles == 0) return hipSuccess;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)tiles), block(256);
+  if (Dqk == 64) hipLaunchKernelGGL((preprocess_kernel<64, 64>), grid, block, 0, s, pp);
+  else if (Dqk == 128) hipLaunchKernelGGL((preprocess_kernel<128, 128>), grid, block, 0, s, pp);
+  else if (Dqk == 192) hipLaunchKernelGGL((preprocess_kernel<192, 128>), grid, block, 0, s, pp);
+  else hipLaunchKernelGGL((preprocess_kernel<256, 256>), grid, block, 0, s, pp);
   return hipGetLastError();
 }
 
@@ -176,7 +181,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   if (c.total > 0 && ((uintptr_t)workspace % kAlign) != 0) return SDPA_BWD_UNSUPPORTED;
   if (!(scale > 0.f) || !isfinite(scale)) scale = 1.0f / sqrtf((float)Dqk);
   auto rec = [&](int n) {
-    if (events) hipEventRecord((hipEvent_t)events[n], stream);
+    if (events) (void)hipEventRecord((hipEvent_t)events[n], stream);
   };
 
   hipError_t e = hipSuccess;
@@ -195,23 +200,26 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   }
 
   char* ws = (char*)workspace;
-  float* delta = (float*)(ws + c.delta);
+  float* stats = (float*)(ws + c.stats);
   float* dq_accum = det ? nullptr : (float*)(ws + c.dq_accum);
   const bool gqa = Hq != Hkv;
 
   PreParams pp;
+  pp.q = (const bf16_t*)q;
   pp.o = (const bf16_t*)o;
   pp.dO = (const bf16_t*)dO;
-  pp.delta = delta;
+  pp.lse = lse;
+  pp.stats = stats;
+  pp.qt = (bf16_t*)(ws + c.qt);
+  pp.dot = (bf16_t*)(ws + c.dot);
   pp.dq_accum = dq_accum;
   pp.seq_q_lens = seq_q_lens;
-  pp.rows = (int64_t)B * Hq * Sq;
   pp.Hq = Hq;
   pp.Sq = Sq;
-  pp.Dv = Dv;
+  pp.sq_pad = (int)c.sq_pad;
   pp.Dqk = Dqk;
   pp.zero_rows = det ? 0 : 1;
-  e = launch_preprocess(pp, Dv, stream);
+  e = launch_preprocess(pp, Dqk, Dv, (int64_t)B * Hq * (c.sq_pad / geo.br), stream);
   if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   rec(1);
 
@@ -220,8 +228,9 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   mp.k = (const bf16_t*)k;
   mp.v = (const bf16_t*)v;
   mp.dO = (const bf16_t*)dO;
-  mp.lse = lse;
-  mp.delta = delta;
+  mp.stats = stats;
+  mp.qt = pp.qt;
+  mp.dot = pp.dot;
   mp.dq_accum = dq_accum;
   mp.ds_ws = det ? (bf16_t*)(ws + c.ds) : nullptr;
   mp.dk_out = gqa ? (bf16_t*)(ws + c.dk_ws) : (bf16_t*)dk;
@@ -290,9 +299,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     dp.window_right = mp.window_right;
     dp.bottom_right = mp.bottom_right;
     dp.n_kv_tiles = mp.n_kv_tiles;
-    dp.n_q_tiles = (Sq + geo.br - 1) / geo.br;
-    dp.sq_pad = (int)c.sq_pad;
-    dp.skv_pad = (int)c.skv_pad;
+    dp.n_q_tiles = (int)(c.sq_pad / geo.br);
     dp.scale = scale;
     const int64_t grid = (int64_t)dp.n_q_tiles * B * Hq;
     if (grid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
@@ -351,29 +358,35 @@ int sdpa_bwd_ex_events(const void* q, const void* k, const void* v, const void* 
              window_right, workspace, workspace_bytes, true, (hipStream_t)stream, events);
 }
 
-int sdpa_bwd_preprocess(const void* o, const void* dO, float* delta, float* dq_accum,
-                        const int* seq_q_lens, int B, int Hq, int Sq, int Dv, int Dqk,
-                        void* stream) {
+int sdpa_bwd_preprocess(const void* o, const void* dO, const float* lse, float* stats,
+                        float* dq_accum, const int* seq_q_lens, int B, int Hq, int Sq, int Dv,
+                        int Dqk, void* stream) {
   if (B < 0 || Hq < 0 || Sq < 0) return SDPA_BWD_INVALID_ARG;
-  if (Dv != 64 && Dv != 128 && Dv != 256) return SDPA_BWD_UNSUPPORTED;
-  if (dq_accum && (Dqk <= 0 || Dqk % 4 != 0)) return SDPA_BWD_INVALID_ARG;
-  if (!o || !dO || !delta) return SDPA_BWD_INVALID_ARG;
-  if (!aligned16(o) || !aligned16(dO) || !aligned16(delta) || (dq_accum && !aligned16(dq_accum)))
+  Geometry geo;
+  if (!geometry_for(Dqk, Dv, &geo)) return SDPA_BWD_UNSUPPORTED;
+  if (!o || !dO || !lse || !stats) return SDPA_BWD_INVALID_ARG;
+  if (!aligned16(o) || !aligned16(dO) || !aligned16(stats) || (dq_accum && !aligned16(dq_accum)) ||
+      ((uintptr_t)lse & 3) != 0)
     return SDPA_BWD_UNSUPPORTED;
   PreParams pp;
+  pp.q = nullptr;
   pp.o = (const bf16_t*)o;
   pp.dO = (const bf16_t*)dO;
-  pp.delta = delta;
+  pp.lse = lse;
+  pp.stats = stats;
+  pp.qt = nullptr;  // statistics (and accumulator zeroing) only
+  pp.dot = nullptr;
   pp.dq_accum = dq_accum;
   pp.seq_q_lens = seq_q_lens;
-  pp.rows = (int64_t)B * Hq * Sq;
+  pp.sq_pad = (int)align_up(Sq, 32);
   pp.Hq = Hq;
   pp.Sq = Sq;
-  pp.Dv = Dv;
   pp.Dqk = Dqk;
   pp.zero_rows = dq_accum ? 1 : 0;
-  return launch_preprocess(pp, Dv, (hipStream_t)stream) == hipSuccess ? SDPA_BWD_OK
-                                                                      : SDPA_BWD_LAUNCH_FAILED;
+  const int64_t tiles = (int64_t)B * Hq * (pp.sq_pad / 32);
+  return launch_preprocess(pp, Dqk, Dv, tiles, (hipStream_t)stream) == hipSuccess
+             ? SDPA_BWD_OK
+             : SDPA_BWD_LAUNCH_FAILED;
 }
 
 const char* sdpa_bwd_status_string(int status) {

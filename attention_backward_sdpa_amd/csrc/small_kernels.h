@@ -8,54 +8,109 @@
 namespace sdpa {
 
 // ---- preprocess ---------------------------------------------------------------------------------
-// One row of Dv bf16 per (Dv / 8) lanes; each lane loads 16 bytes of O and dO, multiplies in fp32
-// and the row's lanes reduce with butterfly shuffles in a fixed order (deterministic).  Rows at or
-// past the batch entry's query length get delta = 0.  When zero_rows is set, the same rows of the
-// fp32 dQ accumulator (Dqk floats each) are cleared.
+// One workgroup per 32-row q tile of one (batch, query head):
+//   * stats[row] = [LSE * log2(e), delta] with delta = rowsum(O * dO) in fp32.  Rows at or past the
+//     batch entry's query length, rows past the buffer and rows whose LSE is -inf (no visible key
+//     in the forward) get [+inf, 0], so the main kernel replays P = 0 for them without a NaN.
+//     The row's Dv/8 lanes reduce with butterfly shuffles in a fixed order (deterministic).
+//   * qt / dot: the tile's Q^T and dO^T as ready-made MFMA A operands (contraction over q) for
+//     the main kernel's GEMM5 and GEMM3: fragment (dt, tb), lane l holds the 8 values
+//     X[16*tb + 4*g + {0..3, 8..11}][32*dt + l % 32], g = l / 32, i.e. the q order in which the
+//     accumulator layout delivers P and dS.  Each fragment is 1 KiB, lane-major, so the main kernel
+//     copies a tile into LDS with linear 16-byte loads and reads it conflict-free.  Rows past the
+//     buffer are zero.
+//   * when zero_rows is set, the tile's rows of the fp32 dQ accumulator are cleared.
 struct PreParams {
+  const bf16_t* q;
   const bf16_t* o;
   const bf16_t* dO;
-  float* delta;
-  float* dq_accum;
+  const float* lse;
+  float* stats;              // (B*Hq, sq_pad, 2)
+  bf16_t* qt;                // (B*Hq, sq_pad/32, Dqk/32*2, 64, 8) or null
+  bf16_t* dot;               // (B*Hq, sq_pad/32, Dv/32*2, 64, 8) or null
+  float* dq_accum;           // (B*Hq, Sq, Dqk) or null
   const int* seq_q_lens;
-  int64_t rows;   // B * Hq * Sq
-  int Hq, Sq, Dv, Dqk;
+  int Hq, Sq, sq_pad, Dqk;
   int zero_rows;
 };
 
-template <int DV>
+template <int DQK, int DV>
 __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
-  constexpr int LPR = DV / 8;              // lanes per row
-  constexpr int RPB = 256 / LPR;           // rows per block
+  constexpr int BR = 32;
+  constexpr int LPR = DV / 8;              // lanes per row for the row dot
+  constexpr int RPP = 256 / LPR;           // rows per pass
+  // the tile's Q and dO rows, staged (row stride padded by 16 bytes against bank conflicts)
+  __shared__ __attribute__((aligned(16))) char sq[BR * (DQK * 2 + 16)];
+  __shared__ __attribute__((aligned(16))) char so[BR * (DV * 2 + 16)];
   const int tid = threadIdx.x;
-  const int sub = tid % LPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;
-  float acc = 0.f;
-  if (row < p.rows) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p.o + row * DV + sub * 8);
-    const u32x4 c = *reinterpret_cast<const u32x4*>(p.dO + row * DV + sub * 8);
+  const int nt = p.sq_pad / BR;
+  const int64_t bh = blockIdx.x / nt;
+  const int i = blockIdx.x % nt;
+  const int q0 = i * BR;
+  const int b = (int)(bh / p.Hq);
+  const int Lq = p.seq_q_lens ? p.seq_q_lens[b] : p.Sq;
+
+  // ---- statistics ------------------------------------------------------------------------------
+  for (int r0 = 0; r0 < BR; r0 += RPP) {
+    const int r = r0 + tid / LPR, sub = tid % LPR, s = q0 + r;
+    const bool real = s < p.Sq;
+    const int64_t row = bh * p.Sq + s;
+    float acc = 0.f;
+    if (real) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(p.o + row * DV + sub * 8);
+      const u32x4 c = *reinterpret_cast<const u32x4*>(p.dO + row * DV + sub * 8);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc += __uint_as_float(a[e] << 16) * __uint_as_float(c[e] << 16);
-      acc += __uint_as_float(a[e] & 0xffff0000u) * __uint_as_float(c[e] & 0xffff0000u);
+      for (int e = 0; e < 4; ++e) {
+        acc += __uint_as_float(a[e] << 16) * __uint_as_float(c[e] << 16);
+        acc += __uint_as_float(a[e] & 0xffff0000u) * __uint_as_float(c[e] & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+    if (sub == 0) {
+      const bool live = real && s < Lq;
+      const float l = live ? p.lse[row] : -INFINITY;
+      const bool none = !(l > -INFINITY);  // -inf (or NaN) LSE: the row saw no key
+      reinterpret_cast<float2*>(p.stats)[bh * p.sq_pad + s] =
+          make_float2(none ? INFINITY : l * kLog2e, (live && !none) ? acc : 0.f);
+    }
+    if (p.zero_rows && real) {
+      float4* dst = reinterpret_cast<float4*>(p.dq_accum + row * p.Dqk);
+      for (int x = sub; x < p.Dqk / 4; x += LPR) dst[x] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
+  if (p.qt == nullptr) return;
+
+  // ---- Q^T / dO^T fragments ---------------------------------------------------------------------
+  for (int c = tid; c < BR * DQK / 8; c += 256) {
+    const int r = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (q0 + r < p.Sq) v = *reinterpret_cast<const u32x4*>(p.q + (bh * p.Sq + q0 + r) * DQK + col);
+    *reinterpret_cast<u32x4*>(sq + r * (DQK * 2 + 16) + col * 2) = v;
+  }
+  for (int c = tid; c < BR * DV / 8; c += 256) {
+    const int r = c / (DV / 8), col = (c % (DV / 8)) * 8;
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (q0 + r < p.Sq) v = *reinterpret_cast<const u32x4*>(p.dO + (bh * p.Sq + q0 + r) * DV + col);
+    *reinterpret_cast<u32x4*>(so + r * (DV * 2 + 16) + col * 2) = v;
+  }
+  __syncthreads();
+  const int lane = tid & 63, g = lane >> 5, lc = lane & 31;
+  auto fragment = [&](const char* st, int rowb, int dt, int tb) {
+    bf16_t v[8];
 #pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-  if (row < p.rows && sub == 0) {
-    const int s = (int)(row % p.Sq);
-    const int b = (int)(row / ((int64_t)p.Sq * p.Hq));
-    const int Lq = p.seq_q_lens ? p.seq_q_lens[b] : p.Sq;
-    p.delta[row] = (s < Lq) ? acc : 0.f;
-  }
-  if (p.zero_rows) {
-    // RPB rows of Dqk floats = RPB * Dqk / 4 float4 stores spread over the block
-    const int64_t row0 = (int64_t)blockIdx.x * RPB;
-    const int64_t nrows = (p.rows - row0) < RPB ? (p.rows - row0) : RPB;
-    const int64_t n4 = nrows * p.Dqk / 4;
-    float4* dst = reinterpret_cast<float4*>(p.dq_accum + row0 * p.Dqk);
-    for (int64_t x = tid; x < n4; x += 256) dst[x] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+    for (int e = 0; e < 8; ++e) {
+      const int qq = 16 * tb + 4 * g + (e & 3) + (e >> 2) * 8;
+      v[e] = *reinterpret_cast<const bf16_t*>(st + qq * (rowb + 16) + (32 * dt + lc) * 2);
+    }
+    return u32x4{v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
+                 v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16)};
+  };
+  constexpr int FQ = DQK / 32 * 2, FO = DV / 32 * 2;
+  u32x4* qtb = reinterpret_cast<u32x4*>(p.qt + (bh * nt + i) * (int64_t)(BR * DQK));
+  u32x4* dotb = reinterpret_cast<u32x4*>(p.dot + (bh * nt + i) * (int64_t)(BR * DV));
+  for (int f = tid >> 6; f < FQ; f += 4) qtb[f * 64 + lane] = fragment(sq, DQK * 2, f >> 1, f & 1);
+  for (int f = tid >> 6; f < FO; f += 4) dotb[f * 64 + lane] = fragment(so, DV * 2, f >> 1, f & 1);
 }
 
 // ---- dQ convert ---------------------------------------------------------------------------------

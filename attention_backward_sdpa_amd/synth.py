@@ -56,8 +56,12 @@ WORKLOADS = {
 
 def bf16_bits(x) -> np.ndarray:
     """Round float32 values to bfloat16 (round to nearest, ties to even); returns uint16 bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(f)):
+        raise ValueError("bf16_bits expects finite values")
+    u = f.view(np.uint32)
+    # finite inputs stay below 2**32 after adding the rounding bias
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return rounded.astype(np.uint16)
 
 

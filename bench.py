@@ -1,0 +1,240 @@
+"""Benchmark of the MI355X attention backward.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one whole backward chain (preprocess, main, GQA reduce, dQ convert or dq2k) over one
+batch of synthetic inputs resident in HBM.  The default workload is causal GQA, B=1, Hq=32, Hkv=8,
+S=4096, D=128 with fp32 atomic dQ.  Prints one JSON line: whole-chain TFLOP/s, the main kernel's
+MFMA roofline (its duration measured with HIP events recorded by the library on the launch stream)
+and the CPU oracle timed on a bounded sample of the same workload.
+
+FLOPs per visible (query, key) pair and head: 2 * (3 * Dqk + 2 * Dv) (S recompute, dP, dV, dQ,
+dK); for a plain causal mask the dense count is halved, with a window or padding the visible
+pairs are counted.
+
+Inputs: Q, K, V, dO drawn by the seeded generator; O and LSE come from a float32 forward computed
+with torch on the GPU (input preparation only, outside the timed region).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from attention_backward_sdpa_amd import synth  # noqa: E402
+
+METRIC = "attention-backward TFLOP/s and % of bf16 MFMA peak, S=4096 D=128 causal"
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU (AMD's 2.5 PFLOP/s)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "main_kernel_traffic.json")
+KERNEL_SOURCES = ["bwd_main.h", "common.h", "masks.h"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "attention_backward_sdpa_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def visible_pairs(w, lens):
+    """Visible (query, key) pairs summed over the batch (the mask rule, counted row by row)."""
+    total = 0
+    for b in range(w.B):
+        L = w.Sq if lens is None else int(lens[b])
+        Lk = w.Skv if lens is None else int(lens[b])
+        i = np.arange(L)
+        hi = np.minimum(i, Lk - 1) if w.causal else np.full(L, Lk - 1)
+        lo = np.maximum(i - w.window_left, 0) if w.window_left >= 0 else np.zeros(L, dtype=np.int64)
+        total += int(np.maximum(hi - lo + 1, 0).sum())
+    return total
+
+
+def algorithmic_flops(w, lens):
+    per_pair = 2 * (3 * w.Dqk + 2 * w.Dv)
+    if w.window_left < 0 and lens is None:
+        return per_pair * w.Sq * w.Skv * (0.5 if w.causal else 1.0) * w.B * w.Hq
+    return per_pair * visible_pairs(w, lens) * w.Hq
+
+
+def gpu_forward_inputs(torch, q, k, v, w, lens):
+    """float32 forward on the GPU -> O (bf16) and natural-log LSE (fp32), rows with no key -inf."""
+    B, Hq, Sq, _ = q.shape
+    group = w.Hq // w.Hkv
+    o = torch.empty(B, Hq, Sq, w.Dv, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
+    i = torch.arange(Sq, device=q.device)[:, None]
+    j = torch.arange(w.Skv, device=q.device)[None, :]
+    for b in range(B):
+        L = Sq if lens is None else int(lens[b])
+        vis = (i < L) & (j < L)
+        if w.causal:
+            vis &= j <= i
+        if w.window_left >= 0:
+            vis &= j >= i - w.window_left
+        for h in range(Hq):
+            kh = h // group
+            kt = k[b, kh].float().t().contiguous()
+            s = (q[b, h].float() @ kt) * w.softmax_scale
+            s = s.masked_fill(~vis, float("-inf"))
+            l = torch.logsumexp(s, dim=-1)
+            p = torch.where(vis, torch.exp(s - torch.where(torch.isinf(l), 0.0, l)[:, None]), 0.0)
+            o[b, h] = (p @ v[b, kh].float()).to(torch.bfloat16)
+            lse[b, h] = l
+    return o, lse
+
+
+def cpu_baseline(w, inp, lens, budget_s=15.0):
+    """The fp64 CPU oracle (unchanged) on the first query heads of batch entry 0, timed until
+    about budget_s seconds of work; the rate is scaled to the same FLOP convention."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    group = w.Hq // w.Hkv
+    f = lambda x: synth.bf16_to_f32(x).astype(np.float64)
+    L = None if lens is None else [int(lens[0])]
+    flops = done = 0.0
+    heads = 0
+    t_total = 0.0
+    while heads < w.Hq and t_total < budget_s:
+        h = heads
+        kh = h // group
+        sl = lambda a, hh: a[0:1, hh:hh + 1]
+        q, kk, vv, do = f(sl(inp.q, h)), f(sl(inp.k, kh)), f(sl(inp.v, kh)), f(sl(inp.do, h))
+        o, lse = oracle.forward(q, kk, vv, w.softmax_scale, causal=w.causal,
+                                window_left=w.window_left, seq_q_lens=L, seq_kv_lens=L)
+        o = synth.round_bf16(o.astype(np.float32)).astype(np.float64)
+        lse = lse.astype(np.float32).astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.backward(q, kk, vv, o, do, lse, w.softmax_scale, causal=w.causal,
+                        window_left=w.window_left, seq_q_lens=L, seq_kv_lens=L)
+        t_total += time.perf_counter() - t0
+        one = synth.small_variant(w, B=1, Hq=1, Hkv=1)
+        flops += algorithmic_flops(one, None if lens is None else [lens[0]])
+        heads += 1
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.Hq} (batch, query-head) slices of {w.name}, "
+                      f"backward only, fp64 numpy, {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa_causal_s4096_d128", choices=list(synth.WORKLOADS))
+    ap.add_argument("--deterministic", type=int, default=-1,
+                    help="override the workload's dQ route (-1: as the workload states)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the "
+              f"attention backward shards over (batch, KV-head group) with no communication, "
+              f"so the whole-job rate is N times the one-GPU rate).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_backward_sdpa_amd as lib
+
+    w = synth.WORKLOADS[args.workload]
+    det = w.deterministic if args.deterministic < 0 else bool(args.deterministic)
+    inp = synth.draw_inputs(w)
+    lens = inp.seq_q_lens
+    dev = torch.device("cuda:0")
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v, do = bf(inp.q), bf(inp.k), bf(inp.v), bf(inp.do)
+    o, lse = gpu_forward_inputs(torch, q, k, v, w, lens)
+    lens_t = None if lens is None else torch.from_numpy(lens).to(dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nws = lib.workspace_size(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.Dqk, w.Dv, w.causal, w.window_left,
+                             det, lens is not None)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        lib.sdpa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale=w.softmax_scale, causal=w.causal,
+                        window_left=w.window_left, deterministic=det, seq_q_lens=lens_t,
+                        seq_kv_lens=lens_t, workspace=ws, stream=stream, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-step stage events (recorded by the library on the launch stream)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record(stream)  # materialise the underlying hipEvent
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        step(evs[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    stage_ms = np.array([[row[i].elapsed_time(row[i + 1]) for i in range(4)] for row in evs])
+    stage_avg = stage_ms.mean(axis=0)
+    main_ms = float(stage_avg[1])
+
+    flops = algorithmic_flops(w, lens)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    # the deterministic route's main kernel skips GEMM4 (dQ = dS K), which dq2k performs
+    main_flops = flops * ((2 * w.Dqk + 2 * w.Dv) / (3 * w.Dqk + 2 * w.Dv) if det else 1.0)
+    main_tflops = main_flops / (main_ms * 1e-3) / 1e12
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        if t.get("kernel_source_hash") == kernel_source_hash() and t.get("workload") == w.name \
+                and bool(t.get("deterministic")) == det:
+            traffic = t["hbm_bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        traffic = None
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq,
+                   "Skv": w.Skv, "Dqk": w.Dqk, "Dv": w.Dv, "causal": w.causal,
+                   "window_left": w.window_left, "padded": w.padded,
+                   "dq_route": "two-kernel deterministic" if det else "fp32 atomic",
+                   "algorithmic_gflop": round(flops / 1e9, 3)},
+        "stage_ms": {"preprocess": round(float(stage_avg[0]), 4), "main": round(main_ms, 4),
+                     "gqa_reduce": round(float(stage_avg[2]), 4),
+                     "dq_convert_or_dq2k": round(float(stage_avg[3]), 4)},
+        "roofline": {"kernel": "bwd_main_kernel", "bound": "mfma",
+                     "achieved": round(main_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, lens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -16,8 +16,8 @@
  *   q, dq : (B, Hq,  Sq,  Dqk) bf16       k, dk : (B, Hkv, Skv, Dqk) bf16
  *   v, dv : (B, Hkv, Skv, Dv)  bf16       o, dO : (B, Hq,  Sq,  Dv)  bf16
  *   lse   : (B, Hq,  Sq)       fp32, natural log; -inf marks a row that saw no key
- * bf16 values are passed as their 16-bit patterns.  All pointers are device pointers and must be
- * 16-byte aligned.  Supported head dims (Dqk, Dv): (64,64), (128,128), (192,128), (256,256).
+ * bf16 values are passed as their 16-bit patterns.  All pointers are device pointers; tensor
+ * pointers must be 16-byte aligned (lse 4-byte aligned) and the workspace 256-byte aligned.  Supported head dims (Dqk, Dv): (64,64), (128,128), (192,128), (256,256).
  *
  * Masks ("API Usage" and "Causal, sliding-window, and padding masks"): query q and key k are
  * visible together when q < seq_q, k < seq_kv, causal => k <= q + diag + window_right, and
@@ -55,9 +55,12 @@ enum {
   SDPA_BWD_LAUNCH_FAILED = 4         /* the HIP runtime reported an error at launch             */
 };
 
-/* Bytes of workspace needed by a call with these arguments (0 when none is needed beyond the
- * outputs; a 256-byte-aligned carve of delta, the fp32 dQ accumulator or the bf16 dS buffer, and
- * the per-query-head dK/dV partials under GQA).  Returns 0 for arguments sdpa_bwd would reject. */
+/* Bytes of workspace needed by a call with these arguments: a 256-byte-aligned carve of the
+ * per-row statistics (LSE * log2 e and delta), the Q^T and dO^T operand tiles the preprocess
+ * writes (B*Hq*Sq_pad*(Dqk+Dv) bf16), then either the fp32 dQ accumulator
+ * (B*Hq*Sq*Dqk floats) or, in deterministic mode, the bf16 dS buffer (B*Hq*Sq_pad*Skv_pad), then
+ * under GQA the bf16 per-query-head dK/dV partials.  Returns 0 for arguments sdpa_bwd rejects and
+ * for empty problems. */
 size_t sdpa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv,
                                int causal, int window_left, int deterministic, int has_seqlens);
 
@@ -93,12 +96,16 @@ int sdpa_bwd_ex_events(const void* q, const void* k, const void* v, const void* 
                        int window_right, void* workspace, size_t workspace_bytes, void* stream,
                        void* const* events);
 
-/* Step 1 of the chain alone ("The kernel chain", dot): delta[r] = sum_d O[r,d] * dO[r,d] in fp32
- * for the B*Hq*Sq rows of O/dO (rows at or past seq_q_lens[b] get 0), and, when dq_accum is not
- * NULL, zero the B*Hq*Sq*Dqk floats of dq_accum.  Dv in {64, 128, 256}. */
-int sdpa_bwd_preprocess(const void* o, const void* dO, float* delta, float* dq_accum,
-                        const int* seq_q_lens, int B, int Hq, int Sq, int Dv, int Dqk,
-                        void* stream);
+/* Step 1 of the chain alone ("The kernel chain", dot), as the chain runs it: for every query row
+ * (rows padded to Sq_pad = Sq rounded up to 32 per (b, h)) write the pair
+ *     stats[(b*Hq + h)*Sq_pad + s] = { LSE * log2(e),  rowsum(O * dO) in fp32 }
+ * and { +inf, 0 } for padding rows, rows at or past seq_q_lens[b] and rows whose LSE is -inf.
+ * When dq_accum is not NULL, also zero its B*Hq*Sq*Dqk floats.  stats holds B*Hq*Sq_pad*2
+ * floats.  (Dqk, Dv) as for sdpa_bwd; o, dO, stats, dq_accum 16-byte aligned, lse 4-byte
+ * aligned. */
+int sdpa_bwd_preprocess(const void* o, const void* dO, const float* lse, float* stats,
+                        float* dq_accum, const int* seq_q_lens, int B, int Hq, int Sq, int Dv,
+                        int Dqk, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* sdpa_bwd_status_string(int status);

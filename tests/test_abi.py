@@ -57,12 +57,16 @@ def _al(n):
 
 
 def test_workspace_size_rules(so):
-    # non-deterministic MHA: delta + fp32 dQ accumulator
-    assert _ws() == _al(4 * 256 * 4) + _al(4 * 256 * 128 * 4)
+    # non-deterministic MHA: per-row statistics (2 floats per row, rows padded to 32), the Q^T and
+    # dO^T operand tiles, fp32 dQ accumulator
+    tiles = 2 * _al(4 * 256 * 128 * 2)
+    assert _ws() == _al(4 * 256 * 8) + tiles + _al(4 * 256 * 128 * 4)
     # GQA adds per-query-head bf16 dK/dV partials
     assert _ws(Hkv=1) == _ws() + 2 * _al(4 * 256 * 128 * 2)
-    # deterministic: delta + bf16 dS (S_kv padded to the key tile, S_q to the q tile), no fp32 dQ
-    assert _ws(deterministic=True, Sq=200, Skv=200) == _al(4 * 200 * 4) + _al(4 * 256 * 256 * 2)
+    # deterministic: statistics + bf16 dS (S_kv padded to the 256-key tile, S_q to the 32-row
+    # q tile), no fp32 dQ
+    assert _ws(deterministic=True, Sq=200, Skv=200) == (_al(4 * 224 * 8) + 2 * _al(4 * 224 * 128 * 2)
+                                                        + _al(4 * 224 * 256 * 2))
     # monotone in the sequence length
     sizes = [_ws(Sq=s, Skv=s) for s in (64, 128, 300, 1000)]
     assert sizes == sorted(sizes)
@@ -100,5 +104,6 @@ def test_rejections_before_launch(so):
 
 def test_preprocess_rejections(so):
     p = ctypes.c_void_p(4096)
-    assert so.sdpa_bwd_preprocess(p, p, p, None, None, 1, 1, 8, 96, 0, None) == lib.UNSUPPORTED
-    assert so.sdpa_bwd_preprocess(None, p, p, None, None, 1, 1, 8, 128, 0, None) == lib.INVALID_ARG
+    assert so.sdpa_bwd_preprocess(p, p, p, p, None, None, 1, 1, 8, 96, 96, None) == lib.UNSUPPORTED
+    assert so.sdpa_bwd_preprocess(None, p, p, p, None, None, 1, 1, 8, 128, 128, None) == lib.INVALID_ARG
+    assert so.sdpa_bwd_preprocess(p, p, p, None, None, None, 1, 1, 8, 128, 128, None) == lib.INVALID_ARG
