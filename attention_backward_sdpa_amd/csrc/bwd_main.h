@@ -14,8 +14,11 @@
 // kernel reduces in ascending KV order.
 //
 // MI355X mapping (differs from the pages' SM120 warp-specialised design):
-//   * 4 waves of 64 lanes, one per SIMD; wave w owns KPW keys (64 at head dim <= 128, else 32),
-//     so the key tile is BC = 4 * KPW.  S and dP are computed with q as the MFMA row index and
+//   * NW waves of 64 lanes; wave w owns KPW = 32 keys, so the key tile is BC = 32 * NW.  At head
+//     dim <= 128 there are 8 waves, two per SIMD, each within 256 registers: the hardware then
+//     overlaps one wave's softmax VALU work and LDS latency with the other wave's MFMAs, and the
+//     256-key tile halves the dQ atomics and the Q/dO re-reads per key.  Above that, 4 waves with
+//     512 registers each hold the larger dK/dV accumulators.  S and dP are computed with q as the MFMA row index and
 //     keys as the column index (v_mfma_f32_32x32x16_bf16), so each wave's P and dS accumulators
 //     are already the B operand of GEMM3/GEMM5 (contraction over q) and its dK^T/dV^T partials
 //     complete inside the wave.
@@ -24,7 +27,7 @@
 //     immediate offset: LDS issue rate, not bytes, bounds this kernel on gfx950, and a 16-byte
 //     read costs the same issue slot as the half-as-wide transpose read.
 //       - Q and dO tiles (32 q rows) as A fragments of GEMM1/GEMM2, gathered straight from Q/dO
-//         with 16-byte global_load_lds;
+//         with 16-byte LDS-DMA buffer loads;
 //       - Q^T and dO^T as A fragments of GEMM5/GEMM3, written once per q tile by the preprocess
 //         kernel and copied linearly;
 //       - the key tile K as B fragments of GEMM1 (registers instead at head dim >= 192).
@@ -65,11 +68,11 @@ struct MainParams {
   float scale_log2;         // scale * log2(e)
 };
 
-template <int DQK_, int DV_, int KPW_, bool DET_>
+template <int DQK_, int DV_, int KPW_, int NW_, bool DET_>
 struct MainCfg {
-  static constexpr int DQK = DQK_, DV = DV_, KPW = KPW_;
+  static constexpr int DQK = DQK_, DV = DV_, KPW = KPW_, NW = NW_;
   static constexpr bool DET = DET_;
-  static constexpr int NW = 4, NT = 256, MT = 32, BR = 32, FRAG = 1024;
+  static constexpr int NT = NW * 64, MT = 32, BR = 32, FRAG = 1024;
   static constexpr int BC = NW * KPW;
   static constexpr int NKT = KPW / 32;         // 32-key MFMA tiles per wave
   static constexpr bool KREG = DQK >= 192;     // GEMM1's K operand from registers
@@ -92,41 +95,131 @@ struct MainCfg {
   static constexpr int OFF_ST = OFF_T + NBUF * TILE_BYTES;
   static constexpr int LDS_BYTES = OFF_ST + SST_BYTES;
   static_assert(KPW % 32 == 0, "keys per wave");
+  static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
   static_assert(DQK % 64 == 0 && DV % 64 == 0, "head dims must be multiples of 64");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-__device__ __forceinline__ void g2lds4(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0, 0);
+// The q-tile, K and dS operands go straight from global memory into LDS with the buffer form of
+// the LDS-DMA load (buffer_load ... lds): each lane supplies a byte offset into a raw buffer
+// resource, the data lands at the wave-uniform LDS base (M0) + 16 (or 4) bytes * lane.  The buffer
+// form (rather than global_load_lds) keeps the compiler's LDS wait counting exact, so the operand
+// reads of the compute stay pipelined while the next tile streams in.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer over `bytes` bytes at `base`; reads past the end return zero.  The host keeps every
+// buffer below 2^31 bytes.
+__device__ __forceinline__ rsrc_t buf_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ void g2lds16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+__device__ __forceinline__ void dma4(rsrc_t r, uint32_t off, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds_wave_base, 4, off, 0, 0, 0);
+}
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t off, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, off, 0, 0, 0);
 }
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Gather `nfrag` MFMA fragments of a row-major (.., D) bf16 matrix into LDS, one 16-byte
-// global_load_lds per fragment and wave: fragment (rt, t) of rows row0 + 32*rt .. +31 holds, for
-// lane l, row 32*rt + l % 32 and columns 16*t + 8*(l / 32) .. +7.  Fragment f = rt*(D/16) + t
-// lands at lds + f * 1 KiB.  Rows at or past rows_valid re-read row rows_valid - 1 (finite data
-// that every product masks out).  Fragments are spread over the 4 waves.
-template <int D>
-__device__ __forceinline__ void gather_frags(const bf16_t* gbase, int row0, int rows_valid,
-                                             int nfrag, char* lds, int w, int lane) {
-  for (int f = w; f < nfrag; f += 4) {
+// Gather `nfrag` MFMA fragments of a row-major (rows_valid, D) bf16 matrix (buffer `src`) into
+// LDS, one 16-byte load per fragment and wave: fragment (rt, t) of rows row0 + 32*rt .. +31 holds,
+// for 16-byte chunk n, row 32*rt + n % 32 and columns 16*t + 8*(n / 32) .. +7 (so lane l of a
+// linear read gets the B/A operand layout of v_mfma_f32_32x32x16_bf16).  Fragment f = rt*(D/16) + t
+// lands at lds + f * 1 KiB.  With SWZ the chunks of each 256-byte row r of fragment f are stored
+// at position (n % 16) ^ (4 * kswz(r, f)) (see kswz): the LDS-DMA destination is fixed per lane,
+// so the permutation is applied to the source rows.  Rows at or past rows_valid re-read row
+// rows_valid - 1 (finite data that every product masks out).  Fragments are spread over the NW
+// waves.
+//
+// kswz spreads the 4 rows of a 32-key group that one ds_read_b64_tr_b16 of GEMM4 touches (two
+// 256-byte rows of two adjacent fragments) over disjoint bank quarters, which makes those
+// transpose reads conflict-free; a linear 16-lane row read stays a permutation of one row.
+__device__ __forceinline__ constexpr int kswz(int row, int frag) { return (row >> 1) + 2 * (frag & 1); }
+
+template <int D, int NW, bool SWZ = false>
+__device__ __forceinline__ void gather_frags(rsrc_t src, int row0, int rows_valid, int nfrag,
+                                             char* lds, int w, int lane) {
+  for (int f = w; f < nfrag; f += NW) {
     const int rt = f / (D / 16), t = f % (D / 16);
-    int row = row0 + 32 * rt + (lane & 31);
+    int n = lane;
+    if constexpr (SWZ) n = (lane & 48) | ((lane & 15) ^ (4 * kswz(lane >> 4, f)));
+    int row = row0 + 32 * rt + (n & 31);
     row = row < rows_valid ? row : rows_valid - 1;
-    g2lds16(gbase + (int64_t)row * D + 16 * t + 8 * (lane >> 5), lds + f * 1024);
+    dma16(src, (uint32_t)(row * D + 16 * t + 8 * (n >> 5)) * 2, lds + f * 1024);
   }
 }
 
-// Linear copy of `nfrag` consecutive 1 KiB fragments from global memory into LDS.
-__device__ __forceinline__ void copy_frags(const bf16_t* gsrc, int nfrag, char* lds, int w,
+// Byte offset of this lane's 16-byte chunk in a linear read of swizzled fragment f (f's parity
+// is all that matters).
+__device__ __forceinline__ int swz_chunk(int lane, int f) {
+  return (lane >> 4) * 256 + ((lane & 15) ^ (4 * kswz(lane >> 4, f))) * 16;
+}
+
+// dS of one 32-key MFMA tile (keys of one wave and key tile) is kept as 2 KiB of 8-byte quads:
+// quad (key, qg) holds dS[q = 4 qg .. 4 qg + 3][key] (bf16) at byte 256 qg + 8 ((key + 4 qg) & 31).
+// The rotation makes both the writer (32 keys of one qg per half-wave) and the GEMM4 transpose
+// reads (4 keys x 8 qg per half-wave) touch 32 distinct bank pairs.  Offset of the quad that lane
+// l stores for accumulator group x (q = 4 (l / 32) + 8 x + 0..3, key = l % 32):
+__device__ __forceinline__ int ds_store_off(int lane, int x) {
+  const int g = lane >> 5;
+  return 512 * x + 256 * g + (((lane & 31) + 4 * g + 8 * x) & 31) * 8;
+}
+
+// Per-lane offsets of the GEMM4 (dQ = dS K) transpose reads: dS as the A operand (rows q,
+// contraction over keys) and K as the B operand (contraction over keys, columns d).  MFMA step t
+// covers keys 16 t .. 16 t + 15 of the key tile; each operand is two ds_read_b64_tr_b16 of 4 keys.
+// Within a 16-lane block, addressing lane r = 4 jj + cc points at key 4-row jj, 4-column group cc.
+struct Gemm4Lanes {
+  int a[4];  // dS: key offsets 0, 4, 16, 20 within the 32-key tile
+  int b[2];  // K: key offsets 0 and 4 within the 16-key step
+  __device__ __forceinline__ explicit Gemm4Lanes(int lane) {
+    const int jj = (lane & 15) >> 2, cc = lane & 3, g = lane >> 5, hi = (lane >> 4) & 1;
+    const int qg = 4 * hi + cc;  // q = 4 qg .. +3 (output lanes 16 hi + 0..15 of the block)
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int key = 16 * (x >> 1) + 4 * (x & 1) + 8 * g + jj;
+      a[x] = 256 * qg + ((key + 4 * qg) & 31) * 8;
+    }
+    // K fragment 2 dt + hi, chunk n = 32 (cc >> 1) + 16 (t & 1) + 8 g + 4 sec + jj, 8-byte half cc & 1
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec)
+      b[sec] = hi * 1024 + (cc >> 1) * 512 +
+               ((8 * g + 4 * sec + jj) ^ (4 * kswz(2 * (cc >> 1), hi))) * 16 + 8 * (cc & 1);
+  }
+  __device__ __forceinline__ bf16x8 ds(const char* sST, int t) const {
+    const int base = (t >> 1) * 2048;
+    return concat(lds_read_tr(sST, base + a[2 * (t & 1)]), lds_read_tr(sST, base + a[2 * (t & 1) + 1]));
+  }
+  template <int DQK>
+  __device__ __forceinline__ bf16x8 k(const char* sK, int t, int dt) const {
+    const int base = ((t >> 1) * (DQK / 16) + 2 * dt) * 1024 + (t & 1) * 256;
+    return concat(lds_read_tr(sK, base + b[0]), lds_read_tr(sK, base + b[1]));
+  }
+};
+
+// Linear copy of `nfrag` consecutive 1 KiB fragments starting at byte `off` of `src` into LDS.
+template <int NW>
+__device__ __forceinline__ void copy_frags(rsrc_t src, uint32_t off, int nfrag, char* lds, int w,
                                            int lane) {
-  for (int f = w; f < nfrag; f += 4) g2lds16(gsrc + f * 512 + lane * 8, lds + f * 1024);
+  for (int f = w; f < nfrag; f += NW) dma16(src, off + f * 1024 + lane * 16, lds + f * 1024);
+}
+
+// Scheduling hint for a block of NMFMA MFMAs fed by NREAD LDS reads: issue AHEAD reads first, then
+// alternate one MFMA with the reads that keep the queue AHEAD deep, so LDS latency hides behind
+// the matrix core instead of stalling each MFMA on an lgkmcnt(0).
+template <int NREAD, int NMFMA, int AHEAD>
+__device__ __forceinline__ void schedule_reads_ahead() {
+  constexpr int first = NREAD < AHEAD ? NREAD : AHEAD;
+  constexpr int rest = NREAD - first;
+  constexpr int per = (rest + NMFMA - 1) / NMFMA;  // reads interleaved after each MFMA
+  __builtin_amdgcn_sched_group_barrier(0x100, first, 0);
+#pragma unroll
+  for (int m = 0; m < NMFMA; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (per > 0) __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
+  }
 }
 
 __device__ __forceinline__ bf16x8 frag(const char* base, int f, int lane) {
@@ -168,32 +261,21 @@ __device__ __forceinline__ void softmax_ds(const floatx16& S, const floatx16& dP
 // GEMM4 of the fp32-atomic route for one q tile: dQ (32 q x Dqk) = dS K over the tile's keys,
 // added into dq_accum with fp32 atomics.  dS sits in sST in register order (block (w,kt,x) of
 // 64 lanes x 4 q, see the writer) and K in sK as B fragments of GEMM1; both are read with the
-// transpose instruction.  Wave w handles the 32-column d tiles w, w + 4, ...
+// transpose instruction.  Wave w handles the 32-column d tiles w, w + NW, ... (with 8 waves only
+// waves 0-3 have a tile; each shares its SIMD with a wave that has none).
 template <class C>
 __device__ __forceinline__ void gemm4_atomic(const char* sST, const char* sK, float* dqb, int q0,
                                              int Lq, int w, int lane) {
   using M = typename C::M;
   using acc_t = typename M::acc_t;
   constexpr int DQK = C::DQK;
-  const int i = lane & 15, g = lane >> 5, lc = lane & 31;
-  const int jj = i >> 2, cc = i & 3;
-  const int q4 = ((lane & 16) >> 2) + cc;  // q / 4 of the 4 values this lane's address covers
-  // dS (A operand): key = 16 t + 8 g + jj (+4), q = 4 q4 .. +3
-  const int a_base = (q4 >> 1) * 512 + (8 * g + jj + 32 * (q4 & 1)) * 8;
-  // K (B operand): key as above, d = 32 dt + (lane & 16) + 4 cc .. +3
-  const int b_base = (2 * 0 + ((lane & 16) >> 4)) * 1024 + (8 * g + jj + 32 * (cc >> 1)) * 16 +
-                     8 * (cc & 1);
+  const int g = lane >> 5, lc = lane & 31;
+  const Gemm4Lanes tl(lane);
   const bool full = q0 + C::BR <= Lq;
   for (int dt = w; dt < C::N_DQT; dt += C::NW) {
     acc_t acc = acc_t{};
 #pragma unroll
-    for (int t = 0; t < C::BC / 16; ++t) {
-      const int ka = (t >> 1) * 2048 + (t & 1) * 128;                      // + 32 for keys +4
-      const int kb = ((t >> 1) * (DQK / 16) + 2 * dt) * 1024 + (t & 1) * 256;  // + 64 for keys +4
-      const bf16x8 a = concat(lds_read_tr(sST, a_base + ka), lds_read_tr(sST, a_base + ka + 32));
-      const bf16x8 bk = concat(lds_read_tr(sK, b_base + kb), lds_read_tr(sK, b_base + kb + 64));
-      acc = M::mma(a, bk, acc);
-    }
+    for (int t = 0; t < C::BC / 16; ++t) acc = M::mma(tl.ds(sST, t), tl.template k<DQK>(sK, t, dt), acc);
     float* dst = dqb + dt * 32 + lc;
     if (full) {
 #pragma unroll
@@ -254,6 +336,11 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
   const float* statb = p.stats + (int64_t)bh * p.sq_pad * 2;
   const bf16_t* qtb = p.qt + (int64_t)bh * n_q_tiles * (BR * DQK);
   const bf16_t* dotb = p.dot + (int64_t)bh * n_q_tiles * (BR * DV);
+  const rsrc_t rQ = buf_rsrc(Qb, (int64_t)p.Sq * DQK * 2);
+  const rsrc_t rdO = buf_rsrc(dOb, (int64_t)p.Sq * DV * 2);
+  const rsrc_t rQT = buf_rsrc(qtb, (int64_t)p.sq_pad * DQK * 2);
+  const rsrc_t rdOT = buf_rsrc(dotb, (int64_t)p.sq_pad * DV * 2);
+  const rsrc_t rStat = buf_rsrc(statb, (int64_t)p.sq_pad * 2 * 4);
 
   acc_t accK[C::N_DQT][NKT], accV[C::N_DVT][NKT];
 #pragma unroll
@@ -266,22 +353,25 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
     for (int kt = 0; kt < NKT; ++kt) accV[t][kt] = acc_t{};
 
   const int key_lane = k0 + w * KPW + lc;  // this lane's key in key tile 0 of the wave
+  const int kofs[2] = {swz_chunk(lane, 0), swz_chunk(lane, 1)};  // K fragment reads, by parity
 
   if (i_lo <= i_hi) {
     auto tile = [&](int i) -> char* { return smem + C::OFF_T + (C::NBUF == 2 ? (i & 1) : 0) * C::TILE_BYTES; };
     // ---- q tile i into its LDS buffer ----------------------------------------------------------
     auto load_tile = [&](int i) {
       char* t = tile(i);
-      gather_frags<DQK>(Qb, i * BR, p.Sq, C::N_KQ, t + C::T_QA, w, lane);
-      copy_frags(qtb + (int64_t)i * (BR * DQK), C::N_DQT * 2, t + C::T_QT, w, lane);
-      gather_frags<DV>(dOb, i * BR, p.Sq, C::N_KV, t + C::T_OA, w, lane);
-      copy_frags(dotb + (int64_t)i * (BR * DV), C::N_DVT * 2, t + C::T_OT, w, lane);
+      gather_frags<DQK, C::NW>(rQ, i * BR, p.Sq, C::N_KQ, t + C::T_QA, w, lane);
+      copy_frags<C::NW>(rQT, (uint32_t)i * (BR * DQK * 2), C::N_DQT * 2, t + C::T_QT, w, lane);
+      gather_frags<DV, C::NW>(rdO, i * BR, p.Sq, C::N_KV, t + C::T_OA, w, lane);
+      copy_frags<C::NW>(rdOT, (uint32_t)i * (BR * DV * 2), C::N_DVT * 2, t + C::T_OT, w, lane);
       if (w == 0)  // 64 floats: [lse2, delta] x 32 rows, already padded to sq_pad rows
-        g2lds4(statb + (int64_t)i * BR * 2 + lane, t + C::T_ST);
+        dma4(rStat, (uint32_t)(i * BR * 2 + lane) * 4, t + C::T_ST);
     };
     load_tile(i_hi);
     // ---- K fragments into LDS (B operand of GEMM1 and/or GEMM4) -------------------------------
-    if constexpr (C::KLDS) gather_frags<DQK>(Kb, k0, p.Skv, (BC / 32) * C::N_KQ, sK, w, lane);
+    if constexpr (C::KLDS)
+      gather_frags<DQK, C::NW, true>(buf_rsrc(Kb, (int64_t)p.Skv * DQK * 2), k0, p.Skv,
+                               (BC / 32) * C::N_KQ, sK, w, lane);
     // ---- V (and K) slices into registers -------------------------------------------------------
     bf16x8 vreg[NKT][C::N_KV];
     bf16x8 kreg[C::KREG ? NKT : 1][C::KREG ? C::N_KQ : 1];
@@ -323,17 +413,21 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) {
         acc_t S = acc_t{}, dP = acc_t{};
+        // GEMM1 and GEMM2 are independent chains: alternate them so neither waits on the other's
+        // accumulator, and keep the operand reads a few MFMAs ahead of their use
 #pragma unroll
-        for (int t = 0; t < C::N_KQ; ++t) {
-          const bf16x8 a = frag(T + C::T_QA, t, lane);
-          if constexpr (C::KREG) {
-            S = M::mma(a, kreg[kt][t], S);
-          } else {
-            S = M::mma(a, frag(sK, (w * NKT + kt) * C::N_KQ + t, lane), S);
+        for (int t = 0; t < (C::N_KQ > C::N_KV ? C::N_KQ : C::N_KV); ++t) {
+          if (t < C::N_KQ) {
+            const bf16x8 a = frag(T + C::T_QA, t, lane);
+            if constexpr (C::KREG) {
+              S = M::mma(a, kreg[kt][t], S);
+            } else {
+              S = M::mma(a, lds_read_b128(sK, ((w * NKT + kt) * C::N_KQ + t) * 1024 + kofs[t & 1]), S);
+            }
           }
+          if (t < C::N_KV) dP = M::mma(frag(T + C::T_OA, t, lane), vreg[kt][t], dP);
         }
-#pragma unroll
-        for (int t = 0; t < C::N_KV; ++t) dP = M::mma(frag(T + C::T_OA, t, lane), vreg[kt][t], dP);
+        schedule_reads_ahead<(C::KREG ? 1 : 2) * C::N_KQ + C::N_KV, C::N_KQ + C::N_KV, 6>();
         if (edge)
           softmax_ds<true>(S, dP, sStat, g, p.scale_log2, mg, q0 + g * 4, key_lane + kt * 32,
                            pb[kt], sb[kt]);
@@ -341,19 +435,18 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
           softmax_ds<false>(S, dP, sStat, g, p.scale_log2, mg, q0 + g * 4, key_lane + kt * 32,
                             pb[kt], sb[kt]);
 
-        // dS in register order: block (w, kt, x) of 64 lanes x 8 bytes holds, for lane l,
-        // dS^T[key = w*KPW + kt*32 + l%32][q = 4*(l/32) + 8*x + 0..3]
+        // dS of this 32-key tile as 2 KiB of quads (see ds_store_off)
         if constexpr (C::DET) {
-          bf16_t* wsb =
-              p.ds_ws + (((int64_t)bh * p.n_kv_tiles + j) * n_q_tiles + i) * (BC * BR);
+          char* wsb = reinterpret_cast<char*>(
+              p.ds_ws + (((int64_t)bh * p.n_kv_tiles + j) * n_q_tiles + i) * (BC * BR));
 #pragma unroll
           for (int x = 0; x < 4; ++x)
-            *reinterpret_cast<u32x2*>(wsb + (((w * NKT + kt) * 4 + x) * 64 + lane) * 4) =
+            *reinterpret_cast<u32x2*>(wsb + (w * NKT + kt) * 2048 + ds_store_off(lane, x)) =
                 u32x2{sb[kt][2 * x], sb[kt][2 * x + 1]};
         } else {
 #pragma unroll
           for (int x = 0; x < 4; ++x)
-            *reinterpret_cast<u32x2*>(sST + (((w * NKT + kt) * 4 + x) * 64 + lane) * 8) =
+            *reinterpret_cast<u32x2*>(sST + (w * NKT + kt) * 2048 + ds_store_off(lane, x)) =
                 u32x2{sb[kt][2 * x], sb[kt][2 * x + 1]};
         }
       }
@@ -382,6 +475,7 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
           }
         }
       }
+      schedule_reads_ahead<2 * (C::N_DVT + C::N_DQT), 2 * NKT * (C::N_DVT + C::N_DQT), 4>();
       if constexpr (C::NBUF == 1) {
         __syncthreads();  // every wave is done with the single q-tile buffer
         if (i > i_lo) load_tile(i - 1);

@@ -7,8 +7,9 @@
 // The workspace holds each stored (KV tile, q tile) block in the main kernel's register order
 // (see bwd_main.h); any 64 consecutive keys of a block are one contiguous 4 KiB piece.  Chunks of
 // 64 keys of dS and of K (gathered as the main kernel's K fragments) are copied straight into LDS
-// (global_load_lds, double-buffered) and read as MFMA operands with the transpose instruction.
-// Waves split the head dim in 32-column tiles.
+// (LDS-DMA buffer loads, double-buffered) and read as MFMA operands with the transpose instruction.
+// Waves split the head dim in 32-column tiles.  The dS quads and the swizzled K fragments make the
+// transpose reads bank-conflict-free (layouts in bwd_main.h).
 #pragma once
 #include "bwd_main.h"
 
@@ -85,20 +86,18 @@ __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
 
   const bf16_t* wsh = p.ds_ws + (int64_t)bh * p.n_kv_tiles * p.n_q_tiles * (BC * BR);
   const bf16_t* Kb = p.k + (int64_t)(b * p.Hkv + kvh) * p.Skv * DQK;
+  const rsrc_t rK = buf_rsrc(Kb, (int64_t)p.Skv * DQK * 2);
 
   auto load_chunk = [&](int c, int buf) {
     char* base = smem + buf * C::BUF_BYTES;
     const int j = c / CPT, part = c % CPT;
     const bf16_t* blk = wsh + ((int64_t)j * p.n_q_tiles + i) * (BC * BR) + part * KC * BR;
-    copy_frags(blk, C::ST_BYTES / 1024, base, w, lane);
-    gather_frags<DQK>(Kb, c * KC, p.Skv, (KC / 32) * (DQK / 16), base + C::ST_BYTES, w, lane);
+    copy_frags<C::NW>(buf_rsrc(blk, C::ST_BYTES), 0, C::ST_BYTES / 1024, base, w, lane);
+    gather_frags<DQK, C::NW, true>(rK, c * KC, p.Skv, (KC / 32) * (DQK / 16), base + C::ST_BYTES,
+                                   w, lane);
   };
 
-  // per-lane parts of the transpose-read addresses (see gemm4_atomic in bwd_main.h)
-  const int i16 = lane & 15, jj = i16 >> 2, cc = i16 & 3;
-  const int q4 = ((lane & 16) >> 2) + cc;
-  const int a_base = (q4 >> 1) * 512 + (8 * g + jj + 32 * (q4 & 1)) * 8;
-  const int b_base = ((lane & 16) >> 4) * 1024 + (8 * g + jj + 32 * (cc >> 1)) * 16 + 8 * (cc & 1);
+  const Gemm4Lanes tl(lane);
 
   acc_t acc[C::PER_W];
 #pragma unroll
@@ -114,14 +113,12 @@ __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
     const char* sK = sST + C::ST_BYTES;
 #pragma unroll
     for (int t = 0; t < KC / 16; ++t) {
-      const int ka = (t >> 1) * 2048 + (t & 1) * 128;
-      const bf16x8 a = concat(lds_read_tr(sST, a_base + ka), lds_read_tr(sST, a_base + ka + 32));
+      const bf16x8 a = tl.ds(sST, t);
 #pragma unroll
       for (int x = 0; x < C::PER_W; ++x) {
         const int dt = w + x * C::NW;
         if (dt < C::N_DT) {
-          const int kb = ((t >> 1) * (DQK / 16) + 2 * dt) * 1024 + (t & 1) * 256;
-          const bf16x8 bk = concat(lds_read_tr(sK, b_base + kb), lds_read_tr(sK, b_base + kb + 64));
+          const bf16x8 bk = tl.template k<DQK>(sK, t, dt);
           acc[x] = M::mma(a, bk, acc[x]);
         }
       }

@@ -22,18 +22,19 @@ namespace {
 constexpr int64_t kAlign = 256;
 inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-// Tile geometry per supported (Dqk, Dv): keys per wave KPW (the key tile is BC = 4 * KPW) and the
-// q tile BR = 32.  64 keys per wave where the dK^T/dV^T accumulators (KPW * (Dqk + Dv) floats per
-// wave) fit the 256 accumulation registers of a lane, 32 above that.
+// Tile geometry per supported (Dqk, Dv): waves per workgroup NW, keys per wave KPW = 32, key
+// tile BC = NW * KPW, q tile BR = 32.  Head dims <= 128 run 8 waves (two per SIMD, 256 registers
+// each, 256-key tiles); larger head dims run 4 waves with 512 registers for the bigger dK/dV
+// accumulators (128-key tiles).
 struct Geometry {
-  int kpw, bc, br;
+  int nw, kpw, bc, br;
 };
 
 bool geometry_for(int Dqk, int Dv, Geometry* g) {
-  if (Dqk == 64 && Dv == 64) *g = {64, 256, 32};
-  else if (Dqk == 128 && Dv == 128) *g = {64, 256, 32};
-  else if (Dqk == 192 && Dv == 128) *g = {32, 128, 32};
-  else if (Dqk == 256 && Dv == 256) *g = {32, 128, 32};
+  if (Dqk == 64 && Dv == 64) *g = {8, 32, 256, 32};
+  else if (Dqk == 128 && Dv == 128) *g = {8, 32, 256, 32};
+  else if (Dqk == 192 && Dv == 128) *g = {4, 32, 128, 32};
+  else if (Dqk == 256 && Dv == 256) *g = {4, 32, 128, 32};
   else return false;
   return true;
 }
@@ -113,24 +114,33 @@ hipError_t launch_dq2k(const Dq2kParams& dp, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DQK, int DV, int KPW>
-hipError_t dispatch_main(const MainParams& mp, int det, int grid, hipStream_t s) {
-  if (det) return launch_main<MainCfg<DQK, DV, KPW, true>>(mp, grid, s);
-  return launch_main<MainCfg<DQK, DV, KPW, false>>(mp, grid, s);
+template <int DQK, int DV, int KPW, int NW>
+hipError_t dispatch_main(const MainParams& mp, int det, int grid, int bc, hipStream_t s) {
+  // the workspace carve and the grid use the geometry table; the kernel must tile the same way
+  if (MainCfg<DQK, DV, KPW, NW, true>::BC != bc) return hipErrorInvalidValue;
+  if (det) return launch_main<MainCfg<DQK, DV, KPW, NW, true>>(mp, grid, s);
+  return launch_main<MainCfg<DQK, DV, KPW, NW, false>>(mp, grid, s);
 }
 
-hipError_t run_main(int Dqk, int Dv, const MainParams& mp, int det, int grid, hipStream_t s) {
-  if (Dqk == 64) return dispatch_main<64, 64, 64>(mp, det, grid, s);
-  if (Dqk == 128) return dispatch_main<128, 128, 64>(mp, det, grid, s);
-  if (Dqk == 192) return dispatch_main<192, 128, 32>(mp, det, grid, s);
-  return dispatch_main<256, 256, 32>(mp, det, grid, s);
+hipError_t run_main(int Dqk, int Dv, const MainParams& mp, int det, int grid, int bc,
+                    hipStream_t s) {
+  if (Dqk == 64) return dispatch_main<64, 64, 32, 8>(mp, det, grid, bc, s);
+  if (Dqk == 128) return dispatch_main<128, 128, 32, 8>(mp, det, grid, bc, s);
+  if (Dqk == 192) return dispatch_main<192, 128, 32, 4>(mp, det, grid, bc, s);
+  return dispatch_main<256, 256, 32, 4>(mp, det, grid, bc, s);
 }
 
-hipError_t run_dq2k(int Dqk, const Dq2kParams& dp, int grid, hipStream_t s) {
-  if (Dqk == 64) return launch_dq2k<Dq2kCfg<64, 256>>(dp, grid, s);
-  if (Dqk == 128) return launch_dq2k<Dq2kCfg<128, 256>>(dp, grid, s);
-  if (Dqk == 192) return launch_dq2k<Dq2kCfg<192, 128>>(dp, grid, s);
-  return launch_dq2k<Dq2kCfg<256, 128>>(dp, grid, s);
+template <int DQK, int BC>
+hipError_t dispatch_dq2k(const Dq2kParams& dp, int grid, int bc, hipStream_t s) {
+  if (BC != bc) return hipErrorInvalidValue;  // must read the dS blocks the main kernel wrote
+  return launch_dq2k<Dq2kCfg<DQK, BC>>(dp, grid, s);
+}
+
+hipError_t run_dq2k(int Dqk, const Dq2kParams& dp, int grid, int bc, hipStream_t s) {
+  if (Dqk == 64) return dispatch_dq2k<64, 256>(dp, grid, bc, s);
+  if (Dqk == 128) return dispatch_dq2k<128, 256>(dp, grid, bc, s);
+  if (Dqk == 192) return dispatch_dq2k<192, 128>(dp, grid, bc, s);
+  return dispatch_dq2k<256, 128>(dp, grid, bc, s);
 }
 
 hipError_t launch_preprocess(const PreParams& pp, int Dqk, int Dv, int64_t tiles, hipStream_t s) {
@@ -255,7 +265,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   mp.scale_log2 = scale * kLog2e;
   const int64_t main_grid = (int64_t)mp.n_kv_tiles * B * Hq;
   if (main_grid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
-  e = run_main(Dqk, Dv, mp, det, (int)main_grid, stream);
+  e = run_main(Dqk, Dv, mp, det, (int)main_grid, geo.bc, stream);
   if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   rec(2);
 
@@ -303,7 +313,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     dp.scale = scale;
     const int64_t grid = (int64_t)dp.n_q_tiles * B * Hq;
     if (grid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
-    e = run_dq2k(Dqk, dp, (int)grid, stream);
+    e = run_dq2k(Dqk, dp, (int)grid, geo.bc, stream);
     if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   }
   rec(4);
