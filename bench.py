@@ -91,6 +91,68 @@ def gpu_forward_inputs(torch, q, k, v, w, lens):
     return o, lse
 
 
+COPY_PROBE_BYTES = 1 << 30  # read and written once per launch; 4x the 256 MB Infinity Cache
+
+
+def copy_probe(torch, dev):
+    """A plain fp32 copy (dst = -src, an elementwise kernel no other step of this script launches)
+    of COPY_PROBE_BYTES, launched three times: the kernel whose FETCH_SIZE / WRITE_SIZE readings
+    calibrate the counters to bytes."""
+    n = COPY_PROBE_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def _pmc_means(directory, counter):
+    """Mean per-dispatch value of `counter` for each kernel name in a rocprofv3 --pmc CSV."""
+    import csv
+    import glob
+    per = {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"),
+                          recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return {name: (sum(v) / len(v), len(v)) for name, v in out.items()}
+
+
+def write_traffic_record(workload, det_arg, fetch_dir, write_dir):
+    w = synth.WORKLOADS[workload]
+    det = w.deterministic if det_arg < 0 else bool(det_arg)
+    rec = {"kernel_source_hash": kernel_source_hash(), "workload": w.name, "deterministic": det,
+           "copy_probe_bytes": COPY_PROBE_BYTES}
+    total = 0.0
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        means = _pmc_means(d, counter)
+        main = [(n, v) for n, v in means.items() if "bwd_main_kernel" in n]
+        copy = [(n, v) for n, v in means.items() if "neg_kernel" in n]
+        if len(main) != 1 or len(copy) != 1:
+            raise SystemExit(f"{d}: expected one main kernel and one copy-probe kernel for "
+                             f"{counter}, found {len(main)} and {len(copy)}")
+        main_kib, n_main = main[0][1]
+        copy_kib, n_copy = copy[0][1]
+        factor = (COPY_PROBE_BYTES / 1024.0) / copy_kib  # true KiB per counted KiB
+        bytes_ = main_kib * factor * 1024.0
+        rec[counter] = {"main_kib_per_dispatch": main_kib, "main_dispatches": n_main,
+                        "copy_kib_per_dispatch": copy_kib, "copy_dispatches": n_copy,
+                        "scale_factor": factor, "main_bytes_per_launch": bytes_,
+                        "kernel": main[0][0]}
+        total += bytes_
+    rec["hbm_bytes_per_launch"] = total
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def cpu_baseline(w, inp, lens, budget_s=15.0):
     """The fp64 CPU oracle (unchanged) on the first query heads of batch entry 0, timed until
     about budget_s seconds of work; the rate is scaled to the same FLOP convention."""
@@ -131,13 +193,22 @@ def cpu_baseline(w, inp, lens, budget_s=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa_causal_s4096_d128", choices=list(synth.WORKLOADS))
     ap.add_argument("--deterministic", type=int, default=-1,
                     help="override the workload's dQ route (-1: as the workload states)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed steps, run a plain 1 GiB fp32 copy kernel three times "
+                         "(the calibration kernel of the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: read two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) "
+                         "of a --copy-probe run and write the main kernel's HBM traffic record")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic_record(args.workload, args.deterministic, *args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the "
               f"attention backward shards over (batch, KV-head group) with no communication, "
@@ -231,6 +302,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
+    if args.copy_probe:
+        copy_probe(torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, lens)
     print(json.dumps(out), flush=True)
