@@ -20,6 +20,9 @@ FLAGS = [
     # keep the compiler from forming packed-fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
+    # the LDS-DMA loads are inline assembly that sets M0; clang warns that M0 is a reserved
+    # register (tests/test_isa.py checks that nothing else in the kernels uses it)
+    "-Wno-inline-asm",
 ]
 
 
@@ -35,6 +38,17 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
     os.replace(tmp, OUT)
     return OUT
+
+
+def device_assembly() -> str:
+    """The gfx950 assembly of the library's kernels (device pass only), for inspection."""
+    cmd = [HIPCC, *[f for f in FLAGS if f not in ("-shared", "-fPIC")], "--offload-device-only",
+           "-S", SRC, "-o", "-"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    return res.stdout
 
 
 if __name__ == "__main__":

@@ -102,24 +102,38 @@ struct MainCfg {
 
 // The q-tile, K and dS operands go straight from global memory into LDS with the buffer form of
 // the LDS-DMA load (buffer_load ... lds): each lane supplies a byte offset into a raw buffer
-// resource, the data lands at the wave-uniform LDS base (M0) + 16 (or 4) bytes * lane.  The buffer
-// form (rather than global_load_lds) keeps the compiler's LDS wait counting exact, so the operand
-// reads of the compute stay pipelined while the next tile streams in.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// resource, the data lands at the wave-uniform LDS base (M0) + 16 (or 4) bytes * lane.  The loads
+// are issued from inline assembly, so the compiler neither sees them as pending LDS writes (which
+// would make it wait for every one of them before any LDS read or workgroup barrier) nor counts
+// them: every consumer waits for them explicitly with vmcnt before a barrier.  M0 is written only
+// here (no other instruction in these kernels reads it).
+typedef u32x4 rsrc_t;
 
-// Raw buffer over `bytes` bytes at `base`; reads past the end return zero.  The host keeps every
-// buffer below 2^31 bytes.
+// Raw buffer descriptor over `bytes` bytes at `base` (stride 0, 32-bit data format); reads past
+// the end return zero.  The host keeps every buffer below 2^31 bytes.
 __device__ __forceinline__ rsrc_t buf_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return rsrc_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, (uint32_t)bytes, 0x00020000u};
 }
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma4(rsrc_t r, uint32_t off, void* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, (__attribute__((address_space(3))) void*)lds_wave_base, 4, off, 0, 0, 0);
+  const uint32_t l = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(r), "s"(l)
+               : "memory", "m0");
 }
 __device__ __forceinline__ void dma16(rsrc_t r, uint32_t off, void* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, off, 0, 0, 0);
+  const uint32_t l = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(r), "s"(l)
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
+
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -393,15 +407,15 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
       const int q0 = i * BR;
       const char* T = tile(i);
       const float* sStat = reinterpret_cast<const float*>(T + C::T_ST);
-      wait_vmem();
-      __syncthreads();  // tile i landed everywhere; every wave is done with the previous tile
+      wait_vmem();      // this wave's loads of tile i (and its older atomics / stores) are done
+      lds_barrier();    // tile i landed everywhere; every wave is done with the previous tile
       if (C::NBUF == 2 && i > i_lo) load_tile(i - 1);
 
       if constexpr (!C::DET) {
         // GEMM4 of the previous q tile (dS in sST), deferred so its atomics overlap this tile
         if (i < i_hi) {
           gemm4_atomic<C>(sST, sK, p.dq_accum + (q_row0 + q0 + BR) * DQK, q0 + BR, mg.Lq, w, lane);
-          __syncthreads();  // every wave is done reading sST
+          lds_barrier();  // every wave is done reading sST (the atomics keep draining)
         }
       }
 
@@ -477,12 +491,12 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
       }
       schedule_reads_ahead<2 * (C::N_DVT + C::N_DQT), 2 * NKT * (C::N_DVT + C::N_DQT), 4>();
       if constexpr (C::NBUF == 1) {
-        __syncthreads();  // every wave is done with the single q-tile buffer
+        lds_barrier();  // every wave is done with the single q-tile buffer
         if (i > i_lo) load_tile(i - 1);
       }
     }
     if constexpr (!C::DET) {
-      __syncthreads();  // the last tile's dS is complete
+      lds_barrier();  // the last tile's dS is complete
       gemm4_atomic<C>(sST, sK, p.dq_accum + (q_row0 + i_lo * BR) * DQK, i_lo * BR, mg.Lq, w, lane);
     }
   }

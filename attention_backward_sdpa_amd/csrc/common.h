@@ -89,6 +89,16 @@ struct PadTile {
   static constexpr int bytes(int rows) { return rows * STRIDE; }
 };
 
+// Workgroup barrier that orders LDS only: this wave's LDS accesses complete first (lgkmcnt(0)),
+// while its global loads, stores and atomics keep draining (unlike __syncthreads, whose fence also
+// waits for every outstanding global access).  Data brought in by LDS-DMA loads must be waited for
+// explicitly (vmcnt) before it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ bf16x8 lds_read_b128(const char* base, int off) {
   return *reinterpret_cast<const bf16x8*>(base + off);
 }

@@ -81,6 +81,9 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
   if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return SDPA_BWD_INVALID_ARG;
   if (window_left < -1 || window_right < 0) return SDPA_BWD_INVALID_ARG;
   if (!geometry_for(Dqk, Dv, geo)) return SDPA_BWD_UNSUPPORTED;
+  // the kernels address one head's rows (and its padded tiles) through 32-bit buffer offsets
+  const int64_t s_max = (Sq > Skv ? Sq : Skv) + geo->bc;
+  if (s_max * (Dqk > Dv ? Dqk : Dv) * 2 >= ((int64_t)1 << 31)) return SDPA_BWD_UNSUPPORTED;
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return SDPA_BWD_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
       ((uintptr_t)lse & 3) != 0 || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
@@ -131,16 +134,20 @@ hipError_t run_main(int Dqk, int Dv, const MainParams& mp, int det, int grid, in
 }
 
 template <int DQK, int BC>
-hipError_t dispatch_dq2k(const Dq2kParams& dp, int grid, int bc, hipStream_t s) {
+hipError_t dispatch_dq2k(const Dq2kParams& dp, int bc, hipStream_t s) {
+  using C = Dq2kCfg<DQK, BC>;
   if (BC != bc) return hipErrorInvalidValue;  // must read the dS blocks the main kernel wrote
-  return launch_dq2k<Dq2kCfg<DQK, BC>>(dp, grid, s);
+  // one workgroup per group of C::QT consecutive q tiles of one (batch, query head)
+  const int64_t grid = (int64_t)((dp.n_q_tiles + C::QT - 1) / C::QT) * dp.B * dp.Hq;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  return launch_dq2k<C>(dp, (int)grid, s);
 }
 
-hipError_t run_dq2k(int Dqk, const Dq2kParams& dp, int grid, int bc, hipStream_t s) {
-  if (Dqk == 64) return dispatch_dq2k<64, 256>(dp, grid, bc, s);
-  if (Dqk == 128) return dispatch_dq2k<128, 256>(dp, grid, bc, s);
-  if (Dqk == 192) return dispatch_dq2k<192, 128>(dp, grid, bc, s);
-  return dispatch_dq2k<256, 128>(dp, grid, bc, s);
+hipError_t run_dq2k(int Dqk, const Dq2kParams& dp, int bc, hipStream_t s) {
+  if (Dqk == 64) return dispatch_dq2k<64, 256>(dp, bc, s);
+  if (Dqk == 128) return dispatch_dq2k<128, 256>(dp, bc, s);
+  if (Dqk == 192) return dispatch_dq2k<192, 128>(dp, bc, s);
+  return dispatch_dq2k<256, 128>(dp, bc, s);
 }
 
 hipError_t launch_preprocess(const PreParams& pp, int Dqk, int Dv, int64_t tiles, hipStream_t s) {
@@ -311,9 +318,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     dp.n_kv_tiles = mp.n_kv_tiles;
     dp.n_q_tiles = (int)(c.sq_pad / geo.br);
     dp.scale = scale;
-    const int64_t grid = (int64_t)dp.n_q_tiles * B * Hq;
-    if (grid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
-    e = run_dq2k(Dqk, dp, (int)grid, geo.bc, stream);
+    e = run_dq2k(Dqk, dp, geo.bc, stream);
     if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   }
   rec(4);
