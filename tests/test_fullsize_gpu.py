@@ -1,0 +1,153 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py times.
+
+The whole chain runs on the GPU at full size; the fp64 oracle then recomputes sampled rows one by
+one (dQ rows and dK/dV key rows, including tile edges and padding boundaries) from exactly the
+inputs the GPU received, and the benchmark spec's tolerance max|err| <= 1e-2 * max|ref| is applied per
+tensor over the samples.  Properties that hold at any size are checked on the full outputs: the
+column sums of dV equal the summed dO of the rows that see a key (sum_j P_ij = 1), the column
+sums of dK vanish (sum_j dS_ij = 0), padded rows are exactly zero, and the deterministic route is
+bitwise identical over 10 runs.
+
+O and LSE are inputs: at full size they come from a float32 forward computed with torch on the
+GPU (the same preparation bench.py uses; the oracle forward would take minutes per workload).
+Both the GPU path and the oracle backward consume exactly these tensors.
+"""
+import hashlib
+
+import numpy as np
+import pytest
+
+import oracle
+from attention_backward_sdpa_amd import synth
+
+from tests import _common as C
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu]
+
+W = synth.WORKLOADS
+
+CASES = [
+    ("mha_causal_s2048_d128", None),
+    ("gqa_causal_s4096_d128", False),
+    ("gqa_causal_s4096_d128", True),
+    ("mha_det_s8192_d256", None),
+    ("mla_window_padded_s4096", None),
+]
+
+
+def _prepare(w):
+    import bench
+    C.log(f"full-size case {w.name}: drawing inputs")
+    inp = synth.draw_inputs(w)
+    dev = torch.device("cuda:0")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    t = dict(q=bf(inp.q), k=bf(inp.k), v=bf(inp.v), do=bf(inp.do))
+    lens = inp.seq_q_lens
+    C.log(f"full-size case {w.name}: float32 forward for O and LSE")
+    t["o"], t["lse"] = bench.gpu_forward_inputs(torch, t["q"], t["k"], t["v"], w, lens)
+    t["lens"] = None if lens is None else torch.from_numpy(lens).to(dev)
+    torch.cuda.synchronize()
+    host = dict(q=inp.q, k=inp.k, v=inp.v, do=inp.do,
+                o=t["o"].cpu().view(torch.int16).numpy().view(np.uint16),
+                lse=t["lse"].cpu().numpy(), lens=lens)
+    return t, host
+
+
+_PREP = {}
+
+
+def prepared(name):
+    if name not in _PREP:
+        _PREP.clear()
+        _PREP[name] = _prepare(W[name])
+    return _PREP[name]
+
+
+def _run(w, t, det):
+    case = dict(w=w, lens=t["lens"])
+    C.log(f"full-size case {w.name}: GPU chain (deterministic={det})")
+    return C.run_gpu(case, torch, deterministic=det, dev_inputs=t)
+
+
+def _edge_rows(S, L=None):
+    rows = {0, 1, 31, 32, 33, 127, 128, 255, 256, 257, S // 2, S - 33, S - 32, S - 1}
+    if L is not None:
+        rows |= {L - 33, L - 1, L, L + 1}
+    return sorted(r for r in rows if 0 <= r < S)
+
+
+def _f64(bits):
+    return synth.bf16_to_f32(bits).astype(np.float64)
+
+
+@pytest.mark.parametrize("name,det", CASES, ids=[f"{n}-{'det' if d else 'atomic' if d is not None else 'default'}" for n, d in CASES])
+def test_fullsize_sampled_rows(name, det):
+    w = W[name]
+    det = w.deterministic if det is None else det
+    t, host = prepared(name)
+    dq, dk, dv = _run(w, t, det)
+    lens = host["lens"]
+    lens_l = None if lens is None else [int(x) for x in lens]
+    kw = dict(causal=w.causal, window_left=w.window_left, seq_q_lens=lens_l, seq_kv_lens=lens_l)
+    q, k, v, o, do = (_f64(host[x]) for x in ("q", "k", "v", "o", "do"))
+    lse = host["lse"].astype(np.float64)
+    rng = np.random.default_rng(1234)
+    # dQ rows
+    got_q, ref_q = [], []
+    heads = sorted({(0, 0), (w.B - 1, w.Hq - 1), (int(rng.integers(w.B)), int(rng.integers(w.Hq)))})
+    for b, h in heads:
+        L = None if lens is None else int(lens[b])
+        rows = _edge_rows(w.Sq, L) + sorted(rng.choice(w.Sq, 4, replace=False).tolist())
+        ref_q.append(oracle.backward_dq_rows(q, k, v, o, do, lse, w.softmax_scale, b, h, rows, **kw))
+        got_q.append(dq[b, h, rows])
+    # dK / dV key rows (summed over the query heads of the group)
+    got_k, ref_k, got_v, ref_v = [], [], [], []
+    kvheads = sorted({(0, 0), (w.B - 1, w.Hkv - 1)})
+    for b, kh in kvheads:
+        L = None if lens is None else int(lens[b])
+        rows = _edge_rows(w.Skv, L) + sorted(rng.choice(w.Skv, 4, replace=False).tolist())
+        rk, rv = oracle.backward_dkdv_rows(q, k, v, o, do, lse, w.softmax_scale, b, kh, rows, **kw)
+        ref_k.append(rk)
+        ref_v.append(rv)
+        got_k.append(dk[b, kh, rows])
+        got_v.append(dv[b, kh, rows])
+    tag = f"{name} ({'deterministic' if det else 'fp32 atomic'})"
+    C.assert_close(f"{tag} dQ sampled rows", np.concatenate(got_q), np.concatenate(ref_q))
+    C.assert_close(f"{tag} dK sampled rows", np.concatenate(got_k), np.concatenate(ref_k))
+    C.assert_close(f"{tag} dV sampled rows", np.concatenate(got_v), np.concatenate(ref_v))
+
+    # properties over the full outputs
+    group = w.Hq // w.Hkv
+    for b in range(w.B):
+        L = w.Sq if lens is None else int(lens[b])
+        vis = oracle.visible_mask(w.Sq, w.Skv, w.causal, w.window_left, L, L)
+        has_key = vis.any(axis=1)
+        for kh in range(w.Hkv):
+            hs = slice(kh * group, (kh + 1) * group)
+            lhs = dv[b, kh].astype(np.float64).sum(axis=0)
+            rhs = do[b, hs][:, has_key].sum(axis=(0, 1))
+            scale = max(float(np.abs(rhs).max()), float(np.abs(dv[b, kh]).max()))
+            assert np.abs(lhs - rhs).max() <= 1e-2 * scale, f"{tag}: sum_j dV != sum_i dO (b={b})"
+            colsum = np.abs(dk[b, kh].astype(np.float64).sum(axis=0)).max()
+            assert colsum <= 1e-2 * np.abs(dk[b, kh]).astype(np.float64).sum(axis=0).max(), \
+                f"{tag}: sum_j dK != 0 (b={b})"
+        if lens is not None:
+            assert np.all(dq[b, :, L:] == 0), f"{tag}: dQ rows past seq_q must be zero"
+            assert np.all(dk[b, :, L:] == 0) and np.all(dv[b, :, L:] == 0)
+
+
+def test_fullsize_deterministic_bitwise():
+    # the S=8192, D=256 deterministic workload: 10 runs, identical bits
+    name = "mha_det_s8192_d256"
+    w = W[name]
+    t, _ = prepared(name)
+    digests = set()
+    for run in range(10):
+        out = _run(w, t, True)
+        h = hashlib.sha256()
+        for x in out:
+            h.update(np.ascontiguousarray(x).view(np.uint32).tobytes())
+        digests.add(h.hexdigest())
+    assert len(digests) == 1, f"{len(digests)} distinct results over 10 runs"
