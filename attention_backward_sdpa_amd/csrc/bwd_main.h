@@ -18,19 +18,19 @@
 //     dim <= 128 there are 8 waves, two per SIMD, each within 256 registers: the hardware then
 //     overlaps one wave's softmax VALU work and LDS latency with the other wave's MFMAs, and the
 //     256-key tile halves the dQ atomics and the Q/dO re-reads per key.  Above that, 4 waves with
-//     512 registers each hold the larger dK/dV accumulators.  S and dP are computed with q as the MFMA row index and
-//     keys as the column index (v_mfma_f32_32x32x16_bf16), so each wave's P and dS accumulators
-//     are already the B operand of GEMM3/GEMM5 (contraction over q) and its dK^T/dV^T partials
-//     complete inside the wave.
-//   * LDS holds every shared operand as ready-made MFMA fragments (1 KiB each, lane-major), so
-//     every operand read is one linear, bank-conflict-free ds_read_b128 at a per-lane base plus an
-//     immediate offset: LDS issue rate, not bytes, bounds this kernel on gfx950, and a 16-byte
-//     read costs the same issue slot as the half-as-wide transpose read.
-//       - Q and dO tiles (32 q rows) as A fragments of GEMM1/GEMM2, gathered straight from Q/dO
-//         with 16-byte LDS-DMA buffer loads;
-//       - Q^T and dO^T as A fragments of GEMM5/GEMM3, written once per q tile by the preprocess
-//         kernel and copied linearly;
-//       - the key tile K as B fragments of GEMM1 (registers instead at head dim >= 192).
+//     512 registers each hold the larger dK/dV accumulators.
+//   * S and dP are computed with q as the MFMA row index and keys as the column index
+//     (v_mfma_f32_32x32x16_bf16), so each wave's P and dS accumulators are already the B operand of
+//     GEMM3/GEMM5 (contraction over q) and its dK^T/dV^T partials complete inside the wave.
+//   * LDS holds every shared operand as ready-made MFMA fragments (1 KiB each, lane-major, the 16-byte
+//     chunks of each 256-byte row XOR-swizzled), so every GEMM1/GEMM2 operand read is one
+//     bank-conflict-free ds_read_b128 at a per-lane base plus an immediate offset, and the same
+//     fragments read transposed (ds_read_b64_tr_b16, also conflict-free) give the contraction-over-q
+//     operands of GEMM3/GEMM5 and the contraction-over-keys operand K of GEMM4:
+//       - Q and dO tiles (32 q rows), gathered straight from Q / dO with 16-byte LDS-DMA loads;
+//         read as A operands of GEMM1 / GEMM2 and, transposed, as Q^T / dO^T for GEMM5 / GEMM3;
+//       - the key tile K as B operands of GEMM1 (registers instead at head dim >= 192) and,
+//         transposed, of GEMM4.
 //     The q-tile buffers are double-buffered and filled one tile ahead of the compute.
 //   * The wave's V slice is held in registers as the B operand of GEMM2.
 //   * Deterministic route: each lane stores its bf16 dS values straight from registers (512
@@ -52,8 +52,6 @@ struct MainParams {
   const bf16_t* v;
   const bf16_t* dO;
   const float* stats;       // (B*Hq, sq_pad, 2): [LSE*log2e or +inf, delta] per q row
-  const bf16_t* qt;         // (B*Hq, sq_pad/32) tiles of Q^T fragments
-  const bf16_t* dot;        // (B*Hq, sq_pad/32) tiles of dO^T fragments
   float* dq_accum;          // (B, Hq, Sq, Dqk) fp32, non-deterministic route
   bf16_t* ds_ws;            // (B*Hq, n_kv_tiles, sq_pad/32) blocks of BC x 32 bf16 dS
   bf16_t* dk_out;           // (B, out_heads, Skv, Dqk)
@@ -80,12 +78,10 @@ struct MainCfg {
   using M = Mfma<32>;
   static constexpr int N_DQT = DQK / MT, N_DVT = DV / MT;
   static constexpr int N_KQ = DQK / 16, N_KV = DV / 16;
-  // q-tile buffer: [Q A-frags | Q^T frags | dO A-frags | dO^T frags | stats]
+  // q-tile buffer: [Q A-frags | dO A-frags | stats], fragments swizzled (see gather_frags)
   static constexpr int T_QA = 0;
-  static constexpr int T_QT = T_QA + N_KQ * FRAG;
-  static constexpr int T_OA = T_QT + N_DQT * 2 * FRAG;
-  static constexpr int T_OT = T_OA + N_KV * FRAG;
-  static constexpr int T_ST = T_OT + N_DVT * 2 * FRAG;
+  static constexpr int T_OA = T_QA + N_KQ * FRAG;
+  static constexpr int T_ST = T_OA + N_KV * FRAG;
   static constexpr int TILE_BYTES = T_ST + 2 * BR * 4;
   static constexpr int SK_BYTES = KLDS ? BC * DQK * 2 : 0;
   static constexpr int SST_BYTES = DET ? 0 : BC * BR * 2;
@@ -106,7 +102,8 @@ struct MainCfg {
 // are issued from inline assembly, so the compiler neither sees them as pending LDS writes (which
 // would make it wait for every one of them before any LDS read or workgroup barrier) nor counts
 // them: every consumer waits for them explicitly with vmcnt before a barrier.  M0 is written only
-// here (no other instruction in these kernels reads it).
+// here (no other instruction in these kernels reads it).  The LDS base is wave-uniform by
+// construction; readfirstlane states that to the compiler so it lands in a scalar register.
 typedef u32x4 rsrc_t;
 
 // Raw buffer descriptor over `bytes` bytes at `base` (stride 0, 32-bit data format); reads past
@@ -119,14 +116,16 @@ __device__ __forceinline__ rsrc_t buf_rsrc(const void* base, int64_t bytes) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma4(rsrc_t r, uint32_t off, void* lds_wave_base) {
-  const uint32_t l = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base;
+  const uint32_t l = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base);
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
                : "v"(off), "s"(r), "s"(l)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma16(rsrc_t r, uint32_t off, void* lds_wave_base) {
-  const uint32_t l = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base;
+  const uint32_t l = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base);
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(off), "s"(r), "s"(l)
@@ -236,10 +235,6 @@ __device__ __forceinline__ void schedule_reads_ahead() {
   }
 }
 
-__device__ __forceinline__ bf16x8 frag(const char* base, int f, int lane) {
-  return *reinterpret_cast<const bf16x8*>(base + f * 1024 + lane * 16);
-}
-
 // Softmax replay and dS for one 32-key MFMA tile (keys key_col .. of this lane's column):
 // P = exp2(S * scale * log2e - LSE * log2e) (0 on masked pairs), dS = P * (dP - delta); both are
 // packed to bf16 pairs in accumulator order (pb/sb[v/2] holds registers v, v+1).
@@ -271,6 +266,27 @@ __device__ __forceinline__ void softmax_ds(const floatx16& S, const floatx16& dP
     sb[2 * x + 1] = pack_bf16x2(dv[2], dv[3]);
   }
 }
+
+// Per-lane offsets of the GEMM3 / GEMM5 A operands, dO^T and Q^T (rows d, contraction over the
+// tile's 32 q rows), read with ds_read_b64_tr_b16 straight from the swizzled A fragments of GEMM1 /
+// GEMM2.  MFMA step tb covers q 16 tb .. +15 in the order in which the accumulator layout delivers P
+// and dS as B operands: k slot 8 g + 4 sec + m holds q = 16 tb + 8 sec + 4 g + m.  Addressing lane
+// r = 4 jj + cc of a 16-lane block points at q row 16 tb + 8 sec + 4 g + jj, columns 4 cc .. +3 of
+// fragment 2 dt + (lane / 16) % 2.
+struct TrALanes {
+  int o[2];  // sec = 0, 1
+  __device__ __forceinline__ explicit TrALanes(int lane) {
+    const int jj = (lane & 15) >> 2, cc = lane & 3, g = lane >> 5, hi = (lane >> 4) & 1;
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec)
+      o[sec] = hi * 1024 + (cc >> 1) * 512 +
+               ((8 * sec + 4 * g + jj) ^ (4 * kswz(2 * (cc >> 1), hi))) * 16 + 8 * (cc & 1);
+  }
+  __device__ __forceinline__ bf16x8 read(const char* frags, int dt, int tb) const {
+    const int base = dt * 2048 + tb * 256;
+    return concat(lds_read_tr(frags, base + o[0]), lds_read_tr(frags, base + o[1]));
+  }
+};
 
 // GEMM4 of the fp32-atomic route for one q tile: dQ (32 q x Dqk) = dS K over the tile's keys,
 // added into dq_accum with fp32 atomics.  dS sits in sST in register order (block (w,kt,x) of
@@ -348,12 +364,8 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
   const bf16_t* Qb = p.q + q_row0 * DQK;
   const bf16_t* dOb = p.dO + q_row0 * DV;
   const float* statb = p.stats + (int64_t)bh * p.sq_pad * 2;
-  const bf16_t* qtb = p.qt + (int64_t)bh * n_q_tiles * (BR * DQK);
-  const bf16_t* dotb = p.dot + (int64_t)bh * n_q_tiles * (BR * DV);
   const rsrc_t rQ = buf_rsrc(Qb, (int64_t)p.Sq * DQK * 2);
   const rsrc_t rdO = buf_rsrc(dOb, (int64_t)p.Sq * DV * 2);
-  const rsrc_t rQT = buf_rsrc(qtb, (int64_t)p.sq_pad * DQK * 2);
-  const rsrc_t rdOT = buf_rsrc(dotb, (int64_t)p.sq_pad * DV * 2);
   const rsrc_t rStat = buf_rsrc(statb, (int64_t)p.sq_pad * 2 * 4);
 
   acc_t accK[C::N_DQT][NKT], accV[C::N_DVT][NKT];
@@ -367,17 +379,16 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
     for (int kt = 0; kt < NKT; ++kt) accV[t][kt] = acc_t{};
 
   const int key_lane = k0 + w * KPW + lc;  // this lane's key in key tile 0 of the wave
-  const int kofs[2] = {swz_chunk(lane, 0), swz_chunk(lane, 1)};  // K fragment reads, by parity
+  const int kofs[2] = {swz_chunk(lane, 0), swz_chunk(lane, 1)};  // fragment reads, by parity
+  const TrALanes tra(lane);
 
   if (i_lo <= i_hi) {
     auto tile = [&](int i) -> char* { return smem + C::OFF_T + (C::NBUF == 2 ? (i & 1) : 0) * C::TILE_BYTES; };
     // ---- q tile i into its LDS buffer ----------------------------------------------------------
     auto load_tile = [&](int i) {
       char* t = tile(i);
-      gather_frags<DQK, C::NW>(rQ, i * BR, p.Sq, C::N_KQ, t + C::T_QA, w, lane);
-      copy_frags<C::NW>(rQT, (uint32_t)i * (BR * DQK * 2), C::N_DQT * 2, t + C::T_QT, w, lane);
-      gather_frags<DV, C::NW>(rdO, i * BR, p.Sq, C::N_KV, t + C::T_OA, w, lane);
-      copy_frags<C::NW>(rdOT, (uint32_t)i * (BR * DV * 2), C::N_DVT * 2, t + C::T_OT, w, lane);
+      gather_frags<DQK, C::NW, true>(rQ, i * BR, p.Sq, C::N_KQ, t + C::T_QA, w, lane);
+      gather_frags<DV, C::NW, true>(rdO, i * BR, p.Sq, C::N_KV, t + C::T_OA, w, lane);
       if (w == 0)  // 64 floats: [lse2, delta] x 32 rows, already padded to sq_pad rows
         dma4(rStat, (uint32_t)(i * BR * 2 + lane) * 4, t + C::T_ST);
     };
@@ -432,14 +443,15 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
 #pragma unroll
         for (int t = 0; t < (C::N_KQ > C::N_KV ? C::N_KQ : C::N_KV); ++t) {
           if (t < C::N_KQ) {
-            const bf16x8 a = frag(T + C::T_QA, t, lane);
+            const bf16x8 a = lds_read_b128(T + C::T_QA, t * 1024 + kofs[t & 1]);
             if constexpr (C::KREG) {
               S = M::mma(a, kreg[kt][t], S);
             } else {
               S = M::mma(a, lds_read_b128(sK, ((w * NKT + kt) * C::N_KQ + t) * 1024 + kofs[t & 1]), S);
             }
           }
-          if (t < C::N_KV) dP = M::mma(frag(T + C::T_OA, t, lane), vreg[kt][t], dP);
+          if (t < C::N_KV)
+            dP = M::mma(lds_read_b128(T + C::T_OA, t * 1024 + kofs[t & 1]), vreg[kt][t], dP);
         }
         schedule_reads_ahead<(C::KREG ? 1 : 2) * C::N_KQ + C::N_KV, C::N_KQ + C::N_KV, 6>();
         if (edge)
@@ -470,7 +482,7 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
       for (int tb = 0; tb < 2; ++tb) {  // 32 q rows = two 16-deep contraction steps
 #pragma unroll
         for (int dt = 0; dt < C::N_DVT; ++dt) {
-          const bf16x8 a = frag(T + C::T_OT, dt * 2 + tb, lane);
+          const bf16x8 a = tra.read(T + C::T_OA, dt, tb);
 #pragma unroll
           for (int kt = 0; kt < NKT; ++kt) {
             const bf16x8 bP = __builtin_bit_cast(
@@ -480,7 +492,7 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
         }
 #pragma unroll
         for (int dt = 0; dt < C::N_DQT; ++dt) {
-          const bf16x8 a = frag(T + C::T_QT, dt * 2 + tb, lane);
+          const bf16x8 a = tra.read(T + C::T_QA, dt, tb);
 #pragma unroll
           for (int kt = 0; kt < NKT; ++kt) {
             const bf16x8 bS = __builtin_bit_cast(
@@ -489,7 +501,7 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
           }
         }
       }
-      schedule_reads_ahead<2 * (C::N_DVT + C::N_DQT), 2 * NKT * (C::N_DVT + C::N_DQT), 4>();
+      schedule_reads_ahead<4 * (C::N_DVT + C::N_DQT), 2 * NKT * (C::N_DVT + C::N_DQT), 6>();
       if constexpr (C::NBUF == 1) {
         lds_barrier();  // every wave is done with the single q-tile buffer
         if (i > i_lo) load_tile(i - 1);

@@ -40,7 +40,7 @@ bool geometry_for(int Dqk, int Dv, Geometry* g) {
 }
 
 struct Carve {
-  int64_t stats = 0, qt = 0, dot = 0, dq_accum = -1, ds = -1, dk_ws = -1, dv_ws = -1, total = 0;
+  int64_t stats = 0, dq_accum = -1, ds = -1, dk_ws = -1, dv_ws = -1, total = 0;
   int64_t sq_pad = 0, skv_pad = 0;
 };
 
@@ -51,10 +51,6 @@ Carve carve(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv, int det, c
   c.skv_pad = align_up(Skv, g.bc);
   c.stats = off;  // [LSE * log2e, delta] per padded q row
   off = align_up(off + (int64_t)B * Hq * c.sq_pad * 2 * 4, kAlign);
-  c.qt = off;     // Q^T fragments per 32-row q tile
-  off = align_up(off + (int64_t)B * Hq * c.sq_pad * Dqk * 2, kAlign);
-  c.dot = off;    // dO^T fragments per 32-row q tile
-  off = align_up(off + (int64_t)B * Hq * c.sq_pad * Dv * 2, kAlign);
   if (!det) {
     c.dq_accum = off;
     off = align_up(off + (int64_t)B * Hq * Sq * Dqk * 4, kAlign);
@@ -154,10 +150,10 @@ hipError_t launch_preprocess(const PreParams& pp, int Dqk, int Dv, int64_t tiles
   if (tiles == 0) return hipSuccess;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)tiles), block(256);
-  if (Dqk == 64) hipLaunchKernelGGL((preprocess_kernel<64, 64>), grid, block, 0, s, pp);
-  else if (Dqk == 128) hipLaunchKernelGGL((preprocess_kernel<128, 128>), grid, block, 0, s, pp);
-  else if (Dqk == 192) hipLaunchKernelGGL((preprocess_kernel<192, 128>), grid, block, 0, s, pp);
-  else hipLaunchKernelGGL((preprocess_kernel<256, 256>), grid, block, 0, s, pp);
+  (void)Dqk;
+  if (Dv == 64) hipLaunchKernelGGL((preprocess_kernel<64>), grid, block, 0, s, pp);
+  else if (Dv == 128) hipLaunchKernelGGL((preprocess_kernel<128>), grid, block, 0, s, pp);
+  else hipLaunchKernelGGL((preprocess_kernel<256>), grid, block, 0, s, pp);
   return hipGetLastError();
 }
 
@@ -222,13 +218,10 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   const bool gqa = Hq != Hkv;
 
   PreParams pp;
-  pp.q = (const bf16_t*)q;
   pp.o = (const bf16_t*)o;
   pp.dO = (const bf16_t*)dO;
   pp.lse = lse;
   pp.stats = stats;
-  pp.qt = (bf16_t*)(ws + c.qt);
-  pp.dot = (bf16_t*)(ws + c.dot);
   pp.dq_accum = dq_accum;
   pp.seq_q_lens = seq_q_lens;
   pp.Hq = Hq;
@@ -246,8 +239,6 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   mp.v = (const bf16_t*)v;
   mp.dO = (const bf16_t*)dO;
   mp.stats = stats;
-  mp.qt = pp.qt;
-  mp.dot = pp.dot;
   mp.dq_accum = dq_accum;
   mp.ds_ws = det ? (bf16_t*)(ws + c.ds) : nullptr;
   mp.dk_out = gqa ? (bf16_t*)(ws + c.dk_ws) : (bf16_t*)dk;
@@ -384,13 +375,10 @@ int sdpa_bwd_preprocess(const void* o, const void* dO, const float* lse, float* 
       ((uintptr_t)lse & 3) != 0)
     return SDPA_BWD_UNSUPPORTED;
   PreParams pp;
-  pp.q = nullptr;
   pp.o = (const bf16_t*)o;
   pp.dO = (const bf16_t*)dO;
   pp.lse = lse;
   pp.stats = stats;
-  pp.qt = nullptr;  // statistics (and accumulator zeroing) only
-  pp.dot = nullptr;
   pp.dq_accum = dq_accum;
   pp.seq_q_lens = seq_q_lens;
   pp.sq_pad = (int)align_up(Sq, 32);

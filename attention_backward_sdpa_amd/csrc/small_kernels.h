@@ -13,35 +13,23 @@ namespace sdpa {
 //     batch entry's query length, rows past the buffer and rows whose LSE is -inf (no visible key
 //     in the forward) get [+inf, 0], so the main kernel replays P = 0 for them without a NaN.
 //     The row's Dv/8 lanes reduce with butterfly shuffles in a fixed order (deterministic).
-//   * qt / dot: the tile's Q^T and dO^T as ready-made MFMA A operands (contraction over q) for
-//     the main kernel's GEMM5 and GEMM3: fragment (dt, tb), lane l holds the 8 values
-//     X[16*tb + 4*g + {0..3, 8..11}][32*dt + l % 32], g = l / 32, i.e. the q order in which the
-//     accumulator layout delivers P and dS.  Each fragment is 1 KiB, lane-major, so the main kernel
-//     copies a tile into LDS with linear 16-byte loads and reads it conflict-free.  Rows past the
-//     buffer are zero.
 //   * when zero_rows is set, the tile's rows of the fp32 dQ accumulator are cleared.
 struct PreParams {
-  const bf16_t* q;
   const bf16_t* o;
   const bf16_t* dO;
   const float* lse;
   float* stats;              // (B*Hq, sq_pad, 2)
-  bf16_t* qt;                // (B*Hq, sq_pad/32, Dqk/32*2, 64, 8) or null
-  bf16_t* dot;               // (B*Hq, sq_pad/32, Dv/32*2, 64, 8) or null
   float* dq_accum;           // (B*Hq, Sq, Dqk) or null
   const int* seq_q_lens;
   int Hq, Sq, sq_pad, Dqk;
   int zero_rows;
 };
 
-template <int DQK, int DV>
+template <int DV>
 __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
   constexpr int BR = 32;
   constexpr int LPR = DV / 8;              // lanes per row for the row dot
   constexpr int RPP = 256 / LPR;           // rows per pass
-  // the tile's Q and dO rows, staged (row stride padded by 16 bytes against bank conflicts)
-  __shared__ __attribute__((aligned(16))) char sq[BR * (DQK * 2 + 16)];
-  __shared__ __attribute__((aligned(16))) char so[BR * (DV * 2 + 16)];
   const int tid = threadIdx.x;
   const int nt = p.sq_pad / BR;
   const int64_t bh = blockIdx.x / nt;
@@ -50,7 +38,6 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
   const int b = (int)(bh / p.Hq);
   const int Lq = p.seq_q_lens ? p.seq_q_lens[b] : p.Sq;
 
-  // ---- statistics ------------------------------------------------------------------------------
   for (int r0 = 0; r0 < BR; r0 += RPP) {
     const int r = r0 + tid / LPR, sub = tid % LPR, s = q0 + r;
     const bool real = s < p.Sq;
@@ -79,38 +66,6 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
       for (int x = sub; x < p.Dqk / 4; x += LPR) dst[x] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
-  if (p.qt == nullptr) return;
-
-  // ---- Q^T / dO^T fragments ---------------------------------------------------------------------
-  for (int c = tid; c < BR * DQK / 8; c += 256) {
-    const int r = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (q0 + r < p.Sq) v = *reinterpret_cast<const u32x4*>(p.q + (bh * p.Sq + q0 + r) * DQK + col);
-    *reinterpret_cast<u32x4*>(sq + r * (DQK * 2 + 16) + col * 2) = v;
-  }
-  for (int c = tid; c < BR * DV / 8; c += 256) {
-    const int r = c / (DV / 8), col = (c % (DV / 8)) * 8;
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (q0 + r < p.Sq) v = *reinterpret_cast<const u32x4*>(p.dO + (bh * p.Sq + q0 + r) * DV + col);
-    *reinterpret_cast<u32x4*>(so + r * (DV * 2 + 16) + col * 2) = v;
-  }
-  __syncthreads();
-  const int lane = tid & 63, g = lane >> 5, lc = lane & 31;
-  auto fragment = [&](const char* st, int rowb, int dt, int tb) {
-    bf16_t v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int qq = 16 * tb + 4 * g + (e & 3) + (e >> 2) * 8;
-      v[e] = *reinterpret_cast<const bf16_t*>(st + qq * (rowb + 16) + (32 * dt + lc) * 2);
-    }
-    return u32x4{v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
-                 v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16)};
-  };
-  constexpr int FQ = DQK / 32 * 2, FO = DV / 32 * 2;
-  u32x4* qtb = reinterpret_cast<u32x4*>(p.qt + (bh * nt + i) * (int64_t)(BR * DQK));
-  u32x4* dotb = reinterpret_cast<u32x4*>(p.dot + (bh * nt + i) * (int64_t)(BR * DV));
-  for (int f = tid >> 6; f < FQ; f += 4) qtb[f * 64 + lane] = fragment(sq, DQK * 2, f >> 1, f & 1);
-  for (int f = tid >> 6; f < FO; f += 4) dotb[f * 64 + lane] = fragment(so, DV * 2, f >> 1, f & 1);
 }
 
 // ---- dQ convert ---------------------------------------------------------------------------------

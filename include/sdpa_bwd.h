@@ -56,10 +56,9 @@ enum {
 };
 
 /* Bytes of workspace needed by a call with these arguments: a 256-byte-aligned carve of the
- * per-row statistics (LSE * log2 e and delta), the Q^T and dO^T operand tiles the preprocess
- * writes (B*Hq*Sq_pad*(Dqk+Dv) bf16), then either the fp32 dQ accumulator
- * (B*Hq*Sq*Dqk floats) or, in deterministic mode, the bf16 dS buffer (B*Hq*Sq_pad*Skv_pad), then
- * under GQA the bf16 per-query-head dK/dV partials.  Returns 0 for arguments sdpa_bwd rejects and
+ * per-row statistics (LSE * log2 e and delta, B*Hq*Sq_pad float pairs), then either the fp32 dQ
+ * accumulator (B*Hq*Sq*Dqk floats) or, in deterministic mode, the bf16 dS buffer
+ * (B*Hq*Sq_pad*Skv_pad), then under GQA the bf16 per-query-head dK/dV partials.  Returns 0 for arguments sdpa_bwd rejects and
  * for empty problems. */
 size_t sdpa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv,
                                int causal, int window_left, int deterministic, int has_seqlens);

@@ -57,16 +57,14 @@ def _al(n):
 
 
 def test_workspace_size_rules(so):
-    # non-deterministic MHA: per-row statistics (2 floats per row, rows padded to 32), the Q^T and
-    # dO^T operand tiles, fp32 dQ accumulator
-    tiles = 2 * _al(4 * 256 * 128 * 2)
-    assert _ws() == _al(4 * 256 * 8) + tiles + _al(4 * 256 * 128 * 4)
+    # non-deterministic MHA: per-row statistics (2 floats per row, rows padded to 32) and the fp32
+    # dQ accumulator
+    assert _ws() == _al(4 * 256 * 8) + _al(4 * 256 * 128 * 4)
     # GQA adds per-query-head bf16 dK/dV partials
     assert _ws(Hkv=1) == _ws() + 2 * _al(4 * 256 * 128 * 2)
     # deterministic: statistics + bf16 dS (S_kv padded to the 256-key tile, S_q to the 32-row
     # q tile), no fp32 dQ
-    assert _ws(deterministic=True, Sq=200, Skv=200) == (_al(4 * 224 * 8) + 2 * _al(4 * 224 * 128 * 2)
-                                                        + _al(4 * 224 * 256 * 2))
+    assert _ws(deterministic=True, Sq=200, Skv=200) == _al(4 * 224 * 8) + _al(4 * 224 * 256 * 2)
     # monotone in the sequence length
     sizes = [_ws(Sq=s, Skv=s) for s in (64, 128, 300, 1000)]
     assert sizes == sorted(sizes)
