@@ -5,10 +5,11 @@
 // atomics and a fixed order per q tile, so the result is bitwise reproducible.
 //
 // The pass streams the dS workspace once from HBM, so it is bound by how many bytes are in flight:
-//   * a workgroup of 4 waves owns 4 consecutive q tiles of one head, so every 64-key chunk of K
-//     (re-read from L2) serves 128 query rows;
+//   * a workgroup of NW waves owns NW consecutive q tiles of one head, so every 64-key chunk of K
+//     (re-read from L2) serves 32 * NW query rows (NW = 8 at head dim <= 128: two waves per SIMD
+//     hide each other's LDS latency; NW = 4 above, where the accumulators are twice as large);
 //   * chunks are staged through LDS with LDS-DMA buffer loads, NSTAGE deep (3 or 4), so up to
-//     NSTAGE - 1 chunks of dS (16 KiB each) are in flight per workgroup while one is consumed.
+//     NSTAGE - 1 chunks of dS (4 KiB per q tile) are in flight per workgroup while one is consumed.
 // The workspace holds each stored (KV tile, q tile) block as 2 KiB dS quads per 32 keys (layout in
 // bwd_main.h), so any 64 consecutive keys of a block are one contiguous 4 KiB piece.  dS and K (as
 // swizzled GEMM1 fragments) are read as MFMA operands with the transpose instruction, which the
@@ -30,17 +31,18 @@ struct Dq2kParams {
   float scale;
 };
 
-template <int DQK_, int BC_>
+template <int DQK_, int BC_, int NW_>
 struct Dq2kCfg {
-  static constexpr int DQK = DQK_, BC = BC_;
-  static constexpr int BR = 32, NW = 4, NT = 256, KC = 64;   // KC: keys per chunk
+  static constexpr int DQK = DQK_, BC = BC_, NW = NW_;
+  static constexpr int BR = 32, NT = NW * 64, KC = 64;       // KC: keys per chunk
   static constexpr int QT = NW;                              // q tiles per workgroup, one per wave
   static constexpr int N_DT = DQK / 32;                      // 32-column d tiles per wave
   static constexpr int ST_BYTES = KC * BR * 2;               // 4 KiB of dS per q tile and chunk
   static constexpr int DS_BYTES = QT * ST_BYTES;
   static constexpr int K_FRAGS = (KC / 32) * (DQK / 16);     // K fragments of one chunk
   static constexpr int STAGE_BYTES = DS_BYTES + K_FRAGS * 1024;
-  static constexpr int NSTAGE = (4 * STAGE_BYTES <= 160 * 1024) ? 4 : 3;
+  static constexpr int NSTAGE_FIT = (160 * 1024) / STAGE_BYTES;
+  static constexpr int NSTAGE = NSTAGE_FIT < 4 ? NSTAGE_FIT : 4;
   static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
   // LDS-DMA instructions each wave issues per stage (the same for every stage and wave, so "all
   // but the newest k stages have landed" is a constant vmcnt)
@@ -49,7 +51,7 @@ struct Dq2kCfg {
   static constexpr int OPS_PER_STAGE = DS_PER_WAVE + K_PER_WAVE;
   static_assert(BC % KC == 0, "whole chunks per KV tile");
   static_assert((DS_BYTES / 1024) % NW == 0 && K_FRAGS % NW == 0, "even DMA split over waves");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(NSTAGE >= 2 && LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert((NSTAGE - 2) * OPS_PER_STAGE < 64, "vmcnt range");
 };
 
