@@ -54,11 +54,13 @@ struct MainParams {
   const float* stats;       // (B*Hq, sq_pad, 2): [LSE*log2e or +inf, delta] per q row
   float* dq_accum;          // (B, Hq, Sq, Dqk) fp32, non-deterministic route
   bf16_t* ds_ws;            // (B*Hq, n_kv_tiles, sq_pad/32) blocks of BC x 32 bf16 dS
-  bf16_t* dk_out;           // (B, out_heads, Skv, Dqk)
-  bf16_t* dv_out;           // (B, out_heads, Skv, Dv)
+  bf16_t* dk_out;           // dK: (B, Hkv, Skv, Dqk), or partials (B, Hq, n_split, Skv, Dqk)
+  bf16_t* dv_out;           // dV: likewise with Dv
   const int* seq_q_lens;    // (B,) or null
   const int* seq_kv_lens;   // (B,) or null
-  int B, Hq, Hkv, Sq, Skv, group, out_heads;
+  int B, Hq, Hkv, Sq, Skv, group;
+  int partials;             // 1: write per-(query head, part) partials for the reduction
+  int n_split;              // parts the q-tile range of a key tile is split into
   int causal, window_left, window_right, bottom_right;
   int n_kv_tiles;
   int sq_pad, skv_pad;      // statistics / dS workspace extents
@@ -337,11 +339,13 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
   const int g = lane >> 5, lc = lane & 31;
 
-  // Longest-first order: all heads of key tile 0 first (causal tiles near the start see the most
-  // q tiles).  Consecutive blocks are different heads, so the 8 XCDs split the heads.
+  // Longest-first order: all heads of key tile 0 (part 0, then the other parts of its q-tile
+  // range) first: causal tiles near the start see the most q tiles.  Consecutive blocks are
+  // different heads, so the 8 XCDs split the heads.
   const int nbh = p.B * p.Hq;
   const int bh = blockIdx.x % nbh;
-  const int j = blockIdx.x / nbh;
+  const int js = blockIdx.x / nbh;
+  const int j = js / p.n_split, part = js % p.n_split;
   const int h = bh % p.Hq, b = bh / p.Hq;
   const int kvh = h / p.group;
 
@@ -355,6 +359,11 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
   const int k0 = j * BC;
   int i_lo, i_hi;
   q_tile_range(mg, k0, BC, BR, &i_lo, &i_hi);
+  if (p.n_split > 1 && i_lo <= i_hi) {  // this workgroup's part of the range (part 0 on top)
+    const int per = (i_hi - i_lo + p.n_split) / p.n_split;
+    i_hi -= part * per;
+    i_lo = i_hi - per + 1 > i_lo ? i_hi - per + 1 : i_lo;
+  }
 
   const int n_q_tiles = p.sq_pad / BR;
   const int64_t kv_row0 = (int64_t)(b * p.Hkv + kvh) * p.Skv;
@@ -514,12 +523,12 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
   }
 
   // ---- epilogue: dK (scaled) and dV, written once; keys past the sequence are zero -------------
-  const int oh = (p.out_heads == p.Hq) ? h : kvh;
+  const int64_t oslot = p.partials ? (int64_t)bh * p.n_split + part : (int64_t)b * p.Hkv + kvh;
 #pragma unroll
   for (int kt = 0; kt < NKT; ++kt) {
     const int key = key_lane + kt * 32;
     if (key < p.Skv) {
-      const int64_t orow = (int64_t)(b * p.out_heads + oh) * p.Skv + key;
+      const int64_t orow = oslot * p.Skv + key;
       bf16_t* dkr = p.dk_out + orow * DQK;
       bf16_t* dvr = p.dv_out + orow * DV;
 #pragma unroll

@@ -39,6 +39,21 @@ bool geometry_for(int Dqk, int Dv, Geometry* g) {
   return true;
 }
 
+// Number of parts the q-tile range of every key tile is split into (each part a workgroup of its
+// own, writing dK/dV partials that the reduction sums in a fixed order).  A grid of fewer than
+// two workgroups per CU leaves CUs idle, and under a causal mask the key tiles near the start see
+// many more q tiles than the rest; splitting the ranges evens the per-workgroup work.  Parts keep
+// at least 8 q tiles.
+constexpr int kNumCUs = 256;
+
+int q_split(int B, int Hq, int Sq, int Skv, const Geometry& g) {
+  const int64_t grid = (int64_t)((Skv + g.bc - 1) / g.bc) * B * Hq;
+  const int n_q_tiles = (Sq + g.br - 1) / g.br;
+  int split = 1;
+  while (split < 4 && grid * split < 2 * kNumCUs && n_q_tiles / (2 * split) >= 8) split *= 2;
+  return split;
+}
+
 struct Carve {
   int64_t stats = 0, dq_accum = -1, ds = -1, dk_ws = -1, dv_ws = -1, total = 0;
   int64_t sq_pad = 0, skv_pad = 0;
@@ -58,11 +73,12 @@ Carve carve(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv, int det, c
     c.ds = off;
     off = align_up(off + (int64_t)B * Hq * c.skv_pad * c.sq_pad * 2, kAlign);
   }
-  if (Hq != Hkv) {
+  const int split = q_split(B, Hq, Sq, Skv, g);
+  if (Hq != Hkv || split > 1) {  // per-(query head, part) dK/dV partials
     c.dk_ws = off;
-    off = align_up(off + (int64_t)B * Hq * Skv * Dqk * 2, kAlign);
+    off = align_up(off + (int64_t)B * Hq * split * Skv * Dqk * 2, kAlign);
     c.dv_ws = off;
-    off = align_up(off + (int64_t)B * Hq * Skv * Dv * 2, kAlign);
+    off = align_up(off + (int64_t)B * Hq * split * Skv * Dv * 2, kAlign);
   }
   c.total = off;
   return c;
@@ -215,7 +231,8 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   char* ws = (char*)workspace;
   float* stats = (float*)(ws + c.stats);
   float* dq_accum = det ? nullptr : (float*)(ws + c.dq_accum);
-  const bool gqa = Hq != Hkv;
+  const int split = q_split(B, Hq, Sq, Skv, geo);
+  const bool partials = Hq != Hkv || split > 1;  // dK/dV go through the reduction
 
   PreParams pp;
   pp.o = (const bf16_t*)o;
@@ -241,8 +258,8 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   mp.stats = stats;
   mp.dq_accum = dq_accum;
   mp.ds_ws = det ? (bf16_t*)(ws + c.ds) : nullptr;
-  mp.dk_out = gqa ? (bf16_t*)(ws + c.dk_ws) : (bf16_t*)dk;
-  mp.dv_out = gqa ? (bf16_t*)(ws + c.dv_ws) : (bf16_t*)dv;
+  mp.dk_out = partials ? (bf16_t*)(ws + c.dk_ws) : (bf16_t*)dk;
+  mp.dv_out = partials ? (bf16_t*)(ws + c.dv_ws) : (bf16_t*)dv;
   mp.seq_q_lens = seq_q_lens;
   mp.seq_kv_lens = seq_kv_lens;
   mp.B = B;
@@ -251,7 +268,8 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   mp.Sq = Sq;
   mp.Skv = Skv;
   mp.group = Hq / Hkv;
-  mp.out_heads = gqa ? Hq : Hkv;
+  mp.partials = partials ? 1 : 0;
+  mp.n_split = split;
   mp.causal = causal ? 1 : 0;
   mp.window_left = window_left;
   mp.window_right = causal ? window_right : 0;
@@ -261,13 +279,13 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   mp.skv_pad = (int)c.skv_pad;
   mp.scale = scale;
   mp.scale_log2 = scale * kLog2e;
-  const int64_t main_grid = (int64_t)mp.n_kv_tiles * B * Hq;
+  const int64_t main_grid = (int64_t)mp.n_kv_tiles * split * B * Hq;
   if (main_grid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
   e = run_main(Dqk, Dv, mp, det, (int)main_grid, geo.bc, stream);
   if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   rec(2);
 
-  if (gqa) {
+  if (partials) {
     ReduceParams rp;
     rp.dk_ws = mp.dk_out;
     rp.dv_ws = mp.dv_out;
@@ -277,7 +295,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     rp.head_v8 = (int64_t)Skv * Dv / 8;
     rp.nk8 = (int64_t)B * Hkv * rp.head_k8;
     rp.nv8 = (int64_t)B * Hkv * rp.head_v8;
-    rp.group = Hq / Hkv;
+    rp.group = (Hq / Hkv) * split;  // slots (query head of the group, part), in that order
     hipLaunchKernelGGL(gqa_reduce_kernel, dim3(grid_stride_blocks(rp.nk8 + rp.nv8)), dim3(256), 0,
                        stream, rp);
     if (hipGetLastError() != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;

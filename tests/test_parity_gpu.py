@@ -45,6 +45,15 @@ SMALL_CASES = {
     # non-deterministic D = 256
     "nondet_d256_s200": V(W["mha_det_s8192_d256"], Hq=2, Hkv=2, Sq=200, Skv=200,
                           deterministic=False),
+    # few workgroups per CU: every key tile's q-tile range is split in parts whose dK/dV
+    # partials the reduction sums (causal MHA, 3 key tiles x 2 heads, 19 q tiles)
+    "split_causal_d128_s600": V(W["mha_causal_s2048_d128"], B=1, Hq=2, Hkv=2, Sq=600, Skv=600),
+    # split ranges under GQA on the deterministic route
+    "det_gqa_split_d128_s700": V(W["gqa_causal_s4096_d128"], Hq=4, Hkv=2, Sq=700, Skv=700,
+                                 deterministic=True),
+    # split ranges with the 4-wave MLA kernel, a window and padding
+    "mla_split_window_padded_s900": V(W["mla_window_padded_s4096"], B=2, Hq=2, Hkv=2, Sq=900,
+                                      Skv=900, window_left=300, len_lo=500),
 }
 
 
