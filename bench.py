@@ -106,6 +106,28 @@ def copy_probe(torch, dev):
     torch.cuda.synchronize()
 
 
+def atomic_probe():
+    """fp32 atomic adds per second through torch's index_add_ (one atomic per element, consecutive
+    lanes on consecutive addresses): the ceiling that bounds a dQ built from fp32 atomics."""
+    import torch
+    dev = torch.device("cuda:0")
+    n_out, n = 16 << 20, 64 << 20
+    out = torch.zeros(n_out, device=dev)
+    src = torch.ones(n, device=dev)
+    idx = torch.arange(n, device=dev) % n_out
+    out.index_add_(0, idx, src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        out.index_add_(0, idx, src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    print(json.dumps({"probe": "fp32 atomic add", "adds": n, "ms": round(ms, 4),
+                      "g_adds_per_s": round(n / ms / 1e6, 1)}), flush=True)
+
+
 def _pmc_means(directory, counter):
     """Mean per-dispatch value of `counter` for each kernel name in a rocprofv3 --pmc CSV."""
     import csv
@@ -202,12 +224,18 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run a plain 1 GiB fp32 copy kernel three times "
                          "(the calibration kernel of the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--atomic-probe", action="store_true",
+                    help="measure the device's fp32 atomic-add rate (torch index_add_, 64 Mi "
+                         "coalesced adds into 16 Mi floats) and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: read two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) "
                          "of a --copy-probe run and write the main kernel's HBM traffic record")
     args = ap.parse_args()
     if args.traffic_from:
         write_traffic_record(args.workload, args.deterministic, *args.traffic_from)
+        return
+    if args.atomic_probe:
+        atomic_probe()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the "
