@@ -75,8 +75,11 @@ struct MainCfg {
   static constexpr int NT = NW * 64, MT = 32, BR = 32, FRAG = 1024;
   static constexpr int BC = NW * KPW;
   static constexpr int NKT = KPW / 32;         // 32-key MFMA tiles per wave
-  static constexpr bool KREG = DQK >= 192;     // GEMM1's K operand from registers
+  static constexpr bool KREG = DQK >= 192 && NW == 4;  // GEMM1's K operand from registers
   static constexpr bool KLDS = !KREG || !DET;  // K fragments in LDS (GEMM1 and/or GEMM4)
+  // LDS operand reads kept in flight ahead of the MFMAs (fewer where the 256-register budget of
+  // the two-waves-per-SIMD layout is nearly full with the head-dim-192 accumulators)
+  static constexpr int AHEAD = (NW == 8 && DQK > 128) ? 2 : 6;
   using M = Mfma<32>;
   static constexpr int N_DQT = DQK / MT, N_DVT = DV / MT;
   static constexpr int N_KQ = DQK / 16, N_KV = DV / 16;
@@ -237,14 +240,31 @@ __device__ __forceinline__ void schedule_reads_ahead() {
   }
 }
 
-// Softmax replay and dS for one 32-key MFMA tile (keys key_col .. of this lane's column):
-// P = exp2(S * scale * log2e - LSE * log2e) (0 on masked pairs), dS = P * (dP - delta); both are
-// packed to bf16 pairs in accumulator order (pb/sb[v/2] holds registers v, v+1).
+// The rows of an edge tile that see one key, as offsets from the lane's first row q_lane: the
+// visibility rule of masks.h solved for q (causal: q >= k - diag - R; window: q <= k - diag + W;
+// q < len_q; none when k >= len_kv), so the per-element test is two compares.
+struct KeyRows {
+  int lo = 0, hi = 0;
+  KeyRows() = default;
+  __device__ __forceinline__ KeyRows(const MaskGeom& mg, int q_lane, int key) {
+    int a = 0, z = mg.Lq - 1;
+    if (key >= mg.Lkv) z = -1;
+    if (mg.causal) a = max(a, key - mg.diag - mg.R);
+    if (mg.W >= 0) z = min(z, key - mg.diag + mg.W);
+    lo = a - q_lane;
+    hi = z - q_lane;
+  }
+};
+
+// Softmax replay and dS for one 32-key MFMA tile of this lane's key column:
+// P = exp2(S * scale * log2e - LSE * log2e) (0 on masked pairs, edge tiles only), dS =
+// P * (dP - delta); both are packed to bf16 pairs in accumulator order (pb/sb[v/2] holds registers
+// v, v+1).
 template <bool MASK>
 __device__ __forceinline__ void softmax_ds(const floatx16& S, const floatx16& dP,
                                            const float* sStat, int g, float scale_log2,
-                                           const MaskGeom& mg, int q_lane, int key_col,
-                                           uint32_t (&pb)[8], uint32_t (&sb)[8]) {
+                                           const KeyRows& vis, uint32_t (&pb)[8],
+                                           uint32_t (&sb)[8]) {
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
     // rows of accumulator registers 4x..4x+3 of this lane: g*4 + 8x + 0..3
@@ -257,7 +277,8 @@ __device__ __forceinline__ void softmax_ds(const floatx16& S, const floatx16& dP
     for (int e = 0; e < 4; ++e) {
       float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * x + e], scale_log2, -l4[e]));
       if constexpr (MASK) {
-        if (!mask_visible(mg, q_lane + 8 * x + e, key_col)) pe = 0.f;
+        const int c = 8 * x + e;  // row offset of this register from q_lane
+        if (c < vis.lo || c > vis.hi) pe = 0.f;
       }
       pv[e] = pe;
       dv[e] = pe * (dP[4 * x + e] - d4[e]);
@@ -462,13 +483,12 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
           if (t < C::N_KV)
             dP = M::mma(lds_read_b128(T + C::T_OA, t * 1024 + kofs[t & 1]), vreg[kt][t], dP);
         }
-        schedule_reads_ahead<(C::KREG ? 1 : 2) * C::N_KQ + C::N_KV, C::N_KQ + C::N_KV, 6>();
+        schedule_reads_ahead<(C::KREG ? 1 : 2) * C::N_KQ + C::N_KV, C::N_KQ + C::N_KV, C::AHEAD>();
         if (edge)
-          softmax_ds<true>(S, dP, sStat, g, p.scale_log2, mg, q0 + g * 4, key_lane + kt * 32,
-                           pb[kt], sb[kt]);
+          softmax_ds<true>(S, dP, sStat, g, p.scale_log2,
+                           KeyRows(mg, q0 + g * 4, key_lane + kt * 32), pb[kt], sb[kt]);
         else
-          softmax_ds<false>(S, dP, sStat, g, p.scale_log2, mg, q0 + g * 4, key_lane + kt * 32,
-                            pb[kt], sb[kt]);
+          softmax_ds<false>(S, dP, sStat, g, p.scale_log2, KeyRows(), pb[kt], sb[kt]);
 
         // dS of this 32-key tile as 2 KiB of quads (see ds_store_off)
         if constexpr (C::DET) {
@@ -510,7 +530,7 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
           }
         }
       }
-      schedule_reads_ahead<4 * (C::N_DVT + C::N_DQT), 2 * NKT * (C::N_DVT + C::N_DQT), 6>();
+      schedule_reads_ahead<4 * (C::N_DVT + C::N_DQT), 2 * NKT * (C::N_DVT + C::N_DQT), C::AHEAD>();
       if constexpr (C::NBUF == 1) {
         lds_barrier();  // every wave is done with the single q-tile buffer
         if (i > i_lo) load_tile(i - 1);

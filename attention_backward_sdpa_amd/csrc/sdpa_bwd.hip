@@ -33,7 +33,7 @@ struct Geometry {
 bool geometry_for(int Dqk, int Dv, Geometry* g) {
   if (Dqk == 64 && Dv == 64) *g = {8, 32, 256, 32};
   else if (Dqk == 128 && Dv == 128) *g = {8, 32, 256, 32};
-  else if (Dqk == 192 && Dv == 128) *g = {4, 32, 128, 32};
+  else if (Dqk == 192 && Dv == 128) *g = {8, 32, 256, 32};
   else if (Dqk == 256 && Dv == 256) *g = {4, 32, 128, 32};
   else return false;
   return true;
@@ -141,7 +141,7 @@ hipError_t run_main(int Dqk, int Dv, const MainParams& mp, int det, int grid, in
                     hipStream_t s) {
   if (Dqk == 64) return dispatch_main<64, 64, 32, 8>(mp, det, grid, bc, s);
   if (Dqk == 128) return dispatch_main<128, 128, 32, 8>(mp, det, grid, bc, s);
-  if (Dqk == 192) return dispatch_main<192, 128, 32, 4>(mp, det, grid, bc, s);
+  if (Dqk == 192) return dispatch_main<192, 128, 32, 8>(mp, det, grid, bc, s);
   return dispatch_main<256, 256, 32, 4>(mp, det, grid, bc, s);
 }
 
@@ -158,7 +158,7 @@ hipError_t dispatch_dq2k(const Dq2kParams& dp, int bc, hipStream_t s) {
 hipError_t run_dq2k(int Dqk, const Dq2kParams& dp, int bc, hipStream_t s) {
   if (Dqk == 64) return dispatch_dq2k<64, 256, 8>(dp, bc, s);
   if (Dqk == 128) return dispatch_dq2k<128, 256, 8>(dp, bc, s);
-  if (Dqk == 192) return dispatch_dq2k<192, 128, 4>(dp, bc, s);
+  if (Dqk == 192) return dispatch_dq2k<192, 256, 4>(dp, bc, s);
   return dispatch_dq2k<256, 128, 4>(dp, bc, s);
 }
 
