@@ -147,3 +147,58 @@ def test_fully_masked_rows_and_zero_lengths():
     assert np.all(got[0][0] == 0) and np.all(got[1][0] == 0) and np.all(got[2][0] == 0)
     for tname, g, r in zip(("dQ", "dK", "dV"), got, ref):
         C.assert_close(f"masked {tname}", g, r)
+
+
+# ---- mask and shape surface: S_q != S_kv, bottom-right causal, right band, separate q / kv
+# padding lengths ("SDPA Backward (SM120)", "API Usage" and "Causal, sliding-window, and padding
+# masks").  Each case: (name, base workload, overrides, q lens, kv lens, bottom_right, window_right)
+SURFACE_CASES = [
+    ("sq_lt_skv_bottom_right", "gqa_causal_s4096_d128", dict(B=2, Hq=4, Hkv=2, Sq=300, Skv=520),
+     [300, 180], [520, 260], True, 0),
+    ("sq_gt_skv_top_left", "mha_causal_s2048_d128", dict(B=1, Hq=2, Hkv=2, Sq=520, Skv=300),
+     None, None, False, 0),
+    ("right_band_window", "mha_causal_s2048_d128", dict(B=1, Hq=2, Hkv=2, Sq=400, Skv=400,
+                                                       window_left=90), None, None, False, 37),
+    ("mla_bottom_right_window_lens", "mla_window_padded_s4096", dict(B=2, Hq=2, Hkv=2, Sq=330,
+     Skv=610, window_left=150, padded=False), [330, 201], [610, 333], True, 0),
+    ("det_d256_bottom_right_lens", "mha_det_s8192_d256", dict(B=2, Hq=2, Hkv=2, Sq=260, Skv=390,
+     causal=True), [260, 99], [390, 150], True, 0),
+]
+
+
+@pytest.mark.parametrize("det", [False, True], ids=["atomic", "det"])
+@pytest.mark.parametrize("case_def", SURFACE_CASES, ids=[c[0] for c in SURFACE_CASES])
+def test_mask_and_shape_surface(case_def, det):
+    import attention_backward_sdpa_amd as lib
+    name, base, over, lq, lkv, br, wr = case_def
+    w = V(W[base], **over)
+    inp = synth.draw_inputs(w)
+    f = C.f64
+    q, k, v = f(inp.q), f(inp.k), f(inp.v)
+    kw = dict(causal=w.causal, window_left=w.window_left, seq_q_lens=lq, seq_kv_lens=lkv,
+              bottom_right=br, window_right=wr)
+    o64, lse64 = C.oracle.forward(q, k, v, w.softmax_scale, **kw)
+    o_bits = synth.bf16_bits(o64.astype(np.float32))
+    lse = lse64.astype(np.float32)
+    ref = C.oracle.backward(q, k, v, f(o_bits), f(inp.do), lse.astype(np.float64),
+                            w.softmax_scale, **kw)
+    dev = "cuda"
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    tq, tk, tv, to, tdo = bf(inp.q), bf(inp.k), bf(inp.v), bf(o_bits), bf(inp.do)
+    tlse = torch.from_numpy(lse).to(dev)
+    tlq = None if lq is None else torch.tensor(lq, dtype=torch.int32, device=dev)
+    tlkv = None if lkv is None else torch.tensor(lkv, dtype=torch.int32, device=dev)
+    outs = [torch.empty_like(x) for x in (tq, tk, tv)]
+    for x in outs:
+        x.view(torch.int16).fill_(0x7FC0)
+    n = lib.workspace_size(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.Dqk, w.Dv, w.causal, w.window_left,
+                           det, lq is not None)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    C.log(f"surface case {name} deterministic={det}")
+    lib.sdpa_bwd_ex(tq, tk, tv, to, tdo, tlse, *outs, scale=w.softmax_scale, causal=w.causal,
+                    window_left=w.window_left, deterministic=det, seq_q_lens=tlq,
+                    seq_kv_lens=tlkv, causal_bottom_right=br, window_right=wr, workspace=ws)
+    torch.cuda.synchronize()
+    got = [C.bf16_tensor_to_f32(x) for x in outs]
+    for tname, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        C.assert_close(f"{name} {'det' if det else 'atomic'} {tname}", g, r)
