@@ -507,6 +507,8 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
       }
 
       // ---- GEMM3 (dV^T += dO^T P) and GEMM5 (dK^T += Q^T dS) ----------------------------------
+      // (raised wave priority: this MFMA-only phase issues ahead of the other wave's softmax)
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {  // 32 q rows = two 16-deep contraction steps
 #pragma unroll
@@ -531,6 +533,7 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
         }
       }
       schedule_reads_ahead<4 * (C::N_DVT + C::N_DQT), 2 * NKT * (C::N_DVT + C::N_DQT), C::AHEAD>();
+      __builtin_amdgcn_s_setprio(0);
       if constexpr (C::NBUF == 1) {
         lds_barrier();  // every wave is done with the single q-tile buffer
         if (i > i_lo) load_tile(i - 1);
