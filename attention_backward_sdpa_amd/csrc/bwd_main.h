@@ -33,8 +33,8 @@
 //         transposed, of GEMM4.
 //     The q-tile buffers are double-buffered and filled one tile ahead of the compute.
 //   * The wave's V slice is held in registers as the B operand of GEMM2.
-//   * Deterministic route: each lane stores its bf16 dS values straight from registers (512
-//     contiguous bytes per instruction); no LDS round trip.
+//   * Deterministic route: each lane stores its bf16 dS values straight from registers as 8-byte
+//     quads (512 contiguous bytes per instruction, non-temporal); no LDS round trip.
 //   * fp32-atomic route: dS is written to LDS in the same register order and GEMM4 reads it (and
 //     K) with ds_read_b64_tr_b16.  GEMM4 of q tile i runs at the start of the next iteration so
 //     its atomics drain while that iteration computes.
@@ -156,17 +156,22 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // transpose reads conflict-free; a linear 16-lane row read stays a permutation of one row.
 __device__ __forceinline__ constexpr int kswz(int row, int frag) { return (row >> 1) + 2 * (frag & 1); }
 
+// Element offset (in the row-major source) of the 16 bytes this lane contributes to fragment f.
+template <int D, bool SWZ>
+__device__ __forceinline__ int frag_src_elem(int f, int row0, int rows_valid, int lane) {
+  const int rt = f / (D / 16), t = f % (D / 16);
+  int n = lane;
+  if constexpr (SWZ) n = (lane & 48) | ((lane & 15) ^ (4 * kswz(lane >> 4, f)));
+  int row = row0 + 32 * rt + (n & 31);
+  row = row < rows_valid ? row : rows_valid - 1;
+  return row * D + 16 * t + 8 * (n >> 5);
+}
+
 template <int D, int NW, bool SWZ = false>
 __device__ __forceinline__ void gather_frags(rsrc_t src, int row0, int rows_valid, int nfrag,
                                              char* lds, int w, int lane) {
-  for (int f = w; f < nfrag; f += NW) {
-    const int rt = f / (D / 16), t = f % (D / 16);
-    int n = lane;
-    if constexpr (SWZ) n = (lane & 48) | ((lane & 15) ^ (4 * kswz(lane >> 4, f)));
-    int row = row0 + 32 * rt + (n & 31);
-    row = row < rows_valid ? row : rows_valid - 1;
-    dma16(src, (uint32_t)(row * D + 16 * t + 8 * (n >> 5)) * 2, lds + f * 1024);
-  }
+  for (int f = w; f < nfrag; f += NW)
+    dma16(src, (uint32_t)frag_src_elem<D, SWZ>(f, row0, rows_valid, lane) * 2, lds + f * 1024);
 }
 
 // Byte offset of this lane's 16-byte chunk in a linear read of swizzled fragment f (f's parity
@@ -492,12 +497,15 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
 
         // dS of this 32-key tile as 2 KiB of quads (see ds_store_off)
         if constexpr (C::DET) {
+          // streaming stores (read once, by the dQ kernel): written past the last-level cache
+          // while this kernel computes, rather than evicted dirty during the dQ kernel's reads
           char* wsb = reinterpret_cast<char*>(
               p.ds_ws + (((int64_t)bh * p.n_kv_tiles + j) * n_q_tiles + i) * (BC * BR));
 #pragma unroll
           for (int x = 0; x < 4; ++x)
-            *reinterpret_cast<u32x2*>(wsb + (w * NKT + kt) * 2048 + ds_store_off(lane, x)) =
-                u32x2{sb[kt][2 * x], sb[kt][2 * x + 1]};
+            __builtin_nontemporal_store(
+                u32x2{sb[kt][2 * x], sb[kt][2 * x + 1]},
+                reinterpret_cast<u32x2*>(wsb + (w * NKT + kt) * 2048 + ds_store_off(lane, x)));
         } else {
 #pragma unroll
           for (int x = 0; x < 4; ++x)

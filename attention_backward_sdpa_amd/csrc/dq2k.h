@@ -5,15 +5,20 @@
 // atomics and a fixed order per q tile, so the result is bitwise reproducible.
 //
 // The pass streams the dS workspace once from HBM, so it is bound by how many bytes are in flight:
-//   * a workgroup of NW waves owns NW consecutive q tiles of one head, so every 64-key chunk of K
-//     (re-read from L2) serves 32 * NW query rows (NW = 8 at head dim <= 128: two waves per SIMD
-//     hide each other's LDS latency; NW = 4 above, where the accumulators are twice as large);
-//   * chunks are staged through LDS with LDS-DMA buffer loads, NSTAGE deep (3 or 4), so up to
-//     NSTAGE - 1 chunks of dS (4 KiB per q tile) are in flight per workgroup while one is consumed.
-// The workspace holds each stored (KV tile, q tile) block as 2 KiB dS quads per 32 keys (layout in
-// bwd_main.h), so any 64 consecutive keys of a block are one contiguous 4 KiB piece.  dS and K (as
-// swizzled GEMM1 fragments) are read as MFMA operands with the transpose instruction, which the
-// quad rotation and the K swizzle keep free of bank conflicts.
+//   * each wave loads its own q tile's dS straight into registers (the workspace holds each stored
+//     (KV tile, q tile) block as 2 KiB quads per 32 keys, layout in bwd_main.h, so 64 consecutive
+//     keys are one contiguous 4 KiB piece, four 16-byte non-temporal loads per lane), AHEAD chunks
+//     ahead of its MFMAs: 8 waves x AHEAD x 4 KiB in flight per workgroup, with no shared LDS space
+//     or barrier spent on dS.  Just before use the wave writes the chunk to its own 4 KiB LDS area
+//     and reads it back transposed (ds_read_b64_tr_b16) as the A operand; the quad rotation keeps
+//     both conflict-free;
+//   * K is the only shared operand.  A workgroup of 8 waves owns 8 consecutive q tiles of one head,
+//     so every 64-key chunk of K (as swizzled GEMM1 fragments, re-read from L2) serves 256 query
+//     rows.  Each wave loads its share of a chunk into registers KR chunks early and writes it to
+//     one of two LDS buffers at the end of the previous chunk; one barrier per chunk.  K is read
+//     as the B operand with the transpose instruction, conflict-free under the swizzle;
+//   * every load is an ordinary load, so the compiler's own vmcnt waits are exact.  Loads past the
+//     group's last chunk re-read that chunk (L2 hits) so the pipeline has no conditional loads.
 #pragma once
 #include "bwd_main.h"
 
@@ -31,56 +36,31 @@ struct Dq2kParams {
   float scale;
 };
 
-template <int DQK_, int BC_, int NW_>
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
+
+template <int DQK_, int BC_>
 struct Dq2kCfg {
-  static constexpr int DQK = DQK_, BC = BC_, NW = NW_;
+  static constexpr int DQK = DQK_, BC = BC_, NW = 8;
   static constexpr int BR = 32, NT = NW * 64, KC = 64;       // KC: keys per chunk
   static constexpr int QT = NW;                              // q tiles per workgroup, one per wave
   static constexpr int N_DT = DQK / 32;                      // 32-column d tiles per wave
-  static constexpr int ST_BYTES = KC * BR * 2;               // 4 KiB of dS per q tile and chunk
-  static constexpr int DS_BYTES = QT * ST_BYTES;
+  static constexpr int STEPS = KC / 16;                      // MFMA key steps per chunk
+  static constexpr int DS_LOADS = KC * BR * 2 / 1024;        // 16-byte loads per lane and chunk
   static constexpr int K_FRAGS = (KC / 32) * (DQK / 16);     // K fragments of one chunk
-  static constexpr int STAGE_BYTES = DS_BYTES + K_FRAGS * 1024;
-  static constexpr int NSTAGE_FIT = (160 * 1024) / STAGE_BYTES;
-  static constexpr int NSTAGE = NSTAGE_FIT < 4 ? NSTAGE_FIT : 4;
-  static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
-  // LDS-DMA instructions each wave issues per stage (the same for every stage and wave, so "all
-  // but the newest k stages have landed" is a constant vmcnt)
-  static constexpr int DS_PER_WAVE = DS_BYTES / 1024 / NW;
+  static constexpr int K_BYTES = K_FRAGS * 1024;
   static constexpr int K_PER_WAVE = K_FRAGS / NW;
-  static constexpr int OPS_PER_STAGE = DS_PER_WAVE + K_PER_WAVE;
+  // chunks of dS in flight per wave, and of K held in registers (fewer at head dim 256, where the
+  // 128 accumulator registers leave less room)
+  static constexpr int AHEAD = DQK > 192 ? 3 : 4;
+  static constexpr int KR = DQK > 192 ? 2 : 3;
+  static constexpr int UNROLL = lcm_c(lcm_c(AHEAD, KR), 2);  // ring slots and LDS buffer constant
+  static constexpr int OFF_DS = 2 * K_BYTES;                 // per-wave dS transpose areas
+  static constexpr int LDS_BYTES = OFF_DS + NW * KC * BR * 2;
   static_assert(BC % KC == 0, "whole chunks per KV tile");
-  static_assert((DS_BYTES / 1024) % NW == 0 && K_FRAGS % NW == 0, "even DMA split over waves");
-  static_assert(NSTAGE >= 2 && LDS_BYTES <= 160 * 1024, "LDS budget");
-  static_assert((NSTAGE - 2) * OPS_PER_STAGE < 64, "vmcnt range");
+  static_assert(K_FRAGS % NW == 0, "even K split over waves");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
-
-// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left alone (gfx9 encoding: vmcnt bits [3:0] and [15:14])
-template <int N>
-__device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
-// Wait until at most `ahead` stages of OPS LDS-DMA instructions, issued after the stage about to
-// be consumed, are still in flight (ahead <= MAXA <= 2).
-template <int OPS, int MAXA>
-__device__ __forceinline__ void wait_stage(int ahead) {
-  static_assert(MAXA <= 2, "at most two stages ahead");
-  if constexpr (MAXA >= 2) {
-    if (ahead >= 2) {
-      wait_vmem_le<2 * OPS>();
-      return;
-    }
-  }
-  if constexpr (MAXA >= 1) {
-    if (ahead >= 1) {
-      wait_vmem_le<OPS>();
-      return;
-    }
-  }
-  wait_vmem_le<0>();
-}
 
 template <class C>
 __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
@@ -88,7 +68,7 @@ __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
   using acc_t = M::acc_t;
   constexpr int BR = C::BR, BC = C::BC, DQK = C::DQK, KC = C::KC, QT = C::QT;
   constexpr int CPT = BC / KC;  // chunks per KV tile
-  constexpr int PIECES = C::ST_BYTES / 1024;
+  constexpr int AHEAD = C::AHEAD, KR = C::KR, U = C::UNROLL;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -113,26 +93,38 @@ __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
 
   // Chunk range [cf, ce) of each q tile of the group: the KV tiles whose stored band contains the
   // tile form one contiguous run (both ends of q_tile_range are non-decreasing in the KV tile
-  // index); chunks that start past the keys hold only zeros and are skipped.
+  // index); chunks that start past the keys hold only zeros and are skipped.  The lanes evaluate
+  // 64 KV tiles at a time and a ballot per q tile picks the run's ends (a per-tile scalar loop
+  // would cost every wave thousands of scalar instructions on the CU's shared scalar unit).
   const int c_keys = (p.Skv + KC - 1) / KC;
+  int j_first[QT], j_last[QT];
+#pragma unroll
+  for (int x = 0; x < QT; ++x) {
+    j_first[x] = p.n_kv_tiles;
+    j_last[x] = -1;
+  }
+  for (int jb = 0; jb < p.n_kv_tiles; jb += 64) {
+    const int j = jb + lane;
+    int lo = 0, hi = -1;
+    if (j < p.n_kv_tiles) q_tile_range(mg, j * BC, BC, BR, &lo, &hi);
+#pragma unroll
+    for (int x = 0; x < QT; ++x) {
+      const int i = i0 + x;
+      const uint64_t m = __ballot(i < p.n_q_tiles && lo <= i && i <= hi);
+      if (m != 0) {
+        const int f = jb + __ffsll((unsigned long long)m) - 1;
+        const int l = jb + 63 - __clzll((long long)m);
+        j_first[x] = f < j_first[x] ? f : j_first[x];
+        j_last[x] = l;
+      }
+    }
+  }
   int cf[QT], ce[QT];
   int c_lo = 0x7fffffff, c_hi = 0;
 #pragma unroll
   for (int x = 0; x < QT; ++x) {
-    const int i = i0 + x;
-    int j_first = p.n_kv_tiles, j_last = -1;
-    if (i < p.n_q_tiles) {
-      for (int j = 0; j < p.n_kv_tiles; ++j) {
-        int lo, hi;
-        q_tile_range(mg, j * BC, BC, BR, &lo, &hi);
-        if (lo <= i && i <= hi) {
-          j_first = j < j_first ? j : j_first;
-          j_last = j;
-        }
-      }
-    }
-    cf[x] = j_first * CPT;
-    ce[x] = (j_last + 1) * CPT < c_keys ? (j_last + 1) * CPT : c_keys;
+    cf[x] = j_first[x] * CPT;
+    ce[x] = (j_last[x] + 1) * CPT < c_keys ? (j_last[x] + 1) * CPT : c_keys;
     if (cf[x] < ce[x]) {
       c_lo = cf[x] < c_lo ? cf[x] : c_lo;
       c_hi = ce[x] > c_hi ? ce[x] : c_hi;
@@ -140,61 +132,79 @@ __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
   }
   const int my_first = cf[w], my_end = ce[w];
 
-  const bf16_t* wsh = p.ds_ws + (int64_t)bh * p.n_kv_tiles * p.n_q_tiles * (BC * BR);
+  // this wave's q tile (clamped: a wave past the last q tile loads a valid block it never uses)
+  const int my_tile = (i0 + w) < p.n_q_tiles ? (i0 + w) : (p.n_q_tiles - 1);
+  const char* wsq = reinterpret_cast<const char*>(
+                        p.ds_ws + ((int64_t)bh * p.n_kv_tiles * p.n_q_tiles + my_tile) * (BC * BR)) +
+                    lane * 16;
   const bf16_t* Kb = p.k + (int64_t)(b * p.Hkv + kvh) * p.Skv * DQK;
-  const rsrc_t rK = buf_rsrc(Kb, (int64_t)p.Skv * DQK * 2);
-
-  // Stage of chunk c: the 4 KiB dS pieces of the group's q tiles, then the K fragments.  Every
-  // wave issues the same number of DMA instructions for every stage: a piece of a q tile that does
-  // not cover chunk c (or lies past the last q tile) is still read, from an allocated block of the
-  // same head, and never consumed.
-  auto load_stage = [&](int c, int s) {
-    char* base = smem + s * C::STAGE_BYTES;
-    const int j = c / CPT, part = c % CPT;
-#pragma unroll
-    for (int u = 0; u < C::DS_PER_WAVE; ++u) {
-      const int f = w + u * C::NW;  // 1 KiB piece f of the stage's dS area
-      const int x = f / PIECES;
-      const int tile = (i0 + x) < p.n_q_tiles ? (i0 + x) : (p.n_q_tiles - 1);
-      const bf16_t* blk = wsh + ((int64_t)j * p.n_q_tiles + tile) * (BC * BR) + part * (KC * BR);
-      dma16(buf_rsrc(blk, C::ST_BYTES), (uint32_t)(f % PIECES) * 1024 + lane * 16,
-            base + f * 1024);
-    }
-    gather_frags<DQK, C::NW, true>(rK, c * KC, p.Skv, C::K_FRAGS, base + C::DS_BYTES, w, lane);
-  };
 
   const Gemm4Lanes tl(lane);
   acc_t acc[C::N_DT];
 #pragma unroll
   for (int t = 0; t < C::N_DT; ++t) acc[t] = acc_t{};
 
-  if (c_lo < c_hi) {
+  const int n = c_hi - c_lo;  // chunks of the group (uniform over the workgroup)
+  if (n > 0) {
+    // chunk r (relative to c_lo; loads past the end re-read the last chunk)
+    // (the rings hold raw 32-bit words: kept as bf16 vectors across the loop, the compiler splits
+    // them into 16-bit halves, which waits for every outstanding load)
+    auto load_ds = [&](int r, u32x4 (&dst)[C::DS_LOADS]) {
+      const int c = c_lo + (r < n ? r : n - 1);
+      const char* src = wsq + ((int64_t)(c / CPT) * p.n_q_tiles * (BC * BR) + (c % CPT) * (KC * BR)) * 2;
 #pragma unroll
-    for (int s = 0; s < C::NSTAGE - 1; ++s)
-      if (c_lo + s < c_hi) load_stage(c_lo + s, s);
-    // chunk c sits in stage (c - c_lo) % NSTAGE; unrolled by NSTAGE so every stage offset is a
-    // constant and the compiler can tell the stage being read from the ones being filled
-    for (int cb = c_lo; cb < c_hi; cb += C::NSTAGE) {
+      for (int s = 0; s < C::DS_LOADS; ++s)
+        dst[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + s * 1024));
+    };
+    auto load_k = [&](int r, u32x4 (&dst)[C::K_PER_WAVE]) {
+      const int c = c_lo + (r < n ? r : n - 1);
 #pragma unroll
-      for (int u = 0; u < C::NSTAGE; ++u) {
-        const int c = cb + u;
-        if (c >= c_hi) break;
-        // stages this wave issued after chunk c: min(NSTAGE - 2, c_hi - 1 - c)
-        const int ahead = (c_hi - 1 - c) < (C::NSTAGE - 2) ? (c_hi - 1 - c) : (C::NSTAGE - 2);
-        wait_stage<C::OPS_PER_STAGE, C::NSTAGE - 2>(ahead);
-        lds_barrier();  // chunk c landed for every wave; every wave is done with chunk c - 1
-        if (c + C::NSTAGE - 1 < c_hi) load_stage(c + C::NSTAGE - 1, (u + C::NSTAGE - 1) % C::NSTAGE);
+      for (int u = 0; u < C::K_PER_WAVE; ++u)
+        dst[u] = *reinterpret_cast<const u32x4*>(
+            Kb + frag_src_elem<DQK, true>(w + u * C::NW, c * KC, p.Skv, lane));
+    };
+    auto store_k = [&](const u32x4 (&src)[C::K_PER_WAVE], int buf) {
+#pragma unroll
+      for (int u = 0; u < C::K_PER_WAVE; ++u)
+        *reinterpret_cast<u32x4*>(smem + buf * C::K_BYTES + (w + u * C::NW) * 1024 + lane * 16) =
+            src[u];
+    };
+
+    u32x4 dsr[AHEAD][C::DS_LOADS];
+    char* sdS = smem + C::OFF_DS + w * (KC * BR * 2);  // this wave's transpose area
+    u32x4 kr[KR][C::K_PER_WAVE];
+    load_k(0, kr[0]);
+#pragma unroll
+    for (int a = 0; a < AHEAD; ++a) load_ds(a, dsr[a]);
+    store_k(kr[0], 0);
+#pragma unroll
+    for (int a = 1; a <= KR; ++a) load_k(a, kr[a % KR]);
+    lds_barrier();  // K chunk 0 in buffer 0
+
+    for (int rb = 0; rb < n; rb += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = rb + u;
+        if (r >= n) break;
+        const int c = c_lo + r;
         if (my_first <= c && c < my_end) {
-          const char* sST = smem + u * C::STAGE_BYTES + w * C::ST_BYTES;
-          const char* sK = smem + u * C::STAGE_BYTES + C::DS_BYTES;
+          const char* sK = smem + (u & 1) * C::K_BYTES;
 #pragma unroll
-          for (int t = 0; t < KC / 16; ++t) {
-            const bf16x8 a = tl.ds(sST, t);
+          for (int s = 0; s < C::DS_LOADS; ++s)
+            *reinterpret_cast<u32x4*>(sdS + s * 1024 + lane * 16) = dsr[u % AHEAD][s];
 #pragma unroll
-            for (int dt = 0; dt < C::N_DT; ++dt)
-              acc[dt] = M::mma(a, tl.template k<DQK>(sK, t, dt), acc[dt]);
+          for (int s = 0; s < C::STEPS; ++s) {
+            const bf16x8 a = tl.ds(sdS, s);
+#pragma unroll
+            for (int dt = 0; dt < C::N_DT; ++dt) acc[dt] = M::mma(a, tl.template k<DQK>(sK, s, dt), acc[dt]);
           }
         }
+        load_ds(r + AHEAD, dsr[u % AHEAD]);
+        // K of chunk r + 1 into the other buffer (every wave finished reading it before the last
+        // barrier), then refill its register slot
+        store_k(kr[(u + 1) % KR], (u + 1) & 1);
+        load_k(r + 1 + KR, kr[(u + 1) % KR]);
+        lds_barrier();
       }
     }
   }

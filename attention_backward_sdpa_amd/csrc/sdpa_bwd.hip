@@ -145,9 +145,9 @@ hipError_t run_main(int Dqk, int Dv, const MainParams& mp, int det, int grid, in
   return dispatch_main<256, 256, 32, 4>(mp, det, grid, bc, s);
 }
 
-template <int DQK, int BC, int NW>
+template <int DQK, int BC>
 hipError_t dispatch_dq2k(const Dq2kParams& dp, int bc, hipStream_t s) {
-  using C = Dq2kCfg<DQK, BC, NW>;
+  using C = Dq2kCfg<DQK, BC>;
   if (BC != bc) return hipErrorInvalidValue;  // must read the dS blocks the main kernel wrote
   // one workgroup per group of C::QT consecutive q tiles of one (batch, query head)
   const int64_t grid = (int64_t)((dp.n_q_tiles + C::QT - 1) / C::QT) * dp.B * dp.Hq;
@@ -156,10 +156,10 @@ hipError_t dispatch_dq2k(const Dq2kParams& dp, int bc, hipStream_t s) {
 }
 
 hipError_t run_dq2k(int Dqk, const Dq2kParams& dp, int bc, hipStream_t s) {
-  if (Dqk == 64) return dispatch_dq2k<64, 256, 8>(dp, bc, s);
-  if (Dqk == 128) return dispatch_dq2k<128, 256, 8>(dp, bc, s);
-  if (Dqk == 192) return dispatch_dq2k<192, 256, 4>(dp, bc, s);
-  return dispatch_dq2k<256, 128, 4>(dp, bc, s);
+  if (Dqk == 64) return dispatch_dq2k<64, 256>(dp, bc, s);
+  if (Dqk == 128) return dispatch_dq2k<128, 256>(dp, bc, s);
+  if (Dqk == 192) return dispatch_dq2k<192, 256>(dp, bc, s);
+  return dispatch_dq2k<256, 128>(dp, bc, s);
 }
 
 hipError_t launch_preprocess(const PreParams& pp, int Dqk, int Dv, int64_t tiles, hipStream_t s) {
