@@ -95,7 +95,7 @@ struct MainCfg {
   static constexpr int OFF_T = OFF_K + SK_BYTES;
   static constexpr int OFF_ST = OFF_T + NBUF * TILE_BYTES;
   static constexpr int LDS_BYTES = OFF_ST + SST_BYTES;
-  static_assert(KPW % 32 == 0, "keys per wave");
+  static_assert(KPW == 32, "one 32-key MFMA tile per wave (the q-tile loop body assumes it)");
   static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
   static_assert(DQK % 64 == 0 && DV % 64 == 0, "head dims must be multiples of 64");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -261,17 +261,17 @@ struct KeyRows {
   }
 };
 
-// Softmax replay and dS for one 32-key MFMA tile of this lane's key column:
-// P = exp2(S * scale * log2e - LSE * log2e) (0 on masked pairs, edge tiles only), dS =
-// P * (dP - delta); both are packed to bf16 pairs in accumulator order (pb/sb[v/2] holds registers
-// v, v+1).
-template <bool MASK>
+// Softmax replay and dS for one 32-key MFMA tile of this lane's key column, accumulator groups
+// X0 and X0 + 1 (the q rows of contraction step X0 / 2 of GEMM3/GEMM5):
+// P = exp2(S * scale * log2e - LSE * log2e), dS = P * (dP - delta); both are packed to bf16 pairs
+// in accumulator order (pb/sb[v/2] holds registers v, v+1).  No masking here: on edge tiles
+// mask_pairs clears the invisible pairs afterwards.
+template <int X0>
 __device__ __forceinline__ void softmax_ds(const floatx16& S, const floatx16& dP,
                                            const float* sStat, int g, float scale_log2,
-                                           const KeyRows& vis, uint32_t (&pb)[8],
-                                           uint32_t (&sb)[8]) {
+                                           uint32_t (&pb)[8], uint32_t (&sb)[8]) {
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
+  for (int x = X0; x < X0 + 2; ++x) {
     // rows of accumulator registers 4x..4x+3 of this lane: g*4 + 8x + 0..3
     const floatx4 a = *reinterpret_cast<const floatx4*>(sStat + 2 * (g * 4 + 8 * x));
     const floatx4 c = *reinterpret_cast<const floatx4*>(sStat + 2 * (g * 4 + 8 * x) + 4);
@@ -280,13 +280,8 @@ __device__ __forceinline__ void softmax_ds(const floatx16& S, const floatx16& dP
     float pv[4], dv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * x + e], scale_log2, -l4[e]));
-      if constexpr (MASK) {
-        const int c = 8 * x + e;  // row offset of this register from q_lane
-        if (c < vis.lo || c > vis.hi) pe = 0.f;
-      }
-      pv[e] = pe;
-      dv[e] = pe * (dP[4 * x + e] - d4[e]);
+      pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * x + e], scale_log2, -l4[e]));
+      dv[e] = pv[e] * (dP[4 * x + e] - d4[e]);
     }
     pb[2 * x] = pack_bf16x2(pv[0], pv[1]);
     pb[2 * x + 1] = pack_bf16x2(pv[2], pv[3]);
@@ -294,6 +289,36 @@ __device__ __forceinline__ void softmax_ds(const floatx16& S, const floatx16& dP
     sb[2 * x + 1] = pack_bf16x2(dv[2], dv[3]);
   }
 }
+
+// Visible rows of this lane's key among its accumulator rows, as a 32-bit mask over the row
+// offset c = 8 x + e from the lane's first row (KeyRows gives the visible offsets [lo, hi]).
+__device__ __forceinline__ uint32_t visible_rows(const KeyRows& vis) {
+  const int lo = vis.lo > 0 ? vis.lo : 0;
+  const int hi = vis.hi < 31 ? vis.hi : 31;
+  if (lo > hi) return 0u;
+  return ((2u << hi) - 1u) & ~((1u << lo) - 1u);
+}
+
+// Edge tiles: clear the packed P / dS of invisible pairs in accumulator groups X0, X0 + 1 (their
+// unmasked replay may be anything, even inf or NaN; the result is exactly 0).
+template <int X0>
+__device__ __forceinline__ void mask_pairs(uint32_t m, uint32_t (&pb)[8], uint32_t (&sb)[8]) {
+#pragma unroll
+  for (int x = X0; x < X0 + 2; ++x) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = 8 * x + 2 * h;  // rows c, c + 1 in the two halves of the word
+      const uint32_t keep = (((m >> c) & 1u) * 0x0000FFFFu) | (((m >> (c + 1)) & 1u) * 0xFFFF0000u);
+      pb[2 * x + h] &= keep;
+      sb[2 * x + h] &= keep;
+    }
+  }
+}
+
+template <int V>
+struct IntTag {
+  static constexpr int value = V;
+};
 
 // Per-lane offsets of the GEMM3 / GEMM5 A operands, dO^T and Q^T (rows d, contraction over the
 // tile's 32 q rows), read with ds_read_b64_tr_b16 straight from the swizzled A fragments of GEMM1 /
@@ -465,82 +490,76 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
         }
       }
 
-      // ---- per 32-key tile: GEMM1, GEMM2, softmax replay, dS -------------------------------------
-      // (one key tile at a time keeps only one S/dP pair live, leaving registers for operand
-      // prefetch; the Q and dO fragments are re-read from LDS for the second key tile)
+      // ---- the wave's 32 keys: GEMM1, GEMM2, softmax replay, dS, GEMM3, GEMM5 --------------------
       const bool edge = tile_needs_mask(mg, q0, BR, k0, BC);
-      uint32_t pb[NKT][8], sb[NKT][8];
+      acc_t S = acc_t{}, dP = acc_t{};
+      // GEMM1 and GEMM2 are independent chains: alternate them so neither waits on the other's
+      // accumulator, and keep the operand reads a few MFMAs ahead of their use
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
-        acc_t S = acc_t{}, dP = acc_t{};
-        // GEMM1 and GEMM2 are independent chains: alternate them so neither waits on the other's
-        // accumulator, and keep the operand reads a few MFMAs ahead of their use
-#pragma unroll
-        for (int t = 0; t < (C::N_KQ > C::N_KV ? C::N_KQ : C::N_KV); ++t) {
-          if (t < C::N_KQ) {
-            const bf16x8 a = lds_read_b128(T + C::T_QA, t * 1024 + kofs[t & 1]);
-            if constexpr (C::KREG) {
-              S = M::mma(a, kreg[kt][t], S);
-            } else {
-              S = M::mma(a, lds_read_b128(sK, ((w * NKT + kt) * C::N_KQ + t) * 1024 + kofs[t & 1]), S);
-            }
+      for (int t = 0; t < (C::N_KQ > C::N_KV ? C::N_KQ : C::N_KV); ++t) {
+        if (t < C::N_KQ) {
+          const bf16x8 a = lds_read_b128(T + C::T_QA, t * 1024 + kofs[t & 1]);
+          if constexpr (C::KREG) {
+            S = M::mma(a, kreg[0][t], S);
+          } else {
+            S = M::mma(a, lds_read_b128(sK, (w * C::N_KQ + t) * 1024 + kofs[t & 1]), S);
           }
-          if (t < C::N_KV)
-            dP = M::mma(lds_read_b128(T + C::T_OA, t * 1024 + kofs[t & 1]), vreg[kt][t], dP);
         }
-        schedule_reads_ahead<(C::KREG ? 1 : 2) * C::N_KQ + C::N_KV, C::N_KQ + C::N_KV, C::AHEAD>();
-        if (edge)
-          softmax_ds<true>(S, dP, sStat, g, p.scale_log2,
-                           KeyRows(mg, q0 + g * 4, key_lane + kt * 32), pb[kt], sb[kt]);
-        else
-          softmax_ds<false>(S, dP, sStat, g, p.scale_log2, KeyRows(), pb[kt], sb[kt]);
-
-        // dS of this 32-key tile as 2 KiB of quads (see ds_store_off)
-        if constexpr (C::DET) {
-          // streaming stores (read once, by the dQ kernel): written past the last-level cache
-          // while this kernel computes, rather than evicted dirty during the dQ kernel's reads
-          char* wsb = reinterpret_cast<char*>(
-              p.ds_ws + (((int64_t)bh * p.n_kv_tiles + j) * n_q_tiles + i) * (BC * BR));
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            __builtin_nontemporal_store(
-                u32x2{sb[kt][2 * x], sb[kt][2 * x + 1]},
-                reinterpret_cast<u32x2*>(wsb + (w * NKT + kt) * 2048 + ds_store_off(lane, x)));
-        } else {
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            *reinterpret_cast<u32x2*>(sST + (w * NKT + kt) * 2048 + ds_store_off(lane, x)) =
-                u32x2{sb[kt][2 * x], sb[kt][2 * x + 1]};
-        }
+        if (t < C::N_KV)
+          dP = M::mma(lds_read_b128(T + C::T_OA, t * 1024 + kofs[t & 1]), vreg[0][t], dP);
       }
+      schedule_reads_ahead<(C::KREG ? 1 : 2) * C::N_KQ + C::N_KV, C::N_KQ + C::N_KV, C::AHEAD>();
 
-      // ---- GEMM3 (dV^T += dO^T P) and GEMM5 (dK^T += Q^T dS) ----------------------------------
+      // GEMM3 (dV^T += dO^T P) and GEMM5 (dK^T += Q^T dS), contraction step tb over q rows
+      // 16 tb .. 16 tb + 15, whose P / dS come from accumulator groups 2 tb and 2 tb + 1
+      // (the step index is a type so the P / dS register indices are constants)
+      uint32_t pb[8], sb[8];
+      auto gemm35_step = [&](auto tb_tag) __attribute__((always_inline)) {
+        constexpr int tb = decltype(tb_tag)::value;
+#pragma unroll
+        for (int dt = 0; dt < C::N_DVT; ++dt)
+          accV[dt][0] = M::mma(tra.read(T + C::T_OA, dt, tb),
+                               __builtin_bit_cast(bf16x8, u32x4{pb[4 * tb], pb[4 * tb + 1],
+                                                                pb[4 * tb + 2], pb[4 * tb + 3]}),
+                               accV[dt][0]);
+#pragma unroll
+        for (int dt = 0; dt < C::N_DQT; ++dt)
+          accK[dt][0] = M::mma(tra.read(T + C::T_QA, dt, tb),
+                               __builtin_bit_cast(bf16x8, u32x4{sb[4 * tb], sb[4 * tb + 1],
+                                                                sb[4 * tb + 2], sb[4 * tb + 3]}),
+                               accK[dt][0]);
+      };
+      // Softmax replay of all 32 rows, unmasked and branch-free; edge tiles then clear their
+      // invisible pairs in the packed words (keeping the masking out of the block the MFMA
+      // accumulators flow through avoids register copies at the join).
+      softmax_ds<0>(S, dP, sStat, g, p.scale_log2, pb, sb);
+      softmax_ds<2>(S, dP, sStat, g, p.scale_log2, pb, sb);
+      if (edge) {
+        const uint32_t vis_m = visible_rows(KeyRows(mg, q0 + g * 4, key_lane));
+        mask_pairs<0>(vis_m, pb, sb);
+        mask_pairs<2>(vis_m, pb, sb);
+      }
+      // dS of the wave's 32 keys as 2 KiB of quads (see ds_store_off)
+      if constexpr (C::DET) {
+        // streaming stores (read once, by the dQ kernel): written past the last-level cache
+        // while this kernel computes, rather than evicted dirty during the dQ kernel's reads
+        char* wsb = reinterpret_cast<char*>(
+            p.ds_ws + (((int64_t)bh * p.n_kv_tiles + j) * n_q_tiles + i) * (BC * BR));
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          __builtin_nontemporal_store(u32x2{sb[2 * x], sb[2 * x + 1]},
+                                      reinterpret_cast<u32x2*>(wsb + w * 2048 + ds_store_off(lane, x)));
+      } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          *reinterpret_cast<u32x2*>(sST + w * 2048 + ds_store_off(lane, x)) =
+              u32x2{sb[2 * x], sb[2 * x + 1]};
+      }
       // (raised wave priority: this MFMA-only phase issues ahead of the other wave's softmax)
       __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {  // 32 q rows = two 16-deep contraction steps
-#pragma unroll
-        for (int dt = 0; dt < C::N_DVT; ++dt) {
-          const bf16x8 a = tra.read(T + C::T_OA, dt, tb);
-#pragma unroll
-          for (int kt = 0; kt < NKT; ++kt) {
-            const bf16x8 bP = __builtin_bit_cast(
-                bf16x8, u32x4{pb[kt][4 * tb], pb[kt][4 * tb + 1], pb[kt][4 * tb + 2], pb[kt][4 * tb + 3]});
-            accV[dt][kt] = M::mma(a, bP, accV[dt][kt]);
-          }
-        }
-#pragma unroll
-        for (int dt = 0; dt < C::N_DQT; ++dt) {
-          const bf16x8 a = tra.read(T + C::T_QA, dt, tb);
-#pragma unroll
-          for (int kt = 0; kt < NKT; ++kt) {
-            const bf16x8 bS = __builtin_bit_cast(
-                bf16x8, u32x4{sb[kt][4 * tb], sb[kt][4 * tb + 1], sb[kt][4 * tb + 2], sb[kt][4 * tb + 3]});
-            accK[dt][kt] = M::mma(a, bS, accK[dt][kt]);
-          }
-        }
-      }
-      schedule_reads_ahead<4 * (C::N_DVT + C::N_DQT), 2 * NKT * (C::N_DVT + C::N_DQT), C::AHEAD>();
+      gemm35_step(IntTag<0>{});
+      gemm35_step(IntTag<1>{});
+      schedule_reads_ahead<4 * (C::N_DVT + C::N_DQT), 2 * (C::N_DVT + C::N_DQT), C::AHEAD>();
       __builtin_amdgcn_s_setprio(0);
       if constexpr (C::NBUF == 1) {
         lds_barrier();  // every wave is done with the single q-tile buffer

@@ -162,6 +162,14 @@ hipError_t run_dq2k(int Dqk, const Dq2kParams& dp, int bc, hipStream_t s) {
   return dispatch_dq2k<256, 128>(dp, bc, s);
 }
 
+hipError_t launch_convert(const ConvertParams& cp, int Dqk, int grid, hipStream_t s) {
+  if (Dqk == 64) hipLaunchKernelGGL((dq_convert_kernel<64>), dim3(grid), dim3(256), 0, s, cp);
+  else if (Dqk == 128) hipLaunchKernelGGL((dq_convert_kernel<128>), dim3(grid), dim3(256), 0, s, cp);
+  else if (Dqk == 192) hipLaunchKernelGGL((dq_convert_kernel<192>), dim3(grid), dim3(256), 0, s, cp);
+  else hipLaunchKernelGGL((dq_convert_kernel<256>), dim3(grid), dim3(256), 0, s, cp);
+  return hipGetLastError();
+}
+
 hipError_t launch_preprocess(const PreParams& pp, int Dqk, int Dv, int64_t tiles, hipStream_t s) {
   if (tiles == 0) return hipSuccess;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
@@ -303,10 +311,17 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   rec(3);
 
   if (!det) {
-    const int64_t n8 = (int64_t)B * Hq * Sq * Dqk / 8;
-    hipLaunchKernelGGL(dq_convert_kernel, dim3(grid_stride_blocks(n8)), dim3(256), 0, stream,
-                       dq_accum, (bf16_t*)dq, n8, scale);
-    if (hipGetLastError() != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
+    ConvertParams cp;
+    cp.acc = dq_accum;
+    cp.dq = (bf16_t*)dq;
+    cp.seq_q_lens = seq_q_lens;
+    cp.Hq = Hq;
+    cp.Sq = Sq;
+    cp.scale = scale;
+    const int64_t cgrid = (int64_t)B * Hq * ((Sq + 31) / 32);
+    if (cgrid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
+    e = launch_convert(cp, Dqk, (int)cgrid, stream);
+    if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   } else {
     Dq2kParams dp;
     dp.ds_ws = mp.ds_ws;

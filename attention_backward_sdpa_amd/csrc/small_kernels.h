@@ -13,7 +13,9 @@ namespace sdpa {
 //     batch entry's query length, rows past the buffer and rows whose LSE is -inf (no visible key
 //     in the forward) get [+inf, 0], so the main kernel replays P = 0 for them without a NaN.
 //     The row's Dv/8 lanes reduce with butterfly shuffles in a fixed order (deterministic).
-//   * when zero_rows is set, the tile's rows of the fp32 dQ accumulator are cleared.
+//   * when zero_rows is set, the tile's rows of the fp32 dQ accumulator below the batch entry's
+//     query length are cleared (the main kernel adds into no other row, and the convert kernel
+//     writes the rest of dQ as zeros without reading them).  O and dO are read only for those rows.
 struct PreParams {
   const bf16_t* o;
   const bf16_t* dO;
@@ -36,14 +38,14 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
   const int i = blockIdx.x % nt;
   const int q0 = i * BR;
   const int b = (int)(bh / p.Hq);
-  const int Lq = p.seq_q_lens ? p.seq_q_lens[b] : p.Sq;
+  const int Lq = p.seq_q_lens ? min(max(p.seq_q_lens[b], 0), p.Sq) : p.Sq;
 
   for (int r0 = 0; r0 < BR; r0 += RPP) {
     const int r = r0 + tid / LPR, sub = tid % LPR, s = q0 + r;
-    const bool real = s < p.Sq;
+    const bool live = s < Lq;
     const int64_t row = bh * p.Sq + s;
     float acc = 0.f;
-    if (real) {
+    if (live) {
       const u32x4 a = *reinterpret_cast<const u32x4*>(p.o + row * DV + sub * 8);
       const u32x4 c = *reinterpret_cast<const u32x4*>(p.dO + row * DV + sub * 8);
 #pragma unroll
@@ -55,13 +57,12 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
 #pragma unroll
     for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPR);
     if (sub == 0) {
-      const bool live = real && s < Lq;
       const float l = live ? p.lse[row] : -INFINITY;
       const bool none = !(l > -INFINITY);  // -inf (or NaN) LSE: the row saw no key
       reinterpret_cast<float2*>(p.stats)[bh * p.sq_pad + s] =
           make_float2(none ? INFINITY : l * kLog2e, (live && !none) ? acc : 0.f);
     }
-    if (p.zero_rows && real) {
+    if (p.zero_rows && live) {
       float4* dst = reinterpret_cast<float4*>(p.dq_accum + row * p.Dqk);
       for (int x = sub; x < p.Dqk / 4; x += LPR) dst[x] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -69,17 +70,39 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
 }
 
 // ---- dQ convert ---------------------------------------------------------------------------------
-// dQ = bf16(scale * dq_accum); 8 elements per thread (two 16-byte loads, one 16-byte store).
-__global__ void __launch_bounds__(256) dq_convert_kernel(const float* __restrict__ acc,
-                                                         bf16_t* __restrict__ dq, int64_t n8,
-                                                         float scale) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n8; x += stride) {
-    const floatx4 a = reinterpret_cast<const floatx4*>(acc)[2 * x];
-    const floatx4 c = reinterpret_cast<const floatx4*>(acc)[2 * x + 1];
-    reinterpret_cast<u32x4*>(dq)[x] =
-        u32x4{pack_bf16x2(a[0] * scale, a[1] * scale), pack_bf16x2(a[2] * scale, a[3] * scale),
-              pack_bf16x2(c[0] * scale, c[1] * scale), pack_bf16x2(c[2] * scale, c[3] * scale)};
+// dQ = bf16(scale * dq_accum) for the rows below the batch entry's query length; the other rows
+// (never added into, and not cleared by the preprocess) are written as zeros without reading the
+// accumulator.  One workgroup per 32-row q tile of one (batch, query head); 8 elements per thread
+// and step (two 16-byte loads, one 16-byte store).
+struct ConvertParams {
+  const float* acc;          // (B*Hq, Sq, Dqk)
+  bf16_t* dq;                // (B*Hq, Sq, Dqk)
+  const int* seq_q_lens;
+  int Hq, Sq;
+  float scale;
+};
+
+template <int DQK>
+__global__ void __launch_bounds__(256) dq_convert_kernel(ConvertParams p) {
+  constexpr int V = DQK / 8;  // 8-element vectors per row
+  const int nt = (p.Sq + 31) / 32;
+  const int64_t bh = blockIdx.x / nt;
+  const int q0 = (int)(blockIdx.x % nt) * 32;
+  const int b = (int)(bh / p.Hq);
+  const int Lq = p.seq_q_lens ? min(max(p.seq_q_lens[b], 0), p.Sq) : p.Sq;
+  for (int v = threadIdx.x; v < 32 * V; v += 256) {
+    const int s = q0 + v / V;
+    if (s >= p.Sq) break;
+    const int64_t x = (bh * p.Sq + s) * V + v % V;
+    u32x4 out = u32x4{0u, 0u, 0u, 0u};
+    if (s < Lq) {
+      const floatx4 a = reinterpret_cast<const floatx4*>(p.acc)[2 * x];
+      const floatx4 c = reinterpret_cast<const floatx4*>(p.acc)[2 * x + 1];
+      const float k = p.scale;
+      out = u32x4{pack_bf16x2(a[0] * k, a[1] * k), pack_bf16x2(a[2] * k, a[3] * k),
+                  pack_bf16x2(c[0] * k, c[1] * k), pack_bf16x2(c[2] * k, c[3] * k)};
+    }
+    reinterpret_cast<u32x4*>(p.dq)[x] = out;
   }
 }
 

@@ -99,7 +99,9 @@ int sdpa_bwd_ex_events(const void* q, const void* k, const void* v, const void* 
  * (rows padded to Sq_pad = Sq rounded up to 32 per (b, h)) write the pair
  *     stats[(b*Hq + h)*Sq_pad + s] = { LSE * log2(e),  rowsum(O * dO) in fp32 }
  * and { +inf, 0 } for padding rows, rows at or past seq_q_lens[b] and rows whose LSE is -inf.
- * When dq_accum is not NULL, also zero its B*Hq*Sq*Dqk floats.  stats holds B*Hq*Sq_pad*2
+ * When dq_accum is not NULL, also zero its rows s < seq_q_lens[b] (all Sq rows when seq_q_lens is
+ * NULL), Dqk floats each: the main kernel adds into no other row and the chain writes the other
+ * rows of dQ as zeros without reading them.  stats holds B*Hq*Sq_pad*2
  * floats.  (Dqk, Dv) as for sdpa_bwd; o, dO, stats, dq_accum 16-byte aligned, lse 4-byte
  * aligned. */
 int sdpa_bwd_preprocess(const void* o, const void* dO, const float* lse, float* stats,
