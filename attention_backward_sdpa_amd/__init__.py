@@ -107,7 +107,8 @@ def sdpa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, windo
                 deterministic=False, seq_q_lens=None, seq_kv_lens=None,
                 causal_bottom_right=False, window_right=0, workspace=None, stream=None,
                 events=None):
-    """sdpa_bwd_ex() (or sdpa_bwd_ex_events() when `events` lists five torch.cuda.Event)."""
+    """sdpa_bwd_ex() (or sdpa_bwd_ex_events() when `events` lists five torch.cuda.Event or
+    None, a None entry not being recorded)."""
     dims = _dims(q, k, v)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
@@ -118,7 +119,8 @@ def sdpa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, windo
     if events is None:
         _check(lib.sdpa_bwd_ex(*args))
     else:
-        handles = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        handles = (ctypes.c_void_p * 5)(
+            *[ctypes.c_void_p(None if e is None else e.cuda_event) for e in events])
         _check(lib.sdpa_bwd_ex_events(*args, handles))
 
 

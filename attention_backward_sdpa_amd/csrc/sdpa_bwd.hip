@@ -218,7 +218,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   if (c.total > 0 && ((uintptr_t)workspace % kAlign) != 0) return SDPA_BWD_UNSUPPORTED;
   if (!(scale > 0.f) || !isfinite(scale)) scale = 1.0f / sqrtf((float)Dqk);
   auto rec = [&](int n) {
-    if (events) (void)hipEventRecord((hipEvent_t)events[n], stream);
+    if (events && events[n]) (void)hipEventRecord((hipEvent_t)events[n], stream);
   };
 
   hipError_t e = hipSuccess;

@@ -85,8 +85,9 @@ int sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
 
 /* sdpa_bwd_ex that also records five HIP events (hipEvent_t, created by the caller) on `stream`:
  * before the preprocess, after the preprocess, after the main kernel, after the GQA reduce (same
- * point as the previous one when there is none) and after the dQ convert / dq2k kernel.  For
- * measuring each kernel's share of the chain; the arithmetic is identical to sdpa_bwd_ex. */
+ * point as the previous one when there is none) and after the dQ convert / dq2k kernel.  A NULL
+ * entry is skipped (each recorded event is one more packet on the stream).  For measuring each
+ * kernel's share of the chain; the arithmetic is identical to sdpa_bwd_ex. */
 int sdpa_bwd_ex_events(const void* q, const void* k, const void* v, const void* o, const void* dO,
                        const float* lse, void* dq, void* dk, void* dv,
                        int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv,
