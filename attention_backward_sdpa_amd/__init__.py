@@ -91,7 +91,7 @@ def _dims(q, k, v):
 
 def sdpa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, window_left=-1,
              deterministic=False, workspace=None, stream=None):
-    """sdpa_bwd(): the spec entry point on torch tensors (bf16 BHSD, lse fp32 (B,Hq,Sq)).
+    """sdpa_bwd(): the plain entry point on torch tensors (bf16 BHSD, lse fp32 (B,Hq,Sq)).
 
     Outputs dq, dk, dv are written in place.  `workspace` is a uint8 device tensor of at least
     workspace_size(...) bytes.  Raises SdpaBwdError on a non-zero status.

@@ -12,7 +12,7 @@ import numpy as np
 import oracle
 from attention_backward_sdpa_amd import synth
 
-# spec tolerance: max |err| <= 1e-2 * max |ref|, per tensor
+# parity tolerance: max |err| <= 1e-2 * max |ref|, per tensor
 REL_TOL = 1e-2
 
 _CACHE = {}

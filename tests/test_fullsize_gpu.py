@@ -2,7 +2,7 @@
 
 The whole chain runs on the GPU at full size; the fp64 oracle then recomputes sampled rows one by
 one (dQ rows and dK/dV key rows, including tile edges and padding boundaries) from exactly the
-inputs the GPU received, and the benchmark spec's tolerance max|err| <= 1e-2 * max|ref| is applied per
+inputs the GPU received, and the parity tolerance max|err| <= 1e-2 * max|ref| is applied per
 tensor over the samples.  Properties that hold at any size are checked on the full outputs: the
 column sums of dV equal the summed dO of the rows that see a key (sum_j P_ij = 1), the column
 sums of dK vanish (sum_j dS_ij = 0), padded rows are exactly zero, and the deterministic route is
