@@ -539,17 +539,20 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
         mask_pairs<0>(vis_m, pb, sb);
         mask_pairs<2>(vis_m, pb, sb);
       }
-      // dS of the wave's 32 keys as 2 KiB of quads (see ds_store_off)
       if constexpr (C::DET) {
-        // streaming stores (read once, by the dQ kernel): written past the last-level cache
-        // while this kernel computes, rather than evicted dirty during the dQ kernel's reads
+        // dS of the wave's 32 keys to the workspace: 2 KiB per 32 keys, lane l's quads of
+        // accumulator groups 2h and 2h + 1 as 16 contiguous bytes at 1024 h + 16 l (one coalesced
+        // 1 KiB store per h; the dQ kernel rebuilds the quad layout below in LDS).  Streaming
+        // stores (read once, by the dQ kernel): written past the last-level cache while this kernel
+        // computes, rather than evicted dirty during the dQ kernel's reads.
         char* wsb = reinterpret_cast<char*>(
             p.ds_ws + (((int64_t)bh * p.n_kv_tiles + j) * n_q_tiles + i) * (BC * BR));
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-          __builtin_nontemporal_store(u32x2{sb[2 * x], sb[2 * x + 1]},
-                                      reinterpret_cast<u32x2*>(wsb + w * 2048 + ds_store_off(lane, x)));
+        for (int h = 0; h < 2; ++h)
+          __builtin_nontemporal_store(u32x4{sb[4 * h], sb[4 * h + 1], sb[4 * h + 2], sb[4 * h + 3]},
+                                      reinterpret_cast<u32x4*>(wsb + w * 2048 + h * 1024 + lane * 16));
       } else {
+        // dS of the wave's 32 keys to LDS as 2 KiB of quads (see ds_store_off)
 #pragma unroll
         for (int x = 0; x < 4; ++x)
           *reinterpret_cast<u32x2*>(sST + w * 2048 + ds_store_off(lane, x)) =

@@ -6,12 +6,13 @@
 //
 // The pass streams the dS workspace once from HBM, so it is bound by how many bytes are in flight:
 //   * each wave loads its own q tile's dS straight into registers (the workspace holds each stored
-//     (KV tile, q tile) block as 2 KiB quads per 32 keys, layout in bwd_main.h, so 64 consecutive
-//     keys are one contiguous 4 KiB piece, four 16-byte non-temporal loads per lane), AHEAD chunks
-//     ahead of its MFMAs: 8 waves x AHEAD x 4 KiB in flight per workgroup, with no shared LDS space
-//     or barrier spent on dS.  Just before use the wave writes the chunk to its own 4 KiB LDS area
-//     and reads it back transposed (ds_read_b64_tr_b16) as the A operand; the quad rotation keeps
-//     both conflict-free;
+//     (KV tile, q tile) block as 2 KiB per 32 keys, the writing lane's two quad pairs as 16-byte
+//     pieces, layout in bwd_main.h, so 64 consecutive keys are one contiguous 4 KiB piece, four
+//     16-byte non-temporal loads per lane), AHEAD chunks ahead of its MFMAs: 8 waves x AHEAD x
+//     4 KiB in flight per workgroup, with no shared LDS space or barrier spent on dS.  Just before
+//     use the wave writes the chunk to its own 4 KiB LDS area as quads (ds_store_off) and reads it
+//     back transposed (ds_read_b64_tr_b16) as the A operand; the quad rotation keeps both
+//     conflict-free;
 //   * K is the only shared operand.  A workgroup of 8 waves owns 8 consecutive q tiles of one head,
 //     so every 64-key chunk of K (as swizzled GEMM1 fragments, re-read from L2) serves 256 query
 //     rows.  Each wave loads its share of a chunk into registers KR chunks early and writes it to
@@ -189,9 +190,15 @@ __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
         const int c = c_lo + r;
         if (my_first <= c && c < my_end) {
           const char* sK = smem + (u & 1) * C::K_BYTES;
+          // piece s = 32-key tile s / 2, accumulator groups 2 (s % 2) and 2 (s % 2) + 1 of the
+          // writing lane: back to the quad layout
 #pragma unroll
-          for (int s = 0; s < C::DS_LOADS; ++s)
-            *reinterpret_cast<u32x4*>(sdS + s * 1024 + lane * 16) = dsr[u % AHEAD][s];
+          for (int s = 0; s < C::DS_LOADS; ++s) {
+            const u32x4 v = dsr[u % AHEAD][s];
+            char* t = sdS + (s >> 1) * 2048;
+            *reinterpret_cast<u32x2*>(t + ds_store_off(lane, 2 * (s & 1))) = u32x2{v[0], v[1]};
+            *reinterpret_cast<u32x2*>(t + ds_store_off(lane, 2 * (s & 1) + 1)) = u32x2{v[2], v[3]};
+          }
 #pragma unroll
           for (int s = 0; s < C::STEPS; ++s) {
             const bf16x8 a = tl.ds(sdS, s);
