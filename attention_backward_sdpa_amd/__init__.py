@@ -13,6 +13,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsdpa_bwd.so")
 
 OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, LAUNCH_FAILED = 0, 1, 2, 3, 4
+BF16, FP16 = 0, 1
+
+
+class Layout(ctypes.Structure):
+    """sdpa_bwd_layout: element strides (batch, head, seq) of a (B, H, S, D) tensor."""
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("seq", ctypes.c_int64)]
 
 _lib = None
 
@@ -41,6 +47,9 @@ def _load():
     lib.sdpa_bwd_ex.restype = i
     lib.sdpa_bwd_ex_events.argtypes = ex + [vp]
     lib.sdpa_bwd_ex_events.restype = i
+    lib.sdpa_bwd_flex.argtypes = ([vp] * 9 + [i] * 7 + [f, i, i, i, vp, vp, i, i, vp, i, vp, sz, vp,
+                                                    vp])
+    lib.sdpa_bwd_flex.restype = i
     lib.sdpa_bwd_preprocess.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.sdpa_bwd_preprocess.restype = i
     lib.sdpa_bwd_status_string.argtypes = [i]
@@ -103,25 +112,48 @@ def sdpa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, window_l
                             _stream_handle(stream)))
 
 
+def _layouts(tensors):
+    """Eight sdpa_bwd_layout entries from the tensors' strides (head dim must be contiguous)."""
+    arr = (Layout * 8)()
+    for x, t in enumerate(tensors):
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError("sdpa_bwd_flex needs 4-D (B, H, S, D) tensors with a contiguous head dim")
+        arr[x] = Layout(t.stride(0), t.stride(1), t.stride(2))
+    return arr
+
+
+def _io_dtype(q):
+    import torch
+    return FP16 if q.dtype == torch.float16 else BF16
+
+
 def sdpa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, window_left=-1,
                 deterministic=False, seq_q_lens=None, seq_kv_lens=None,
                 causal_bottom_right=False, window_right=0, workspace=None, stream=None,
                 events=None):
     """sdpa_bwd_ex() (or sdpa_bwd_ex_events() when `events` lists five torch.cuda.Event or
-    None, a None entry not being recorded)."""
+    None, a None entry not being recorded).  Tensors that are not all contiguous bf16 go through
+    sdpa_bwd_flex with their own strides (any dense layout with a contiguous head dim)."""
     dims = _dims(q, k, v)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+    head = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
             *dims, -1.0 if scale is None else float(scale), int(causal), int(window_left),
             int(deterministic), _ptr(seq_q_lens), _ptr(seq_kv_lens), int(causal_bottom_right),
-            int(window_right), _ptr(workspace), ws_bytes, _stream_handle(stream)]
-    lib = _load()
-    if events is None:
-        _check(lib.sdpa_bwd_ex(*args))
-    else:
+            int(window_right)]
+    tail = [_ptr(workspace), ws_bytes, _stream_handle(stream)]
+    handles = None
+    if events is not None:
         handles = (ctypes.c_void_p * 5)(
             *[ctypes.c_void_p(None if e is None else e.cuda_event) for e in events])
-        _check(lib.sdpa_bwd_ex_events(*args, handles))
+    lib = _load()
+    tensors = (q, k, v, o, do, dq, dk, dv)
+    if all(t.is_contiguous() for t in tensors) and _io_dtype(q) == BF16:
+        if handles is None:
+            _check(lib.sdpa_bwd_ex(*head, *tail))
+        else:
+            _check(lib.sdpa_bwd_ex_events(*head, *tail, handles))
+    else:
+        _check(lib.sdpa_bwd_flex(*head, _layouts(tensors), _io_dtype(q), *tail, handles))
 
 
 def sdpa_bwd_preprocess(o, do, lse, stats, dq_accum=None, seq_q_lens=None, Dqk=0, stream=None):

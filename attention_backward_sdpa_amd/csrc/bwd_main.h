@@ -51,6 +51,8 @@ struct MainParams {
   const bf16_t* k;
   const bf16_t* v;
   const bf16_t* dO;
+  Strides sq, sk, sv, sdo;  // element strides of q, k, v, dO
+  Strides sdk, sdv;         // of dk, dv (used when dK/dV are written directly, not as partials)
   const float* stats;       // (B*Hq, sq_pad, 2): [LSE*log2e or +inf, delta] per q row
   float* dq_accum;          // (B, Hq, Sq, Dqk) fp32, non-deterministic route
   bf16_t* ds_ws;            // (B*Hq, n_kv_tiles, sq_pad/32) blocks of BC x 32 bf16 dS
@@ -156,22 +158,23 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // transpose reads conflict-free; a linear 16-lane row read stays a permutation of one row.
 __device__ __forceinline__ constexpr int kswz(int row, int frag) { return (row >> 1) + 2 * (frag & 1); }
 
-// Element offset (in the row-major source) of the 16 bytes this lane contributes to fragment f.
+// Element offset (in the source, rows rs elements apart) of the 16 bytes this lane contributes to
+// fragment f.
 template <int D, bool SWZ>
-__device__ __forceinline__ int frag_src_elem(int f, int row0, int rows_valid, int lane) {
+__device__ __forceinline__ int frag_src_elem(int f, int row0, int rows_valid, int lane, int rs) {
   const int rt = f / (D / 16), t = f % (D / 16);
   int n = lane;
   if constexpr (SWZ) n = (lane & 48) | ((lane & 15) ^ (4 * kswz(lane >> 4, f)));
   int row = row0 + 32 * rt + (n & 31);
   row = row < rows_valid ? row : rows_valid - 1;
-  return row * D + 16 * t + 8 * (n >> 5);
+  return row * rs + 16 * t + 8 * (n >> 5);
 }
 
 template <int D, int NW, bool SWZ = false>
-__device__ __forceinline__ void gather_frags(rsrc_t src, int row0, int rows_valid, int nfrag,
-                                             char* lds, int w, int lane) {
+__device__ __forceinline__ void gather_frags(rsrc_t src, int row0, int rows_valid, int rs,
+                                             int nfrag, char* lds, int w, int lane) {
   for (int f = w; f < nfrag; f += NW)
-    dma16(src, (uint32_t)frag_src_elem<D, SWZ>(f, row0, rows_valid, lane) * 2, lds + f * 1024);
+    dma16(src, (uint32_t)frag_src_elem<D, SWZ>(f, row0, rows_valid, lane, rs) * 2, lds + f * 1024);
 }
 
 // Byte offset of this lane's 16-byte chunk in a linear read of swizzled fragment f (f's parity
@@ -417,15 +420,15 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
   }
 
   const int n_q_tiles = p.sq_pad / BR;
-  const int64_t kv_row0 = (int64_t)(b * p.Hkv + kvh) * p.Skv;
-  const int64_t q_row0 = (int64_t)(b * p.Hq + h) * p.Sq;
-  const bf16_t* Kb = p.k + kv_row0 * DQK;
-  const bf16_t* Vb = p.v + kv_row0 * DV;
-  const bf16_t* Qb = p.q + q_row0 * DQK;
-  const bf16_t* dOb = p.dO + q_row0 * DV;
+  const int64_t q_row0 = (int64_t)(b * p.Hq + h) * p.Sq;  // row of the contiguous dq_accum
+  const bf16_t* Kb = p.k + b * p.sk.b + kvh * p.sk.h;
+  const bf16_t* Vb = p.v + b * p.sv.b + kvh * p.sv.h;
+  const bf16_t* Qb = p.q + b * p.sq.b + h * p.sq.h;
+  const bf16_t* dOb = p.dO + b * p.sdo.b + h * p.sdo.h;
   const float* statb = p.stats + (int64_t)bh * p.sq_pad * 2;
-  const rsrc_t rQ = buf_rsrc(Qb, (int64_t)p.Sq * DQK * 2);
-  const rsrc_t rdO = buf_rsrc(dOb, (int64_t)p.Sq * DV * 2);
+  // one head's rows (the host keeps each span below 2^31 bytes)
+  const rsrc_t rQ = buf_rsrc(Qb, ((int64_t)(p.Sq - 1) * p.sq.s + DQK) * 2);
+  const rsrc_t rdO = buf_rsrc(dOb, ((int64_t)(p.Sq - 1) * p.sdo.s + DV) * 2);
   const rsrc_t rStat = buf_rsrc(statb, (int64_t)p.sq_pad * 2 * 4);
 
   acc_t accK[C::N_DQT][NKT], accV[C::N_DVT][NKT];
@@ -447,16 +450,16 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
     // ---- q tile i into its LDS buffer ----------------------------------------------------------
     auto load_tile = [&](int i) {
       char* t = tile(i);
-      gather_frags<DQK, C::NW, true>(rQ, i * BR, p.Sq, C::N_KQ, t + C::T_QA, w, lane);
-      gather_frags<DV, C::NW, true>(rdO, i * BR, p.Sq, C::N_KV, t + C::T_OA, w, lane);
+      gather_frags<DQK, C::NW, true>(rQ, i * BR, p.Sq, (int)p.sq.s, C::N_KQ, t + C::T_QA, w, lane);
+      gather_frags<DV, C::NW, true>(rdO, i * BR, p.Sq, (int)p.sdo.s, C::N_KV, t + C::T_OA, w, lane);
       if (w == 0)  // 64 floats: [lse2, delta] x 32 rows, already padded to sq_pad rows
         dma4(rStat, (uint32_t)(i * BR * 2 + lane) * 4, t + C::T_ST);
     };
     load_tile(i_hi);
     // ---- K fragments into LDS (B operand of GEMM1 and/or GEMM4) -------------------------------
     if constexpr (C::KLDS)
-      gather_frags<DQK, C::NW, true>(buf_rsrc(Kb, (int64_t)p.Skv * DQK * 2), k0, p.Skv,
-                               (BC / 32) * C::N_KQ, sK, w, lane);
+      gather_frags<DQK, C::NW, true>(buf_rsrc(Kb, ((int64_t)(p.Skv - 1) * p.sk.s + DQK) * 2), k0,
+                                     p.Skv, (int)p.sk.s, (BC / 32) * C::N_KQ, sK, w, lane);
     // ---- V (and K) slices into registers -------------------------------------------------------
     bf16x8 vreg[NKT][C::N_KV];
     bf16x8 kreg[C::KREG ? NKT : 1][C::KREG ? C::N_KQ : 1];
@@ -464,11 +467,11 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
     for (int kt = 0; kt < NKT; ++kt) {
       int key = key_lane + kt * 32;
       key = key < p.Skv ? key : p.Skv - 1;  // keys past the sequence are masked out of every product
-      const bf16_t* vr = Vb + (int64_t)key * DV + g * 8;
+      const bf16_t* vr = Vb + (int64_t)key * p.sv.s + g * 8;
 #pragma unroll
       for (int t = 0; t < C::N_KV; ++t) vreg[kt][t] = *reinterpret_cast<const bf16x8*>(vr + t * 16);
       if constexpr (C::KREG) {
-        const bf16_t* kr = Kb + (int64_t)key * DQK + g * 8;
+        const bf16_t* kr = Kb + (int64_t)key * p.sk.s + g * 8;
 #pragma unroll
         for (int t = 0; t < C::N_KQ; ++t) kreg[kt][t] = *reinterpret_cast<const bf16x8*>(kr + t * 16);
       }
@@ -581,9 +584,11 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
   for (int kt = 0; kt < NKT; ++kt) {
     const int key = key_lane + kt * 32;
     if (key < p.Skv) {
-      const int64_t orow = oslot * p.Skv + key;
-      bf16_t* dkr = p.dk_out + orow * DQK;
-      bf16_t* dvr = p.dv_out + orow * DV;
+      // partials: contiguous per (query head, part); final dK/dV: the caller's layout
+      bf16_t* dkr = p.partials ? p.dk_out + (oslot * p.Skv + key) * DQK
+                               : p.dk_out + b * p.sdk.b + kvh * p.sdk.h + key * p.sdk.s;
+      bf16_t* dvr = p.partials ? p.dv_out + (oslot * p.Skv + key) * DV
+                               : p.dv_out + b * p.sdv.b + kvh * p.sdv.h + key * p.sdv.s;
 #pragma unroll
       for (int dt = 0; dt < C::N_DQT; ++dt)
 #pragma unroll

@@ -16,6 +16,12 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Element strides of one logical (B, H, S, D) tensor whose head dim is contiguous ("dense_flex"
+// layouts of "SDPA Backward (SM120)", section "API Usage": any dense layout, addressed in place).
+struct Strides {
+  int64_t b, h, s;
+};
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf16_to_float(bf16_t x) {

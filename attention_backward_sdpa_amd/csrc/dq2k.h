@@ -27,8 +27,9 @@ namespace sdpa {
 
 struct Dq2kParams {
   const bf16_t* ds_ws;        // (B*Hq, n_kv_tiles, n_q_tiles) blocks of BC x 32 bf16
-  const bf16_t* k;            // (B, Hkv, Skv, Dqk)
-  bf16_t* dq;                 // (B, Hq, Sq, Dqk)
+  const bf16_t* k;            // (B, Hkv, Skv, Dqk), element strides sk
+  bf16_t* dq;                 // (B, Hq, Sq, Dqk), element strides sdq
+  Strides sk, sdq;
   const int* seq_q_lens;
   const int* seq_kv_lens;
   int B, Hq, Hkv, Sq, Skv, group;
@@ -138,7 +139,7 @@ __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
   const char* wsq = reinterpret_cast<const char*>(
                         p.ds_ws + ((int64_t)bh * p.n_kv_tiles * p.n_q_tiles + my_tile) * (BC * BR)) +
                     lane * 16;
-  const bf16_t* Kb = p.k + (int64_t)(b * p.Hkv + kvh) * p.Skv * DQK;
+  const bf16_t* Kb = p.k + b * p.sk.b + kvh * p.sk.h;
 
   const Gemm4Lanes tl(lane);
   acc_t acc[C::N_DT];
@@ -162,7 +163,7 @@ __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
 #pragma unroll
       for (int u = 0; u < C::K_PER_WAVE; ++u)
         dst[u] = *reinterpret_cast<const u32x4*>(
-            Kb + frag_src_elem<DQK, true>(w + u * C::NW, c * KC, p.Skv, lane));
+            Kb + frag_src_elem<DQK, true>(w + u * C::NW, c * KC, p.Skv, lane, (int)p.sk.s));
     };
     auto store_k = [&](const u32x4 (&src)[C::K_PER_WAVE], int buf) {
 #pragma unroll
@@ -219,13 +220,13 @@ __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
   // dQ = scale * acc; rows past the buffer are not stored, rows past len_q come out exactly zero
   if (i0 + w < p.n_q_tiles) {
     const int q0 = (i0 + w) * BR;
-    bf16_t* dqb = p.dq + (int64_t)(b * p.Hq + h) * p.Sq * DQK;
+    bf16_t* dqb = p.dq + b * p.sdq.b + h * p.sdq.h;
 #pragma unroll
     for (int dt = 0; dt < C::N_DT; ++dt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int q = q0 + acc_row<32>(r, g);
-        if (q < p.Sq) dqb[(int64_t)q * DQK + dt * 32 + lc] = float_to_bf16(acc[dt][r] * p.scale);
+        if (q < p.Sq) dqb[(int64_t)q * p.sdq.s + dt * 32 + lc] = float_to_bf16(acc[dt][r] * p.scale);
       }
     }
   }

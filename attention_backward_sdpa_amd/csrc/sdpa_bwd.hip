@@ -86,6 +86,39 @@ Carve carve(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv, int det, c
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// Element strides of the eight (B, H, S, D) tensors, head dim contiguous.
+enum { T_Q, T_K, T_V, T_O, T_DO, T_DQ, T_DK, T_DV, N_TENSORS };
+struct Layouts {
+  Strides t[N_TENSORS];
+};
+
+Layouts contiguous_layouts(int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv) {
+  auto bhsd = [](int H, int S, int D) {
+    return Strides{(int64_t)H * S * D, (int64_t)S * D, (int64_t)D};
+  };
+  Layouts L;
+  L.t[T_Q] = L.t[T_DQ] = bhsd(Hq, Sq, Dqk);
+  L.t[T_O] = L.t[T_DO] = bhsd(Hq, Sq, Dv);
+  L.t[T_K] = L.t[T_DK] = bhsd(Hkv, Skv, Dqk);
+  L.t[T_V] = L.t[T_DV] = bhsd(Hkv, Skv, Dv);
+  return L;
+}
+
+// Every row 16-byte aligned (with a 16-byte-aligned base), rows of one head at least a row
+// apart, and one head's span addressable through 32-bit buffer offsets.
+int check_layouts(const Layouts& L, int Sq, int Skv, int Dqk, int Dv) {
+  const int S[N_TENSORS] = {Sq, Skv, Skv, Sq, Sq, Sq, Skv, Skv};
+  const int D[N_TENSORS] = {Dqk, Dqk, Dv, Dv, Dv, Dqk, Dqk, Dv};
+  for (int x = 0; x < N_TENSORS; ++x) {
+    const Strides& st = L.t[x];
+    if (st.b < 0 || st.h < 0 || st.s < D[x]) return SDPA_BWD_INVALID_ARG;
+    if ((st.b | st.h | st.s) & 7) return SDPA_BWD_UNSUPPORTED;
+    if (S[x] > 0 && ((int64_t)(S[x] - 1) * st.s + D[x]) * 2 >= ((int64_t)1 << 31))
+      return SDPA_BWD_UNSUPPORTED;
+  }
+  return SDPA_BWD_OK;
+}
+
 int validate(const void* q, const void* k, const void* v, const void* o, const void* dO,
              const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
              int Skv, int Dqk, int Dv, int window_left, int window_right, Geometry* geo) {
@@ -96,7 +129,10 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
   // the kernels address one head's rows (and its padded tiles) through 32-bit buffer offsets
   const int64_t s_max = (Sq > Skv ? Sq : Skv) + geo->bc;
   if (s_max * (Dqk > Dv ? Dqk : Dv) * 2 >= ((int64_t)1 << 31)) return SDPA_BWD_UNSUPPORTED;
-  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return SDPA_BWD_INVALID_ARG;
+  // a tensor with no elements may be NULL
+  const bool has_q = (int64_t)B * Sq > 0, has_k = (int64_t)B * Skv > 0;
+  if (has_q && (!q || !o || !dO || !lse || !dq)) return SDPA_BWD_INVALID_ARG;
+  if (has_k && (!k || !v || !dk || !dv)) return SDPA_BWD_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
       ((uintptr_t)lse & 3) != 0 || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return SDPA_BWD_UNSUPPORTED;
@@ -181,17 +217,14 @@ hipError_t launch_preprocess(const PreParams& pp, int Dqk, int Dv, int64_t tiles
   return hipGetLastError();
 }
 
-__global__ void fill_zero_kernel(uint32_t* p, int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += stride) p[x] = 0;
-}
-
-hipError_t zero_buffer(void* p, int64_t bytes, hipStream_t s) {
-  const int64_t n = bytes / 4;
-  if (n == 0) return hipSuccess;
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, s, (uint32_t*)p, n);
+hipError_t zero_rows(void* p, const Strides& st, int B, int H, int S, int D, hipStream_t s) {
+  const int64_t nbh = (int64_t)B * H;
+  if (nbh == 0 || S == 0) return hipSuccess;
+  int64_t bx = ((int64_t)S * D / 8 + 255) / 256;
+  bx = bx > 1024 ? 1024 : bx;
+  const int by = nbh > 65535 ? 65535 : (int)nbh;
+  hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)bx, by), dim3(256), 0, s, (bf16_t*)p, st, H,
+                     S, D, (int)nbh);
   return hipGetLastError();
 }
 
@@ -205,14 +238,23 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
         const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Skv,
         int Dqk, int Dv, float scale, int causal, int window_left, int deterministic,
         const int* seq_q_lens, const int* seq_kv_lens, int bottom_right, int window_right,
-        void* workspace, size_t workspace_bytes, bool check_ws, hipStream_t stream,
-        void* const* events) {
+        const sdpa_bwd_layout* layouts, int dtype, void* workspace, size_t workspace_bytes,
+        bool check_ws, hipStream_t stream, void* const* events) {
   Geometry geo;
   int st = validate(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, window_left,
                     window_right, &geo);
   if (st != SDPA_BWD_OK) return st;
+  if (dtype != SDPA_BWD_BF16) return SDPA_BWD_UNSUPPORTED;
+  Layouts L = contiguous_layouts(Hq, Hkv, Sq, Skv, Dqk, Dv);
+  if (layouts)
+    for (int x = 0; x < N_TENSORS; ++x)
+      L.t[x] = Strides{layouts[x].batch, layouts[x].head, layouts[x].seq};
+  st = check_layouts(L, Sq, Skv, Dqk, Dv);
+  if (st != SDPA_BWD_OK) return st;
   const int det = deterministic ? 1 : 0;
-  const Carve c = carve(B, Hq, Hkv, Sq, Skv, Dqk, Dv, det, geo);
+  // empty problems need no workspace (sdpa_bwd_workspace_size returns 0 for them)
+  const bool empty = B == 0 || Sq == 0 || Skv == 0;
+  const Carve c = empty ? Carve{} : carve(B, Hq, Hkv, Sq, Skv, Dqk, Dv, det, geo);
   if (c.total > 0 && workspace == nullptr) return SDPA_BWD_INVALID_ARG;
   if (check_ws && (uint64_t)c.total > (uint64_t)workspace_bytes) return SDPA_BWD_WORKSPACE_TOO_SMALL;
   if (c.total > 0 && ((uintptr_t)workspace % kAlign) != 0) return SDPA_BWD_UNSUPPORTED;
@@ -223,15 +265,11 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
 
   hipError_t e = hipSuccess;
   rec(0);
-  if (B == 0 || Hq == 0) {
-    for (int n = 1; n < 5; ++n) rec(n);
-    return SDPA_BWD_OK;
-  }
-  if (Sq == 0 || Skv == 0) {
+  if (empty) {
     // nothing attends: every gradient that exists is zero
-    e = zero_buffer(dq, (int64_t)B * Hq * Sq * Dqk * 2, stream);
-    if (e == hipSuccess) e = zero_buffer(dk, (int64_t)B * Hkv * Skv * Dqk * 2, stream);
-    if (e == hipSuccess) e = zero_buffer(dv, (int64_t)B * Hkv * Skv * Dv * 2, stream);
+    e = zero_rows(dq, L.t[T_DQ], B, Hq, Sq, Dqk, stream);
+    if (e == hipSuccess) e = zero_rows(dk, L.t[T_DK], B, Hkv, Skv, Dqk, stream);
+    if (e == hipSuccess) e = zero_rows(dv, L.t[T_DV], B, Hkv, Skv, Dv, stream);
     for (int n = 1; n < 5; ++n) rec(n);
     return e == hipSuccess ? SDPA_BWD_OK : SDPA_BWD_LAUNCH_FAILED;
   }
@@ -245,6 +283,8 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   PreParams pp;
   pp.o = (const bf16_t*)o;
   pp.dO = (const bf16_t*)dO;
+  pp.so = L.t[T_O];
+  pp.sdo = L.t[T_DO];
   pp.lse = lse;
   pp.stats = stats;
   pp.dq_accum = dq_accum;
@@ -263,6 +303,12 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   mp.k = (const bf16_t*)k;
   mp.v = (const bf16_t*)v;
   mp.dO = (const bf16_t*)dO;
+  mp.sq = L.t[T_Q];
+  mp.sk = L.t[T_K];
+  mp.sv = L.t[T_V];
+  mp.sdo = L.t[T_DO];
+  mp.sdk = L.t[T_DK];
+  mp.sdv = L.t[T_DV];
   mp.stats = stats;
   mp.dq_accum = dq_accum;
   mp.ds_ws = det ? (bf16_t*)(ws + c.ds) : nullptr;
@@ -299,13 +345,19 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     rp.dv_ws = mp.dv_out;
     rp.dk = (bf16_t*)dk;
     rp.dv = (bf16_t*)dv;
-    rp.head_k8 = (int64_t)Skv * Dqk / 8;
-    rp.head_v8 = (int64_t)Skv * Dv / 8;
-    rp.nk8 = (int64_t)B * Hkv * rp.head_k8;
-    rp.nv8 = (int64_t)B * Hkv * rp.head_v8;
+    rp.sdk = L.t[T_DK];
+    rp.sdv = L.t[T_DV];
+    rp.n_kvh = B * Hkv;
+    rp.Hkv = Hkv;
+    rp.Skv = Skv;
+    rp.Dqk = Dqk;
+    rp.Dv = Dv;
     rp.group = (Hq / Hkv) * split;  // slots (query head of the group, part), in that order
-    hipLaunchKernelGGL(gqa_reduce_kernel, dim3(grid_stride_blocks(rp.nk8 + rp.nv8)), dim3(256), 0,
-                       stream, rp);
+    const int64_t per_head = (int64_t)Skv * (Dqk + Dv) / 8;
+    int64_t bx = (per_head + 255) / 256;
+    bx = bx > 4096 ? 4096 : bx;
+    const int by = rp.n_kvh > 65535 ? 65535 : rp.n_kvh;
+    hipLaunchKernelGGL(gqa_reduce_kernel, dim3((unsigned)bx, by), dim3(256), 0, stream, rp);
     if (hipGetLastError() != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   }
   rec(3);
@@ -314,6 +366,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     ConvertParams cp;
     cp.acc = dq_accum;
     cp.dq = (bf16_t*)dq;
+    cp.sdq = L.t[T_DQ];
     cp.seq_q_lens = seq_q_lens;
     cp.Hq = Hq;
     cp.Sq = Sq;
@@ -327,6 +380,8 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     dp.ds_ws = mp.ds_ws;
     dp.k = (const bf16_t*)k;
     dp.dq = (bf16_t*)dq;
+    dp.sk = L.t[T_K];
+    dp.sdq = L.t[T_DQ];
     dp.seq_q_lens = seq_q_lens;
     dp.seq_kv_lens = seq_kv_lens;
     dp.B = B;
@@ -370,8 +425,8 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int Skv, int Dqk, int Dv, float scale, int causal, int window_left,
              int deterministic, void* workspace, void* stream) {
   return run(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, scale, causal,
-             window_left, deterministic, nullptr, nullptr, 0, 0, workspace, 0, false,
-             (hipStream_t)stream, nullptr);
+             window_left, deterministic, nullptr, nullptr, 0, 0, nullptr, SDPA_BWD_BF16,
+             workspace, 0, false, (hipStream_t)stream, nullptr);
 }
 
 int sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -382,7 +437,8 @@ int sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
                 size_t workspace_bytes, void* stream) {
   return run(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, scale, causal,
              window_left, deterministic, seq_q_lens, seq_kv_lens, causal_bottom_right,
-             window_right, workspace, workspace_bytes, true, (hipStream_t)stream, nullptr);
+             window_right, nullptr, SDPA_BWD_BF16, workspace, workspace_bytes, true,
+             (hipStream_t)stream, nullptr);
 }
 
 int sdpa_bwd_ex_events(const void* q, const void* k, const void* v, const void* o,
@@ -394,7 +450,21 @@ int sdpa_bwd_ex_events(const void* q, const void* k, const void* v, const void* 
                        void* const* events) {
   return run(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, scale, causal,
              window_left, deterministic, seq_q_lens, seq_kv_lens, causal_bottom_right,
-             window_right, workspace, workspace_bytes, true, (hipStream_t)stream, events);
+             window_right, nullptr, SDPA_BWD_BF16, workspace, workspace_bytes, true,
+             (hipStream_t)stream, events);
+}
+
+int sdpa_bwd_flex(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                  const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
+                  int Skv, int Dqk, int Dv, float scale, int causal, int window_left,
+                  int deterministic, const int* seq_q_lens, const int* seq_kv_lens,
+                  int causal_bottom_right, int window_right, const sdpa_bwd_layout* layouts,
+                  int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                  void* const* events) {
+  return run(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, scale, causal,
+             window_left, deterministic, seq_q_lens, seq_kv_lens, causal_bottom_right,
+             window_right, layouts, dtype, workspace, workspace_bytes, true, (hipStream_t)stream,
+             events);
 }
 
 int sdpa_bwd_preprocess(const void* o, const void* dO, const float* lse, float* stats,

@@ -19,6 +19,7 @@ namespace sdpa {
 struct PreParams {
   const bf16_t* o;
   const bf16_t* dO;
+  Strides so, sdo;           // element strides of o and dO
   const float* lse;
   float* stats;              // (B*Hq, sq_pad, 2)
   float* dq_accum;           // (B*Hq, Sq, Dqk) or null
@@ -37,7 +38,9 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
   const int64_t bh = blockIdx.x / nt;
   const int i = blockIdx.x % nt;
   const int q0 = i * BR;
-  const int b = (int)(bh / p.Hq);
+  const int b = (int)(bh / p.Hq), h = (int)(bh % p.Hq);
+  const bf16_t* ob = p.o + b * p.so.b + h * p.so.h;
+  const bf16_t* dob = p.dO + b * p.sdo.b + h * p.sdo.h;
   const int Lq = p.seq_q_lens ? min(max(p.seq_q_lens[b], 0), p.Sq) : p.Sq;
 
   for (int r0 = 0; r0 < BR; r0 += RPP) {
@@ -46,8 +49,8 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
     const int64_t row = bh * p.Sq + s;
     float acc = 0.f;
     if (live) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(p.o + row * DV + sub * 8);
-      const u32x4 c = *reinterpret_cast<const u32x4*>(p.dO + row * DV + sub * 8);
+      const u32x4 a = *reinterpret_cast<const u32x4*>(ob + s * p.so.s + sub * 8);
+      const u32x4 c = *reinterpret_cast<const u32x4*>(dob + s * p.sdo.s + sub * 8);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         acc += __uint_as_float(a[e] << 16) * __uint_as_float(c[e] << 16);
@@ -75,8 +78,9 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
 // accumulator.  One workgroup per 32-row q tile of one (batch, query head); 8 elements per thread
 // and step (two 16-byte loads, one 16-byte store).
 struct ConvertParams {
-  const float* acc;          // (B*Hq, Sq, Dqk)
-  bf16_t* dq;                // (B*Hq, Sq, Dqk)
+  const float* acc;          // (B*Hq, Sq, Dqk), contiguous
+  bf16_t* dq;                // (B, Hq, Sq, Dqk), element strides sdq
+  Strides sdq;
   const int* seq_q_lens;
   int Hq, Sq;
   float scale;
@@ -88,59 +92,83 @@ __global__ void __launch_bounds__(256) dq_convert_kernel(ConvertParams p) {
   const int nt = (p.Sq + 31) / 32;
   const int64_t bh = blockIdx.x / nt;
   const int q0 = (int)(blockIdx.x % nt) * 32;
-  const int b = (int)(bh / p.Hq);
+  const int b = (int)(bh / p.Hq), h = (int)(bh % p.Hq);
   const int Lq = p.seq_q_lens ? min(max(p.seq_q_lens[b], 0), p.Sq) : p.Sq;
+  bf16_t* dqb = p.dq + b * p.sdq.b + h * p.sdq.h;
   for (int v = threadIdx.x; v < 32 * V; v += 256) {
-    const int s = q0 + v / V;
+    const int s = q0 + v / V, c = v % V;
     if (s >= p.Sq) break;
-    const int64_t x = (bh * p.Sq + s) * V + v % V;
+    const int64_t x = (bh * p.Sq + s) * V + c;
     u32x4 out = u32x4{0u, 0u, 0u, 0u};
     if (s < Lq) {
       const floatx4 a = reinterpret_cast<const floatx4*>(p.acc)[2 * x];
-      const floatx4 c = reinterpret_cast<const floatx4*>(p.acc)[2 * x + 1];
+      const floatx4 d = reinterpret_cast<const floatx4*>(p.acc)[2 * x + 1];
       const float k = p.scale;
       out = u32x4{pack_bf16x2(a[0] * k, a[1] * k), pack_bf16x2(a[2] * k, a[3] * k),
-                  pack_bf16x2(c[0] * k, c[1] * k), pack_bf16x2(c[2] * k, c[3] * k)};
+                  pack_bf16x2(d[0] * k, d[1] * k), pack_bf16x2(d[2] * k, d[3] * k)};
     }
-    reinterpret_cast<u32x4*>(p.dq)[x] = out;
+    *reinterpret_cast<u32x4*>(dqb + s * p.sdq.s + c * 8) = out;
   }
 }
 
 // ---- GQA reduce ---------------------------------------------------------------------------------
 // out[b, kvh, s, :] = bf16( sum_{g = 0 .. group-1} ws[b, kvh*group + g, s, :] ), summed in fp32
-// in ascending g.  One thread per 16-byte output vector; dK and dV handled by one launch
-// (vectors [0, nk8) are dK, [nk8, nk8 + nv8) are dV).
+// in ascending g.  The partials are contiguous per slot; the outputs follow the caller's layout.
+// grid.y walks the KV heads (b * Hkv + kvh), grid.x one 16-byte output vector per thread over
+// the head's dK vectors and then its dV vectors.
 struct ReduceParams {
   const bf16_t* dk_ws;
   const bf16_t* dv_ws;
   bf16_t* dk;
   bf16_t* dv;
-  int64_t nk8, nv8;          // output 8-element vectors of dK and dV
-  int64_t head_k8, head_v8;  // 8-element vectors per head (Skv * D / 8)
-  int group;
+  Strides sdk, sdv;
+  int n_kvh, Hkv;            // B * Hkv, Hkv
+  int Skv, Dqk, Dv;
+  int group;                 // partial slots per KV head, summed in this order
 };
 
 __global__ void __launch_bounds__(256) gqa_reduce_kernel(ReduceParams p) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < p.nk8 + p.nv8; x += stride) {
-    const bool isk = x < p.nk8;
-    const int64_t y = isk ? x : x - p.nk8;
-    const int64_t per = isk ? p.head_k8 : p.head_v8;
-    const int64_t kvhead = y / per, within = y % per;  // kvhead = b * Hkv + kvh
-    const u32x4* src = reinterpret_cast<const u32x4*>(isk ? p.dk_ws : p.dv_ws) +
-                       (kvhead * p.group) * per + within;
-    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int gi = 0; gi < p.group; ++gi) {
-      const u32x4 v = src[(int64_t)gi * per];
+  const int k8 = p.Dqk / 8, v8 = p.Dv / 8;
+  const int nk = p.Skv * k8, nv = p.Skv * v8;  // vectors per head (the host keeps these < 2^28)
+  for (int kvhead = blockIdx.y; kvhead < p.n_kvh; kvhead += gridDim.y) {
+    const int b = kvhead / p.Hkv, kvh = kvhead % p.Hkv;
+    for (int x = blockIdx.x * 256 + threadIdx.x; x < nk + nv; x += gridDim.x * 256) {
+      const bool isk = x < nk;
+      const int y = isk ? x : x - nk;
+      const int per = isk ? nk : nv, d8 = isk ? k8 : v8;
+      const int key = y / d8, c = y - key * d8;
+      const u32x4* src = reinterpret_cast<const u32x4*>(isk ? p.dk_ws : p.dv_ws) +
+                         (int64_t)kvhead * p.group * per + y;
+      float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int gi = 0; gi < p.group; ++gi) {
+        const u32x4 v = src[(int64_t)gi * per];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s[2 * e] += __uint_as_float(v[e] << 16);
-        s[2 * e + 1] += __uint_as_float(v[e] & 0xffff0000u);
+        for (int e = 0; e < 4; ++e) {
+          s[2 * e] += __uint_as_float(v[e] << 16);
+          s[2 * e + 1] += __uint_as_float(v[e] & 0xffff0000u);
+        }
       }
+      const Strides& st = isk ? p.sdk : p.sdv;
+      bf16_t* dst = (isk ? p.dk : p.dv) + b * st.b + kvh * st.h + key * st.s + c * 8;
+      *reinterpret_cast<u32x4*>(dst) =
+          u32x4{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]), pack_bf16x2(s[4], s[5]),
+                pack_bf16x2(s[6], s[7])};
     }
-    reinterpret_cast<u32x4*>(isk ? p.dk : p.dv)[y] =
-        u32x4{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]), pack_bf16x2(s[4], s[5]),
-              pack_bf16x2(s[6], s[7])};
+  }
+}
+
+// ---- strided zero fill (gradients of shapes where nothing attends) ------------------------------
+// out[b, h, s, :] = 0 for a (B, H, S, D) bf16 tensor with element strides st; one thread per
+// 16-byte vector, grid.y over (b, h).
+__global__ void __launch_bounds__(256) zero_rows_kernel(bf16_t* out, Strides st, int H, int S,
+                                                        int D, int nbh) {
+  const int d8 = D / 8;
+  for (int bhi = blockIdx.y; bhi < nbh; bhi += gridDim.y) {
+    bf16_t* base = out + (bhi / H) * st.b + (bhi % H) * st.h;
+    for (int x = blockIdx.x * 256 + threadIdx.x; x < S * d8; x += gridDim.x * 256) {
+      const int s = x / d8, c = x - s * d8;
+      *reinterpret_cast<u32x4*>(base + s * st.s + c * 8) = u32x4{0u, 0u, 0u, 0u};
+    }
   }
 }
 

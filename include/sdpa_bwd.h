@@ -12,12 +12,16 @@
  * GQA/MQA: H_kv divides H_q, query head h uses KV head h / (H_q / H_kv), and dK/dV of a KV head
  * sum over its query-head group in a fixed order ("GQA/MQA group reduction").
  *
- * Layout and types.  Every tensor is contiguous (B, H, S, D) with the head dim innermost:
+ * Layout and types.  Every tensor is contiguous (B, H, S, D) with the head dim innermost (any other
+ * dense layout with a contiguous head dim through sdpa_bwd_flex):
  *   q, dq : (B, Hq,  Sq,  Dqk) bf16       k, dk : (B, Hkv, Skv, Dqk) bf16
  *   v, dv : (B, Hkv, Skv, Dv)  bf16       o, dO : (B, Hq,  Sq,  Dv)  bf16
  *   lse   : (B, Hq,  Sq)       fp32, natural log; -inf marks a row that saw no key
  * bf16 values are passed as their 16-bit patterns.  All pointers are device pointers; tensor
- * pointers must be 16-byte aligned (lse 4-byte aligned) and the workspace 256-byte aligned.  Supported head dims (Dqk, Dv): (64,64), (128,128), (192,128), (256,256).
+ * pointers must be 16-byte aligned (lse 4-byte aligned) and the workspace 256-byte aligned; a
+ * tensor with no elements may be NULL.  Supported head dims (Dqk, Dv): (64,64), (128,128),
+ * (192,128), (256,256).  Empty problems (B, Sq or Skv zero) need no workspace: the gradients that
+ * have elements are written as zeros.
  *
  * Masks ("API Usage" and "Causal, sliding-window, and padding masks"): query q and key k are
  * visible together when q < seq_q, k < seq_kv, causal => k <= q + diag + window_right, and
@@ -42,6 +46,7 @@
 #define SDPA_BWD_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -95,6 +100,35 @@ int sdpa_bwd_ex_events(const void* q, const void* k, const void* v, const void* 
                        const int* seq_q_lens, const int* seq_kv_lens, int causal_bottom_right,
                        int window_right, void* workspace, size_t workspace_bytes, void* stream,
                        void* const* events);
+
+/* io element types of sdpa_bwd_flex */
+enum { SDPA_BWD_BF16 = 0, SDPA_BWD_FP16 = 1 };
+
+/* Strides, in elements, of one logical (B, H, S, D) tensor whose head dim is contiguous (stride 1):
+ * "dense_flex" layouts ("SDPA Backward (SM120)", section "API Usage": any dense layout with the
+ * head dim innermost-contiguous, addressed in place).  BHSD contiguous is {H*S*D, S*D, D}; BSHD
+ * (B, S, H, D) storage viewed as (B, H, S, D) is {S*H*D, D, H*D}. */
+typedef struct sdpa_bwd_layout {
+  int64_t batch, head, seq;
+} sdpa_bwd_layout;
+
+/* sdpa_bwd_ex_events with per-tensor layouts and an io dtype.
+ * layouts: NULL (every tensor contiguous BHSD) or 8 entries, in the order q, k, v, o, dO, dq, dk,
+ *   dv.  Each stride must be a multiple of 8 elements (with 16-byte-aligned base pointers every
+ *   row is 16-byte aligned; else SDPA_BWD_UNSUPPORTED), batch/head strides >= 0 and the seq
+ *   stride >= the head dim (else SDPA_BWD_INVALID_ARG), and one head's span,
+ *   ((S - 1) * seq + D) * 2 bytes, below 2^31 (else SDPA_BWD_UNSUPPORTED).  Outputs must not
+ *   overlap each other or the inputs.  lse stays contiguous (B, Hq, Sq); the workspace is the
+ *   same as for sdpa_bwd_ex.
+ * dtype: SDPA_BWD_BF16 for q, k, v, o, dO, dq, dk, dv (fp16 declined with SDPA_BWD_UNSUPPORTED).
+ * events: NULL or five entries as for sdpa_bwd_ex_events. */
+int sdpa_bwd_flex(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                  const float* lse, void* dq, void* dk, void* dv,
+                  int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv,
+                  float scale, int causal, int window_left, int deterministic,
+                  const int* seq_q_lens, const int* seq_kv_lens, int causal_bottom_right,
+                  int window_right, const sdpa_bwd_layout* layouts, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream, void* const* events);
 
 /* Step 1 of the chain alone ("The kernel chain", dot), as the chain runs it: for every query row
  * (rows padded to Sq_pad = Sq rounded up to 32 per (b, h)) write the pair

@@ -29,7 +29,7 @@ def so():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("sdpa_bwd", "sdpa_bwd_ex", "sdpa_bwd_workspace_size", "sdpa_bwd_status_string",
-              "sdpa_bwd_ex_events", "sdpa_bwd_preprocess"):
+              "sdpa_bwd_ex_events", "sdpa_bwd_preprocess", "sdpa_bwd_flex"):
         assert n in names
 
 
@@ -98,6 +98,50 @@ def test_rejections_before_launch(so):
     need = _ws(Sq=64, Skv=64)
     assert _call(so, ws=ctypes.c_void_p(1 << 20), ws_bytes=need - 1) == lib.WORKSPACE_TOO_SMALL
     assert _call(so, ws=ctypes.c_void_p((1 << 20) + 16), ws_bytes=need) == lib.UNSUPPORTED
+
+
+def _flex(so, layouts=None, dtype=lib.BF16, S=64, D=128, ws=None, ws_bytes=0):
+    p = ctypes.c_void_p(4096)  # aligned, never dereferenced: validation fails before any launch
+    return so.sdpa_bwd_flex(p, p, p, p, p, p, p, p, p, 1, 4, 4, S, S, D, D, 0.0, 0, -1, 0, None,
+                            None, 0, 0, layouts, dtype, ws, ws_bytes, None, None)
+
+
+def _bhsd(H=4, S=64, D=128):
+    return (H * S * D, S * D, D)
+
+
+def _lay(entries):
+    arr = (lib.Layout * 8)()
+    for x, e in enumerate(entries):
+        arr[x] = lib.Layout(*e)
+    return arr
+
+
+def test_flex_rejections_before_launch(so):
+    good = [_bhsd()] * 8
+    # contiguous layouts pass every check and stop at the missing workspace
+    assert _flex(so, _lay(good)) == lib.INVALID_ARG
+    assert _flex(so, None) == lib.INVALID_ARG
+    ws = ctypes.c_void_p(1 << 20)
+    need = _ws(Sq=64, Skv=64)
+    assert _flex(so, _lay(good), ws=ws, ws_bytes=need - 1) == lib.WORKSPACE_TOO_SMALL
+    # BSHD storage viewed as BHSD: (S*H*D, D, H*D)
+    bshd = [(64 * 4 * 128, 128, 4 * 128)] * 8
+    assert _flex(so, _lay(bshd), ws=ws, ws_bytes=need - 1) == lib.WORKSPACE_TOO_SMALL
+    assert _flex(so, dtype=lib.FP16) == lib.UNSUPPORTED            # fp16 io is declined
+    assert _flex(so, dtype=7) == lib.UNSUPPORTED
+    for x in range(8):
+        bad = list(good)
+        bad[x] = (good[x][0], good[x][1], 120)                     # rows overlap (seq < D)
+        assert _flex(so, _lay(bad)) == lib.INVALID_ARG
+        bad[x] = (good[x][0], good[x][1], 132)                     # rows not 16-byte aligned
+        assert _flex(so, _lay(bad)) == lib.UNSUPPORTED
+        bad[x] = (good[x][0] + 4, good[x][1], good[x][2])          # batch stride not a multiple of 8
+        assert _flex(so, _lay(bad)) == lib.UNSUPPORTED
+        bad[x] = (-good[x][0], good[x][1], good[x][2])             # negative stride
+        assert _flex(so, _lay(bad)) == lib.INVALID_ARG
+        bad[x] = (good[x][0], good[x][1], 1 << 25)                 # one head spans >= 2^31 bytes
+        assert _flex(so, _lay(bad)) == lib.UNSUPPORTED
 
 
 def test_preprocess_rejections(so):

@@ -1,0 +1,136 @@
+"""GPU parity for strided ("dense_flex") layouts: every tensor is a (B, H, S, D) view with a
+contiguous head dim inside a larger device buffer -- BSHD storage, or rows padded and heads and
+batches separated by gaps -- passed to sdpa_bwd_flex with its own strides.  The expected
+gradients are the fp64 oracle's on the same values (layout does not enter the oracle).  Every
+output buffer is filled with a bf16 NaN sentinel first: the views must be fully overwritten and
+every element outside them must keep the sentinel.
+"""
+import numpy as np
+import pytest
+
+from attention_backward_sdpa_amd import synth
+from tests import _common as C
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+V = synth.small_variant
+SENT = 0x7FC0  # bf16 NaN
+
+
+def strides_of(kind, H, S, D):
+    """(strides in elements, buffer elements per batch entry) of a layout kind."""
+    if kind == "bhsd":
+        return (H * S * D, S * D, D), H * S * D
+    if kind == "bshd":
+        return (S * H * D, D, H * D), S * H * D
+    assert kind == "gappy"  # rows padded by 16 elements, 64 between heads, 128 between batches
+    rs = D + 16
+    hs = S * rs + 64
+    bs = H * hs + 128
+    return (bs, hs, rs), bs
+
+
+def place(bits, kind, fill):
+    """A (B, H, S, D) bf16 view of layout `kind` holding `bits` inside a buffer of `fill`."""
+    B, H, S, D = bits.shape
+    st, per_b = strides_of(kind, H, S, D)
+    buf = torch.full((B * per_b + 64,), fill, dtype=torch.int16, device="cuda")
+    view = buf.view(torch.bfloat16).as_strided((B, H, S, D), st + (1,))
+    src = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda")
+    view.copy_(src.view(torch.bfloat16))
+    return buf, view
+
+
+def covered_mask(buf, view):
+    """Boolean mask of the buffer elements the view covers."""
+    idx = torch.arange(buf.numel(), device="cuda", dtype=torch.int64)
+    hit = torch.zeros(buf.numel(), dtype=torch.bool, device="cuda")
+    hit[idx.as_strided(view.shape, view.stride()).reshape(-1)] = True
+    return hit
+
+
+CASES = [
+    # name, workload, overrides, layouts of (q, k, v, o, do), layouts of (dq, dk, dv)
+    ("bshd_gqa_causal_d128", V(W["gqa_causal_s4096_d128"], B=2, Hq=4, Hkv=2, Sq=200, Skv=200),
+     ["bshd"] * 5, ["bshd"] * 3),
+    ("gappy_mla_window_lens", V(W["mla_window_padded_s4096"], B=2, Hq=2, Hkv=2, Sq=330, Skv=330,
+                                window_left=100, len_lo=100),
+     ["gappy"] * 5, ["gappy"] * 3),
+    ("mixed_d256", V(W["mha_det_s8192_d256"], B=2, Hq=2, Hkv=2, Sq=260, Skv=260, causal=True),
+     ["bshd", "bshd", "gappy", "gappy", "bhsd"], ["bshd", "gappy", "bhsd"]),
+    ("mixed_d64_noncausal", V(W["mha_s128_d64"], B=2, Hq=2, Hkv=1, Sq=150, Skv=150),
+     ["gappy", "bhsd", "bshd", "bhsd", "gappy"], ["gappy", "bshd", "gappy"]),
+]
+
+
+@pytest.mark.parametrize("det", [False, True], ids=["atomic", "det"])
+@pytest.mark.parametrize("case_def", CASES, ids=[c[0] for c in CASES])
+def test_strided_layouts(case_def, det):
+    import attention_backward_sdpa_amd as lib
+    name, w, in_kinds, out_kinds = case_def
+    C.log(f"layout case {name} ({'det' if det else 'atomic'}): {w}")
+    case = C.make_case(w)
+    ref = C.oracle_backward(case)
+    ins = [place(case[x], kind, 0x1234)[1] for x, kind in zip(("q", "k", "v", "o", "do"), in_kinds)]
+    outs = []
+    for like, kind in zip(("q", "k", "v"), out_kinds):
+        shape = case[like].shape
+        buf, view = place(np.zeros(shape, dtype=np.uint16), kind, SENT)
+        view.view(torch.int16).fill_(SENT)
+        outs.append((buf, view))
+    lse = torch.from_numpy(case["lse"]).to("cuda")
+    lens = None if case["lens"] is None else torch.from_numpy(case["lens"]).to("cuda")
+    n = lib.workspace_size(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.Dqk, w.Dv, w.causal, w.window_left,
+                           det, lens is not None)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    lib.sdpa_bwd_ex(*ins, lse, *(v for _, v in outs), scale=w.softmax_scale, causal=w.causal,
+                    window_left=w.window_left, deterministic=det, seq_q_lens=lens,
+                    seq_kv_lens=lens, workspace=ws)
+    torch.cuda.synchronize()
+    for tname, (buf, view), r in zip(("dQ", "dK", "dV"), outs, ref):
+        got = C.bf16_tensor_to_f32(view.contiguous())
+        C.assert_close(f"{name} {tname}", got, r)
+        outside = buf[~covered_mask(buf, view)]
+        assert bool((outside == SENT).all()), f"{name} {tname}: a write landed outside the view"
+
+
+def test_strided_empty_keys_zero_fill():
+    """S_kv = 0: nothing attends, dQ is exactly zero in its own layout and nothing else changes."""
+    import attention_backward_sdpa_amd as lib
+    B, Hq, Hkv, Sq, D = 2, 2, 1, 70, 128
+    mk = lambda H, S, kind: place(np.zeros((B, H, S, D), dtype=np.uint16), kind, SENT)
+    q = mk(Hq, Sq, "bshd")[1]
+    k = mk(Hkv, 0, "bhsd")[1]
+    v = mk(Hkv, 0, "bhsd")[1]
+    o = mk(Hq, Sq, "gappy")[1]
+    do = mk(Hq, Sq, "gappy")[1]
+    dq_buf, dq = mk(Hq, Sq, "gappy")
+    dk = mk(Hkv, 0, "bshd")[1]
+    dv = mk(Hkv, 0, "bshd")[1]
+    lse = torch.zeros((B, Hq, Sq), dtype=torch.float32, device="cuda")
+    lib.sdpa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, causal=False, workspace=None)
+    torch.cuda.synchronize()
+    assert bool((dq.view(torch.int16) == 0).all())
+    assert bool((dq_buf[~covered_mask(dq_buf, dq)] == SENT).all())
+
+
+@pytest.mark.parametrize("shape", [(2, 2, 1, 0, 50), (2, 2, 1, 50, 0), (0, 2, 1, 40, 40)],
+                         ids=["sq0", "skv0", "b0"])
+def test_empty_problems_contiguous(shape):
+    """Degenerate sizes with contiguous tensors and no workspace: the gradients that have elements
+    are exactly zero; torch's empty tensors may carry NULL pointers."""
+    import attention_backward_sdpa_amd as lib
+    B, Hq, Hkv, Sq, Skv = shape
+    D = 64
+    mk = lambda H, S: torch.full((B, H, S, D), 1.0, dtype=torch.bfloat16, device="cuda")
+    q, o, do = mk(Hq, Sq), mk(Hq, Sq), mk(Hq, Sq)
+    k, v = mk(Hkv, Skv), mk(Hkv, Skv)
+    dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
+    lse = torch.zeros((B, Hq, Sq), dtype=torch.float32, device="cuda")
+    assert lib.workspace_size(B, Hq, Hkv, Sq, Skv, D, D) == 0
+    lib.sdpa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, causal=True, workspace=None)
+    torch.cuda.synchronize()
+    for x in (dq, dk, dv):
+        assert bool((x == 0).all())
