@@ -70,10 +70,11 @@ struct MainParams {
   float scale_log2;         // scale * log2(e)
 };
 
-template <int DQK_, int DV_, int KPW_, int NW_, bool DET_>
+template <int DQK_, int DV_, int KPW_, int NW_, bool DET_, bool F16_ = false>
 struct MainCfg {
   static constexpr int DQK = DQK_, DV = DV_, KPW = KPW_, NW = NW_;
   static constexpr bool DET = DET_;
+  static constexpr bool F16 = F16_;  // fp16 io (and fp16 P / dS operands) instead of bf16
   static constexpr int NT = NW * 64, MT = 32, BR = 32, FRAG = 1024;
   static constexpr int BC = NW * KPW;
   static constexpr int NKT = KPW / 32;         // 32-key MFMA tiles per wave
@@ -82,7 +83,7 @@ struct MainCfg {
   // LDS operand reads kept in flight ahead of the MFMAs (fewer where the 256-register budget of
   // the two-waves-per-SIMD layout is nearly full with the head-dim-192 accumulators)
   static constexpr int AHEAD = (NW == 8 && DQK > 128) ? 2 : 6;
-  using M = Mfma<32>;
+  using M = Mfma32<F16>;
   static constexpr int N_DQT = DQK / MT, N_DVT = DV / MT;
   static constexpr int N_KQ = DQK / 16, N_KV = DV / 16;
   // q-tile buffer: [Q A-frags | dO A-frags | stats], fragments swizzled (see gather_frags)
@@ -266,10 +267,10 @@ struct KeyRows {
 
 // Softmax replay and dS for one 32-key MFMA tile of this lane's key column, accumulator groups
 // X0 and X0 + 1 (the q rows of contraction step X0 / 2 of GEMM3/GEMM5):
-// P = exp2(S * scale * log2e - LSE * log2e), dS = P * (dP - delta); both are packed to bf16 pairs
-// in accumulator order (pb/sb[v/2] holds registers v, v+1).  No masking here: on edge tiles
+// P = exp2(S * scale * log2e - LSE * log2e), dS = P * (dP - delta); both are packed to io-type
+// pairs in accumulator order (pb/sb[v/2] holds registers v, v+1).  No masking here: on edge tiles
 // mask_pairs clears the invisible pairs afterwards.
-template <int X0>
+template <bool F16, int X0>
 __device__ __forceinline__ void softmax_ds(const floatx16& S, const floatx16& dP,
                                            const float* sStat, int g, float scale_log2,
                                            uint32_t (&pb)[8], uint32_t (&sb)[8]) {
@@ -286,10 +287,10 @@ __device__ __forceinline__ void softmax_ds(const floatx16& S, const floatx16& dP
       pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * x + e], scale_log2, -l4[e]));
       dv[e] = pv[e] * (dP[4 * x + e] - d4[e]);
     }
-    pb[2 * x] = pack_bf16x2(pv[0], pv[1]);
-    pb[2 * x + 1] = pack_bf16x2(pv[2], pv[3]);
-    sb[2 * x] = pack_bf16x2(dv[0], dv[1]);
-    sb[2 * x + 1] = pack_bf16x2(dv[2], dv[3]);
+    pb[2 * x] = Elem<F16>::pack2(pv[0], pv[1]);
+    pb[2 * x + 1] = Elem<F16>::pack2(pv[2], pv[3]);
+    sb[2 * x] = Elem<F16>::pack2(dv[0], dv[1]);
+    sb[2 * x + 1] = Elem<F16>::pack2(dv[2], dv[3]);
   }
 }
 
@@ -535,8 +536,8 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
       // Softmax replay of all 32 rows, unmasked and branch-free; edge tiles then clear their
       // invisible pairs in the packed words (keeping the masking out of the block the MFMA
       // accumulators flow through avoids register copies at the join).
-      softmax_ds<0>(S, dP, sStat, g, p.scale_log2, pb, sb);
-      softmax_ds<2>(S, dP, sStat, g, p.scale_log2, pb, sb);
+      softmax_ds<C::F16, 0>(S, dP, sStat, g, p.scale_log2, pb, sb);
+      softmax_ds<C::F16, 2>(S, dP, sStat, g, p.scale_log2, pb, sb);
       if (edge) {
         const uint32_t vis_m = visible_rows(KeyRows(mg, q0 + g * 4, key_lane));
         mask_pairs<0>(vis_m, pb, sb);
@@ -594,9 +595,9 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
 #pragma unroll
         for (int r0 = 0; r0 < 16; r0 += 4) {
           const int d = dt * 32 + acc_row<32>(r0, g);
-          *reinterpret_cast<u32x2*>(dkr + d) =
-              u32x2{pack_bf16x2(accK[dt][kt][r0] * p.scale, accK[dt][kt][r0 + 1] * p.scale),
-                    pack_bf16x2(accK[dt][kt][r0 + 2] * p.scale, accK[dt][kt][r0 + 3] * p.scale)};
+          *reinterpret_cast<u32x2*>(dkr + d) = u32x2{
+              Elem<C::F16>::pack2(accK[dt][kt][r0] * p.scale, accK[dt][kt][r0 + 1] * p.scale),
+              Elem<C::F16>::pack2(accK[dt][kt][r0 + 2] * p.scale, accK[dt][kt][r0 + 3] * p.scale)};
         }
 #pragma unroll
       for (int dt = 0; dt < C::N_DVT; ++dt)
@@ -604,8 +605,8 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
         for (int r0 = 0; r0 < 16; r0 += 4) {
           const int d = dt * 32 + acc_row<32>(r0, g);
           *reinterpret_cast<u32x2*>(dvr + d) =
-              u32x2{pack_bf16x2(accV[dt][kt][r0], accV[dt][kt][r0 + 1]),
-                    pack_bf16x2(accV[dt][kt][r0 + 2], accV[dt][kt][r0 + 3])};
+              u32x2{Elem<C::F16>::pack2(accV[dt][kt][r0], accV[dt][kt][r0 + 1]),
+                    Elem<C::F16>::pack2(accV[dt][kt][r0 + 2], accV[dt][kt][r0 + 3])};
         }
     }
   }

@@ -15,6 +15,8 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 
 // Element strides of one logical (B, H, S, D) tensor whose head dim is contiguous ("dense_flex"
 // layouts of "SDPA Backward (SM120)", section "API Usage": any dense layout, addressed in place).
@@ -38,6 +40,42 @@ __device__ __forceinline__ bf16_t float_to_bf16(float x) {
   __bf16 h = (__bf16)x;
   return __builtin_bit_cast(bf16_t, h);
 }
+
+// The io element type ("Support surface": FP16 / BF16), 16-bit patterns in memory (bf16_t holds
+// either).  Float -> element converts round to nearest even (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
+template <bool F16>
+struct Elem {
+  __device__ __forceinline__ static uint32_t pack2(float lo, float hi) {
+    if constexpr (F16) {
+      const half2 v = {(_Float16)lo, (_Float16)hi};
+      return __builtin_bit_cast(uint32_t, v);
+    } else {
+      return pack_bf16x2(lo, hi);
+    }
+  }
+  __device__ __forceinline__ static bf16_t one(float x) {
+    if constexpr (F16) {
+      return __builtin_bit_cast(bf16_t, (_Float16)x);
+    } else {
+      return float_to_bf16(x);
+    }
+  }
+  // the element in bits 0..15 / 16..31 of a word
+  __device__ __forceinline__ static float lo(uint32_t w) {
+    if constexpr (F16) {
+      return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    } else {
+      return __uint_as_float(w << 16);
+    }
+  }
+  __device__ __forceinline__ static float hi(uint32_t w) {
+    if constexpr (F16) {
+      return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    } else {
+      return __uint_as_float(w & 0xffff0000u);
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------------------------
 // MFMA tiles.  MT = 32 selects v_mfma_f32_32x32x16_bf16, MT = 16 selects v_mfma_f32_16x16x32_bf16.
@@ -70,6 +108,20 @@ struct Mfma<16> {
   typedef floatx4 acc_t;
   __device__ __forceinline__ static acc_t mma(bf16x8 a, bf16x8 b, acc_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// 32x32x16 MFMA on bf16 or fp16 operands (v_mfma_f32_32x32x16_bf16 / _f16, same lane layouts);
+// operands travel as 128-bit bf16x8 containers of 16-bit patterns either way.
+template <bool F16>
+struct Mfma32 : Mfma<32> {
+  __device__ __forceinline__ static acc_t mma(bf16x8 a, bf16x8 b, acc_t c) {
+    if constexpr (F16) {
+      return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a),
+                                                    __builtin_bit_cast(half8, b), c, 0, 0, 0);
+    } else {
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
   }
 };
 

@@ -41,9 +41,10 @@ struct Dq2kParams {
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
 
-template <int DQK_, int BC_>
+template <int DQK_, int BC_, bool F16_ = false>
 struct Dq2kCfg {
   static constexpr int DQK = DQK_, BC = BC_, NW = 8;
+  static constexpr bool F16 = F16_;  // fp16 io and dS instead of bf16
   static constexpr int BR = 32, NT = NW * 64, KC = 64;       // KC: keys per chunk
   static constexpr int QT = NW;                              // q tiles per workgroup, one per wave
   static constexpr int N_DT = DQK / 32;                      // 32-column d tiles per wave
@@ -66,8 +67,8 @@ struct Dq2kCfg {
 
 template <class C>
 __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
-  using M = Mfma<32>;
-  using acc_t = M::acc_t;
+  using M = Mfma32<C::F16>;
+  using acc_t = typename M::acc_t;
   constexpr int BR = C::BR, BC = C::BC, DQK = C::DQK, KC = C::KC, QT = C::QT;
   constexpr int CPT = BC / KC;  // chunks per KV tile
   constexpr int AHEAD = C::AHEAD, KR = C::KR, U = C::UNROLL;
@@ -226,7 +227,8 @@ __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int q = q0 + acc_row<32>(r, g);
-        if (q < p.Sq) dqb[(int64_t)q * p.sdq.s + dt * 32 + lc] = float_to_bf16(acc[dt][r] * p.scale);
+        if (q < p.Sq)
+          dqb[(int64_t)q * p.sdq.s + dt * 32 + lc] = Elem<C::F16>::one(acc[dt][r] * p.scale);
       }
     }
   }

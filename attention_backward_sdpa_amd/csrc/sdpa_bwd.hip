@@ -166,24 +166,28 @@ hipError_t launch_dq2k(const Dq2kParams& dp, int grid, hipStream_t s) {
 }
 
 template <int DQK, int DV, int KPW, int NW>
-hipError_t dispatch_main(const MainParams& mp, int det, int grid, int bc, hipStream_t s) {
+hipError_t dispatch_main(const MainParams& mp, int det, bool f16, int grid, int bc, hipStream_t s) {
   // the workspace carve and the grid use the geometry table; the kernel must tile the same way
   if (MainCfg<DQK, DV, KPW, NW, true>::BC != bc) return hipErrorInvalidValue;
+  if (f16) {
+    if (det) return launch_main<MainCfg<DQK, DV, KPW, NW, true, true>>(mp, grid, s);
+    return launch_main<MainCfg<DQK, DV, KPW, NW, false, true>>(mp, grid, s);
+  }
   if (det) return launch_main<MainCfg<DQK, DV, KPW, NW, true>>(mp, grid, s);
   return launch_main<MainCfg<DQK, DV, KPW, NW, false>>(mp, grid, s);
 }
 
-hipError_t run_main(int Dqk, int Dv, const MainParams& mp, int det, int grid, int bc,
+hipError_t run_main(int Dqk, int Dv, const MainParams& mp, int det, bool f16, int grid, int bc,
                     hipStream_t s) {
-  if (Dqk == 64) return dispatch_main<64, 64, 32, 8>(mp, det, grid, bc, s);
-  if (Dqk == 128) return dispatch_main<128, 128, 32, 8>(mp, det, grid, bc, s);
-  if (Dqk == 192) return dispatch_main<192, 128, 32, 8>(mp, det, grid, bc, s);
-  return dispatch_main<256, 256, 32, 4>(mp, det, grid, bc, s);
+  if (Dqk == 64) return dispatch_main<64, 64, 32, 8>(mp, det, f16, grid, bc, s);
+  if (Dqk == 128) return dispatch_main<128, 128, 32, 8>(mp, det, f16, grid, bc, s);
+  if (Dqk == 192) return dispatch_main<192, 128, 32, 8>(mp, det, f16, grid, bc, s);
+  return dispatch_main<256, 256, 32, 4>(mp, det, f16, grid, bc, s);
 }
 
-template <int DQK, int BC>
+template <int DQK, int BC, bool F16>
 hipError_t dispatch_dq2k(const Dq2kParams& dp, int bc, hipStream_t s) {
-  using C = Dq2kCfg<DQK, BC>;
+  using C = Dq2kCfg<DQK, BC, F16>;
   if (BC != bc) return hipErrorInvalidValue;  // must read the dS blocks the main kernel wrote
   // one workgroup per group of C::QT consecutive q tiles of one (batch, query head)
   const int64_t grid = (int64_t)((dp.n_q_tiles + C::QT - 1) / C::QT) * dp.B * dp.Hq;
@@ -191,29 +195,44 @@ hipError_t dispatch_dq2k(const Dq2kParams& dp, int bc, hipStream_t s) {
   return launch_dq2k<C>(dp, (int)grid, s);
 }
 
-hipError_t run_dq2k(int Dqk, const Dq2kParams& dp, int bc, hipStream_t s) {
-  if (Dqk == 64) return dispatch_dq2k<64, 256>(dp, bc, s);
-  if (Dqk == 128) return dispatch_dq2k<128, 256>(dp, bc, s);
-  if (Dqk == 192) return dispatch_dq2k<192, 256>(dp, bc, s);
-  return dispatch_dq2k<256, 128>(dp, bc, s);
+template <bool F16>
+hipError_t run_dq2k_t(int Dqk, const Dq2kParams& dp, int bc, hipStream_t s) {
+  if (Dqk == 64) return dispatch_dq2k<64, 256, F16>(dp, bc, s);
+  if (Dqk == 128) return dispatch_dq2k<128, 256, F16>(dp, bc, s);
+  if (Dqk == 192) return dispatch_dq2k<192, 256, F16>(dp, bc, s);
+  return dispatch_dq2k<256, 128, F16>(dp, bc, s);
 }
 
-hipError_t launch_convert(const ConvertParams& cp, int Dqk, int grid, hipStream_t s) {
-  if (Dqk == 64) hipLaunchKernelGGL((dq_convert_kernel<64>), dim3(grid), dim3(256), 0, s, cp);
-  else if (Dqk == 128) hipLaunchKernelGGL((dq_convert_kernel<128>), dim3(grid), dim3(256), 0, s, cp);
-  else if (Dqk == 192) hipLaunchKernelGGL((dq_convert_kernel<192>), dim3(grid), dim3(256), 0, s, cp);
-  else hipLaunchKernelGGL((dq_convert_kernel<256>), dim3(grid), dim3(256), 0, s, cp);
+hipError_t run_dq2k(int Dqk, bool f16, const Dq2kParams& dp, int bc, hipStream_t s) {
+  return f16 ? run_dq2k_t<true>(Dqk, dp, bc, s) : run_dq2k_t<false>(Dqk, dp, bc, s);
+}
+
+template <bool F16>
+hipError_t launch_convert_t(const ConvertParams& cp, int Dqk, int grid, hipStream_t s) {
+  if (Dqk == 64) hipLaunchKernelGGL((dq_convert_kernel<64, F16>), dim3(grid), dim3(256), 0, s, cp);
+  else if (Dqk == 128) hipLaunchKernelGGL((dq_convert_kernel<128, F16>), dim3(grid), dim3(256), 0, s, cp);
+  else if (Dqk == 192) hipLaunchKernelGGL((dq_convert_kernel<192, F16>), dim3(grid), dim3(256), 0, s, cp);
+  else hipLaunchKernelGGL((dq_convert_kernel<256, F16>), dim3(grid), dim3(256), 0, s, cp);
   return hipGetLastError();
 }
 
-hipError_t launch_preprocess(const PreParams& pp, int Dqk, int Dv, int64_t tiles, hipStream_t s) {
+hipError_t launch_convert(const ConvertParams& cp, int Dqk, bool f16, int grid, hipStream_t s) {
+  return f16 ? launch_convert_t<true>(cp, Dqk, grid, s) : launch_convert_t<false>(cp, Dqk, grid, s);
+}
+
+template <bool F16>
+void launch_preprocess_t(const PreParams& pp, int Dv, dim3 grid, hipStream_t s) {
+  const dim3 block(256);
+  if (Dv == 64) hipLaunchKernelGGL((preprocess_kernel<64, F16>), grid, block, 0, s, pp);
+  else if (Dv == 128) hipLaunchKernelGGL((preprocess_kernel<128, F16>), grid, block, 0, s, pp);
+  else hipLaunchKernelGGL((preprocess_kernel<256, F16>), grid, block, 0, s, pp);
+}
+
+hipError_t launch_preprocess(const PreParams& pp, int Dv, bool f16, int64_t tiles, hipStream_t s) {
   if (tiles == 0) return hipSuccess;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)tiles), block(256);
-  (void)Dqk;
-  if (Dv == 64) hipLaunchKernelGGL((preprocess_kernel<64>), grid, block, 0, s, pp);
-  else if (Dv == 128) hipLaunchKernelGGL((preprocess_kernel<128>), grid, block, 0, s, pp);
-  else hipLaunchKernelGGL((preprocess_kernel<256>), grid, block, 0, s, pp);
+  if (f16) launch_preprocess_t<true>(pp, Dv, dim3((unsigned)tiles), s);
+  else launch_preprocess_t<false>(pp, Dv, dim3((unsigned)tiles), s);
   return hipGetLastError();
 }
 
@@ -244,7 +263,8 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   int st = validate(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, window_left,
                     window_right, &geo);
   if (st != SDPA_BWD_OK) return st;
-  if (dtype != SDPA_BWD_BF16) return SDPA_BWD_UNSUPPORTED;
+  if (dtype != SDPA_BWD_BF16 && dtype != SDPA_BWD_FP16) return SDPA_BWD_UNSUPPORTED;
+  const bool f16 = dtype == SDPA_BWD_FP16;
   Layouts L = contiguous_layouts(Hq, Hkv, Sq, Skv, Dqk, Dv);
   if (layouts)
     for (int x = 0; x < N_TENSORS; ++x)
@@ -294,7 +314,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   pp.sq_pad = (int)c.sq_pad;
   pp.Dqk = Dqk;
   pp.zero_rows = det ? 0 : 1;
-  e = launch_preprocess(pp, Dqk, Dv, (int64_t)B * Hq * (c.sq_pad / geo.br), stream);
+  e = launch_preprocess(pp, Dv, f16, (int64_t)B * Hq * (c.sq_pad / geo.br), stream);
   if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   rec(1);
 
@@ -335,7 +355,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   mp.scale_log2 = scale * kLog2e;
   const int64_t main_grid = (int64_t)mp.n_kv_tiles * split * B * Hq;
   if (main_grid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
-  e = run_main(Dqk, Dv, mp, det, (int)main_grid, geo.bc, stream);
+  e = run_main(Dqk, Dv, mp, det, f16, (int)main_grid, geo.bc, stream);
   if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   rec(2);
 
@@ -357,7 +377,10 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     int64_t bx = (per_head + 255) / 256;
     bx = bx > 4096 ? 4096 : bx;
     const int by = rp.n_kvh > 65535 ? 65535 : rp.n_kvh;
-    hipLaunchKernelGGL(gqa_reduce_kernel, dim3((unsigned)bx, by), dim3(256), 0, stream, rp);
+    if (f16)
+      hipLaunchKernelGGL(gqa_reduce_kernel<true>, dim3((unsigned)bx, by), dim3(256), 0, stream, rp);
+    else
+      hipLaunchKernelGGL(gqa_reduce_kernel<false>, dim3((unsigned)bx, by), dim3(256), 0, stream, rp);
     if (hipGetLastError() != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   }
   rec(3);
@@ -373,7 +396,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     cp.scale = scale;
     const int64_t cgrid = (int64_t)B * Hq * ((Sq + 31) / 32);
     if (cgrid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
-    e = launch_convert(cp, Dqk, (int)cgrid, stream);
+    e = launch_convert(cp, Dqk, f16, (int)cgrid, stream);
     if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   } else {
     Dq2kParams dp;
@@ -397,7 +420,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     dp.n_kv_tiles = mp.n_kv_tiles;
     dp.n_q_tiles = (int)(c.sq_pad / geo.br);
     dp.scale = scale;
-    e = run_dq2k(Dqk, dp, geo.bc, stream);
+    e = run_dq2k(Dqk, f16, dp, geo.bc, stream);
     if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   }
   rec(4);
@@ -490,7 +513,7 @@ int sdpa_bwd_preprocess(const void* o, const void* dO, const float* lse, float* 
   pp.Dqk = Dqk;
   pp.zero_rows = dq_accum ? 1 : 0;
   const int64_t tiles = (int64_t)B * Hq * (pp.sq_pad / 32);
-  return launch_preprocess(pp, Dqk, Dv, tiles, (hipStream_t)stream) == hipSuccess
+  return launch_preprocess(pp, Dv, false, tiles, (hipStream_t)stream) == hipSuccess
              ? SDPA_BWD_OK
              : SDPA_BWD_LAUNCH_FAILED;
 }

@@ -28,7 +28,7 @@ struct PreParams {
   int zero_rows;
 };
 
-template <int DV>
+template <int DV, bool F16>
 __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
   constexpr int BR = 32;
   constexpr int LPR = DV / 8;              // lanes per row for the row dot
@@ -53,8 +53,8 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
       const u32x4 c = *reinterpret_cast<const u32x4*>(dob + s * p.sdo.s + sub * 8);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc += __uint_as_float(a[e] << 16) * __uint_as_float(c[e] << 16);
-        acc += __uint_as_float(a[e] & 0xffff0000u) * __uint_as_float(c[e] & 0xffff0000u);
+        acc += Elem<F16>::lo(a[e]) * Elem<F16>::lo(c[e]);
+        acc += Elem<F16>::hi(a[e]) * Elem<F16>::hi(c[e]);
       }
     }
 #pragma unroll
@@ -86,7 +86,7 @@ struct ConvertParams {
   float scale;
 };
 
-template <int DQK>
+template <int DQK, bool F16>
 __global__ void __launch_bounds__(256) dq_convert_kernel(ConvertParams p) {
   constexpr int V = DQK / 8;  // 8-element vectors per row
   const int nt = (p.Sq + 31) / 32;
@@ -104,8 +104,8 @@ __global__ void __launch_bounds__(256) dq_convert_kernel(ConvertParams p) {
       const floatx4 a = reinterpret_cast<const floatx4*>(p.acc)[2 * x];
       const floatx4 d = reinterpret_cast<const floatx4*>(p.acc)[2 * x + 1];
       const float k = p.scale;
-      out = u32x4{pack_bf16x2(a[0] * k, a[1] * k), pack_bf16x2(a[2] * k, a[3] * k),
-                  pack_bf16x2(d[0] * k, d[1] * k), pack_bf16x2(d[2] * k, d[3] * k)};
+      out = u32x4{Elem<F16>::pack2(a[0] * k, a[1] * k), Elem<F16>::pack2(a[2] * k, a[3] * k),
+                  Elem<F16>::pack2(d[0] * k, d[1] * k), Elem<F16>::pack2(d[2] * k, d[3] * k)};
     }
     *reinterpret_cast<u32x4*>(dqb + s * p.sdq.s + c * 8) = out;
   }
@@ -127,6 +127,7 @@ struct ReduceParams {
   int group;                 // partial slots per KV head, summed in this order
 };
 
+template <bool F16>
 __global__ void __launch_bounds__(256) gqa_reduce_kernel(ReduceParams p) {
   const int k8 = p.Dqk / 8, v8 = p.Dv / 8;
   const int nk = p.Skv * k8, nv = p.Skv * v8;  // vectors per head (the host keeps these < 2^28)
@@ -144,15 +145,15 @@ __global__ void __launch_bounds__(256) gqa_reduce_kernel(ReduceParams p) {
         const u32x4 v = src[(int64_t)gi * per];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          s[2 * e] += __uint_as_float(v[e] << 16);
-          s[2 * e + 1] += __uint_as_float(v[e] & 0xffff0000u);
+          s[2 * e] += Elem<F16>::lo(v[e]);
+          s[2 * e + 1] += Elem<F16>::hi(v[e]);
         }
       }
       const Strides& st = isk ? p.sdk : p.sdv;
       bf16_t* dst = (isk ? p.dk : p.dv) + b * st.b + kvh * st.h + key * st.s + c * 8;
       *reinterpret_cast<u32x4*>(dst) =
-          u32x4{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]), pack_bf16x2(s[4], s[5]),
-                pack_bf16x2(s[6], s[7])};
+          u32x4{Elem<F16>::pack2(s[0], s[1]), Elem<F16>::pack2(s[2], s[3]),
+                Elem<F16>::pack2(s[4], s[5]), Elem<F16>::pack2(s[6], s[7])};
     }
   }
 }

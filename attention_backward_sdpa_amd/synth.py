@@ -2,8 +2,8 @@
 CPU oracle's callers.
 
 This module holds no arithmetic of the attention method: it draws random numbers, rounds them to
-bfloat16 (round-to-nearest-even, from the definition of the format) and describes the workload
-shapes.  It imports nothing else from this package, so it can be used without the GPU library.
+bfloat16 (round-to-nearest-even, from the definition of the format) or to IEEE binary16 (numpy's
+own round-to-nearest-even conversion) and describes the workload shapes.  It imports nothing else from this package, so it can be used without the GPU library.
 The forward outputs O and LSE that the backward consumes are not made here; the caller obtains
 them from a forward pass of its choice.
 """
@@ -70,6 +70,27 @@ def bf16_to_f32(bits) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def fp16_bits(x) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (round to nearest, ties to even); uint16 bit patterns."""
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(f)):
+        raise ValueError("fp16_bits expects finite values")
+    h = f.astype(np.float16)
+    if not np.all(np.isfinite(h)):
+        raise ValueError("fp16_bits: value outside the binary16 range")
+    return h.view(np.uint16)
+
+
+def fp16_to_f32(bits) -> np.ndarray:
+    """Exact float32 value of binary16 bit patterns."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def bits_to_f32(bits, dtype: str = "bf16") -> np.ndarray:
+    """Exact float32 value of 16-bit patterns of the given io type ("bf16" or "fp16")."""
+    return fp16_to_f32(bits) if dtype == "fp16" else bf16_to_f32(bits)
+
+
 def round_bf16(x) -> np.ndarray:
     """float32 -> nearest bfloat16 value, returned as float32."""
     return bf16_to_f32(bf16_bits(x))
@@ -87,8 +108,9 @@ class Inputs:
     extra: dict = field(default_factory=dict)
 
 
-def draw_inputs(w: Workload, seed: Optional[int] = None) -> Inputs:
-    """Q, K, V, dO iid input_scale * N(0,1) in float32, rounded to bf16; lengths drawn first.
+def draw_inputs(w: Workload, seed: Optional[int] = None, dtype: str = "bf16") -> Inputs:
+    """Q, K, V, dO iid input_scale * N(0,1) in float32, rounded to bf16 (or to fp16 with
+    dtype="fp16"); lengths drawn first.
 
     Lengths (padded workloads) are uniform integers in [len_lo, Sq], seq_q = seq_kv.  Rows past a
     batch entry's length are still filled with random values, so any leak through the padding
@@ -103,7 +125,7 @@ def draw_inputs(w: Workload, seed: Optional[int] = None) -> Inputs:
         x = rng.standard_normal(shape, dtype=np.float32)
         if w.input_scale != 1.0:
             x *= np.float32(w.input_scale)
-        return bf16_bits(x)
+        return fp16_bits(x) if dtype == "fp16" else bf16_bits(x)
 
     q = draw((w.B, w.Hq, w.Sq, w.Dqk))
     k = draw((w.B, w.Hkv, w.Skv, w.Dqk))

@@ -120,7 +120,10 @@ typedef struct sdpa_bwd_layout {
  *   ((S - 1) * seq + D) * 2 bytes, below 2^31 (else SDPA_BWD_UNSUPPORTED).  Outputs must not
  *   overlap each other or the inputs.  lse stays contiguous (B, Hq, Sq); the workspace is the
  *   same as for sdpa_bwd_ex.
- * dtype: SDPA_BWD_BF16 for q, k, v, o, dO, dq, dk, dv (fp16 declined with SDPA_BWD_UNSUPPORTED).
+ * dtype: the element type of q, k, v, o, dO, dq, dk, dv ("Support surface": FP16 / BF16, LSE
+ *   fp32): SDPA_BWD_BF16, or SDPA_BWD_FP16, for which P and dS enter the MFMAs as fp16 and the
+ *   GQA partials and the deterministic dS workspace are fp16 too (accumulation stays fp32);
+ *   any other value gives SDPA_BWD_UNSUPPORTED.
  * events: NULL or five entries as for sdpa_bwd_ex_events. */
 int sdpa_bwd_flex(const void* q, const void* k, const void* v, const void* o, const void* dO,
                   const float* lse, void* dq, void* dk, void* dv,

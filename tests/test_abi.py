@@ -128,8 +128,8 @@ def test_flex_rejections_before_launch(so):
     # BSHD storage viewed as BHSD: (S*H*D, D, H*D)
     bshd = [(64 * 4 * 128, 128, 4 * 128)] * 8
     assert _flex(so, _lay(bshd), ws=ws, ws_bytes=need - 1) == lib.WORKSPACE_TOO_SMALL
-    assert _flex(so, dtype=lib.FP16) == lib.UNSUPPORTED            # fp16 io is declined
-    assert _flex(so, dtype=7) == lib.UNSUPPORTED
+    assert _flex(so, dtype=lib.FP16) == lib.INVALID_ARG            # fp16 accepted (no workspace)
+    assert _flex(so, dtype=7) == lib.UNSUPPORTED                   # unknown io type
     for x in range(8):
         bad = list(good)
         bad[x] = (good[x][0], good[x][1], 120)                     # rows overlap (seq < D)
