@@ -65,10 +65,11 @@ def algorithmic_flops(w, lens):
 
 
 def gpu_forward_inputs(torch, q, k, v, w, lens):
-    """float32 forward on the GPU -> O (bf16) and natural-log LSE (fp32), rows with no key -inf."""
+    """float32 forward on the GPU -> O (in q's io type) and natural-log LSE (fp32), rows with no
+    key -inf."""
     B, Hq, Sq, _ = q.shape
     group = w.Hq // w.Hkv
-    o = torch.empty(B, Hq, Sq, w.Dv, dtype=torch.bfloat16, device=q.device)
+    o = torch.empty(B, Hq, Sq, w.Dv, dtype=q.dtype, device=q.device)
     lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
     i = torch.arange(Sq, device=q.device)[:, None]
     j = torch.arange(w.Skv, device=q.device)[None, :]
@@ -86,7 +87,7 @@ def gpu_forward_inputs(torch, q, k, v, w, lens):
             s = s.masked_fill(~vis, float("-inf"))
             l = torch.logsumexp(s, dim=-1)
             p = torch.where(vis, torch.exp(s - torch.where(torch.isinf(l), 0.0, l)[:, None]), 0.0)
-            o[b, h] = (p @ v[b, kh].float()).to(torch.bfloat16)
+            o[b, h] = (p @ v[b, kh].float()).to(q.dtype)
             lse[b, h] = l
     return o, lse
 
@@ -147,11 +148,11 @@ def _pmc_means(directory, counter):
     return {name: (sum(v) / len(v), len(v)) for name, v in out.items()}
 
 
-def write_traffic_record(workload, det_arg, fetch_dir, write_dir):
+def write_traffic_record(workload, det_arg, dtype, fetch_dir, write_dir):
     w = synth.WORKLOADS[workload]
     det = w.deterministic if det_arg < 0 else bool(det_arg)
     rec = {"kernel_source_hash": kernel_source_hash(), "workload": w.name, "deterministic": det,
-           "copy_probe_bytes": COPY_PROBE_BYTES}
+           "dtype": dtype, "copy_probe_bytes": COPY_PROBE_BYTES}
     total = 0.0
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         means = _pmc_means(d, counter)
@@ -175,7 +176,7 @@ def write_traffic_record(workload, det_arg, fetch_dir, write_dir):
     print(json.dumps(rec, indent=1))
 
 
-def cpu_baseline(w, inp, lens, budget_s=15.0):
+def cpu_baseline(w, inp, lens, dtype="bf16", budget_s=15.0):
     """The fp64 CPU oracle (unchanged) on the first query heads of batch entry 0, timed until
     about budget_s seconds of work; the rate is scaled to the same FLOP convention."""
     import oracle
@@ -185,7 +186,8 @@ def cpu_baseline(w, inp, lens, budget_s=15.0):
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
     group = w.Hq // w.Hkv
-    f = lambda x: synth.bf16_to_f32(x).astype(np.float64)
+    f = lambda x: synth.bits_to_f32(x, dtype).astype(np.float64)
+    to_io = synth.fp16_bits if dtype == "fp16" else synth.bf16_bits
     L = None if lens is None else [int(lens[0])]
     flops = done = 0.0
     heads = 0
@@ -197,7 +199,7 @@ def cpu_baseline(w, inp, lens, budget_s=15.0):
         q, kk, vv, do = f(sl(inp.q, h)), f(sl(inp.k, kh)), f(sl(inp.v, kh)), f(sl(inp.do, h))
         o, lse = oracle.forward(q, kk, vv, w.softmax_scale, causal=w.causal,
                                 window_left=w.window_left, seq_q_lens=L, seq_kv_lens=L)
-        o = synth.round_bf16(o.astype(np.float32)).astype(np.float64)
+        o = f(to_io(o.astype(np.float32)))
         lse = lse.astype(np.float32).astype(np.float64)
         t0 = time.perf_counter()
         oracle.backward(q, kk, vv, o, do, lse, w.softmax_scale, causal=w.causal,
@@ -220,6 +222,8 @@ def main():
     ap.add_argument("--workload", default="gqa_causal_s4096_d128", choices=list(synth.WORKLOADS))
     ap.add_argument("--deterministic", type=int, default=-1,
                     help="override the workload's dQ route (-1: as the workload states)")
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"],
+                    help="io element type of Q, K, V, O, dO and the gradients")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run a plain 1 GiB fp32 copy kernel three times "
@@ -232,7 +236,7 @@ def main():
                          "of a --copy-probe run and write the main kernel's HBM traffic record")
     args = ap.parse_args()
     if args.traffic_from:
-        write_traffic_record(args.workload, args.deterministic, *args.traffic_from)
+        write_traffic_record(args.workload, args.deterministic, args.dtype, *args.traffic_from)
         return
     if args.atomic_probe:
         atomic_probe()
@@ -248,10 +252,11 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     det = w.deterministic if args.deterministic < 0 else bool(args.deterministic)
-    inp = synth.draw_inputs(w)
+    inp = synth.draw_inputs(w, dtype=args.dtype)
     lens = inp.seq_q_lens
     dev = torch.device("cuda:0")
-    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    io = torch.float16 if args.dtype == "fp16" else torch.bfloat16
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(io).to(dev)
     q, k, v, do = bf(inp.q), bf(inp.k), bf(inp.v), bf(inp.do)
     o, lse = gpu_forward_inputs(torch, q, k, v, w, lens)
     lens_t = None if lens is None else torch.from_numpy(lens).to(dev)
@@ -309,7 +314,7 @@ def main():
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
         if t.get("kernel_source_hash") == kernel_source_hash() and t.get("workload") == w.name \
-                and bool(t.get("deterministic")) == det:
+                and bool(t.get("deterministic")) == det and t.get("dtype", "bf16") == args.dtype:
             traffic = t["hbm_bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         traffic = None
@@ -325,7 +330,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq,
@@ -344,7 +349,7 @@ def main():
     if args.copy_probe:
         copy_probe(torch, dev)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inp, lens)
+        out["cpu_baseline"] = cpu_baseline(w, inp, lens, args.dtype)
     print(json.dumps(out), flush=True)
 
 
