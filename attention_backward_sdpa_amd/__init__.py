@@ -14,6 +14,8 @@ LIB_PATH = os.path.join(_HERE, "libsdpa_bwd.so")
 
 OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, LAUNCH_FAILED = 0, 1, 2, 3, 4
 BF16, FP16 = 0, 1
+# values of the `deterministic` argument (dQ routes); False / True are 0 / 1
+DQ_ATOMIC, DQ_DETERMINISTIC, DQ_DS_PANELS, DQ_PARTIALS = 0, 1, 2, 3
 
 
 class Layout(ctypes.Structure):
@@ -52,6 +54,8 @@ def _load():
     lib.sdpa_bwd_flex.restype = i
     lib.sdpa_bwd_preprocess.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.sdpa_bwd_preprocess.restype = i
+    lib.sdpa_bwd_dq_route.argtypes = [i, i, i]
+    lib.sdpa_bwd_dq_route.restype = i
     lib.sdpa_bwd_status_string.argtypes = [i]
     lib.sdpa_bwd_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -89,6 +93,12 @@ def workspace_size(B, Hq, Hkv, Sq, Skv, Dqk, Dv, causal=False, window_left=-1,
     return int(_load().sdpa_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, Dqk, Dv, int(causal),
                                                int(window_left), int(deterministic),
                                                int(has_seqlens)))
+
+
+def dq_route(Dqk, Dv, deterministic) -> int:
+    """sdpa_bwd_dq_route(): the dQ route (DQ_ATOMIC, DQ_DS_PANELS or DQ_PARTIALS) a call takes,
+    -1 for unsupported arguments."""
+    return int(_load().sdpa_bwd_dq_route(int(Dqk), int(Dv), int(deterministic)))
 
 
 def _dims(q, k, v):

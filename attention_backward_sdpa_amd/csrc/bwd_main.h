@@ -9,9 +9,12 @@
 //     GEMM5  dK += dS^T Q      (bf16 dS)
 //     GEMM4  dQ  = dS K  -> fp32 atomic add into dq_accum
 // dK/dV stay in registers for the whole pass and are written once (dK scaled by the softmax
-// scale).  On the deterministic route ("Deterministic vs. non-deterministic dQ") GEMM4 and the
-// atomics are replaced by a store of the unscaled bf16 dS tile to a workspace that the dq2k
-// kernel reduces in ascending KV order.
+// scale).  The deterministic routes ("Deterministic vs. non-deterministic dQ": per-KV-tile
+// partials, then an ordered reduction) replace the atomics by plain stores, either
+//   * of the unscaled bf16 dS tile (GEMM4 moves to the dq2k kernel, which reduces in ascending KV
+//     order), or
+//   * of GEMM4's fp32 result, one 32 x Dqk dQ partial per (KV tile, q tile), which the dq_reduce
+//     kernel sums in ascending KV order.
 //
 // MI355X mapping (differs from the pages' SM120 warp-specialised design):
 //   * NW waves of 64 lanes; wave w owns KPW = 32 keys, so the key tile is BC = 32 * NW.  At head
@@ -35,9 +38,9 @@
 //   * The wave's V slice is held in registers as the B operand of GEMM2.
 //   * Deterministic route: each lane stores its bf16 dS values straight from registers as 8-byte
 //     quads (512 contiguous bytes per instruction, non-temporal); no LDS round trip.
-//   * fp32-atomic route: dS is written to LDS in the same register order and GEMM4 reads it (and
-//     K) with ds_read_b64_tr_b16.  GEMM4 of q tile i runs at the start of the next iteration so
-//     its atomics drain while that iteration computes.
+//   * fp32-atomic and dQ-partial routes: dS is written to LDS in the same register order and
+//     GEMM4 reads it (and K) with ds_read_b64_tr_b16.  GEMM4 of q tile i runs at the start of the
+//     next iteration so its atomics (or partial stores) drain while that iteration computes.
 //   * The preprocess kernel supplies LSE * log2(e) per row (+inf for rows without keys), so the
 //     replay is one FMA and one v_exp_f32 per element.
 #pragma once
@@ -55,6 +58,7 @@ struct MainParams {
   Strides sdk, sdv;         // of dk, dv (used when dK/dV are written directly, not as partials)
   const float* stats;       // (B*Hq, sq_pad, 2): [LSE*log2e or +inf, delta] per q row
   float* dq_accum;          // (B, Hq, Sq, Dqk) fp32, non-deterministic route
+  float* dqp_ws;            // (B*Hq, n_kv_tiles, sq_pad/32) blocks of 32 x Dqk fp32 dQ partials
   bf16_t* ds_ws;            // (B*Hq, n_kv_tiles, sq_pad/32) blocks of BC x 32 bf16 dS
   bf16_t* dk_out;           // dK: (B, Hkv, Skv, Dqk), or partials (B, Hq, n_split, Skv, Dqk)
   bf16_t* dv_out;           // dV: likewise with Dv
@@ -70,16 +74,25 @@ struct MainParams {
   float scale_log2;         // scale * log2(e)
 };
 
-template <int DQK_, int DV_, int KPW_, int NW_, bool DET_, bool F16_ = false>
+// How the main kernel emits dQ.
+enum DqMode {
+  DQ_ATOMIC = 0,   // GEMM4 in the kernel, fp32 atomic adds into dq_accum
+  DQ_DS = 1,       // no GEMM4: bf16 dS tiles to the workspace (dq2k reduces)
+  DQ_PARTIAL = 2,  // GEMM4 in the kernel, fp32 partial tiles to the workspace (dq_reduce sums)
+};
+
+template <int DQK_, int DV_, int KPW_, int NW_, int MODE_, bool F16_ = false>
 struct MainCfg {
   static constexpr int DQK = DQK_, DV = DV_, KPW = KPW_, NW = NW_;
-  static constexpr bool DET = DET_;
+  static constexpr int MODE = MODE_;
+  static constexpr bool DS_OUT = MODE == DQ_DS;  // dS leaves the kernel, GEMM4 does not run here
+  static constexpr bool G4 = !DS_OUT;            // GEMM4 runs here (dS staged in LDS)
   static constexpr bool F16 = F16_;  // fp16 io (and fp16 P / dS operands) instead of bf16
   static constexpr int NT = NW * 64, MT = 32, BR = 32, FRAG = 1024;
   static constexpr int BC = NW * KPW;
   static constexpr int NKT = KPW / 32;         // 32-key MFMA tiles per wave
   static constexpr bool KREG = DQK >= 192 && NW == 4;  // GEMM1's K operand from registers
-  static constexpr bool KLDS = !KREG || !DET;  // K fragments in LDS (GEMM1 and/or GEMM4)
+  static constexpr bool KLDS = !KREG || G4;  // K fragments in LDS (GEMM1 and/or GEMM4)
   // LDS operand reads kept in flight ahead of the MFMAs (fewer where the 256-register budget of
   // the two-waves-per-SIMD layout is nearly full with the head-dim-192 accumulators)
   static constexpr int AHEAD = (NW == 8 && DQK > 128) ? 2 : 6;
@@ -92,12 +105,16 @@ struct MainCfg {
   static constexpr int T_ST = T_OA + N_KV * FRAG;
   static constexpr int TILE_BYTES = T_ST + 2 * BR * 4;
   static constexpr int SK_BYTES = KLDS ? BC * DQK * 2 : 0;
-  static constexpr int SST_BYTES = DET ? 0 : BC * BR * 2;
+  static constexpr int SST_BYTES = G4 ? BC * BR * 2 : 0;
   static constexpr int NBUF = (SK_BYTES + 2 * TILE_BYTES + SST_BYTES <= 160 * 1024) ? 2 : 1;
+  // dS staging for GEMM4, double-buffered by q-tile parity where LDS allows: GEMM4 of the previous
+  // q tile then needs no barrier of its own and overlaps the other waves' work
+  static constexpr int NSST =
+      (G4 && SK_BYTES + NBUF * TILE_BYTES + 2 * SST_BYTES <= 160 * 1024) ? 2 : 1;
   static constexpr int OFF_K = 0;
   static constexpr int OFF_T = OFF_K + SK_BYTES;
   static constexpr int OFF_ST = OFF_T + NBUF * TILE_BYTES;
-  static constexpr int LDS_BYTES = OFF_ST + SST_BYTES;
+  static constexpr int LDS_BYTES = OFF_ST + NSST * SST_BYTES;
   static_assert(KPW == 32, "one 32-key MFMA tile per wave (the q-tile loop body assumes it)");
   static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
   static_assert(DQK % 64 == 0 && DV % 64 == 0, "head dims must be multiples of 64");
@@ -345,14 +362,21 @@ struct TrALanes {
   }
 };
 
-// GEMM4 of the fp32-atomic route for one q tile: dQ (32 q x Dqk) = dS K over the tile's keys,
-// added into dq_accum with fp32 atomics.  dS sits in sST in register order (block (w,kt,x) of
-// 64 lanes x 4 q, see the writer) and K in sK as B fragments of GEMM1; both are read with the
-// transpose instruction.  Wave w handles the 32-column d tiles w, w + NW, ... (with 8 waves only
-// waves 0-3 have a tile; each shares its SIMD with a wave that has none).
+// GEMM4 for one q tile: dQ (32 q x Dqk) = dS K over the tile's keys.  dS sits in sST in register
+// order (block (w,kt,x) of 64 lanes x 4 q, see the writer) and K in sK as B fragments of GEMM1;
+// both are read with the transpose instruction.  Wave w handles the 32-column d tiles w, w + NW,
+// ... (with 8 waves and Dqk = 128 only waves 0-3 have a tile; each shares its SIMD with a wave
+// that has none).  The result leaves the kernel as
+//   * DQ_ATOMIC: fp32 atomic adds into the dq_accum rows starting at `dst` (row q0); rows at or
+//     past Lq are skipped;
+//   * DQ_PARTIAL: plain non-temporal stores of the tile's partial block at `dst`: d tile dt is
+//     4 KiB at float offset 1024 dt, lane l's accumulator registers 4x .. 4x + 3 (rows
+//     8x + 4(l / 32) + 0..3, column 32 dt + l % 32) being the 16 bytes at float offset
+//     256 x + 4 l, so every store instruction writes 1 KiB contiguously.  Rows past Lq hold the
+//     products of their cleared dS (zeros); the reduction does not use them.
 template <class C>
-__device__ __forceinline__ void gemm4_atomic(const char* sST, const char* sK, float* dqb, int q0,
-                                             int Lq, int w, int lane) {
+__device__ __forceinline__ void gemm4(const char* sST, const char* sK, float* dst, int q0, int Lq,
+                                      int w, int lane) {
   using M = typename C::M;
   using acc_t = typename M::acc_t;
   constexpr int DQK = C::DQK;
@@ -363,19 +387,27 @@ __device__ __forceinline__ void gemm4_atomic(const char* sST, const char* sK, fl
     acc_t acc = acc_t{};
 #pragma unroll
     for (int t = 0; t < C::BC / 16; ++t) acc = M::mma(tl.ds(sST, t), tl.template k<DQK>(sK, t, dt), acc);
-    float* dst = dqb + dt * 32 + lc;
-    if (full) {
+    if constexpr (C::MODE == DQ_PARTIAL) {
+      floatx4* blk = reinterpret_cast<floatx4*>(dst + dt * 1024) + lane;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        __hip_atomic_fetch_add(dst + acc_row<32>(r, g) * DQK, acc[r], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+      for (int x = 0; x < 4; ++x)
+        __builtin_nontemporal_store(floatx4{acc[4 * x], acc[4 * x + 1], acc[4 * x + 2], acc[4 * x + 3]},
+                                    blk + 64 * x);
     } else {
+      float* row0 = dst + dt * 32 + lc;
+      if (full) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = acc_row<32>(r, g);
-        if (q0 + row < Lq)
-          __hip_atomic_fetch_add(dst + row * DQK, acc[r], __ATOMIC_RELAXED,
+        for (int r = 0; r < 16; ++r)
+          __hip_atomic_fetch_add(row0 + acc_row<32>(r, g) * DQK, acc[r], __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = acc_row<32>(r, g);
+          if (q0 + row < Lq)
+            __hip_atomic_fetch_add(row0 + row * DQK, acc[r], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
   }
@@ -388,7 +420,10 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
   constexpr int BR = C::BR, BC = C::BC, DQK = C::DQK, DV = C::DV, KPW = C::KPW, NKT = C::NKT;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* sK = smem + C::OFF_K;
-  char* sST = smem + C::OFF_ST;
+  // dS staging buffer of q tile i
+  auto sST = [&](int i) -> char* {
+    return smem + C::OFF_ST + (C::NSST == 2 ? (i & 1) : 0) * C::SST_BYTES;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
@@ -422,6 +457,14 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
 
   const int n_q_tiles = p.sq_pad / BR;
   const int64_t q_row0 = (int64_t)(b * p.Hq + h) * p.Sq;  // row of the contiguous dq_accum
+  // where GEMM4's result for q tile i goes: the tile's first dq_accum row (atomic route) or its
+  // partial block (bh, j, i) of 32 x Dqk floats
+  auto dq_dst = [&](int i) -> float* {
+    if constexpr (C::MODE == DQ_PARTIAL)
+      return p.dqp_ws + (((int64_t)bh * p.n_kv_tiles + j) * n_q_tiles + i) * (BR * DQK);
+    else
+      return p.dq_accum + (q_row0 + (int64_t)i * BR) * DQK;
+  };
   const bf16_t* Kb = p.k + b * p.sk.b + kvh * p.sk.h;
   const bf16_t* Vb = p.v + b * p.sv.b + kvh * p.sv.h;
   const bf16_t* Qb = p.q + b * p.sq.b + h * p.sq.h;
@@ -478,6 +521,25 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
       }
     }
 
+    // dS-panel route: the previous q tile's packed dS, stored at the start of the next iteration
+    // (after that iteration's tile loads), so the wait for those loads one iteration later
+    // finds the stores long done instead of stalling on stores issued just before it
+    uint32_t sb_prev[8];
+    auto store_ds = [&](int i_t) {
+      // dS of the wave's 32 keys to the workspace: 2 KiB per 32 keys, lane l's quads of
+      // accumulator groups 2h and 2h + 1 as 16 contiguous bytes at 1024 h + 16 l (one coalesced
+      // 1 KiB store per h; the dQ kernel rebuilds the quad layout below in LDS).  Streaming
+      // stores (read once, by the dQ kernel): written past the last-level cache while this kernel
+      // computes, rather than evicted dirty during the dQ kernel's reads.
+      char* wsb = reinterpret_cast<char*>(
+          p.ds_ws + (((int64_t)bh * p.n_kv_tiles + j) * n_q_tiles + i_t) * (BC * BR));
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        __builtin_nontemporal_store(
+            u32x4{sb_prev[4 * h], sb_prev[4 * h + 1], sb_prev[4 * h + 2], sb_prev[4 * h + 3]},
+            reinterpret_cast<u32x4*>(wsb + w * 2048 + h * 1024 + lane * 16));
+    };
+
     for (int i = i_hi; i >= i_lo; --i) {
       const int q0 = i * BR;
       const char* T = tile(i);
@@ -485,12 +547,18 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
       wait_vmem();      // this wave's loads of tile i (and its older atomics / stores) are done
       lds_barrier();    // tile i landed everywhere; every wave is done with the previous tile
       if (C::NBUF == 2 && i > i_lo) load_tile(i - 1);
+      if constexpr (C::DS_OUT) {
+        if (i < i_hi) store_ds(i + 1);
+      }
 
-      if constexpr (!C::DET) {
-        // GEMM4 of the previous q tile (dS in sST), deferred so its atomics overlap this tile
+      if constexpr (C::G4) {
+        // GEMM4 of the previous q tile (dS in sST), deferred so its atomics / partial stores
+        // overlap this tile
         if (i < i_hi) {
-          gemm4_atomic<C>(sST, sK, p.dq_accum + (q_row0 + q0 + BR) * DQK, q0 + BR, mg.Lq, w, lane);
-          lds_barrier();  // every wave is done reading sST (the atomics keep draining)
+          gemm4<C>(sST(i + 1), sK, dq_dst(i + 1), q0 + BR, mg.Lq, w, lane);
+          // single buffer: every wave is done reading it before this tile's dS overwrites it
+          // (the atomics / stores keep draining)
+          if constexpr (C::NSST == 1) lds_barrier();
         }
       }
 
@@ -543,23 +611,14 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
         mask_pairs<0>(vis_m, pb, sb);
         mask_pairs<2>(vis_m, pb, sb);
       }
-      if constexpr (C::DET) {
-        // dS of the wave's 32 keys to the workspace: 2 KiB per 32 keys, lane l's quads of
-        // accumulator groups 2h and 2h + 1 as 16 contiguous bytes at 1024 h + 16 l (one coalesced
-        // 1 KiB store per h; the dQ kernel rebuilds the quad layout below in LDS).  Streaming
-        // stores (read once, by the dQ kernel): written past the last-level cache while this kernel
-        // computes, rather than evicted dirty during the dQ kernel's reads.
-        char* wsb = reinterpret_cast<char*>(
-            p.ds_ws + (((int64_t)bh * p.n_kv_tiles + j) * n_q_tiles + i) * (BC * BR));
+      if constexpr (C::DS_OUT) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          __builtin_nontemporal_store(u32x4{sb[4 * h], sb[4 * h + 1], sb[4 * h + 2], sb[4 * h + 3]},
-                                      reinterpret_cast<u32x4*>(wsb + w * 2048 + h * 1024 + lane * 16));
+        for (int x = 0; x < 8; ++x) sb_prev[x] = sb[x];
       } else {
         // dS of the wave's 32 keys to LDS as 2 KiB of quads (see ds_store_off)
 #pragma unroll
         for (int x = 0; x < 4; ++x)
-          *reinterpret_cast<u32x2*>(sST + w * 2048 + ds_store_off(lane, x)) =
+          *reinterpret_cast<u32x2*>(sST(i) + w * 2048 + ds_store_off(lane, x)) =
               u32x2{sb[2 * x], sb[2 * x + 1]};
       }
       // (raised wave priority: this MFMA-only phase issues ahead of the other wave's softmax)
@@ -573,9 +632,10 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
         if (i > i_lo) load_tile(i - 1);
       }
     }
-    if constexpr (!C::DET) {
+    if constexpr (C::DS_OUT) store_ds(i_lo);
+    if constexpr (C::G4) {
       lds_barrier();  // the last tile's dS is complete
-      gemm4_atomic<C>(sST, sK, p.dq_accum + (q_row0 + i_lo * BR) * DQK, i_lo * BR, mg.Lq, w, lane);
+      gemm4<C>(sST(i_lo), sK, dq_dst(i_lo), i_lo * BR, mg.Lq, w, lane);
     }
   }
 

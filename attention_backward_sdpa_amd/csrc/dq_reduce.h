@@ -1,0 +1,122 @@
+// Ordered dQ reduction of the dQ-partial route ("SDPA Backward (SM120)", sections "Determinism" and
+// "Deterministic vs. non-deterministic dQ": per-KV-tile dQ partials, then a reduction in a fixed
+// KV order):
+//     dQ[b, h, q, :] = io( scale * sum_{j ascending} partial[bh, j, q tile] )
+// The main kernel stores one 32 x Dqk fp32 block per (KV tile j, q tile i) it visits (GEMM4's
+// result, layout in bwd_main.h); this kernel sums, for each q tile, exactly those blocks in
+// ascending j with one fp32 accumulator per element and rounds once.  No atomics and a fixed
+// order, so the result is bitwise reproducible.
+//
+// It is a pure stream of the partials (bound by HBM): one workgroup per (q tile, batch, query
+// head), one thread per (32-column d tile, lane) holding the 16 floats that lane wrote, four
+// blocks of loads (16 x 16 bytes per thread) in flight ahead of the adds.  The sums go through LDS
+// once to leave as row-major 16-byte vectors of the io type.
+#pragma once
+#include "common.h"
+#include "masks.h"
+
+namespace sdpa {
+
+struct DqReduceParams {
+  const float* dqp_ws;  // (B*Hq, n_kv_tiles, n_q_tiles) blocks of 32 x Dqk fp32
+  bf16_t* dq;           // (B, Hq, Sq, Dqk), element strides sdq
+  Strides sdq;
+  const int* seq_q_lens;
+  const int* seq_kv_lens;
+  int B, Hq, Sq, Skv;
+  int causal, window_left, window_right, bottom_right;
+  int n_kv_tiles, n_q_tiles;
+  int bc;               // keys per KV tile of the main kernel
+  float scale;
+};
+
+template <int DQK, bool F16>
+__global__ void __launch_bounds__(DQK * 2) dq_reduce_kernel(DqReduceParams p) {
+  constexpr int NT = DQK * 2, BR = 32, U = 4;
+  constexpr int ROWF = DQK + 4;  // padded LDS row (floats)
+  __shared__ __attribute__((aligned(16))) float sT[BR * ROWF];
+  const int tid = threadIdx.x, lane = tid & 63, dt = tid >> 6;
+
+  // q tiles in descending order (under a causal mask the last ones sum the most blocks);
+  // consecutive workgroups are different heads
+  const int nbh = p.B * p.Hq;
+  const int bh = blockIdx.x % nbh;
+  const int i = p.n_q_tiles - 1 - (int)(blockIdx.x / nbh);
+  const int b = bh / p.Hq, h = bh % p.Hq;
+  MaskGeom mg;
+  mg.Lq = p.seq_q_lens ? min(max(p.seq_q_lens[b], 0), p.Sq) : p.Sq;
+  mg.Lkv = p.seq_kv_lens ? min(max(p.seq_kv_lens[b], 0), p.Skv) : p.Skv;
+  mg.diag = p.bottom_right ? mg.Lkv - mg.Lq : 0;
+  mg.causal = p.causal;
+  mg.W = p.window_left;
+  mg.R = p.window_right;
+  const int q0 = i * BR;
+
+  // KV tiles the live rows of this q tile can see (the union of the rows' key ranges); each one
+  // is summed when the main kernel's q-tile range for it contains i, which is exactly the set of
+  // blocks it stored
+  int jlo = 0, jhi = -1;
+  if (q0 < mg.Lq && mg.Lkv > 0) {
+    const int qlast = min(q0 + BR, mg.Lq) - 1;
+    int klo = 0, khi = mg.Lkv - 1;
+    if (mg.causal) khi = min(khi, qlast + mg.diag + mg.R);
+    if (mg.W >= 0) klo = max(klo, q0 + mg.diag - mg.W);
+    if (klo <= khi) {
+      jlo = klo / p.bc;
+      jhi = khi / p.bc;
+    }
+  }
+  auto stored = [&](int j) {
+    int lo, hi;
+    q_tile_range(mg, j * p.bc, p.bc, BR, &lo, &hi);
+    return lo <= i && i <= hi;
+  };
+
+  const int64_t blk = (int64_t)BR * DQK / 4;  // float4s per block
+  const floatx4* src = reinterpret_cast<const floatx4*>(p.dqp_ws) +
+                       ((int64_t)bh * p.n_kv_tiles * p.n_q_tiles + i) * blk + dt * 256 + lane;
+  const int64_t jstride = (int64_t)p.n_q_tiles * blk;
+  floatx4 s[4] = {floatx4{}, floatx4{}, floatx4{}, floatx4{}};
+  for (int j0 = jlo; j0 <= jhi; j0 += U) {
+    floatx4 v[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int jj = min(j0 + u, jhi);  // past the range: re-read the last block, unused
+#pragma unroll
+      for (int x = 0; x < 4; ++x) v[u][x] = __builtin_nontemporal_load(src + jj * jstride + 64 * x);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j0 + u <= jhi && stored(j0 + u)) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) s[x] += v[u][x];
+      }
+    }
+  }
+
+  // lane's floats: rows 8x + 4(lane / 32) + e, column 32 dt + lane % 32
+  const int g = lane >> 5, col = dt * 32 + (lane & 31);
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sT[(8 * x + 4 * g + e) * ROWF + col] = s[x][e] * p.scale;
+  __syncthreads();
+
+  constexpr int V = DQK / 8;  // 8-element output vectors per row
+  bf16_t* dqb = p.dq + b * p.sdq.b + h * p.sdq.h;
+#pragma unroll
+  for (int c = tid; c < BR * V; c += NT) {
+    const int r = c / V, cv = c % V, q = q0 + r;
+    if (q >= p.Sq) continue;
+    u32x4 out = u32x4{0u, 0u, 0u, 0u};
+    if (q < mg.Lq) {
+      const floatx4 a = *reinterpret_cast<const floatx4*>(sT + r * ROWF + cv * 8);
+      const floatx4 d = *reinterpret_cast<const floatx4*>(sT + r * ROWF + cv * 8 + 4);
+      out = u32x4{Elem<F16>::pack2(a[0], a[1]), Elem<F16>::pack2(a[2], a[3]),
+                  Elem<F16>::pack2(d[0], d[1]), Elem<F16>::pack2(d[2], d[3])};
+    }
+    *reinterpret_cast<u32x4*>(dqb + q * p.sdq.s + cv * 8) = out;
+  }
+}
+
+}  // namespace sdpa

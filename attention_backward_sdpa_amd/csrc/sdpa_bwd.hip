@@ -2,8 +2,9 @@
 // choice and kernel launches on the caller's stream.  Implements include/sdpa_bwd.h.
 //
 // Chain ("SDPA Backward (SM120)", section "The kernel chain"):
-//   preprocess -> main -> [GQA reduce] -> dQ convert        (fp32-atomic dQ route)
-//   preprocess -> main(dS out) -> [GQA reduce] -> dq2k      (deterministic two-kernel route)
+//   preprocess -> main -> [GQA reduce] -> dQ convert           (fp32-atomic dQ route)
+//   preprocess -> main(dS out) -> [GQA reduce] -> dq2k         (deterministic, dS panels)
+//   preprocess -> main(dQ partials) -> [GQA reduce] -> dq_reduce  (deterministic, dQ partials)
 // The pages overlap consecutive launches with programmatic dependent launch; CDNA has no such
 // feature, so the launches are simply ordered on the stream.
 #include <hip/hip_runtime.h>
@@ -13,6 +14,7 @@
 #include "../../include/sdpa_bwd.h"
 #include "bwd_main.h"
 #include "dq2k.h"
+#include "dq_reduce.h"
 #include "small_kernels.h"
 
 using namespace sdpa;
@@ -54,24 +56,44 @@ int q_split(int B, int Hq, int Sq, int Skv, const Geometry& g) {
   return split;
 }
 
+// dQ routes.  The `deterministic` argument: 0 fp32 atomics, 1 deterministic (the fp32 dQ partials
+// where they are a smaller workspace stream per (KV tile, q row) than the BC bf16 dS values, else
+// the dS panels: at equal bytes, head dim 128, the dS-panel chain measured faster on MI355X),
+// 2 dS panels + dq2k, 3 fp32 dQ partials + dq_reduce.
+enum Route { R_ATOMIC = 0, R_DS = 1, R_DQP = 2, R_INVALID = -1 };
+
+Route route_for(int deterministic, int Dqk, const Geometry& g) {
+  switch (deterministic) {
+    case 0: return R_ATOMIC;
+    case 1: return (int64_t)Dqk * 4 < (int64_t)g.bc * 2 ? R_DQP : R_DS;
+    case 2: return R_DS;
+    case 3: return R_DQP;
+    default: return R_INVALID;
+  }
+}
+
 struct Carve {
-  int64_t stats = 0, dq_accum = -1, ds = -1, dk_ws = -1, dv_ws = -1, total = 0;
+  int64_t stats = 0, dq_accum = -1, ds = -1, dqp = -1, dk_ws = -1, dv_ws = -1, total = 0;
   int64_t sq_pad = 0, skv_pad = 0;
 };
 
-Carve carve(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv, int det, const Geometry& g) {
+Carve carve(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv, Route route,
+            const Geometry& g) {
   Carve c;
   int64_t off = 0;
   c.sq_pad = align_up(Sq, g.br);
   c.skv_pad = align_up(Skv, g.bc);
   c.stats = off;  // [LSE * log2e, delta] per padded q row
   off = align_up(off + (int64_t)B * Hq * c.sq_pad * 2 * 4, kAlign);
-  if (!det) {
+  if (route == R_ATOMIC) {
     c.dq_accum = off;
     off = align_up(off + (int64_t)B * Hq * Sq * Dqk * 4, kAlign);
-  } else {
+  } else if (route == R_DS) {
     c.ds = off;
     off = align_up(off + (int64_t)B * Hq * c.skv_pad * c.sq_pad * 2, kAlign);
+  } else {  // one 32 x Dqk fp32 block per (b, h, KV tile, q tile)
+    c.dqp = off;
+    off = align_up(off + (int64_t)B * Hq * (c.skv_pad / g.bc) * c.sq_pad * Dqk * 4, kAlign);
   }
   const int split = q_split(B, Hq, Sq, Skv, g);
   if (Hq != Hkv || split > 1) {  // per-(query head, part) dK/dV partials
@@ -165,24 +187,37 @@ hipError_t launch_dq2k(const Dq2kParams& dp, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DQK, int DV, int KPW, int NW>
-hipError_t dispatch_main(const MainParams& mp, int det, bool f16, int grid, int bc, hipStream_t s) {
+template <int DQK, int DV, int KPW, int NW, bool F16>
+hipError_t dispatch_main_t(const MainParams& mp, Route route, int grid, int bc, hipStream_t s) {
   // the workspace carve and the grid use the geometry table; the kernel must tile the same way
-  if (MainCfg<DQK, DV, KPW, NW, true>::BC != bc) return hipErrorInvalidValue;
-  if (f16) {
-    if (det) return launch_main<MainCfg<DQK, DV, KPW, NW, true, true>>(mp, grid, s);
-    return launch_main<MainCfg<DQK, DV, KPW, NW, false, true>>(mp, grid, s);
-  }
-  if (det) return launch_main<MainCfg<DQK, DV, KPW, NW, true>>(mp, grid, s);
-  return launch_main<MainCfg<DQK, DV, KPW, NW, false>>(mp, grid, s);
+  if (MainCfg<DQK, DV, KPW, NW, DQ_ATOMIC>::BC != bc) return hipErrorInvalidValue;
+  if (route == R_DS) return launch_main<MainCfg<DQK, DV, KPW, NW, DQ_DS, F16>>(mp, grid, s);
+  if (route == R_DQP) return launch_main<MainCfg<DQK, DV, KPW, NW, DQ_PARTIAL, F16>>(mp, grid, s);
+  return launch_main<MainCfg<DQK, DV, KPW, NW, DQ_ATOMIC, F16>>(mp, grid, s);
 }
 
-hipError_t run_main(int Dqk, int Dv, const MainParams& mp, int det, bool f16, int grid, int bc,
-                    hipStream_t s) {
-  if (Dqk == 64) return dispatch_main<64, 64, 32, 8>(mp, det, f16, grid, bc, s);
-  if (Dqk == 128) return dispatch_main<128, 128, 32, 8>(mp, det, f16, grid, bc, s);
-  if (Dqk == 192) return dispatch_main<192, 128, 32, 8>(mp, det, f16, grid, bc, s);
-  return dispatch_main<256, 256, 32, 4>(mp, det, f16, grid, bc, s);
+template <int DQK, int DV, int KPW, int NW>
+hipError_t dispatch_main(const MainParams& mp, Route route, bool f16, int grid, int bc,
+                         hipStream_t s) {
+  if (f16) return dispatch_main_t<DQK, DV, KPW, NW, true>(mp, route, grid, bc, s);
+  return dispatch_main_t<DQK, DV, KPW, NW, false>(mp, route, grid, bc, s);
+}
+
+hipError_t run_main(int Dqk, int Dv, const MainParams& mp, Route route, bool f16, int grid,
+                    int bc, hipStream_t s) {
+  if (Dqk == 64) return dispatch_main<64, 64, 32, 8>(mp, route, f16, grid, bc, s);
+  if (Dqk == 128) return dispatch_main<128, 128, 32, 8>(mp, route, f16, grid, bc, s);
+  if (Dqk == 192) return dispatch_main<192, 128, 32, 8>(mp, route, f16, grid, bc, s);
+  return dispatch_main<256, 256, 32, 4>(mp, route, f16, grid, bc, s);
+}
+
+template <bool F16>
+hipError_t launch_dq_reduce_t(const DqReduceParams& rp, int Dqk, int grid, hipStream_t s) {
+  if (Dqk == 64) hipLaunchKernelGGL((dq_reduce_kernel<64, F16>), dim3(grid), dim3(128), 0, s, rp);
+  else if (Dqk == 128) hipLaunchKernelGGL((dq_reduce_kernel<128, F16>), dim3(grid), dim3(256), 0, s, rp);
+  else if (Dqk == 192) hipLaunchKernelGGL((dq_reduce_kernel<192, F16>), dim3(grid), dim3(384), 0, s, rp);
+  else hipLaunchKernelGGL((dq_reduce_kernel<256, F16>), dim3(grid), dim3(512), 0, s, rp);
+  return hipGetLastError();
 }
 
 template <int DQK, int BC, bool F16>
@@ -218,6 +253,10 @@ hipError_t launch_convert_t(const ConvertParams& cp, int Dqk, int grid, hipStrea
 
 hipError_t launch_convert(const ConvertParams& cp, int Dqk, bool f16, int grid, hipStream_t s) {
   return f16 ? launch_convert_t<true>(cp, Dqk, grid, s) : launch_convert_t<false>(cp, Dqk, grid, s);
+}
+
+hipError_t launch_dq_reduce(const DqReduceParams& rp, int Dqk, bool f16, int grid, hipStream_t s) {
+  return f16 ? launch_dq_reduce_t<true>(rp, Dqk, grid, s) : launch_dq_reduce_t<false>(rp, Dqk, grid, s);
 }
 
 template <bool F16>
@@ -271,10 +310,11 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
       L.t[x] = Strides{layouts[x].batch, layouts[x].head, layouts[x].seq};
   st = check_layouts(L, Sq, Skv, Dqk, Dv);
   if (st != SDPA_BWD_OK) return st;
-  const int det = deterministic ? 1 : 0;
+  const Route route = route_for(deterministic, Dqk, geo);
+  if (route == R_INVALID) return SDPA_BWD_INVALID_ARG;
   // empty problems need no workspace (sdpa_bwd_workspace_size returns 0 for them)
   const bool empty = B == 0 || Sq == 0 || Skv == 0;
-  const Carve c = empty ? Carve{} : carve(B, Hq, Hkv, Sq, Skv, Dqk, Dv, det, geo);
+  const Carve c = empty ? Carve{} : carve(B, Hq, Hkv, Sq, Skv, Dqk, Dv, route, geo);
   if (c.total > 0 && workspace == nullptr) return SDPA_BWD_INVALID_ARG;
   if (check_ws && (uint64_t)c.total > (uint64_t)workspace_bytes) return SDPA_BWD_WORKSPACE_TOO_SMALL;
   if (c.total > 0 && ((uintptr_t)workspace % kAlign) != 0) return SDPA_BWD_UNSUPPORTED;
@@ -296,7 +336,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
 
   char* ws = (char*)workspace;
   float* stats = (float*)(ws + c.stats);
-  float* dq_accum = det ? nullptr : (float*)(ws + c.dq_accum);
+  float* dq_accum = route == R_ATOMIC ? (float*)(ws + c.dq_accum) : nullptr;
   const int split = q_split(B, Hq, Sq, Skv, geo);
   const bool partials = Hq != Hkv || split > 1;  // dK/dV go through the reduction
 
@@ -313,7 +353,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   pp.Sq = Sq;
   pp.sq_pad = (int)c.sq_pad;
   pp.Dqk = Dqk;
-  pp.zero_rows = det ? 0 : 1;
+  pp.zero_rows = route == R_ATOMIC ? 1 : 0;
   e = launch_preprocess(pp, Dv, f16, (int64_t)B * Hq * (c.sq_pad / geo.br), stream);
   if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   rec(1);
@@ -331,7 +371,8 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   mp.sdv = L.t[T_DV];
   mp.stats = stats;
   mp.dq_accum = dq_accum;
-  mp.ds_ws = det ? (bf16_t*)(ws + c.ds) : nullptr;
+  mp.ds_ws = route == R_DS ? (bf16_t*)(ws + c.ds) : nullptr;
+  mp.dqp_ws = route == R_DQP ? (float*)(ws + c.dqp) : nullptr;
   mp.dk_out = partials ? (bf16_t*)(ws + c.dk_ws) : (bf16_t*)dk;
   mp.dv_out = partials ? (bf16_t*)(ws + c.dv_ws) : (bf16_t*)dv;
   mp.seq_q_lens = seq_q_lens;
@@ -355,7 +396,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   mp.scale_log2 = scale * kLog2e;
   const int64_t main_grid = (int64_t)mp.n_kv_tiles * split * B * Hq;
   if (main_grid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
-  e = run_main(Dqk, Dv, mp, det, f16, (int)main_grid, geo.bc, stream);
+  e = run_main(Dqk, Dv, mp, route, f16, (int)main_grid, geo.bc, stream);
   if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   rec(2);
 
@@ -385,7 +426,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   }
   rec(3);
 
-  if (!det) {
+  if (route == R_ATOMIC) {
     ConvertParams cp;
     cp.acc = dq_accum;
     cp.dq = (bf16_t*)dq;
@@ -397,6 +438,29 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     const int64_t cgrid = (int64_t)B * Hq * ((Sq + 31) / 32);
     if (cgrid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
     e = launch_convert(cp, Dqk, f16, (int)cgrid, stream);
+    if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
+  } else if (route == R_DQP) {
+    DqReduceParams rp;
+    rp.dqp_ws = mp.dqp_ws;
+    rp.dq = (bf16_t*)dq;
+    rp.sdq = L.t[T_DQ];
+    rp.seq_q_lens = seq_q_lens;
+    rp.seq_kv_lens = seq_kv_lens;
+    rp.B = B;
+    rp.Hq = Hq;
+    rp.Sq = Sq;
+    rp.Skv = Skv;
+    rp.causal = mp.causal;
+    rp.window_left = window_left;
+    rp.window_right = mp.window_right;
+    rp.bottom_right = mp.bottom_right;
+    rp.n_kv_tiles = mp.n_kv_tiles;
+    rp.n_q_tiles = (int)(c.sq_pad / geo.br);
+    rp.bc = geo.bc;
+    rp.scale = scale;
+    const int64_t rgrid = (int64_t)B * Hq * rp.n_q_tiles;
+    if (rgrid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
+    e = launch_dq_reduce(rp, Dqk, f16, (int)rgrid, stream);
     if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   } else {
     Dq2kParams dp;
@@ -440,7 +504,20 @@ size_t sdpa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk,
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || Hq % Hkv != 0) return 0;
   if (!geometry_for(Dqk, Dv, &geo)) return 0;
   if (B == 0 || Sq == 0 || Skv == 0) return 0;
-  return (size_t)carve(B, Hq, Hkv, Sq, Skv, Dqk, Dv, deterministic ? 1 : 0, geo).total;
+  const Route route = route_for(deterministic, Dqk, geo);
+  if (route == R_INVALID) return 0;
+  return (size_t)carve(B, Hq, Hkv, Sq, Skv, Dqk, Dv, route, geo).total;
+}
+
+int sdpa_bwd_dq_route(int Dqk, int Dv, int deterministic) {
+  Geometry geo;
+  if (!geometry_for(Dqk, Dv, &geo)) return -1;
+  switch (route_for(deterministic, Dqk, geo)) {
+    case R_ATOMIC: return SDPA_BWD_DQ_ATOMIC;
+    case R_DS: return SDPA_BWD_DQ_DS_PANELS;
+    case R_DQP: return SDPA_BWD_DQ_PARTIALS;
+    default: return -1;
+  }
 }
 
 int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,

@@ -31,6 +31,10 @@ sys.path.insert(0, ROOT)
 from attention_backward_sdpa_amd import synth  # noqa: E402
 
 METRIC = "attention-backward TFLOP/s and % of bf16 MFMA peak, S=4096 D=128 causal"
+# dQ routes as sdpa_bwd_dq_route() reports them, and the kernel that ends each chain
+ROUTE_NAMES = {0: "fp32 atomic", 2: "deterministic: dS panels + dq2k",
+               3: "deterministic: fp32 dQ partials + ordered reduction"}
+ROUTE_STAGE = {0: "dq_convert", 2: "dq2k", 3: "dq_reduce"}
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU (AMD's 2.5 PFLOP/s)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "main_kernel_traffic.json")
 KERNEL_SOURCES = ["bwd_main.h", "common.h", "masks.h"]
@@ -149,10 +153,12 @@ def _pmc_means(directory, counter):
 
 
 def write_traffic_record(workload, det_arg, dtype, fetch_dir, write_dir):
+    import attention_backward_sdpa_amd as lib
     w = synth.WORKLOADS[workload]
-    det = w.deterministic if det_arg < 0 else bool(det_arg)
-    rec = {"kernel_source_hash": kernel_source_hash(), "workload": w.name, "deterministic": det,
-           "dtype": dtype, "copy_probe_bytes": COPY_PROBE_BYTES}
+    det = int(w.deterministic) if det_arg < 0 else det_arg
+    rec = {"kernel_source_hash": kernel_source_hash(), "workload": w.name,
+           "dq_route": lib.dq_route(w.Dqk, w.Dv, det), "dtype": dtype,
+           "copy_probe_bytes": COPY_PROBE_BYTES}
     total = 0.0
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         means = _pmc_means(d, counter)
@@ -221,7 +227,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa_causal_s4096_d128", choices=list(synth.WORKLOADS))
     ap.add_argument("--deterministic", type=int, default=-1,
-                    help="override the workload's dQ route (-1: as the workload states)")
+                    help="override the workload's dQ route (-1: as the workload states; 0 fp32 "
+                         "atomics, 1 deterministic (the library's choice), 2 dS panels + dq2k, "
+                         "3 dQ partials + ordered reduction)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"],
                     help="io element type of Q, K, V, O, dO and the gradients")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -251,7 +259,10 @@ def main():
     import attention_backward_sdpa_amd as lib
 
     w = synth.WORKLOADS[args.workload]
-    det = w.deterministic if args.deterministic < 0 else bool(args.deterministic)
+    det = int(w.deterministic) if args.deterministic < 0 else args.deterministic
+    route = lib.dq_route(w.Dqk, w.Dv, det)
+    if route < 0:
+        raise SystemExit(f"--deterministic {det}: not a dQ route")
     inp = synth.draw_inputs(w, dtype=args.dtype)
     lens = inp.seq_q_lens
     dev = torch.device("cuda:0")
@@ -306,15 +317,16 @@ def main():
 
     flops = algorithmic_flops(w, lens)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    # the deterministic route's main kernel skips GEMM4 (dQ = dS K), which dq2k performs
-    main_flops = flops * ((2 * w.Dqk + 2 * w.Dv) / (3 * w.Dqk + 2 * w.Dv) if det else 1.0)
+    # on the dS-panel route the main kernel skips GEMM4 (dQ = dS K), which dq2k performs
+    main_flops = flops * ((2 * w.Dqk + 2 * w.Dv) / (3 * w.Dqk + 2 * w.Dv)
+                          if route == lib.DQ_DS_PANELS else 1.0)
     main_tflops = main_flops / (main_ms * 1e-3) / 1e12
     traffic = None
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
         if t.get("kernel_source_hash") == kernel_source_hash() and t.get("workload") == w.name \
-                and bool(t.get("deterministic")) == det and t.get("dtype", "bf16") == args.dtype:
+                and t.get("dq_route") == route and t.get("dtype", "bf16") == args.dtype:
             traffic = t["hbm_bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         traffic = None
@@ -336,11 +348,11 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq,
                    "Skv": w.Skv, "Dqk": w.Dqk, "Dv": w.Dv, "causal": w.causal,
                    "window_left": w.window_left, "padded": w.padded,
-                   "dq_route": "two-kernel deterministic" if det else "fp32 atomic",
+                   "dq_route": ROUTE_NAMES[route],
                    "algorithmic_gflop": round(flops / 1e9, 3)},
         "stage_ms": {"preprocess": round(float(stage_avg[0]), 4), "main": round(float(stage_avg[1]), 4),
                      "gqa_reduce": round(float(stage_avg[2]), 4),
-                     "dq_convert_or_dq2k": round(float(stage_avg[3]), 4)},
+                     ROUTE_STAGE[route]: round(float(stage_avg[3]), 4)},
         "roofline": {"kernel": "bwd_main_kernel", "bound": "mfma",
                      "achieved": round(main_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),

@@ -37,10 +37,19 @@
  * Errors.  Functions return SDPA_BWD_OK (0) or a status code; validation happens before the first
  * launch, so a rejected call leaves every output untouched.  Nothing aborts or throws.
  *
- * Determinism ("Determinism"): deterministic != 0 selects the two-kernel route (dS streamed to the
- * workspace, dQ reduced by a separate kernel in ascending KV order) and makes dq, dk, dv bitwise
- * reproducible; otherwise dQ is accumulated with fp32 atomics and its low bits may vary between
- * runs.  dK and dV are reproducible in both modes.
+ * Determinism ("Determinism", "Deterministic vs. non-deterministic dQ"): the `deterministic`
+ * argument selects how dQ is formed (SDPA_BWD_DQ_*):
+ *   0  fp32 atomic adds into an fp32 accumulator, converted once; the low bits of dq may vary
+ *      between runs;
+ *   2  dS panels: the main kernel stores the bf16 dS tiles in the workspace and a second kernel
+ *      forms dQ = scale * dS K in ascending KV order;
+ *   3  dQ partials: the main kernel stores one fp32 dQ partial per (KV tile, 32-row q tile) in
+ *      the workspace and a second kernel sums them in ascending KV order;
+ *   1  deterministic, the library's choice between 2 and 3: 3 where its workspace holds fewer
+ *      bytes per (KV tile, q row) (Dqk fp32 partials against the key tile's bf16 dS values),
+ *      else 2 (head dim 64 takes 3; 128, 192 and 256 take 2).
+ * Routes 1-3 make dq, dk, dv bitwise reproducible run to run; dK and dV are reproducible on every
+ * route.  Any other value gives SDPA_BWD_INVALID_ARG.
  */
 #ifndef SDPA_BWD_H
 #define SDPA_BWD_H
@@ -52,6 +61,14 @@
 extern "C" {
 #endif
 
+/* values of the `deterministic` argument */
+enum {
+  SDPA_BWD_DQ_ATOMIC = 0,
+  SDPA_BWD_DQ_DETERMINISTIC = 1,
+  SDPA_BWD_DQ_DS_PANELS = 2,
+  SDPA_BWD_DQ_PARTIALS = 3
+};
+
 enum {
   SDPA_BWD_OK = 0,
   SDPA_BWD_INVALID_ARG = 1,          /* null pointer, negative size, H_kv not dividing H_q, ... */
@@ -61,12 +78,21 @@ enum {
 };
 
 /* Bytes of workspace needed by a call with these arguments: a 256-byte-aligned carve of the
- * per-row statistics (LSE * log2 e and delta, B*Hq*Sq_pad float pairs), then either the fp32 dQ
- * accumulator (B*Hq*Sq*Dqk floats) or, in deterministic mode, the bf16 dS buffer
- * (B*Hq*Sq_pad*Skv_pad), then under GQA the bf16 per-query-head dK/dV partials.  Returns 0 for arguments sdpa_bwd rejects and
- * for empty problems. */
+ * per-row statistics (LSE * log2 e and delta, B*Hq*Sq_pad float pairs, Sq_pad = Sq rounded up to
+ * 32), then the dQ route's buffer: the fp32 dQ accumulator (B*Hq*Sq*Dqk floats, route 0), the
+ * bf16 dS panels (B*Hq*Sq_pad*Skv_pad, route 2) or the fp32 dQ partials
+ * (B*Hq*(Skv_pad/BC)*Sq_pad*Dqk floats, route 3), where BC is the key tile (256 keys for head
+ * dims up to 192, 128 for 256) and Skv_pad is Skv rounded up to BC; then, under GQA or when the
+ * main grid splits its q ranges, the bf16 per-(query head, part) dK/dV partials.  Returns 0 for
+ * arguments sdpa_bwd rejects and for empty problems. */
 size_t sdpa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv,
                                int causal, int window_left, int deterministic, int has_seqlens);
+
+/* The dQ route a call with these head dims and this `deterministic` value takes:
+ * SDPA_BWD_DQ_ATOMIC, SDPA_BWD_DQ_DS_PANELS or SDPA_BWD_DQ_PARTIALS (never
+ * SDPA_BWD_DQ_DETERMINISTIC, which resolves to one of the last two); -1 for head dims outside the
+ * supported set or an unknown value.  Host only, no GPU work. */
+int sdpa_bwd_dq_route(int Dqk, int Dv, int deterministic);
 
 /* The backward pass with top-left causal masking, no padding and no right band.
  * scale <= 0 selects 1/sqrt(Dqk) ("API Usage": None -> 1/sqrt(D)).  window_left = -1 disables the
@@ -90,7 +116,7 @@ int sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
 
 /* sdpa_bwd_ex that also records five HIP events (hipEvent_t, created by the caller) on `stream`:
  * before the preprocess, after the preprocess, after the main kernel, after the GQA reduce (same
- * point as the previous one when there is none) and after the dQ convert / dq2k kernel.  A NULL
+ * point as the previous one when there is none) and after the dQ convert / dq2k / dq_reduce kernel.  A NULL
  * entry is skipped (each recorded event is one more packet on the stream).  For measuring each
  * kernel's share of the chain; the arithmetic is identical to sdpa_bwd_ex. */
 int sdpa_bwd_ex_events(const void* q, const void* k, const void* v, const void* o, const void* dO,

@@ -29,7 +29,7 @@ def so():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("sdpa_bwd", "sdpa_bwd_ex", "sdpa_bwd_workspace_size", "sdpa_bwd_status_string",
-              "sdpa_bwd_ex_events", "sdpa_bwd_preprocess", "sdpa_bwd_flex"):
+              "sdpa_bwd_ex_events", "sdpa_bwd_preprocess", "sdpa_bwd_flex", "sdpa_bwd_dq_route"):
         assert n in names
 
 
@@ -43,6 +43,18 @@ def test_status_strings(so):
     for s in range(1, 5):
         assert lib.status_string(s) != "ok"
     assert lib.status_string(99) == "unknown status"
+
+
+def test_dq_route_choice(so):
+    assert lib.dq_route(64, 64, 1) == lib.DQ_PARTIALS
+    for d in ((128, 128), (192, 128), (256, 256)):
+        assert lib.dq_route(*d, 1) == lib.DQ_DS_PANELS
+    for d in ((64, 64), (128, 128), (192, 128), (256, 256)):
+        assert lib.dq_route(*d, 0) == lib.DQ_ATOMIC
+        assert lib.dq_route(*d, 2) == lib.DQ_DS_PANELS
+        assert lib.dq_route(*d, 3) == lib.DQ_PARTIALS
+        assert lib.dq_route(*d, 4) == -1
+    assert lib.dq_route(96, 96, 0) == -1
 
 
 def _ws(**kw):
@@ -65,6 +77,29 @@ def test_workspace_size_rules(so):
     # deterministic: statistics + bf16 dS (S_kv padded to the 256-key tile, S_q to the 32-row
     # q tile), no fp32 dQ
     assert _ws(deterministic=True, Sq=200, Skv=200) == _al(4 * 224 * 8) + _al(4 * 224 * 256 * 2)
+    # explicit dS panels: the same as the deterministic choice at head dim 256
+    assert _ws(deterministic=lib.DQ_DS_PANELS, Sq=200, Skv=200) == \
+        _al(4 * 224 * 8) + _al(4 * 224 * 256 * 2)
+    # dQ partials: one 32 x Dqk fp32 block per (KV tile of 256 keys, q tile)
+    parts = _al(4 * 224 * 8) + _al(4 * 1 * 224 * 128 * 4)
+    assert _ws(deterministic=lib.DQ_PARTIALS, Sq=200, Skv=200) == parts
+    # the deterministic choice at head dim 64 (64 fp32 per q row < 256 bf16 dS values)
+    d64 = dict(Dqk=64, Dv=64, Sq=200, Skv=200)
+    assert _ws(deterministic=True, **d64) == _ws(deterministic=lib.DQ_PARTIALS, **d64) == \
+        _al(4 * 224 * 8) + _al(4 * 1 * 224 * 64 * 4)
+    assert _ws(deterministic=lib.DQ_PARTIALS, Sq=200, Skv=300) == \
+        _al(4 * 224 * 8) + _al(4 * 2 * 224 * 128 * 4)
+    # head dim 256 (128-key tiles): the deterministic choice is the dS panels
+    d256 = dict(Dqk=256, Dv=256, Sq=200, Skv=200)
+    assert _ws(deterministic=True, **d256) == _ws(deterministic=lib.DQ_DS_PANELS, **d256) == \
+        _al(4 * 224 * 8) + _al(4 * 224 * 256 * 2)
+    assert _ws(deterministic=lib.DQ_PARTIALS, **d256) == \
+        _al(4 * 224 * 8) + _al(4 * 2 * 224 * 256 * 4)
+    # head dim 192 (256-key tiles): 192 fp32 per q row > 256 bf16 -> dS panels
+    d192 = dict(Dqk=192, Dv=128, Sq=200, Skv=200)
+    assert _ws(deterministic=True, **d192) == _ws(deterministic=lib.DQ_DS_PANELS, **d192)
+    # unknown route values are rejected
+    assert _ws(deterministic=4) == 0 and _ws(deterministic=-1) == 0
     # monotone in the sequence length
     sizes = [_ws(Sq=s, Skv=s) for s in (64, 128, 300, 1000)]
     assert sizes == sorted(sizes)
@@ -90,6 +125,8 @@ def test_rejections_before_launch(so):
     assert _call(so, Hq=-1) == lib.INVALID_ARG
     assert _call(so, wl=-2) == lib.INVALID_ARG                    # window_left < -1
     assert _call(so, wr=-1) == lib.INVALID_ARG
+    assert _call(so, det=4) == lib.INVALID_ARG                    # unknown dQ route
+    assert _call(so, det=-1) == lib.INVALID_ARG
     assert _call(so, Dqk=96, Dv=96) == lib.UNSUPPORTED            # head dims outside the set
     assert _call(so, Dqk=128, Dv=192) == lib.UNSUPPORTED          # D_v > D_qk
     assert _call(so, q=ctypes.c_void_p(4098)) == lib.UNSUPPORTED  # misaligned pointer

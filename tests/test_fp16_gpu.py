@@ -49,12 +49,12 @@ def to_half(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.float16)
 
 
-@pytest.mark.parametrize("det", [False, True], ids=["atomic", "det"])
+@pytest.mark.parametrize("det", [0, 2, 3], ids=["atomic", "dspanels", "dqpartials"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_fp16_parity(name, det):
     import attention_backward_sdpa_amd as lib
     w = CASES[name]
-    C.log(f"fp16 case {name} ({'det' if det else 'atomic'}): {w}")
+    C.log(f"fp16 case {name} (dQ route {det}): {w}")
     inp, o_bits, lse, lens, ref = fp16_case(w)
     q, k, v, o, do = (to_half(x) for x in (inp.q, inp.k, inp.v, o_bits, inp.do))
     outs = [torch.empty_like(x) for x in (q, k, v)]
@@ -76,19 +76,20 @@ def test_fp16_parity(name, det):
                 assert bool((x[b, :, L:] == 0).all()), "rows past the length must be zero"
 
 
-def test_fp16_deterministic_bitwise():
+@pytest.mark.parametrize("det", [2, 3], ids=["dspanels", "dqpartials"])
+def test_fp16_deterministic_bitwise(det):
     import attention_backward_sdpa_amd as lib
     w = CASES["gqa_causal_d128_s333"]
     inp, o_bits, lse, lens, _ = fp16_case(w)
     q, k, v, o, do = (to_half(x) for x in (inp.q, inp.k, inp.v, o_bits, inp.do))
     tlse = torch.from_numpy(lse).to("cuda")
-    n = lib.workspace_size(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.Dqk, w.Dv, w.causal, -1, True)
+    n = lib.workspace_size(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.Dqk, w.Dv, w.causal, -1, det)
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
     first = None
     for _ in range(3):
         outs = [torch.empty_like(x) for x in (q, k, v)]
         lib.sdpa_bwd_ex(q, k, v, o, do, tlse, *outs, scale=w.softmax_scale, causal=True,
-                        deterministic=True, workspace=ws)
+                        deterministic=det, workspace=ws)
         torch.cuda.synchronize()
         bits = [x.view(torch.int16).cpu() for x in outs]
         if first is None:
@@ -97,12 +98,12 @@ def test_fp16_deterministic_bitwise():
             assert all(bool((a == b).all()) for a, b in zip(first, bits))
 
 
-@pytest.mark.parametrize("det", [False, True], ids=["atomic", "det"])
+@pytest.mark.parametrize("det", [0, 2, 3], ids=["atomic", "dspanels", "dqpartials"])
 def test_fp16_bshd_layout(det):
     """fp16 io through BSHD storage (strided views) on a GQA window case with padding lengths."""
     import attention_backward_sdpa_amd as lib
     w = V(W["gqa_causal_s4096_d128"], B=2, Hq=4, Hkv=2, Sq=230, Skv=230, window_left=90)
-    C.log(f"fp16 bshd ({'det' if det else 'atomic'}): {w}")
+    C.log(f"fp16 bshd (dQ route {det}): {w}")
     inp, o_bits, lse, lens, ref = fp16_case(w)
 
     def bshd(bits):

@@ -28,13 +28,19 @@ pytestmark = [pytest.mark.gpu]
 
 W = synth.WORKLOADS
 
+# (workload, dQ route): None = the workload's own route, else the `deterministic` argument
+# (0 fp32 atomics, 2 dS panels, 3 dQ partials)
 CASES = [
     ("mha_causal_s2048_d128", None),
-    ("gqa_causal_s4096_d128", False),
-    ("gqa_causal_s4096_d128", True),
+    ("mha_causal_s2048_d128", 3),
+    ("gqa_causal_s4096_d128", 0),
+    ("gqa_causal_s4096_d128", 2),
+    ("gqa_causal_s4096_d128", 3),
     ("mha_det_s8192_d256", None),
     ("mla_window_padded_s4096", None),
+    ("mla_window_padded_s4096", 3),
 ]
+ROUTE_NAMES = {0: "atomic", 1: "det", 2: "dspanels", 3: "dqpartials", None: "default"}
 
 
 def _prepare(w):
@@ -82,7 +88,7 @@ def _f64(bits):
     return synth.bf16_to_f32(bits).astype(np.float64)
 
 
-@pytest.mark.parametrize("name,det", CASES, ids=[f"{n}-{'det' if d else 'atomic' if d is not None else 'default'}" for n, d in CASES])
+@pytest.mark.parametrize("name,det", CASES, ids=[f"{n}-{ROUTE_NAMES[d]}" for n, d in CASES])
 def test_fullsize_sampled_rows(name, det):
     w = W[name]
     det = w.deterministic if det is None else det
@@ -113,7 +119,7 @@ def test_fullsize_sampled_rows(name, det):
         ref_v.append(rv)
         got_k.append(dk[b, kh, rows])
         got_v.append(dv[b, kh, rows])
-    tag = f"{name} ({'deterministic' if det else 'fp32 atomic'})"
+    tag = f"{name} (dQ route {ROUTE_NAMES[int(det)]})"
     C.assert_close(f"{tag} dQ sampled rows", np.concatenate(got_q), np.concatenate(ref_q))
     C.assert_close(f"{tag} dK sampled rows", np.concatenate(got_k), np.concatenate(ref_k))
     C.assert_close(f"{tag} dV sampled rows", np.concatenate(got_v), np.concatenate(ref_v))
@@ -138,14 +144,15 @@ def test_fullsize_sampled_rows(name, det):
             assert np.all(dk[b, :, L:] == 0) and np.all(dv[b, :, L:] == 0)
 
 
-def test_fullsize_deterministic_bitwise():
-    # the S=8192, D=256 deterministic workload: 10 runs, identical bits
-    name = "mha_det_s8192_d256"
+@pytest.mark.parametrize("name,det", [("mha_det_s8192_d256", True), ("gqa_causal_s4096_d128", 3)],
+                         ids=["mha_det_s8192_d256-det", "gqa_causal_s4096_d128-dqpartials"])
+def test_fullsize_deterministic_bitwise(name, det):
+    # 10 runs of a deterministic route at full size, identical bits
     w = W[name]
     t, _ = prepared(name)
     digests = set()
     for run in range(10):
-        out = _run(w, t, True)
+        out = _run(w, t, det)
         h = hashlib.sha256()
         for x in out:
             h.update(np.ascontiguousarray(x).view(np.uint32).tobytes())

@@ -65,12 +65,12 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("det", [False, True], ids=["atomic", "det"])
+@pytest.mark.parametrize("det", [0, 2, 3], ids=["atomic", "dspanels", "dqpartials"])
 @pytest.mark.parametrize("case_def", CASES, ids=[c[0] for c in CASES])
 def test_strided_layouts(case_def, det):
     import attention_backward_sdpa_amd as lib
     name, w, in_kinds, out_kinds = case_def
-    C.log(f"layout case {name} ({'det' if det else 'atomic'}): {w}")
+    C.log(f"layout case {name} (dQ route {det}): {w}")
     case = C.make_case(w)
     ref = C.oracle_backward(case)
     ins = [place(case[x], kind, 0x1234)[1] for x, kind in zip(("q", "k", "v", "o", "do"), in_kinds)]

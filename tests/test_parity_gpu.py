@@ -57,13 +57,18 @@ SMALL_CASES = {
 }
 
 
+# dQ routes (the `deterministic` argument): None = the workload's own (False / True)
+ROUTES = {"default": None, "dspanels": 2, "dqpartials": 3}
+
+
+@pytest.mark.parametrize("route", list(ROUTES))
 @pytest.mark.parametrize("name", list(SMALL_CASES))
-def test_small_parity(name):
+def test_small_parity(name, route):
     w = SMALL_CASES[name]
-    C.log(f"case {name}: {w}")
+    C.log(f"case {name} route {route}: {w}")
     case = C.make_case(w)
     ref = C.oracle_backward(case)
-    got = C.run_gpu(case, torch)
+    got = C.run_gpu(case, torch, deterministic=ROUTES[route])
     for tname, g, r in zip(("dQ", "dK", "dV"), got, ref):
         C.assert_close(f"{name} {tname}", g, r)
     # padded rows are exactly zero
@@ -73,8 +78,11 @@ def test_small_parity(name):
             assert np.all(got[1][b, :, L:] == 0) and np.all(got[2][b, :, L:] == 0)
 
 
-def test_deterministic_bitwise_over_runs():
-    w = SMALL_CASES["det_d256_s200"]
+@pytest.mark.parametrize("name,det", [("det_d256_s200", True), ("gqa_causal_d128_s333", 2),
+                                      ("gqa_causal_d128_s333", 3), ("split_causal_d128_s600", 3)])
+def test_deterministic_bitwise_over_runs(name, det):
+    # 10 runs over a workspace refilled with random bytes each time: identical bits
+    w = SMALL_CASES[name]
     case = C.make_case(w)
     t = C.to_device(case, torch)
     gen = torch.Generator(device="cpu").manual_seed(0)
@@ -84,7 +92,7 @@ def test_deterministic_bitwise_over_runs():
 
     first = None
     for run in range(10):
-        out = C.run_gpu(case, torch, dev_inputs=t, ws_fill=random_bytes)
+        out = C.run_gpu(case, torch, deterministic=det, dev_inputs=t, ws_fill=random_bytes)
         if first is None:
             first = out
         else:
@@ -92,17 +100,20 @@ def test_deterministic_bitwise_over_runs():
                 assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"run {run} differs"
 
 
-def test_deterministic_agrees_with_atomic_route():
+def test_routes_agree():
     w = SMALL_CASES["gqa_causal_d128_s333"]
     case = C.make_case(w)
-    a = C.run_gpu(case, torch, deterministic=False)
-    b = C.run_gpu(case, torch, deterministic=True)
     ref = C.oracle_backward(case)
-    for tname, x, y, r in zip(("dQ", "dK", "dV"), a, b, ref):
-        C.assert_close(f"det-vs-atomic {tname}", x, r)
-        C.assert_close(f"det-vs-atomic {tname} (det)", y, r)
-    # dK and dV are deterministic in both modes and computed by the same main kernel
-    assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+    outs = {r: C.run_gpu(case, torch, deterministic=r) for r in (0, 1, 2, 3)}
+    for r, out in outs.items():
+        for tname, x, rr in zip(("dQ", "dK", "dV"), out, ref):
+            C.assert_close(f"route {r} {tname}", x, rr)
+    # dK and dV are deterministic on every route and come from the same GEMM3/GEMM5 arithmetic
+    for r in (1, 2, 3):
+        assert np.array_equal(outs[0][1], outs[r][1]) and np.array_equal(outs[0][2], outs[r][2])
+    # at head dim 128 the deterministic choice is the dS-panel route
+    for x, y in zip(outs[1], outs[2]):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
 
 
 def test_linear_in_dO_bitwise():
@@ -166,7 +177,7 @@ SURFACE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("det", [False, True], ids=["atomic", "det"])
+@pytest.mark.parametrize("det", [0, 2, 3], ids=["atomic", "dspanels", "dqpartials"])
 @pytest.mark.parametrize("case_def", SURFACE_CASES, ids=[c[0] for c in SURFACE_CASES])
 def test_mask_and_shape_surface(case_def, det):
     import attention_backward_sdpa_amd as lib
@@ -201,4 +212,4 @@ def test_mask_and_shape_surface(case_def, det):
     torch.cuda.synchronize()
     got = [C.bf16_tensor_to_f32(x) for x in outs]
     for tname, g, r in zip(("dQ", "dK", "dV"), got, ref):
-        C.assert_close(f"{name} {'det' if det else 'atomic'} {tname}", g, r)
+        C.assert_close(f"{name} route {det} {tname}", g, r)
