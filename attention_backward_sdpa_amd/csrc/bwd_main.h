@@ -98,6 +98,15 @@ struct MainCfg {
   static constexpr int AHEAD = (NW == 8 && DQK > 128) ? 2 : 6;
   using M = Mfma32<F16>;
   static constexpr int N_DQT = DQK / MT, N_DVT = DV / MT;
+  // GEMM4 on 16 x 16 output blocks (v_mfma_f32_16x16x32) where the 32-column d tiles would leave
+  // whole SIMDs without GEMM4 work (fewer tiles than SIMDs: head dim 64): DQK / 8 blocks, NB4 per
+  // wave.  Where every SIMD gets a tile (head dims 128, 192) the 32 x 32 tiles stay: measured on
+  // MI355X, spreading GEMM4 over all waves there was slower (the causal GQA S=4096 D=128 main
+  // kernel 350 -> 385 us on the dQ-partial route, head dim 192 724 -> 809 us on the atomic
+  // route), because the waves without a tile start the next q tile early and so offset the two
+  // waves of each SIMD between their softmax and MFMA phases.
+  static constexpr bool G4_16 = G4 && N_DQT < 4 && ((DQK / 8) % NW) == 0;
+  static constexpr int NB4 = (DQK / 8) / NW;
   static constexpr int N_KQ = DQK / 16, N_KV = DV / 16;
   // q-tile buffer: [Q A-frags | dO A-frags | stats], fragments swizzled (see gather_frags)
   static constexpr int T_QA = 0;
@@ -362,6 +371,86 @@ struct TrALanes {
   }
 };
 
+// dS staging layout of the 16x16 GEMM4 (same 2 KiB per 32-key wave tile as the quads above, with
+// its own rotation): quad (key, qg) at byte 256 qg + 8 ((key + rot16(qg)) & 31).  The writer (32
+// keys of one qg per half-wave) and the GEMM4 transpose reads (keys 8G + 4 sec + 0..3 of lane
+// groups G = 0, 1 or 2, 3, four consecutive qg per half-wave) both touch every bank pair once.
+__device__ __forceinline__ constexpr int rot16(int qg) { return 4 * (qg & 1) + 16 * ((qg >> 1) & 1); }
+__device__ __forceinline__ int ds_store_off16(int lane, int x) {
+  const int qg = 2 * x + (lane >> 5);
+  return 256 * qg + (((lane & 31) + rot16(qg)) & 31) * 8;
+}
+
+// Per-lane offsets of the 16x16 GEMM4 transpose reads of wave w.  Its blocks all lie in row half
+// h = w % 2 and have 16-column blocks cb of one parity c = (w / 2) % 2 (NW / 2 is even).  MFMA
+// step s covers the keys of wave tile s (32 keys); lane group G = lane / 16 holds k slots
+// 8G .. 8G + 7 = keys 8G + 0..7 of the step, as two ds_read_b64_tr_b16 of 4 keys (sec 0, 1).
+// Within a 16-lane block, addressing lane r = 4 jj + cc points at key 8G + 4 sec + jj and
+//   dS: q group qg = 4h + cc (rows 4 qg .. +3 of the quad), output lane i = q row 16h + i;
+//   K:  row (G / 2) + 2 (cc / 2) of the fragment, chunk 8 (G % 2) + 4 sec + jj (swizzled as
+//       gather_frags stores it), 8-byte half cc % 2: d columns 4 cc .. +3 of the 16-column block.
+struct Gemm4Lanes16 {
+  int a[2], b[2];
+  __device__ __forceinline__ Gemm4Lanes16(int lane, int w) {
+    const int G = lane >> 4, jj = (lane & 15) >> 2, cc = lane & 3;
+    const int h = w & 1, c = (w >> 1) & 1;
+    const int qg = 4 * h + cc;
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int key = 8 * G + 4 * sec + jj;
+      a[sec] = 256 * qg + 8 * ((key + rot16(qg)) & 31);
+      b[sec] = ((G >> 1) + 2 * (cc >> 1)) * 256 +
+               ((8 * (G & 1) + 4 * sec + jj) ^ (4 * kswz(2 * (cc >> 1), c))) * 16 + 8 * (cc & 1);
+    }
+  }
+  __device__ __forceinline__ bf16x8 ds(const char* sST, int s) const {
+    return concat(lds_read_tr(sST, s * 2048 + a[0]), lds_read_tr(sST, s * 2048 + a[1]));
+  }
+  template <int DQK>
+  __device__ __forceinline__ bf16x8 k(const char* sK, int s, int cb) const {
+    const int base = (s * (DQK / 16) + cb) * 1024;
+    return concat(lds_read_tr(sK, base + b[0]), lds_read_tr(sK, base + b[1]));
+  }
+};
+
+// GEMM4 for one q tile on 16 x 16 blocks (C::G4_16): wave w computes blocks w + NW m, m < NB4,
+// block b = (row half b % 2, 16-column block b / 2).  Emission as in gemm4 below, with the
+// partial block's layout: block (h, cb) is 1 KiB at float offset 256 (h (Dqk / 16) + cb), lane l's
+// four floats (rows 16h + 4 (l / 16) + 0..3, column 16 cb + l % 16) the 16 bytes at 4 l.
+template <class C>
+__device__ __forceinline__ void gemm4_16(const char* sST, const char* sK, float* dst, int q0,
+                                         int Lq, int w, int lane) {
+  using M16 = Mfma16<C::F16>;
+  constexpr int DQK = C::DQK, NB = C::NB4, NW = C::NW;
+  const Gemm4Lanes16 tl(lane, w);
+  floatx4 acc[NB];
+#pragma unroll
+  for (int m = 0; m < NB; ++m) acc[m] = floatx4{};
+#pragma unroll
+  for (int s = 0; s < C::BC / 32; ++s) {
+    const bf16x8 a = tl.ds(sST, s);
+#pragma unroll
+    for (int m = 0; m < NB; ++m) acc[m] = M16::mma(a, tl.template k<DQK>(sK, s, (w + NW * m) >> 1), acc[m]);
+  }
+  const int h = w & 1, G = lane >> 4, col_l = lane & 15;
+#pragma unroll
+  for (int m = 0; m < NB; ++m) {
+    const int cb = (w + NW * m) >> 1;
+    if constexpr (C::MODE == DQ_PARTIAL) {
+      __builtin_nontemporal_store(acc[m], reinterpret_cast<floatx4*>(dst + (h * (DQK / 16) + cb) * 256) + lane);
+    } else {
+      float* col0 = dst + 16 * cb + col_l;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * h + 4 * G + r;
+        if (q0 + row < Lq)
+          __hip_atomic_fetch_add(col0 + row * DQK, acc[m][r], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
 // GEMM4 for one q tile: dQ (32 q x Dqk) = dS K over the tile's keys.  dS sits in sST in register
 // order (block (w,kt,x) of 64 lanes x 4 q, see the writer) and K in sK as B fragments of GEMM1;
 // both are read with the transpose instruction.  Wave w handles the 32-column d tiles w, w + NW,
@@ -555,7 +644,10 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
         // GEMM4 of the previous q tile (dS in sST), deferred so its atomics / partial stores
         // overlap this tile
         if (i < i_hi) {
-          gemm4<C>(sST(i + 1), sK, dq_dst(i + 1), q0 + BR, mg.Lq, w, lane);
+          if constexpr (C::G4_16)
+            gemm4_16<C>(sST(i + 1), sK, dq_dst(i + 1), q0 + BR, mg.Lq, w, lane);
+          else
+            gemm4<C>(sST(i + 1), sK, dq_dst(i + 1), q0 + BR, mg.Lq, w, lane);
           // single buffer: every wave is done reading it before this tile's dS overwrites it
           // (the atomics / stores keep draining)
           if constexpr (C::NSST == 1) lds_barrier();
@@ -615,10 +707,11 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
 #pragma unroll
         for (int x = 0; x < 8; ++x) sb_prev[x] = sb[x];
       } else {
-        // dS of the wave's 32 keys to LDS as 2 KiB of quads (see ds_store_off)
+        // dS of the wave's 32 keys to LDS as 2 KiB of quads (see ds_store_off / ds_store_off16)
 #pragma unroll
         for (int x = 0; x < 4; ++x)
-          *reinterpret_cast<u32x2*>(sST(i) + w * 2048 + ds_store_off(lane, x)) =
+          *reinterpret_cast<u32x2*>(sST(i) + w * 2048 +
+                                    (C::G4_16 ? ds_store_off16(lane, x) : ds_store_off(lane, x))) =
               u32x2{sb[2 * x], sb[2 * x + 1]};
       }
       // (raised wave priority: this MFMA-only phase issues ahead of the other wave's softmax)
@@ -635,7 +728,10 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
     if constexpr (C::DS_OUT) store_ds(i_lo);
     if constexpr (C::G4) {
       lds_barrier();  // the last tile's dS is complete
-      gemm4<C>(sST(i_lo), sK, dq_dst(i_lo), i_lo * BR, mg.Lq, w, lane);
+      if constexpr (C::G4_16)
+        gemm4_16<C>(sST(i_lo), sK, dq_dst(i_lo), i_lo * BR, mg.Lq, w, lane);
+      else
+        gemm4<C>(sST(i_lo), sK, dq_dst(i_lo), i_lo * BR, mg.Lq, w, lane);
     }
   }
 

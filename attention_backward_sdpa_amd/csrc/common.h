@@ -125,6 +125,19 @@ struct Mfma32 : Mfma<32> {
   }
 };
 
+// 16x16x32 MFMA on bf16 or fp16 operands (v_mfma_f32_16x16x32_bf16 / _f16, same lane layouts).
+template <bool F16>
+struct Mfma16 : Mfma<16> {
+  __device__ __forceinline__ static acc_t mma(bf16x8 a, bf16x8 b, acc_t c) {
+    if constexpr (F16) {
+      return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
+                                                    __builtin_bit_cast(half8, b), c, 0, 0, 0);
+    } else {
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+  }
+};
+
 // Row (within the tile) of accumulator register r for lane group g.
 template <int MT>
 __device__ __forceinline__ constexpr int acc_row(int r, int g) {

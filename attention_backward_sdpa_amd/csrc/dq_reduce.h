@@ -8,9 +8,13 @@
 // order, so the result is bitwise reproducible.
 //
 // It is a pure stream of the partials (bound by HBM): one workgroup per (q tile, batch, query
-// head), one thread per (32-column d tile, lane) holding the 16 floats that lane wrote, four
-// blocks of loads (16 x 16 bytes per thread) in flight ahead of the adds.  The sums go through LDS
-// once to leave as row-major 16-byte vectors of the io type.
+// head) of 2 Dqk threads, each summing four 16-byte vectors of every block (coalesced: vector
+// tid + 2 Dqk x), four blocks of loads in flight ahead of the adds.  The sums go through LDS once
+// to leave as row-major 16-byte vectors of the io type.  A block's layout is GEMM4's (bwd_main.h):
+//   L16 (16 x 16 output blocks): vector v = 64 (h Dqk/16 + cb) + l holds rows 16h + 4(l/16) + 0..3,
+//        column 16 cb + l % 16;
+//   else (32 x 32 d tiles):      vector v = 256 dt + 64 x + l holds rows 8x + 4(l/32) + 0..3,
+//        column 32 dt + l % 32.
 #pragma once
 #include "common.h"
 #include "masks.h"
@@ -30,12 +34,12 @@ struct DqReduceParams {
   float scale;
 };
 
-template <int DQK, bool F16>
+template <int DQK, bool F16, bool L16>
 __global__ void __launch_bounds__(DQK * 2) dq_reduce_kernel(DqReduceParams p) {
   constexpr int NT = DQK * 2, BR = 32, U = 4;
   constexpr int ROWF = DQK + 4;  // padded LDS row (floats)
   __shared__ __attribute__((aligned(16))) float sT[BR * ROWF];
-  const int tid = threadIdx.x, lane = tid & 63, dt = tid >> 6;
+  const int tid = threadIdx.x;
 
   // q tiles in descending order (under a causal mask the last ones sum the most blocks);
   // consecutive workgroups are different heads
@@ -74,7 +78,7 @@ __global__ void __launch_bounds__(DQK * 2) dq_reduce_kernel(DqReduceParams p) {
 
   const int64_t blk = (int64_t)BR * DQK / 4;  // float4s per block
   const floatx4* src = reinterpret_cast<const floatx4*>(p.dqp_ws) +
-                       ((int64_t)bh * p.n_kv_tiles * p.n_q_tiles + i) * blk + dt * 256 + lane;
+                       ((int64_t)bh * p.n_kv_tiles * p.n_q_tiles + i) * blk + tid;
   const int64_t jstride = (int64_t)p.n_q_tiles * blk;
   floatx4 s[4] = {floatx4{}, floatx4{}, floatx4{}, floatx4{}};
   for (int j0 = jlo; j0 <= jhi; j0 += U) {
@@ -83,7 +87,7 @@ __global__ void __launch_bounds__(DQK * 2) dq_reduce_kernel(DqReduceParams p) {
     for (int u = 0; u < U; ++u) {
       const int jj = min(j0 + u, jhi);  // past the range: re-read the last block, unused
 #pragma unroll
-      for (int x = 0; x < 4; ++x) v[u][x] = __builtin_nontemporal_load(src + jj * jstride + 64 * x);
+      for (int x = 0; x < 4; ++x) v[u][x] = __builtin_nontemporal_load(src + jj * jstride + NT * x);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -94,12 +98,21 @@ __global__ void __launch_bounds__(DQK * 2) dq_reduce_kernel(DqReduceParams p) {
     }
   }
 
-  // lane's floats: rows 8x + 4(lane / 32) + e, column 32 dt + lane % 32
-  const int g = lane >> 5, col = dt * 32 + (lane & 31);
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < 4; ++x) {
+    const int vec = tid + NT * x, l = vec & 63;
+    int row0, col;
+    if constexpr (L16) {
+      const int b16 = vec >> 6;
+      row0 = 16 * (b16 / (DQK / 16)) + 4 * (l >> 4);
+      col = 16 * (b16 % (DQK / 16)) + (l & 15);
+    } else {
+      row0 = 8 * ((vec >> 6) & 3) + 4 * (l >> 5);
+      col = 32 * (vec >> 8) + (l & 31);
+    }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sT[(8 * x + 4 * g + e) * ROWF + col] = s[x][e] * p.scale;
+    for (int e = 0; e < 4; ++e) sT[(row0 + e) * ROWF + col] = s[x][e] * p.scale;
+  }
   __syncthreads();
 
   constexpr int V = DQK / 8;  // 8-element output vectors per row

@@ -211,12 +211,20 @@ hipError_t run_main(int Dqk, int Dv, const MainParams& mp, Route route, bool f16
   return dispatch_main<256, 256, 32, 4>(mp, route, f16, grid, bc, s);
 }
 
+// the reduction reads the partial blocks in the layout of the main kernel that wrote them
+template <int DQK, int DV, int NW>
+constexpr bool partial_l16() { return MainCfg<DQK, DV, 32, NW, DQ_PARTIAL>::G4_16; }
+
 template <bool F16>
 hipError_t launch_dq_reduce_t(const DqReduceParams& rp, int Dqk, int grid, hipStream_t s) {
-  if (Dqk == 64) hipLaunchKernelGGL((dq_reduce_kernel<64, F16>), dim3(grid), dim3(128), 0, s, rp);
-  else if (Dqk == 128) hipLaunchKernelGGL((dq_reduce_kernel<128, F16>), dim3(grid), dim3(256), 0, s, rp);
-  else if (Dqk == 192) hipLaunchKernelGGL((dq_reduce_kernel<192, F16>), dim3(grid), dim3(384), 0, s, rp);
-  else hipLaunchKernelGGL((dq_reduce_kernel<256, F16>), dim3(grid), dim3(512), 0, s, rp);
+  if (Dqk == 64)
+    hipLaunchKernelGGL((dq_reduce_kernel<64, F16, partial_l16<64, 64, 8>()>), dim3(grid), dim3(128), 0, s, rp);
+  else if (Dqk == 128)
+    hipLaunchKernelGGL((dq_reduce_kernel<128, F16, partial_l16<128, 128, 8>()>), dim3(grid), dim3(256), 0, s, rp);
+  else if (Dqk == 192)
+    hipLaunchKernelGGL((dq_reduce_kernel<192, F16, partial_l16<192, 128, 8>()>), dim3(grid), dim3(384), 0, s, rp);
+  else
+    hipLaunchKernelGGL((dq_reduce_kernel<256, F16, partial_l16<256, 256, 4>()>), dim3(grid), dim3(512), 0, s, rp);
   return hipGetLastError();
 }
 
