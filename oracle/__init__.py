@@ -8,6 +8,7 @@ from .sdpa_oracle import (  # noqa: F401
     visible_mask,
     forward,
     backward,
+    dsink,
     backward_dq_rows,
     backward_dkdv_rows,
     attention_flops,

@@ -24,10 +24,18 @@ Sources (cited by page title and section):
     printed equations place the softmax scale as dQ = scale * dS K and dK = scale * dS^T Q, with dS
     the unscaled softmax vector-Jacobian product, and dV = P^T dO.
 
+  * same page, "The kernel chain" (dsink) and "Support surface" (sink tokens): a per-query-head sink
+    logit joins every row's softmax denominator without a value vector; the forward LSE folds it
+    in, so dQ/dK/dV need no sink term, and the sink's gradient is
+    dsink[h] = -sum over batch entries and query rows of exp(sink[h] - LSE) * delta.
+
 Readings taken where the pages leave a step open:
   * the default scale uses D_qk (the contraction length of Q K^T) when D_qk != D_v;
   * delta is formed from the O that is handed in (not re-derived as rowsum(P * dP));
-  * the window bound is inclusive: W + 1 keys are visible on a causal row, the diagonal included.
+  * the window bound is inclusive: W + 1 keys are visible on a causal row, the diagonal included;
+  * with a sink, a query row below seq_q that sees no key still has the sink in its denominator
+    (LSE = sink, O = 0); rows at or past seq_q do not exist (LSE = -inf, O = 0) and contribute
+    nothing to dsink.
 """
 import math
 
@@ -63,12 +71,14 @@ def _lens(B, S, lens):
 
 
 def forward(q, k, v, scale, causal=False, window_left=-1, seq_q_lens=None, seq_kv_lens=None,
-            bottom_right=False, window_right=0):
+            bottom_right=False, window_right=0, sink=None):
     """Softmax-attention forward in fp64; returns (O, LSE), O (B,Hq,Sq,Dv), LSE (B,Hq,Sq) natural log.
 
     s_ij = scale * q_i . k_j on visible pairs and -inf elsewhere; LSE_i = log sum_j exp(s_ij) with
     LSE_i = -inf on a row that sees no key; P = exp(s - LSE); O = P V.  Rows with no visible key
-    have O = 0.  (The forward is not the method; it produces the O and LSE the backward consumes.)
+    have O = 0.  With sink (Hq,) logits, every row below seq_q adds exp(sink[h]) to its
+    denominator (the sink has no value vector).  (The forward is not the method; it produces the
+    O and LSE the backward consumes.)
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -81,14 +91,19 @@ def forward(q, k, v, scale, causal=False, window_left=-1, seq_q_lens=None, seq_k
     LSE = np.full((B, Hq, Sq), -np.inf)
     for b in range(B):
         vis = visible_mask(Sq, Skv, causal, window_left, Lq[b], Lkv[b], bottom_right, window_right)
-        rows = vis.any(axis=1)
         for h in range(Hq):
             kh = h // group
             s = scale * (q[b, h] @ k[b, kh].T)
             s = np.where(vis, s, -np.inf)
-            m = np.where(rows, s.max(axis=1, initial=-np.inf), 0.0)
-            p_un = np.where(vis, np.exp(s - m[:, None]), 0.0)
-            denom = p_un.sum(axis=1)
+            if sink is not None and np.isfinite(sink[h]):
+                # the sink is one more logit in the denominator of every existing row
+                s_all = np.concatenate([s, np.where(np.arange(Sq) < Lq[b], float(sink[h]),
+                                                    -np.inf)[:, None]], axis=1)
+            else:
+                s_all = s
+            rows = np.isfinite(s_all).any(axis=1)
+            m = np.where(rows, s_all.max(axis=1, initial=-np.inf), 0.0)
+            denom = np.exp(s_all - m[:, None]).sum(axis=1)
             lse = np.where(rows, m + np.log(np.where(rows, denom, 1.0)), -np.inf)
             p = np.where(vis, np.exp(s - np.where(rows, lse, 0.0)[:, None]), 0.0)
             O[b, h] = p @ v[b, kh]
@@ -156,6 +171,32 @@ def backward(q, k, v, o, do, lse, scale, causal=False, window_left=-1, seq_q_len
     if return_intermediates:
         return dq, dk, dv, delta_all, ds_all
     return dq, dk, dv
+
+
+def dsink(o, do, lse, sink, seq_q_lens=None):
+    """Gradient of the sink logits, (Hq,): dsink[h] = -sum_{b, q} exp(sink[h] - LSE[b,h,q]) * delta[b,h,q].
+
+    "SDPA Backward (SM120)", "The kernel chain" (dsink) and "Support surface" (sink tokens): the
+    sink is a logit without a value vector, so its softmax VJP entry on row q is
+    P_sink * (0 - delta) with P_sink = exp(sink - LSE) and delta = rowsum(O * dO); the sink is
+    shared by every batch entry and row.  Rows at or past seq_q and rows whose LSE is -inf
+    contribute nothing.
+    """
+    o = np.asarray(o, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    B, Hq, Sq, _ = o.shape
+    Lq = _lens(B, Sq, seq_q_lens)
+    out = np.zeros(Hq)
+    for h in range(Hq):
+        total = 0.0
+        for b in range(B):
+            delta = np.sum(o[b, h] * do[b, h], axis=1)
+            live = (np.arange(Sq) < Lq[b]) & np.isfinite(lse[b, h])
+            p_sink = np.exp(float(sink[h]) - np.where(live, lse[b, h], 0.0))
+            total += float(np.sum(np.where(live, p_sink * delta, 0.0)))
+        out[h] = -total
+    return out
 
 
 def backward_dq_rows(q, k, v, o, do, lse, scale, b, h, rows, causal=False, window_left=-1,

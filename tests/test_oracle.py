@@ -11,7 +11,9 @@
 * structure: GQA equals MHA on repeated K/V with group-summed dK/dV, padding equals the unpadded
   per-batch slice, linearity in dO;
 * the row-sampled functions equal the full backward;
-* mutation checks: deliberately broken backwards (planted here, on the CPU) fail the same checks.
+* mutation checks: deliberately broken backwards (planted here, on the CPU) fail the same checks;
+* sink tokens: finite differences in the sink logits and in Q, K, V with the sink folded into the
+  forward, a one-key closed form, the -inf limit (no sink) and the row sums of dS.
 """
 import math
 import os
@@ -356,3 +358,121 @@ def test_planted_mistakes_are_caught(kind):
     q, k, v, do, o, lse, scale, kw = _problem(23, B=1, Hq=2, Hkv=2, Sq=5, Skv=5, Dqk=4, Dv=4,
                                               causal=True)
     assert _fd_check(_mutant(kind), q, k, v, do, scale, kw) > 1e-3
+
+
+# ----------------------------------------------------------------------------------------------
+# sink tokens ("SDPA Backward (SM120)", "The kernel chain" (dsink) and "Support surface"):
+# finite differences of L = sum(dO * O(Q, K, V, sink)), a closed form, the -inf limit and the
+# row-sum identity with the sink's own softmax entry
+SINK_MASKS = [dict(causal=False, W=-1), dict(causal=True, W=-1), dict(causal=True, W=1, lens=[4]),
+              dict(causal=True, W=-1, br=True)]
+
+
+def _sink_problem(seed, mask, B=1, Hq=2, Hkv=1, S=5, D=4):
+    q, k, v, do, _, _, scale, kw = _problem(seed, B=B, Hq=Hq, Hkv=Hkv, Sq=S, Skv=S, Dqk=D, Dv=D,
+                                            **dict(mask, lens=None if mask.get("lens") is None
+                                                   else mask["lens"] * B))
+    sink = np.random.default_rng(seed + 100).standard_normal(Hq) + 0.5
+    o, lse = oracle.forward(q, k, v, scale, sink=sink, **kw)
+    return q, k, v, do, o, lse, scale, kw, sink
+
+
+@pytest.mark.parametrize("mask", SINK_MASKS, ids=str)
+def test_sink_finite_differences(mask):
+    q, k, v, do, o, lse, scale, kw, sink = _sink_problem(31, mask, B=2)
+    h = 1e-6
+    # dsink against central differences in each sink logit
+    got = oracle.dsink(o, do, lse, sink, seq_q_lens=kw["seq_q_lens"])
+    for hh in range(len(sink)):
+        sp, sm = sink.copy(), sink.copy()
+        sp[hh] += h
+        sm[hh] -= h
+        lp = np.sum(do * oracle.forward(q, k, v, scale, sink=sp, **kw)[0])
+        lm = np.sum(do * oracle.forward(q, k, v, scale, sink=sm, **kw)[0])
+        fd = (lp - lm) / (2 * h)
+        assert abs(got[hh] - fd) <= 1e-6 * max(1.0, abs(fd)), (hh, got[hh], fd)
+    # dQ/dK/dV need no sink term: the backward fed the sink-folded LSE matches the differences
+    grads = oracle.backward(q, k, v, o, do, lse, scale, **kw)
+    for idx, x in enumerate((q, k, v)):
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            mi = it.multi_index
+            old = x[mi]
+            x[mi] = old + h
+            lp = np.sum(do * oracle.forward(q, k, v, scale, sink=sink, **kw)[0])
+            x[mi] = old - h
+            lm = np.sum(do * oracle.forward(q, k, v, scale, sink=sink, **kw)[0])
+            x[mi] = old
+            fd[mi] = (lp - lm) / (2 * h)
+        assert np.max(np.abs(grads[idx] - fd)) <= 1e-6 * max(1.0, np.max(np.abs(fd)))
+
+
+def test_sink_single_key_closed_form():
+    # one key per row: P_key = 1 / (1 + exp(sink - x)), x = scale q.k; O = P_key v;
+    # dL/dsink = -P_key (1 - P_key) (v . dO) per row, summed over rows and batch entries
+    rng = np.random.default_rng(32)
+    B, Sq, D = 2, 4, 3
+    q = rng.standard_normal((B, 1, Sq, D))
+    k = rng.standard_normal((B, 1, 1, D))
+    v = rng.standard_normal((B, 1, 1, D))
+    do = rng.standard_normal((B, 1, Sq, D))
+    scale, sink = 0.7, np.array([0.3])
+    o, lse = oracle.forward(q, k, v, scale, sink=sink)
+    x = scale * np.einsum("bqd,bd->bq", q[:, 0], k[:, 0, 0])
+    p_key = 1.0 / (1.0 + np.exp(sink[0] - x))
+    np.testing.assert_allclose(o[:, 0], p_key[..., None] * v[:, 0, 0][:, None, :], atol=1e-14)
+    np.testing.assert_allclose(lse[:, 0], np.logaddexp(x, sink[0]), atol=1e-14)
+    vdo = np.einsum("bd,bqd->bq", v[:, 0, 0], do[:, 0])
+    ref = -np.sum(p_key * (1.0 - p_key) * vdo)
+    np.testing.assert_allclose(oracle.dsink(o, do, lse, sink), [ref], rtol=1e-13)
+
+
+def test_sink_at_minus_infinity_is_no_sink():
+    q, k, v, do, o, lse, scale, kw = _problem(33, B=1, Hq=2, Hkv=1, Sq=6, Skv=6, causal=True)
+    o2, lse2 = oracle.forward(q, k, v, scale, sink=np.array([-np.inf, -np.inf]), **kw)
+    np.testing.assert_array_equal(o2, o)
+    np.testing.assert_array_equal(lse2, lse)
+    assert np.all(oracle.dsink(o, do, lse, np.array([-np.inf, -np.inf])) == 0)
+
+
+@pytest.mark.parametrize("mask", SINK_MASKS, ids=str)
+def test_sink_row_sums(mask):
+    # with the sink in the softmax, sum_j dS_ij over the keys equals minus the sink's own entry
+    # P_sink (0 - delta): sum_j dS_ij = exp(sink - LSE_i) * delta_i; every row with a sink exists
+    q, k, v, do, o, lse, scale, kw, sink = _sink_problem(34, mask, B=1, Hq=2, S=7)
+    dq, dk, dv, delta, ds = oracle.backward(q, k, v, o, do, lse, scale, return_intermediates=True,
+                                            **kw)
+    L = 7 if kw["seq_q_lens"] is None else kw["seq_q_lens"][0]
+    for h in range(2):
+        p_sink = np.exp(sink[h] - lse[0, h, :L])
+        np.testing.assert_allclose(ds[0, h, :L].sum(axis=1), p_sink * delta[0, h, :L], atol=1e-12)
+        assert np.all(np.isneginf(lse[0, h, L:]))
+    np.testing.assert_allclose(oracle.dsink(o, do, lse, sink, seq_q_lens=kw["seq_q_lens"]),
+                               [-np.sum(np.exp(sink[h] - lse[0, h, :L]) * delta[0, h, :L])
+                                for h in range(2)], rtol=1e-13)
+
+
+@pytest.mark.parametrize("kind", ["sign", "no_delta", "rows_past_len"])
+def test_planted_dsink_mistakes_are_caught(kind):
+    q, k, v, do, o, lse, scale, kw, sink = _sink_problem(35, dict(causal=True, W=-1, lens=[3]),
+                                                         B=1, Hq=2, S=5)
+    o_bad = o.copy()
+    if kind == "no_delta":
+        o_bad = np.ones_like(o)          # delta from the wrong O
+    got = oracle.dsink(o_bad, do, lse, sink, seq_q_lens=None if kind == "rows_past_len" else
+                       kw["seq_q_lens"])
+    if kind == "sign":
+        got = -got
+    if kind == "rows_past_len":          # padded rows given a finite LSE would leak in
+        lse2 = np.where(np.isfinite(lse), lse, 0.0)
+        got = oracle.dsink(o + 1.0, do, lse2, sink)
+    h = 1e-6
+    fd = []
+    for hh in range(2):
+        sp, sm = sink.copy(), sink.copy()
+        sp[hh] += h
+        sm[hh] -= h
+        fd.append((np.sum(do * oracle.forward(q, k, v, scale, sink=sp, **kw)[0]) -
+                   np.sum(do * oracle.forward(q, k, v, scale, sink=sm, **kw)[0])) / (2 * h))
+    assert np.max(np.abs(np.asarray(got) - np.asarray(fd))) > 1e-3
