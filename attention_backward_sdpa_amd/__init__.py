@@ -22,6 +22,22 @@ class Layout(ctypes.Structure):
     """sdpa_bwd_layout: element strides (batch, head, seq) of a (B, H, S, D) tensor."""
     _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("seq", ctypes.c_int64)]
 
+
+
+class Args(ctypes.Structure):
+    """sdpa_bwd_args: every argument of one sdpa_bwd_run call."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "k", "v", "o", "dO", "lse", "dq", "dk", "dv")] + \
+        [(n, ctypes.c_int) for n in ("B", "Hq", "Hkv", "Sq", "Skv", "Dqk", "Dv")] + \
+        [("scale", ctypes.c_float)] + \
+        [(n, ctypes.c_int) for n in ("causal", "causal_bottom_right", "window_left",
+                                     "window_right", "deterministic")] + \
+        [("seq_q_lens", ctypes.c_void_p), ("seq_kv_lens", ctypes.c_void_p),
+         ("layouts", ctypes.c_void_p), ("dtype", ctypes.c_int), ("sink", ctypes.c_void_p),
+         ("dsink", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+         ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
+         ("events", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -54,6 +70,8 @@ def _load():
     lib.sdpa_bwd_flex.restype = i
     lib.sdpa_bwd_preprocess.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.sdpa_bwd_preprocess.restype = i
+    lib.sdpa_bwd_run.argtypes = [ctypes.POINTER(Args)]
+    lib.sdpa_bwd_run.restype = i
     lib.sdpa_bwd_dq_route.argtypes = [i, i, i]
     lib.sdpa_bwd_dq_route.restype = i
     lib.sdpa_bwd_status_string.argtypes = [i]
@@ -164,6 +182,38 @@ def sdpa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, windo
             _check(lib.sdpa_bwd_ex_events(*head, *tail, handles))
     else:
         _check(lib.sdpa_bwd_flex(*head, _layouts(tensors), _io_dtype(q), *tail, handles))
+
+
+def sdpa_bwd_run(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, window_left=-1,
+                 deterministic=False, seq_q_lens=None, seq_kv_lens=None,
+                 causal_bottom_right=False, window_right=0, sink=None, dsink=None,
+                 workspace=None, stream=None, events=None):
+    """sdpa_bwd_run(): the superset entry point (any dense layout with a contiguous head dim,
+    bf16 or fp16, and the sink gradient: dsink (Hq,) fp32 is written when given, from the sink
+    (Hq,) fp32 logits)."""
+    B, Hq, Hkv, Sq, Skv, Dqk, Dv = _dims(q, k, v)
+    tensors = (q, k, v, o, do, dq, dk, dv)
+    lay = _layouts(tensors)
+    handles = None
+    if events is not None:
+        handles = (ctypes.c_void_p * 5)(
+            *[ctypes.c_void_p(None if e is None else e.cuda_event) for e in events])
+    a = Args()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dO", do), ("lse", lse), ("dq", dq),
+                 ("dk", dk), ("dv", dv), ("seq_q_lens", seq_q_lens), ("seq_kv_lens", seq_kv_lens),
+                 ("sink", sink), ("dsink", dsink), ("workspace", workspace)):
+        setattr(a, n, None if t is None else t.data_ptr())
+    a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.Dqk, a.Dv = B, Hq, Hkv, Sq, Skv, Dqk, Dv
+    a.scale = -1.0 if scale is None else float(scale)
+    a.causal, a.causal_bottom_right = int(causal), int(causal_bottom_right)
+    a.window_left, a.window_right = int(window_left), int(window_right)
+    a.deterministic = int(deterministic)
+    a.layouts = ctypes.cast(lay, ctypes.c_void_p).value
+    a.dtype = _io_dtype(q)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.stream = _stream_handle(stream).value
+    a.events = None if handles is None else ctypes.cast(handles, ctypes.c_void_p).value
+    _check(_load().sdpa_bwd_run(ctypes.byref(a)))
 
 
 def sdpa_bwd_preprocess(o, do, lse, stats, dq_accum=None, seq_q_lens=None, Dqk=0, stream=None):

@@ -304,13 +304,15 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
         const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Skv,
         int Dqk, int Dv, float scale, int causal, int window_left, int deterministic,
         const int* seq_q_lens, const int* seq_kv_lens, int bottom_right, int window_right,
-        const sdpa_bwd_layout* layouts, int dtype, void* workspace, size_t workspace_bytes,
-        bool check_ws, hipStream_t stream, void* const* events) {
+        const sdpa_bwd_layout* layouts, int dtype, const float* sink, float* dsink,
+        void* workspace, size_t workspace_bytes, bool check_ws, hipStream_t stream,
+        void* const* events) {
   Geometry geo;
   int st = validate(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, window_left,
                     window_right, &geo);
   if (st != SDPA_BWD_OK) return st;
   if (dtype != SDPA_BWD_BF16 && dtype != SDPA_BWD_FP16) return SDPA_BWD_UNSUPPORTED;
+  if (dsink && (!sink || ((uintptr_t)sink & 3) || ((uintptr_t)dsink & 3))) return SDPA_BWD_INVALID_ARG;
   const bool f16 = dtype == SDPA_BWD_FP16;
   Layouts L = contiguous_layouts(Hq, Hkv, Sq, Skv, Dqk, Dv);
   if (layouts)
@@ -332,12 +334,29 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   };
 
   hipError_t e = hipSuccess;
+  // dsink over the preprocess's delta (no rows when the problem is empty: zeros)
+  auto launch_dsink = [&](const float* stats, int sq_pad, bool none) -> hipError_t {
+    if (!dsink) return hipSuccess;
+    DsinkParams dp;
+    dp.sink = sink;
+    dp.lse = lse;
+    dp.stats = stats;
+    dp.dsink = dsink;
+    dp.seq_q_lens = seq_q_lens;
+    dp.B = none ? 0 : B;
+    dp.Hq = Hq;
+    dp.Sq = Sq;
+    dp.sq_pad = sq_pad;
+    hipLaunchKernelGGL(dsink_kernel, dim3(Hq), dim3(256), 0, stream, dp);
+    return hipGetLastError();
+  };
   rec(0);
   if (empty) {
     // nothing attends: every gradient that exists is zero
     e = zero_rows(dq, L.t[T_DQ], B, Hq, Sq, Dqk, stream);
     if (e == hipSuccess) e = zero_rows(dk, L.t[T_DK], B, Hkv, Skv, Dqk, stream);
     if (e == hipSuccess) e = zero_rows(dv, L.t[T_DV], B, Hkv, Skv, Dv, stream);
+    if (e == hipSuccess) e = launch_dsink(nullptr, 0, true);
     for (int n = 1; n < 5; ++n) rec(n);
     return e == hipSuccess ? SDPA_BWD_OK : SDPA_BWD_LAUNCH_FAILED;
   }
@@ -363,6 +382,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   pp.Dqk = Dqk;
   pp.zero_rows = route == R_ATOMIC ? 1 : 0;
   e = launch_preprocess(pp, Dv, f16, (int64_t)B * Hq * (c.sq_pad / geo.br), stream);
+  if (e == hipSuccess) e = launch_dsink(stats, (int)c.sq_pad, false);
   if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   rec(1);
 
@@ -533,8 +553,8 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int Skv, int Dqk, int Dv, float scale, int causal, int window_left,
              int deterministic, void* workspace, void* stream) {
   return run(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, scale, causal,
-             window_left, deterministic, nullptr, nullptr, 0, 0, nullptr, SDPA_BWD_BF16,
-             workspace, 0, false, (hipStream_t)stream, nullptr);
+             window_left, deterministic, nullptr, nullptr, 0, 0, nullptr, SDPA_BWD_BF16, nullptr,
+             nullptr, workspace, 0, false, (hipStream_t)stream, nullptr);
 }
 
 int sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -545,8 +565,8 @@ int sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
                 size_t workspace_bytes, void* stream) {
   return run(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, scale, causal,
              window_left, deterministic, seq_q_lens, seq_kv_lens, causal_bottom_right,
-             window_right, nullptr, SDPA_BWD_BF16, workspace, workspace_bytes, true,
-             (hipStream_t)stream, nullptr);
+             window_right, nullptr, SDPA_BWD_BF16, nullptr, nullptr, workspace, workspace_bytes,
+             true, (hipStream_t)stream, nullptr);
 }
 
 int sdpa_bwd_ex_events(const void* q, const void* k, const void* v, const void* o,
@@ -558,8 +578,8 @@ int sdpa_bwd_ex_events(const void* q, const void* k, const void* v, const void* 
                        void* const* events) {
   return run(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, scale, causal,
              window_left, deterministic, seq_q_lens, seq_kv_lens, causal_bottom_right,
-             window_right, nullptr, SDPA_BWD_BF16, workspace, workspace_bytes, true,
-             (hipStream_t)stream, events);
+             window_right, nullptr, SDPA_BWD_BF16, nullptr, nullptr, workspace, workspace_bytes,
+             true, (hipStream_t)stream, events);
 }
 
 int sdpa_bwd_flex(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -571,8 +591,17 @@ int sdpa_bwd_flex(const void* q, const void* k, const void* v, const void* o, co
                   void* const* events) {
   return run(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, scale, causal,
              window_left, deterministic, seq_q_lens, seq_kv_lens, causal_bottom_right,
-             window_right, layouts, dtype, workspace, workspace_bytes, true, (hipStream_t)stream,
-             events);
+             window_right, layouts, dtype, nullptr, nullptr, workspace, workspace_bytes, true,
+             (hipStream_t)stream, events);
+}
+
+int sdpa_bwd_run(const sdpa_bwd_args* a) {
+  if (!a) return SDPA_BWD_INVALID_ARG;
+  return run(a->q, a->k, a->v, a->o, a->dO, a->lse, a->dq, a->dk, a->dv, a->B, a->Hq, a->Hkv,
+             a->Sq, a->Skv, a->Dqk, a->Dv, a->scale, a->causal, a->window_left, a->deterministic,
+             a->seq_q_lens, a->seq_kv_lens, a->causal_bottom_right, a->window_right, a->layouts,
+             a->dtype, a->sink, a->dsink, a->workspace, a->workspace_bytes, true,
+             (hipStream_t)a->stream, a->events);
 }
 
 int sdpa_bwd_preprocess(const void* o, const void* dO, const float* lse, float* stats,

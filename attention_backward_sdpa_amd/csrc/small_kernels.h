@@ -1,7 +1,7 @@
 // Bandwidth-bound kernels of the attention-backward chain ("SDPA Backward (SM120)", section
 // "The kernel chain"): the row-dot preprocess (delta = rowsum(O * dO), fused with zeroing the fp32
-// dQ accumulator), the dQ convert (fp32 accumulator -> bf16, times the softmax scale) and the
-// fixed-order GQA dK/dV group reduction ("GQA/MQA group reduction").
+// dQ accumulator), the dQ convert (fp32 accumulator -> bf16, times the softmax scale), the
+// fixed-order GQA dK/dV group reduction ("GQA/MQA group reduction") and the sink-gradient reduce.
 #pragma once
 #include "common.h"
 
@@ -156,6 +156,47 @@ __global__ void __launch_bounds__(256) gqa_reduce_kernel(ReduceParams p) {
                 Elem<F16>::pack2(s[4], s[5]), Elem<F16>::pack2(s[6], s[7])};
     }
   }
+}
+
+// ---- dsink ----------------------------------------------------------------------------------------
+// "The kernel chain" (dsink) and "Support surface" (sink tokens): the gradient of a per-query-head
+// sink logit, dsink[h] = -sum_{b, q} exp(sink[h] - LSE[b,h,q]) * delta[b,h,q], over the rows below
+// the batch entry's query length whose LSE is finite (delta as the preprocess stored it).  One
+// workgroup per query head; each thread sums the rows tid, tid + 256, ... in fp64, then a fixed
+// tree adds the 256 partial sums: the same order on every run, so the result is bitwise
+// reproducible.  Empty problems (B * Sq = 0) write 0.
+struct DsinkParams {
+  const float* sink;    // (Hq,)
+  const float* lse;     // (B, Hq, Sq)
+  const float* stats;   // (B*Hq, sq_pad, 2) from the preprocess, or null when B * Sq = 0
+  float* dsink;         // (Hq,)
+  const int* seq_q_lens;
+  int B, Hq, Sq, sq_pad;
+};
+
+__global__ void __launch_bounds__(256) dsink_kernel(DsinkParams p) {
+  __shared__ double part[256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const double sk = (double)p.sink[h];
+  double acc = 0.0;
+  const int64_t rows = (int64_t)p.B * p.Sq;
+  for (int64_t x = tid; x < rows; x += 256) {
+    const int b = (int)(x / p.Sq), q = (int)(x % p.Sq);
+    const int Lq = p.seq_q_lens ? min(max(p.seq_q_lens[b], 0), p.Sq) : p.Sq;
+    if (q >= Lq) continue;
+    const int64_t bh = (int64_t)b * p.Hq + h;
+    const float l = p.lse[bh * p.Sq + q];
+    if (!(l > -INFINITY)) continue;  // no key and no sink in the forward (or NaN): nothing
+    const float delta = p.stats[(bh * p.sq_pad + q) * 2 + 1];
+    acc += exp(sk - (double)l) * (double)delta;
+  }
+  part[tid] = acc;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) part[tid] += part[tid + off];
+    __syncthreads();
+  }
+  if (tid == 0) p.dsink[h] = (float)(0.0 - part[0]);
 }
 
 // ---- strided zero fill (gradients of shapes where nothing attends) ------------------------------

@@ -159,6 +159,50 @@ int sdpa_bwd_flex(const void* q, const void* k, const void* v, const void* o, co
                   int window_right, const sdpa_bwd_layout* layouts, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream, void* const* events);
 
+/* Every argument of one backward call, for sdpa_bwd_run.  The fields mean what the arguments of
+ * the same names mean for sdpa_bwd_flex (layouts NULL = every tensor contiguous BHSD; events NULL
+ * or five entries), plus the sink tokens ("SDPA Backward (SM120)", "API Usage" sink_token,
+ * "The kernel chain" dsink, "Support surface" sink tokens):
+ *   sink   (Hq,) fp32 device array of per-query-head sink logits, 4-byte aligned, or NULL.  The
+ *          forward's LSE already folds the sink into each row's softmax denominator, so dq, dk
+ *          and dv do not depend on it.
+ *   dsink  (Hq,) fp32 device output, 4-byte aligned, or NULL (then sink is not read):
+ *          dsink[h] = -sum over batch entries b and query rows q < seq_q_lens[b] whose LSE is
+ *          finite of exp(sink[h] - lse[b,h,q]) * rowsum(O * dO)[b,h,q], summed in a fixed order
+ *          (bitwise reproducible on every dQ route).  Overwritten, not accumulated into; 0 when
+ *          B or Sq is 0.  A non-NULL dsink with a NULL sink gives SDPA_BWD_INVALID_ARG.
+ * The dsink kernel runs right after the preprocess (inside the first event interval). */
+typedef struct sdpa_bwd_args {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dO;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, Sq, Skv, Dqk, Dv;
+  float scale;
+  int causal, causal_bottom_right, window_left, window_right;
+  int deterministic;
+  const int* seq_q_lens;
+  const int* seq_kv_lens;
+  const sdpa_bwd_layout* layouts;
+  int dtype;
+  const float* sink;
+  float* dsink;
+  void* workspace;
+  size_t workspace_bytes;
+  void* stream;
+  void* const* events;
+} sdpa_bwd_args;
+
+/* The superset entry point: everything sdpa_bwd_flex does, plus the sink gradient.  Same
+ * validation, workspace (sdpa_bwd_workspace_size; dsink needs none), stream and status rules;
+ * args NULL gives SDPA_BWD_INVALID_ARG. */
+int sdpa_bwd_run(const sdpa_bwd_args* args);
+
 /* Step 1 of the chain alone ("The kernel chain", dot), as the chain runs it: for every query row
  * (rows padded to Sq_pad = Sq rounded up to 32 per (b, h)) write the pair
  *     stats[(b*Hq + h)*Sq_pad + s] = { LSE * log2(e),  rowsum(O * dO) in fp32 }

@@ -29,7 +29,8 @@ def so():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("sdpa_bwd", "sdpa_bwd_ex", "sdpa_bwd_workspace_size", "sdpa_bwd_status_string",
-              "sdpa_bwd_ex_events", "sdpa_bwd_preprocess", "sdpa_bwd_flex", "sdpa_bwd_dq_route"):
+              "sdpa_bwd_ex_events", "sdpa_bwd_preprocess", "sdpa_bwd_flex", "sdpa_bwd_dq_route",
+              "sdpa_bwd_run"):
         assert n in names
 
 
@@ -186,3 +187,46 @@ def test_preprocess_rejections(so):
     assert so.sdpa_bwd_preprocess(p, p, p, p, None, None, 1, 1, 8, 96, 96, None) == lib.UNSUPPORTED
     assert so.sdpa_bwd_preprocess(None, p, p, p, None, None, 1, 1, 8, 128, 128, None) == lib.INVALID_ARG
     assert so.sdpa_bwd_preprocess(p, p, p, None, None, None, 1, 1, 8, 128, 128, None) == lib.INVALID_ARG
+
+
+def test_args_struct_layout_matches_header(tmp_path):
+    # the ctypes mirror of sdpa_bwd_args has the C layout: compile the header with gcc and compare
+    # the size and every field offset
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    names = [f[0] for f in lib.Args._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "sdpa_bwd.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(sdpa_bwd_args));\n' +
+                   "".join(f'  printf("%zu\\n", offsetof(sdpa_bwd_args, {n}));\n' for n in names) +
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(lib.Args)
+    assert out[1:] == [getattr(lib.Args, n).offset for n in names]
+
+
+def test_run_rejections_before_launch(so):
+    assert so.sdpa_bwd_run(None) == lib.INVALID_ARG
+    p = 4096  # aligned, never dereferenced: validation fails before any launch
+    a = lib.Args()
+    for n in ("q", "k", "v", "o", "dO", "lse", "dq", "dk", "dv"):
+        setattr(a, n, p)
+    a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.Dqk, a.Dv = 1, 4, 4, 64, 64, 128, 128
+    a.window_left = -1
+    need = _ws(Sq=64, Skv=64)
+    a.workspace, a.workspace_bytes = 1 << 20, need
+    a.dsink = 8192                      # dsink without sink logits
+    assert so.sdpa_bwd_run(ctypes.byref(a)) == lib.INVALID_ARG
+    a.sink = 8194                       # misaligned sink
+    assert so.sdpa_bwd_run(ctypes.byref(a)) == lib.INVALID_ARG
+    a.sink = 8196
+    a.workspace_bytes = need - 1        # with valid sink arguments the workspace check is reached
+    assert so.sdpa_bwd_run(ctypes.byref(a)) == lib.WORKSPACE_TOO_SMALL
+    a.deterministic = 5
+    assert so.sdpa_bwd_run(ctypes.byref(a)) == lib.INVALID_ARG

@@ -1,0 +1,110 @@
+"""GPU parity of the sink gradient ("SDPA Backward (SM120)", "API Usage" sink_token, "The kernel
+chain" dsink, "Support surface" sink tokens) through sdpa_bwd_run, against the fp64 oracle.
+
+The oracle's forward folds the sink logits into LSE (and O); the GPU chain receives exactly those
+bf16 / fp32 tensors.  dQ/dK/dV must match the oracle backward (the sink needs no term there) and
+dsink must match oracle.dsink, both to max|err| <= 1e-2 * max|ref|, on every dQ route; dsink is
+bitwise reproducible.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from attention_backward_sdpa_amd import synth
+from tests import _common as C
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+V = synth.small_variant
+
+CASES = {
+    # causal GQA, ragged S
+    "gqa_causal_d128_s333": V(W["gqa_causal_s4096_d128"], Hq=8, Hkv=2, Sq=333, Skv=333),
+    # MLA 192/128 with a window and padding (rows past seq_q must not enter dsink)
+    "mla_window_padded_s400": V(W["mla_window_padded_s4096"], B=3, Hq=2, Hkv=2, Sq=400, Skv=400,
+                                window_left=100, len_lo=100),
+    # non-causal D = 64, more rows than the dsink kernel's threads per head
+    "mha_d64_b3_s700": V(W["mha_s128_d64"], B=3, Hq=2, Hkv=2, Sq=700, Skv=300),
+}
+
+
+def _case(w, seed=7):
+    inp = synth.draw_inputs(w)
+    sink = np.random.default_rng(seed).standard_normal(w.Hq).astype(np.float32) + 1.0
+    f = C.f64
+    lens = None if inp.seq_q_lens is None else [int(x) for x in inp.seq_q_lens]
+    kw = dict(causal=w.causal, window_left=w.window_left, seq_q_lens=lens, seq_kv_lens=lens)
+    o64, lse64 = oracle.forward(f(inp.q), f(inp.k), f(inp.v), w.softmax_scale,
+                                sink=sink.astype(np.float64), **kw)
+    o_bits = synth.bf16_bits(o64.astype(np.float32))
+    lse = lse64.astype(np.float32)
+    ref = oracle.backward(f(inp.q), f(inp.k), f(inp.v), f(o_bits), f(inp.do),
+                          lse.astype(np.float64), w.softmax_scale, **kw)
+    ref_ds = oracle.dsink(f(o_bits), f(inp.do), lse.astype(np.float64), sink.astype(np.float64),
+                          seq_q_lens=lens)
+    return inp, o_bits, lse, sink, lens, ref, ref_ds
+
+
+def _run(w, inp, o_bits, lse, sink, lens, det, ws=None):
+    import attention_backward_sdpa_amd as lib
+    dev = "cuda"
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v, o, do = bf(inp.q), bf(inp.k), bf(inp.v), bf(o_bits), bf(inp.do)
+    tl = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=dev)
+    outs = [torch.empty_like(x) for x in (q, k, v)]
+    for x in outs:
+        x.view(torch.int16).fill_(0x7FC0)
+    dsink = torch.full((w.Hq,), float("nan"), dtype=torch.float32, device=dev)
+    if ws is None:
+        n = lib.workspace_size(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.Dqk, w.Dv, w.causal, w.window_left,
+                               det, lens is not None)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    lib.sdpa_bwd_run(q, k, v, o, do, torch.from_numpy(lse).to(dev), *outs, scale=w.softmax_scale,
+                     causal=w.causal, window_left=w.window_left, deterministic=det,
+                     seq_q_lens=tl, seq_kv_lens=tl, sink=torch.from_numpy(sink).to(dev),
+                     dsink=dsink, workspace=ws)
+    torch.cuda.synchronize()
+    return [C.bf16_tensor_to_f32(x) for x in outs], dsink.cpu().numpy()
+
+
+@pytest.mark.parametrize("det", [0, 2, 3], ids=["atomic", "dspanels", "dqpartials"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_sink_parity(name, det):
+    w = CASES[name]
+    C.log(f"sink case {name} route {det}: {w}")
+    inp, o_bits, lse, sink, lens, ref, ref_ds = _case(w)
+    got, ds = _run(w, inp, o_bits, lse, sink, lens, det)
+    for tname, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        C.assert_close(f"sink {name} route {det} {tname}", g, r)
+    C.assert_close(f"sink {name} route {det} dsink", ds, ref_ds)
+
+
+def test_dsink_bitwise_and_limits():
+    w = CASES["mha_d64_b3_s700"]
+    inp, o_bits, lse, sink, lens, ref, ref_ds = _case(w)
+    first = None
+    for _ in range(5):
+        _, ds = _run(w, inp, o_bits, lse, sink, lens, 0)
+        if first is None:
+            first = ds
+        assert np.array_equal(first.view(np.uint32), ds.view(np.uint32))
+    # a sink logit of -inf has no gradient
+    _, ds = _run(w, inp, o_bits, lse, np.full(w.Hq, -np.inf, dtype=np.float32), lens, 3)
+    assert np.all(ds == 0)
+
+
+def test_dsink_empty_problem_is_zero():
+    import attention_backward_sdpa_amd as lib
+    dev = "cuda"
+    q = torch.zeros(2, 2, 0, 64, dtype=torch.bfloat16, device=dev)
+    k = torch.zeros(2, 1, 40, 64, dtype=torch.bfloat16, device=dev)
+    v = torch.zeros(2, 1, 40, 64, dtype=torch.bfloat16, device=dev)
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    dsink = torch.full((2,), float("nan"), device=dev)
+    lib.sdpa_bwd_run(q, k, v, q, q, torch.zeros(2, 2, 0, device=dev), torch.empty_like(q), dk, dv,
+                     sink=torch.ones(2, device=dev), dsink=dsink)
+    torch.cuda.synchronize()
+    assert bool((dsink == 0).all()) and bool((dk == 0).all()) and bool((dv == 0).all())
