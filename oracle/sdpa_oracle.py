@@ -29,6 +29,11 @@ Sources (cited by page title and section):
     in, so dQ/dK/dV need no sink term, and the sink's gradient is
     dsink[h] = -sum over batch entries and query rows of exp(sink[h] - LSE) * delta.
 
+  * same page, "API Usage" (bias_tensor) and "Support surface" (bias): an additive bias of shape
+    (1 or B, H_q, S_q, S_kv) joins the scores after the softmax scale and before the softmax; its
+    gradient is dBias = dS (the unscaled softmax VJP), summed over the batch entries when the bias
+    has batch 1.
+
 Readings taken where the pages leave a step open:
   * the default scale uses D_qk (the contraction length of Q K^T) when D_qk != D_v;
   * delta is formed from the O that is handed in (not re-derived as rowsum(P * dP));
@@ -70,15 +75,24 @@ def _lens(B, S, lens):
     return [S] * B if lens is None else [int(x) for x in lens]
 
 
+def _bias_for(bias, b, h):
+    """The (S_q, S_kv) bias of batch entry b and query head h (batch-1 biases broadcast)."""
+    if bias is None:
+        return 0.0
+    bias = np.asarray(bias)
+    return np.asarray(bias[0 if bias.shape[0] == 1 else b, h], dtype=np.float64)
+
+
 def forward(q, k, v, scale, causal=False, window_left=-1, seq_q_lens=None, seq_kv_lens=None,
-            bottom_right=False, window_right=0, sink=None):
+            bottom_right=False, window_right=0, sink=None, bias=None):
     """Softmax-attention forward in fp64; returns (O, LSE), O (B,Hq,Sq,Dv), LSE (B,Hq,Sq) natural log.
 
     s_ij = scale * q_i . k_j on visible pairs and -inf elsewhere; LSE_i = log sum_j exp(s_ij) with
     LSE_i = -inf on a row that sees no key; P = exp(s - LSE); O = P V.  Rows with no visible key
     have O = 0.  With sink (Hq,) logits, every row below seq_q adds exp(sink[h]) to its
-    denominator (the sink has no value vector).  (The forward is not the method; it produces the
-    O and LSE the backward consumes.)
+    denominator (the sink has no value vector).  With bias (1 or B, Hq, Sq, Skv), s_ij gains
+    bias[b, h, i, j] on visible pairs.  (The forward is not the method; it produces the O and LSE
+    the backward consumes.)
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -93,7 +107,7 @@ def forward(q, k, v, scale, causal=False, window_left=-1, seq_q_lens=None, seq_k
         vis = visible_mask(Sq, Skv, causal, window_left, Lq[b], Lkv[b], bottom_right, window_right)
         for h in range(Hq):
             kh = h // group
-            s = scale * (q[b, h] @ k[b, kh].T)
+            s = scale * (q[b, h] @ k[b, kh].T) + _bias_for(bias, b, h)
             s = np.where(vis, s, -np.inf)
             if sink is not None and np.isfinite(sink[h]):
                 # the sink is one more logit in the denominator of every existing row
@@ -123,7 +137,8 @@ def _probabilities(s_scaled, lse, vis):
 
 
 def backward(q, k, v, o, do, lse, scale, causal=False, window_left=-1, seq_q_lens=None,
-             seq_kv_lens=None, bottom_right=False, window_right=0, return_intermediates=False):
+             seq_kv_lens=None, bottom_right=False, window_right=0, return_intermediates=False,
+             bias=None, return_dbias=False):
     """Exact SDPA backward in fp64: returns (dQ, dK, dV) shaped like Q, K, V.
 
     Per (batch b, query head h), with K/V taken from KV head h // group ("SDPA Backward (SM120)",
@@ -137,6 +152,9 @@ def backward(q, k, v, o, do, lse, scale, causal=False, window_left=-1, seq_q_len
         dK   += scale * dS^T Q
         dQ    = scale * dS K
     dK and dV of a KV head are summed over its group of query heads ("GQA/MQA group reduction").
+    With bias, P = exp(scale * Q K^T + bias - LSE) and, when return_dbias is set, dBias = dS
+    (summed over the batch entries for a batch-1 bias) is appended to the results ("API Usage"
+    bias_tensor, "Support surface" bias).
     With return_intermediates=True also returns delta (B,Hq,Sq) and dS (B,Hq,Sq,Skv).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -153,24 +171,31 @@ def backward(q, k, v, o, do, lse, scale, causal=False, window_left=-1, seq_q_len
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     delta_all = np.zeros((B, Hq, Sq)) if return_intermediates else None
+    dbias = None
+    if return_dbias:
+        dbias = np.zeros((np.asarray(bias).shape[0], Hq, Sq, Skv))
     ds_all = np.zeros((B, Hq, Sq, Skv)) if return_intermediates else None
     for b in range(B):
         vis = visible_mask(Sq, Skv, causal, window_left, Lq[b], Lkv[b], bottom_right, window_right)
         for h in range(Hq):
             kh = h // group
-            p = _probabilities(scale * (q[b, h] @ k[b, kh].T), lse[b, h], vis)
+            p = _probabilities(scale * (q[b, h] @ k[b, kh].T) + _bias_for(bias, b, h), lse[b, h],
+                               vis)
             delta = np.sum(o[b, h] * do[b, h], axis=1)
             dp = do[b, h] @ v[b, kh].T
             ds = p * (dp - delta[:, None])
+            if dbias is not None:
+                dbias[0 if dbias.shape[0] == 1 else b, h] += ds
             dv[b, kh] += p.T @ do[b, h]
             dk[b, kh] += scale * (ds.T @ q[b, h])
             dq[b, h] = scale * (ds @ k[b, kh])
             if return_intermediates:
                 delta_all[b, h] = delta
                 ds_all[b, h] = ds
+    out = (dq, dk, dv) + ((dbias,) if return_dbias else ())
     if return_intermediates:
-        return dq, dk, dv, delta_all, ds_all
-    return dq, dk, dv
+        return out + (delta_all, ds_all)
+    return out
 
 
 def dsink(o, do, lse, sink, seq_q_lens=None):

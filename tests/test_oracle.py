@@ -13,7 +13,10 @@
 * the row-sampled functions equal the full backward;
 * mutation checks: deliberately broken backwards (planted here, on the CPU) fail the same checks;
 * sink tokens: finite differences in the sink logits and in Q, K, V with the sink folded into the
-  forward, a one-key closed form, the -inf limit (no sink) and the row sums of dS.
+  forward, a one-key closed form, the -inf limit (no sink) and the row sums of dS;
+* additive bias: finite differences in every bias element (per-batch and batch-1 biases, whose
+  gradient sums over the batch) and in Q, K, V, row-shift invariance, a causal mask written as a
+  bias, zero bias = no bias, and planted dBias mistakes.
 """
 import math
 import os
@@ -476,3 +479,113 @@ def test_planted_dsink_mistakes_are_caught(kind):
         fd.append((np.sum(do * oracle.forward(q, k, v, scale, sink=sp, **kw)[0]) -
                    np.sum(do * oracle.forward(q, k, v, scale, sink=sm, **kw)[0])) / (2 * h))
     assert np.max(np.abs(np.asarray(got) - np.asarray(fd))) > 1e-3
+
+
+# ----------------------------------------------------------------------------------------------
+# additive bias ("SDPA Backward (SM120)", "API Usage" bias_tensor and "Support surface" bias):
+# finite differences in every bias element (per-batch and batch-1 biases) and in Q, K, V with the
+# bias in the forward, row-shift invariance, a mask written as a bias, and zero bias = no bias
+BIAS_MASKS = [dict(causal=False, W=-1), dict(causal=True, W=-1), dict(causal=True, W=1, lens=[4])]
+
+
+def _bias_problem(seed, mask, B=2, Hq=2, Hkv=1, S=5, D=4, bias_batch=None):
+    q, k, v, do, _, _, scale, kw = _problem(seed, B=B, Hq=Hq, Hkv=Hkv, Sq=S, Skv=S, Dqk=D, Dv=D,
+                                            **dict(mask, lens=None if mask.get("lens") is None
+                                                   else mask["lens"] * B))
+    bias = np.random.default_rng(seed + 200).standard_normal((bias_batch or B, Hq, S, S))
+    o, lse = oracle.forward(q, k, v, scale, bias=bias, **kw)
+    return q, k, v, do, o, lse, scale, kw, bias
+
+
+@pytest.mark.parametrize("bias_batch", [None, 1], ids=["per_batch", "batch1"])
+@pytest.mark.parametrize("mask", BIAS_MASKS, ids=str)
+def test_bias_finite_differences(mask, bias_batch):
+    q, k, v, do, o, lse, scale, kw, bias = _bias_problem(41, mask, bias_batch=bias_batch)
+    dq, dk, dv, dbias = oracle.backward(q, k, v, o, do, lse, scale, bias=bias, return_dbias=True,
+                                        **kw)
+    h = 1e-6
+
+    def loss():
+        return np.sum(do * oracle.forward(q, k, v, scale, bias=bias, **kw)[0])
+
+    for x, g in ((bias, dbias), (q, dq), (k, dk), (v, dv)):
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            mi = it.multi_index
+            old = x[mi]
+            x[mi] = old + h
+            lp = loss()
+            x[mi] = old - h
+            lm = loss()
+            x[mi] = old
+            fd[mi] = (lp - lm) / (2 * h)
+        assert np.max(np.abs(g - fd)) <= 1e-6 * max(1.0, np.max(np.abs(fd)))
+
+
+def test_bias_row_shift_invariance_and_row_sums():
+    q, k, v, do, o, lse, scale, kw, bias = _bias_problem(42, dict(causal=True, W=-1), B=1, S=6)
+    g1 = oracle.backward(q, k, v, o, do, lse, scale, bias=bias, return_dbias=True, **kw)
+    shifted = bias + np.random.default_rng(3).standard_normal((1, 2, 6, 1)) * 5.0
+    o2, lse2 = oracle.forward(q, k, v, scale, bias=shifted, **kw)
+    np.testing.assert_allclose(o2, o, atol=1e-13)
+    g2 = oracle.backward(q, k, v, o2, do, lse2, scale, bias=shifted, return_dbias=True, **kw)
+    for a, b in zip(g1, g2):
+        np.testing.assert_allclose(b, a, atol=1e-12)
+    # each row of dBias (= dS) sums to zero
+    np.testing.assert_allclose(g1[3].sum(axis=-1), 0.0, atol=1e-12)
+
+
+def test_causal_mask_as_bias():
+    # a causal mask written as a bias of -inf above the diagonal, in a non-causal call
+    q, k, v, do, o, lse, scale, kw = _problem(43, B=1, Hq=2, Hkv=1, Sq=6, Skv=6, causal=True)
+    mask_bias = np.where(np.tril(np.ones((6, 6), dtype=bool)), 0.0, -np.inf)[None, None]
+    mask_bias = np.repeat(mask_bias, 2, axis=1)
+    o2, lse2 = oracle.forward(q, k, v, scale, bias=mask_bias)
+    np.testing.assert_allclose(o2, o, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse, atol=1e-14)
+    ref = oracle.backward(q, k, v, o, do, lse, scale, return_intermediates=True, **kw)
+    got = oracle.backward(q, k, v, o2, do, lse2, scale, bias=mask_bias, return_dbias=True)
+    for a, b in zip(ref[:3], got[:3]):
+        np.testing.assert_allclose(b, a, atol=1e-13)
+    np.testing.assert_allclose(got[3], ref[4], atol=1e-13)   # dBias = dS of the causal call
+
+
+def test_zero_bias_is_no_bias():
+    q, k, v, do, o, lse, scale, kw = _problem(44, B=2, Hq=2, Hkv=2, Sq=5, Skv=7, causal=True, W=2)
+    zb = np.zeros((1, 2, 5, 7))
+    o2, lse2 = oracle.forward(q, k, v, scale, bias=zb, **kw)
+    np.testing.assert_array_equal(o2, o)
+    np.testing.assert_array_equal(lse2, lse)
+    a = oracle.backward(q, k, v, o, do, lse, scale, **kw)
+    b = oracle.backward(q, k, v, o, do, lse, scale, bias=zb, return_dbias=True, **kw)
+    for x, y in zip(a, b[:3]):
+        np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("kind", ["scaled", "no_batch_sum", "sign"])
+def test_planted_dbias_mistakes_are_caught(kind):
+    q, k, v, do, o, lse, scale, kw, bias = _bias_problem(45, dict(causal=True, W=-1), B=2, S=4,
+                                                         bias_batch=1)
+    dbias = oracle.backward(q, k, v, o, do, lse, scale, bias=bias, return_dbias=True, **kw)[3]
+    if kind == "scaled":                 # dBias = scale * dS (scale applied like dK's)
+        dbias = scale * dbias
+    elif kind == "no_batch_sum":         # batch-1 bias given only batch entry 0's dS
+        d0 = oracle.backward(q[:1], k[:1], v[:1], o[:1], do[:1], lse[:1], scale, bias=bias,
+                             return_dbias=True, **kw)[3]
+        dbias = d0
+    else:
+        dbias = -dbias
+    h = 1e-6
+    fd = np.zeros_like(bias)
+    it = np.nditer(bias, flags=["multi_index"])
+    for _ in it:
+        mi = it.multi_index
+        old = bias[mi]
+        bias[mi] = old + h
+        lp = np.sum(do * oracle.forward(q, k, v, scale, bias=bias, **kw)[0])
+        bias[mi] = old - h
+        lm = np.sum(do * oracle.forward(q, k, v, scale, bias=bias, **kw)[0])
+        bias[mi] = old
+        fd[mi] = (lp - lm) / (2 * h)
+    assert np.max(np.abs(dbias - fd)) > 1e-3
