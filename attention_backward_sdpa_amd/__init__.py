@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsdpa_bwd.so")
 
 OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, LAUNCH_FAILED = 0, 1, 2, 3, 4
-BF16, FP16 = 0, 1
+BF16, FP16, FP32 = 0, 1, 2
 # values of the `deterministic` argument (dQ routes); False / True are 0 / 1
 DQ_ATOMIC, DQ_DETERMINISTIC, DQ_DS_PANELS, DQ_PARTIALS = 0, 1, 2, 3
 
@@ -33,7 +33,8 @@ class Args(ctypes.Structure):
                                      "window_right", "deterministic")] + \
         [("seq_q_lens", ctypes.c_void_p), ("seq_kv_lens", ctypes.c_void_p),
          ("layouts", ctypes.c_void_p), ("dtype", ctypes.c_int), ("sink", ctypes.c_void_p),
-         ("dsink", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+         ("dsink", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("bias_dtype", ctypes.c_int),
+         ("bias_batch", ctypes.c_int), ("dbias", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
          ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
          ("events", ctypes.c_void_p)]
 
@@ -72,6 +73,8 @@ def _load():
     lib.sdpa_bwd_preprocess.restype = i
     lib.sdpa_bwd_run.argtypes = [ctypes.POINTER(Args)]
     lib.sdpa_bwd_run.restype = i
+    lib.sdpa_bwd_run_workspace_size.argtypes = [ctypes.POINTER(Args)]
+    lib.sdpa_bwd_run_workspace_size.restype = sz
     lib.sdpa_bwd_dq_route.argtypes = [i, i, i]
     lib.sdpa_bwd_dq_route.restype = i
     lib.sdpa_bwd_status_string.argtypes = [i]
@@ -184,13 +187,18 @@ def sdpa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, windo
         _check(lib.sdpa_bwd_flex(*head, _layouts(tensors), _io_dtype(q), *tail, handles))
 
 
-def sdpa_bwd_run(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, window_left=-1,
-                 deterministic=False, seq_q_lens=None, seq_kv_lens=None,
-                 causal_bottom_right=False, window_right=0, sink=None, dsink=None,
-                 workspace=None, stream=None, events=None):
-    """sdpa_bwd_run(): the superset entry point (any dense layout with a contiguous head dim,
-    bf16 or fp16, and the sink gradient: dsink (Hq,) fp32 is written when given, from the sink
-    (Hq,) fp32 logits)."""
+def _bias_dtype(bias, q):
+    import torch
+    if bias is None:
+        return _io_dtype(q)
+    return FP32 if bias.dtype == torch.float32 else FP16 if bias.dtype == torch.float16 else BF16
+
+
+def run_args(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, window_left=-1,
+             deterministic=False, seq_q_lens=None, seq_kv_lens=None, causal_bottom_right=False,
+             window_right=0, sink=None, dsink=None, bias=None, dbias=None, workspace=None,
+             stream=None, events=None):
+    """The sdpa_bwd_args struct of one call (tensors marshalled to device pointers)."""
     B, Hq, Hkv, Sq, Skv, Dqk, Dv = _dims(q, k, v)
     tensors = (q, k, v, o, do, dq, dk, dv)
     lay = _layouts(tensors)
@@ -211,8 +219,35 @@ def sdpa_bwd_run(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, wind
     a.layouts = ctypes.cast(lay, ctypes.c_void_p).value
     a.dtype = _io_dtype(q)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    a.stream = _stream_handle(stream).value
+    a.stream = None if stream is False else _stream_handle(stream).value
     a.events = None if handles is None else ctypes.cast(handles, ctypes.c_void_p).value
+    a.bias = None if bias is None else bias.data_ptr()
+    a.bias_dtype = _bias_dtype(bias, q)
+    a.bias_batch = 1 if bias is None else int(bias.shape[0])
+    a.dbias = None if dbias is None else dbias.data_ptr()
+    # keep the pointed-to ctypes arrays alive with the struct
+    a._keep = (lay, handles)
+    return a
+
+
+def run_workspace_size(q, k, v, **kw) -> int:
+    """sdpa_bwd_run_workspace_size() for a call on these q, k, v and keyword arguments (the other
+    tensors' pointers, the workspace and the stream are not read)."""
+    a = run_args(q, k, v, q, q, None, q, k, v, stream=False, **kw)
+    return int(_load().sdpa_bwd_run_workspace_size(ctypes.byref(a)))
+
+
+def sdpa_bwd_run(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, window_left=-1,
+                 deterministic=False, seq_q_lens=None, seq_kv_lens=None,
+                 causal_bottom_right=False, window_right=0, sink=None, dsink=None, bias=None,
+                 dbias=None, workspace=None, stream=None, events=None):
+    """sdpa_bwd_run(): the superset entry point (any dense layout with a contiguous head dim,
+    bf16 or fp16; the sink gradient: dsink (Hq,) fp32 is written when given, from the sink
+    (Hq,) fp32 logits; an additive bias (1 or B, Hq, Sq, Skv) of the io type or fp32, with its
+    fp32 gradient dbias when given).  `workspace` must hold run_workspace_size(...) bytes."""
+    a = run_args(q, k, v, o, do, lse, dq, dk, dv, scale, causal, window_left, deterministic,
+                 seq_q_lens, seq_kv_lens, causal_bottom_right, window_right, sink, dsink, bias,
+                 dbias, workspace, stream, events)
     _check(_load().sdpa_bwd_run(ctypes.byref(a)))
 
 

@@ -72,6 +72,12 @@ struct MainParams {
   int sq_pad, skv_pad;      // statistics / dS workspace extents
   float scale;              // softmax scale
   float scale_log2;         // scale * log2(e)
+  // additive bias ("API Usage" bias_tensor): (Bb, Hq, Sq, Skv) contiguous, Bb = 1 or B
+  const void* bias;         // io-type or fp32 elements
+  float* dbias;             // (Bb, Hq, Sq, Skv) fp32 dBias = dS, or null
+  int64_t bias_bstride;     // elements between batch entries of bias / dbias (0 for Bb = 1)
+  int bias_f32;             // bias elements are fp32 (else the io type)
+  int dbias_atomic;         // dBias accumulates over batch entries (Bb = 1, B > 1): fp32 atomics
 };
 
 // How the main kernel emits dQ.
@@ -81,10 +87,12 @@ enum DqMode {
   DQ_PARTIAL = 2,  // GEMM4 in the kernel, fp32 partial tiles to the workspace (dq_reduce sums)
 };
 
-template <int DQK_, int DV_, int KPW_, int NW_, int MODE_, bool F16_ = false>
+template <int DQK_, int DV_, int KPW_, int NW_, int MODE_, bool F16_ = false, int BIAS_ = 0>
 struct MainCfg {
   static constexpr int DQK = DQK_, DV = DV_, KPW = KPW_, NW = NW_;
   static constexpr int MODE = MODE_;
+  // 0: no bias; 1: additive bias in the replayed scores; 2: bias and its gradient dBias = dS
+  static constexpr int BIAS = BIAS_;
   static constexpr bool DS_OUT = MODE == DQ_DS;  // dS leaves the kernel, GEMM4 does not run here
   static constexpr bool G4 = !DS_OUT;            // GEMM4 runs here (dS staged in LDS)
   static constexpr bool F16 = F16_;  // fp16 io (and fp16 P / dS operands) instead of bf16
@@ -296,10 +304,11 @@ struct KeyRows {
 // P = exp2(S * scale * log2e - LSE * log2e), dS = P * (dP - delta); both are packed to io-type
 // pairs in accumulator order (pb/sb[v/2] holds registers v, v+1).  No masking here: on edge tiles
 // mask_pairs clears the invisible pairs afterwards.
-template <bool F16, int X0>
+template <bool F16, int X0, int BIAS = 0>
 __device__ __forceinline__ void softmax_ds(const floatx16& S, const floatx16& dP,
                                            const float* sStat, int g, float scale_log2,
-                                           uint32_t (&pb)[8], uint32_t (&sb)[8]) {
+                                           uint32_t (&pb)[8], uint32_t (&sb)[8],
+                                           const float* bl = nullptr, float* dsf = nullptr) {
 #pragma unroll
   for (int x = X0; x < X0 + 2; ++x) {
     // rows of accumulator registers 4x..4x+3 of this lane: g*4 + 8x + 0..3
@@ -310,8 +319,11 @@ __device__ __forceinline__ void softmax_ds(const floatx16& S, const floatx16& dP
     float pv[4], dv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * x + e], scale_log2, -l4[e]));
+      // with a bias: exponent + bias * log2(e) (bl holds the lane's bias * log2 e per register)
+      const float off = BIAS ? bl[4 * x + e] - l4[e] : -l4[e];
+      pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * x + e], scale_log2, off));
       dv[e] = pv[e] * (dP[4 * x + e] - d4[e]);
+      if constexpr (BIAS == 2) dsf[4 * x + e] = dv[e];
     }
     pb[2 * x] = Elem<F16>::pack2(pv[0], pv[1]);
     pb[2 * x + 1] = Elem<F16>::pack2(pv[2], pv[3]);
@@ -629,6 +641,46 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
             reinterpret_cast<u32x4*>(wsb + w * 2048 + h * 1024 + lane * 16));
     };
 
+    // Additive bias: the lane's 16 bias values of a q tile (accumulator rows, its key), times
+    // log2(e), loaded one q tile ahead; they are complete at the next tile's memory wait.
+    // dBias: the previous tile's masked fp32 dS, stored (or, for a batch-1 bias summed over the
+    // batch, added with fp32 atomics) after the next tile's loads are issued.
+    constexpr int NBV = C::BIAS ? 16 : 1;
+    float bcur[NBV], bnext[NBV], dsf[C::BIAS == 2 ? 16 : 1];
+    const int64_t bias_bh = (int64_t)b * p.bias_bstride + (int64_t)h * p.Sq * p.Skv;
+    const int bias_key = min(key_lane, p.Skv - 1);
+    auto load_bias = [&](int i_t, float (&dst)[NBV]) {
+      if constexpr (C::BIAS) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = min(i_t * BR + acc_row<32>(r, g), p.Sq - 1);
+          const int64_t x = bias_bh + (int64_t)row * p.Skv + bias_key;
+          const float bv = p.bias_f32 ? reinterpret_cast<const float*>(p.bias)[x]
+                                      : Elem<C::F16>::lo(reinterpret_cast<const bf16_t*>(p.bias)[x]);
+          dst[r] = bv * kLog2e;
+        }
+      }
+    };
+    auto store_dbias = [&](int i_t) {
+      if constexpr (C::BIAS == 2) {
+        if (key_lane < p.Skv) {
+          float* base = p.dbias + bias_bh + key_lane;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = i_t * BR + acc_row<32>(r, g);
+            if (row < p.Sq) {
+              if (p.dbias_atomic)
+                __hip_atomic_fetch_add(base + (int64_t)row * p.Skv, dsf[r], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+              else
+                base[(int64_t)row * p.Skv] = dsf[r];
+            }
+          }
+        }
+      }
+    };
+    load_bias(i_hi, bcur);
+
     for (int i = i_hi; i >= i_lo; --i) {
       const int q0 = i * BR;
       const char* T = tile(i);
@@ -638,6 +690,10 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
       if (C::NBUF == 2 && i > i_lo) load_tile(i - 1);
       if constexpr (C::DS_OUT) {
         if (i < i_hi) store_ds(i + 1);
+      }
+      if constexpr (C::BIAS) {
+        if (i < i_hi) store_dbias(i + 1);
+        if (i > i_lo) load_bias(i - 1, bnext);
       }
 
       if constexpr (C::G4) {
@@ -696,12 +752,22 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
       // Softmax replay of all 32 rows, unmasked and branch-free; edge tiles then clear their
       // invisible pairs in the packed words (keeping the masking out of the block the MFMA
       // accumulators flow through avoids register copies at the join).
-      softmax_ds<C::F16, 0>(S, dP, sStat, g, p.scale_log2, pb, sb);
-      softmax_ds<C::F16, 2>(S, dP, sStat, g, p.scale_log2, pb, sb);
+      softmax_ds<C::F16, 0, C::BIAS>(S, dP, sStat, g, p.scale_log2, pb, sb, bcur, dsf);
+      softmax_ds<C::F16, 2, C::BIAS>(S, dP, sStat, g, p.scale_log2, pb, sb, bcur, dsf);
       if (edge) {
         const uint32_t vis_m = visible_rows(KeyRows(mg, q0 + g * 4, key_lane));
         mask_pairs<0>(vis_m, pb, sb);
         mask_pairs<2>(vis_m, pb, sb);
+        if constexpr (C::BIAS == 2) {
+          // register 4x + e holds row offset 8x + e from the lane's first row
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!((vis_m >> (8 * (r / 4) + (r % 4))) & 1u)) dsf[r] = 0.f;
+        }
+      }
+      if constexpr (C::BIAS) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bcur[r] = bnext[r];
       }
       if constexpr (C::DS_OUT) {
 #pragma unroll
@@ -726,6 +792,7 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
       }
     }
     if constexpr (C::DS_OUT) store_ds(i_lo);
+    store_dbias(i_lo);
     if constexpr (C::G4) {
       lds_barrier();  // the last tile's dS is complete
       if constexpr (C::G4_16)

@@ -32,14 +32,25 @@ struct Geometry {
   int nw, kpw, bc, br;
 };
 
-bool geometry_for(int Dqk, int Dv, Geometry* g) {
+// With an additive bias every head dim runs the 4-wave layout (512 registers per wave): the
+// bias values of the next q tile are held in registers while the current one computes.
+bool geometry_for(int Dqk, int Dv, Geometry* g, bool bias = false) {
   if (Dqk == 64 && Dv == 64) *g = {8, 32, 256, 32};
   else if (Dqk == 128 && Dv == 128) *g = {8, 32, 256, 32};
   else if (Dqk == 192 && Dv == 128) *g = {8, 32, 256, 32};
   else if (Dqk == 256 && Dv == 256) *g = {4, 32, 128, 32};
   else return false;
+  if (bias) *g = {4, 32, 128, 32};
   return true;
 }
+
+// The additive bias of one call ("API Usage" bias_tensor): (bias_batch, Hq, Sq, Skv) contiguous.
+struct BiasArgs {
+  const void* bias = nullptr;
+  float* dbias = nullptr;
+  int dtype = SDPA_BWD_BF16;  // SDPA_BWD_BF16 / SDPA_BWD_FP16 (the io type) or SDPA_BWD_FP32
+  int batch = 1;              // 1 or B
+};
 
 // Number of parts the q-tile range of every key tile is split into (each part a workgroup of its
 // own, writing dK/dV partials that the reduction sums in a fixed order).  A grid of fewer than
@@ -143,11 +154,12 @@ int check_layouts(const Layouts& L, int Sq, int Skv, int Dqk, int Dv) {
 
 int validate(const void* q, const void* k, const void* v, const void* o, const void* dO,
              const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
-             int Skv, int Dqk, int Dv, int window_left, int window_right, Geometry* geo) {
+             int Skv, int Dqk, int Dv, int window_left, int window_right, Geometry* geo,
+             bool bias = false) {
   if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0) return SDPA_BWD_INVALID_ARG;
   if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return SDPA_BWD_INVALID_ARG;
   if (window_left < -1 || window_right < 0) return SDPA_BWD_INVALID_ARG;
-  if (!geometry_for(Dqk, Dv, geo)) return SDPA_BWD_UNSUPPORTED;
+  if (!geometry_for(Dqk, Dv, geo, bias)) return SDPA_BWD_UNSUPPORTED;
   // the kernels address one head's rows (and its padded tiles) through 32-bit buffer offsets
   const int64_t s_max = (Sq > Skv ? Sq : Skv) + geo->bc;
   if (s_max * (Dqk > Dv ? Dqk : Dv) * 2 >= ((int64_t)1 << 31)) return SDPA_BWD_UNSUPPORTED;
@@ -187,33 +199,54 @@ hipError_t launch_dq2k(const Dq2kParams& dp, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DQK, int DV, int KPW, int NW, bool F16>
+template <int DQK, int DV, int KPW, int NW, bool F16, int BIAS>
 hipError_t dispatch_main_t(const MainParams& mp, Route route, int grid, int bc, hipStream_t s) {
   // the workspace carve and the grid use the geometry table; the kernel must tile the same way
   if (MainCfg<DQK, DV, KPW, NW, DQ_ATOMIC>::BC != bc) return hipErrorInvalidValue;
-  if (route == R_DS) return launch_main<MainCfg<DQK, DV, KPW, NW, DQ_DS, F16>>(mp, grid, s);
-  if (route == R_DQP) return launch_main<MainCfg<DQK, DV, KPW, NW, DQ_PARTIAL, F16>>(mp, grid, s);
-  return launch_main<MainCfg<DQK, DV, KPW, NW, DQ_ATOMIC, F16>>(mp, grid, s);
+  if (route == R_DS) return launch_main<MainCfg<DQK, DV, KPW, NW, DQ_DS, F16, BIAS>>(mp, grid, s);
+  if (route == R_DQP)
+    return launch_main<MainCfg<DQK, DV, KPW, NW, DQ_PARTIAL, F16, BIAS>>(mp, grid, s);
+  return launch_main<MainCfg<DQK, DV, KPW, NW, DQ_ATOMIC, F16, BIAS>>(mp, grid, s);
 }
 
-template <int DQK, int DV, int KPW, int NW>
+template <int DQK, int DV, int KPW, int NW, int BIAS>
 hipError_t dispatch_main(const MainParams& mp, Route route, bool f16, int grid, int bc,
                          hipStream_t s) {
-  if (f16) return dispatch_main_t<DQK, DV, KPW, NW, true>(mp, route, grid, bc, s);
-  return dispatch_main_t<DQK, DV, KPW, NW, false>(mp, route, grid, bc, s);
+  if (f16) return dispatch_main_t<DQK, DV, KPW, NW, true, BIAS>(mp, route, grid, bc, s);
+  return dispatch_main_t<DQK, DV, KPW, NW, false, BIAS>(mp, route, grid, bc, s);
 }
 
-hipError_t run_main(int Dqk, int Dv, const MainParams& mp, Route route, bool f16, int grid,
+// bias: 0 none, 1 bias, 2 bias and dBias (the 4-wave layout of geometry_for)
+template <int BIAS>
+hipError_t run_main_b(int Dqk, const MainParams& mp, Route route, bool f16, int grid, int bc,
+                      hipStream_t s) {
+  if constexpr (BIAS == 0) {
+    if (Dqk == 64) return dispatch_main<64, 64, 32, 8, 0>(mp, route, f16, grid, bc, s);
+    if (Dqk == 128) return dispatch_main<128, 128, 32, 8, 0>(mp, route, f16, grid, bc, s);
+    if (Dqk == 192) return dispatch_main<192, 128, 32, 8, 0>(mp, route, f16, grid, bc, s);
+  } else {
+    if (Dqk == 64) return dispatch_main<64, 64, 32, 4, BIAS>(mp, route, f16, grid, bc, s);
+    if (Dqk == 128) return dispatch_main<128, 128, 32, 4, BIAS>(mp, route, f16, grid, bc, s);
+    if (Dqk == 192) return dispatch_main<192, 128, 32, 4, BIAS>(mp, route, f16, grid, bc, s);
+  }
+  return dispatch_main<256, 256, 32, 4, BIAS>(mp, route, f16, grid, bc, s);
+}
+
+hipError_t run_main(int Dqk, const MainParams& mp, Route route, bool f16, int bias, int grid,
                     int bc, hipStream_t s) {
-  if (Dqk == 64) return dispatch_main<64, 64, 32, 8>(mp, route, f16, grid, bc, s);
-  if (Dqk == 128) return dispatch_main<128, 128, 32, 8>(mp, route, f16, grid, bc, s);
-  if (Dqk == 192) return dispatch_main<192, 128, 32, 8>(mp, route, f16, grid, bc, s);
-  return dispatch_main<256, 256, 32, 4>(mp, route, f16, grid, bc, s);
+  if (bias == 1) return run_main_b<1>(Dqk, mp, route, f16, grid, bc, s);
+  if (bias == 2) return run_main_b<2>(Dqk, mp, route, f16, grid, bc, s);
+  return run_main_b<0>(Dqk, mp, route, f16, grid, bc, s);
 }
 
-// the reduction reads the partial blocks in the layout of the main kernel that wrote them
+// the reduction reads the partial blocks in the layout of the main kernel that wrote them (the
+// 8- and 4-wave layouts of a head dim write the same one)
 template <int DQK, int DV, int NW>
 constexpr bool partial_l16() { return MainCfg<DQK, DV, 32, NW, DQ_PARTIAL>::G4_16; }
+static_assert(partial_l16<64, 64, 8>() == partial_l16<64, 64, 4>() &&
+                  partial_l16<128, 128, 8>() == partial_l16<128, 128, 4>() &&
+                  partial_l16<192, 128, 8>() == partial_l16<192, 128, 4>(),
+              "one partial-block layout per head dim");
 
 template <bool F16>
 hipError_t launch_dq_reduce_t(const DqReduceParams& rp, int Dqk, int grid, hipStream_t s) {
@@ -240,9 +273,16 @@ hipError_t dispatch_dq2k(const Dq2kParams& dp, int bc, hipStream_t s) {
 
 template <bool F16>
 hipError_t run_dq2k_t(int Dqk, const Dq2kParams& dp, int bc, hipStream_t s) {
-  if (Dqk == 64) return dispatch_dq2k<64, 256, F16>(dp, bc, s);
-  if (Dqk == 128) return dispatch_dq2k<128, 256, F16>(dp, bc, s);
-  if (Dqk == 192) return dispatch_dq2k<192, 256, F16>(dp, bc, s);
+  if (bc == 256) {
+    if (Dqk == 64) return dispatch_dq2k<64, 256, F16>(dp, bc, s);
+    if (Dqk == 128) return dispatch_dq2k<128, 256, F16>(dp, bc, s);
+    if (Dqk == 192) return dispatch_dq2k<192, 256, F16>(dp, bc, s);
+    return hipErrorInvalidValue;
+  }
+  // 128-key tiles: head dim 256, and every head dim under a bias
+  if (Dqk == 64) return dispatch_dq2k<64, 128, F16>(dp, bc, s);
+  if (Dqk == 128) return dispatch_dq2k<128, 128, F16>(dp, bc, s);
+  if (Dqk == 192) return dispatch_dq2k<192, 128, F16>(dp, bc, s);
   return dispatch_dq2k<256, 128, F16>(dp, bc, s);
 }
 
@@ -305,13 +345,21 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
         int Dqk, int Dv, float scale, int causal, int window_left, int deterministic,
         const int* seq_q_lens, const int* seq_kv_lens, int bottom_right, int window_right,
         const sdpa_bwd_layout* layouts, int dtype, const float* sink, float* dsink,
-        void* workspace, size_t workspace_bytes, bool check_ws, hipStream_t stream,
-        void* const* events) {
+        const BiasArgs& ba, void* workspace, size_t workspace_bytes, bool check_ws,
+        hipStream_t stream, void* const* events) {
   Geometry geo;
+  const bool has_bias = ba.bias != nullptr;
   int st = validate(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, window_left,
-                    window_right, &geo);
+                    window_right, &geo, has_bias);
   if (st != SDPA_BWD_OK) return st;
   if (dtype != SDPA_BWD_BF16 && dtype != SDPA_BWD_FP16) return SDPA_BWD_UNSUPPORTED;
+  if (ba.dbias && !has_bias) return SDPA_BWD_INVALID_ARG;
+  if (has_bias) {
+    if (ba.batch != 1 && ba.batch != B) return SDPA_BWD_INVALID_ARG;
+    if (ba.dtype != dtype && ba.dtype != SDPA_BWD_FP32) return SDPA_BWD_UNSUPPORTED;
+    if (((uintptr_t)ba.bias & (ba.dtype == SDPA_BWD_FP32 ? 3 : 1)) || ((uintptr_t)ba.dbias & 3))
+      return SDPA_BWD_UNSUPPORTED;
+  }
   if (dsink && (!sink || ((uintptr_t)sink & 3) || ((uintptr_t)dsink & 3))) return SDPA_BWD_INVALID_ARG;
   const bool f16 = dtype == SDPA_BWD_FP16;
   Layouts L = contiguous_layouts(Hq, Hkv, Sq, Skv, Dqk, Dv);
@@ -322,6 +370,10 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   if (st != SDPA_BWD_OK) return st;
   const Route route = route_for(deterministic, Dqk, geo);
   if (route == R_INVALID) return SDPA_BWD_INVALID_ARG;
+  // dBias of a batch-1 bias sums over the batch with fp32 atomics: not reproducible ("Support
+  // surface", bias), so the deterministic routes need a per-batch bias then
+  const bool dbias_atomic = ba.dbias && ba.batch == 1 && B > 1;
+  if (dbias_atomic && route != R_ATOMIC) return SDPA_BWD_UNSUPPORTED;
   // empty problems need no workspace (sdpa_bwd_workspace_size returns 0 for them)
   const bool empty = B == 0 || Sq == 0 || Skv == 0;
   const Carve c = empty ? Carve{} : carve(B, Hq, Hkv, Sq, Skv, Dqk, Dv, route, geo);
@@ -357,6 +409,13 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     if (e == hipSuccess) e = zero_rows(dk, L.t[T_DK], B, Hkv, Skv, Dqk, stream);
     if (e == hipSuccess) e = zero_rows(dv, L.t[T_DV], B, Hkv, Skv, Dv, stream);
     if (e == hipSuccess) e = launch_dsink(nullptr, 0, true);
+    if (e == hipSuccess && ba.dbias && (int64_t)ba.batch * Sq * Skv > 0) {
+      // nothing attends: dBias is zero
+      DbiasFillParams fp{ba.dbias, nullptr, nullptr, Hq, Sq, Skv, geo.bc, geo.br, 0, -1, 0, 0, 1};
+      hipLaunchKernelGGL(dbias_fill_kernel, dim3((unsigned)((int64_t)ba.batch * Hq * ((Sq + 31) / 32))),
+                         dim3(256), 0, stream, fp);
+      e = hipGetLastError();
+    }
     for (int n = 1; n < 5; ++n) rec(n);
     return e == hipSuccess ? SDPA_BWD_OK : SDPA_BWD_LAUNCH_FAILED;
   }
@@ -383,6 +442,27 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   pp.zero_rows = route == R_ATOMIC ? 1 : 0;
   e = launch_preprocess(pp, Dv, f16, (int64_t)B * Hq * (c.sq_pad / geo.br), stream);
   if (e == hipSuccess) e = launch_dsink(stats, (int)c.sq_pad, false);
+  if (e == hipSuccess && ba.dbias) {
+    // zero the dBias blocks the main kernel does not write (all of them when it accumulates)
+    DbiasFillParams fp;
+    fp.dbias = ba.dbias;
+    fp.seq_q_lens = seq_q_lens;
+    fp.seq_kv_lens = seq_kv_lens;
+    fp.Hq = Hq;
+    fp.Sq = Sq;
+    fp.Skv = Skv;
+    fp.bc = geo.bc;
+    fp.br = geo.br;
+    fp.causal = causal ? 1 : 0;
+    fp.window_left = window_left;
+    fp.window_right = causal ? window_right : 0;
+    fp.bottom_right = bottom_right ? 1 : 0;
+    fp.all = dbias_atomic ? 1 : 0;
+    const int64_t fgrid = (int64_t)ba.batch * Hq * ((Sq + geo.br - 1) / geo.br);
+    if (fgrid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
+    hipLaunchKernelGGL(dbias_fill_kernel, dim3((unsigned)fgrid), dim3(256), 0, stream, fp);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   rec(1);
 
@@ -422,9 +502,15 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   mp.skv_pad = (int)c.skv_pad;
   mp.scale = scale;
   mp.scale_log2 = scale * kLog2e;
+  mp.bias = ba.bias;
+  mp.dbias = ba.dbias;
+  mp.bias_bstride = ba.batch == 1 ? 0 : (int64_t)Hq * Sq * Skv;
+  mp.bias_f32 = ba.dtype == SDPA_BWD_FP32 ? 1 : 0;
+  mp.dbias_atomic = dbias_atomic ? 1 : 0;
   const int64_t main_grid = (int64_t)mp.n_kv_tiles * split * B * Hq;
   if (main_grid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
-  e = run_main(Dqk, Dv, mp, route, f16, (int)main_grid, geo.bc, stream);
+  e = run_main(Dqk, mp, route, f16, has_bias ? (ba.dbias ? 2 : 1) : 0, (int)main_grid, geo.bc,
+               stream);
   if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   rec(2);
 
@@ -554,7 +640,7 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int deterministic, void* workspace, void* stream) {
   return run(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, scale, causal,
              window_left, deterministic, nullptr, nullptr, 0, 0, nullptr, SDPA_BWD_BF16, nullptr,
-             nullptr, workspace, 0, false, (hipStream_t)stream, nullptr);
+             nullptr, BiasArgs{}, workspace, 0, false, (hipStream_t)stream, nullptr);
 }
 
 int sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -565,8 +651,8 @@ int sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
                 size_t workspace_bytes, void* stream) {
   return run(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, scale, causal,
              window_left, deterministic, seq_q_lens, seq_kv_lens, causal_bottom_right,
-             window_right, nullptr, SDPA_BWD_BF16, nullptr, nullptr, workspace, workspace_bytes,
-             true, (hipStream_t)stream, nullptr);
+             window_right, nullptr, SDPA_BWD_BF16, nullptr, nullptr, BiasArgs{}, workspace,
+             workspace_bytes, true, (hipStream_t)stream, nullptr);
 }
 
 int sdpa_bwd_ex_events(const void* q, const void* k, const void* v, const void* o,
@@ -578,8 +664,8 @@ int sdpa_bwd_ex_events(const void* q, const void* k, const void* v, const void* 
                        void* const* events) {
   return run(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, scale, causal,
              window_left, deterministic, seq_q_lens, seq_kv_lens, causal_bottom_right,
-             window_right, nullptr, SDPA_BWD_BF16, nullptr, nullptr, workspace, workspace_bytes,
-             true, (hipStream_t)stream, events);
+             window_right, nullptr, SDPA_BWD_BF16, nullptr, nullptr, BiasArgs{}, workspace,
+             workspace_bytes, true, (hipStream_t)stream, events);
 }
 
 int sdpa_bwd_flex(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -591,17 +677,34 @@ int sdpa_bwd_flex(const void* q, const void* k, const void* v, const void* o, co
                   void* const* events) {
   return run(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, scale, causal,
              window_left, deterministic, seq_q_lens, seq_kv_lens, causal_bottom_right,
-             window_right, layouts, dtype, nullptr, nullptr, workspace, workspace_bytes, true,
-             (hipStream_t)stream, events);
+             window_right, layouts, dtype, nullptr, nullptr, BiasArgs{}, workspace, workspace_bytes,
+             true, (hipStream_t)stream, events);
 }
 
 int sdpa_bwd_run(const sdpa_bwd_args* a) {
   if (!a) return SDPA_BWD_INVALID_ARG;
+  BiasArgs ba;
+  ba.bias = a->bias;
+  ba.dbias = a->dbias;
+  ba.dtype = a->bias_dtype;
+  ba.batch = a->bias_batch;
   return run(a->q, a->k, a->v, a->o, a->dO, a->lse, a->dq, a->dk, a->dv, a->B, a->Hq, a->Hkv,
              a->Sq, a->Skv, a->Dqk, a->Dv, a->scale, a->causal, a->window_left, a->deterministic,
              a->seq_q_lens, a->seq_kv_lens, a->causal_bottom_right, a->window_right, a->layouts,
-             a->dtype, a->sink, a->dsink, a->workspace, a->workspace_bytes, true,
+             a->dtype, a->sink, a->dsink, ba, a->workspace, a->workspace_bytes, true,
              (hipStream_t)a->stream, a->events);
+}
+
+size_t sdpa_bwd_run_workspace_size(const sdpa_bwd_args* a) {
+  if (!a) return 0;
+  Geometry geo;
+  if (a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Sq < 0 || a->Skv < 0 || a->Hq % a->Hkv != 0)
+    return 0;
+  if (!geometry_for(a->Dqk, a->Dv, &geo, a->bias != nullptr)) return 0;
+  if (a->B == 0 || a->Sq == 0 || a->Skv == 0) return 0;
+  const Route route = route_for(a->deterministic, a->Dqk, geo);
+  if (route == R_INVALID) return 0;
+  return (size_t)carve(a->B, a->Hq, a->Hkv, a->Sq, a->Skv, a->Dqk, a->Dv, route, geo).total;
 }
 
 int sdpa_bwd_preprocess(const void* o, const void* dO, const float* lse, float* stats,

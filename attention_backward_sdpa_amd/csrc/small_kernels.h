@@ -4,6 +4,7 @@
 // fixed-order GQA dK/dV group reduction ("GQA/MQA group reduction") and the sink-gradient reduce.
 #pragma once
 #include "common.h"
+#include "masks.h"
 
 namespace sdpa {
 
@@ -197,6 +198,48 @@ __global__ void __launch_bounds__(256) dsink_kernel(DsinkParams p) {
     __syncthreads();
   }
   if (tid == 0) p.dsink[h] = (float)(0.0 - part[0]);
+}
+
+// ---- dBias fill -----------------------------------------------------------------------------------
+// dBias (Bb, Hq, Sq, Skv) fp32: the main kernel writes every element of the (q tile, key tile)
+// blocks it visits (masked pairs as 0); this kernel zeroes the elements of every other block, or
+// of every block when the main kernel accumulates dBias over the batch with atomics.  One
+// workgroup per (bias batch entry, query head, q tile); threads stride over the columns of the
+// tile's rows, a column's key tile deciding whether it is written here.
+struct DbiasFillParams {
+  float* dbias;
+  const int* seq_q_lens;
+  const int* seq_kv_lens;
+  int Hq, Sq, Skv;
+  int bc, br;               // key tile and q tile of the main kernel
+  int causal, window_left, window_right, bottom_right;
+  int all;                  // zero every element
+};
+
+__global__ void __launch_bounds__(256) dbias_fill_kernel(DbiasFillParams p) {
+  const int nqt = (p.Sq + p.br - 1) / p.br;
+  const int64_t bh = blockIdx.x / nqt;
+  const int i = (int)(blockIdx.x % nqt);
+  const int b = (int)(bh / p.Hq);  // the bias batch entry is the batch entry when Bb = B
+  MaskGeom mg;
+  mg.Lq = p.seq_q_lens ? min(max(p.seq_q_lens[b], 0), p.Sq) : p.Sq;
+  mg.Lkv = p.seq_kv_lens ? min(max(p.seq_kv_lens[b], 0), p.Skv) : p.Skv;
+  mg.diag = p.bottom_right ? mg.Lkv - mg.Lq : 0;
+  mg.causal = p.causal;
+  mg.W = p.window_left;
+  mg.R = p.window_right;
+  float* base = p.dbias + (bh * p.Sq + (int64_t)i * p.br) * p.Skv;
+  const int rows = min(p.br, p.Sq - i * p.br);
+  for (int c = threadIdx.x; c < p.Skv; c += 256) {
+    bool visited = false;
+    if (!p.all) {
+      int lo, hi;
+      q_tile_range(mg, (c / p.bc) * p.bc, p.bc, p.br, &lo, &hi);
+      visited = lo <= i && i <= hi;
+    }
+    if (!visited)
+      for (int r = 0; r < rows; ++r) base[(int64_t)r * p.Skv + c] = 0.f;
+  }
 }
 
 // ---- strided zero fill (gradients of shapes where nothing attends) ------------------------------

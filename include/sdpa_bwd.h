@@ -127,8 +127,8 @@ int sdpa_bwd_ex_events(const void* q, const void* k, const void* v, const void* 
                        int window_right, void* workspace, size_t workspace_bytes, void* stream,
                        void* const* events);
 
-/* io element types of sdpa_bwd_flex */
-enum { SDPA_BWD_BF16 = 0, SDPA_BWD_FP16 = 1 };
+/* element types: the io type of sdpa_bwd_flex (BF16, FP16); a bias may also be FP32 */
+enum { SDPA_BWD_BF16 = 0, SDPA_BWD_FP16 = 1, SDPA_BWD_FP32 = 2 };
 
 /* Strides, in elements, of one logical (B, H, S, D) tensor whose head dim is contiguous (stride 1):
  * "dense_flex" layouts ("SDPA Backward (SM120)", section "API Usage": any dense layout with the
@@ -171,7 +171,23 @@ int sdpa_bwd_flex(const void* q, const void* k, const void* v, const void* o, co
  *          finite of exp(sink[h] - lse[b,h,q]) * rowsum(O * dO)[b,h,q], summed in a fixed order
  *          (bitwise reproducible on every dQ route).  Overwritten, not accumulated into; 0 when
  *          B or Sq is 0.  A non-NULL dsink with a NULL sink gives SDPA_BWD_INVALID_ARG.
- * The dsink kernel runs right after the preprocess (inside the first event interval). */
+ * The dsink kernel runs right after the preprocess (inside the first event interval).
+ * And the additive bias ("API Usage" bias_tensor, "Support surface" bias):
+ *   bias        (bias_batch, Hq, Sq, Skv) contiguous device array added to the scores after the
+ *               softmax scale and before the softmax (the forward's LSE must include it), or
+ *               NULL; elements of the io type (bias_dtype = dtype, 2-byte aligned) or fp32
+ *               (bias_dtype = SDPA_BWD_FP32, 4-byte aligned); another bias_dtype gives
+ *               SDPA_BWD_UNSUPPORTED.
+ *   bias_batch  1 (one bias shared by every batch entry) or B; another value gives
+ *               SDPA_BWD_INVALID_ARG.
+ *   dbias       (bias_batch, Hq, Sq, Skv) fp32 device output, 4-byte aligned, or NULL (needs bias,
+ *               else SDPA_BWD_INVALID_ARG): dBias = dS, the unscaled softmax VJP, 0 on masked
+ *               pairs and padded rows/keys; every element is overwritten.  With bias_batch = 1 and
+ *               B > 1 it sums over the batch entries through fp32 atomics, so it is not bitwise
+ *               reproducible, and the deterministic dQ routes then give SDPA_BWD_UNSUPPORTED
+ *               (use a per-batch bias).  Otherwise each element is written once (reproducible).
+ * With a bias every head dim runs 128-key tiles, so the workspace can differ from the one
+ * sdpa_bwd_workspace_size reports: size it with sdpa_bwd_run_workspace_size. */
 typedef struct sdpa_bwd_args {
   const void* q;
   const void* k;
@@ -192,6 +208,10 @@ typedef struct sdpa_bwd_args {
   int dtype;
   const float* sink;
   float* dsink;
+  const void* bias;
+  int bias_dtype;
+  int bias_batch;
+  float* dbias;
   void* workspace;
   size_t workspace_bytes;
   void* stream;
@@ -202,6 +222,10 @@ typedef struct sdpa_bwd_args {
  * validation, workspace (sdpa_bwd_workspace_size; dsink needs none), stream and status rules;
  * args NULL gives SDPA_BWD_INVALID_ARG. */
 int sdpa_bwd_run(const sdpa_bwd_args* args);
+
+/* Bytes of workspace sdpa_bwd_run needs for these arguments (the workspace, workspace_bytes,
+ * stream and events fields are not read); 0 for arguments it rejects and for empty problems. */
+size_t sdpa_bwd_run_workspace_size(const sdpa_bwd_args* args);
 
 /* Step 1 of the chain alone ("The kernel chain", dot), as the chain runs it: for every query row
  * (rows padded to Sq_pad = Sq rounded up to 32 per (b, h)) write the pair

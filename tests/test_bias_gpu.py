@@ -1,0 +1,135 @@
+"""GPU parity of the additive bias and its gradient ("SDPA Backward (SM120)", "API Usage"
+bias_tensor, "Support surface" bias) through sdpa_bwd_run, against the fp64 oracle.
+
+The bias (1 or B, Hq, Sq, Skv) is drawn N(0,1), rounded to the io type (or kept fp32); the oracle
+forward folds it into O and LSE, and the GPU chain receives exactly those tensors.  dQ/dK/dV and
+dBias must match the oracle to max|err| <= 1e-2 * max|ref| per tensor, on every dQ route; dBias
+elements of masked pairs, padded rows and padded keys are exactly 0; a batch-1 bias with B > 1
+sums dBias over the batch (fp32 atomics, the atomic route only).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from attention_backward_sdpa_amd import synth
+from tests import _common as C
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+V = synth.small_variant
+
+CASES = {
+    # causal GQA, ragged S, per-batch bias
+    "gqa_causal_d128_s333": (V(W["gqa_causal_s4096_d128"], B=2, Hq=4, Hkv=2, Sq=333, Skv=333), "B"),
+    # same shape, one bias shared by the batch (dBias summed over it)
+    "gqa_causal_d128_s333_b1": (V(W["gqa_causal_s4096_d128"], B=2, Hq=4, Hkv=2, Sq=333, Skv=333), 1),
+    # MLA 192/128, causal window and padding
+    "mla_window_padded_s300": (V(W["mla_window_padded_s4096"], B=2, Hq=2, Hkv=2, Sq=300, Skv=300,
+                                 window_left=90, len_lo=100), "B"),
+    # non-causal D = 64, S_q != S_kv
+    "mha_d64_s200x330": (V(W["mha_s128_d64"], B=1, Hq=2, Hkv=2, Sq=200, Skv=330), "B"),
+    # non-causal D = 256
+    "det_d256_s200": (V(W["mha_det_s8192_d256"], Hq=2, Hkv=2, Sq=200, Skv=200), "B"),
+}
+
+
+def _case(w, bias_batch, bias_f32, seed=11):
+    inp = synth.draw_inputs(w)
+    Bb = w.B if bias_batch == "B" else 1
+    rng = np.random.default_rng(seed)
+    bias32 = rng.standard_normal((Bb, w.Hq, w.Sq, w.Skv)).astype(np.float32)
+    bias_bits = None if bias_f32 else synth.bf16_bits(bias32)
+    bias64 = (bias32 if bias_f32 else synth.bf16_to_f32(bias_bits)).astype(np.float64)
+    f = C.f64
+    lens = None if inp.seq_q_lens is None else [int(x) for x in inp.seq_q_lens]
+    kw = dict(causal=w.causal, window_left=w.window_left, seq_q_lens=lens, seq_kv_lens=lens)
+    o64, lse64 = oracle.forward(f(inp.q), f(inp.k), f(inp.v), w.softmax_scale, bias=bias64, **kw)
+    o_bits = synth.bf16_bits(o64.astype(np.float32))
+    lse = lse64.astype(np.float32)
+    ref = oracle.backward(f(inp.q), f(inp.k), f(inp.v), f(o_bits), f(inp.do),
+                          lse.astype(np.float64), w.softmax_scale, bias=bias64,
+                          return_dbias=True, **kw)
+    return inp, o_bits, lse, bias32 if bias_f32 else bias_bits, lens, ref
+
+
+def _run(w, inp, o_bits, lse, bias, lens, det, want_dbias=True, ws_fill=None):
+    import attention_backward_sdpa_amd as lib
+    dev = "cuda"
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v, o, do = bf(inp.q), bf(inp.k), bf(inp.v), bf(o_bits), bf(inp.do)
+    tb = torch.from_numpy(bias).to(dev) if bias.dtype == np.float32 else bf(bias)
+    tl = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=dev)
+    outs = [torch.empty_like(x) for x in (q, k, v)]
+    for x in outs:
+        x.view(torch.int16).fill_(0x7FC0)
+    dbias = torch.full(tuple(bias.shape), float("nan"), dtype=torch.float32, device=dev) \
+        if want_dbias else None
+    kw = dict(scale=w.softmax_scale, causal=w.causal, window_left=w.window_left, deterministic=det,
+              seq_q_lens=tl, seq_kv_lens=tl, bias=tb, dbias=dbias)
+    n = lib.run_workspace_size(q, k, v, **kw)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    if ws_fill is not None:
+        ws.copy_(ws_fill(ws.numel()))
+    lib.sdpa_bwd_run(q, k, v, o, do, torch.from_numpy(lse).to(dev), *outs, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    got = [C.bf16_tensor_to_f32(x) for x in outs]
+    return got, None if dbias is None else dbias.cpu().numpy()
+
+
+@pytest.mark.parametrize("det", [0, 2, 3], ids=["atomic", "dspanels", "dqpartials"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_bias_parity(name, det):
+    import attention_backward_sdpa_amd as lib
+    w, bias_batch = CASES[name]
+    C.log(f"bias case {name} route {det}: {w}")
+    inp, o_bits, lse, bias, lens, ref = _case(w, bias_batch, bias_f32=False)
+    if bias_batch == 1 and w.B > 1 and det != 0:
+        # a batch-summed dBias needs atomics: the deterministic routes decline before any launch
+        with pytest.raises(lib.SdpaBwdError) as e:
+            _run(w, inp, o_bits, lse, bias, lens, det)
+        assert e.value.status == lib.UNSUPPORTED
+        return
+    got, dbias = _run(w, inp, o_bits, lse, bias, lens, det)
+    for tname, g, r in zip(("dQ", "dK", "dV", "dBias"), got + [dbias], ref):
+        C.assert_close(f"bias {name} route {det} {tname}", g, r)
+    # masked pairs, padded rows and padded keys: exactly zero
+    for bb in range(dbias.shape[0]):
+        L = None if lens is None else lens[bb]
+        vis = oracle.visible_mask(w.Sq, w.Skv, w.causal, w.window_left, L, L)
+        if bias_batch == 1 and w.B > 1:
+            vis = np.any([oracle.visible_mask(w.Sq, w.Skv, w.causal, w.window_left,
+                                              None if lens is None else lens[x],
+                                              None if lens is None else lens[x])
+                          for x in range(w.B)], axis=0)
+        assert np.all(dbias[bb][:, ~vis] == 0)
+
+
+@pytest.mark.parametrize("det", [0, 3], ids=["atomic", "dqpartials"])
+def test_fp32_bias_and_no_dbias(det):
+    w, _ = CASES["gqa_causal_d128_s333"]
+    inp, o_bits, lse, bias, lens, ref = _case(w, "B", bias_f32=True)
+    got, dbias = _run(w, inp, o_bits, lse, bias, lens, det)
+    for tname, g, r in zip(("dQ", "dK", "dV", "dBias"), got + [dbias], ref):
+        C.assert_close(f"fp32 bias route {det} {tname}", g, r)
+    # the bias alone (no dBias output) gives the same dQ/dK/dV
+    got2, _ = _run(w, inp, o_bits, lse, bias, lens, det, want_dbias=False)
+    for tname, g, r in zip(("dQ", "dK", "dV"), got2, ref):
+        C.assert_close(f"fp32 bias, no dBias, route {det} {tname}", g, r)
+
+
+@pytest.mark.parametrize("det", [2, 3], ids=["dspanels", "dqpartials"])
+def test_bias_deterministic_bitwise(det):
+    w, _ = CASES["mla_window_padded_s300"]
+    inp, o_bits, lse, bias, lens, ref = _case(w, "B", bias_f32=False)
+    gen = torch.Generator(device="cpu").manual_seed(0)
+    fill = lambda n: torch.randint(0, 256, (n,), dtype=torch.uint8, generator=gen).cuda()
+    first = None
+    for _ in range(5):
+        got, dbias = _run(w, inp, o_bits, lse, bias, lens, det, ws_fill=fill)
+        bits = [x.view(np.uint32) for x in got + [dbias]]
+        if first is None:
+            first = bits
+        else:
+            assert all(np.array_equal(a, b) for a, b in zip(first, bits))
