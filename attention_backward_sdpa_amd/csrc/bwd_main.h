@@ -641,33 +641,50 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
             reinterpret_cast<u32x4*>(wsb + w * 2048 + h * 1024 + lane * 16));
     };
 
-    // Additive bias: the lane's 16 bias values of a q tile (accumulator rows, its key), times
-    // log2(e), loaded one q tile ahead; they are complete at the next tile's memory wait.
+    // Additive bias: the lane's 16 bias elements of a q tile (accumulator rows, its key) as raw
+    // 32-bit words (an fp32 value or a zero-extended 16-bit one), loaded one q tile ahead and not
+    // touched until that tile's replay, so the loads complete under the previous tile's work.
     // dBias: the previous tile's masked fp32 dS, stored (or, for a batch-1 bias summed over the
     // batch, added with fp32 atomics) after the next tile's loads are issued.
     constexpr int NBV = C::BIAS ? 16 : 1;
-    float bcur[NBV], bnext[NBV], dsf[C::BIAS == 2 ? 16 : 1];
+    uint32_t bcur[NBV], bnext[NBV];
+    float dsf[C::BIAS == 2 ? 16 : 1];
     const int64_t bias_bh = (int64_t)b * p.bias_bstride + (int64_t)h * p.Sq * p.Skv;
     const int bias_key = min(key_lane, p.Skv - 1);
-    auto load_bias = [&](int i_t, float (&dst)[NBV]) {
+    auto load_bias = [&](int i_t, uint32_t (&dst)[NBV]) {
+      if constexpr (C::BIAS) {
+        int64_t x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          x[r] = bias_bh + (int64_t)min(i_t * BR + acc_row<32>(r, g), p.Sq - 1) * p.Skv + bias_key;
+        if (p.bias_f32) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dst[r] = reinterpret_cast<const uint32_t*>(p.bias)[x[r]];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dst[r] = reinterpret_cast<const bf16_t*>(p.bias)[x[r]];
+        }
+      }
+    };
+    // the bias of the raw words, times log2(e), for the replay's exponent
+    auto bias_log2 = [&](const uint32_t (&raw)[NBV], float (&dst)[NBV]) {
       if constexpr (C::BIAS) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = min(i_t * BR + acc_row<32>(r, g), p.Sq - 1);
-          const int64_t x = bias_bh + (int64_t)row * p.Skv + bias_key;
-          const float bv = p.bias_f32 ? reinterpret_cast<const float*>(p.bias)[x]
-                                      : Elem<C::F16>::lo(reinterpret_cast<const bf16_t*>(p.bias)[x]);
-          dst[r] = bv * kLog2e;
-        }
+        for (int r = 0; r < 16; ++r)
+          dst[r] = (p.bias_f32 ? __uint_as_float(raw[r]) : Elem<C::F16>::lo(raw[r])) * kLog2e;
       }
     };
     auto store_dbias = [&](int i_t) {
       if constexpr (C::BIAS == 2) {
-        if (key_lane < p.Skv) {
-          float* base = p.dbias + bias_bh + key_lane;
+        float* base = p.dbias + bias_bh + key_lane;
+        const int row0 = i_t * BR;
+        if (row0 + BR <= p.Sq && k0 + BC <= p.Skv && !p.dbias_atomic) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) base[(int64_t)(row0 + acc_row<32>(r, g)) * p.Skv] = dsf[r];
+        } else if (key_lane < p.Skv) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int row = i_t * BR + acc_row<32>(r, g);
+            const int row = row0 + acc_row<32>(r, g);
             if (row < p.Sq) {
               if (p.dbias_atomic)
                 __hip_atomic_fetch_add(base + (int64_t)row * p.Skv, dsf[r], __ATOMIC_RELAXED,
@@ -752,8 +769,10 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
       // Softmax replay of all 32 rows, unmasked and branch-free; edge tiles then clear their
       // invisible pairs in the packed words (keeping the masking out of the block the MFMA
       // accumulators flow through avoids register copies at the join).
-      softmax_ds<C::F16, 0, C::BIAS>(S, dP, sStat, g, p.scale_log2, pb, sb, bcur, dsf);
-      softmax_ds<C::F16, 2, C::BIAS>(S, dP, sStat, g, p.scale_log2, pb, sb, bcur, dsf);
+      float bl[NBV];
+      bias_log2(bcur, bl);
+      softmax_ds<C::F16, 0, C::BIAS>(S, dP, sStat, g, p.scale_log2, pb, sb, bl, dsf);
+      softmax_ds<C::F16, 2, C::BIAS>(S, dP, sStat, g, p.scale_log2, pb, sb, bl, dsf);
       if (edge) {
         const uint32_t vis_m = visible_rows(KeyRows(mg, q0 + g * 4, key_lane));
         mask_pairs<0>(vis_m, pb, sb);

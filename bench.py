@@ -68,9 +68,9 @@ def algorithmic_flops(w, lens):
     return per_pair * visible_pairs(w, lens) * w.Hq
 
 
-def gpu_forward_inputs(torch, q, k, v, w, lens):
+def gpu_forward_inputs(torch, q, k, v, w, lens, bias=None):
     """float32 forward on the GPU -> O (in q's io type) and natural-log LSE (fp32), rows with no
-    key -inf."""
+    key -inf; an additive bias (B, Hq, Sq, Skv) joins the scores after the scale."""
     B, Hq, Sq, _ = q.shape
     group = w.Hq // w.Hkv
     o = torch.empty(B, Hq, Sq, w.Dv, dtype=q.dtype, device=q.device)
@@ -88,6 +88,8 @@ def gpu_forward_inputs(torch, q, k, v, w, lens):
             kh = h // group
             kt = k[b, kh].float().t().contiguous()
             s = (q[b, h].float() @ kt) * w.softmax_scale
+            if bias is not None:
+                s = s + bias[b, h].float()
             s = s.masked_fill(~vis, float("-inf"))
             l = torch.logsumexp(s, dim=-1)
             p = torch.where(vis, torch.exp(s - torch.where(torch.isinf(l), 0.0, l)[:, None]), 0.0)
@@ -232,6 +234,9 @@ def main():
                          "3 dQ partials + ordered reduction)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"],
                     help="io element type of Q, K, V, O, dO and the gradients")
+    ap.add_argument("--bias", default="none", choices=["none", "bias", "dbias"],
+                    help="add a per-batch additive bias (B, Hq, Sq, Skv) of the io type, drawn "
+                         "N(0,1) (bias), and also produce its fp32 gradient (dbias)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run a plain 1 GiB fp32 copy kernel three times "
@@ -269,18 +274,30 @@ def main():
     io = torch.float16 if args.dtype == "fp16" else torch.bfloat16
     bf = lambda a: torch.from_numpy(a.view(np.int16)).view(io).to(dev)
     q, k, v, do = bf(inp.q), bf(inp.k), bf(inp.v), bf(inp.do)
-    o, lse = gpu_forward_inputs(torch, q, k, v, w, lens)
+    bias = dbias = None
+    if args.bias != "none":
+        gen = torch.Generator(device=dev).manual_seed(1000)
+        bias = torch.randn(w.B, w.Hq, w.Sq, w.Skv, generator=gen, device=dev).to(io)
+        if args.bias == "dbias":
+            dbias = torch.empty(w.B, w.Hq, w.Sq, w.Skv, dtype=torch.float32, device=dev)
+    o, lse = gpu_forward_inputs(torch, q, k, v, w, lens, bias)
     lens_t = None if lens is None else torch.from_numpy(lens).to(dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    nws = lib.workspace_size(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.Dqk, w.Dv, w.causal, w.window_left,
-                             det, lens is not None)
+    kw = dict(scale=w.softmax_scale, causal=w.causal, window_left=w.window_left,
+              deterministic=det, seq_q_lens=lens_t, seq_kv_lens=lens_t, bias=bias, dbias=dbias)
+    nws = lib.run_workspace_size(q, k, v, **kw)
     ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(events=None):
-        lib.sdpa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale=w.softmax_scale, causal=w.causal,
-                        window_left=w.window_left, deterministic=det, seq_q_lens=lens_t,
-                        seq_kv_lens=lens_t, workspace=ws, stream=stream, events=events)
+        if bias is None:
+            lib.sdpa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale=w.softmax_scale,
+                            causal=w.causal, window_left=w.window_left, deterministic=det,
+                            seq_q_lens=lens_t, seq_kv_lens=lens_t, workspace=ws, stream=stream,
+                            events=events)
+        else:
+            lib.sdpa_bwd_run(q, k, v, o, do, lse, dq, dk, dv, workspace=ws, stream=stream,
+                             events=events, **kw)
 
     for _ in range(args.warmup):
         step()
@@ -326,7 +343,8 @@ def main():
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
         if t.get("kernel_source_hash") == kernel_source_hash() and t.get("workload") == w.name \
-                and t.get("dq_route") == route and t.get("dtype", "bf16") == args.dtype:
+                and t.get("dq_route") == route and t.get("dtype", "bf16") == args.dtype \
+                and args.bias == "none":
             traffic = t["hbm_bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         traffic = None
@@ -349,6 +367,8 @@ def main():
                    "Skv": w.Skv, "Dqk": w.Dqk, "Dv": w.Dv, "causal": w.causal,
                    "window_left": w.window_left, "padded": w.padded,
                    "dq_route": ROUTE_NAMES[route],
+                   "bias": {"none": "none", "bias": f"{args.dtype} (B, Hq, Sq, Skv)",
+                            "dbias": f"{args.dtype} (B, Hq, Sq, Skv) with fp32 dBias"}[args.bias],
                    "algorithmic_gflop": round(flops / 1e9, 3)},
         "stage_ms": {"preprocess": round(float(stage_avg[0]), 4), "main": round(float(stage_avg[1]), 4),
                      "gqa_reduce": round(float(stage_avg[2]), 4),
