@@ -5,9 +5,14 @@
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc", "sdpa_bwd.hip")
+# translation units: the host side with the small kernels, and the main kernel's instantiations
+# of each kernel head dim (the bulk of the compile time), built in parallel
+SOURCES = [SRC] + [os.path.join(HERE, "csrc", f"main_d{d}.hip") for d in (64, 128, 192, 256)]
 OUT = os.path.join(HERE, "libsdpa_bwd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -26,29 +31,40 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library (always recompiles); returns the path of the shared object."""
-    tmp = OUT + ".tmp"
-    cmd = [HIPCC, *FLAGS, SRC, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    return res.stdout
+
+
+def _parallel(cmds, verbose):
+    workers = max(1, min(len(cmds), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(lambda c: _run(c, verbose), cmds))
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library (always recompiles); returns the path of the shared object."""
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="sdpa_bwd_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in SOURCES]
+        _parallel([[HIPCC, *compile_flags, "-c", src, "-o", obj]
+                   for src, obj in zip(SOURCES, objs)], verbose)
+        tmp = OUT + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, OUT)
     return OUT
 
 
 def device_assembly() -> str:
     """The gfx950 assembly of the library's kernels (device pass only), for inspection."""
-    cmd = [HIPCC, *[f for f in FLAGS if f not in ("-shared", "-fPIC")], "--offload-device-only",
-           "-S", SRC, "-o", "-"]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    return res.stdout
+    flags = [f for f in FLAGS if f not in ("-shared", "-fPIC")]
+    return "\n".join(_parallel([[HIPCC, *flags, "--offload-device-only", "-S", src, "-o", "-"]
+                                for src in SOURCES], False))
 
 
 if __name__ == "__main__":

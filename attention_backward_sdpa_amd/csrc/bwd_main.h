@@ -64,6 +64,8 @@ struct MainParams {
   bf16_t* dv_out;           // dV: likewise with Dv
   const int* seq_q_lens;    // (B,) or null
   const int* seq_kv_lens;   // (B,) or null
+  int dqk_act, dv_act;      // the tensors' head dims (<= the kernel's DQK / DV; columns past
+                            // them read as zero and are not written)
   int B, Hq, Hkv, Sq, Skv, group;
   int partials;             // 1: write per-(query head, part) partials for the reduction
   int n_split;              // parts the q-tile range of a key tile is split into
@@ -87,10 +89,15 @@ enum DqMode {
   DQ_PARTIAL = 2,  // GEMM4 in the kernel, fp32 partial tiles to the workspace (dq_reduce sums)
 };
 
-template <int DQK_, int DV_, int KPW_, int NW_, int MODE_, bool F16_ = false, int BIAS_ = 0>
+template <int DQK_, int DV_, int KPW_, int NW_, int MODE_, bool F16_ = false, int BIAS_ = 0,
+          bool PAD_ = false>
 struct MainCfg {
   static constexpr int DQK = DQK_, DV = DV_, KPW = KPW_, NW = NW_;
   static constexpr int MODE = MODE_;
+  // the tensors' head dims are below DQK / DV (MainParams::dqk_act, dv_act): operand columns past
+  // them read as zero, result columns past them are not stored.  Without it the code is that of
+  // exact head dims.
+  static constexpr bool PAD = PAD_;
   // 0: no bias; 1: additive bias in the replayed scores; 2: bias and its gradient dBias = dS
   static constexpr int BIAS = BIAS_;
   static constexpr bool DS_OUT = MODE == DQ_DS;  // dS leaves the kernel, GEMM4 does not run here
@@ -194,22 +201,39 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 __device__ __forceinline__ constexpr int kswz(int row, int frag) { return (row >> 1) + 2 * (frag & 1); }
 
 // Element offset (in the source, rows rs elements apart) of the 16 bytes this lane contributes to
-// fragment f.
+// fragment f, and the first column of those 16 bytes.
+template <int D, bool SWZ>
+__device__ __forceinline__ int frag_src_col(int f, int lane) {
+  int n = lane;
+  if constexpr (SWZ) n = (lane & 48) | ((lane & 15) ^ (4 * kswz(lane >> 4, f)));
+  return 16 * (f % (D / 16)) + 8 * (n >> 5);
+}
+
 template <int D, bool SWZ>
 __device__ __forceinline__ int frag_src_elem(int f, int row0, int rows_valid, int lane, int rs) {
-  const int rt = f / (D / 16), t = f % (D / 16);
+  const int rt = f / (D / 16);
   int n = lane;
   if constexpr (SWZ) n = (lane & 48) | ((lane & 15) ^ (4 * kswz(lane >> 4, f)));
   int row = row0 + 32 * rt + (n & 31);
   row = row < rows_valid ? row : rows_valid - 1;
-  return row * rs + 16 * t + 8 * (n >> 5);
+  return row * rs + frag_src_col<D, SWZ>(f, lane);
 }
+
+// A byte offset past every buffer's range (the host keeps ranges below 2^31): the load returns
+// zeros.  Used for the 16-byte chunks at or past the tensor's head dim (D is a multiple of 8),
+// which pad the operands to the kernel's head dim.
+constexpr uint32_t kOutOfRange = 0x80000000u;
 
 template <int D, int NW, bool SWZ = false>
 __device__ __forceinline__ void gather_frags(rsrc_t src, int row0, int rows_valid, int rs,
-                                             int nfrag, char* lds, int w, int lane) {
+                                             int nfrag, char* lds, int w, int lane,
+                                             int d_act = D) {
   for (int f = w; f < nfrag; f += NW)
-    dma16(src, (uint32_t)frag_src_elem<D, SWZ>(f, row0, rows_valid, lane, rs) * 2, lds + f * 1024);
+    dma16(src,
+          frag_src_col<D, SWZ>(f, lane) < d_act
+              ? (uint32_t)frag_src_elem<D, SWZ>(f, row0, rows_valid, lane, rs) * 2
+              : kOutOfRange,
+          lds + f * 1024);
 }
 
 // Byte offset of this lane's 16-byte chunk in a linear read of swizzled fragment f (f's parity
@@ -572,8 +596,9 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
   const bf16_t* dOb = p.dO + b * p.sdo.b + h * p.sdo.h;
   const float* statb = p.stats + (int64_t)bh * p.sq_pad * 2;
   // one head's rows (the host keeps each span below 2^31 bytes)
-  const rsrc_t rQ = buf_rsrc(Qb, ((int64_t)(p.Sq - 1) * p.sq.s + DQK) * 2);
-  const rsrc_t rdO = buf_rsrc(dOb, ((int64_t)(p.Sq - 1) * p.sdo.s + DV) * 2);
+  const int dqk_act = C::PAD ? p.dqk_act : DQK, dv_act = C::PAD ? p.dv_act : DV;
+  const rsrc_t rQ = buf_rsrc(Qb, ((int64_t)(p.Sq - 1) * p.sq.s + dqk_act) * 2);
+  const rsrc_t rdO = buf_rsrc(dOb, ((int64_t)(p.Sq - 1) * p.sdo.s + dv_act) * 2);
   const rsrc_t rStat = buf_rsrc(statb, (int64_t)p.sq_pad * 2 * 4);
 
   acc_t accK[C::N_DQT][NKT], accV[C::N_DVT][NKT];
@@ -595,16 +620,19 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
     // ---- q tile i into its LDS buffer ----------------------------------------------------------
     auto load_tile = [&](int i) {
       char* t = tile(i);
-      gather_frags<DQK, C::NW, true>(rQ, i * BR, p.Sq, (int)p.sq.s, C::N_KQ, t + C::T_QA, w, lane);
-      gather_frags<DV, C::NW, true>(rdO, i * BR, p.Sq, (int)p.sdo.s, C::N_KV, t + C::T_OA, w, lane);
+      gather_frags<DQK, C::NW, true>(rQ, i * BR, p.Sq, (int)p.sq.s, C::N_KQ, t + C::T_QA, w, lane,
+                                     dqk_act);
+      gather_frags<DV, C::NW, true>(rdO, i * BR, p.Sq, (int)p.sdo.s, C::N_KV, t + C::T_OA, w, lane,
+                                    dv_act);
       if (w == 0)  // 64 floats: [lse2, delta] x 32 rows, already padded to sq_pad rows
         dma4(rStat, (uint32_t)(i * BR * 2 + lane) * 4, t + C::T_ST);
     };
     load_tile(i_hi);
     // ---- K fragments into LDS (B operand of GEMM1 and/or GEMM4) -------------------------------
     if constexpr (C::KLDS)
-      gather_frags<DQK, C::NW, true>(buf_rsrc(Kb, ((int64_t)(p.Skv - 1) * p.sk.s + DQK) * 2), k0,
-                                     p.Skv, (int)p.sk.s, (BC / 32) * C::N_KQ, sK, w, lane);
+      gather_frags<DQK, C::NW, true>(buf_rsrc(Kb, ((int64_t)(p.Skv - 1) * p.sk.s + dqk_act) * 2),
+                                     k0, p.Skv, (int)p.sk.s, (BC / 32) * C::N_KQ, sK, w, lane,
+                                     dqk_act);
     // ---- V (and K) slices into registers -------------------------------------------------------
     bf16x8 vreg[NKT][C::N_KV];
     bf16x8 kreg[C::KREG ? NKT : 1][C::KREG ? C::N_KQ : 1];
@@ -612,13 +640,22 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
     for (int kt = 0; kt < NKT; ++kt) {
       int key = key_lane + kt * 32;
       key = key < p.Skv ? key : p.Skv - 1;  // keys past the sequence are masked out of every product
-      const bf16_t* vr = Vb + (int64_t)key * p.sv.s + g * 8;
+      // columns at or past the tensor's head dim are zero (read from column 0, then cleared)
+      const bf16_t* vr = Vb + (int64_t)key * p.sv.s;
 #pragma unroll
-      for (int t = 0; t < C::N_KV; ++t) vreg[kt][t] = *reinterpret_cast<const bf16x8*>(vr + t * 16);
+      for (int t = 0; t < C::N_KV; ++t) {
+        const int col = g * 8 + t * 16;
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(vr + (col < dv_act ? col : 0));
+        vreg[kt][t] = col < dv_act ? x : bf16x8{};
+      }
       if constexpr (C::KREG) {
-        const bf16_t* kr = Kb + (int64_t)key * p.sk.s + g * 8;
+        const bf16_t* kr = Kb + (int64_t)key * p.sk.s;
 #pragma unroll
-        for (int t = 0; t < C::N_KQ; ++t) kreg[kt][t] = *reinterpret_cast<const bf16x8*>(kr + t * 16);
+        for (int t = 0; t < C::N_KQ; ++t) {
+          const int col = g * 8 + t * 16;
+          const bf16x8 x = *reinterpret_cast<const bf16x8*>(kr + (col < dqk_act ? col : 0));
+          kreg[kt][t] = col < dqk_act ? x : bf16x8{};
+        }
       }
     }
 
@@ -837,6 +874,7 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
 #pragma unroll
         for (int r0 = 0; r0 < 16; r0 += 4) {
           const int d = dt * 32 + acc_row<32>(r0, g);
+          if (C::PAD && !p.partials && d >= dqk_act) continue;  // past the tensor's head dim
           *reinterpret_cast<u32x2*>(dkr + d) = u32x2{
               Elem<C::F16>::pack2(accK[dt][kt][r0] * p.scale, accK[dt][kt][r0 + 1] * p.scale),
               Elem<C::F16>::pack2(accK[dt][kt][r0 + 2] * p.scale, accK[dt][kt][r0 + 3] * p.scale)};
@@ -846,6 +884,7 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
 #pragma unroll
         for (int r0 = 0; r0 < 16; r0 += 4) {
           const int d = dt * 32 + acc_row<32>(r0, g);
+          if (C::PAD && !p.partials && d >= dv_act) continue;
           *reinterpret_cast<u32x2*>(dvr + d) =
               u32x2{Elem<C::F16>::pack2(accV[dt][kt][r0], accV[dt][kt][r0 + 1]),
                     Elem<C::F16>::pack2(accV[dt][kt][r0 + 2], accV[dt][kt][r0 + 3])};

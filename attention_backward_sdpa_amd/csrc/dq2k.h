@@ -35,6 +35,8 @@ struct Dq2kParams {
   int B, Hq, Hkv, Sq, Skv, group;
   int causal, window_left, window_right, bottom_right;
   int n_kv_tiles, n_q_tiles;
+  int dqk_act;                // K / dQ head dim (<= DQK): dQ columns past it are not written, so
+                              // the K columns past it are read unmasked (in bounds)
   float scale;
 };
 
@@ -141,6 +143,12 @@ __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
                         p.ds_ws + ((int64_t)bh * p.n_kv_tiles * p.n_q_tiles + my_tile) * (BC * BR)) +
                     lane * 16;
   const bf16_t* Kb = p.k + b * p.sk.b + kvh * p.sk.h;
+  // K columns at or past the tensor's head dim only reach dQ columns that are not stored, so they
+  // need no zeroing, only in-bounds reads: a range-checked buffer over the head's rows (the host
+  // keeps the span below 2^31 bytes) returns zeros past the last row's last column
+  const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(Kb), (short)0, (int)(((int64_t)(p.Skv - 1) * p.sk.s + p.dqk_act) * 2),
+      0x00020000);
 
   const Gemm4Lanes tl(lane);
   acc_t acc[C::N_DT];
@@ -163,8 +171,8 @@ __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
       const int c = c_lo + (r < n ? r : n - 1);
 #pragma unroll
       for (int u = 0; u < C::K_PER_WAVE; ++u)
-        dst[u] = *reinterpret_cast<const u32x4*>(
-            Kb + frag_src_elem<DQK, true>(w + u * C::NW, c * KC, p.Skv, lane, (int)p.sk.s));
+        dst[u] = __builtin_amdgcn_raw_buffer_load_b128(
+            rK, frag_src_elem<DQK, true>(w + u * C::NW, c * KC, p.Skv, lane, (int)p.sk.s) * 2, 0, 0);
     };
     auto store_k = [&](const u32x4 (&src)[C::K_PER_WAVE], int buf) {
 #pragma unroll
@@ -227,7 +235,7 @@ __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int q = q0 + acc_row<32>(r, g);
-        if (q < p.Sq)
+        if (q < p.Sq && dt * 32 + lc < p.dqk_act)
           dqb[(int64_t)q * p.sdq.s + dt * 32 + lc] = Elem<C::F16>::one(acc[dt][r] * p.scale);
       }
     }

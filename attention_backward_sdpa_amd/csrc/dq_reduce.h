@@ -31,6 +31,7 @@ struct DqReduceParams {
   int causal, window_left, window_right, bottom_right;
   int n_kv_tiles, n_q_tiles;
   int bc;               // keys per KV tile of the main kernel
+  int dqk_act;          // dQ head dim (<= DQK): the columns written
   float scale;
 };
 
@@ -120,7 +121,7 @@ __global__ void __launch_bounds__(DQK * 2) dq_reduce_kernel(DqReduceParams p) {
 #pragma unroll
   for (int c = tid; c < BR * V; c += NT) {
     const int r = c / V, cv = c % V, q = q0 + r;
-    if (q >= p.Sq) continue;
+    if (q >= p.Sq || cv * 8 >= p.dqk_act) continue;
     u32x4 out = u32x4{0u, 0u, 0u, 0u};
     if (q < mg.Lq) {
       const floatx4 a = *reinterpret_cast<const floatx4*>(sT + r * ROWF + cv * 8);

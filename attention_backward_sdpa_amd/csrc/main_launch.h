@@ -1,0 +1,81 @@
+// Launch of the fused main kernel (bwd_main.h) for one kernel head dim.  Each head dim's
+// instantiations (3 dQ modes x bf16/fp16 x bias none/bias/dBias x exact/padded head dims) live in
+// a translation unit of their own (main_d<DQK>.hip), so the library's objects compile in
+// parallel; the host side (sdpa_bwd.hip) calls launch_main_dqk<DQK>.
+#pragma once
+#include "bwd_main.h"
+
+namespace sdpa {
+
+// Tile geometry of the main kernel for a kernel head dim: 8 waves (256 registers each, 256-key
+// tiles) for DQK <= 192 without a bias; 4 waves (512 registers, 128-key tiles) for DQK = 256 and
+// for every head dim with a bias, whose next-tile values are held in registers.
+template <int DQK>
+struct MainShape {
+  static constexpr int DV = DQK == 192 ? 128 : DQK;
+  static constexpr int KPW = 32;
+  static constexpr int nw(bool bias) { return DQK == 256 || bias ? 4 : 8; }
+};
+
+// bias: 0 none, 1 additive bias, 2 bias and dBias.  `bc` is the key tile the caller's workspace
+// carve and grid assume; a mismatch with the kernel's is hipErrorInvalidValue.
+template <int DQK>
+hipError_t launch_main_dqk(const MainParams& mp, DqMode mode, bool f16, int bias, int grid, int bc,
+                           hipStream_t s);
+
+template <class C>
+hipError_t launch_main_cfg(const MainParams& mp, int grid, hipStream_t s) {
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute((const void*)bwd_main_kernel<C>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL(bwd_main_kernel<C>, dim3(grid), dim3(C::NT), C::LDS_BYTES, s, mp);
+  return hipGetLastError();
+}
+
+template <int DQK, int DV, int KPW, int NW, bool F16, int BIAS, bool PAD>
+hipError_t launch_main_mode(const MainParams& mp, DqMode mode, int grid, hipStream_t s) {
+  if (mode == DQ_DS)
+    return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_DS, F16, BIAS, PAD>>(mp, grid, s);
+  if (mode == DQ_PARTIAL)
+    return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_PARTIAL, F16, BIAS, PAD>>(mp, grid, s);
+  return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_ATOMIC, F16, BIAS, PAD>>(mp, grid, s);
+}
+
+template <int DQK, int NW, int BIAS>
+hipError_t launch_main_nw(const MainParams& mp, DqMode mode, bool f16, int grid, int bc,
+                          hipStream_t s) {
+  constexpr int DV = MainShape<DQK>::DV, KPW = MainShape<DQK>::KPW;
+  if (MainCfg<DQK, DV, KPW, NW, DQ_ATOMIC>::BC != bc) return hipErrorInvalidValue;
+  // head dims below the kernel's take the variant that zero-pads the operands
+  const bool pad = mp.dqk_act != DQK || mp.dv_act != DV;
+  if (f16)
+    return pad ? launch_main_mode<DQK, DV, KPW, NW, true, BIAS, true>(mp, mode, grid, s)
+               : launch_main_mode<DQK, DV, KPW, NW, true, BIAS, false>(mp, mode, grid, s);
+  return pad ? launch_main_mode<DQK, DV, KPW, NW, false, BIAS, true>(mp, mode, grid, s)
+             : launch_main_mode<DQK, DV, KPW, NW, false, BIAS, false>(mp, mode, grid, s);
+}
+
+template <int DQK>
+hipError_t launch_main_dqk(const MainParams& mp, DqMode mode, bool f16, int bias, int grid, int bc,
+                           hipStream_t s) {
+  constexpr int NW0 = MainShape<DQK>::nw(false), NW1 = MainShape<DQK>::nw(true);
+  if (bias == 1) return launch_main_nw<DQK, NW1, 1>(mp, mode, f16, grid, bc, s);
+  if (bias == 2) return launch_main_nw<DQK, NW1, 2>(mp, mode, f16, grid, bc, s);
+  return launch_main_nw<DQK, NW0, 0>(mp, mode, f16, grid, bc, s);
+}
+
+// instantiated once each, in main_d<DQK>.hip
+#define SDPA_MAIN_DQK(D)                                                                           \
+  extern template hipError_t launch_main_dqk<D>(const MainParams&, DqMode, bool, int, int, int,    \
+                                                hipStream_t);
+SDPA_MAIN_DQK(64)
+SDPA_MAIN_DQK(128)
+SDPA_MAIN_DQK(192)
+SDPA_MAIN_DQK(256)
+#undef SDPA_MAIN_DQK
+
+}  // namespace sdpa

@@ -12,9 +12,9 @@
 #include <stdint.h>
 
 #include "../../include/sdpa_bwd.h"
-#include "bwd_main.h"
 #include "dq2k.h"
 #include "dq_reduce.h"
+#include "main_launch.h"
 #include "small_kernels.h"
 
 using namespace sdpa;
@@ -31,6 +31,21 @@ inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 struct Geometry {
   int nw, kpw, bc, br;
 };
+
+// The kernel head dims that serve a call's (Dqk, Dv) ("Support surface": head dims that are
+// multiples of 8 up to 256 compute on the next supported size, reading zeros past the actual
+// extent): the smallest supported pair covering both.  Dv <= Dqk.
+bool kernel_dims(int Dqk, int Dv, int* kq, int* kv) {
+  if (Dqk < 8 || Dv < 8 || Dqk > 256 || Dv > Dqk || (Dqk & 7) || (Dv & 7)) return false;
+  static const int pairs[4][2] = {{64, 64}, {128, 128}, {192, 128}, {256, 256}};
+  for (const auto& pr : pairs)
+    if (Dqk <= pr[0] && Dv <= pr[1]) {
+      *kq = pr[0];
+      *kv = pr[1];
+      return true;
+    }
+  return false;
+}
 
 // With an additive bias every head dim runs the 4-wave layout (512 registers per wave): the
 // bias values of the next q tile are held in registers while the current one computes.
@@ -159,10 +174,12 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
   if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0) return SDPA_BWD_INVALID_ARG;
   if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return SDPA_BWD_INVALID_ARG;
   if (window_left < -1 || window_right < 0) return SDPA_BWD_INVALID_ARG;
-  if (!geometry_for(Dqk, Dv, geo, bias)) return SDPA_BWD_UNSUPPORTED;
+  int kq, kv;
+  if (!kernel_dims(Dqk, Dv, &kq, &kv) || !geometry_for(kq, kv, geo, bias))
+    return SDPA_BWD_UNSUPPORTED;
   // the kernels address one head's rows (and its padded tiles) through 32-bit buffer offsets
   const int64_t s_max = (Sq > Skv ? Sq : Skv) + geo->bc;
-  if (s_max * (Dqk > Dv ? Dqk : Dv) * 2 >= ((int64_t)1 << 31)) return SDPA_BWD_UNSUPPORTED;
+  if (s_max * (kq > kv ? kq : kv) * 2 >= ((int64_t)1 << 31)) return SDPA_BWD_UNSUPPORTED;
   // a tensor with no elements may be NULL
   const bool has_q = (int64_t)B * Sq > 0, has_k = (int64_t)B * Skv > 0;
   if (has_q && (!q || !o || !dO || !lse || !dq)) return SDPA_BWD_INVALID_ARG;
@@ -171,19 +188,6 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
       ((uintptr_t)lse & 3) != 0 || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return SDPA_BWD_UNSUPPORTED;
   return SDPA_BWD_OK;
-}
-
-template <class C>
-hipError_t launch_main(const MainParams& mp, int grid, hipStream_t s) {
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)bwd_main_kernel<C>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
-  hipLaunchKernelGGL(bwd_main_kernel<C>, dim3(grid), dim3(C::NT), C::LDS_BYTES, s, mp);
-  return hipGetLastError();
 }
 
 template <class C>
@@ -199,44 +203,15 @@ hipError_t launch_dq2k(const Dq2kParams& dp, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DQK, int DV, int KPW, int NW, bool F16, int BIAS>
-hipError_t dispatch_main_t(const MainParams& mp, Route route, int grid, int bc, hipStream_t s) {
-  // the workspace carve and the grid use the geometry table; the kernel must tile the same way
-  if (MainCfg<DQK, DV, KPW, NW, DQ_ATOMIC>::BC != bc) return hipErrorInvalidValue;
-  if (route == R_DS) return launch_main<MainCfg<DQK, DV, KPW, NW, DQ_DS, F16, BIAS>>(mp, grid, s);
-  if (route == R_DQP)
-    return launch_main<MainCfg<DQK, DV, KPW, NW, DQ_PARTIAL, F16, BIAS>>(mp, grid, s);
-  return launch_main<MainCfg<DQK, DV, KPW, NW, DQ_ATOMIC, F16, BIAS>>(mp, grid, s);
-}
-
-template <int DQK, int DV, int KPW, int NW, int BIAS>
-hipError_t dispatch_main(const MainParams& mp, Route route, bool f16, int grid, int bc,
-                         hipStream_t s) {
-  if (f16) return dispatch_main_t<DQK, DV, KPW, NW, true, BIAS>(mp, route, grid, bc, s);
-  return dispatch_main_t<DQK, DV, KPW, NW, false, BIAS>(mp, route, grid, bc, s);
-}
-
-// bias: 0 none, 1 bias, 2 bias and dBias (the 4-wave layout of geometry_for)
-template <int BIAS>
-hipError_t run_main_b(int Dqk, const MainParams& mp, Route route, bool f16, int grid, int bc,
-                      hipStream_t s) {
-  if constexpr (BIAS == 0) {
-    if (Dqk == 64) return dispatch_main<64, 64, 32, 8, 0>(mp, route, f16, grid, bc, s);
-    if (Dqk == 128) return dispatch_main<128, 128, 32, 8, 0>(mp, route, f16, grid, bc, s);
-    if (Dqk == 192) return dispatch_main<192, 128, 32, 8, 0>(mp, route, f16, grid, bc, s);
-  } else {
-    if (Dqk == 64) return dispatch_main<64, 64, 32, 4, BIAS>(mp, route, f16, grid, bc, s);
-    if (Dqk == 128) return dispatch_main<128, 128, 32, 4, BIAS>(mp, route, f16, grid, bc, s);
-    if (Dqk == 192) return dispatch_main<192, 128, 32, 4, BIAS>(mp, route, f16, grid, bc, s);
-  }
-  return dispatch_main<256, 256, 32, 4, BIAS>(mp, route, f16, grid, bc, s);
-}
-
+// The main kernel of the route for kernel head dim Dqk (instantiated in main_d<Dqk>.hip).
+// bias: 0 none, 1 bias, 2 bias and dBias (the 4-wave layout of geometry_for).
 hipError_t run_main(int Dqk, const MainParams& mp, Route route, bool f16, int bias, int grid,
                     int bc, hipStream_t s) {
-  if (bias == 1) return run_main_b<1>(Dqk, mp, route, f16, grid, bc, s);
-  if (bias == 2) return run_main_b<2>(Dqk, mp, route, f16, grid, bc, s);
-  return run_main_b<0>(Dqk, mp, route, f16, grid, bc, s);
+  const DqMode mode = route == R_DS ? DQ_DS : route == R_DQP ? DQ_PARTIAL : DQ_ATOMIC;
+  if (Dqk == 64) return launch_main_dqk<64>(mp, mode, f16, bias, grid, bc, s);
+  if (Dqk == 128) return launch_main_dqk<128>(mp, mode, f16, bias, grid, bc, s);
+  if (Dqk == 192) return launch_main_dqk<192>(mp, mode, f16, bias, grid, bc, s);
+  return launch_main_dqk<256>(mp, mode, f16, bias, grid, bc, s);
 }
 
 // the reduction reads the partial blocks in the layout of the main kernel that wrote them (the
@@ -352,6 +327,8 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   int st = validate(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, window_left,
                     window_right, &geo, has_bias);
   if (st != SDPA_BWD_OK) return st;
+  int KDqk, KDv;  // the kernel's head dims (>= the tensors' Dqk, Dv)
+  kernel_dims(Dqk, Dv, &KDqk, &KDv);
   if (dtype != SDPA_BWD_BF16 && dtype != SDPA_BWD_FP16) return SDPA_BWD_UNSUPPORTED;
   if (ba.dbias && !has_bias) return SDPA_BWD_INVALID_ARG;
   if (has_bias) {
@@ -368,7 +345,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
       L.t[x] = Strides{layouts[x].batch, layouts[x].head, layouts[x].seq};
   st = check_layouts(L, Sq, Skv, Dqk, Dv);
   if (st != SDPA_BWD_OK) return st;
-  const Route route = route_for(deterministic, Dqk, geo);
+  const Route route = route_for(deterministic, KDqk, geo);
   if (route == R_INVALID) return SDPA_BWD_INVALID_ARG;
   // dBias of a batch-1 bias sums over the batch with fp32 atomics: not reproducible ("Support
   // surface", bias), so the deterministic routes need a per-batch bias then
@@ -376,7 +353,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   if (dbias_atomic && route != R_ATOMIC) return SDPA_BWD_UNSUPPORTED;
   // empty problems need no workspace (sdpa_bwd_workspace_size returns 0 for them)
   const bool empty = B == 0 || Sq == 0 || Skv == 0;
-  const Carve c = empty ? Carve{} : carve(B, Hq, Hkv, Sq, Skv, Dqk, Dv, route, geo);
+  const Carve c = empty ? Carve{} : carve(B, Hq, Hkv, Sq, Skv, KDqk, KDv, route, geo);
   if (c.total > 0 && workspace == nullptr) return SDPA_BWD_INVALID_ARG;
   if (check_ws && (uint64_t)c.total > (uint64_t)workspace_bytes) return SDPA_BWD_WORKSPACE_TOO_SMALL;
   if (c.total > 0 && ((uintptr_t)workspace % kAlign) != 0) return SDPA_BWD_UNSUPPORTED;
@@ -438,9 +415,10 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   pp.Hq = Hq;
   pp.Sq = Sq;
   pp.sq_pad = (int)c.sq_pad;
-  pp.Dqk = Dqk;
+  pp.Dqk = KDqk;
+  pp.dv_act = Dv;
   pp.zero_rows = route == R_ATOMIC ? 1 : 0;
-  e = launch_preprocess(pp, Dv, f16, (int64_t)B * Hq * (c.sq_pad / geo.br), stream);
+  e = launch_preprocess(pp, KDv, f16, (int64_t)B * Hq * (c.sq_pad / geo.br), stream);
   if (e == hipSuccess) e = launch_dsink(stats, (int)c.sq_pad, false);
   if (e == hipSuccess && ba.dbias) {
     // zero the dBias blocks the main kernel does not write (all of them when it accumulates)
@@ -485,6 +463,8 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   mp.dv_out = partials ? (bf16_t*)(ws + c.dv_ws) : (bf16_t*)dv;
   mp.seq_q_lens = seq_q_lens;
   mp.seq_kv_lens = seq_kv_lens;
+  mp.dqk_act = Dqk;
+  mp.dv_act = Dv;
   mp.B = B;
   mp.Hq = Hq;
   mp.Hkv = Hkv;
@@ -509,7 +489,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   mp.dbias_atomic = dbias_atomic ? 1 : 0;
   const int64_t main_grid = (int64_t)mp.n_kv_tiles * split * B * Hq;
   if (main_grid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
-  e = run_main(Dqk, mp, route, f16, has_bias ? (ba.dbias ? 2 : 1) : 0, (int)main_grid, geo.bc,
+  e = run_main(KDqk, mp, route, f16, has_bias ? (ba.dbias ? 2 : 1) : 0, (int)main_grid, geo.bc,
                stream);
   if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   rec(2);
@@ -525,10 +505,12 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     rp.n_kvh = B * Hkv;
     rp.Hkv = Hkv;
     rp.Skv = Skv;
-    rp.Dqk = Dqk;
-    rp.Dv = Dv;
+    rp.Dqk = KDqk;
+    rp.Dv = KDv;
+    rp.dqk_act = Dqk;
+    rp.dv_act = Dv;
     rp.group = (Hq / Hkv) * split;  // slots (query head of the group, part), in that order
-    const int64_t per_head = (int64_t)Skv * (Dqk + Dv) / 8;
+    const int64_t per_head = (int64_t)Skv * (KDqk + KDv) / 8;
     int64_t bx = (per_head + 255) / 256;
     bx = bx > 4096 ? 4096 : bx;
     const int by = rp.n_kvh > 65535 ? 65535 : rp.n_kvh;
@@ -548,10 +530,11 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     cp.seq_q_lens = seq_q_lens;
     cp.Hq = Hq;
     cp.Sq = Sq;
+    cp.dqk_act = Dqk;
     cp.scale = scale;
     const int64_t cgrid = (int64_t)B * Hq * ((Sq + 31) / 32);
     if (cgrid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
-    e = launch_convert(cp, Dqk, f16, (int)cgrid, stream);
+    e = launch_convert(cp, KDqk, f16, (int)cgrid, stream);
     if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   } else if (route == R_DQP) {
     DqReduceParams rp;
@@ -571,10 +554,11 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     rp.n_kv_tiles = mp.n_kv_tiles;
     rp.n_q_tiles = (int)(c.sq_pad / geo.br);
     rp.bc = geo.bc;
+    rp.dqk_act = Dqk;
     rp.scale = scale;
     const int64_t rgrid = (int64_t)B * Hq * rp.n_q_tiles;
     if (rgrid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
-    e = launch_dq_reduce(rp, Dqk, f16, (int)rgrid, stream);
+    e = launch_dq_reduce(rp, KDqk, f16, (int)rgrid, stream);
     if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   } else {
     Dq2kParams dp;
@@ -597,8 +581,9 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     dp.bottom_right = mp.bottom_right;
     dp.n_kv_tiles = mp.n_kv_tiles;
     dp.n_q_tiles = (int)(c.sq_pad / geo.br);
+    dp.dqk_act = Dqk;
     dp.scale = scale;
-    e = run_dq2k(Dqk, f16, dp, geo.bc, stream);
+    e = run_dq2k(KDqk, f16, dp, geo.bc, stream);
     if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   }
   rec(4);
@@ -615,18 +600,20 @@ size_t sdpa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk,
   (void)window_left;
   (void)has_seqlens;
   Geometry geo;
+  int kq, kv;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || Hq % Hkv != 0) return 0;
-  if (!geometry_for(Dqk, Dv, &geo)) return 0;
+  if (!kernel_dims(Dqk, Dv, &kq, &kv) || !geometry_for(kq, kv, &geo)) return 0;
   if (B == 0 || Sq == 0 || Skv == 0) return 0;
-  const Route route = route_for(deterministic, Dqk, geo);
+  const Route route = route_for(deterministic, kq, geo);
   if (route == R_INVALID) return 0;
-  return (size_t)carve(B, Hq, Hkv, Sq, Skv, Dqk, Dv, route, geo).total;
+  return (size_t)carve(B, Hq, Hkv, Sq, Skv, kq, kv, route, geo).total;
 }
 
 int sdpa_bwd_dq_route(int Dqk, int Dv, int deterministic) {
   Geometry geo;
-  if (!geometry_for(Dqk, Dv, &geo)) return -1;
-  switch (route_for(deterministic, Dqk, geo)) {
+  int kq, kv;
+  if (!kernel_dims(Dqk, Dv, &kq, &kv) || !geometry_for(kq, kv, &geo)) return -1;
+  switch (route_for(deterministic, kq, geo)) {
     case R_ATOMIC: return SDPA_BWD_DQ_ATOMIC;
     case R_DS: return SDPA_BWD_DQ_DS_PANELS;
     case R_DQP: return SDPA_BWD_DQ_PARTIALS;
@@ -700,19 +687,21 @@ size_t sdpa_bwd_run_workspace_size(const sdpa_bwd_args* a) {
   Geometry geo;
   if (a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Sq < 0 || a->Skv < 0 || a->Hq % a->Hkv != 0)
     return 0;
-  if (!geometry_for(a->Dqk, a->Dv, &geo, a->bias != nullptr)) return 0;
+  int kq, kv;
+  if (!kernel_dims(a->Dqk, a->Dv, &kq, &kv) || !geometry_for(kq, kv, &geo, a->bias != nullptr))
+    return 0;
   if (a->B == 0 || a->Sq == 0 || a->Skv == 0) return 0;
-  const Route route = route_for(a->deterministic, a->Dqk, geo);
+  const Route route = route_for(a->deterministic, kq, geo);
   if (route == R_INVALID) return 0;
-  return (size_t)carve(a->B, a->Hq, a->Hkv, a->Sq, a->Skv, a->Dqk, a->Dv, route, geo).total;
+  return (size_t)carve(a->B, a->Hq, a->Hkv, a->Sq, a->Skv, kq, kv, route, geo).total;
 }
 
 int sdpa_bwd_preprocess(const void* o, const void* dO, const float* lse, float* stats,
                         float* dq_accum, const int* seq_q_lens, int B, int Hq, int Sq, int Dv,
                         int Dqk, void* stream) {
   if (B < 0 || Hq < 0 || Sq < 0) return SDPA_BWD_INVALID_ARG;
-  Geometry geo;
-  if (!geometry_for(Dqk, Dv, &geo)) return SDPA_BWD_UNSUPPORTED;
+  int kq, kv;
+  if (!kernel_dims(Dqk, Dv, &kq, &kv)) return SDPA_BWD_UNSUPPORTED;
   if (!o || !dO || !lse || !stats) return SDPA_BWD_INVALID_ARG;
   if (!aligned16(o) || !aligned16(dO) || !aligned16(stats) || (dq_accum && !aligned16(dq_accum)) ||
       ((uintptr_t)lse & 3) != 0)
@@ -727,10 +716,11 @@ int sdpa_bwd_preprocess(const void* o, const void* dO, const float* lse, float* 
   pp.sq_pad = (int)align_up(Sq, 32);
   pp.Hq = Hq;
   pp.Sq = Sq;
-  pp.Dqk = Dqk;
+  pp.Dqk = Dqk;     // the caller's dq_accum rows are Dqk floats
+  pp.dv_act = Dv;
   pp.zero_rows = dq_accum ? 1 : 0;
   const int64_t tiles = (int64_t)B * Hq * (pp.sq_pad / 32);
-  return launch_preprocess(pp, Dv, false, tiles, (hipStream_t)stream) == hipSuccess
+  return launch_preprocess(pp, kv, false, tiles, (hipStream_t)stream) == hipSuccess
              ? SDPA_BWD_OK
              : SDPA_BWD_LAUNCH_FAILED;
 }

@@ -25,7 +25,8 @@ struct PreParams {
   float* stats;              // (B*Hq, sq_pad, 2)
   float* dq_accum;           // (B*Hq, Sq, Dqk) or null
   const int* seq_q_lens;
-  int Hq, Sq, sq_pad, Dqk;
+  int Hq, Sq, sq_pad, Dqk;   // Dqk: the dq_accum row length (the kernel's head dim)
+  int dv_act;                // O / dO head dim (<= DV); the row dot covers these columns
   int zero_rows;
 };
 
@@ -49,7 +50,7 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
     const bool live = s < Lq;
     const int64_t row = bh * p.Sq + s;
     float acc = 0.f;
-    if (live) {
+    if (live && sub * 8 < p.dv_act) {
       const u32x4 a = *reinterpret_cast<const u32x4*>(ob + s * p.so.s + sub * 8);
       const u32x4 c = *reinterpret_cast<const u32x4*>(dob + s * p.sdo.s + sub * 8);
 #pragma unroll
@@ -84,6 +85,7 @@ struct ConvertParams {
   Strides sdq;
   const int* seq_q_lens;
   int Hq, Sq;
+  int dqk_act;               // dQ head dim (<= DQK, the accumulator's row length)
   float scale;
 };
 
@@ -99,6 +101,7 @@ __global__ void __launch_bounds__(256) dq_convert_kernel(ConvertParams p) {
   for (int v = threadIdx.x; v < 32 * V; v += 256) {
     const int s = q0 + v / V, c = v % V;
     if (s >= p.Sq) break;
+    if (c * 8 >= p.dqk_act) continue;
     const int64_t x = (bh * p.Sq + s) * V + c;
     u32x4 out = u32x4{0u, 0u, 0u, 0u};
     if (s < Lq) {
@@ -124,7 +127,8 @@ struct ReduceParams {
   bf16_t* dv;
   Strides sdk, sdv;
   int n_kvh, Hkv;            // B * Hkv, Hkv
-  int Skv, Dqk, Dv;
+  int Skv, Dqk, Dv;          // the partials' row lengths (the kernel's head dims)
+  int dqk_act, dv_act;       // dK / dV head dims (<= Dqk / Dv): the columns written
   int group;                 // partial slots per KV head, summed in this order
 };
 
@@ -139,6 +143,7 @@ __global__ void __launch_bounds__(256) gqa_reduce_kernel(ReduceParams p) {
       const int y = isk ? x : x - nk;
       const int per = isk ? nk : nv, d8 = isk ? k8 : v8;
       const int key = y / d8, c = y - key * d8;
+      if (c * 8 >= (isk ? p.dqk_act : p.dv_act)) continue;
       const u32x4* src = reinterpret_cast<const u32x4*>(isk ? p.dk_ws : p.dv_ws) +
                          (int64_t)kvhead * p.group * per + y;
       float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};

@@ -19,9 +19,12 @@
  *   lse   : (B, Hq,  Sq)       fp32, natural log; -inf marks a row that saw no key
  * bf16 values are passed as their 16-bit patterns.  All pointers are device pointers; tensor
  * pointers must be 16-byte aligned (lse 4-byte aligned) and the workspace 256-byte aligned; a
- * tensor with no elements may be NULL.  Supported head dims (Dqk, Dv): (64,64), (128,128),
- * (192,128), (256,256).  Empty problems (B, Sq or Skv zero) need no workspace: the gradients that
- * have elements are written as zeros.
+ * tensor with no elements may be NULL.  Head dims ("Support surface"): Dqk and Dv multiples of 8
+ * with 8 <= Dv <= Dqk <= 256.  A call computes on the kernel head dims (Kqk, Kv), the first of
+ * (64,64), (128,128), (192,128), (256,256) that covers (Dqk, Dv): those four run as they are, any
+ * other pair reads the operand columns past its head dims as zeros and writes no column past them
+ * (so the gaps of a strided layout are left untouched).  Empty problems (B, Sq or Skv zero) need
+ * no workspace: the gradients that have elements are written as zeros.
  *
  * Masks ("API Usage" and "Causal, sliding-window, and padding masks"): query q and key k are
  * visible together when q < seq_q, k < seq_kv, causal => k <= q + diag + window_right, and
@@ -46,8 +49,8 @@
  *   3  dQ partials: the main kernel stores one fp32 dQ partial per (KV tile, 32-row q tile) in
  *      the workspace and a second kernel sums them in ascending KV order;
  *   1  deterministic, the library's choice between 2 and 3: 3 where its workspace holds fewer
- *      bytes per (KV tile, q row) (Dqk fp32 partials against the key tile's bf16 dS values),
- *      else 2 (head dim 64 takes 3; 128, 192 and 256 take 2).
+ *      bytes per (KV tile, q row) (Kqk fp32 partials against the key tile's bf16 dS values),
+ *      else 2 (kernel head dim 64 takes 3; 128, 192 and 256 take 2).
  * Routes 1-3 make dq, dk, dv bitwise reproducible run to run; dK and dV are reproducible on every
  * route.  Any other value gives SDPA_BWD_INVALID_ARG.
  */
@@ -79,12 +82,13 @@ enum {
 
 /* Bytes of workspace needed by a call with these arguments: a 256-byte-aligned carve of the
  * per-row statistics (LSE * log2 e and delta, B*Hq*Sq_pad float pairs, Sq_pad = Sq rounded up to
- * 32), then the dQ route's buffer: the fp32 dQ accumulator (B*Hq*Sq*Dqk floats, route 0), the
+ * 32), then the dQ route's buffer: the fp32 dQ accumulator (B*Hq*Sq*Kqk floats, route 0), the
  * bf16 dS panels (B*Hq*Sq_pad*Skv_pad, route 2) or the fp32 dQ partials
- * (B*Hq*(Skv_pad/BC)*Sq_pad*Dqk floats, route 3), where BC is the key tile (256 keys for head
- * dims up to 192, 128 for 256) and Skv_pad is Skv rounded up to BC; then, under GQA or when the
- * main grid splits its q ranges, the bf16 per-(query head, part) dK/dV partials.  Returns 0 for
- * arguments sdpa_bwd rejects and for empty problems. */
+ * (B*Hq*(Skv_pad/BC)*Sq_pad*Kqk floats, route 3), where (Kqk, Kv) are the kernel head dims of
+ * the call (see above), BC is the key tile (256 keys for kernel head dims up to 192, 128 for 256)
+ * and Skv_pad is Skv rounded up to BC; then, under GQA or when the main grid splits its q ranges,
+ * the bf16 per-(query head, part) dK/dV partials (Kqk + Kv per key row).  Returns 0 for arguments
+ * sdpa_bwd rejects and for empty problems. */
 size_t sdpa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv,
                                int causal, int window_left, int deterministic, int has_seqlens);
 

@@ -55,7 +55,11 @@ def test_dq_route_choice(so):
         assert lib.dq_route(*d, 2) == lib.DQ_DS_PANELS
         assert lib.dq_route(*d, 3) == lib.DQ_PARTIALS
         assert lib.dq_route(*d, 4) == -1
-    assert lib.dq_route(96, 96, 0) == -1
+    # head dims that are multiples of 8 up to 256 run on the next supported size
+    assert lib.dq_route(96, 96, 1) == lib.dq_route(128, 128, 1)
+    assert lib.dq_route(40, 40, 1) == lib.dq_route(64, 64, 1)
+    for bad in ((100, 100), (264, 264), (128, 192), (4, 4)):
+        assert lib.dq_route(*bad, 0) == -1
 
 
 def _ws(**kw):
@@ -106,7 +110,11 @@ def test_workspace_size_rules(so):
     assert sizes == sorted(sizes)
     # rejected shapes need nothing
     assert _ws(Hkv=3) == 0
-    assert _ws(Dqk=96, Dv=96) == 0
+    # head dims that are multiples of 8 up to 256 use the next supported size's workspace
+    assert _ws(Dqk=96, Dv=96) == _ws(Dqk=128, Dv=128)
+    assert _ws(Dqk=176, Dv=104) == _ws(Dqk=192, Dv=128)
+    assert _ws(Dqk=160, Dv=160) == _ws(Dqk=256, Dv=256)
+    assert _ws(Dqk=100, Dv=100) == 0 and _ws(Dqk=272, Dv=272) == 0
     assert _ws(Sq=0) == 0
 
 
@@ -128,7 +136,9 @@ def test_rejections_before_launch(so):
     assert _call(so, wr=-1) == lib.INVALID_ARG
     assert _call(so, det=4) == lib.INVALID_ARG                    # unknown dQ route
     assert _call(so, det=-1) == lib.INVALID_ARG
-    assert _call(so, Dqk=96, Dv=96) == lib.UNSUPPORTED            # head dims outside the set
+    assert _call(so, Dqk=100, Dv=100) == lib.UNSUPPORTED          # not a multiple of 8
+    assert _call(so, Dqk=264, Dv=264) == lib.UNSUPPORTED          # above 256
+    assert _call(so, Dqk=96, Dv=96) == lib.INVALID_ARG            # served as 128: no workspace
     assert _call(so, Dqk=128, Dv=192) == lib.UNSUPPORTED          # D_v > D_qk
     assert _call(so, q=ctypes.c_void_p(4098)) == lib.UNSUPPORTED  # misaligned pointer
     assert _call(so, dk=None) == lib.INVALID_ARG                  # null output
@@ -184,7 +194,7 @@ def test_flex_rejections_before_launch(so):
 
 def test_preprocess_rejections(so):
     p = ctypes.c_void_p(4096)
-    assert so.sdpa_bwd_preprocess(p, p, p, p, None, None, 1, 1, 8, 96, 96, None) == lib.UNSUPPORTED
+    assert so.sdpa_bwd_preprocess(p, p, p, p, None, None, 1, 1, 8, 100, 100, None) == lib.UNSUPPORTED
     assert so.sdpa_bwd_preprocess(None, p, p, p, None, None, 1, 1, 8, 128, 128, None) == lib.INVALID_ARG
     assert so.sdpa_bwd_preprocess(p, p, p, None, None, None, 1, 1, 8, 128, 128, None) == lib.INVALID_ARG
 
