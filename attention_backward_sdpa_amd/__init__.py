@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libsdpa_bwd.so")
 OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, LAUNCH_FAILED = 0, 1, 2, 3, 4
 BF16, FP16, FP32 = 0, 1, 2
 # values of the `deterministic` argument (dQ routes); False / True are 0 / 1
-DQ_ATOMIC, DQ_DETERMINISTIC, DQ_DS_PANELS, DQ_PARTIALS = 0, 1, 2, 3
+DQ_ATOMIC, DQ_DETERMINISTIC, DQ_DS_PANELS, DQ_PARTIALS, DQ_RELAY = 0, 1, 2, 3, 4
 
 
 class Layout(ctypes.Structure):
@@ -117,7 +117,7 @@ def workspace_size(B, Hq, Hkv, Sq, Skv, Dqk, Dv, causal=False, window_left=-1,
 
 
 def dq_route(Dqk, Dv, deterministic) -> int:
-    """sdpa_bwd_dq_route(): the dQ route (DQ_ATOMIC, DQ_DS_PANELS or DQ_PARTIALS) a call takes,
+    """sdpa_bwd_dq_route(): the dQ route (DQ_ATOMIC, DQ_DS_PANELS, DQ_PARTIALS or DQ_RELAY) a call takes,
     -1 for unsupported arguments."""
     return int(_load().sdpa_bwd_dq_route(int(Dqk), int(Dv), int(deterministic)))
 

@@ -14,7 +14,10 @@
 //   * of the unscaled bf16 dS tile (GEMM4 moves to the dq2k kernel, which reduces in ascending KV
 //     order), or
 //   * of GEMM4's fp32 result, one 32 x Dqk dQ partial per (KV tile, q tile), which the dq_reduce
-//     kernel sums in ascending KV order.
+//     kernel sums in ascending KV order,
+// or keep GEMM4 and pass one running fp32 sum per (query head, q tile) from KV tile to KV tile in
+// ascending order ("Deterministic vs. non-deterministic dQ", ordered-reduction relay; see the
+// relay notes below).
 //
 // MI355X mapping (differs from the pages' SM120 warp-specialised design):
 //   * NW waves of 64 lanes; wave w owns KPW = 32 keys, so the key tile is BC = 32 * NW.  At head
@@ -80,6 +83,11 @@ struct MainParams {
   int64_t bias_bstride;     // elements between batch entries of bias / dbias (0 for Bb = 1)
   int bias_f32;             // bias elements are fp32 (else the io type)
   int dbias_atomic;         // dBias accumulates over batch entries (Bb = 1, B > 1): fp32 atomics
+  // ordered relay (DQ_RELAY)
+  float* relay_acc;         // (B*Hq, sq_pad/32) blocks of 32 x Dqk fp32: the running dQ sums
+  int* relay_turn;          // (B*Hq, sq_pad/32): KV tiles that have added into each sum (zeroed)
+  int* relay_ctl;           // [0, 8) per-XCD item tickets, [8] items done, [9] waits abandoned
+  int relay_queues;         // XCDs of the device (1..8): one item queue each
 };
 
 // How the main kernel emits dQ.
@@ -87,6 +95,7 @@ enum DqMode {
   DQ_ATOMIC = 0,   // GEMM4 in the kernel, fp32 atomic adds into dq_accum
   DQ_DS = 1,       // no GEMM4: bf16 dS tiles to the workspace (dq2k reduces)
   DQ_PARTIAL = 2,  // GEMM4 in the kernel, fp32 partial tiles to the workspace (dq_reduce sums)
+  DQ_RELAY = 3,    // GEMM4 in the kernel, added in ascending KV order into one fp32 sum per q tile
 };
 
 template <int DQK_, int DV_, int KPW_, int NW_, int MODE_, bool F16_ = false, int BIAS_ = 0,
@@ -130,15 +139,20 @@ struct MainCfg {
   static constexpr int TILE_BYTES = T_ST + 2 * BR * 4;
   static constexpr int SK_BYTES = KLDS ? BC * DQK * 2 : 0;
   static constexpr int SST_BYTES = G4 ? BC * BR * 2 : 0;
-  static constexpr int NBUF = (SK_BYTES + 2 * TILE_BYTES + SST_BYTES <= 160 * 1024) ? 2 : 1;
+  // relay: the running sum of the next q tile, staged one iteration ahead (each wave stages the
+  // parts of the block its GEMM4 adds to)
+  static constexpr int RS_BYTES = MODE == DQ_RELAY ? BR * DQK * 4 : 0;
+  static constexpr int NBUF =
+      (SK_BYTES + 2 * TILE_BYTES + SST_BYTES + RS_BYTES <= 160 * 1024) ? 2 : 1;
   // dS staging for GEMM4, double-buffered by q-tile parity where LDS allows: GEMM4 of the previous
   // q tile then needs no barrier of its own and overlaps the other waves' work
   static constexpr int NSST =
-      (G4 && SK_BYTES + NBUF * TILE_BYTES + 2 * SST_BYTES <= 160 * 1024) ? 2 : 1;
+      (G4 && SK_BYTES + NBUF * TILE_BYTES + 2 * SST_BYTES + RS_BYTES <= 160 * 1024) ? 2 : 1;
   static constexpr int OFF_K = 0;
   static constexpr int OFF_T = OFF_K + SK_BYTES;
   static constexpr int OFF_ST = OFF_T + NBUF * TILE_BYTES;
-  static constexpr int LDS_BYTES = OFF_ST + NSST * SST_BYTES;
+  static constexpr int OFF_RS = OFF_ST + NSST * SST_BYTES;
+  static constexpr int LDS_BYTES = OFF_RS + RS_BYTES;
   static_assert(KPW == 32, "one 32-key MFMA tile per wave (the q-tile loop body assumes it)");
   static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
   static_assert(DQK % 64 == 0 && DV % 64 == 0, "head dims must be multiples of 64");
@@ -176,6 +190,16 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint32_t off, void* lds_wave_bas
   const uint32_t l = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base);
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(r), "s"(l)
+               : "memory", "m0");
+}
+// The same at device scope (sc1): the load is coherent with the device-scope stores of other CUs
+// and XCDs (the relay's running sums)
+__device__ __forceinline__ void dma16_dev(rsrc_t r, uint32_t off, void* lds_wave_base) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen sc1 lds"
                :
                : "v"(off), "s"(r), "s"(l)
                : "memory", "m0");
@@ -449,13 +473,69 @@ struct Gemm4Lanes16 {
   }
 };
 
+// ---- ordered relay ("Deterministic vs. non-deterministic dQ", ordered-reduction relay) ----------
+// The KV tiles that see q tile i of a query head add their GEMM4 results into one fp32 running sum
+// of that (head, q tile), in ascending KV order; turn[head, i] counts the KV tiles that have added.
+// The visitors of a q tile are contiguous in KV index (both ends of a key tile's q-tile range grow
+// with the key tile), so key tile j's turn at q tile i is j - jfirst(i), jfirst(i) being the first
+// visitor, which stores its result without reading.  The sum of a (head, q tile) block uses the
+// dQ-partial block layout of GEMM4 (below).  On MI355X:
+//   * forward progress: a workgroup does not work on the item of its blockIdx but takes the next
+//     ticket of its XCD's queue once it runs, and an item only ever waits for items earlier in the
+//     same queue.  The earliest unfinished item is therefore held by a running workgroup that waits
+//     for nothing unfinished, whatever order the workgroups are dispatched in.
+//   * coherence: sums and turns are written and read with device-scope (sc1) accesses only, which
+//     miss the CU's L1 and are coherent across the device; the turn is published once every wave's
+//     stores of the sum have completed.  No cache-wide writeback or invalidation is needed.  (XCD
+//     x's queue holds the query heads bh with bh % queues == x, as the blockIdx order of the other
+//     routes does, so a head's K/V and Q/dO stay in one L2.)
+//   * the successor stages the sum into LDS with LDS-DMA loads one q tile ahead (after waiting for
+//     its turn), together with the next tile's operands, and adds it in GEMM4.
+//   * a wait longer than kRelaySpinLimit polls is abandoned and counted in ctl[9]; once that has
+//     happened the other waits end at once, so every launch finishes (the dQ conversion then
+//     writes NaN).
+constexpr int kRelaySpinLimit = 1 << 18;
+constexpr int kHwregXccId = 20 | (0 << 6) | (3 << 11);  // hwreg(HW_REG_XCC_ID, 0, 4)
+constexpr int kSc1 = 16;  // cache-policy operand of the buffer builtins: sc1 (device scope)
+
+// Wave-uniform wait until *turn >= want.
+__device__ __forceinline__ void relay_wait(int* turn, int want, int* ctl, int lane) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(turn, (short)0, 4, 0x00020000);
+  for (int n = 0;; ++n) {
+    const int v = __builtin_amdgcn_readfirstlane((int)__builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, kSc1));
+    if (v >= want) return;
+    if ((n & 63) == 63 &&
+        (n >= kRelaySpinLimit ||
+         __hip_atomic_load(ctl + 9, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)) {
+      if (n >= kRelaySpinLimit && lane == 0)
+        __hip_atomic_fetch_add(ctl + 9, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Publish a turn (one lane), device scope.
+__device__ __forceinline__ void relay_publish(int* turn, int value) {
+  __builtin_amdgcn_raw_buffer_store_b32(
+      value, __builtin_amdgcn_make_buffer_rsrc(turn, (short)0, 4, 0x00020000), 0, 0, kSc1);
+}
+
+// Store 16 bytes of a running sum (a block of `bytes` at base), device scope.
+__device__ __forceinline__ void relay_store16(float* base, int bytes, int byte_off, floatx4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(
+      __builtin_bit_cast(u32x4, v), __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000),
+      byte_off, 0, kSc1);
+}
+
 // GEMM4 for one q tile on 16 x 16 blocks (C::G4_16): wave w computes blocks w + NW m, m < NB4,
 // block b = (row half b % 2, 16-column block b / 2).  Emission as in gemm4 below, with the
 // partial block's layout: block (h, cb) is 1 KiB at float offset 256 (h (Dqk / 16) + cb), lane l's
 // four floats (rows 16h + 4 (l / 16) + 0..3, column 16 cb + l % 16) the 16 bytes at 4 l.
 template <class C>
 __device__ __forceinline__ void gemm4_16(const char* sST, const char* sK, float* dst, int q0,
-                                         int Lq, int w, int lane) {
+                                         int Lq, int w, int lane, const char* rs = nullptr,
+                                         bool add = false) {
   using M16 = Mfma16<C::F16>;
   constexpr int DQK = C::DQK, NB = C::NB4, NW = C::NW;
   const Gemm4Lanes16 tl(lane, w);
@@ -474,6 +554,12 @@ __device__ __forceinline__ void gemm4_16(const char* sST, const char* sK, float*
     const int cb = (w + NW * m) >> 1;
     if constexpr (C::MODE == DQ_PARTIAL) {
       __builtin_nontemporal_store(acc[m], reinterpret_cast<floatx4*>(dst + (h * (DQK / 16) + cb) * 256) + lane);
+    } else if constexpr (C::MODE == DQ_RELAY) {
+      // the running sum (staged in LDS at the block's offset) plus this key tile's block
+      const int off = (h * (DQK / 16) + cb) * 256;
+      floatx4 v = acc[m];
+      if (add) v += reinterpret_cast<const floatx4*>(rs)[off / 4 + lane];
+      relay_store16(dst, C::BR * DQK * 4, (off + 4 * lane) * 4, v);
     } else {
       float* col0 = dst + 16 * cb + col_l;
 #pragma unroll
@@ -498,10 +584,12 @@ __device__ __forceinline__ void gemm4_16(const char* sST, const char* sK, float*
 //     4 KiB at float offset 1024 dt, lane l's accumulator registers 4x .. 4x + 3 (rows
 //     8x + 4(l / 32) + 0..3, column 32 dt + l % 32) being the 16 bytes at float offset
 //     256 x + 4 l, so every store instruction writes 1 KiB contiguously.  Rows past Lq hold the
-//     products of their cleared dS (zeros); the reduction does not use them.
+//     products of their cleared dS (zeros); the reduction does not use them;
+//   * DQ_RELAY: the same block layout, as the running sum of the (head, q tile): the block plus
+//     the sum staged in LDS at `rs` (when `add`), stored at device scope.
 template <class C>
 __device__ __forceinline__ void gemm4(const char* sST, const char* sK, float* dst, int q0, int Lq,
-                                      int w, int lane) {
+                                      int w, int lane, const char* rs = nullptr, bool add = false) {
   using M = typename C::M;
   using acc_t = typename M::acc_t;
   constexpr int DQK = C::DQK;
@@ -518,6 +606,15 @@ __device__ __forceinline__ void gemm4(const char* sST, const char* sK, float* ds
       for (int x = 0; x < 4; ++x)
         __builtin_nontemporal_store(floatx4{acc[4 * x], acc[4 * x + 1], acc[4 * x + 2], acc[4 * x + 3]},
                                     blk + 64 * x);
+    } else if constexpr (C::MODE == DQ_RELAY) {
+      // the running sum (staged in LDS in the block layout) plus this key tile's block
+      const floatx4* stg = reinterpret_cast<const floatx4*>(rs) + dt * 256 + lane;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        floatx4 v = floatx4{acc[4 * x], acc[4 * x + 1], acc[4 * x + 2], acc[4 * x + 3]};
+        if (add) v += stg[64 * x];
+        relay_store16(dst, C::BR * DQK * 4, (dt * 1024 + 256 * x + 4 * lane) * 4, v);
+      }
     } else {
       float* row0 = dst + dt * 32 + lc;
       if (full) {
@@ -558,8 +655,25 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
   // range) first: causal tiles near the start see the most q tiles.  Consecutive blocks are
   // different heads, so the 8 XCDs split the heads.
   const int nbh = p.B * p.Hq;
-  const int bh = blockIdx.x % nbh;
-  const int js = blockIdx.x / nbh;
+  int item = blockIdx.x;
+  if constexpr (C::MODE == DQ_RELAY) {
+    // the relay takes the next item of this XCD's queue instead (same order within a queue; see
+    // the relay notes): queue x holds the heads bh = x, x + queues, ... of every key tile
+    __shared__ int s_item;
+    if (tid == 0) {
+      const int nq = p.relay_queues;
+      const int x = (int)((unsigned)__builtin_amdgcn_s_getreg(kHwregXccId) % (unsigned)nq);
+      const int t = __hip_atomic_fetch_add(p.relay_ctl + x, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      const int nbh_x = (nbh - x + nq - 1) / nq;
+      s_item = t < p.n_kv_tiles * p.n_split * nbh_x ? (t / nbh_x) * nbh + x + nq * (t % nbh_x) : -1;
+    }
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(s_item);
+    if (item < 0) return;  // more workgroups than items on this XCD
+  }
+  const int bh = item % nbh;
+  const int js = item / nbh;
   const int j = js / p.n_split, part = js % p.n_split;
   const int h = bh % p.Hq, b = bh / p.Hq;
   const int kvh = h / p.group;
@@ -587,9 +701,14 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
   auto dq_dst = [&](int i) -> float* {
     if constexpr (C::MODE == DQ_PARTIAL)
       return p.dqp_ws + (((int64_t)bh * p.n_kv_tiles + j) * n_q_tiles + i) * (BR * DQK);
+    else if constexpr (C::MODE == DQ_RELAY)
+      return p.relay_acc + ((int64_t)bh * n_q_tiles + i) * (BR * DQK);
     else
       return p.dq_accum + (q_row0 + (int64_t)i * BR) * DQK;
   };
+  // relay: this key tile's turn at q tile i, and the turn counter
+  auto relay_rank = [&](int i) { return j - first_kv_tile(mg, i, BR, BC); };
+  auto relay_turn = [&](int i) { return p.relay_turn + (int64_t)bh * n_q_tiles + i; };
   const bf16_t* Kb = p.k + b * p.sk.b + kvh * p.sk.h;
   const bf16_t* Vb = p.v + b * p.sv.b + kvh * p.sv.h;
   const bf16_t* Qb = p.q + b * p.sq.b + h * p.sq.h;
@@ -735,12 +854,46 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
     };
     load_bias(i_hi, bcur);
 
+    // relay: the LDS copy of a running sum, and the staging of this wave's parts of it (the
+    // 1 KiB chunks its GEMM4 adds to: 32 x 32 d tiles dt = w, w + NW, ..., or the 16 x 16 blocks
+    // of gemm4_16), after waiting for this key tile's turn
+    const char* rs = smem + C::OFF_RS;
+    auto relay_stage = [&](int i_t) {
+      if constexpr (C::MODE == DQ_RELAY) {
+        const int rk = relay_rank(i_t);
+        const bool has_part = C::G4_16 || w < C::N_DQT;
+        if (rk > 0 && has_part) {
+          relay_wait(relay_turn(i_t), rk, p.relay_ctl, lane);
+          const rsrc_t src = buf_rsrc(dq_dst(i_t), BR * DQK * 4);
+          char* dstl = smem + C::OFF_RS;
+          if constexpr (C::G4_16) {
+#pragma unroll
+            for (int m = 0; m < C::NB4; ++m) {
+              const int off = ((w & 1) * (DQK / 16) + ((w + C::NW * m) >> 1)) * 1024;
+              dma16_dev(src, off + lane * 16, dstl + off);
+            }
+          } else {
+            for (int dt = w; dt < C::N_DQT; dt += C::NW)
+#pragma unroll
+              for (int x = 0; x < 4; ++x) {
+                const int off = dt * 4096 + x * 1024;
+                dma16_dev(src, off + lane * 16, dstl + off);
+              }
+          }
+        }
+      }
+    };
+
     for (int i = i_hi; i >= i_lo; --i) {
       const int q0 = i * BR;
       const char* T = tile(i);
       const float* sStat = reinterpret_cast<const float*>(T + C::T_ST);
       wait_vmem();      // this wave's loads of tile i (and its older atomics / stores) are done
       lds_barrier();    // tile i landed everywhere; every wave is done with the previous tile
+      if constexpr (C::MODE == DQ_RELAY) {
+        // every wave's sums of q tile i + 2 (stored in the previous iteration) are complete
+        if (tid == 0 && i + 2 <= i_hi) relay_publish(relay_turn(i + 2), relay_rank(i + 2) + 1);
+      }
       if (C::NBUF == 2 && i > i_lo) load_tile(i - 1);
       if constexpr (C::DS_OUT) {
         if (i < i_hi) store_ds(i + 1);
@@ -754,14 +907,18 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
         // GEMM4 of the previous q tile (dS in sST), deferred so its atomics / partial stores
         // overlap this tile
         if (i < i_hi) {
+          const bool add = C::MODE == DQ_RELAY && relay_rank(i + 1) > 0;
           if constexpr (C::G4_16)
-            gemm4_16<C>(sST(i + 1), sK, dq_dst(i + 1), q0 + BR, mg.Lq, w, lane);
+            gemm4_16<C>(sST(i + 1), sK, dq_dst(i + 1), q0 + BR, mg.Lq, w, lane, rs, add);
           else
-            gemm4<C>(sST(i + 1), sK, dq_dst(i + 1), q0 + BR, mg.Lq, w, lane);
+            gemm4<C>(sST(i + 1), sK, dq_dst(i + 1), q0 + BR, mg.Lq, w, lane, rs, add);
           // single buffer: every wave is done reading it before this tile's dS overwrites it
           // (the atomics / stores keep draining)
           if constexpr (C::NSST == 1) lds_barrier();
         }
+        // relay: once the key tile before this one has added into q tile i's sum, stage that sum
+        // (this wave's parts of it) for GEMM4 of tile i in the next iteration
+        if constexpr (C::MODE == DQ_RELAY) relay_stage(i);
       }
 
       // ---- the wave's 32 keys: GEMM1, GEMM2, softmax replay, dS, GEMM3, GEMM5 --------------------
@@ -850,12 +1007,26 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
     if constexpr (C::DS_OUT) store_ds(i_lo);
     store_dbias(i_lo);
     if constexpr (C::G4) {
+      if constexpr (C::MODE == DQ_RELAY) wait_vmem();  // the staged sum of q tile i_lo
       lds_barrier();  // the last tile's dS is complete
+      const bool add = C::MODE == DQ_RELAY && relay_rank(i_lo) > 0;
       if constexpr (C::G4_16)
-        gemm4_16<C>(sST(i_lo), sK, dq_dst(i_lo), i_lo * BR, mg.Lq, w, lane);
+        gemm4_16<C>(sST(i_lo), sK, dq_dst(i_lo), i_lo * BR, mg.Lq, w, lane, rs, add);
       else
-        gemm4<C>(sST(i_lo), sK, dq_dst(i_lo), i_lo * BR, mg.Lq, w, lane);
+        gemm4<C>(sST(i_lo), sK, dq_dst(i_lo), i_lo * BR, mg.Lq, w, lane, rs, add);
     }
+    if constexpr (C::MODE == DQ_RELAY) {
+      wait_vmem();  // this wave's sums of q tiles i_lo + 1 and i_lo are stored
+      lds_barrier();
+      if (tid == 0) {
+        if (i_lo + 1 <= i_hi) relay_publish(relay_turn(i_lo + 1), relay_rank(i_lo + 1) + 1);
+        relay_publish(relay_turn(i_lo), relay_rank(i_lo) + 1);
+      }
+    }
+  }
+  if constexpr (C::MODE == DQ_RELAY) {
+    if (tid == 0)
+      __hip_atomic_fetch_add(p.relay_ctl + 8, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- epilogue: dK (scaled) and dV, written once; keys past the sequence are zero -------------

@@ -33,6 +33,11 @@ struct DqReduceParams {
   int bc;               // keys per KV tile of the main kernel
   int dqk_act;          // dQ head dim (<= DQK): the columns written
   float scale;
+  // relay route: dqp_ws holds one finished sum per (head, q tile) (n_kv_tiles = 1), present when
+  // the tile has a visitor; relay_ctl[8] must equal relay_items and relay_ctl[9] be 0, else every
+  // dQ element is written as NaN
+  const int* relay_ctl;
+  int relay_items;
 };
 
 template <int DQK, bool F16, bool L16>
@@ -76,6 +81,15 @@ __global__ void __launch_bounds__(DQK * 2) dq_reduce_kernel(DqReduceParams p) {
     q_tile_range(mg, j * p.bc, p.bc, BR, &lo, &hi);
     return lo <= i && i <= hi;
   };
+  bool bad = false;
+  if (p.relay_ctl) {
+    // the relay's sum of this q tile, present when its first possible visitor saw it
+    bad = p.relay_ctl[8] != p.relay_items || p.relay_ctl[9] != 0;
+    const int jf = first_kv_tile(mg, i, BR, p.bc);
+    const bool any = jlo <= jhi && stored(jf);
+    jlo = 0;
+    jhi = any ? 0 : -1;
+  }
 
   const int64_t blk = (int64_t)BR * DQK / 4;  // float4s per block
   const floatx4* src = reinterpret_cast<const floatx4*>(p.dqp_ws) +
@@ -92,7 +106,7 @@ __global__ void __launch_bounds__(DQK * 2) dq_reduce_kernel(DqReduceParams p) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (j0 + u <= jhi && stored(j0 + u)) {
+      if (j0 + u <= jhi && (p.relay_ctl || stored(j0 + u))) {
 #pragma unroll
         for (int x = 0; x < 4; ++x) s[x] += v[u][x];
       }
@@ -123,7 +137,10 @@ __global__ void __launch_bounds__(DQK * 2) dq_reduce_kernel(DqReduceParams p) {
     const int r = c / V, cv = c % V, q = q0 + r;
     if (q >= p.Sq || cv * 8 >= p.dqk_act) continue;
     u32x4 out = u32x4{0u, 0u, 0u, 0u};
-    if (q < mg.Lq) {
+    if (bad) {
+      const uint32_t nan2 = Elem<F16>::pack2(__builtin_nanf(""), __builtin_nanf(""));
+      out = u32x4{nan2, nan2, nan2, nan2};
+    } else if (q < mg.Lq) {
       const floatx4 a = *reinterpret_cast<const floatx4*>(sT + r * ROWF + cv * 8);
       const floatx4 d = *reinterpret_cast<const floatx4*>(sT + r * ROWF + cv * 8 + 4);
       out = u32x4{Elem<F16>::pack2(a[0], a[1]), Elem<F16>::pack2(a[2], a[3]),

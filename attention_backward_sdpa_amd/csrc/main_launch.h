@@ -1,5 +1,5 @@
 // Launch of the fused main kernel (bwd_main.h) for one kernel head dim.  Each head dim's
-// instantiations (3 dQ modes x bf16/fp16 x bias none/bias/dBias x exact/padded head dims) live in
+// instantiations (4 dQ modes x bf16/fp16 x bias none/bias/dBias x exact/padded head dims) live in
 // a translation unit of their own (main_d<DQK>.hip), so the library's objects compile in
 // parallel; the host side (sdpa_bwd.hip) calls launch_main_dqk<DQK>.
 #pragma once
@@ -42,6 +42,8 @@ hipError_t launch_main_mode(const MainParams& mp, DqMode mode, int grid, hipStre
     return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_DS, F16, BIAS, PAD>>(mp, grid, s);
   if (mode == DQ_PARTIAL)
     return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_PARTIAL, F16, BIAS, PAD>>(mp, grid, s);
+  if (mode == DQ_RELAY)
+    return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_RELAY, F16, BIAS, PAD>>(mp, grid, s);
   return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_ATOMIC, F16, BIAS, PAD>>(mp, grid, s);
 }
 

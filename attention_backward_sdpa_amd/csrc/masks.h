@@ -49,6 +49,15 @@ __host__ __device__ __forceinline__ void q_tile_range(const MaskGeom& m, int k0,
   *hi = qhi / BR;
 }
 
+// The first key tile (BC keys) that sees q tile i (BR rows), when any does: the key tiles that see
+// a q tile are contiguous, and only a left window moves the first of them off tile 0
+// ("SDPA Backward (SM120)", "Deterministic vs. non-deterministic dQ", the relay's turn offset).
+__host__ __device__ __forceinline__ int first_kv_tile(const MaskGeom& m, int i, int BR, int BC) {
+  if (m.W < 0) return 0;
+  const int t = i * BR + m.diag - m.W;
+  return t > 0 ? t / BC : 0;
+}
+
 // Does tile (q0 .. q0+BR-1) x (k0 .. k0+BC-1) contain any masked pair?
 __host__ __device__ __forceinline__ bool tile_needs_mask(const MaskGeom& m, int q0, int BR, int k0,
                                                          int BC) {

@@ -85,8 +85,9 @@ int q_split(int B, int Hq, int Sq, int Skv, const Geometry& g) {
 // dQ routes.  The `deterministic` argument: 0 fp32 atomics, 1 deterministic (the fp32 dQ partials
 // where they are a smaller workspace stream per (KV tile, q row) than the BC bf16 dS values, else
 // the dS panels: at equal bytes, head dim 128, the dS-panel chain measured faster on MI355X),
-// 2 dS panels + dq2k, 3 fp32 dQ partials + dq_reduce.
-enum Route { R_ATOMIC = 0, R_DS = 1, R_DQP = 2, R_INVALID = -1 };
+// 2 dS panels + dq2k, 3 fp32 dQ partials + dq_reduce, 4 the ordered relay (one running fp32 sum
+// per q tile, passed from key tile to key tile in ascending order).
+enum Route { R_ATOMIC = 0, R_DS = 1, R_DQP = 2, R_RELAY = 3, R_INVALID = -1 };
 
 Route route_for(int deterministic, int Dqk, const Geometry& g) {
   switch (deterministic) {
@@ -94,12 +95,27 @@ Route route_for(int deterministic, int Dqk, const Geometry& g) {
     case 1: return (int64_t)Dqk * 4 < (int64_t)g.bc * 2 ? R_DQP : R_DS;
     case 2: return R_DS;
     case 3: return R_DQP;
+    case 4: return R_RELAY;
     default: return R_INVALID;
   }
 }
 
+// Item queues of the relay: one per XCD of the current device (1..8), queried once per device.
+int relay_queues() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 1;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 1;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || n < 1) n = 1;
+  n = n > 8 ? 8 : n;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
 struct Carve {
   int64_t stats = 0, dq_accum = -1, ds = -1, dqp = -1, dk_ws = -1, dv_ws = -1, total = 0;
+  int64_t relay_turn = -1, relay_ctl = -1;
   int64_t sq_pad = 0, skv_pad = 0;
 };
 
@@ -117,6 +133,13 @@ Carve carve(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv, Route rout
   } else if (route == R_DS) {
     c.ds = off;
     off = align_up(off + (int64_t)B * Hq * c.skv_pad * c.sq_pad * 2, kAlign);
+  } else if (route == R_RELAY) {  // one 32 x Dqk fp32 running sum per (b, h, q tile)
+    c.dqp = off;
+    off = align_up(off + (int64_t)B * Hq * c.sq_pad * Dqk * 4, kAlign);
+    c.relay_turn = off;  // one turn counter per (b, h, q tile)
+    off = align_up(off + (int64_t)B * Hq * (c.sq_pad / g.br) * 4, kAlign);
+    c.relay_ctl = off;   // 16 control words
+    off = align_up(off + 16 * 4, kAlign);
   } else {  // one 32 x Dqk fp32 block per (b, h, KV tile, q tile)
     c.dqp = off;
     off = align_up(off + (int64_t)B * Hq * (c.skv_pad / g.bc) * c.sq_pad * Dqk * 4, kAlign);
@@ -207,7 +230,10 @@ hipError_t launch_dq2k(const Dq2kParams& dp, int grid, hipStream_t s) {
 // bias: 0 none, 1 bias, 2 bias and dBias (the 4-wave layout of geometry_for).
 hipError_t run_main(int Dqk, const MainParams& mp, Route route, bool f16, int bias, int grid,
                     int bc, hipStream_t s) {
-  const DqMode mode = route == R_DS ? DQ_DS : route == R_DQP ? DQ_PARTIAL : DQ_ATOMIC;
+  const DqMode mode = route == R_DS    ? DQ_DS
+                      : route == R_DQP ? DQ_PARTIAL
+                      : route == R_RELAY ? DQ_RELAY
+                                         : DQ_ATOMIC;
   if (Dqk == 64) return launch_main_dqk<64>(mp, mode, f16, bias, grid, bc, s);
   if (Dqk == 128) return launch_main_dqk<128>(mp, mode, f16, bias, grid, bc, s);
   if (Dqk == 192) return launch_main_dqk<192>(mp, mode, f16, bias, grid, bc, s);
@@ -418,6 +444,8 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   pp.Dqk = KDqk;
   pp.dv_act = Dv;
   pp.zero_rows = route == R_ATOMIC ? 1 : 0;
+  pp.relay_turn = route == R_RELAY ? (int*)(ws + c.relay_turn) : nullptr;
+  pp.relay_ctl = route == R_RELAY ? (int*)(ws + c.relay_ctl) : nullptr;
   e = launch_preprocess(pp, KDv, f16, (int64_t)B * Hq * (c.sq_pad / geo.br), stream);
   if (e == hipSuccess) e = launch_dsink(stats, (int)c.sq_pad, false);
   if (e == hipSuccess && ba.dbias) {
@@ -459,6 +487,10 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   mp.dq_accum = dq_accum;
   mp.ds_ws = route == R_DS ? (bf16_t*)(ws + c.ds) : nullptr;
   mp.dqp_ws = route == R_DQP ? (float*)(ws + c.dqp) : nullptr;
+  mp.relay_acc = route == R_RELAY ? (float*)(ws + c.dqp) : nullptr;
+  mp.relay_turn = pp.relay_turn;
+  mp.relay_ctl = pp.relay_ctl;
+  mp.relay_queues = 1;
   mp.dk_out = partials ? (bf16_t*)(ws + c.dk_ws) : (bf16_t*)dk;
   mp.dv_out = partials ? (bf16_t*)(ws + c.dv_ws) : (bf16_t*)dv;
   mp.seq_q_lens = seq_q_lens;
@@ -487,7 +519,15 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   mp.bias_bstride = ba.batch == 1 ? 0 : (int64_t)Hq * Sq * Skv;
   mp.bias_f32 = ba.dtype == SDPA_BWD_FP32 ? 1 : 0;
   mp.dbias_atomic = dbias_atomic ? 1 : 0;
-  const int64_t main_grid = (int64_t)mp.n_kv_tiles * split * B * Hq;
+  int64_t main_grid = (int64_t)mp.n_kv_tiles * split * B * Hq;
+  const int64_t relay_items = main_grid;
+  if (route == R_RELAY) {
+    // one item queue per XCD; every XCD gets as many workgroups as its longest queue (workgroups
+    // are spread over the XCDs round-robin; those without an item exit at once)
+    const int nq = relay_queues();
+    mp.relay_queues = nq;
+    main_grid = (int64_t)nq * mp.n_kv_tiles * split * (((int64_t)B * Hq + nq - 1) / nq);
+  }
   if (main_grid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
   e = run_main(KDqk, mp, route, f16, has_bias ? (ba.dbias ? 2 : 1) : 0, (int)main_grid, geo.bc,
                stream);
@@ -536,9 +576,9 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     if (cgrid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
     e = launch_convert(cp, KDqk, f16, (int)cgrid, stream);
     if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
-  } else if (route == R_DQP) {
+  } else if (route == R_DQP || route == R_RELAY) {
     DqReduceParams rp;
-    rp.dqp_ws = mp.dqp_ws;
+    rp.dqp_ws = route == R_RELAY ? mp.relay_acc : mp.dqp_ws;
     rp.dq = (bf16_t*)dq;
     rp.sdq = L.t[T_DQ];
     rp.seq_q_lens = seq_q_lens;
@@ -551,11 +591,13 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     rp.window_left = window_left;
     rp.window_right = mp.window_right;
     rp.bottom_right = mp.bottom_right;
-    rp.n_kv_tiles = mp.n_kv_tiles;
+    rp.n_kv_tiles = route == R_RELAY ? 1 : mp.n_kv_tiles;
     rp.n_q_tiles = (int)(c.sq_pad / geo.br);
     rp.bc = geo.bc;
     rp.dqk_act = Dqk;
     rp.scale = scale;
+    rp.relay_ctl = route == R_RELAY ? mp.relay_ctl : nullptr;
+    rp.relay_items = (int)relay_items;
     const int64_t rgrid = (int64_t)B * Hq * rp.n_q_tiles;
     if (rgrid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
     e = launch_dq_reduce(rp, KDqk, f16, (int)rgrid, stream);
@@ -617,6 +659,7 @@ int sdpa_bwd_dq_route(int Dqk, int Dv, int deterministic) {
     case R_ATOMIC: return SDPA_BWD_DQ_ATOMIC;
     case R_DS: return SDPA_BWD_DQ_DS_PANELS;
     case R_DQP: return SDPA_BWD_DQ_PARTIALS;
+    case R_RELAY: return SDPA_BWD_DQ_RELAY;
     default: return -1;
   }
 }

@@ -28,6 +28,8 @@ struct PreParams {
   int Hq, Sq, sq_pad, Dqk;   // Dqk: the dq_accum row length (the kernel's head dim)
   int dv_act;                // O / dO head dim (<= DV); the row dot covers these columns
   int zero_rows;
+  int* relay_turn;           // (B*Hq, sq_pad/32) turn counters of the relay route, zeroed, or null
+  int* relay_ctl;            // the relay's 16 control words, zeroed by workgroup 0, or null
 };
 
 template <int DV, bool F16>
@@ -44,6 +46,8 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
   const bf16_t* ob = p.o + b * p.so.b + h * p.so.h;
   const bf16_t* dob = p.dO + b * p.sdo.b + h * p.sdo.h;
   const int Lq = p.seq_q_lens ? min(max(p.seq_q_lens[b], 0), p.Sq) : p.Sq;
+  if (p.relay_turn && tid == 0) p.relay_turn[blockIdx.x] = 0;
+  if (p.relay_ctl && blockIdx.x == 0 && tid < 16) p.relay_ctl[tid] = 0;
 
   for (int r0 = 0; r0 < BR; r0 += RPP) {
     const int r = r0 + tid / LPR, sub = tid % LPR, s = q0 + r;

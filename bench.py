@@ -33,8 +33,9 @@ from attention_backward_sdpa_amd import synth  # noqa: E402
 METRIC = "attention-backward TFLOP/s and % of bf16 MFMA peak, S=4096 D=128 causal"
 # dQ routes as sdpa_bwd_dq_route() reports them, and the kernel that ends each chain
 ROUTE_NAMES = {0: "fp32 atomic", 2: "deterministic: dS panels + dq2k",
-               3: "deterministic: fp32 dQ partials + ordered reduction"}
-ROUTE_STAGE = {0: "dq_convert", 2: "dq2k", 3: "dq_reduce"}
+               3: "deterministic: fp32 dQ partials + ordered reduction",
+               4: "deterministic: ordered relay"}
+ROUTE_STAGE = {0: "dq_convert", 2: "dq2k", 3: "dq_reduce", 4: "dq_convert"}
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU (AMD's 2.5 PFLOP/s)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "main_kernel_traffic.json")
 KERNEL_SOURCES = ["bwd_main.h", "common.h", "masks.h"]
@@ -231,7 +232,7 @@ def main():
     ap.add_argument("--deterministic", type=int, default=-1,
                     help="override the workload's dQ route (-1: as the workload states; 0 fp32 "
                          "atomics, 1 deterministic (the library's choice), 2 dS panels + dq2k, "
-                         "3 dQ partials + ordered reduction)")
+                         "3 dQ partials + ordered reduction, 4 ordered relay)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"],
                     help="io element type of Q, K, V, O, dO and the gradients")
     ap.add_argument("--bias", default="none", choices=["none", "bias", "dbias"],

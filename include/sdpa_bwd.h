@@ -48,10 +48,17 @@
  *      forms dQ = scale * dS K in ascending KV order;
  *   3  dQ partials: the main kernel stores one fp32 dQ partial per (KV tile, 32-row q tile) in
  *      the workspace and a second kernel sums them in ascending KV order;
+ *   4  ordered relay ("Deterministic vs. non-deterministic dQ", ordered-reduction relay): the
+ *      main kernel keeps one fp32 running sum per (query head, 32-row q tile) in the workspace and
+ *      the key tiles that see the q tile add into it one after another in ascending KV order,
+ *      passing a turn counter; a conversion kernel then writes dq.  The workspace stays linear in
+ *      the sequence lengths.  The key tiles of one query head run on one XCD (of the device's
+ *      hipDeviceAttributeNumberOfXccs), taking their work from per-XCD queues; if a wait for a
+ *      turn is ever abandoned (it is bounded), or not every work item ran, dq is written as NaN;
  *   1  deterministic, the library's choice between 2 and 3: 3 where its workspace holds fewer
  *      bytes per (KV tile, q row) (Kqk fp32 partials against the key tile's bf16 dS values),
  *      else 2 (kernel head dim 64 takes 3; 128, 192 and 256 take 2).
- * Routes 1-3 make dq, dk, dv bitwise reproducible run to run; dK and dV are reproducible on every
+ * Routes 1-4 make dq, dk, dv bitwise reproducible run to run; dK and dV are reproducible on every
  * route.  Any other value gives SDPA_BWD_INVALID_ARG.
  */
 #ifndef SDPA_BWD_H
@@ -69,7 +76,8 @@ enum {
   SDPA_BWD_DQ_ATOMIC = 0,
   SDPA_BWD_DQ_DETERMINISTIC = 1,
   SDPA_BWD_DQ_DS_PANELS = 2,
-  SDPA_BWD_DQ_PARTIALS = 3
+  SDPA_BWD_DQ_PARTIALS = 3,
+  SDPA_BWD_DQ_RELAY = 4
 };
 
 enum {
@@ -83,8 +91,9 @@ enum {
 /* Bytes of workspace needed by a call with these arguments: a 256-byte-aligned carve of the
  * per-row statistics (LSE * log2 e and delta, B*Hq*Sq_pad float pairs, Sq_pad = Sq rounded up to
  * 32), then the dQ route's buffer: the fp32 dQ accumulator (B*Hq*Sq*Kqk floats, route 0), the
- * bf16 dS panels (B*Hq*Sq_pad*Skv_pad, route 2) or the fp32 dQ partials
- * (B*Hq*(Skv_pad/BC)*Sq_pad*Kqk floats, route 3), where (Kqk, Kv) are the kernel head dims of
+ * bf16 dS panels (B*Hq*Sq_pad*Skv_pad, route 2), the fp32 dQ partials
+ * (B*Hq*(Skv_pad/BC)*Sq_pad*Kqk floats, route 3) or the relay's running sums (B*Hq*Sq_pad*Kqk
+ * floats), its turn counters (B*Hq*Sq_pad/32 int32) and 16 int32 control words (route 4), where (Kqk, Kv) are the kernel head dims of
  * the call (see above), BC is the key tile (256 keys for kernel head dims up to 192, 128 for 256)
  * and Skv_pad is Skv rounded up to BC; then, under GQA or when the main grid splits its q ranges,
  * the bf16 per-(query head, part) dK/dV partials (Kqk + Kv per key row).  Returns 0 for arguments
@@ -93,8 +102,8 @@ size_t sdpa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk,
                                int causal, int window_left, int deterministic, int has_seqlens);
 
 /* The dQ route a call with these head dims and this `deterministic` value takes:
- * SDPA_BWD_DQ_ATOMIC, SDPA_BWD_DQ_DS_PANELS or SDPA_BWD_DQ_PARTIALS (never
- * SDPA_BWD_DQ_DETERMINISTIC, which resolves to one of the last two); -1 for head dims outside the
+ * SDPA_BWD_DQ_ATOMIC, SDPA_BWD_DQ_DS_PANELS, SDPA_BWD_DQ_PARTIALS or SDPA_BWD_DQ_RELAY (never
+ * SDPA_BWD_DQ_DETERMINISTIC, which resolves to SDPA_BWD_DQ_DS_PANELS or SDPA_BWD_DQ_PARTIALS); -1 for head dims outside the
  * supported set or an unknown value.  Host only, no GPU work. */
 int sdpa_bwd_dq_route(int Dqk, int Dv, int deterministic);
 

@@ -54,7 +54,8 @@ def test_dq_route_choice(so):
         assert lib.dq_route(*d, 0) == lib.DQ_ATOMIC
         assert lib.dq_route(*d, 2) == lib.DQ_DS_PANELS
         assert lib.dq_route(*d, 3) == lib.DQ_PARTIALS
-        assert lib.dq_route(*d, 4) == -1
+        assert lib.dq_route(*d, 4) == lib.DQ_RELAY
+        assert lib.dq_route(*d, 5) == -1
     # head dims that are multiples of 8 up to 256 run on the next supported size
     assert lib.dq_route(96, 96, 1) == lib.dq_route(128, 128, 1)
     assert lib.dq_route(40, 40, 1) == lib.dq_route(64, 64, 1)
@@ -103,8 +104,15 @@ def test_workspace_size_rules(so):
     # head dim 192 (256-key tiles): 192 fp32 per q row > 256 bf16 -> dS panels
     d192 = dict(Dqk=192, Dv=128, Sq=200, Skv=200)
     assert _ws(deterministic=True, **d192) == _ws(deterministic=lib.DQ_DS_PANELS, **d192)
+    # the relay: one 32 x Dqk fp32 running sum per q tile, one int32 turn counter per q tile and
+    # 16 int32 control words, whatever the key length (linear in the sequence lengths)
+    relay = _al(4 * 224 * 8) + _al(4 * 224 * 128 * 4) + _al(4 * 7 * 4) + _al(16 * 4)
+    assert _ws(deterministic=lib.DQ_RELAY, Sq=200, Skv=200) == relay
+    assert _ws(deterministic=lib.DQ_RELAY, Sq=200, Skv=5000) == relay
+    assert _ws(deterministic=lib.DQ_RELAY, Sq=200, Skv=200, Hkv=1) == \
+        relay + _al(4 * 200 * 128 * 2) * 2
     # unknown route values are rejected
-    assert _ws(deterministic=4) == 0 and _ws(deterministic=-1) == 0
+    assert _ws(deterministic=5) == 0 and _ws(deterministic=-1) == 0
     # monotone in the sequence length
     sizes = [_ws(Sq=s, Skv=s) for s in (64, 128, 300, 1000)]
     assert sizes == sorted(sizes)
@@ -134,7 +142,8 @@ def test_rejections_before_launch(so):
     assert _call(so, Hq=-1) == lib.INVALID_ARG
     assert _call(so, wl=-2) == lib.INVALID_ARG                    # window_left < -1
     assert _call(so, wr=-1) == lib.INVALID_ARG
-    assert _call(so, det=4) == lib.INVALID_ARG                    # unknown dQ route
+    assert _call(so, det=5) == lib.INVALID_ARG                    # unknown dQ route
+    assert _call(so, det=4) == lib.INVALID_ARG                    # relay: needs a workspace
     assert _call(so, det=-1) == lib.INVALID_ARG
     assert _call(so, Dqk=100, Dv=100) == lib.UNSUPPORTED          # not a multiple of 8
     assert _call(so, Dqk=264, Dv=264) == lib.UNSUPPORTED          # above 256

@@ -78,7 +78,7 @@ def _run(w, inp, o_bits, lse, bias, lens, det, want_dbias=True, ws_fill=None):
     return got, None if dbias is None else dbias.cpu().numpy()
 
 
-@pytest.mark.parametrize("det", [0, 2, 3], ids=["atomic", "dspanels", "dqpartials"])
+@pytest.mark.parametrize("det", [0, 2, 3, 4], ids=["atomic", "dspanels", "dqpartials", "relay"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_bias_parity(name, det):
     import attention_backward_sdpa_amd as lib

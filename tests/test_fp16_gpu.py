@@ -49,7 +49,7 @@ def to_half(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.float16)
 
 
-@pytest.mark.parametrize("det", [0, 2, 3], ids=["atomic", "dspanels", "dqpartials"])
+@pytest.mark.parametrize("det", [0, 2, 3, 4], ids=["atomic", "dspanels", "dqpartials", "relay"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_fp16_parity(name, det):
     import attention_backward_sdpa_amd as lib
@@ -98,7 +98,7 @@ def test_fp16_deterministic_bitwise(det):
             assert all(bool((a == b).all()) for a, b in zip(first, bits))
 
 
-@pytest.mark.parametrize("det", [0, 2, 3], ids=["atomic", "dspanels", "dqpartials"])
+@pytest.mark.parametrize("det", [0, 2, 3, 4], ids=["atomic", "dspanels", "dqpartials", "relay"])
 def test_fp16_bshd_layout(det):
     """fp16 io through BSHD storage (strided views) on a GQA window case with padding lengths."""
     import attention_backward_sdpa_amd as lib

@@ -39,8 +39,11 @@ CASES = [
     ("mha_det_s8192_d256", None),
     ("mla_window_padded_s4096", None),
     ("mla_window_padded_s4096", 3),
+    ("gqa_causal_s4096_d128", 4),
+    ("mha_det_s8192_d256", 4),
+    ("mla_window_padded_s4096", 4),
 ]
-ROUTE_NAMES = {0: "atomic", 1: "det", 2: "dspanels", 3: "dqpartials", None: "default"}
+ROUTE_NAMES = {0: "atomic", 1: "det", 2: "dspanels", 3: "dqpartials", 4: "relay", None: "default"}
 
 
 def _prepare(w):
@@ -144,8 +147,10 @@ def test_fullsize_sampled_rows(name, det):
             assert np.all(dk[b, :, L:] == 0) and np.all(dv[b, :, L:] == 0)
 
 
-@pytest.mark.parametrize("name,det", [("mha_det_s8192_d256", True), ("gqa_causal_s4096_d128", 3)],
-                         ids=["mha_det_s8192_d256-det", "gqa_causal_s4096_d128-dqpartials"])
+@pytest.mark.parametrize("name,det", [("mha_det_s8192_d256", True), ("gqa_causal_s4096_d128", 3),
+                                      ("gqa_causal_s4096_d128", 4)],
+                         ids=["mha_det_s8192_d256-det", "gqa_causal_s4096_d128-dqpartials",
+                              "gqa_causal_s4096_d128-relay"])
 def test_fullsize_deterministic_bitwise(name, det):
     # 10 runs of a deterministic route at full size, identical bits
     w = W[name]

@@ -33,7 +33,7 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("det", [0, 2, 3], ids=["atomic", "dspanels", "dqpartials"])
+@pytest.mark.parametrize("det", [0, 2, 3, 4], ids=["atomic", "dspanels", "dqpartials", "relay"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_headdim_envelope_parity(name, det):
     w = CASES[name]

@@ -35,7 +35,7 @@ def test_m0_written_only_for_lds_dma(asm):
             continue
         assert re.fullmatch(r"s_mov_b32 m0, s\d+", t), f"unexpected M0 use: {t}"
         nxt = ins[i + 1]
-        assert re.match(r"buffer_load_dword(x4)? v\d+, s\[\d+:\d+\], 0 offen lds", nxt), \
+        assert re.match(r"buffer_load_dword(x4)? v\d+, s\[\d+:\d+\], 0 offen (sc1 )?lds", nxt), \
             f"M0 write not followed by its LDS-DMA load: {t} / {nxt}"
         n_dma += 1
     assert n_dma > 0

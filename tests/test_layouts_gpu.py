@@ -65,7 +65,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("det", [0, 2, 3], ids=["atomic", "dspanels", "dqpartials"])
+@pytest.mark.parametrize("det", [0, 2, 3, 4], ids=["atomic", "dspanels", "dqpartials", "relay"])
 @pytest.mark.parametrize("case_def", CASES, ids=[c[0] for c in CASES])
 def test_strided_layouts(case_def, det):
     import attention_backward_sdpa_amd as lib

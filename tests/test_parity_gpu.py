@@ -58,7 +58,7 @@ SMALL_CASES = {
 
 
 # dQ routes (the `deterministic` argument): None = the workload's own (False / True)
-ROUTES = {"default": None, "dspanels": 2, "dqpartials": 3}
+ROUTES = {"default": None, "dspanels": 2, "dqpartials": 3, "relay": 4}
 
 
 @pytest.mark.parametrize("route", list(ROUTES))
@@ -79,7 +79,10 @@ def test_small_parity(name, route):
 
 
 @pytest.mark.parametrize("name,det", [("det_d256_s200", True), ("gqa_causal_d128_s333", 2),
-                                      ("gqa_causal_d128_s333", 3), ("split_causal_d128_s600", 3)])
+                                      ("gqa_causal_d128_s333", 3), ("split_causal_d128_s600", 3),
+                                      ("gqa_causal_d128_s333", 4), ("split_causal_d128_s600", 4),
+                                      ("det_mla_window_padded_s400", 4), ("mha_s128_d64", 4),
+                                      ("det_d256_s200", 4)])
 def test_deterministic_bitwise_over_runs(name, det):
     # 10 runs over a workspace refilled with random bytes each time: identical bits
     w = SMALL_CASES[name]
@@ -104,16 +107,32 @@ def test_routes_agree():
     w = SMALL_CASES["gqa_causal_d128_s333"]
     case = C.make_case(w)
     ref = C.oracle_backward(case)
-    outs = {r: C.run_gpu(case, torch, deterministic=r) for r in (0, 1, 2, 3)}
+    outs = {r: C.run_gpu(case, torch, deterministic=r) for r in (0, 1, 2, 3, 4)}
     for r, out in outs.items():
         for tname, x, rr in zip(("dQ", "dK", "dV"), out, ref):
             C.assert_close(f"route {r} {tname}", x, rr)
     # dK and dV are deterministic on every route and come from the same GEMM3/GEMM5 arithmetic
-    for r in (1, 2, 3):
+    for r in (1, 2, 3, 4):
         assert np.array_equal(outs[0][1], outs[r][1]) and np.array_equal(outs[0][2], outs[r][2])
     # at head dim 128 the deterministic choice is the dS-panel route
     for x, y in zip(outs[1], outs[2]):
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["gqa_causal_d128_s333", "split_causal_d128_s600", "mha_s128_d64",
+                                  "det_d256_s200", "mla_window_padded_s400",
+                                  "mla_split_window_padded_s900", "window_only_d64_s260", "s1_d128"])
+def test_relay_equals_dq_partials(name):
+    # the relay adds the same fp32 GEMM4 blocks in the same ascending key-tile order as the
+    # dQ-partial reduction (whose sum starts from 0, the relay's from the first block), with the
+    # same final scaling: equal values
+    w = SMALL_CASES[name]
+    case = C.make_case(w)
+    t = C.to_device(case, torch)
+    a = C.run_gpu(case, torch, deterministic=3, dev_inputs=t)
+    b = C.run_gpu(case, torch, deterministic=4, dev_inputs=t)
+    for tname, x, y in zip(("dQ", "dK", "dV"), a, b):
+        assert np.array_equal(x, y), f"{name} {tname}: relay differs from the dQ-partial route"
 
 
 def test_linear_in_dO_bitwise():
@@ -177,7 +196,7 @@ SURFACE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("det", [0, 2, 3], ids=["atomic", "dspanels", "dqpartials"])
+@pytest.mark.parametrize("det", [0, 2, 3, 4], ids=["atomic", "dspanels", "dqpartials", "relay"])
 @pytest.mark.parametrize("case_def", SURFACE_CASES, ids=[c[0] for c in SURFACE_CASES])
 def test_mask_and_shape_surface(case_def, det):
     import attention_backward_sdpa_amd as lib

@@ -69,7 +69,7 @@ def _run(w, inp, o_bits, lse, sink, lens, det, ws=None):
     return [C.bf16_tensor_to_f32(x) for x in outs], dsink.cpu().numpy()
 
 
-@pytest.mark.parametrize("det", [0, 2, 3], ids=["atomic", "dspanels", "dqpartials"])
+@pytest.mark.parametrize("det", [0, 2, 3, 4], ids=["atomic", "dspanels", "dqpartials", "relay"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_sink_parity(name, det):
     w = CASES[name]
