@@ -13,3 +13,10 @@ from .sdpa_oracle import (  # noqa: F401
     backward_dkdv_rows,
     attention_flops,
 )
+from .nvfp4_qat import (  # noqa: F401
+    e4m3_round,
+    e2m1_round,
+    fake_nvfp4,
+    qat_forward,
+    qat_backward,
+)
