@@ -75,6 +75,10 @@ def _load():
     lib.sdpa_bwd_run.restype = i
     lib.sdpa_bwd_run_workspace_size.argtypes = [ctypes.POINTER(Args)]
     lib.sdpa_bwd_run_workspace_size.restype = sz
+    lib.sdpa_bwd_nvfp4_qat.argtypes = [vp] * 9 + [i] * 5 + [f, i, i, vp, sz, vp, vp]
+    lib.sdpa_bwd_nvfp4_qat.restype = i
+    lib.sdpa_bwd_nvfp4_qat_workspace_size.argtypes = [i] * 7
+    lib.sdpa_bwd_nvfp4_qat_workspace_size.restype = sz
     lib.sdpa_bwd_dq_route.argtypes = [i, i, i]
     lib.sdpa_bwd_dq_route.restype = i
     lib.sdpa_bwd_status_string.argtypes = [i]
@@ -99,6 +103,14 @@ def _check(status):
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _events(events):
+    """Five torch.cuda.Event (or None entries) as the hipEvent_t array of the C ABI, or NULL."""
+    if events is None:
+        return None
+    return (ctypes.c_void_p * 5)(*[ctypes.c_void_p(None if e is None else e.cuda_event)
+                                   for e in events])
 
 
 def _stream_handle(stream):
@@ -249,6 +261,26 @@ def sdpa_bwd_run(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, wind
                  seq_q_lens, seq_kv_lens, causal_bottom_right, window_right, sink, dsink, bias,
                  dbias, workspace, stream, events)
     _check(_load().sdpa_bwd_run(ctypes.byref(a)))
+
+
+def nvfp4_qat_workspace_size(B, H, Sq, Skv, D=128, causal=False, deterministic=0) -> int:
+    """sdpa_bwd_nvfp4_qat_workspace_size()."""
+    return int(_load().sdpa_bwd_nvfp4_qat_workspace_size(int(B), int(H), int(Sq), int(Skv), int(D),
+                                                         int(bool(causal)), int(deterministic)))
+
+
+def sdpa_bwd_nvfp4_qat(q, k, v, o_hp, do, lse, dq, dk, dv, scale=None, causal=False,
+                       deterministic=0, workspace=None, stream=None, events=None):
+    """sdpa_bwd_nvfp4_qat(): the NVFP4 attention-QAT backward on contiguous (B, H, S, 128) bf16
+    tensors; `workspace` must hold nvfp4_qat_workspace_size(...) bytes."""
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_load().sdpa_bwd_nvfp4_qat(_ptr(q), _ptr(k), _ptr(v), _ptr(o_hp), _ptr(do), _ptr(lse),
+                                      _ptr(dq), _ptr(dk), _ptr(dv), B, H, Sq, Skv, D,
+                                      0.0 if scale is None else float(scale), int(bool(causal)),
+                                      int(deterministic), _ptr(workspace), ws_bytes,
+                                      _stream_handle(stream), _events(events)))
 
 
 def sdpa_bwd_preprocess(o, do, lse, stats, dq_accum=None, seq_q_lens=None, Dqk=0, stream=None):

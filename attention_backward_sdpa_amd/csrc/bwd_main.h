@@ -49,6 +49,7 @@
 #pragma once
 #include "common.h"
 #include "masks.h"
+#include "nvfp4.h"
 
 namespace sdpa {
 
@@ -99,7 +100,7 @@ enum DqMode {
 };
 
 template <int DQK_, int DV_, int KPW_, int NW_, int MODE_, bool F16_ = false, int BIAS_ = 0,
-          bool PAD_ = false>
+          bool PAD_ = false, bool QAT_ = false>
 struct MainCfg {
   static constexpr int DQK = DQK_, DV = DV_, KPW = KPW_, NW = NW_;
   static constexpr int MODE = MODE_;
@@ -107,6 +108,13 @@ struct MainCfg {
   // them read as zero, result columns past them are not stored.  Without it the code is that of
   // exact head dims.
   static constexpr bool PAD = PAD_;
+  // NVFP4 attention QAT ("NVFP4 Attention QAT Backward", "Overview"): the inputs are already
+  // fake-quantised; GEMM3 takes the fake-quantised P (dV = fake(P)^T dO) while dS, and so dQ and
+  // dK, use the unquantised P.  MHA, head dim 128, bf16, the 4-wave layout (the fp32 P is kept
+  // for the quantisation).
+  static constexpr bool QAT = QAT_;
+  static_assert(!QAT_ || (DQK_ == 128 && DV_ == 128 && !F16_ && BIAS_ == 0 && NW_ == 4),
+                "the QAT variant is bf16, head dim 128, no bias, 4 waves");
   // 0: no bias; 1: additive bias in the replayed scores; 2: bias and its gradient dBias = dS
   static constexpr int BIAS = BIAS_;
   static constexpr bool DS_OUT = MODE == DQ_DS;  // dS leaves the kernel, GEMM4 does not run here
@@ -352,11 +360,12 @@ struct KeyRows {
 // P = exp2(S * scale * log2e - LSE * log2e), dS = P * (dP - delta); both are packed to io-type
 // pairs in accumulator order (pb/sb[v/2] holds registers v, v+1).  No masking here: on edge tiles
 // mask_pairs clears the invisible pairs afterwards.
-template <bool F16, int X0, int BIAS = 0>
+template <bool F16, int X0, int BIAS = 0, bool QAT = false>
 __device__ __forceinline__ void softmax_ds(const floatx16& S, const floatx16& dP,
                                            const float* sStat, int g, float scale_log2,
                                            uint32_t (&pb)[8], uint32_t (&sb)[8],
-                                           const float* bl = nullptr, float* dsf = nullptr) {
+                                           const float* bl = nullptr, float* dsf = nullptr,
+                                           float* pf = nullptr) {
 #pragma unroll
   for (int x = X0; x < X0 + 2; ++x) {
     // rows of accumulator registers 4x..4x+3 of this lane: g*4 + 8x + 0..3
@@ -372,6 +381,7 @@ __device__ __forceinline__ void softmax_ds(const floatx16& S, const floatx16& dP
       pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * x + e], scale_log2, off));
       dv[e] = pv[e] * (dP[4 * x + e] - d4[e]);
       if constexpr (BIAS == 2) dsf[4 * x + e] = dv[e];
+      if constexpr (QAT) pf[4 * x + e] = pv[e];  // fp32 P for the fake quantisation
     }
     pb[2 * x] = Elem<F16>::pack2(pv[0], pv[1]);
     pb[2 * x + 1] = Elem<F16>::pack2(pv[2], pv[3]);
@@ -805,6 +815,7 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
     constexpr int NBV = C::BIAS ? 16 : 1;
     uint32_t bcur[NBV], bnext[NBV];
     float dsf[C::BIAS == 2 ? 16 : 1];
+    float pf[C::QAT ? 16 : 1];
     const int64_t bias_bh = (int64_t)b * p.bias_bstride + (int64_t)h * p.Sq * p.Skv;
     const int bias_key = min(key_lane, p.Skv - 1);
     auto load_bias = [&](int i_t, uint32_t (&dst)[NBV]) {
@@ -965,8 +976,8 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
       // accumulators flow through avoids register copies at the join).
       float bl[NBV];
       bias_log2(bcur, bl);
-      softmax_ds<C::F16, 0, C::BIAS>(S, dP, sStat, g, p.scale_log2, pb, sb, bl, dsf);
-      softmax_ds<C::F16, 2, C::BIAS>(S, dP, sStat, g, p.scale_log2, pb, sb, bl, dsf);
+      softmax_ds<C::F16, 0, C::BIAS, C::QAT>(S, dP, sStat, g, p.scale_log2, pb, sb, bl, dsf, pf);
+      softmax_ds<C::F16, 2, C::BIAS, C::QAT>(S, dP, sStat, g, p.scale_log2, pb, sb, bl, dsf, pf);
       if (edge) {
         const uint32_t vis_m = visible_rows(KeyRows(mg, q0 + g * 4, key_lane));
         mask_pairs<0>(vis_m, pb, sb);
@@ -977,7 +988,14 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
           for (int r = 0; r < 16; ++r)
             if (!((vis_m >> (8 * (r / 4) + (r % 4))) & 1u)) dsf[r] = 0.f;
         }
+        if constexpr (C::QAT) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!((vis_m >> (8 * (r / 4) + (r % 4))) & 1u)) pf[r] = 0.f;
+        }
       }
+      // QAT: GEMM3's P operand is the fake-quantised masked P (groups of 16 keys of a row)
+      if constexpr (C::QAT) nvfp4_p_pack(pf, pb);
       if constexpr (C::BIAS) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) bcur[r] = bnext[r];

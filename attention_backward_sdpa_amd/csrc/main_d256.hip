@@ -2,4 +2,4 @@
 #include "main_launch.h"
 
 template hipError_t sdpa::launch_main_dqk<256>(const MainParams&, DqMode, bool, int, int, int,
-                                              hipStream_t);
+                                              hipStream_t, bool);

@@ -21,7 +21,7 @@ struct MainShape {
 // carve and grid assume; a mismatch with the kernel's is hipErrorInvalidValue.
 template <int DQK>
 hipError_t launch_main_dqk(const MainParams& mp, DqMode mode, bool f16, int bias, int grid, int bc,
-                           hipStream_t s);
+                           hipStream_t s, bool qat = false);
 
 template <class C>
 hipError_t launch_main_cfg(const MainParams& mp, int grid, hipStream_t s) {
@@ -36,15 +36,15 @@ hipError_t launch_main_cfg(const MainParams& mp, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DQK, int DV, int KPW, int NW, bool F16, int BIAS, bool PAD>
+template <int DQK, int DV, int KPW, int NW, bool F16, int BIAS, bool PAD, bool QAT = false>
 hipError_t launch_main_mode(const MainParams& mp, DqMode mode, int grid, hipStream_t s) {
   if (mode == DQ_DS)
-    return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_DS, F16, BIAS, PAD>>(mp, grid, s);
+    return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_DS, F16, BIAS, PAD, QAT>>(mp, grid, s);
   if (mode == DQ_PARTIAL)
-    return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_PARTIAL, F16, BIAS, PAD>>(mp, grid, s);
+    return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_PARTIAL, F16, BIAS, PAD, QAT>>(mp, grid, s);
   if (mode == DQ_RELAY)
-    return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_RELAY, F16, BIAS, PAD>>(mp, grid, s);
-  return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_ATOMIC, F16, BIAS, PAD>>(mp, grid, s);
+    return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_RELAY, F16, BIAS, PAD, QAT>>(mp, grid, s);
+  return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_ATOMIC, F16, BIAS, PAD, QAT>>(mp, grid, s);
 }
 
 template <int DQK, int NW, int BIAS>
@@ -63,8 +63,18 @@ hipError_t launch_main_nw(const MainParams& mp, DqMode mode, bool f16, int grid,
 
 template <int DQK>
 hipError_t launch_main_dqk(const MainParams& mp, DqMode mode, bool f16, int bias, int grid, int bc,
-                           hipStream_t s) {
+                           hipStream_t s, bool qat) {
   constexpr int NW0 = MainShape<DQK>::nw(false), NW1 = MainShape<DQK>::nw(true);
+  if (qat) {  // NVFP4 QAT: head dim 128, bf16, no bias, the 4-wave layout, exact head dims
+    if constexpr (DQK == 128) {
+      if (f16 || bias || mp.dqk_act != 128 || mp.dv_act != 128 ||
+          MainCfg<128, 128, 32, NW1, DQ_ATOMIC>::BC != bc)
+        return hipErrorInvalidValue;
+      return launch_main_mode<128, 128, 32, NW1, false, 0, false, true>(mp, mode, grid, s);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   if (bias == 1) return launch_main_nw<DQK, NW1, 1>(mp, mode, f16, grid, bc, s);
   if (bias == 2) return launch_main_nw<DQK, NW1, 2>(mp, mode, f16, grid, bc, s);
   return launch_main_nw<DQK, NW0, 0>(mp, mode, f16, grid, bc, s);
@@ -73,7 +83,7 @@ hipError_t launch_main_dqk(const MainParams& mp, DqMode mode, bool f16, int bias
 // instantiated once each, in main_d<DQK>.hip
 #define SDPA_MAIN_DQK(D)                                                                           \
   extern template hipError_t launch_main_dqk<D>(const MainParams&, DqMode, bool, int, int, int,    \
-                                                hipStream_t);
+                                                hipStream_t, bool);
 SDPA_MAIN_DQK(64)
 SDPA_MAIN_DQK(128)
 SDPA_MAIN_DQK(192)

@@ -1,0 +1,71 @@
+// NVFP4 fake quantisation for the attention-QAT backward ("NVFP4 Attention QAT Backward",
+// "Overview"): every group of 16 consecutive values is mapped to E2M1 values (0, 0.5, 1, 1.5, 2,
+// 3, 4, 6 and their negatives) times one E4M3 scale, then dequantised:
+//     scale = E4M3(amax / 6),   x^ = E2M1(x / scale) * scale   (0 where amax = 0)
+// Both roundings are to nearest even; the divisions are correctly rounded fp32 divisions, so an
+// x / scale that lands exactly on an E2M1 midpoint keeps the tie.  The scale saturates at 448
+// (the largest finite E4M3 value), the E2M1 value at 6.  x^ has at most 6 significant bits and is
+// exact in bf16.
+#pragma once
+#include "common.h"
+
+namespace sdpa {
+
+// E4M3 (4 exponent bits, bias 7, 3 mantissa bits, subnormal step 2^-9) nearest-even rounding of a
+// non-negative fp32 value, saturating at 448.
+__device__ __forceinline__ float e4m3_rne(float a) {
+  if (!(a > 0.f)) return 0.f;
+  if (a < 0.015625f) return __builtin_rintf(a * 512.f) * (1.f / 512.f);  // below 2^-6
+  uint32_t u = __float_as_uint(a);
+  u += 0x7FFFFu + ((u >> 20) & 1u);  // round away the 20 low mantissa bits, ties to even
+  u &= 0xFFF00000u;
+  const float r = __uint_as_float(u);
+  return r < 448.f ? r : 448.f;
+}
+
+// E2M1 nearest-even rounding of a non-negative value (steps 0.5 below 2, 1 below 4, 2 above; the
+// even integers of each step are the even codes), saturating at 6.
+__device__ __forceinline__ float e2m1_rne(float y) {
+  float r;
+  if (y < 2.f) r = __builtin_rintf(y * 2.f) * 0.5f;
+  else if (y < 4.f) r = __builtin_rintf(y);
+  else r = __builtin_rintf(y * 0.5f) * 2.f;
+  return r < 6.f ? r : 6.f;
+}
+
+// The dequantised value of x in a group with this scale (scale > 0).
+__device__ __forceinline__ float nvfp4_value(float x, float scale) {
+  return __builtin_copysignf(e2m1_rne(__builtin_fabsf(x) / scale), x) * scale;
+}
+
+__device__ __forceinline__ float nvfp4_scale(float amax) { return e4m3_rne(amax / 6.f); }
+
+// max of a and the value of lane DPP(ctrl) of the same 16-lane row (DPP permutes within rows)
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float a) {
+  const int b = __builtin_amdgcn_update_dpp(0, __float_as_int(a), CTRL, 0xF, 0xF, false);
+  return fmaxf(a, __int_as_float(b));
+}
+
+// The probability operand of GEMM3 (dV += fake(P)^T dO) from the fp32 P of one wave's 32 keys:
+// lane l holds key l % 32 and accumulator rows r (16 of them), so a group of 16 consecutive keys
+// of one row is the same register in one 16-lane DPP row; its amax takes four DPP max steps
+// (swap neighbours, swap pairs, mirror within 8, mirror within 16).  Returns the packed bf16
+// words in the order of the plain P words.
+__device__ __forceinline__ void nvfp4_p_pack(const float (&pf)[16], uint32_t (&pb)[8]) {
+  float pq[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float amax = pf[r];  // P >= 0
+    amax = dpp_max<0xB1>(amax);   // quad_perm [1, 0, 3, 2]
+    amax = dpp_max<0x4E>(amax);   // quad_perm [2, 3, 0, 1]
+    amax = dpp_max<0x141>(amax);  // row_half_mirror
+    amax = dpp_max<0x140>(amax);  // row_mirror
+    const float scale = nvfp4_scale(amax);
+    pq[r] = scale > 0.f ? nvfp4_value(pf[r], scale) : 0.f;
+  }
+#pragma unroll
+  for (int x = 0; x < 8; ++x) pb[x] = pack_bf16x2(pq[2 * x], pq[2 * x + 1]);
+}
+
+}  // namespace sdpa

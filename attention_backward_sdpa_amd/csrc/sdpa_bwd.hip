@@ -229,15 +229,15 @@ hipError_t launch_dq2k(const Dq2kParams& dp, int grid, hipStream_t s) {
 // The main kernel of the route for kernel head dim Dqk (instantiated in main_d<Dqk>.hip).
 // bias: 0 none, 1 bias, 2 bias and dBias (the 4-wave layout of geometry_for).
 hipError_t run_main(int Dqk, const MainParams& mp, Route route, bool f16, int bias, int grid,
-                    int bc, hipStream_t s) {
+                    int bc, hipStream_t s, bool qat = false) {
   const DqMode mode = route == R_DS    ? DQ_DS
                       : route == R_DQP ? DQ_PARTIAL
                       : route == R_RELAY ? DQ_RELAY
                                          : DQ_ATOMIC;
-  if (Dqk == 64) return launch_main_dqk<64>(mp, mode, f16, bias, grid, bc, s);
-  if (Dqk == 128) return launch_main_dqk<128>(mp, mode, f16, bias, grid, bc, s);
-  if (Dqk == 192) return launch_main_dqk<192>(mp, mode, f16, bias, grid, bc, s);
-  return launch_main_dqk<256>(mp, mode, f16, bias, grid, bc, s);
+  if (Dqk == 64) return launch_main_dqk<64>(mp, mode, f16, bias, grid, bc, s, qat);
+  if (Dqk == 128) return launch_main_dqk<128>(mp, mode, f16, bias, grid, bc, s, qat);
+  if (Dqk == 192) return launch_main_dqk<192>(mp, mode, f16, bias, grid, bc, s, qat);
+  return launch_main_dqk<256>(mp, mode, f16, bias, grid, bc, s, qat);
 }
 
 // the reduction reads the partial blocks in the layout of the main kernel that wrote them (the
@@ -347,11 +347,12 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
         const int* seq_q_lens, const int* seq_kv_lens, int bottom_right, int window_right,
         const sdpa_bwd_layout* layouts, int dtype, const float* sink, float* dsink,
         const BiasArgs& ba, void* workspace, size_t workspace_bytes, bool check_ws,
-        hipStream_t stream, void* const* events) {
+        hipStream_t stream, void* const* events, bool qat = false) {
   Geometry geo;
   const bool has_bias = ba.bias != nullptr;
+  // a bias or the QAT variant runs the 4-wave layout
   int st = validate(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, window_left,
-                    window_right, &geo, has_bias);
+                    window_right, &geo, has_bias || qat);
   if (st != SDPA_BWD_OK) return st;
   int KDqk, KDv;  // the kernel's head dims (>= the tensors' Dqk, Dv)
   kernel_dims(Dqk, Dv, &KDqk, &KDv);
@@ -530,7 +531,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   }
   if (main_grid > 0x7fffffff) return SDPA_BWD_UNSUPPORTED;
   e = run_main(KDqk, mp, route, f16, has_bias ? (ba.dbias ? 2 : 1) : 0, (int)main_grid, geo.bc,
-               stream);
+               stream, qat);
   if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   rec(2);
 
@@ -634,6 +635,22 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
 
 }  // namespace
 
+// NVFP4 QAT: the fake-quantised copies of Q, K and V at the start of the workspace.
+int64_t qat_hat_bytes(int B, int H, int Sq, int Skv) {
+  return align_up((int64_t)B * H * Sq * 128 * 2, kAlign) +
+         2 * align_up((int64_t)B * H * Skv * 128 * 2, kAlign);
+}
+
+hipError_t launch_fake_quant(const void* x, void* y, int64_t elems, hipStream_t s) {
+  const int64_t groups = elems / 16;
+  if (groups == 0) return hipSuccess;
+  int64_t grid = (groups + 255) / 256;
+  grid = grid > 8192 ? 8192 : grid;
+  hipLaunchKernelGGL(nvfp4_fake_quant_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                     (const bf16_t*)x, (bf16_t*)y, groups);
+  return hipGetLastError();
+}
+
 extern "C" {
 
 size_t sdpa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv,
@@ -662,6 +679,53 @@ int sdpa_bwd_dq_route(int Dqk, int Dv, int deterministic) {
     case R_RELAY: return SDPA_BWD_DQ_RELAY;
     default: return -1;
   }
+}
+
+size_t sdpa_bwd_nvfp4_qat_workspace_size(int B, int H, int Sq, int Skv, int D, int causal,
+                                         int deterministic) {
+  if (B < 0 || H <= 0 || Sq < 0 || Skv < 0 || D != 128 || (causal && Sq != Skv)) return 0;
+  if (B == 0 || Sq == 0 || Skv == 0) return 0;
+  Geometry geo;
+  geometry_for(128, 128, &geo, true);
+  const Route route = route_for(deterministic, 128, geo);
+  if (route == R_INVALID) return 0;
+  return (size_t)(qat_hat_bytes(B, H, Sq, Skv) + carve(B, H, H, Sq, Skv, 128, 128, route, geo).total);
+}
+
+int sdpa_bwd_nvfp4_qat(const void* q, const void* k, const void* v, const void* o_hp,
+                       const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
+                       int H, int Sq, int Skv, int D, float scale, int causal, int deterministic,
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       void* const* events) {
+  if (B < 0 || H <= 0 || Sq < 0 || Skv < 0) return SDPA_BWD_INVALID_ARG;
+  if (D != 128 || (causal && Sq != Skv)) return SDPA_BWD_UNSUPPORTED;
+  // everything run() checks, on the caller's tensors, before the quantisation launches
+  Geometry geo;
+  int st = validate(q, k, v, o_hp, dO, lse, dq, dk, dv, B, H, H, Sq, Skv, D, D, -1, 0, &geo, true);
+  if (st != SDPA_BWD_OK) return st;
+  if (route_for(deterministic, 128, geo) == R_INVALID) return SDPA_BWD_INVALID_ARG;
+  const hipStream_t s = (hipStream_t)stream;
+  if (B == 0 || Sq == 0 || Skv == 0)  // nothing to quantise; the chain writes the zeros
+    return run(q, k, v, o_hp, dO, lse, dq, dk, dv, B, H, H, Sq, Skv, D, D, scale, causal, -1,
+               deterministic, nullptr, nullptr, 0, 0, nullptr, SDPA_BWD_BF16, nullptr, nullptr,
+               BiasArgs{}, workspace, workspace_bytes, true, s, events, true);
+  const size_t need = sdpa_bwd_nvfp4_qat_workspace_size(B, H, Sq, Skv, D, causal, deterministic);
+  if (workspace == nullptr) return SDPA_BWD_INVALID_ARG;
+  if (workspace_bytes < need) return SDPA_BWD_WORKSPACE_TOO_SMALL;
+  if (((uintptr_t)workspace % kAlign) != 0) return SDPA_BWD_UNSUPPORTED;
+  char* ws = (char*)workspace;
+  const int64_t nq = (int64_t)B * H * Sq * 128, nk = (int64_t)B * H * Skv * 128;
+  char* qh = ws;
+  char* kh = qh + align_up(nq * 2, kAlign);
+  char* vh = kh + align_up(nk * 2, kAlign);
+  const int64_t hat = qat_hat_bytes(B, H, Sq, Skv);
+  hipError_t e = launch_fake_quant(q, qh, nq, s);
+  if (e == hipSuccess) e = launch_fake_quant(k, kh, nk, s);
+  if (e == hipSuccess) e = launch_fake_quant(v, vh, nk, s);
+  if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
+  return run(qh, kh, vh, o_hp, dO, lse, dq, dk, dv, B, H, H, Sq, Skv, D, D, scale, causal, -1,
+             deterministic, nullptr, nullptr, 0, 0, nullptr, SDPA_BWD_BF16, nullptr, nullptr,
+             BiasArgs{}, ws + hat, workspace_bytes - (size_t)hat, true, s, events, true);
 }
 
 int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,

@@ -5,6 +5,7 @@
 #pragma once
 #include "common.h"
 #include "masks.h"
+#include "nvfp4.h"
 
 namespace sdpa {
 
@@ -263,6 +264,37 @@ __global__ void __launch_bounds__(256) zero_rows_kernel(bf16_t* out, Strides st,
       const int s = x / d8, c = x - s * d8;
       *reinterpret_cast<u32x4*>(base + s * st.s + c * 8) = u32x4{0u, 0u, 0u, 0u};
     }
+  }
+}
+
+// ---- NVFP4 QAT input quantisation ---------------------------------------------------------------
+// Fake-quantise a contiguous bf16 tensor in groups of 16 consecutive elements: one thread per
+// group (two 16-byte loads and stores), grid-stride over n_groups.
+__global__ void __launch_bounds__(256) nvfp4_fake_quant_kernel(const bf16_t* x, bf16_t* y,
+                                                               int64_t n_groups) {
+  for (int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x; gi < n_groups;
+       gi += (int64_t)gridDim.x * 256) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + gi * 16);
+    const u32x4 w0 = src[0], w1 = src[1];
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = __uint_as_float(w0[e] << 16);
+      v[2 * e + 1] = __uint_as_float(w0[e] & 0xffff0000u);
+      v[8 + 2 * e] = __uint_as_float(w1[e] << 16);
+      v[8 + 2 * e + 1] = __uint_as_float(w1[e] & 0xffff0000u);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, __builtin_fabsf(v[e]));
+    const float scale = nvfp4_scale(amax);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = scale > 0.f ? nvfp4_value(v[e], scale) : 0.f;
+    u32x4* dst = reinterpret_cast<u32x4*>(y + gi * 16);
+    dst[0] = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                   pack_bf16x2(v[6], v[7])};
+    dst[1] = u32x4{pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]), pack_bf16x2(v[12], v[13]),
+                   pack_bf16x2(v[14], v[15])};
   }
 }
 

@@ -39,7 +39,8 @@ class Workload:
         return self.scale if self.scale is not None else 1.0 / math.sqrt(self.Dqk)
 
 
-# The five workloads of the attention-backward study, seeded by their index.
+# The five workloads of the attention-backward study and the NVFP4-QAT example shape, seeded by
+# their index.
 WORKLOADS = {
     "mha_s128_d64": Workload("mha_s128_d64", 1, 2, 2, 128, 128, 64, 64, causal=False, seed=1),
     "mha_causal_s2048_d128": Workload("mha_causal_s2048_d128", 2, 16, 16, 2048, 2048, 128, 128,
@@ -51,6 +52,10 @@ WORKLOADS = {
     "mla_window_padded_s4096": Workload("mla_window_padded_s4096", 4, 16, 16, 4096, 4096, 192, 128,
                                         causal=True, window_left=1024, padded=True, len_lo=1024,
                                         seed=5),
+    # the NVFP4 attention-QAT example shape ("NVFP4 Attention QAT Backward", "High-level wrapper"):
+    # non-causal MHA, head dim 128
+    "qat_mha_s4096_d128": Workload("qat_mha_s4096_d128", 1, 16, 16, 4096, 4096, 128, 128,
+                                   causal=False, seed=6),
 }
 
 

@@ -185,7 +185,7 @@ def write_traffic_record(workload, det_arg, dtype, fetch_dir, write_dir):
     print(json.dumps(rec, indent=1))
 
 
-def cpu_baseline(w, inp, lens, dtype="bf16", budget_s=15.0):
+def cpu_baseline(w, inp, lens, dtype="bf16", budget_s=15.0, qat=False):
     """The fp64 CPU oracle (unchanged) on the first query heads of batch entry 0, timed until
     about budget_s seconds of work; the rate is scaled to the same FLOP convention."""
     import oracle
@@ -211,8 +211,11 @@ def cpu_baseline(w, inp, lens, dtype="bf16", budget_s=15.0):
         o = f(to_io(o.astype(np.float32)))
         lse = lse.astype(np.float32).astype(np.float64)
         t0 = time.perf_counter()
-        oracle.backward(q, kk, vv, o, do, lse, w.softmax_scale, causal=w.causal,
-                        window_left=w.window_left, seq_q_lens=L, seq_kv_lens=L)
+        if qat:
+            oracle.qat_backward(q, kk, vv, o, do, lse, w.softmax_scale, causal=w.causal)
+        else:
+            oracle.backward(q, kk, vv, o, do, lse, w.softmax_scale, causal=w.causal,
+                            window_left=w.window_left, seq_q_lens=L, seq_kv_lens=L)
         t_total += time.perf_counter() - t0
         one = synth.small_variant(w, B=1, Hq=1, Hkv=1)
         flops += algorithmic_flops(one, None if lens is None else [lens[0]])
@@ -220,7 +223,7 @@ def cpu_baseline(w, inp, lens, dtype="bf16", budget_s=15.0):
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{heads} of {w.B * w.Hq} (batch, query-head) slices of {w.name}, "
-                      f"backward only, fp64 numpy, {t_total:.1f} s"}
+                      f"{'NVFP4-QAT ' if qat else ''}backward only, fp64 numpy, {t_total:.1f} s"}
 
 
 def main():
@@ -238,6 +241,10 @@ def main():
     ap.add_argument("--bias", default="none", choices=["none", "bias", "dbias"],
                     help="add a per-batch additive bias (B, Hq, Sq, Skv) of the io type, drawn "
                          "N(0,1) (bias), and also produce its fp32 gradient (dbias)")
+    ap.add_argument("--qat", action="store_true",
+                    help="the NVFP4 attention-QAT backward (sdpa_bwd_nvfp4_qat) on the workload's "
+                         "shape (MHA, head dim 128, no window or padding); O and LSE come from the "
+                         "forward on the unquantised inputs, which changes no timed work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run a plain 1 GiB fp32 copy kernel three times "
@@ -281,17 +288,25 @@ def main():
         bias = torch.randn(w.B, w.Hq, w.Sq, w.Skv, generator=gen, device=dev).to(io)
         if args.bias == "dbias":
             dbias = torch.empty(w.B, w.Hq, w.Sq, w.Skv, dtype=torch.float32, device=dev)
+    if args.qat and (w.Hq != w.Hkv or w.Dqk != 128 or w.Dv != 128 or w.window_left >= 0 or
+                     lens is not None or args.bias != "none" or args.dtype != "bf16"):
+        raise SystemExit("--qat: MHA, head dim 128, bf16, no window, padding or bias")
     o, lse = gpu_forward_inputs(torch, q, k, v, w, lens, bias)
     lens_t = None if lens is None else torch.from_numpy(lens).to(dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     kw = dict(scale=w.softmax_scale, causal=w.causal, window_left=w.window_left,
               deterministic=det, seq_q_lens=lens_t, seq_kv_lens=lens_t, bias=bias, dbias=dbias)
-    nws = lib.run_workspace_size(q, k, v, **kw)
+    nws = (lib.nvfp4_qat_workspace_size(w.B, w.Hq, w.Sq, w.Skv, 128, w.causal, det) if args.qat
+           else lib.run_workspace_size(q, k, v, **kw))
     ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(events=None):
-        if bias is None:
+        if args.qat:
+            lib.sdpa_bwd_nvfp4_qat(q, k, v, o, do, lse, dq, dk, dv, scale=w.softmax_scale,
+                                   causal=w.causal, deterministic=det, workspace=ws, stream=stream,
+                                   events=events)
+        elif bias is None:
             lib.sdpa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale=w.softmax_scale,
                             causal=w.causal, window_left=w.window_left, deterministic=det,
                             seq_q_lens=lens_t, seq_kv_lens=lens_t, workspace=ws, stream=stream,
@@ -368,6 +383,7 @@ def main():
                    "Skv": w.Skv, "Dqk": w.Dqk, "Dv": w.Dv, "causal": w.causal,
                    "window_left": w.window_left, "padded": w.padded,
                    "dq_route": ROUTE_NAMES[route],
+                   "nvfp4_qat": bool(args.qat),
                    "bias": {"none": "none", "bias": f"{args.dtype} (B, Hq, Sq, Skv)",
                             "dbias": f"{args.dtype} (B, Hq, Sq, Skv) with fp32 dBias"}[args.bias],
                    "algorithmic_gflop": round(flops / 1e9, 3)},
@@ -382,7 +398,7 @@ def main():
     if args.copy_probe:
         copy_probe(torch, dev)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inp, lens, args.dtype)
+        out["cpu_baseline"] = cpu_baseline(w, inp, lens, args.dtype, qat=args.qat)
     print(json.dumps(out), flush=True)
 
 

@@ -240,6 +240,34 @@ int sdpa_bwd_run(const sdpa_bwd_args* args);
  * stream and events fields are not read); 0 for arguments it rejects and for empty problems. */
 size_t sdpa_bwd_run_workspace_size(const sdpa_bwd_args* args);
 
+/* NVFP4 attention-QAT backward ("NVFP4 Attention QAT Backward", "Overview", "Tensor contract",
+ * "Current support and limitations").  Q, K and V are fake-quantised to NVFP4 (every 16
+ * consecutive head-dim values: E2M1 values times one E4M3 scale E4M3(amax / 6), round to nearest
+ * even after correctly rounded fp32 divisions, then dequantised) into bf16 copies Q^, K^, V^ in the
+ * workspace, and the chain computes
+ *     P = softmax(scale Q^ K^T),  dS = P * (dO V^T - rowsum(o_hp * dO)),
+ *     dq = scale dS K^,  dk = scale dS^T Q^   (unquantised P: straight-through estimator),
+ *     dv = fake_nvfp4(P)^T dO                 (P fake-quantised in groups of 16 consecutive keys of a
+ *                                              row, after masking)
+ * o_hp is the forward's softmax(scale Q^ K^T) V^ before any probability quantisation, lse its
+ * natural-log statistic (B, H, Sq) fp32.  Tensors: contiguous (B, H, S, 128) bf16 device buffers
+ * (q, o_hp, dO, dq with Sq rows; k, v, dk, dv with Skv rows), 16-byte aligned.  Supported: MHA,
+ * D = 128 (else SDPA_BWD_UNSUPPORTED), causal only with Sq == Skv (top-left, self-attention; else
+ * SDPA_BWD_UNSUPPORTED), non-causal cross-attention with any lengths.  scale <= 0 selects
+ * 1/sqrt(128).  `deterministic` selects the dQ route as for sdpa_bwd.  The workspace (256-byte
+ * aligned, at least sdpa_bwd_nvfp4_qat_workspace_size() bytes) holds Q^, K^, V^ first, then the
+ * chain's buffers.  Validation happens before any launch; the work is ordered on `stream`.
+ * `events` (or NULL) are the five stage events of sdpa_bwd_ex_events, recorded around the chain
+ * after the quantisation. */
+int sdpa_bwd_nvfp4_qat(const void* q, const void* k, const void* v, const void* o_hp,
+                       const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
+                       int H, int Sq, int Skv, int D, float scale, int causal, int deterministic,
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       void* const* events);
+/* Bytes of workspace sdpa_bwd_nvfp4_qat needs; 0 for rejected arguments and empty problems. */
+size_t sdpa_bwd_nvfp4_qat_workspace_size(int B, int H, int Sq, int Skv, int D, int causal,
+                                         int deterministic);
+
 /* Step 1 of the chain alone ("The kernel chain", dot), as the chain runs it: for every query row
  * (rows padded to Sq_pad = Sq rounded up to 32 per (b, h)) write the pair
  *     stats[(b*Hq + h)*Sq_pad + s] = { LSE * log2(e),  rowsum(O * dO) in fp32 }

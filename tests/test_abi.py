@@ -249,3 +249,28 @@ def test_run_rejections_before_launch(so):
     assert so.sdpa_bwd_run(ctypes.byref(a)) == lib.WORKSPACE_TOO_SMALL
     a.deterministic = 5
     assert so.sdpa_bwd_run(ctypes.byref(a)) == lib.INVALID_ARG
+
+
+def test_nvfp4_qat_workspace_and_rejections(so):
+    # the fake-quantised Q, K, V copies, then the chain's carve in the 4-wave layout (128-key
+    # tiles): statistics and, on the atomic route, the fp32 dQ accumulator
+    B, H, Sq, Skv = 1, 2, 200, 300
+    hat = _al(B * H * Sq * 128 * 2) + 2 * _al(B * H * Skv * 128 * 2)
+    assert lib.nvfp4_qat_workspace_size(B, H, Sq, Skv, 128, False, 0) == \
+        hat + _al(B * H * 224 * 8) + _al(B * H * Sq * 128 * 4)
+    # dS panels over 128-key tiles (Skv padded to 384)
+    assert lib.nvfp4_qat_workspace_size(B, H, Sq, Skv, 128, False, 2) == \
+        hat + _al(B * H * 224 * 8) + _al(B * H * 224 * 384 * 2)
+    assert lib.nvfp4_qat_workspace_size(B, H, Sq, Skv, 64, False, 0) == 0      # head dim 128 only
+    assert lib.nvfp4_qat_workspace_size(B, H, Sq, Skv, 128, True, 0) == 0      # causal: Sq == Skv
+    assert lib.nvfp4_qat_workspace_size(B, H, Sq, Skv, 128, False, 5) == 0
+    p = ctypes.c_void_p(4096)
+
+    def call(D=128, causal=0, det=0, Sq=64, Skv=64, ws=None, ws_bytes=0):
+        return so.sdpa_bwd_nvfp4_qat(p, p, p, p, p, p, p, p, p, 1, 2, Sq, Skv, D, 0.0, causal, det,
+                                     ws, ws_bytes, None, None)
+    assert call(D=64) == lib.UNSUPPORTED
+    assert call(causal=1, Skv=65) == lib.UNSUPPORTED
+    assert call(det=5) == lib.INVALID_ARG
+    assert call() == lib.INVALID_ARG                                  # no workspace
+    assert call(ws=p, ws_bytes=16) == lib.WORKSPACE_TOO_SMALL
