@@ -150,17 +150,22 @@ struct MainCfg {
   // relay: the running sum of the next q tile, staged one iteration ahead (each wave stages the
   // parts of the block its GEMM4 adds to)
   static constexpr int RS_BYTES = MODE == DQ_RELAY ? BR * DQK * 4 : 0;
+  // QAT: one 4 KiB fp32 P tile and 256 bytes of group scales per wave
+  static constexpr int QS_WAVE = 4096 + 256;
+  static constexpr int QS_BYTES = QAT_ ? NW * QS_WAVE : 0;
   static constexpr int NBUF =
-      (SK_BYTES + 2 * TILE_BYTES + SST_BYTES + RS_BYTES <= 160 * 1024) ? 2 : 1;
+      (SK_BYTES + 2 * TILE_BYTES + SST_BYTES + RS_BYTES + QS_BYTES <= 160 * 1024) ? 2 : 1;
   // dS staging for GEMM4, double-buffered by q-tile parity where LDS allows: GEMM4 of the previous
   // q tile then needs no barrier of its own and overlaps the other waves' work
   static constexpr int NSST =
-      (G4 && SK_BYTES + NBUF * TILE_BYTES + 2 * SST_BYTES + RS_BYTES <= 160 * 1024) ? 2 : 1;
+      (G4 && SK_BYTES + NBUF * TILE_BYTES + 2 * SST_BYTES + RS_BYTES + QS_BYTES <= 160 * 1024) ? 2
+                                                                                              : 1;
   static constexpr int OFF_K = 0;
   static constexpr int OFF_T = OFF_K + SK_BYTES;
   static constexpr int OFF_ST = OFF_T + NBUF * TILE_BYTES;
   static constexpr int OFF_RS = OFF_ST + NSST * SST_BYTES;
-  static constexpr int LDS_BYTES = OFF_RS + RS_BYTES;
+  static constexpr int OFF_QS = OFF_RS + RS_BYTES;
+  static constexpr int LDS_BYTES = OFF_QS + QS_BYTES;
   static_assert(KPW == 32, "one 32-key MFMA tile per wave (the q-tile loop body assumes it)");
   static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
   static_assert(DQK % 64 == 0 && DV % 64 == 0, "head dims must be multiples of 64");
@@ -995,7 +1000,7 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
         }
       }
       // QAT: GEMM3's P operand is the fake-quantised masked P (groups of 16 keys of a row)
-      if constexpr (C::QAT) nvfp4_p_pack(pf, pb);
+      if constexpr (C::QAT) nvfp4_p_pack_lds(pf, pb, smem + C::OFF_QS + w * C::QS_WAVE, lane);
       if constexpr (C::BIAS) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) bcur[r] = bnext[r];

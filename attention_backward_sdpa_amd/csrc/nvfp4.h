@@ -68,4 +68,47 @@ __device__ __forceinline__ void nvfp4_p_pack(const float (&pf)[16], uint32_t (&p
   for (int x = 0; x < 8; ++x) pb[x] = pack_bf16x2(pq[2 * x], pq[2 * x + 1]);
 }
 
+// The same through a wave-private LDS area `qs` of 4096 + 256 bytes, so that each group's scale is
+// computed once rather than in all 16 of its lanes: the wave's 32 x 32 fp32 P tile is written row
+// major, lane L reduces row L / 2, key group L % 2 (its four 16-byte chunks read in a rotated
+// order, which keeps every read instruction free of bank conflicts) and stores that group's scale;
+// each lane then reads the scales of its 16 rows.  Only this wave touches `qs`, and a wave's LDS
+// instructions execute in order, so no barrier is needed.
+__device__ __forceinline__ void nvfp4_p_pack_lds(const float (&pf)[16], uint32_t (&pb)[8],
+                                                 char* qs, int lane) {
+  const int g = lane >> 5, lc = lane & 31;
+  float* tile = reinterpret_cast<float*>(qs);            // [32 rows][32 keys]
+  float* sc = reinterpret_cast<float*>(qs + 4096);       // [2 groups][32 rows]
+#pragma unroll
+  for (int r = 0; r < 16; ++r) tile[acc_row<32>(r, g) * 32 + lc] = pf[r];
+  asm volatile("" ::: "memory");
+  {
+    const int row = lane >> 1, grp = lane & 1;
+    const floatx4* src = reinterpret_cast<const floatx4*>(tile + row * 32 + grp * 16);
+    float amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const floatx4 v = src[(c + row) & 3];
+      amax = fmaxf(fmaxf(amax, fmaxf(v[0], v[1])), fmaxf(v[2], v[3]));
+    }
+    sc[grp * 32 + row] = nvfp4_scale(amax);
+  }
+  asm volatile("" ::: "memory");
+  float scale[16];
+  const floatx4* scr = reinterpret_cast<const floatx4*>(sc + (lc >> 4) * 32 + g * 4);
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {  // registers 4x .. 4x+3: rows 8x + 4g + 0..3
+    const floatx4 v = scr[2 * x];
+    scale[4 * x] = v[0];
+    scale[4 * x + 1] = v[1];
+    scale[4 * x + 2] = v[2];
+    scale[4 * x + 3] = v[3];
+  }
+  float pq[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) pq[r] = scale[r] > 0.f ? nvfp4_value(pf[r], scale[r]) : 0.f;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) pb[x] = pack_bf16x2(pq[2 * x], pq[2 * x + 1]);
+}
+
 }  // namespace sdpa
