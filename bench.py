@@ -35,7 +35,7 @@ METRIC = "attention-backward TFLOP/s and % of bf16 MFMA peak, S=4096 D=128 causa
 ROUTE_NAMES = {0: "fp32 atomic", 2: "deterministic: dS panels + dq2k",
                3: "deterministic: fp32 dQ partials + ordered reduction",
                4: "deterministic: ordered relay"}
-ROUTE_STAGE = {0: "dq_convert", 2: "dq2k", 3: "dq_reduce", 4: "dq_convert"}
+ROUTE_STAGE = {0: "dq_convert", 2: "dq2k", 3: "dq_reduce", 4: "dq_reduce"}
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU (AMD's 2.5 PFLOP/s)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "main_kernel_traffic.json")
 KERNEL_SOURCES = ["bwd_main.h", "common.h", "masks.h"]

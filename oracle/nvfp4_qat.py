@@ -108,3 +108,34 @@ def qat_backward(q, k, v, o_hp, do, lse, scale, causal=False, quantize=True):
             p = _sdpa._probabilities(s, np.asarray(lse, np.float64)[b, h], vis)
             dv[b, h] = fp(p).T @ np.asarray(do, np.float64)[b, h]
     return dq, dk, dv
+
+
+def qat_backward_rows(q, k, v, o_hp, do, lse, scale, b, h, q_rows, kv_rows, causal=False):
+    """Sampled rows of the QAT backward for one (batch, head): dQ[q_rows] and (dK, dV)[kv_rows].
+    Only the score entries the equations need are formed: the listed query rows against all keys
+    for dQ; for dK and dV every query row against the listed keys, and against the whole 16-key
+    group of each listed key, since fake(P) of a key depends on its group's amax."""
+    qh = fake_nvfp4(np.asarray(q[b, h], np.float32)).astype(np.float64)
+    kh = fake_nvfp4(np.asarray(k[b, h], np.float32)).astype(np.float64)
+    vh = fake_nvfp4(np.asarray(v[b, h], np.float32)).astype(np.float64)
+    dob = np.asarray(do[b, h], np.float64)
+    lseb = np.asarray(lse[b, h], np.float64)
+    delta = np.sum(np.asarray(o_hp[b, h], np.float64) * dob, axis=1)
+    Sq, Skv = qh.shape[0], kh.shape[0]
+    vis = _sdpa.visible_mask(Sq, Skv, causal)
+    q_rows = np.asarray(q_rows)
+    p = _sdpa._probabilities(scale * (qh[q_rows] @ kh.T), lseb[q_rows], vis[q_rows])
+    ds = p * (dob[q_rows] @ vh.T - delta[q_rows][:, None])
+    dq = scale * (ds @ kh)
+    dk = np.zeros((len(kv_rows), kh.shape[1]))
+    dv = np.zeros((len(kv_rows), vh.shape[1]))
+    for n, j in enumerate(kv_rows):
+        g0 = (j // GROUP) * GROUP
+        cols = np.arange(g0, min(g0 + GROUP, Skv))
+        pg = _sdpa._probabilities(scale * (qh @ kh[cols].T), lseb, vis[:, cols])
+        pq = fake_nvfp4(pg.astype(np.float32)).astype(np.float64)  # the group's fake(P), rows
+        c = j - g0
+        dv[n] = pq[:, c] @ dob
+        dsj = pg[:, c] * (dob @ vh[j] - delta)
+        dk[n] = scale * (dsj @ qh)
+    return dq, dk, dv

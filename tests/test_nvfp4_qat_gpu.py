@@ -97,3 +97,42 @@ def test_nvfp4_qat_dv_uses_quantised_probability():
     assert C.max_rel_err(plain[2].astype(np.float32), ref[2]) > 5e-2
     got, _ = _run(w, inp, o_bits, lse, 0)
     assert C.max_rel_err(got[2], plain[2]) > 5e-2
+
+
+@pytest.mark.parametrize("det", [0, 2], ids=["atomic", "dspanels"])
+def test_nvfp4_qat_fullsize_sampled_rows(det):
+    # the QAT page's example shape, B1 H16 S4096 D128 non-causal (and its causal variant on the
+    # atomic route), in the launch configuration bench.py --qat times: sampled rows of three heads
+    import bench
+    from oracle import nvfp4_qat as Q
+    w = W["qat_mha_s4096_d128"]
+    for causal in ([False, True] if det == 0 else [False]):
+        wc = V(w, causal=causal)
+        C.log(f"qat full size causal={causal} route {det}: drawing inputs")
+        inp = synth.draw_inputs(wc)
+        f32 = lambda bits: synth.bf16_to_f32(bits)
+        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        hat = {x: bf(synth.bf16_bits(oracle.fake_nvfp4(f32(getattr(inp, x))))) for x in ("q", "k", "v")}
+        C.log("qat full size: float32 forward of the fake-quantised inputs for O_hp and LSE")
+        o, lse = bench.gpu_forward_inputs(torch, hat["q"], hat["k"], hat["v"], wc, None)
+        q, k, v, do = bf(inp.q), bf(inp.k), bf(inp.v), bf(inp.do)
+        outs = [torch.empty_like(x) for x in (q, k, v)]
+        import attention_backward_sdpa_amd as lib
+        n = lib.nvfp4_qat_workspace_size(w.B, w.Hq, w.Sq, w.Skv, 128, causal, det)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        C.log("qat full size: GPU chain")
+        lib.sdpa_bwd_nvfp4_qat(q, k, v, o, do, lse, *outs, scale=w.softmax_scale, causal=causal,
+                               deterministic=det, workspace=ws)
+        torch.cuda.synchronize()
+        got = [C.bf16_tensor_to_f32(x) for x in outs]
+        o_h = synth.bf16_to_f32(o.cpu().view(torch.int16).numpy().view(np.uint16))
+        lse_h = lse.cpu().numpy()
+        xs = [f32(inp.q), f32(inp.k), f32(inp.v)]
+        rows = [0, 1, 15, 16, 31, 32, 127, 128, 2047, 4064, 4095]
+        for h in (0, 7, 15):
+            C.log(f"qat full size: oracle rows of head {h}")
+            dq, dk, dv = Q.qat_backward_rows(*xs, o_h, f32(inp.do), lse_h, w.softmax_scale, 0, h,
+                                             rows, rows, causal=causal)
+            for tname, g, r in (("dQ", got[0][0, h, rows], dq), ("dK", got[1][0, h, rows], dk),
+                                ("dV", got[2][0, h, rows], dv)):
+                C.assert_close(f"qat full size causal={causal} route {det} head {h} {tname}", g, r)

@@ -136,3 +136,17 @@ def test_qat_backward_without_quantisation_is_plain_backward():
     ref = oracle.backward(f(q), f(k), f(v), o, f(do), lse, 0.3)
     for a, b in zip(got, ref):
         assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal,Sq,Skv", [(True, 70, 70), (False, 50, 83)])
+def test_qat_sampled_rows_match_full_backward(causal, Sq, Skv):
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((1, 2, Sq, 32)).astype(np.float32)
+    k, v = (rng.standard_normal((1, 2, Skv, 32)).astype(np.float32) for _ in range(2))
+    do = rng.standard_normal((1, 2, Sq, 32)).astype(np.float32)
+    o, lse = oracle.qat_forward(q, k, v, 0.3, causal=causal)
+    full = oracle.qat_backward(q, k, v, o, do, lse, 0.3, causal=causal)
+    qr, kr = [0, 17, Sq - 1], [0, 15, 16, Skv - 1]
+    rows = Q.qat_backward_rows(q, k, v, o, do, lse, 0.3, 0, 1, qr, kr, causal=causal)
+    for got, ref in zip(rows, (full[0][0, 1, qr], full[1][0, 1, kr], full[2][0, 1, kr])):
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
