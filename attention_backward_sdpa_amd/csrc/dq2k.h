@@ -82,10 +82,16 @@ __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
   // Longest-first: under a causal mask the last q tiles see the most keys, so they go first.
   const int nbh = p.B * p.Hq;
   const int n_groups = (p.n_q_tiles + QT - 1) / QT;
-  const int bh = blockIdx.x % nbh;
+  // Consecutive workgroups take the (batch, KV head) pairs first and the group's query heads
+  // second (slot = member * B*Hkv + b*Hkv + kvh), so with B*Hkv a multiple of the 8 XCDs the query
+  // heads sharing a K land on one XCD (workgroup n runs on XCD n % 8) and its K reads hit that L2.
+  const int slot = blockIdx.x % nbh;
   const int grp = n_groups - 1 - (int)(blockIdx.x / nbh);
-  const int h = bh % p.Hq, b = bh / p.Hq;
-  const int kvh = h / p.group;
+  const int nbkv = p.B * p.Hkv;
+  const int member = slot / nbkv, bk = slot % nbkv;
+  const int b = bk / p.Hkv, kvh = bk % p.Hkv;
+  const int h = kvh * p.group + member;
+  const int bh = b * p.Hq + h;
   const int i0 = grp * QT;
 
   MaskGeom mg;

@@ -38,7 +38,7 @@ ROUTE_NAMES = {0: "fp32 atomic", 2: "deterministic: dS panels + dq2k",
 ROUTE_STAGE = {0: "dq_convert", 2: "dq2k", 3: "dq_reduce", 4: "dq_reduce"}
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU (AMD's 2.5 PFLOP/s)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "main_kernel_traffic.json")
-KERNEL_SOURCES = ["bwd_main.h", "common.h", "masks.h"]
+KERNEL_SOURCES = ["bwd_main.h", "common.h", "masks.h", "nvfp4.h"]
 
 
 def kernel_source_hash():
