@@ -1,8 +1,9 @@
 // Fused five-GEMM attention-backward main kernel for gfx950.
 //
-// "SDPA Backward (SM120)", section "Main-kernel pipeline: KV-stationary, five chained GEMMs": one
-// workgroup owns one KV tile of one query head (its KV head is q_head / group), loads K and V once
-// and walks the visible q tiles in descending order.  Per q tile:
+// "SDPA Backward (SM120)", section "Main-kernel pipeline: KV-stationary, five chained GEMMs": each
+// workgroup holds one key/value tile for one query head (the K and V rows of KV head
+// q_head / group), reads it a single time, then visits the q tiles that can see it, last first.
+// Per q tile:
 //     GEMM1  S  = Q K^T                       P  = exp2(S * scale * log2e - LSE * log2e)
 //     GEMM2  dP = dO V^T                      dS = P * (dP - delta)
 //     GEMM3  dV += P^T dO      (bf16 P)

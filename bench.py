@@ -42,10 +42,16 @@ KERNEL_SOURCES = ["bwd_main.h", "common.h", "masks.h", "nvfp4.h"]
 
 
 def kernel_source_hash():
+    """Hash of the main kernel's sources with comments and whitespace removed, so that the traffic
+    record stays valid across edits that do not change the code."""
+    import re
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "attention_backward_sdpa_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "attention_backward_sdpa_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,9 +1,9 @@
 /*
  * sdpa_bwd.h -- C ABI of the MI355X (gfx950) scaled-dot-product-attention backward library.
  *
- * The operation ("SDPA Backward (SM120)", sections "Overview" and "API Usage"): given the forward
- * activations Q, K, V, O, the loss gradient dO and the forward's natural-log log-sum-exp LSE,
- * produce dQ, dK, dV of softmax(scale * Q K^T + mask) V, with
+ * The operation ("SDPA Backward (SM120)", sections "Overview" and "API Usage"): from the forward
+ * pass's inputs and output (Q, K, V, O), the gradient that reaches O (dO) and the forward's
+ * log-sum-exp in natural log (LSE), compute dQ, dK, dV of softmax(scale * Q K^T + mask) V, with
  *     P     = exp(scale * Q K^T - LSE)                (replayed from LSE; masked pairs give 0)
  *     delta = rowsum(O * dO)                           ("The kernel chain")
  *     dS    = P * (dO V^T - delta)                     (unscaled softmax VJP)

@@ -1,6 +1,6 @@
 """GPU parity for head dims outside the native kernel sizes ("SDPA Backward (SM120)", "Support
-surface": any multiple of 8 up to 256 computes on the next supported size, reading zeros past
-the actual extent; rectangular d_qk >= d_v).  Each case runs the whole chain on tensors whose
+surface": head dims that are multiples of 8 up to 256 run on the next larger native kernel, which
+sees zeros beyond the actual head dim; d_qk >= d_v).  Each case runs the whole chain on tensors whose
 head dim is the actual one (rows Dqk / Dv elements long, or strided views) and is compared with
 the fp64 oracle on every dQ route, max|err| <= 1e-2 * max|ref| per tensor; every output element
 is overwritten (outputs start as NaN)."""
