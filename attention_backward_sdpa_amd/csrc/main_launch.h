@@ -3,6 +3,8 @@
 // a translation unit of their own (main_d<DQK>.hip), so the library's objects compile in
 // parallel; the host side (sdpa_bwd.hip) calls launch_main_dqk<DQK>.
 #pragma once
+#include <atomic>
+
 #include "bwd_main.h"
 
 namespace sdpa {
@@ -23,15 +25,25 @@ template <int DQK>
 hipError_t launch_main_dqk(const MainParams& mp, DqMode mode, bool f16, int bias, int grid, int bc,
                            hipStream_t s, bool qat = false);
 
+// Raise a kernel's dynamic-LDS limit to `bytes`, once per device (the attribute is set for the
+// current device); Tag names the kernel instantiation.
+template <class Tag, class F>
+hipError_t lds_limit_once(F* kernel, int bytes) {
+  static std::atomic<uint64_t> done{0};  // bit d: set on device d (devices >= 64: every call)
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t{1} << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
 template <class C>
 hipError_t launch_main_cfg(const MainParams& mp, int grid, hipStream_t s) {
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)bwd_main_kernel<C>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  const hipError_t e = lds_limit_once<C>(bwd_main_kernel<C>, C::LDS_BYTES);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_main_kernel<C>, dim3(grid), dim3(C::NT), C::LDS_BYTES, s, mp);
   return hipGetLastError();
 }

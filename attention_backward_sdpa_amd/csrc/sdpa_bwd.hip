@@ -102,14 +102,17 @@ Route route_for(int deterministic, int Dqk, const Geometry& g) {
 
 // Item queues of the relay: one per XCD of the current device (1..8), queried once per device.
 int relay_queues() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];  // 0 until queried
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 1;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 1;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || n < 1) n = 1;
   n = n > 8 ? 8 : n;
-  if (dev < 64) cached[dev] = n;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
@@ -215,13 +218,8 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
 
 template <class C>
 hipError_t launch_dq2k(const Dq2kParams& dp, int grid, hipStream_t s) {
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)dq2k_kernel<C>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  const hipError_t e = lds_limit_once<C>(dq2k_kernel<C>, C::LDS_BYTES);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(dq2k_kernel<C>, dim3(grid), dim3(C::NT), C::LDS_BYTES, s, dp);
   return hipGetLastError();
 }
