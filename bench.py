@@ -251,6 +251,9 @@ def main():
                     help="the NVFP4 attention-QAT backward (sdpa_bwd_nvfp4_qat) on the workload's "
                          "shape (MHA, head dim 128, no window or padding); O and LSE come from the "
                          "forward on the unquantised inputs, which changes no timed work")
+    ap.add_argument("--dims", default=None, metavar="DQK,DV",
+                    help="override the workload's head dims (multiples of 8 up to 256, DV <= DQK: "
+                         "other than the native pairs they run on the next native kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run a plain 1 GiB fp32 copy kernel three times "
@@ -278,6 +281,9 @@ def main():
     import attention_backward_sdpa_amd as lib
 
     w = synth.WORKLOADS[args.workload]
+    if args.dims:
+        dqk, dv = (int(x) for x in args.dims.split(","))
+        w = synth.small_variant(w, Dqk=dqk, Dv=dv, name=f"{w.name}_dims{dqk}x{dv}")
     det = int(w.deterministic) if args.deterministic < 0 else args.deterministic
     route = lib.dq_route(w.Dqk, w.Dv, det)
     if route < 0:
