@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc", "sdpa_bwd.hip")
 # translation units: the host side with the small kernels, and the main kernel's instantiations
 # of each kernel head dim (the bulk of the compile time), built in parallel
-SOURCES = [SRC] + [os.path.join(HERE, "csrc", f"main_d{d}.hip") for d in (64, 128, 192, 256)]
+SOURCES = [SRC] + [os.path.join(HERE, "csrc", f"main_d{d}.hip") for d in (32, 64, 128, 192, 256)]
 OUT = os.path.join(HERE, "libsdpa_bwd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

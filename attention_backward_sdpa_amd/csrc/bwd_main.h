@@ -138,8 +138,11 @@ struct MainCfg {
   // kernel 350 -> 385 us on the dQ-partial route, head dim 192 724 -> 809 us on the atomic
   // route), because the waves without a tile start the next q tile early and so offset the two
   // waves of each SIMD between their softmax and MFMA phases.
-  static constexpr bool G4_16 = G4 && N_DQT < 4 && ((DQK / 8) % NW) == 0;
-  static constexpr int NB4 = (DQK / 8) / NW;
+  // Head dim 32 has only DQK / 8 = 4 blocks: waves 0-3 take one each, the others none.
+  static constexpr int G4_BLOCKS = DQK / 8;
+  static constexpr bool G4_16 =
+      G4 && N_DQT < 4 && (G4_BLOCKS % NW == 0 || NW % G4_BLOCKS == 0);
+  static constexpr int NB4 = G4_BLOCKS >= NW ? G4_BLOCKS / NW : 1;
   static constexpr int N_KQ = DQK / 16, N_KV = DV / 16;
   // q-tile buffer: [Q A-frags | dO A-frags | stats], fragments swizzled (see gather_frags)
   static constexpr int T_QA = 0;
@@ -169,7 +172,7 @@ struct MainCfg {
   static constexpr int LDS_BYTES = OFF_QS + QS_BYTES;
   static_assert(KPW == 32, "one 32-key MFMA tile per wave (the q-tile loop body assumes it)");
   static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
-  static_assert(DQK % 64 == 0 && DV % 64 == 0, "head dims must be multiples of 64");
+  static_assert(DQK % 32 == 0 && DV % 32 == 0, "head dims must be multiples of 32");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -554,6 +557,7 @@ __device__ __forceinline__ void gemm4_16(const char* sST, const char* sK, float*
                                          bool add = false) {
   using M16 = Mfma16<C::F16>;
   constexpr int DQK = C::DQK, NB = C::NB4, NW = C::NW;
+  if (w >= C::G4_BLOCKS) return;  // head dim 32: waves past the 4 blocks have none
   const Gemm4Lanes16 tl(lane, w);
   floatx4 acc[NB];
 #pragma unroll
@@ -878,7 +882,7 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
     auto relay_stage = [&](int i_t) {
       if constexpr (C::MODE == DQ_RELAY) {
         const int rk = relay_rank(i_t);
-        const bool has_part = C::G4_16 || w < C::N_DQT;
+        const bool has_part = C::G4_16 ? w < C::G4_BLOCKS : w < C::N_DQT;
         if (rk > 0 && has_part) {
           relay_wait(relay_turn(i_t), rk, p.relay_ctl, lane);
           const rsrc_t src = buf_rsrc(dq_dst(i_t), BR * DQK * 4);

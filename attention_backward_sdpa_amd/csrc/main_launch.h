@@ -96,6 +96,7 @@ hipError_t launch_main_dqk(const MainParams& mp, DqMode mode, bool f16, int bias
 #define SDPA_MAIN_DQK(D)                                                                           \
   extern template hipError_t launch_main_dqk<D>(const MainParams&, DqMode, bool, int, int, int,    \
                                                 hipStream_t, bool);
+SDPA_MAIN_DQK(32)
 SDPA_MAIN_DQK(64)
 SDPA_MAIN_DQK(128)
 SDPA_MAIN_DQK(192)

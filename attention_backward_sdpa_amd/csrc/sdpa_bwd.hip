@@ -37,7 +37,7 @@ struct Geometry {
 // extent): the smallest supported pair covering both.  Dv <= Dqk.
 bool kernel_dims(int Dqk, int Dv, int* kq, int* kv) {
   if (Dqk < 8 || Dv < 8 || Dqk > 256 || Dv > Dqk || (Dqk & 7) || (Dv & 7)) return false;
-  static const int pairs[4][2] = {{64, 64}, {128, 128}, {192, 128}, {256, 256}};
+  static const int pairs[5][2] = {{32, 32}, {64, 64}, {128, 128}, {192, 128}, {256, 256}};
   for (const auto& pr : pairs)
     if (Dqk <= pr[0] && Dv <= pr[1]) {
       *kq = pr[0];
@@ -50,7 +50,8 @@ bool kernel_dims(int Dqk, int Dv, int* kq, int* kv) {
 // With an additive bias every head dim runs the 4-wave layout (512 registers per wave): the
 // bias values of the next q tile are held in registers while the current one computes.
 bool geometry_for(int Dqk, int Dv, Geometry* g, bool bias = false) {
-  if (Dqk == 64 && Dv == 64) *g = {8, 32, 256, 32};
+  if (Dqk == 32 && Dv == 32) *g = {8, 32, 256, 32};
+  else if (Dqk == 64 && Dv == 64) *g = {8, 32, 256, 32};
   else if (Dqk == 128 && Dv == 128) *g = {8, 32, 256, 32};
   else if (Dqk == 192 && Dv == 128) *g = {8, 32, 256, 32};
   else if (Dqk == 256 && Dv == 256) *g = {4, 32, 128, 32};
@@ -232,6 +233,7 @@ hipError_t run_main(int Dqk, const MainParams& mp, Route route, bool f16, int bi
                       : route == R_DQP ? DQ_PARTIAL
                       : route == R_RELAY ? DQ_RELAY
                                          : DQ_ATOMIC;
+  if (Dqk == 32) return launch_main_dqk<32>(mp, mode, f16, bias, grid, bc, s, qat);
   if (Dqk == 64) return launch_main_dqk<64>(mp, mode, f16, bias, grid, bc, s, qat);
   if (Dqk == 128) return launch_main_dqk<128>(mp, mode, f16, bias, grid, bc, s, qat);
   if (Dqk == 192) return launch_main_dqk<192>(mp, mode, f16, bias, grid, bc, s, qat);
@@ -242,14 +244,17 @@ hipError_t run_main(int Dqk, const MainParams& mp, Route route, bool f16, int bi
 // 8- and 4-wave layouts of a head dim write the same one)
 template <int DQK, int DV, int NW>
 constexpr bool partial_l16() { return MainCfg<DQK, DV, 32, NW, DQ_PARTIAL>::G4_16; }
-static_assert(partial_l16<64, 64, 8>() == partial_l16<64, 64, 4>() &&
+static_assert(partial_l16<32, 32, 8>() == partial_l16<32, 32, 4>() &&
+                  partial_l16<64, 64, 8>() == partial_l16<64, 64, 4>() &&
                   partial_l16<128, 128, 8>() == partial_l16<128, 128, 4>() &&
                   partial_l16<192, 128, 8>() == partial_l16<192, 128, 4>(),
               "one partial-block layout per head dim");
 
 template <bool F16>
 hipError_t launch_dq_reduce_t(const DqReduceParams& rp, int Dqk, int grid, hipStream_t s) {
-  if (Dqk == 64)
+  if (Dqk == 32)
+    hipLaunchKernelGGL((dq_reduce_kernel<32, F16, partial_l16<32, 32, 8>()>), dim3(grid), dim3(64), 0, s, rp);
+  else if (Dqk == 64)
     hipLaunchKernelGGL((dq_reduce_kernel<64, F16, partial_l16<64, 64, 8>()>), dim3(grid), dim3(128), 0, s, rp);
   else if (Dqk == 128)
     hipLaunchKernelGGL((dq_reduce_kernel<128, F16, partial_l16<128, 128, 8>()>), dim3(grid), dim3(256), 0, s, rp);
@@ -291,7 +296,8 @@ hipError_t run_dq2k(int Dqk, bool f16, const Dq2kParams& dp, int bc, hipStream_t
 
 template <bool F16>
 hipError_t launch_convert_t(const ConvertParams& cp, int Dqk, int grid, hipStream_t s) {
-  if (Dqk == 64) hipLaunchKernelGGL((dq_convert_kernel<64, F16>), dim3(grid), dim3(256), 0, s, cp);
+  if (Dqk == 32) hipLaunchKernelGGL((dq_convert_kernel<32, F16>), dim3(grid), dim3(256), 0, s, cp);
+  else if (Dqk == 64) hipLaunchKernelGGL((dq_convert_kernel<64, F16>), dim3(grid), dim3(256), 0, s, cp);
   else if (Dqk == 128) hipLaunchKernelGGL((dq_convert_kernel<128, F16>), dim3(grid), dim3(256), 0, s, cp);
   else if (Dqk == 192) hipLaunchKernelGGL((dq_convert_kernel<192, F16>), dim3(grid), dim3(256), 0, s, cp);
   else hipLaunchKernelGGL((dq_convert_kernel<256, F16>), dim3(grid), dim3(256), 0, s, cp);
@@ -309,7 +315,8 @@ hipError_t launch_dq_reduce(const DqReduceParams& rp, int Dqk, bool f16, int gri
 template <bool F16>
 void launch_preprocess_t(const PreParams& pp, int Dv, dim3 grid, hipStream_t s) {
   const dim3 block(256);
-  if (Dv == 64) hipLaunchKernelGGL((preprocess_kernel<64, F16>), grid, block, 0, s, pp);
+  if (Dv == 32) hipLaunchKernelGGL((preprocess_kernel<32, F16>), grid, block, 0, s, pp);
+  else if (Dv == 64) hipLaunchKernelGGL((preprocess_kernel<64, F16>), grid, block, 0, s, pp);
   else if (Dv == 128) hipLaunchKernelGGL((preprocess_kernel<128, F16>), grid, block, 0, s, pp);
   else hipLaunchKernelGGL((preprocess_kernel<256, F16>), grid, block, 0, s, pp);
 }
@@ -624,7 +631,8 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     dp.n_q_tiles = (int)(c.sq_pad / geo.br);
     dp.dqk_act = Dqk;
     dp.scale = scale;
-    e = run_dq2k(KDqk, f16, dp, geo.bc, stream);
+    // head dim 32 runs dq2k's 64-wide kernel: K's extra columns reach only unstored dQ columns
+    e = run_dq2k(KDqk == 32 ? 64 : KDqk, f16, dp, geo.bc, stream);
     if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   }
   rec(4);

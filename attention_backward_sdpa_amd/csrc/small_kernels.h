@@ -52,6 +52,7 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
 
   for (int r0 = 0; r0 < BR; r0 += RPP) {
     const int r = r0 + tid / LPR, sub = tid % LPR, s = q0 + r;
+    if (r >= BR) break;  // head dim 32: one pass covers 64 rows, the tile has 32
     const bool live = s < Lq;
     const int64_t row = bh * p.Sq + s;
     float acc = 0.f;

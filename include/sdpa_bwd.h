@@ -21,9 +21,9 @@
  * pointers must be 16-byte aligned (lse 4-byte aligned) and the workspace 256-byte aligned; a
  * tensor with no elements may be NULL.  Head dims ("Support surface"): Dqk and Dv multiples of 8
  * with 8 <= Dv <= Dqk <= 256.  A call computes on the kernel head dims (Kqk, Kv), the first of
- * (64,64), (128,128), (192,128), (256,256) that covers (Dqk, Dv): those four run as they are, any
- * other pair reads the operand columns past its head dims as zeros and writes no column past them
- * (so the gaps of a strided layout are left untouched).  Empty problems (B, Sq or Skv zero) need
+ * (32,32), (64,64), (128,128), (192,128), (256,256) that covers (Dqk, Dv): those five run as they
+ * are, any other pair reads the operand columns past its head dims as zeros and writes no column
+ * past them (so the gaps of a strided layout are left untouched).  Empty problems (B, Sq or Skv zero) need
  * no workspace: the gradients that have elements are written as zeros.
  *
  * Masks ("API Usage" and "Causal, sliding-window, and padding masks"): query q and key k are
@@ -57,7 +57,7 @@
  *      turn is ever abandoned (it is bounded), or not every work item ran, dq is written as NaN;
  *   1  deterministic, the library's choice between 2 and 3: 3 where its workspace holds fewer
  *      bytes per (KV tile, q row) (Kqk fp32 partials against the key tile's bf16 dS values),
- *      else 2 (kernel head dim 64 takes 3; 128, 192 and 256 take 2).
+ *      else 2 (kernel head dims 32 and 64 take 3; 128, 192 and 256 take 2).
  * Routes 1-4 make dq, dk, dv bitwise reproducible run to run; dK and dV are reproducible on every
  * route.  Any other value gives SDPA_BWD_INVALID_ARG.
  */

@@ -59,6 +59,10 @@ def test_dq_route_choice(so):
     # head dims that are multiples of 8 up to 256 run on the next supported size
     assert lib.dq_route(96, 96, 1) == lib.dq_route(128, 128, 1)
     assert lib.dq_route(40, 40, 1) == lib.dq_route(64, 64, 1)
+    # head dim 32 has its own kernel (256-key tiles): the dQ-partial route is the deterministic
+    # choice (32 fp32 per q row < 256 bf16 dS values)
+    assert lib.dq_route(32, 32, 1) == lib.DQ_PARTIALS
+    assert lib.dq_route(24, 24, 1) == lib.dq_route(16, 8, 1) == lib.DQ_PARTIALS
     for bad in ((100, 100), (264, 264), (128, 192), (4, 4)):
         assert lib.dq_route(*bad, 0) == -1
 
@@ -120,6 +124,8 @@ def test_workspace_size_rules(so):
     assert _ws(Hkv=3) == 0
     # head dims that are multiples of 8 up to 256 use the next supported size's workspace
     assert _ws(Dqk=96, Dv=96) == _ws(Dqk=128, Dv=128)
+    assert _ws(Dqk=24, Dv=16) == _ws(Dqk=32, Dv=32) < _ws(Dqk=64, Dv=64)
+    assert _ws(Dqk=40, Dv=40) == _ws(Dqk=64, Dv=64)
     assert _ws(Dqk=176, Dv=104) == _ws(Dqk=192, Dv=128)
     assert _ws(Dqk=160, Dv=160) == _ws(Dqk=256, Dv=256)
     assert _ws(Dqk=100, Dv=100) == 0 and _ws(Dqk=272, Dv=272) == 0

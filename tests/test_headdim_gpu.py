@@ -18,11 +18,15 @@ W = synth.WORKLOADS
 V = synth.small_variant
 
 CASES = {
-    # (Dqk, Dv) -> kernel size: 96 -> 128, 40 -> 64, 32 -> 64, 72/56 -> 128/128, 176/104 -> 192/128,
+    # (Dqk, Dv) -> kernel size: 96 -> 128, 40 -> 64, 32 native, 24 -> 32, 32/16 -> 32/32,
+    # 72/56 -> 128/128, 176/104 -> 192/128,
     # 160 -> 256, 248 -> 256
     "d96_gqa_causal_s300": V(W["gqa_causal_s4096_d128"], Hq=4, Hkv=2, Sq=300, Skv=300, Dqk=96, Dv=96),
     "d40_s200": V(W["mha_s128_d64"], Sq=200, Skv=200, Dqk=40, Dv=40),
     "d32_causal_s257": V(W["mha_causal_s2048_d128"], B=1, Hq=2, Hkv=2, Sq=257, Skv=257, Dqk=32, Dv=32),
+    "d24_s230": V(W["mha_s128_d64"], Sq=230, Skv=230, Dqk=24, Dv=24),
+    "d32x16_window_padded_s280": V(W["mla_window_padded_s4096"], B=2, Hq=2, Hkv=1, Sq=280, Skv=280,
+                                   window_left=50, len_lo=120, Dqk=32, Dv=16),
     "d72x56_window_padded_s280": V(W["mla_window_padded_s4096"], B=2, Hq=2, Hkv=1, Sq=280, Skv=280,
                                    window_left=70, len_lo=120, Dqk=72, Dv=56),
     "d176x104_causal_s300": V(W["mla_window_padded_s4096"], B=1, Hq=2, Hkv=2, Sq=300, Skv=300,

@@ -51,6 +51,8 @@ SMALL_CASES = {
     # split ranges under GQA on the deterministic route
     "det_gqa_split_d128_s700": V(W["gqa_causal_s4096_d128"], Hq=4, Hkv=2, Sq=700, Skv=700,
                                  deterministic=True),
+    # head dim 32 (its own kernel: 16 x 16 GEMM4 blocks on four of the eight waves), causal GQA
+    "d32_gqa_causal_s300": V(W["gqa_causal_s4096_d128"], Hq=4, Hkv=2, Sq=300, Skv=300, Dqk=32, Dv=32),
     # split ranges with the 4-wave MLA kernel, a window and padding
     "mla_split_window_padded_s900": V(W["mla_window_padded_s4096"], B=2, Hq=2, Hkv=2, Sq=900,
                                       Skv=900, window_left=300, len_lo=500),
