@@ -53,11 +53,13 @@ def test_headdim_envelope_parity(name, det):
             assert np.all(got[2][b, :, L:] == 0)
 
 
-def test_headdim_envelope_bshd_layout_and_gaps():
+@pytest.mark.parametrize("name", ["d96_gqa_causal_s300", "d32_causal_s257"])
+def test_headdim_envelope_bshd_layout_and_gaps(name):
     # BSHD storage with a 16-element gap after each row: the gap columns of the inputs hold 7.0
     # and must not reach the result; those of the outputs hold NaN and must not be written
     import attention_backward_sdpa_amd as lib
-    w = CASES["d96_gqa_causal_s300"]
+    w = CASES[name]
+    C.log(f"bshd layout with gaps: {name}")
     case = C.make_case(w)
     ref = C.oracle_backward(case)
     pad = 16
@@ -85,13 +87,25 @@ def test_headdim_envelope_bshd_layout_and_gaps():
     lib.sdpa_bwd_run(t["q"], t["k"], t["v"], t["o"], t["do"], lse, *outs, workspace=ws, **kw)
     torch.cuda.synchronize()
     for tname, g, st, r in zip(("dQ", "dK", "dV"), outs, out_st, ref):
-        C.assert_close(f"bshd d96 {tname}", g.float().cpu().numpy(), r)
+        C.assert_close(f"bshd {name} {tname}", g.float().cpu().numpy(), r)
         assert bool(torch.isnan(st[..., g.shape[-1]:].float()).all()), f"{tname} gap written"
 
 
-def test_headdim_envelope_with_bias_fp16():
+BIAS_CASES = {
+    "d72x56_window_padded_s280": CASES["d72x56_window_padded_s280"],
+    # the native head-dim-32 kernel with bias, fp16, window and per-batch lengths
+    "d32_window_padded_s200": V(W["mla_window_padded_s4096"], B=2, Hq=2, Hkv=1, Sq=200, Skv=200,
+                                window_left=50, len_lo=90, Dqk=32, Dv=32),
+}
+
+
+@pytest.mark.parametrize("name,det", [("d72x56_window_padded_s280", 0),
+                                      ("d32_window_padded_s200", 0),
+                                      ("d32_window_padded_s200", 3)])
+def test_headdim_envelope_with_bias_fp16(name, det):
     import attention_backward_sdpa_amd as lib
-    w = CASES["d72x56_window_padded_s280"]
+    w = BIAS_CASES[name]
+    C.log(f"bias fp16 case {name} route {det}: {w}")
     inp = synth.draw_inputs(w, dtype="fp16")
     f = lambda x: synth.bits_to_f32(x, "fp16").astype(np.float64)
     lens = [int(x) for x in inp.seq_q_lens]
@@ -109,11 +123,11 @@ def test_headdim_envelope_with_bias_fp16():
     outs = [torch.full_like(x, float("nan")) for x in (q, k, v)]
     dbias = torch.full((w.B, w.Hq, w.Sq, w.Skv), float("nan"), device="cuda")
     tl = torch.tensor(lens, dtype=torch.int32, device="cuda")
-    args = dict(scale=w.softmax_scale, causal=True, window_left=w.window_left, deterministic=0,
+    args = dict(scale=w.softmax_scale, causal=True, window_left=w.window_left, deterministic=det,
                 seq_q_lens=tl, seq_kv_lens=tl, bias=torch.from_numpy(bias32).cuda(), dbias=dbias)
     n = lib.run_workspace_size(q, k, v, **args)
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
     lib.sdpa_bwd_run(q, k, v, o, do, torch.from_numpy(lse).cuda(), *outs, workspace=ws, **args)
     torch.cuda.synchronize()
     for tname, g, r in zip(("dQ", "dK", "dV", "dBias"), outs + [dbias], ref):
-        C.assert_close(f"fp16 d72x56 bias {tname}", g.float().cpu().numpy(), r)
+        C.assert_close(f"fp16 {name} bias route {det} {tname}", g.float().cpu().numpy(), r)
