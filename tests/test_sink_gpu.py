@@ -27,6 +27,9 @@ CASES = {
                                 window_left=100, len_lo=100),
     # non-causal D = 64, more rows than the dsink kernel's threads per head
     "mha_d64_b3_s700": V(W["mha_s128_d64"], B=3, Hq=2, Hkv=2, Sq=700, Skv=300),
+    # the native head-dim-32 kernel, GQA, cross-attention lengths
+    "gqa_d32_s290x170": V(W["gqa_causal_s4096_d128"], Hq=4, Hkv=1, Sq=290, Skv=170, causal=False,
+                          Dqk=32, Dv=32),
 }
 
 
