@@ -79,8 +79,10 @@ def _load():
     lib.sdpa_bwd_nvfp4_qat.restype = i
     lib.sdpa_bwd_nvfp4_qat_workspace_size.argtypes = [i] * 7
     lib.sdpa_bwd_nvfp4_qat_workspace_size.restype = sz
-    lib.sdpa_bwd_dq_route.argtypes = [i, i, i]
+    lib.sdpa_bwd_dq_route.argtypes = [i] * 8
     lib.sdpa_bwd_dq_route.restype = i
+    lib.sdpa_bwd_run_dq_route.argtypes = [ctypes.POINTER(Args)]
+    lib.sdpa_bwd_run_dq_route.restype = i
     lib.sdpa_bwd_status_string.argtypes = [i]
     lib.sdpa_bwd_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -128,10 +130,11 @@ def workspace_size(B, Hq, Hkv, Sq, Skv, Dqk, Dv, causal=False, window_left=-1,
                                                int(has_seqlens)))
 
 
-def dq_route(Dqk, Dv, deterministic) -> int:
-    """sdpa_bwd_dq_route(): the dQ route (DQ_ATOMIC, DQ_DS_PANELS, DQ_PARTIALS or DQ_RELAY) a call takes,
-    -1 for unsupported arguments."""
-    return int(_load().sdpa_bwd_dq_route(int(Dqk), int(Dv), int(deterministic)))
+def dq_route(B, Hq, Hkv, Sq, Skv, Dqk, Dv, deterministic) -> int:
+    """sdpa_bwd_dq_route(): the dQ route (DQ_ATOMIC, DQ_DS_PANELS, DQ_PARTIALS or DQ_RELAY) a call
+    with these sizes takes, -1 for unsupported arguments."""
+    return int(_load().sdpa_bwd_dq_route(int(B), int(Hq), int(Hkv), int(Sq), int(Skv), int(Dqk),
+                                         int(Dv), int(deterministic)))
 
 
 def _dims(q, k, v):
@@ -249,6 +252,12 @@ def run_workspace_size(q, k, v, **kw) -> int:
     return int(_load().sdpa_bwd_run_workspace_size(ctypes.byref(a)))
 
 
+def run_dq_route(q, k, v, **kw) -> int:
+    """sdpa_bwd_run_dq_route() for a call on these q, k, v and keyword arguments."""
+    a = run_args(q, k, v, q, q, None, q, k, v, stream=False, **kw)
+    return int(_load().sdpa_bwd_run_dq_route(ctypes.byref(a)))
+
+
 def sdpa_bwd_run(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, window_left=-1,
                  deterministic=False, seq_q_lens=None, seq_kv_lens=None,
                  causal_bottom_right=False, window_right=0, sink=None, dsink=None, bias=None,
@@ -294,7 +303,13 @@ def sdpa_bwd_preprocess(o, do, lse, stats, dq_accum=None, seq_q_lens=None, Dqk=0
 def attention_backward(q, k, v, o, do, lse, scale=None, causal=False, window_left=-1,
                        deterministic=False, seq_q_lens=None, seq_kv_lens=None,
                        causal_bottom_right=False, window_right=0, stream=None):
-    """Allocate dq/dk/dv and the workspace with torch, then run sdpa_bwd_ex; returns (dq, dk, dv)."""
+    """Allocate dq/dk/dv and the workspace with torch, then run sdpa_bwd_ex; returns (dq, dk, dv).
+
+    The chain is enqueued on `stream` (default: torch's current stream), and dq, dk, dv are
+    written there.  The caller orders the producers of the inputs before `stream`.  When `stream`
+    is not the current stream, the workspace and the outputs are recorded on it, so torch's
+    caching allocator does not hand their memory to another allocation before the chain is done
+    with it."""
     import torch
     B, Hq, Hkv, Sq, Skv, Dqk, Dv = _dims(q, k, v)
     dq = torch.empty_like(q)
@@ -305,4 +320,7 @@ def attention_backward(q, k, v, o, do, lse, scale=None, causal=False, window_lef
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
     sdpa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale, causal, window_left, deterministic,
                 seq_q_lens, seq_kv_lens, causal_bottom_right, window_right, ws, stream)
+    if stream is not None and stream != torch.cuda.current_stream(q.device):
+        for t in (ws, dq, dk, dv):
+            t.record_stream(stream)
     return dq, dk, dv

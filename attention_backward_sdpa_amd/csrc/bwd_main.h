@@ -325,13 +325,6 @@ struct Gemm4Lanes {
   }
 };
 
-// Linear copy of `nfrag` consecutive 1 KiB fragments starting at byte `off` of `src` into LDS.
-template <int NW>
-__device__ __forceinline__ void copy_frags(rsrc_t src, uint32_t off, int nfrag, char* lds, int w,
-                                           int lane) {
-  for (int f = w; f < nfrag; f += NW) dma16(src, off + f * 1024 + lane * 16, lds + f * 1024);
-}
-
 // Scheduling hint for a block of NMFMA MFMAs fed by NREAD LDS reads: issue AHEAD reads first, then
 // alternate one MFMA with the reads that keep the queue AHEAD deep, so LDS latency hides behind
 // the matrix core instead of stalling each MFMA on an lgkmcnt(0).

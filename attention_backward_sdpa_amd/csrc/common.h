@@ -26,10 +26,6 @@ struct Strides {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ float bf16_to_float(bf16_t x) {
-  return __uint_as_float(((uint32_t)x) << 16);
-}
-
 // Round-to-nearest-even float -> bf16 using the hardware convert (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
@@ -143,22 +139,6 @@ template <int MT>
 __device__ __forceinline__ constexpr int acc_row(int r, int g) {
   return (r / 4) * (4 * (64 / MT)) + g * 4 + (r % 4);
 }
-
-// ---------------------------------------------------------------------------------------------
-// LDS tiles are stored row-major with every row padded by 32 bytes and bit 0 of the 16-byte chunk
-// index flipped on rows whose bit 2 is set.  With 128-byte bank windows this keeps both access
-// patterns conflict-free: 16-byte row reads of 8 consecutive rows at one column land on 8
-// distinct 16-byte slots, and the transpose reads (4 consecutive rows x 32 bytes) on 4 distinct
-// 32-byte slots.  The chunk flip only touches bit 0, which every loop index leaves alone, so the
-// address of any operand is a per-lane base plus a compile-time constant.
-template <int ROWB>
-struct PadTile {
-  static constexpr int STRIDE = ROWB + 32;
-  __device__ __forceinline__ static constexpr int off(int row, int col) {
-    return row * STRIDE + ((((col >> 3) ^ ((row >> 2) & 1))) << 4) + (col & 7) * 2;
-  }
-  static constexpr int bytes(int rows) { return rows * STRIDE; }
-};
 
 // Workgroup barrier that orders LDS only: this wave's LDS accesses complete first (lgkmcnt(0)),
 // while its global loads, stores and atomics keep draining (unlike __syncthreads, whose fence also

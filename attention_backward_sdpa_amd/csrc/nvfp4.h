@@ -40,40 +40,14 @@ __device__ __forceinline__ float nvfp4_value(float x, float scale) {
 
 __device__ __forceinline__ float nvfp4_scale(float amax) { return e4m3_rne(amax / 6.f); }
 
-// max of a and the value of lane DPP(ctrl) of the same 16-lane row (DPP permutes within rows)
-template <int CTRL>
-__device__ __forceinline__ float dpp_max(float a) {
-  const int b = __builtin_amdgcn_update_dpp(0, __float_as_int(a), CTRL, 0xF, 0xF, false);
-  return fmaxf(a, __int_as_float(b));
-}
-
-// The probability operand of GEMM3 (dV += fake(P)^T dO) from the fp32 P of one wave's 32 keys:
-// lane l holds key l % 32 and accumulator rows r (16 of them), so a group of 16 consecutive keys
-// of one row is the same register in one 16-lane DPP row; its amax takes four DPP max steps
-// (swap neighbours, swap pairs, mirror within 8, mirror within 16).  Returns the packed bf16
-// words in the order of the plain P words.
-__device__ __forceinline__ void nvfp4_p_pack(const float (&pf)[16], uint32_t (&pb)[8]) {
-  float pq[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float amax = pf[r];  // P >= 0
-    amax = dpp_max<0xB1>(amax);   // quad_perm [1, 0, 3, 2]
-    amax = dpp_max<0x4E>(amax);   // quad_perm [2, 3, 0, 1]
-    amax = dpp_max<0x141>(amax);  // row_half_mirror
-    amax = dpp_max<0x140>(amax);  // row_mirror
-    const float scale = nvfp4_scale(amax);
-    pq[r] = scale > 0.f ? nvfp4_value(pf[r], scale) : 0.f;
-  }
-#pragma unroll
-  for (int x = 0; x < 8; ++x) pb[x] = pack_bf16x2(pq[2 * x], pq[2 * x + 1]);
-}
-
-// The same through a wave-private LDS area `qs` of 4096 + 256 bytes, so that each group's scale is
-// computed once rather than in all 16 of its lanes: the wave's 32 x 32 fp32 P tile is written row
-// major, lane L reduces row L / 2, key group L % 2 (its four 16-byte chunks read in a rotated
-// order, which keeps every read instruction free of bank conflicts) and stores that group's scale;
-// each lane then reads the scales of its 16 rows.  Only this wave touches `qs`, and a wave's LDS
-// instructions execute in order, so no barrier is needed.
+// The probability operand of GEMM3 (dV += fake(P)^T dO) from the fp32 P of one wave's 32 keys
+// (lane l holds key l % 32 and 16 accumulator rows), computed through a wave-private LDS area `qs`
+// of 4096 + 256 bytes so that each group's scale is computed once rather than in all 16 of its
+// lanes: the wave's 32 x 32 fp32 P tile is written row major, lane L reduces row L / 2, key group
+// L % 2 (its four 16-byte chunks read in a rotated order, which keeps every read instruction free
+// of bank conflicts) and stores that group's scale; each lane then reads the scales of its 16
+// rows.  Only this wave touches `qs`, and a wave's LDS instructions execute in order, so no
+// barrier is needed.  Returns the packed bf16 words in the order of the plain P words.
 __device__ __forceinline__ void nvfp4_p_pack_lds(const float (&pf)[16], uint32_t (&pb)[8],
                                                  char* qs, int lane) {
   const int g = lane >> 5, lc = lane & 31;

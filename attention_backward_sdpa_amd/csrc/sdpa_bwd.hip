@@ -85,15 +85,32 @@ int q_split(int B, int Hq, int Sq, int Skv, const Geometry& g) {
 
 // dQ routes.  The `deterministic` argument: 0 fp32 atomics, 1 deterministic (the fp32 dQ partials
 // where they are a smaller workspace stream per (KV tile, q row) than the BC bf16 dS values, else
-// the dS panels: at equal bytes, head dim 128, the dS-panel chain measured faster on MI355X),
-// 2 dS panels + dq2k, 3 fp32 dQ partials + dq_reduce, 4 the ordered relay (one running fp32 sum
-// per q tile, passed from key tile to key tile in ascending order).
+// the dS panels: at equal bytes, head dim 128, the dS-panel chain measured faster on MI355X; and
+// the ordered relay when that route's buffer, quadratic in the sequence lengths, would exceed
+// kQuadraticCap), 2 dS panels + dq2k, 3 fp32 dQ partials + dq_reduce, 4 the ordered relay (one
+// running fp32 sum per q tile, passed from key tile to key tile in ascending order).
 enum Route { R_ATOMIC = 0, R_DS = 1, R_DQP = 2, R_RELAY = 3, R_INVALID = -1 };
 
-Route route_for(int deterministic, int Dqk, const Geometry& g) {
+// "Determinism": shapes whose dS buffer does not fit fall back to the relay, whose workspace is
+// linear in the sequence lengths.  The bound is a fixed 4 GiB (under 1.5 % of an MI355X's HBM), so
+// the choice depends on the call's arguments only, never on the device or on free memory.
+constexpr int64_t kQuadraticCap = int64_t{1} << 32;
+
+// Bytes of the route's per-(KV tile, q tile) buffer (0 for the atomic and relay routes).
+int64_t quadratic_bytes(Route r, int B, int Hq, int Sq, int Skv, int Dqk, const Geometry& g) {
+  const int64_t sq_pad = align_up(Sq, g.br), skv_pad = align_up(Skv, g.bc);
+  if (r == R_DS) return (int64_t)B * Hq * skv_pad * sq_pad * 2;
+  if (r == R_DQP) return (int64_t)B * Hq * (skv_pad / g.bc) * sq_pad * Dqk * 4;
+  return 0;
+}
+
+Route route_for(int deterministic, int Dqk, const Geometry& g, int B, int Hq, int Sq, int Skv) {
   switch (deterministic) {
     case 0: return R_ATOMIC;
-    case 1: return (int64_t)Dqk * 4 < (int64_t)g.bc * 2 ? R_DQP : R_DS;
+    case 1: {
+      const Route r = (int64_t)Dqk * 4 < (int64_t)g.bc * 2 ? R_DQP : R_DS;
+      return quadratic_bytes(r, B, Hq, Sq, Skv, Dqk, g) > kQuadraticCap ? R_RELAY : r;
+    }
     case 2: return R_DS;
     case 3: return R_DQP;
     case 4: return R_RELAY;
@@ -377,7 +394,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
       L.t[x] = Strides{layouts[x].batch, layouts[x].head, layouts[x].seq};
   st = check_layouts(L, Sq, Skv, Dqk, Dv);
   if (st != SDPA_BWD_OK) return st;
-  const Route route = route_for(deterministic, KDqk, geo);
+  const Route route = route_for(deterministic, KDqk, geo, B, Hq, Sq, Skv);
   if (route == R_INVALID) return SDPA_BWD_INVALID_ARG;
   // dBias of a batch-1 bias sums over the batch with fp32 atomics: not reproducible ("Support
   // surface", bias), so the deterministic routes need a per-batch bias then
@@ -398,7 +415,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   // dsink over the preprocess's delta (no rows when the problem is empty: zeros)
   auto launch_dsink = [&](const float* stats, int sq_pad, bool none) -> hipError_t {
     if (!dsink) return hipSuccess;
-    DsinkParams dp;
+    DsinkParams dp{};
     dp.sink = sink;
     dp.lse = lse;
     dp.stats = stats;
@@ -435,7 +452,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   const int split = q_split(B, Hq, Sq, Skv, geo);
   const bool partials = Hq != Hkv || split > 1;  // dK/dV go through the reduction
 
-  PreParams pp;
+  PreParams pp{};
   pp.o = (const bf16_t*)o;
   pp.dO = (const bf16_t*)dO;
   pp.so = L.t[T_O];
@@ -456,7 +473,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   if (e == hipSuccess) e = launch_dsink(stats, (int)c.sq_pad, false);
   if (e == hipSuccess && ba.dbias) {
     // zero the dBias blocks the main kernel does not write (all of them when it accumulates)
-    DbiasFillParams fp;
+    DbiasFillParams fp{};
     fp.dbias = ba.dbias;
     fp.seq_q_lens = seq_q_lens;
     fp.seq_kv_lens = seq_kv_lens;
@@ -478,7 +495,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   rec(1);
 
-  MainParams mp;
+  MainParams mp{};
   mp.q = (const bf16_t*)q;
   mp.k = (const bf16_t*)k;
   mp.v = (const bf16_t*)v;
@@ -541,7 +558,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   rec(2);
 
   if (partials) {
-    ReduceParams rp;
+    ReduceParams rp{};
     rp.dk_ws = mp.dk_out;
     rp.dv_ws = mp.dv_out;
     rp.dk = (bf16_t*)dk;
@@ -569,7 +586,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   rec(3);
 
   if (route == R_ATOMIC) {
-    ConvertParams cp;
+    ConvertParams cp{};
     cp.acc = dq_accum;
     cp.dq = (bf16_t*)dq;
     cp.sdq = L.t[T_DQ];
@@ -583,7 +600,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     e = launch_convert(cp, KDqk, f16, (int)cgrid, stream);
     if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   } else if (route == R_DQP || route == R_RELAY) {
-    DqReduceParams rp;
+    DqReduceParams rp{};
     rp.dqp_ws = route == R_RELAY ? mp.relay_acc : mp.dqp_ws;
     rp.dq = (bf16_t*)dq;
     rp.sdq = L.t[T_DQ];
@@ -609,7 +626,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     e = launch_dq_reduce(rp, KDqk, f16, (int)rgrid, stream);
     if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   } else {
-    Dq2kParams dp;
+    Dq2kParams dp{};
     dp.ds_ws = mp.ds_ws;
     dp.k = (const bf16_t*)k;
     dp.dq = (bf16_t*)dq;
@@ -657,6 +674,17 @@ hipError_t launch_fake_quant(const void* x, void* y, int64_t elems, hipStream_t 
   return hipGetLastError();
 }
 
+// The route as the header's SDPA_BWD_DQ_* value (-1 for R_INVALID).
+int route_code(Route r) {
+  switch (r) {
+    case R_ATOMIC: return SDPA_BWD_DQ_ATOMIC;
+    case R_DS: return SDPA_BWD_DQ_DS_PANELS;
+    case R_DQP: return SDPA_BWD_DQ_PARTIALS;
+    case R_RELAY: return SDPA_BWD_DQ_RELAY;
+    default: return -1;
+  }
+}
+
 extern "C" {
 
 size_t sdpa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv,
@@ -669,22 +697,18 @@ size_t sdpa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk,
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || Hq % Hkv != 0) return 0;
   if (!kernel_dims(Dqk, Dv, &kq, &kv) || !geometry_for(kq, kv, &geo)) return 0;
   if (B == 0 || Sq == 0 || Skv == 0) return 0;
-  const Route route = route_for(deterministic, kq, geo);
+  const Route route = route_for(deterministic, kq, geo, B, Hq, Sq, Skv);
   if (route == R_INVALID) return 0;
   return (size_t)carve(B, Hq, Hkv, Sq, Skv, kq, kv, route, geo).total;
 }
 
-int sdpa_bwd_dq_route(int Dqk, int Dv, int deterministic) {
+int sdpa_bwd_dq_route(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv,
+                      int deterministic) {
   Geometry geo;
   int kq, kv;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || Hq % Hkv != 0) return -1;
   if (!kernel_dims(Dqk, Dv, &kq, &kv) || !geometry_for(kq, kv, &geo)) return -1;
-  switch (route_for(deterministic, kq, geo)) {
-    case R_ATOMIC: return SDPA_BWD_DQ_ATOMIC;
-    case R_DS: return SDPA_BWD_DQ_DS_PANELS;
-    case R_DQP: return SDPA_BWD_DQ_PARTIALS;
-    case R_RELAY: return SDPA_BWD_DQ_RELAY;
-    default: return -1;
-  }
+  return route_code(route_for(deterministic, kq, geo, B, Hq, Sq, Skv));
 }
 
 size_t sdpa_bwd_nvfp4_qat_workspace_size(int B, int H, int Sq, int Skv, int D, int causal,
@@ -693,7 +717,7 @@ size_t sdpa_bwd_nvfp4_qat_workspace_size(int B, int H, int Sq, int Skv, int D, i
   if (B == 0 || Sq == 0 || Skv == 0) return 0;
   Geometry geo;
   geometry_for(128, 128, &geo, true);
-  const Route route = route_for(deterministic, 128, geo);
+  const Route route = route_for(deterministic, 128, geo, B, H, Sq, Skv);
   if (route == R_INVALID) return 0;
   return (size_t)(qat_hat_bytes(B, H, Sq, Skv) + carve(B, H, H, Sq, Skv, 128, 128, route, geo).total);
 }
@@ -709,7 +733,7 @@ int sdpa_bwd_nvfp4_qat(const void* q, const void* k, const void* v, const void* 
   Geometry geo;
   int st = validate(q, k, v, o_hp, dO, lse, dq, dk, dv, B, H, H, Sq, Skv, D, D, -1, 0, &geo, true);
   if (st != SDPA_BWD_OK) return st;
-  if (route_for(deterministic, 128, geo) == R_INVALID) return SDPA_BWD_INVALID_ARG;
+  if (route_for(deterministic, 128, geo, B, H, Sq, Skv) == R_INVALID) return SDPA_BWD_INVALID_ARG;
   const hipStream_t s = (hipStream_t)stream;
   if (B == 0 || Sq == 0 || Skv == 0)  // nothing to quantise; the chain writes the zeros
     return run(q, k, v, o_hp, dO, lse, dq, dk, dv, B, H, H, Sq, Skv, D, D, scale, causal, -1,
@@ -804,9 +828,20 @@ size_t sdpa_bwd_run_workspace_size(const sdpa_bwd_args* a) {
   if (!kernel_dims(a->Dqk, a->Dv, &kq, &kv) || !geometry_for(kq, kv, &geo, a->bias != nullptr))
     return 0;
   if (a->B == 0 || a->Sq == 0 || a->Skv == 0) return 0;
-  const Route route = route_for(a->deterministic, kq, geo);
+  const Route route = route_for(a->deterministic, kq, geo, a->B, a->Hq, a->Sq, a->Skv);
   if (route == R_INVALID) return 0;
   return (size_t)carve(a->B, a->Hq, a->Hkv, a->Sq, a->Skv, kq, kv, route, geo).total;
+}
+
+int sdpa_bwd_run_dq_route(const sdpa_bwd_args* a) {
+  if (!a) return -1;
+  Geometry geo;
+  if (a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Sq < 0 || a->Skv < 0 || a->Hq % a->Hkv != 0)
+    return -1;
+  int kq, kv;
+  if (!kernel_dims(a->Dqk, a->Dv, &kq, &kv) || !geometry_for(kq, kv, &geo, a->bias != nullptr))
+    return -1;
+  return route_code(route_for(a->deterministic, kq, geo, a->B, a->Hq, a->Sq, a->Skv));
 }
 
 int sdpa_bwd_preprocess(const void* o, const void* dO, const float* lse, float* stats,
@@ -819,13 +854,16 @@ int sdpa_bwd_preprocess(const void* o, const void* dO, const float* lse, float* 
   if (!aligned16(o) || !aligned16(dO) || !aligned16(stats) || (dq_accum && !aligned16(dq_accum)) ||
       ((uintptr_t)lse & 3) != 0)
     return SDPA_BWD_UNSUPPORTED;
-  PreParams pp;
+  PreParams pp{};  // every field set below; the relay counters stay NULL
   pp.o = (const bf16_t*)o;
   pp.dO = (const bf16_t*)dO;
+  pp.so = pp.sdo = Strides{(int64_t)Hq * Sq * Dv, (int64_t)Sq * Dv, (int64_t)Dv};  // contiguous BHSD
   pp.lse = lse;
   pp.stats = stats;
   pp.dq_accum = dq_accum;
   pp.seq_q_lens = seq_q_lens;
+  pp.relay_turn = nullptr;
+  pp.relay_ctl = nullptr;
   pp.sq_pad = (int)align_up(Sq, 32);
   pp.Hq = Hq;
   pp.Sq = Sq;

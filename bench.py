@@ -166,7 +166,7 @@ def write_traffic_record(workload, det_arg, dtype, fetch_dir, write_dir):
     w = synth.WORKLOADS[workload]
     det = int(w.deterministic) if det_arg < 0 else det_arg
     rec = {"kernel_source_hash": kernel_source_hash(), "workload": w.name,
-           "dq_route": lib.dq_route(w.Dqk, w.Dv, det), "dtype": dtype,
+           "dq_route": lib.dq_route(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.Dqk, w.Dv, det), "dtype": dtype,
            "copy_probe_bytes": COPY_PROBE_BYTES}
     total = 0.0
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -285,7 +285,7 @@ def main():
         dqk, dv = (int(x) for x in args.dims.split(","))
         w = synth.small_variant(w, Dqk=dqk, Dv=dv, name=f"{w.name}_dims{dqk}x{dv}")
     det = int(w.deterministic) if args.deterministic < 0 else args.deterministic
-    route = lib.dq_route(w.Dqk, w.Dv, det)
+    route = lib.dq_route(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.Dqk, w.Dv, det)
     if route < 0:
         raise SystemExit(f"--deterministic {det}: not a dQ route")
     inp = synth.draw_inputs(w, dtype=args.dtype)

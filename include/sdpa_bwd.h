@@ -55,9 +55,12 @@
  *      the sequence lengths.  The key tiles of one query head run on one XCD (of the device's
  *      hipDeviceAttributeNumberOfXccs), taking their work from per-XCD queues; if a wait for a
  *      turn is ever abandoned (it is bounded), or not every work item ran, dq is written as NaN;
- *   1  deterministic, the library's choice between 2 and 3: 3 where its workspace holds fewer
- *      bytes per (KV tile, q row) (Kqk fp32 partials against the key tile's bf16 dS values),
- *      else 2 (kernel head dims 32 and 64 take 3; 128, 192 and 256 take 2).
+ *   1  deterministic, the library's choice: 3 where its workspace holds fewer bytes per
+ *      (KV tile, q row) (Kqk fp32 partials against the key tile's bf16 dS values), else 2
+ *      (kernel head dims 32 and 64 take 3; 128, 192 and 256 take 2); and 4 when that route's
+ *      buffer, quadratic in the sequence lengths, would exceed 4 GiB ("Determinism": shapes whose
+ *      dS buffer does not fit fall back to the relay).  The bound is fixed, so the choice depends
+ *      on the call's arguments only; sdpa_bwd_dq_route reports it.
  * Routes 1-4 make dq, dk, dv bitwise reproducible run to run; dK and dV are reproducible on every
  * route.  Any other value gives SDPA_BWD_INVALID_ARG.
  */
@@ -101,11 +104,14 @@ enum {
 size_t sdpa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv,
                                int causal, int window_left, int deterministic, int has_seqlens);
 
-/* The dQ route a call with these head dims and this `deterministic` value takes:
- * SDPA_BWD_DQ_ATOMIC, SDPA_BWD_DQ_DS_PANELS, SDPA_BWD_DQ_PARTIALS or SDPA_BWD_DQ_RELAY (never
- * SDPA_BWD_DQ_DETERMINISTIC, which resolves to SDPA_BWD_DQ_DS_PANELS or SDPA_BWD_DQ_PARTIALS); -1 for head dims outside the
- * supported set or an unknown value.  Host only, no GPU work. */
-int sdpa_bwd_dq_route(int Dqk, int Dv, int deterministic);
+/* The dQ route a call of sdpa_bwd, sdpa_bwd_ex or sdpa_bwd_flex with these sizes and this
+ * `deterministic` value takes: SDPA_BWD_DQ_ATOMIC, SDPA_BWD_DQ_DS_PANELS, SDPA_BWD_DQ_PARTIALS or
+ * SDPA_BWD_DQ_RELAY (never SDPA_BWD_DQ_DETERMINISTIC, which resolves to one of the last three
+ * by head dim and by the size of its quadratic buffer, see above); -1 for sizes or head dims
+ * sdpa_bwd rejects or an unknown value.  Host only, no GPU work.  sdpa_bwd_workspace_size sizes
+ * the same route's buffers. */
+int sdpa_bwd_dq_route(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv,
+                      int deterministic);
 
 /* The backward pass with top-left causal masking, no padding and no right band.
  * scale <= 0 selects 1/sqrt(Dqk) ("API Usage": None -> 1/sqrt(D)).  window_left = -1 disables the
@@ -239,6 +245,11 @@ int sdpa_bwd_run(const sdpa_bwd_args* args);
 /* Bytes of workspace sdpa_bwd_run needs for these arguments (the workspace, workspace_bytes,
  * stream and events fields are not read); 0 for arguments it rejects and for empty problems. */
 size_t sdpa_bwd_run_workspace_size(const sdpa_bwd_args* args);
+
+/* The dQ route sdpa_bwd_run takes for these arguments (values as for sdpa_bwd_dq_route; with a
+ * bias the 128-key tiles can change the choice of `deterministic` = 1); -1 for arguments it
+ * rejects by size or head dim, an unknown `deterministic` value, or args NULL.  Host only. */
+int sdpa_bwd_run_dq_route(const sdpa_bwd_args* args);
 
 /* NVFP4 attention-QAT backward ("NVFP4 Attention QAT Backward", "Overview", "Tensor contract",
  * "Current support and limitations").  Q, K and V are fake-quantised to NVFP4 (every 16

@@ -97,6 +97,11 @@ def run_gpu(case, torch, deterministic=None, stream=None, poison=True, ws_fill=N
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
     if ws_fill is not None:
         ws.copy_(ws_fill(ws.numel()))
+    if stream is not None:
+        # the inputs, the NaN poison and the workspace fill were enqueued on the current stream
+        stream.wait_stream(torch.cuda.current_stream())
+        for x in (ws, dq, dk, dv):
+            x.record_stream(stream)
     lib.sdpa_bwd_ex(t["q"], t["k"], t["v"], t["o"], t["do"], t["lse"], dq, dk, dv,
                     scale=w.softmax_scale, causal=w.causal, window_left=w.window_left,
                     deterministic=det, seq_q_lens=t["lens"], seq_kv_lens=t["lens"],

@@ -46,25 +46,74 @@ def test_status_strings(so):
     assert lib.status_string(99) == "unknown status"
 
 
+def _route(Dqk, Dv, det, B=1, Hq=4, Hkv=4, Sq=256, Skv=256):
+    return lib.dq_route(B, Hq, Hkv, Sq, Skv, Dqk, Dv, det)
+
+
 def test_dq_route_choice(so):
-    assert lib.dq_route(64, 64, 1) == lib.DQ_PARTIALS
+    assert _route(64, 64, 1) == lib.DQ_PARTIALS
     for d in ((128, 128), (192, 128), (256, 256)):
-        assert lib.dq_route(*d, 1) == lib.DQ_DS_PANELS
+        assert _route(*d, 1) == lib.DQ_DS_PANELS
     for d in ((64, 64), (128, 128), (192, 128), (256, 256)):
-        assert lib.dq_route(*d, 0) == lib.DQ_ATOMIC
-        assert lib.dq_route(*d, 2) == lib.DQ_DS_PANELS
-        assert lib.dq_route(*d, 3) == lib.DQ_PARTIALS
-        assert lib.dq_route(*d, 4) == lib.DQ_RELAY
-        assert lib.dq_route(*d, 5) == -1
+        assert _route(*d, 0) == lib.DQ_ATOMIC
+        assert _route(*d, 2) == lib.DQ_DS_PANELS
+        assert _route(*d, 3) == lib.DQ_PARTIALS
+        assert _route(*d, 4) == lib.DQ_RELAY
+        assert _route(*d, 5) == -1
     # head dims that are multiples of 8 up to 256 run on the next supported size
-    assert lib.dq_route(96, 96, 1) == lib.dq_route(128, 128, 1)
-    assert lib.dq_route(40, 40, 1) == lib.dq_route(64, 64, 1)
+    assert _route(96, 96, 1) == _route(128, 128, 1)
+    assert _route(40, 40, 1) == _route(64, 64, 1)
     # head dim 32 has its own kernel (256-key tiles): the dQ-partial route is the deterministic
     # choice (32 fp32 per q row < 256 bf16 dS values)
-    assert lib.dq_route(32, 32, 1) == lib.DQ_PARTIALS
-    assert lib.dq_route(24, 24, 1) == lib.dq_route(16, 8, 1) == lib.DQ_PARTIALS
+    assert _route(32, 32, 1) == lib.DQ_PARTIALS
+    assert _route(24, 24, 1) == _route(16, 8, 1) == lib.DQ_PARTIALS
     for bad in ((100, 100), (264, 264), (128, 192), (4, 4)):
-        assert lib.dq_route(*bad, 0) == -1
+        assert _route(*bad, 0) == -1
+    # sizes sdpa_bwd rejects
+    assert _route(128, 128, 0, Hkv=3) == -1 and _route(128, 128, 0, Sq=-1) == -1
+
+
+GIB4 = 1 << 32
+
+
+def _route_of(d, det=1):
+    return lib.dq_route(d["B"], d["Hq"], d["Hkv"], d["Sq"], d["Skv"], d["Dqk"], d["Dv"], det)
+
+
+def test_deterministic_choice_falls_back_to_the_relay(so):
+    # "Determinism": a deterministic call whose quadratic buffer would exceed 4 GiB takes the
+    # relay, and its workspace becomes linear in the sequence lengths; route and workspace size
+    # switch together
+    def det_ws(**kw):
+        return _ws(deterministic=True, **kw)
+
+    # dS panels at head dim 128: B*Hq*Skv_pad*Sq_pad*2 bytes; 32 heads at S = 8192 is exactly 4 GiB
+    at = dict(B=1, Hq=32, Hkv=32, Sq=8192, Skv=8192, Dqk=128, Dv=128)
+    assert _route_of(at) == lib.DQ_DS_PANELS
+    assert det_ws(**at) == _al(32 * 8192 * 8) + GIB4
+    over = dict(at, Hq=33, Hkv=33)
+    assert _route_of(over) == lib.DQ_RELAY
+    relay = det_ws(**over)
+    assert relay == _ws(deterministic=lib.DQ_RELAY, **over) < GIB4 // 8
+    # linear from there on: twice the length, twice the relay workspace (up to alignment)
+    long = dict(over, Sq=16384, Skv=16384)
+    assert _route_of(long) == lib.DQ_RELAY
+    assert abs(det_ws(**long) - 2 * relay) <= 4 * 256
+    # the explicit routes keep their buffers whatever the size
+    assert _ws(deterministic=lib.DQ_DS_PANELS, **over) == _al(33 * 8192 * 8) + 33 * GIB4 // 32
+    # head dim 64 takes the dQ partials, B*Hq*(Skv_pad/256)*Sq_pad*64*4 bytes, until they exceed
+    # 4 GiB: 64 heads at S = 8192 are exactly 4 GiB
+    d64 = dict(B=2, Hq=32, Hkv=8, Sq=8192, Skv=8192, Dqk=64, Dv=64)
+    assert _route_of(d64) == lib.DQ_PARTIALS
+    d64o = dict(d64, Sq=8224)
+    assert _route_of(d64o) == lib.DQ_RELAY
+    assert det_ws(**d64o) == _ws(deterministic=lib.DQ_RELAY, **d64o)
+    # sdpa_bwd_run_dq_route agrees without a bias
+    torch = pytest.importorskip("torch")
+    q = torch.empty(1, 33, 8192, 128, dtype=torch.bfloat16, device="meta")
+    k = torch.empty(1, 33, 8192, 128, dtype=torch.bfloat16, device="meta")
+    assert lib.run_dq_route(q, k, k, deterministic=1) == lib.DQ_RELAY
+    assert lib.run_dq_route(q[:, :32], k[:, :32], k[:, :32], deterministic=1) == lib.DQ_DS_PANELS
 
 
 def _ws(**kw):
