@@ -12,7 +12,9 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsdpa_bwd.so")
 
-OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, LAUNCH_FAILED = 0, 1, 2, 3, 4
+OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, LAUNCH_FAILED, SCRATCH_TOO_SMALL = 0, 1, 2, 3, 4, 5
+# the static device scratch of sdpa_bwd_noalloc (SDPA_BWD_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 256 << 20
 BF16, FP16, FP32 = 0, 1, 2
 # values of the `deterministic` argument (dQ routes); False / True are 0 / 1
 DQ_ATOMIC, DQ_DETERMINISTIC, DQ_DS_PANELS, DQ_PARTIALS, DQ_RELAY = 0, 1, 2, 3, 4
@@ -64,6 +66,8 @@ def _load():
     ex = [vp] * 9 + [i] * 7 + [f, i, i, i, vp, vp, i, i, vp, sz, vp]
     lib.sdpa_bwd_ex.argtypes = ex
     lib.sdpa_bwd_ex.restype = i
+    lib.sdpa_bwd_noalloc.argtypes = [vp] * 9 + [i] * 7 + [f, i, i, i, vp, vp, i, i, vp]
+    lib.sdpa_bwd_noalloc.restype = i
     lib.sdpa_bwd_ex_events.argtypes = ex + [vp]
     lib.sdpa_bwd_ex_events.restype = i
     lib.sdpa_bwd_flex.argtypes = ([vp] * 9 + [i] * 7 + [f, i, i, i, vp, vp, i, i, vp, i, vp, sz, vp,
@@ -200,6 +204,20 @@ def sdpa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, windo
             _check(lib.sdpa_bwd_ex_events(*head, *tail, handles))
     else:
         _check(lib.sdpa_bwd_flex(*head, _layouts(tensors), _io_dtype(q), *tail, handles))
+
+
+def sdpa_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, window_left=-1,
+                     deterministic=False, seq_q_lens=None, seq_kv_lens=None,
+                     causal_bottom_right=False, window_right=0, stream=None):
+    """sdpa_bwd_noalloc(): sdpa_bwd_ex on contiguous bf16 tensors with the library's static device
+    scratch as the workspace (no allocation; SdpaBwdError with SCRATCH_TOO_SMALL when the problem
+    needs more than NOALLOC_SCRATCH_BYTES)."""
+    dims = _dims(q, k, v)
+    _check(_load().sdpa_bwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+        *dims, -1.0 if scale is None else float(scale), int(causal), int(window_left),
+        int(deterministic), _ptr(seq_q_lens), _ptr(seq_kv_lens), int(causal_bottom_right),
+        int(window_right), _stream_handle(stream)))
 
 
 def _bias_dtype(bias, q):

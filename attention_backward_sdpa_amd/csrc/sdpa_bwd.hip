@@ -11,6 +11,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/sdpa_bwd.h"
 #include "dq2k.h"
 #include "dq_reduce.h"
@@ -674,6 +676,32 @@ hipError_t launch_fake_quant(const void* x, void* y, int64_t elems, hipStream_t 
   return hipGetLastError();
 }
 
+// ---- allocation-free entry point ---------------------------------------------------------------
+// sdpa_bwd_noalloc carves its workspace from this file-scope device array instead of a caller's
+// buffer.  Each device the library runs on holds its own copy, at its own address, until the
+// process ends.  In host code `scratch` is only the runtime's handle of the symbol: its device
+// address is looked up once per device (scratch_on_current_device) and only that address is
+// passed to the kernels.
+static __device__ __align__(256) char scratch[SDPA_BWD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// The device address of `scratch` on the current device, looked up on the first call made with
+// that device current and kept; NULL when the lookup fails.
+void* scratch_on_current_device() {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
 // The route as the header's SDPA_BWD_DQ_* value (-1 for R_INVALID).
 int route_code(Route r) {
   switch (r) {
@@ -792,6 +820,27 @@ int sdpa_bwd_ex_events(const void* q, const void* k, const void* v, const void* 
              workspace_bytes, true, (hipStream_t)stream, events);
 }
 
+int sdpa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv,
+                     int Sq, int Skv, int Dqk, int Dv, float scale, int causal, int window_left,
+                     int deterministic, const int* seq_q_lens, const int* seq_kv_lens,
+                     int causal_bottom_right, int window_right, void* stream) {
+  // host-side size check first: a problem larger than the scratch is declined before any GPU call
+  const size_t need = sdpa_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, Dqk, Dv, causal, window_left,
+                                              deterministic, seq_q_lens != nullptr);
+  if (need > (size_t)SDPA_BWD_NOALLOC_SCRATCH_BYTES) return SDPA_BWD_SCRATCH_TOO_SMALL;
+  // need == 0: arguments run() rejects, or an empty problem, which uses no workspace
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_on_current_device();
+    if (ws == nullptr) return SDPA_BWD_LAUNCH_FAILED;
+  }
+  return run(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, scale, causal,
+             window_left, deterministic, seq_q_lens, seq_kv_lens, causal_bottom_right,
+             window_right, nullptr, SDPA_BWD_BF16, nullptr, nullptr, BiasArgs{}, ws,
+             ws ? (size_t)SDPA_BWD_NOALLOC_SCRATCH_BYTES : 0, true, (hipStream_t)stream, nullptr);
+}
+
 int sdpa_bwd_flex(const void* q, const void* k, const void* v, const void* o, const void* dO,
                   const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
                   int Skv, int Dqk, int Dv, float scale, int causal, int window_left,
@@ -883,6 +932,8 @@ const char* sdpa_bwd_status_string(int status) {
     case SDPA_BWD_UNSUPPORTED: return "unsupported configuration";
     case SDPA_BWD_WORKSPACE_TOO_SMALL: return "workspace too small";
     case SDPA_BWD_LAUNCH_FAILED: return "kernel launch failed";
+    case SDPA_BWD_SCRATCH_TOO_SMALL:
+      return "problem needs more workspace than the static scratch of sdpa_bwd_noalloc";
     default: return "unknown status";
   }
 }

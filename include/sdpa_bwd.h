@@ -88,7 +88,9 @@ enum {
   SDPA_BWD_INVALID_ARG = 1,          /* null pointer, negative size, H_kv not dividing H_q, ... */
   SDPA_BWD_UNSUPPORTED = 2,          /* head dims outside the supported set, misaligned pointer */
   SDPA_BWD_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below sdpa_bwd_workspace_size()        */
-  SDPA_BWD_LAUNCH_FAILED = 4         /* the HIP runtime reported an error at launch             */
+  SDPA_BWD_LAUNCH_FAILED = 4,        /* the HIP runtime reported an error at launch             */
+  SDPA_BWD_SCRATCH_TOO_SMALL = 5     /* sdpa_bwd_noalloc: the problem's workspace exceeds
+                                        SDPA_BWD_NOALLOC_SCRATCH_BYTES                           */
 };
 
 /* Bytes of workspace needed by a call with these arguments: a 256-byte-aligned carve of the
@@ -145,6 +147,28 @@ int sdpa_bwd_ex_events(const void* q, const void* k, const void* v, const void* 
                        const int* seq_q_lens, const int* seq_kv_lens, int causal_bottom_right,
                        int window_right, void* workspace, size_t workspace_bytes, void* stream,
                        void* const* events);
+
+/* Size of the static device scratch of sdpa_bwd_noalloc, per device (256 MiB). */
+#define SDPA_BWD_NOALLOC_SCRATCH_BYTES (256u * 1024u * 1024u)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): sdpa_bwd_ex without a workspace argument.  The
+ * workspace is carved from a static device array of SDPA_BWD_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every device it runs on until the process ends; the call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine).  The caller still owns every tensor.
+ * Arguments, layout, masks, routes, stream and status rules are those of sdpa_bwd_ex, and the
+ * arithmetic is the same.  A problem whose workspace (sdpa_bwd_workspace_size) exceeds the scratch
+ * gives SDPA_BWD_SCRATCH_TOO_SMALL before any GPU call.  `stream` must belong to the current
+ * device; the scratch's device address is looked up on the first call made with a device current.
+ * Every call on one device shares that device's scratch and finds the previous call's contents
+ * (the chain clears what it accumulates into on its own stream), so calls that overlap on one
+ * device race: order them (one stream, or events).  No stage events. */
+int sdpa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv,
+                     int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv,
+                     float scale, int causal, int window_left, int deterministic,
+                     const int* seq_q_lens, const int* seq_kv_lens, int causal_bottom_right,
+                     int window_right, void* stream);
 
 /* element types: the io type of sdpa_bwd_flex (BF16, FP16); a bias may also be FP32 */
 enum { SDPA_BWD_BF16 = 0, SDPA_BWD_FP16 = 1, SDPA_BWD_FP32 = 2 };
