@@ -38,7 +38,7 @@ class Args(ctypes.Structure):
          ("dsink", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("bias_dtype", ctypes.c_int),
          ("bias_batch", ctypes.c_int), ("dbias", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
          ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
-         ("events", ctypes.c_void_p)]
+         ("events", ctypes.c_void_p), ("dbias_io", ctypes.c_int)]
 
 
 _lib = None
@@ -258,6 +258,10 @@ def run_args(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, window_l
     a.bias_dtype = _bias_dtype(bias, q)
     a.bias_batch = 1 if bias is None else int(bias.shape[0])
     a.dbias = None if dbias is None else dbias.data_ptr()
+    # an io-type dBias (bf16 / fp16 tensor) is accumulated in fp32 and cast by dbias_cvt
+    a.dbias_io = 0 if dbias is None or _bias_dtype(dbias, q) == FP32 else 1
+    if a.dbias_io and dbias.dtype != q.dtype:
+        raise ValueError("dbias must be float32 or of q's dtype")
     # keep the pointed-to ctypes arrays alive with the struct
     a._keep = (lay, handles)
     return a
@@ -283,7 +287,8 @@ def sdpa_bwd_run(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, wind
     """sdpa_bwd_run(): the superset entry point (any dense layout with a contiguous head dim,
     bf16 or fp16; the sink gradient: dsink (Hq,) fp32 is written when given, from the sink
     (Hq,) fp32 logits; an additive bias (1 or B, Hq, Sq, Skv) of the io type or fp32, with its
-    fp32 gradient dbias when given).  `workspace` must hold run_workspace_size(...) bytes."""
+    gradient dbias when given: fp32, or of the io type (then accumulated in fp32 in the workspace
+    and cast once)).  `workspace` must hold run_workspace_size(...) bytes."""
     a = run_args(q, k, v, o, do, lse, dq, dk, dv, scale, causal, window_left, deterministic,
                  seq_q_lens, seq_kv_lens, causal_bottom_right, window_right, sink, dsink, bias,
                  dbias, workspace, stream, events)

@@ -68,6 +68,7 @@ struct BiasArgs {
   float* dbias = nullptr;
   int dtype = SDPA_BWD_BF16;  // SDPA_BWD_BF16 / SDPA_BWD_FP16 (the io type) or SDPA_BWD_FP32
   int batch = 1;              // 1 or B
+  bool dbias_io = false;      // dbias holds io-type elements: accumulate in fp32, then dbias_cvt
 };
 
 // Number of parts the q-tile range of every key tile is split into (each part a workgroup of its
@@ -138,12 +139,14 @@ int relay_queues() {
 
 struct Carve {
   int64_t stats = 0, dq_accum = -1, ds = -1, dqp = -1, dk_ws = -1, dv_ws = -1, total = 0;
+  int64_t dbias_f32 = -1;
   int64_t relay_turn = -1, relay_ctl = -1;
   int64_t sq_pad = 0, skv_pad = 0;
 };
 
+// dbias_elems: elements of an fp32 dBias accumulator (an io-type dBias output), else 0.
 Carve carve(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv, Route route,
-            const Geometry& g) {
+            const Geometry& g, int64_t dbias_elems = 0) {
   Carve c;
   int64_t off = 0;
   c.sq_pad = align_up(Sq, g.br);
@@ -173,6 +176,10 @@ Carve carve(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv, Route rout
     off = align_up(off + (int64_t)B * Hq * split * Skv * Dqk * 2, kAlign);
     c.dv_ws = off;
     off = align_up(off + (int64_t)B * Hq * split * Skv * Dv * 2, kAlign);
+  }
+  if (dbias_elems > 0) {
+    c.dbias_f32 = off;
+    off = align_up(off + dbias_elems * 4, kAlign);
   }
   c.total = off;
   return c;
@@ -359,6 +366,22 @@ hipError_t zero_rows(void* p, const Strides& st, int B, int H, int S, int D, hip
   return hipGetLastError();
 }
 
+// dbias_cvt over n elements (src null: zeros); the vector form when n is a multiple of 8 and dst
+// is 16-byte aligned.
+hipError_t launch_dbias_cvt(const float* src, void* dst, int64_t n, bool f16, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int vec = (n % 8 == 0 && ((uintptr_t)dst & 15) == 0) ? 1 : 0;
+  int64_t grid = ((vec ? n / 8 : n) + 255) / 256;
+  grid = grid > 16384 ? 16384 : grid;
+  if (f16)
+    hipLaunchKernelGGL(dbias_cvt_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, src,
+                       (bf16_t*)dst, n, vec);
+  else
+    hipLaunchKernelGGL(dbias_cvt_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, src,
+                       (bf16_t*)dst, n, vec);
+  return hipGetLastError();
+}
+
 int grid_stride_blocks(int64_t n) {
   int64_t b = (n + 255) / 256;
   if (b > 16384) b = 16384;
@@ -385,7 +408,8 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   if (has_bias) {
     if (ba.batch != 1 && ba.batch != B) return SDPA_BWD_INVALID_ARG;
     if (ba.dtype != dtype && ba.dtype != SDPA_BWD_FP32) return SDPA_BWD_UNSUPPORTED;
-    if (((uintptr_t)ba.bias & (ba.dtype == SDPA_BWD_FP32 ? 3 : 1)) || ((uintptr_t)ba.dbias & 3))
+    if (((uintptr_t)ba.bias & (ba.dtype == SDPA_BWD_FP32 ? 3 : 1)) ||
+        ((uintptr_t)ba.dbias & (ba.dbias_io ? 1 : 3)))
       return SDPA_BWD_UNSUPPORTED;
   }
   if (dsink && (!sink || ((uintptr_t)sink & 3) || ((uintptr_t)dsink & 3))) return SDPA_BWD_INVALID_ARG;
@@ -404,7 +428,10 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   if (dbias_atomic && route != R_ATOMIC) return SDPA_BWD_UNSUPPORTED;
   // empty problems need no workspace (sdpa_bwd_workspace_size returns 0 for them)
   const bool empty = B == 0 || Sq == 0 || Skv == 0;
-  const Carve c = empty ? Carve{} : carve(B, Hq, Hkv, Sq, Skv, KDqk, KDv, route, geo);
+  const int64_t dbias_elems = (int64_t)ba.batch * Hq * Sq * Skv;
+  const Carve c = empty ? Carve{}
+                        : carve(B, Hq, Hkv, Sq, Skv, KDqk, KDv, route, geo,
+                                ba.dbias && ba.dbias_io ? dbias_elems : 0);
   if (c.total > 0 && workspace == nullptr) return SDPA_BWD_INVALID_ARG;
   if (check_ws && (uint64_t)c.total > (uint64_t)workspace_bytes) return SDPA_BWD_WORKSPACE_TOO_SMALL;
   if (c.total > 0 && ((uintptr_t)workspace % kAlign) != 0) return SDPA_BWD_UNSUPPORTED;
@@ -437,7 +464,10 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
     if (e == hipSuccess) e = zero_rows(dk, L.t[T_DK], B, Hkv, Skv, Dqk, stream);
     if (e == hipSuccess) e = zero_rows(dv, L.t[T_DV], B, Hkv, Skv, Dv, stream);
     if (e == hipSuccess) e = launch_dsink(nullptr, 0, true);
-    if (e == hipSuccess && ba.dbias && (int64_t)ba.batch * Sq * Skv > 0) {
+    if (e == hipSuccess && ba.dbias && ba.dbias_io && dbias_elems > 0) {
+      // nothing attends: dBias is zero
+      e = launch_dbias_cvt(nullptr, ba.dbias, dbias_elems, f16, stream);
+    } else if (e == hipSuccess && ba.dbias && (int64_t)ba.batch * Sq * Skv > 0) {
       // nothing attends: dBias is zero
       DbiasFillParams fp{ba.dbias, nullptr, nullptr, Hq, Sq, Skv, geo.bc, geo.br, 0, -1, 0, 0, 1};
       hipLaunchKernelGGL(dbias_fill_kernel, dim3((unsigned)((int64_t)ba.batch * Hq * ((Sq + 31) / 32))),
@@ -473,10 +503,13 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   pp.relay_ctl = route == R_RELAY ? (int*)(ws + c.relay_ctl) : nullptr;
   e = launch_preprocess(pp, KDv, f16, (int64_t)B * Hq * (c.sq_pad / geo.br), stream);
   if (e == hipSuccess) e = launch_dsink(stats, (int)c.sq_pad, false);
+  // the fp32 dBias the main kernel writes: the caller's output, or the workspace accumulator of
+  // an io-type output (converted once after the main kernel)
+  float* dbias32 = ba.dbias && ba.dbias_io ? (float*)(ws + c.dbias_f32) : (float*)ba.dbias;
   if (e == hipSuccess && ba.dbias) {
     // zero the dBias blocks the main kernel does not write (all of them when it accumulates)
     DbiasFillParams fp{};
-    fp.dbias = ba.dbias;
+    fp.dbias = dbias32;
     fp.seq_q_lens = seq_q_lens;
     fp.seq_kv_lens = seq_kv_lens;
     fp.Hq = Hq;
@@ -540,7 +573,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   mp.scale = scale;
   mp.scale_log2 = scale * kLog2e;
   mp.bias = ba.bias;
-  mp.dbias = ba.dbias;
+  mp.dbias = dbias32;
   mp.bias_bstride = ba.batch == 1 ? 0 : (int64_t)Hq * Sq * Skv;
   mp.bias_f32 = ba.dtype == SDPA_BWD_FP32 ? 1 : 0;
   mp.dbias_atomic = dbias_atomic ? 1 : 0;
@@ -557,6 +590,10 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   e = run_main(KDqk, mp, route, f16, has_bias ? (ba.dbias ? 2 : 1) : 0, (int)main_grid, geo.bc,
                stream, qat);
   if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
+  if (ba.dbias && ba.dbias_io) {
+    e = launch_dbias_cvt(dbias32, ba.dbias, dbias_elems, f16, stream);
+    if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
+  }
   rec(2);
 
   if (partials) {
@@ -861,6 +898,7 @@ int sdpa_bwd_run(const sdpa_bwd_args* a) {
   ba.dbias = a->dbias;
   ba.dtype = a->bias_dtype;
   ba.batch = a->bias_batch;
+  ba.dbias_io = a->dbias_io != 0;
   return run(a->q, a->k, a->v, a->o, a->dO, a->lse, a->dq, a->dk, a->dv, a->B, a->Hq, a->Hkv,
              a->Sq, a->Skv, a->Dqk, a->Dv, a->scale, a->causal, a->window_left, a->deterministic,
              a->seq_q_lens, a->seq_kv_lens, a->causal_bottom_right, a->window_right, a->layouts,
@@ -879,7 +917,9 @@ size_t sdpa_bwd_run_workspace_size(const sdpa_bwd_args* a) {
   if (a->B == 0 || a->Sq == 0 || a->Skv == 0) return 0;
   const Route route = route_for(a->deterministic, kq, geo, a->B, a->Hq, a->Sq, a->Skv);
   if (route == R_INVALID) return 0;
-  return (size_t)carve(a->B, a->Hq, a->Hkv, a->Sq, a->Skv, kq, kv, route, geo).total;
+  const int64_t dbias_elems =
+      a->dbias && a->bias && a->dbias_io ? (int64_t)a->bias_batch * a->Hq * a->Sq * a->Skv : 0;
+  return (size_t)carve(a->B, a->Hq, a->Hkv, a->Sq, a->Skv, kq, kv, route, geo, dbias_elems).total;
 }
 
 int sdpa_bwd_run_dq_route(const sdpa_bwd_args* a) {

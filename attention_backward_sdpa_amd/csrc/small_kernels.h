@@ -253,6 +253,33 @@ __global__ void __launch_bounds__(256) dbias_fill_kernel(DbiasFillParams p) {
   }
 }
 
+// ---- dbias_cvt ---------------------------------------------------------------------------------
+// "The kernel chain" (dbias_cvt) and "Support surface" (bias): an io-type dBias output is the
+// fp32 dBias (accumulated in the workspace by the main kernel and the fill above) rounded once
+// to the io type.  Flat over the (Bb, Hq, Sq, Skv) elements; `vec`: 8 elements per thread and step
+// (two 16-byte loads, one 16-byte store; n a multiple of 8 and dst 16-byte aligned), else one.
+// With src = null every element is written as 0 (problems where nothing attends).
+template <bool F16>
+__global__ void __launch_bounds__(256) dbias_cvt_kernel(const float* src, bf16_t* dst, int64_t n,
+                                                        int vec) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  if (vec) {
+    for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n / 8; x += stride) {
+      u32x4 out = u32x4{0u, 0u, 0u, 0u};
+      if (src) {
+        const floatx4 a = reinterpret_cast<const floatx4*>(src)[2 * x];
+        const floatx4 b = reinterpret_cast<const floatx4*>(src)[2 * x + 1];
+        out = u32x4{Elem<F16>::pack2(a[0], a[1]), Elem<F16>::pack2(a[2], a[3]),
+                    Elem<F16>::pack2(b[0], b[1]), Elem<F16>::pack2(b[2], b[3])};
+      }
+      reinterpret_cast<u32x4*>(dst)[x] = out;
+    }
+  } else {
+    for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += stride)
+      dst[x] = Elem<F16>::one(src ? src[x] : 0.f);
+  }
+}
+
 // ---- strided zero fill (gradients of shapes where nothing attends) ------------------------------
 // out[b, h, s, :] = 0 for a (B, H, S, D) bf16 tensor with element strides st; one thread per
 // 16-byte vector, grid.y over (b, h).

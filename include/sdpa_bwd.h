@@ -229,6 +229,12 @@ int sdpa_bwd_flex(const void* q, const void* k, const void* v, const void* o, co
  *               B > 1 it sums over the batch entries through fp32 atomics, so it is not bitwise
  *               reproducible, and the deterministic dQ routes then give SDPA_BWD_UNSUPPORTED
  *               (use a per-batch bias).  Otherwise each element is written once (reproducible).
+ *   dbias_io    0: dbias holds fp32 elements (above).  1: dbias holds elements of the io type
+ *               (dtype), 2-byte aligned ("The kernel chain" dbias_cvt, "Support surface" bias: an
+ *               io-dtype output adds a cast): dBias is accumulated in fp32 in the workspace
+ *               (bias_batch*Hq*Sq*Skv floats, 256-byte aligned, after the other pieces) and rounded
+ *               once to the io type by the dbias_cvt kernel right after the main kernel (inside the
+ *               main kernel's event interval).  Read only when dbias is not NULL.
  * With a bias every head dim runs 128-key tiles, so the workspace can differ from the one
  * sdpa_bwd_workspace_size reports: size it with sdpa_bwd_run_workspace_size. */
 typedef struct sdpa_bwd_args {
@@ -259,6 +265,7 @@ typedef struct sdpa_bwd_args {
   size_t workspace_bytes;
   void* stream;
   void* const* events;
+  int dbias_io;
 } sdpa_bwd_args;
 
 /* The superset entry point: everything sdpa_bwd_flex does, plus the sink gradient.  Same

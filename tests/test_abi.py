@@ -306,6 +306,43 @@ def test_run_rejections_before_launch(so):
     assert so.sdpa_bwd_run(ctypes.byref(a)) == lib.INVALID_ARG
 
 
+def test_io_dtype_dbias_workspace_and_rejections(so):
+    # "The kernel chain" dbias_cvt: an io-type dBias output adds an fp32 accumulator of
+    # bias_batch * Hq * Sq * Skv floats (256-byte aligned) at the end of the carve (host tensors
+    # stand in for device ones: the size query reads only their shapes and whether they exist)
+    torch = pytest.importorskip("torch")
+    for Bb in (1, 2):
+        q = torch.empty(2, 4, 200, 128, dtype=torch.bfloat16, device="cpu")
+        k = torch.empty(2, 2, 300, 128, dtype=torch.bfloat16, device="cpu")
+        bias = torch.empty(Bb, 4, 200, 300, dtype=torch.bfloat16, device="cpu")
+        for det in (0, 2, 3):
+            base = lib.run_workspace_size(q, k, k, causal=True, deterministic=det, bias=bias)
+            f32 = lib.run_workspace_size(q, k, k, causal=True, deterministic=det, bias=bias,
+                                         dbias=torch.empty(Bb, 4, 200, 300, device="cpu"))
+            io = lib.run_workspace_size(q, k, k, causal=True, deterministic=det, bias=bias,
+                                        dbias=torch.empty(Bb, 4, 200, 300, dtype=torch.bfloat16))
+            assert f32 == base and io == base + _al(Bb * 4 * 200 * 300 * 4)
+        # an io-type dBias of another type than the inputs is refused by the binding
+        with pytest.raises(ValueError):
+            lib.run_workspace_size(q, k, k, bias=bias, dbias=torch.empty(
+                Bb, 4, 200, 300, dtype=torch.float16, device="cpu"))
+    # alignment: 2 bytes for an io-type dBias, 4 for fp32
+    p = 4096
+    a = lib.Args()
+    for n in ("q", "k", "v", "o", "dO", "lse", "dq", "dk", "dv"):
+        setattr(a, n, p)
+    a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.Dqk, a.Dv = 1, 4, 4, 64, 64, 128, 128
+    a.window_left = -1
+    a.bias, a.bias_batch, a.bias_dtype = 8192, 1, lib.BF16
+    a.workspace, a.workspace_bytes = 1 << 20, 0
+    a.dbias = 8194  # 2-byte aligned: accepted as io type, rejected as fp32
+    assert so.sdpa_bwd_run(ctypes.byref(a)) == lib.UNSUPPORTED
+    a.dbias_io = 1
+    assert so.sdpa_bwd_run(ctypes.byref(a)) == lib.WORKSPACE_TOO_SMALL
+    a.dbias = 8193
+    assert so.sdpa_bwd_run(ctypes.byref(a)) == lib.UNSUPPORTED
+
+
 def test_nvfp4_qat_workspace_and_rejections(so):
     # the fake-quantised Q, K, V copies, then the chain's carve in the 4-wave layout (128-key
     # tiles): statistics and, on the atomic route, the fp32 dQ accumulator

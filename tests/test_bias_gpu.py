@@ -54,7 +54,7 @@ def _case(w, bias_batch, bias_f32, seed=11):
     return inp, o_bits, lse, bias32 if bias_f32 else bias_bits, lens, ref
 
 
-def _run(w, inp, o_bits, lse, bias, lens, det, want_dbias=True, ws_fill=None):
+def _run(w, inp, o_bits, lse, bias, lens, det, want_dbias=True, ws_fill=None, dbias_io=False):
     import attention_backward_sdpa_amd as lib
     dev = "cuda"
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -64,8 +64,8 @@ def _run(w, inp, o_bits, lse, bias, lens, det, want_dbias=True, ws_fill=None):
     outs = [torch.empty_like(x) for x in (q, k, v)]
     for x in outs:
         x.view(torch.int16).fill_(0x7FC0)
-    dbias = torch.full(tuple(bias.shape), float("nan"), dtype=torch.float32, device=dev) \
-        if want_dbias else None
+    dbias = torch.full(tuple(bias.shape), float("nan"), dtype=torch.bfloat16 if dbias_io else torch.float32,
+                       device=dev) if want_dbias else None
     kw = dict(scale=w.softmax_scale, causal=w.causal, window_left=w.window_left, deterministic=det,
               seq_q_lens=tl, seq_kv_lens=tl, bias=tb, dbias=dbias)
     n = lib.run_workspace_size(q, k, v, **kw)
@@ -75,6 +75,8 @@ def _run(w, inp, o_bits, lse, bias, lens, det, want_dbias=True, ws_fill=None):
     lib.sdpa_bwd_run(q, k, v, o, do, torch.from_numpy(lse).to(dev), *outs, workspace=ws, **kw)
     torch.cuda.synchronize()
     got = [C.bf16_tensor_to_f32(x) for x in outs]
+    if dbias is not None and dbias_io:
+        return got, C.bf16_tensor_to_f32(dbias)
     return got, None if dbias is None else dbias.cpu().numpy()
 
 
@@ -133,3 +135,34 @@ def test_bias_deterministic_bitwise(det):
             first = bits
         else:
             assert all(np.array_equal(a, b) for a, b in zip(first, bits))
+
+
+@pytest.mark.parametrize("det", [0, 2, 3], ids=["atomic", "dspanels", "dqpartials"])
+@pytest.mark.parametrize("name", ["gqa_causal_d128_s333", "gqa_causal_d128_s333_b1", "mla_window_padded_s300",
+                                  "mha_d64_s200x330"])
+def test_io_dtype_dbias(name, det):
+    # "The kernel chain" dbias_cvt: a bf16 dBias output is the fp32 dBias rounded once; within the
+    # parity tolerance of the oracle, masked pairs exactly 0, and the other gradients unchanged
+    w, bias_batch = CASES[name]
+    if bias_batch == 1 and w.B > 1 and det != 0:
+        pytest.skip("a batch-summed dBias needs the atomic route")
+    C.log(f"io-type dBias {name} route {det}")
+    inp, o_bits, lse, bias, lens, ref = _case(w, bias_batch, bias_f32=False)
+    got, dbias = _run(w, inp, o_bits, lse, bias, lens, det, dbias_io=True)
+    for tname, g, r in zip(("dQ", "dK", "dV", "dBias"), got + [dbias], ref):
+        C.assert_close(f"io dBias {name} route {det} {tname}", g, r)
+    got32, dbias32 = _run(w, inp, o_bits, lse, bias, lens, det)
+    # the io-type dBias is the fp32 one rounded to bf16 (exactly, on the deterministic routes)
+    if det != 0:
+        assert np.array_equal(dbias, C.synth.round_bf16(dbias32.astype(np.float32)))
+        for a, b in zip(got, got32):
+            assert np.array_equal(a, b)
+    for bb in range(dbias.shape[0]):
+        L = None if lens is None else lens[bb]
+        vis = oracle.visible_mask(w.Sq, w.Skv, w.causal, w.window_left, L, L)
+        if bias_batch == 1 and w.B > 1:
+            vis = np.any([oracle.visible_mask(w.Sq, w.Skv, w.causal, w.window_left,
+                                              None if lens is None else lens[x],
+                                              None if lens is None else lens[x])
+                          for x in range(w.B)], axis=0)
+        assert np.all(dbias[bb][:, ~vis] == 0)
