@@ -8,9 +8,9 @@ column sums of dV equal the summed dO of the rows that see a key (sum_j P_ij = 1
 sums of dK vanish (sum_j dS_ij = 0), padded rows are exactly zero, and the deterministic route is
 bitwise identical over 10 runs.
 
-O and LSE are inputs: at full size they come from a float32 forward computed with torch on the
-GPU (the same preparation bench.py uses; the oracle forward would take minutes per workload).
-Both the GPU path and the oracle backward consume exactly these tensors.
+O and LSE are the workloads' own inputs: the fp64 oracle forward on the drawn Q, K, V (and
+lengths), rounded to bf16 / fp32, as for the reduced sizes.  Both the GPU path and the oracle
+backward consume exactly these tensors.
 """
 import hashlib
 
@@ -47,20 +47,25 @@ ROUTE_NAMES = {0: "atomic", 1: "det", 2: "dspanels", 3: "dqpartials", 4: "relay"
 
 
 def _prepare(w):
-    import bench
     C.log(f"full-size case {w.name}: drawing inputs")
     inp = synth.draw_inputs(w)
     dev = torch.device("cuda:0")
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
     t = dict(q=bf(inp.q), k=bf(inp.k), v=bf(inp.v), do=bf(inp.do))
     lens = inp.seq_q_lens
-    C.log(f"full-size case {w.name}: float32 forward for O and LSE")
-    t["o"], t["lse"] = bench.gpu_forward_inputs(torch, t["q"], t["k"], t["v"], w, lens)
+    lens_l = None if lens is None else [int(x) for x in lens]
+    C.log(f"full-size case {w.name}: fp64 oracle forward for O and LSE")
+    o64, lse64 = oracle.forward(_f64(inp.q), _f64(inp.k), _f64(inp.v), w.softmax_scale,
+                                causal=w.causal, window_left=w.window_left, seq_q_lens=lens_l,
+                                seq_kv_lens=lens_l)
+    o_bits = synth.bf16_bits(o64.astype(np.float32))
+    lse = lse64.astype(np.float32)
+    del o64, lse64
+    t["o"], t["lse"] = bf(o_bits), torch.from_numpy(lse).to(dev)
     t["lens"] = None if lens is None else torch.from_numpy(lens).to(dev)
     torch.cuda.synchronize()
-    host = dict(q=inp.q, k=inp.k, v=inp.v, do=inp.do,
-                o=t["o"].cpu().view(torch.int16).numpy().view(np.uint16),
-                lse=t["lse"].cpu().numpy(), lens=lens)
+    C.log(f"full-size case {w.name}: inputs ready")
+    host = dict(q=inp.q, k=inp.k, v=inp.v, do=inp.do, o=o_bits, lse=lse, lens=lens)
     return t, host
 
 

@@ -102,8 +102,8 @@ def test_nvfp4_qat_dv_uses_quantised_probability():
 @pytest.mark.parametrize("det", [0, 2], ids=["atomic", "dspanels"])
 def test_nvfp4_qat_fullsize_sampled_rows(det):
     # the QAT page's example shape, B1 H16 S4096 D128 non-causal (and its causal variant on the
-    # atomic route), in the launch configuration bench.py --qat times: sampled rows of three heads
-    import bench
+    # atomic route), in the launch configuration bench.py --qat times: sampled rows of three heads;
+    # O_hp and LSE from the oracle's QAT forward
     from oracle import nvfp4_qat as Q
     w = W["qat_mha_s4096_d128"]
     for causal in ([False, True] if det == 0 else [False]):
@@ -112,9 +112,12 @@ def test_nvfp4_qat_fullsize_sampled_rows(det):
         inp = synth.draw_inputs(wc)
         f32 = lambda bits: synth.bf16_to_f32(bits)
         bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
-        hat = {x: bf(synth.bf16_bits(oracle.fake_nvfp4(f32(getattr(inp, x))))) for x in ("q", "k", "v")}
-        C.log("qat full size: float32 forward of the fake-quantised inputs for O_hp and LSE")
-        o, lse = bench.gpu_forward_inputs(torch, hat["q"], hat["k"], hat["v"], wc, None)
+        C.log("qat full size: fp64 oracle QAT forward (O_hp and LSE of the fake-quantised inputs)")
+        o64, lse64 = oracle.qat_forward(f32(inp.q), f32(inp.k), f32(inp.v), wc.softmax_scale,
+                                        causal=causal)
+        o = bf(synth.bf16_bits(o64.astype(np.float32)))
+        lse = torch.from_numpy(lse64.astype(np.float32)).cuda()
+        del o64, lse64
         q, k, v, do = bf(inp.q), bf(inp.k), bf(inp.v), bf(inp.do)
         outs = [torch.empty_like(x) for x in (q, k, v)]
         import attention_backward_sdpa_amd as lib

@@ -589,3 +589,34 @@ def test_planted_dbias_mistakes_are_caught(kind):
         bias[mi] = old
         fd[mi] = (lp - lm) / (2 * h)
     assert np.max(np.abs(dbias - fd)) > 1e-3
+
+
+@pytest.mark.parametrize("mask", [dict(causal=False, W=-1), dict(causal=True, W=-1),
+                                  dict(causal=True, W=2)], ids=str)
+@pytest.mark.parametrize("scale", [0.37, 2.5])
+def test_bias_matches_torch_float_mask(mask, scale):
+    # the bias's place relative to the softmax scale, pinned by a library routine: torch's fp64 CPU
+    # SDPA with a float attn_mask adds the mask to the already scaled scores; at a scale other than
+    # 1 (and 1/sqrt(D)) a bias applied before the scale, or scaled with it, would differ.  O, LSE
+    # (through O), dQ, dK, dV and dBias (the mask's gradient) must agree.
+    q, k, v, do, _, _, _, kw = _problem(46, B=2, Hq=2, Hkv=2, Sq=7, Skv=7, Dqk=8, Dv=6, **mask)
+    bias = np.random.default_rng(47).standard_normal((2, 2, 7, 7)) * 1.5
+    o, lse = oracle.forward(q, k, v, scale, bias=bias, **kw)
+    dq, dk, dv, dbias = oracle.backward(q, k, v, o, do, lse, scale, bias=bias, return_dbias=True,
+                                        **kw)
+    vis = oracle.visible_mask(7, 7, kw["causal"], kw["window_left"])
+    tb = torch.tensor(bias, requires_grad=True)
+    attn_mask = tb + torch.tensor(np.where(vis, 0.0, -np.inf))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=attn_mask,
+                                                           scale=scale)
+    out.backward(torch.tensor(do))
+    np.testing.assert_allclose(o, out.detach().numpy(), rtol=1e-12, atol=1e-12)
+    for got, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad), (dbias, tb.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-10, atol=1e-12)
+    # the same mask placed before the scale is a different function (the pin discriminates)
+    pre = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q), torch.tensor(k), torch.tensor(v),
+        attn_mask=torch.tensor(bias * scale) + torch.tensor(np.where(vis, 0.0, -np.inf)),
+        scale=scale)
+    assert np.max(np.abs(pre.numpy() - o)) > 1e-3
