@@ -191,15 +191,34 @@ def write_traffic_record(workload, det_arg, dtype, fetch_dir, write_dir):
     print(json.dumps(rec, indent=1))
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, inp, lens, dtype="bf16", budget_s=15.0, qat=False):
     """The fp64 CPU oracle (unchanged) on the first query heads of batch entry 0, timed until
-    about budget_s seconds of work; the rate is scaled to the same FLOP convention."""
+    about budget_s seconds of work; the rate is scaled to the same FLOP convention.  `cores` is
+    the thread count of the BLAS pool the oracle ran on, `cores_available` the CPUs this process
+    may run on (sched_getaffinity)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        affinity = os.cpu_count()
     group = w.Hq // w.Hkv
     f = lambda x: synth.bits_to_f32(x, dtype).astype(np.float64)
     to_io = synth.fp16_bits if dtype == "fp16" else synth.bf16_bits
@@ -227,7 +246,7 @@ def cpu_baseline(w, inp, lens, dtype="bf16", budget_s=15.0, qat=False):
         flops += algorithmic_flops(one, None if lens is None else [lens[0]])
         heads += 1
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "cores_available": int(affinity), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{heads} of {w.B * w.Hq} (batch, query-head) slices of {w.name}, "
                       f"{'NVFP4-QAT ' if qat else ''}backward only, fp64 numpy, {t_total:.1f} s"}
 
