@@ -325,6 +325,15 @@ struct Gemm4Lanes {
   }
 };
 
+// The lane index as a value the compiler cannot see through: offsets derived from it are then
+// recomputed where they are used instead of being hoisted out of the q-tile loop, where at head
+// dims 192 and up they would be spilled and reloaded (each reload waits for every outstanding
+// vector memory access of the wave).
+__device__ __forceinline__ int opaque_lane(int lane) {
+  asm volatile("" : "+v"(lane));
+  return lane;
+}
+
 // Scheduling hint for a block of NMFMA MFMAs fed by NREAD LDS reads: issue AHEAD reads first, then
 // alternate one MFMA with the reads that keep the queue AHEAD deep, so LDS latency hides behind
 // the matrix core instead of stalling each MFMA on an lgkmcnt(0).
@@ -551,7 +560,7 @@ __device__ __forceinline__ void gemm4_16(const char* sST, const char* sK, float*
   using M16 = Mfma16<C::F16>;
   constexpr int DQK = C::DQK, NB = C::NB4, NW = C::NW;
   if (w >= C::G4_BLOCKS) return;  // head dim 32: waves past the 4 blocks have none
-  const Gemm4Lanes16 tl(lane, w);
+  const Gemm4Lanes16 tl(C::DQK >= 192 ? opaque_lane(lane) : lane, w);
   floatx4 acc[NB];
 #pragma unroll
   for (int m = 0; m < NB; ++m) acc[m] = floatx4{};
@@ -606,8 +615,11 @@ __device__ __forceinline__ void gemm4(const char* sST, const char* sK, float* ds
   using M = typename C::M;
   using acc_t = typename M::acc_t;
   constexpr int DQK = C::DQK;
-  const int g = lane >> 5, lc = lane & 31;
-  const Gemm4Lanes tl(lane);
+  // head dims 192 and up: lane offsets recomputed here (see opaque_lane); below, the registers
+  // to hold them are there
+  const int ol = C::DQK >= 192 ? opaque_lane(lane) : lane;
+  const int g = ol >> 5, lc = ol & 31;
+  const Gemm4Lanes tl(ol);
   const bool full = q0 + C::BR <= Lq;
   for (int dt = w; dt < C::N_DQT; dt += C::NW) {
     acc_t acc = acc_t{};
@@ -629,18 +641,21 @@ __device__ __forceinline__ void gemm4(const char* sST, const char* sK, float* ds
         relay_store16(dst, C::BR * DQK * 4, (dt * 1024 + 256 * x + 4 * lane) * 4, v);
       }
     } else {
-      float* row0 = dst + dt * 32 + lc;
+      // register r holds row 4g + rc(r), rc(r) = 8 (r / 4) + r % 4: the lane-dependent part goes
+      // into the base pointer, the rest is a constant per register (no per-row addresses to keep)
+      float* base = dst + dt * 32 + lc + (4 * g) * DQK;
       if (full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          __hip_atomic_fetch_add(row0 + acc_row<32>(r, g) * DQK, acc[r], __ATOMIC_RELAXED,
+          __hip_atomic_fetch_add(base + ((r / 4) * 8 + r % 4) * DQK, acc[r], __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
       } else {
+        const int live = Lq - q0 - 4 * g;  // registers whose rc is below this are rows < Lq
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = acc_row<32>(r, g);
-          if (q0 + row < Lq)
-            __hip_atomic_fetch_add(row0 + row * DQK, acc[r], __ATOMIC_RELAXED,
+          const int rc = (r / 4) * 8 + r % 4;
+          if (rc < live)
+            __hip_atomic_fetch_add(base + rc * DQK, acc[r], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
       }
