@@ -33,7 +33,8 @@ def test_m0_written_only_for_lds_dma(asm):
     for i, t in enumerate(ins):
         if not re.search(r"\bm0\b", t):
             continue
-        assert re.fullmatch(r"s_mov_b32 m0, s\d+", t), f"unexpected M0 use: {t}"
+        # the asm's scalar operand may land in any SGPR, vcc_lo/vcc_hi included
+        assert re.fullmatch(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)", t), f"unexpected M0 use: {t}"
         nxt = ins[i + 1]
         assert re.match(r"buffer_load_dword(x4)? v\d+, s\[\d+:\d+\], 0 offen (sc1 )?lds", nxt), \
             f"M0 write not followed by its LDS-DMA load: {t} / {nxt}"
