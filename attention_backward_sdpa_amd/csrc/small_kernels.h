@@ -50,25 +50,40 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
   if (p.relay_turn && tid == 0) p.relay_turn[blockIdx.x] = 0;
   if (p.relay_ctl && blockIdx.x == 0 && tid < 16) p.relay_ctl[tid] = 0;
 
-  for (int r0 = 0; r0 < BR; r0 += RPP) {
-    const int r = r0 + tid / LPR, sub = tid % LPR, s = q0 + r;
+  // every pass's loads go out before the first row dot
+  constexpr int NP = (BR + RPP - 1) / RPP;
+  const int sub = tid % LPR;
+  u32x4 av[NP], cv[NP];
+  float lv[NP];
+#pragma unroll
+  for (int pi = 0; pi < NP; ++pi) {
+    const int r = pi * RPP + tid / LPR, s = q0 + r;
+    av[pi] = cv[pi] = u32x4{0u, 0u, 0u, 0u};
+    lv[pi] = -INFINITY;
+    if (r < BR && s < Lq) {
+      if (sub == 0) lv[pi] = p.lse[bh * p.Sq + s];
+      if (sub * 8 < p.dv_act) {
+        av[pi] = *reinterpret_cast<const u32x4*>(ob + s * p.so.s + sub * 8);
+        cv[pi] = *reinterpret_cast<const u32x4*>(dob + s * p.sdo.s + sub * 8);
+      }
+    }
+  }
+#pragma unroll
+  for (int pi = 0; pi < NP; ++pi) {
+    const int r = pi * RPP + tid / LPR, s = q0 + r;
     if (r >= BR) break;  // head dim 32: one pass covers 64 rows, the tile has 32
     const bool live = s < Lq;
     const int64_t row = bh * p.Sq + s;
     float acc = 0.f;
-    if (live && sub * 8 < p.dv_act) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(ob + s * p.so.s + sub * 8);
-      const u32x4 c = *reinterpret_cast<const u32x4*>(dob + s * p.sdo.s + sub * 8);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc += Elem<F16>::lo(a[e]) * Elem<F16>::lo(c[e]);
-        acc += Elem<F16>::hi(a[e]) * Elem<F16>::hi(c[e]);
-      }
+    for (int e = 0; e < 4; ++e) {
+      acc += Elem<F16>::lo(av[pi][e]) * Elem<F16>::lo(cv[pi][e]);
+      acc += Elem<F16>::hi(av[pi][e]) * Elem<F16>::hi(cv[pi][e]);
     }
 #pragma unroll
     for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPR);
     if (sub == 0) {
-      const float l = live ? p.lse[row] : -INFINITY;
+      const float l = lv[pi];
       const bool none = !(l > -INFINITY);  // -inf (or NaN) LSE: the row saw no key
       reinterpret_cast<float2*>(p.stats)[bh * p.sq_pad + s] =
           make_float2(none ? INFINITY : l * kLog2e, (live && !none) ? acc : 0.f);
@@ -104,19 +119,28 @@ __global__ void __launch_bounds__(256) dq_convert_kernel(ConvertParams p) {
   const int b = (int)(bh / p.Hq), h = (int)(bh % p.Hq);
   const int Lq = p.seq_q_lens ? min(max(p.seq_q_lens[b], 0), p.Sq) : p.Sq;
   bf16_t* dqb = p.dq + b * p.sdq.b + h * p.sdq.h;
-  for (int v = threadIdx.x; v < 32 * V; v += 256) {
-    const int s = q0 + v / V, c = v % V;
-    if (s >= p.Sq) break;
-    if (c * 8 >= p.dqk_act) continue;
-    const int64_t x = (bh * p.Sq + s) * V + c;
-    u32x4 out = u32x4{0u, 0u, 0u, 0u};
-    if (s < Lq) {
-      const floatx4 a = reinterpret_cast<const floatx4*>(p.acc)[2 * x];
-      const floatx4 d = reinterpret_cast<const floatx4*>(p.acc)[2 * x + 1];
-      const float k = p.scale;
-      out = u32x4{Elem<F16>::pack2(a[0] * k, a[1] * k), Elem<F16>::pack2(a[2] * k, a[3] * k),
-                  Elem<F16>::pack2(d[0] * k, d[1] * k), Elem<F16>::pack2(d[2] * k, d[3] * k)};
+  // every load of the thread goes out before the first conversion
+  constexpr int NIT = (32 * V + 255) / 256;
+  floatx4 a[NIT], d[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int v = threadIdx.x + it * 256, s = q0 + v / V, c = v % V;
+    a[it] = d[it] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (v < 32 * V && s < Lq && c * 8 < p.dqk_act) {
+      const int64_t x = (bh * p.Sq + s) * V + c;
+      a[it] = reinterpret_cast<const floatx4*>(p.acc)[2 * x];
+      d[it] = reinterpret_cast<const floatx4*>(p.acc)[2 * x + 1];
     }
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int v = threadIdx.x + it * 256, s = q0 + v / V, c = v % V;
+    if (v >= 32 * V || s >= p.Sq || c * 8 >= p.dqk_act) continue;
+    const float k = p.scale;
+    const u32x4 out = u32x4{Elem<F16>::pack2(a[it][0] * k, a[it][1] * k),
+                            Elem<F16>::pack2(a[it][2] * k, a[it][3] * k),
+                            Elem<F16>::pack2(d[it][0] * k, d[it][1] * k),
+                            Elem<F16>::pack2(d[it][2] * k, d[it][3] * k)};
     *reinterpret_cast<u32x4*>(dqb + s * p.sdq.s + c * 8) = out;
   }
 }
@@ -152,13 +176,21 @@ __global__ void __launch_bounds__(256) gqa_reduce_kernel(ReduceParams p) {
       if (c * 8 >= (isk ? p.dqk_act : p.dv_act)) continue;
       const u32x4* src = reinterpret_cast<const u32x4*>(isk ? p.dk_ws : p.dv_ws) +
                          (int64_t)kvhead * p.group * per + y;
+      // the slots' loads go out four at a time, then add in ascending slot order
       float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int gi = 0; gi < p.group; ++gi) {
-        const u32x4 v = src[(int64_t)gi * per];
+      for (int g0 = 0; g0 < p.group; g0 += 4) {
+        u32x4 v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          s[2 * e] += Elem<F16>::lo(v[e]);
-          s[2 * e + 1] += Elem<F16>::hi(v[e]);
+        for (int u = 0; u < 4; ++u)
+          if (g0 + u < p.group) v[u] = src[(int64_t)(g0 + u) * per];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (g0 + u >= p.group) break;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s[2 * e] += Elem<F16>::lo(v[u][e]);
+            s[2 * e + 1] += Elem<F16>::hi(v[u][e]);
+          }
         }
       }
       const Strides& st = isk ? p.sdk : p.sdv;
