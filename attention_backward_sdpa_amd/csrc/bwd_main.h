@@ -169,7 +169,11 @@ struct MainCfg {
   static constexpr int OFF_ST = OFF_T + NBUF * TILE_BYTES;
   static constexpr int OFF_RS = OFF_ST + NSST * SST_BYTES;
   static constexpr int OFF_QS = OFF_RS + RS_BYTES;
-  static constexpr int LDS_BYTES = OFF_QS + QS_BYTES;
+  // epilogue: each wave's dK, then dV, tile (32 keys) staged as rows of EPI_PITCH bytes
+  static constexpr int EPI_PITCH = (DQK > DV ? DQK : DV) * 2 + 16;
+  static constexpr int EPI_BYTES = NW * 32 * EPI_PITCH;
+  static constexpr int LDS_BYTES =
+      OFF_QS + QS_BYTES > EPI_BYTES ? OFF_QS + QS_BYTES : EPI_BYTES;
   static_assert(KPW == 32, "one 32-key MFMA tile per wave (the q-tile loop body assumes it)");
   static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
   static_assert(DQK % 32 == 0 && DV % 32 == 0, "head dims must be multiples of 32");
@@ -1066,37 +1070,49 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
   }
 
   // ---- epilogue: dK (scaled) and dV, written once; keys past the sequence are zero -------------
-  const int64_t oslot = p.partials ? (int64_t)bh * p.n_split + part : (int64_t)b * p.Hkv + kvh;
+  // A lane holds one key's column of accumulators (4 consecutive head-dim values per group), so
+  // a direct store would scatter every instruction over 32 key rows.  Each wave instead stages its
+  // 32-key tile in LDS as rows (8-byte writes) and reads it back row-major, so each lane stores 16
+  // contiguous bytes and each store instruction covers whole rows.  dK first, then dV in the same
+  // rows (this wave's own LDS: its accesses stay in order).
+  static_assert(NKT == 1, "one 32-key tile per wave");
+  lds_barrier();  // every wave is done with the loop's LDS (no LDS-DMA is in flight after it)
+  {
+    char* ep = smem + w * 32 * C::EPI_PITCH;
+    const int64_t oslot = p.partials ? (int64_t)bh * p.n_split + part : (int64_t)b * p.Hkv + kvh;
+    const int key0 = key_lane - lc;  // the wave's first key
+    auto out_tile = [&](const acc_t (*acc)[NKT], auto n_dt_tag, float scale, bf16_t* out_base,
+                        const Strides& st, int d_kernel, int d_act) {
+      constexpr int NDT = decltype(n_dt_tag)::value;
 #pragma unroll
-  for (int kt = 0; kt < NKT; ++kt) {
-    const int key = key_lane + kt * 32;
-    if (key < p.Skv) {
-      // partials: contiguous per (query head, part); final dK/dV: the caller's layout
-      bf16_t* dkr = p.partials ? p.dk_out + (oslot * p.Skv + key) * DQK
-                               : p.dk_out + b * p.sdk.b + kvh * p.sdk.h + key * p.sdk.s;
-      bf16_t* dvr = p.partials ? p.dv_out + (oslot * p.Skv + key) * DV
-                               : p.dv_out + b * p.sdv.b + kvh * p.sdv.h + key * p.sdv.s;
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < C::N_DQT; ++dt)
+        for (int r0 = 0; r0 < 16; r0 += 4)
+          *reinterpret_cast<u32x2*>(ep + lc * C::EPI_PITCH + (dt * 32 + acc_row<32>(r0, g)) * 2) =
+              u32x2{Elem<C::F16>::pack2(acc[dt][0][r0] * scale, acc[dt][0][r0 + 1] * scale),
+                    Elem<C::F16>::pack2(acc[dt][0][r0 + 2] * scale, acc[dt][0][r0 + 3] * scale)};
+      constexpr int CPR = NDT * 32 * 2 / 16;  // 16-byte pieces per key row
+      constexpr int NX = 32 * CPR / 64;
+      u32x4 v[NX];
 #pragma unroll
-        for (int r0 = 0; r0 < 16; r0 += 4) {
-          const int d = dt * 32 + acc_row<32>(r0, g);
-          if (C::PAD && !p.partials && d >= dqk_act) continue;  // past the tensor's head dim
-          *reinterpret_cast<u32x2*>(dkr + d) = u32x2{
-              Elem<C::F16>::pack2(accK[dt][kt][r0] * p.scale, accK[dt][kt][r0 + 1] * p.scale),
-              Elem<C::F16>::pack2(accK[dt][kt][r0 + 2] * p.scale, accK[dt][kt][r0 + 3] * p.scale)};
-        }
+      for (int x = 0; x < NX; ++x) {
+        const int k = x * 64 + lane;
+        v[x] = *reinterpret_cast<const u32x4*>(ep + (k / CPR) * C::EPI_PITCH + (k % CPR) * 16);
+      }
 #pragma unroll
-      for (int dt = 0; dt < C::N_DVT; ++dt)
-#pragma unroll
-        for (int r0 = 0; r0 < 16; r0 += 4) {
-          const int d = dt * 32 + acc_row<32>(r0, g);
-          if (C::PAD && !p.partials && d >= dv_act) continue;
-          *reinterpret_cast<u32x2*>(dvr + d) =
-              u32x2{Elem<C::F16>::pack2(accV[dt][kt][r0], accV[dt][kt][r0 + 1]),
-                    Elem<C::F16>::pack2(accV[dt][kt][r0 + 2], accV[dt][kt][r0 + 3])};
-        }
-    }
+      for (int x = 0; x < NX; ++x) {
+        const int k = x * 64 + lane, row = k / CPR, ch = k % CPR;
+        const int key = key0 + row;
+        if (key >= p.Skv) continue;
+        if (C::PAD && !p.partials && ch * 8 >= d_act) continue;  // past the tensor's head dim
+        // partials: contiguous per (query head, part); final dK/dV: the caller's layout
+        bf16_t* dst = p.partials ? out_base + (oslot * p.Skv + key) * d_kernel
+                                 : out_base + b * st.b + kvh * st.h + key * st.s;
+        *reinterpret_cast<u32x4*>(dst + ch * 8) = v[x];
+      }
+    };
+    out_tile(accK, IntTag<C::N_DQT>{}, p.scale, p.dk_out, p.sdk, DQK, dqk_act);
+    out_tile(accV, IntTag<C::N_DVT>{}, 1.0f, p.dv_out, p.sdv, DV, dv_act);
   }
 }
 

@@ -61,7 +61,10 @@ struct Dq2kCfg {
   static constexpr int KR = DQK > 192 ? 2 : 3;
   static constexpr int UNROLL = lcm_c(lcm_c(AHEAD, KR), 2);  // ring slots and LDS buffer constant
   static constexpr int OFF_DS = 2 * K_BYTES;                 // per-wave dS transpose areas
-  static constexpr int LDS_BYTES = OFF_DS + NW * KC * BR * 2;
+  static constexpr int EPI_PITCH = DQK * 2 + 16;             // bytes per dQ row in the epilogue
+  static constexpr int EPI_BYTES = NW * BR * EPI_PITCH;
+  static constexpr int LDS_BYTES =
+      OFF_DS + NW * KC * BR * 2 > EPI_BYTES ? OFF_DS + NW * KC * BR * 2 : EPI_BYTES;
   static_assert(BC % KC == 0, "whole chunks per KV tile");
   static_assert(K_FRAGS % NW == 0, "even K split over waves");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -232,18 +235,49 @@ __global__ void __launch_bounds__(C::NT, 1) dq2k_kernel(Dq2kParams p) {
     }
   }
 
-  // dQ = scale * acc; rows past the buffer are not stored, rows past len_q come out exactly zero
+  // dQ = scale * acc, through LDS as packed rows (the loop's last barrier has passed: every wave
+  // is done with the K and dS areas).  A lane holds one column of 16 rows, so for accumulator rows
+  // r, r + 1 (adjacent rows) an even lane packs row r's columns lc, lc + 1 and an odd lane row
+  // r + 1's columns lc - 1, lc, swapping the missing value with its neighbour (DPP quad
+  // permutation 1, 0, 3, 2); read back row-major, every lane stores 16 contiguous bytes of a row.
+  // Rows past len_q come out exactly zero; rows past the buffer and columns past the head dim are
+  // not stored.
   if (i0 + w < p.n_q_tiles) {
+    char* epi = smem + w * (BR * C::EPI_PITCH);
+    const bool odd = lc & 1;
+#pragma unroll
+    for (int dt = 0; dt < C::N_DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        // both neighbours' values move (the select then picks between two finished words, not
+        // between accumulator elements, which the compiler would turn into a variable index)
+        const float x0 = acc[dt][r] * p.scale, x1 = acc[dt][r + 1] * p.scale;
+        auto swap = [](float v) {
+          return __builtin_bit_cast(
+              float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+        };
+        const uint32_t w_even = Elem<C::F16>::pack2(x0, swap(x0));  // row r: columns lc, lc + 1
+        const uint32_t w_odd = Elem<C::F16>::pack2(swap(x1), x1);   // row r + 1: lc - 1, lc
+        const int row = acc_row<32>(r, g) + (odd ? 1 : 0);
+        *reinterpret_cast<uint32_t*>(epi + row * C::EPI_PITCH + (dt * 32 + (lc & ~1)) * 2) =
+            odd ? w_odd : w_even;
+      }
+    constexpr int CPR = DQK / 8;  // 16-byte pieces per row
+    constexpr int NX = BR * CPR / 64;
     const int q0 = (i0 + w) * BR;
     bf16_t* dqb = p.dq + b * p.sdq.b + h * p.sdq.h;
+    u32x4 v[NX];
 #pragma unroll
-    for (int dt = 0; dt < C::N_DT; ++dt) {
+    for (int x = 0; x < NX; ++x) {
+      const int k = x * 64 + lane;
+      v[x] = *reinterpret_cast<const u32x4*>(epi + (k / CPR) * C::EPI_PITCH + (k % CPR) * 16);
+    }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = q0 + acc_row<32>(r, g);
-        if (q < p.Sq && dt * 32 + lc < p.dqk_act)
-          dqb[(int64_t)q * p.sdq.s + dt * 32 + lc] = Elem<C::F16>::one(acc[dt][r] * p.scale);
-      }
+    for (int x = 0; x < NX; ++x) {
+      const int k = x * 64 + lane, row = k / CPR, ch = k % CPR;
+      const int q = q0 + row;
+      if (q < p.Sq && ch * 8 < p.dqk_act)
+        *reinterpret_cast<u32x4*>(dqb + (int64_t)q * p.sdq.s + ch * 8) = v[x];
     }
   }
 }
