@@ -12,7 +12,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc", "sdpa_bwd.hip")
 # translation units: the host side with the small kernels, and the main kernel's instantiations
 # of each kernel head dim (the bulk of the compile time), built in parallel
-SOURCES = [SRC] + [os.path.join(HERE, "csrc", f"main_d{d}.hip") for d in (32, 64, 128, 192, 256)]
+SOURCES = [SRC] + [os.path.join(HERE, "csrc", f"main_d{d}.hip") for d in (32, 64, 128, 192, 256)] + \
+    [os.path.join(HERE, "csrc", "main_ilp.hip")]
+# per-source flags: main_ilp.hip holds the main-kernel instantiations that run faster under the
+# backend's latency-oriented scheduler (see IlpSched in main_launch.h)
+SOURCE_FLAGS = {"main_ilp.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+
+
+def _src_flags(src):
+    return SOURCE_FLAGS.get(os.path.basename(src), [])
 OUT = os.path.join(HERE, "libsdpa_bwd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -52,7 +60,7 @@ def build(verbose: bool = False) -> str:
     compile_flags = [f for f in FLAGS if f != "-shared"]
     with tempfile.TemporaryDirectory(prefix="sdpa_bwd_build_") as tmpdir:
         objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in SOURCES]
-        _parallel([[HIPCC, *compile_flags, "-c", src, "-o", obj]
+        _parallel([[HIPCC, *compile_flags, *_src_flags(src), "-c", src, "-o", obj]
                    for src, obj in zip(SOURCES, objs)], verbose)
         tmp = OUT + ".tmp"
         _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
@@ -63,8 +71,8 @@ def build(verbose: bool = False) -> str:
 def device_assembly() -> str:
     """The gfx950 assembly of the library's kernels (device pass only), for inspection."""
     flags = [f for f in FLAGS if f not in ("-shared", "-fPIC")]
-    return "\n".join(_parallel([[HIPCC, *flags, "--offload-device-only", "-S", src, "-o", "-"]
-                                for src in SOURCES], False))
+    return "\n".join(_parallel([[HIPCC, *flags, *_src_flags(src), "--offload-device-only", "-S", src,
+                                 "-o", "-"] for src in SOURCES], False))
 
 
 if __name__ == "__main__":

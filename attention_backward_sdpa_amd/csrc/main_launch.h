@@ -40,12 +40,34 @@ hipError_t lds_limit_once(F* kernel, int bytes) {
   return e;
 }
 
+// Instantiations compiled with the backend's latency-oriented scheduler (main_ilp.hip, built with
+// -amdgpu-sched-strategy=iterative-ilp): with every register of a one-wave-per-SIMD kernel taken
+// (head dim 256) the default scheduler issued each GEMM1/GEMM2 operand read one MFMA ahead and
+// waited on it, an LDS round trip per MFMA with no other wave to hide it.  Measured on the
+// kernels listed here only (the others spill or run slower under it): the plain (no bias, exact
+// head dims) head-dim-256 atomic, dS-panel and dQ-partial kernels and the head-dim-128 dS-panel
+// kernel.
+template <class C>
+struct IlpSched {
+  static constexpr bool value =
+      C::BIAS == 0 && !C::PAD && !C::QAT && C::KPW == 32 &&
+      ((C::DQK == 256 && C::DV == 256 && C::NW == 4 && C::MODE != DQ_RELAY) ||
+       (C::DQK == 128 && C::DV == 128 && C::NW == 8 && C::MODE == DQ_DS));
+};
+
+template <class C>
+hipError_t launch_main_cfg_ilp(const MainParams& mp, int grid, hipStream_t s);  // main_ilp.hip
+
 template <class C>
 hipError_t launch_main_cfg(const MainParams& mp, int grid, hipStream_t s) {
-  const hipError_t e = lds_limit_once<C>(bwd_main_kernel<C>, C::LDS_BYTES);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_main_kernel<C>, dim3(grid), dim3(C::NT), C::LDS_BYTES, s, mp);
-  return hipGetLastError();
+  if constexpr (IlpSched<C>::value) {
+    return launch_main_cfg_ilp<C>(mp, grid, s);
+  } else {
+    const hipError_t e = lds_limit_once<C>(bwd_main_kernel<C>, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_main_kernel<C>, dim3(grid), dim3(C::NT), C::LDS_BYTES, s, mp);
+    return hipGetLastError();
+  }
 }
 
 template <int DQK, int DV, int KPW, int NW, bool F16, int BIAS, bool PAD, bool QAT = false>
