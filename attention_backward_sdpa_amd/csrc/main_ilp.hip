@@ -26,5 +26,7 @@ SDPA_ILP(256, 4, DQ_PARTIAL, true)
 SDPA_ILP(128, 8, DQ_DS, false)
 SDPA_ILP(128, 8, DQ_DS, true)
 #undef SDPA_ILP
+template hipError_t launch_main_cfg_ilp<MainCfg<128, 128, 32, 4, DQ_DS, false, 0, false, true>>(
+    const MainParams&, int, hipStream_t);  // NVFP4 QAT
 
 }  // namespace sdpa

@@ -45,14 +45,15 @@ hipError_t lds_limit_once(F* kernel, int bytes) {
 // (head dim 256) the default scheduler issued each GEMM1/GEMM2 operand read one MFMA ahead and
 // waited on it, an LDS round trip per MFMA with no other wave to hide it.  Measured on the
 // kernels listed here only (the others spill or run slower under it): the plain (no bias, exact
-// head dims) head-dim-256 atomic, dS-panel and dQ-partial kernels and the head-dim-128 dS-panel
-// kernel.
+// head dims) head-dim-256 atomic, dS-panel and dQ-partial kernels, the head-dim-128 dS-panel
+// kernel and the NVFP4 QAT dS-panel kernel.
 template <class C>
 struct IlpSched {
   static constexpr bool value =
-      C::BIAS == 0 && !C::PAD && !C::QAT && C::KPW == 32 &&
-      ((C::DQK == 256 && C::DV == 256 && C::NW == 4 && C::MODE != DQ_RELAY) ||
-       (C::DQK == 128 && C::DV == 128 && C::NW == 8 && C::MODE == DQ_DS));
+      C::BIAS == 0 && !C::PAD && C::KPW == 32 &&
+      ((!C::QAT && C::DQK == 256 && C::DV == 256 && C::NW == 4 && C::MODE != DQ_RELAY) ||
+       (!C::QAT && C::DQK == 128 && C::DV == 128 && C::NW == 8 && C::MODE == DQ_DS) ||
+       (C::QAT && C::DQK == 128 && C::DV == 128 && C::NW == 4 && C::MODE == DQ_DS));
 };
 
 template <class C>
