@@ -56,8 +56,10 @@ struct Dq2kCfg {
   static constexpr int K_BYTES = K_FRAGS * 1024;
   static constexpr int K_PER_WAVE = K_FRAGS / NW;
   // chunks of dS in flight per wave, and of K held in registers (fewer at head dim 256, where the
-  // 128 accumulator registers leave less room)
-  static constexpr int AHEAD = DQK > 192 ? 3 : 4;
+  // 128 accumulator registers leave less room).  Measured: two chunks of dS above head dim 128 and
+  // three at or below it beat deeper rings (the registers they free go to a denser schedule; a
+  // single 32 KiB chunk per CU in flight already reaches the stream's rate)
+  static constexpr int AHEAD = DQK > 128 ? 2 : 3;
   static constexpr int KR = DQK > 192 ? 2 : 3;
   static constexpr int UNROLL = lcm_c(lcm_c(AHEAD, KR), 2);  // ring slots and LDS buffer constant
   static constexpr int OFF_DS = 2 * K_BYTES;                 // per-wave dS transpose areas
