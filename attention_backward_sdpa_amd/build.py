@@ -13,10 +13,11 @@ SRC = os.path.join(HERE, "csrc", "sdpa_bwd.hip")
 # translation units: the host side with the small kernels, and the main kernel's instantiations
 # of each kernel head dim (the bulk of the compile time), built in parallel
 SOURCES = [SRC] + [os.path.join(HERE, "csrc", f"main_d{d}.hip") for d in (32, 64, 128, 192, 256)] + \
-    [os.path.join(HERE, "csrc", "main_ilp.hip")]
-# per-source flags: main_ilp.hip holds the main-kernel instantiations that run faster under the
+    [os.path.join(HERE, "csrc", f"main_ilp_d{d}.hip") for d in (128, 256)]
+# per-source flags: main_ilp_d*.hip hold the main-kernel instantiations that run faster under the
 # backend's latency-oriented scheduler (see IlpSched in main_launch.h)
-SOURCE_FLAGS = {"main_ilp.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+_ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+SOURCE_FLAGS = {"main_ilp_d128.hip": _ILP, "main_ilp_d256.hip": _ILP}
 
 
 def _src_flags(src):

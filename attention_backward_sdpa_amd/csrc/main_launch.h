@@ -40,24 +40,24 @@ hipError_t lds_limit_once(F* kernel, int bytes) {
   return e;
 }
 
-// Instantiations compiled with the backend's latency-oriented scheduler (main_ilp.hip, built with
-// -amdgpu-sched-strategy=iterative-ilp): with every register of a one-wave-per-SIMD kernel taken
-// (head dim 256) the default scheduler issued each GEMM1/GEMM2 operand read one MFMA ahead and
-// waited on it, an LDS round trip per MFMA with no other wave to hide it.  Measured on the
-// kernels listed here only (the others spill or run slower under it): the plain (no bias, exact
-// head dims) head-dim-256 atomic, dS-panel and dQ-partial kernels, the head-dim-128 dS-panel
-// kernel and the NVFP4 QAT dS-panel kernel.
+// Instantiations compiled with the backend's latency-oriented scheduler (main_ilp_d<DQK>.hip,
+// built with -amdgpu-sched-strategy=iterative-ilp): with every register of a one-wave-per-SIMD
+// kernel taken (head dim 256) the default scheduler issued each GEMM1/GEMM2 operand read one MFMA
+// ahead and waited on it, an LDS round trip per MFMA with no other wave to hide it.  The set is
+// what measured faster or the same under it without spilling: every bias-free head-dim-256
+// kernel (the bias variants spill), and every head-dim-128 kernel but the 8-wave dQ-partial ones
+// (slower under it).  The other head dims stay on the default schedule (192 spills, 32 does not
+// compile under it, 64 gains nothing).
 template <class C>
 struct IlpSched {
   static constexpr bool value =
-      C::BIAS == 0 && !C::PAD && C::KPW == 32 &&
-      ((!C::QAT && C::DQK == 256 && C::DV == 256 && C::NW == 4 && C::MODE != DQ_RELAY) ||
-       (!C::QAT && C::DQK == 128 && C::DV == 128 && C::NW == 8 && C::MODE == DQ_DS) ||
-       (C::QAT && C::DQK == 128 && C::DV == 128 && C::NW == 4 && C::MODE == DQ_DS));
+      C::KPW == 32 && C::DQK == C::DV &&
+      ((C::DQK == 256 && C::NW == 4 && C::BIAS == 0 && !C::QAT) ||
+       (C::DQK == 128 && !(C::NW == 8 && C::MODE == DQ_PARTIAL)));
 };
 
 template <class C>
-hipError_t launch_main_cfg_ilp(const MainParams& mp, int grid, hipStream_t s);  // main_ilp.hip
+hipError_t launch_main_cfg_ilp(const MainParams& mp, int grid, hipStream_t s);  // main_ilp_d*.hip
 
 template <class C>
 hipError_t launch_main_cfg(const MainParams& mp, int grid, hipStream_t s) {
