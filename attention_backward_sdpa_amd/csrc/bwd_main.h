@@ -47,6 +47,8 @@
 //     next iteration so its atomics (or partial stores) drain while that iteration computes.
 //   * The preprocess kernel supplies LSE * log2(e) per row (+inf for rows without keys), so the
 //     replay is one FMA and one v_exp_f32 per element.
+//   * 8-wave kernels without a bias: the two waves of each SIMD (w and w + 4) run half a q tile
+//     apart (staggered groups, see the q-tile loop), so that their softmax replays do not coincide.
 #pragma once
 #include "common.h"
 #include "masks.h"
@@ -157,13 +159,23 @@ struct MainCfg {
   // QAT: one 4 KiB fp32 P tile and 256 bytes of group scales per wave
   static constexpr int QS_WAVE = 4096 + 256;
   static constexpr int QS_BYTES = QAT_ ? NW * QS_WAVE : 0;
-  static constexpr int NBUF =
+  static constexpr int NBUF2 =
       (SK_BYTES + 2 * TILE_BYTES + SST_BYTES + RS_BYTES + QS_BYTES <= 160 * 1024) ? 2 : 1;
+  // Staggered wave groups (8 waves, no bias, no QAT, not the relay): waves 0-3 and 4-7, which
+  // share the four SIMDs pairwise, run half a q tile apart, so that one wave's softmax replay
+  // (VALU) overlaps the other wave's MFMAs (see the q-tile loop).  Needs a third q-tile buffer.
+  static constexpr bool PP = NW == 8 && MODE != DQ_RELAY && BIAS_ == 0 && !QAT_ &&
+                             SK_BYTES + 3 * TILE_BYTES + 2 * SST_BYTES <= 160 * 1024;
+  static constexpr int NBUF = PP ? 3 : NBUF2;
   // dS staging for GEMM4, double-buffered by q-tile parity where LDS allows: GEMM4 of the previous
   // q tile then needs no barrier of its own and overlaps the other waves' work
   static constexpr int NSST =
-      (G4 && SK_BYTES + NBUF * TILE_BYTES + 2 * SST_BYTES + RS_BYTES + QS_BYTES <= 160 * 1024) ? 2
-                                                                                              : 1;
+      PP ? 2
+         : ((G4 && SK_BYTES + NBUF2 * TILE_BYTES + 2 * SST_BYTES + RS_BYTES + QS_BYTES <= 160 * 1024)
+                ? 2
+                : 1);
+  // staggered groups: waves 4-7 hold GEMM4 blocks too (head dim 64: 16 x 16 blocks on all waves)
+  static constexpr bool G4_B = G4 && (G4_16 ? G4_BLOCKS > NW / 2 : N_DQT > NW / 2);
   static constexpr int OFF_K = 0;
   static constexpr int OFF_T = OFF_K + SK_BYTES;
   static constexpr int OFF_ST = OFF_T + NBUF * TILE_BYTES;
@@ -767,7 +779,10 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
   const TrALanes tra(lane);
 
   if (i_lo <= i_hi) {
-    auto tile = [&](int i) -> char* { return smem + C::OFF_T + (C::NBUF == 2 ? (i & 1) : 0) * C::TILE_BYTES; };
+    auto tile = [&](int i) -> char* {
+      const int buf = C::NBUF == 3 ? i % 3 : C::NBUF == 2 ? (i & 1) : 0;
+      return smem + C::OFF_T + buf * C::TILE_BYTES;
+    };
     // ---- q tile i into its LDS buffer ----------------------------------------------------------
     auto load_tile = [&](int i) {
       char* t = tile(i);
@@ -917,152 +932,296 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
       }
     };
 
-    for (int i = i_hi; i >= i_lo; --i) {
-      const int q0 = i * BR;
-      const char* T = tile(i);
-      const float* sStat = reinterpret_cast<const float*>(T + C::T_ST);
-      wait_vmem();      // this wave's loads of tile i (and its older atomics / stores) are done
-      lds_barrier();    // tile i landed everywhere; every wave is done with the previous tile
-      if constexpr (C::MODE == DQ_RELAY) {
-        // every wave's sums of q tile i + 2 (stored in the previous iteration) are complete
-        if (tid == 0 && i + 2 <= i_hi) relay_publish(relay_turn(i + 2), relay_rank(i + 2) + 1);
-      }
-      if (C::NBUF == 2 && i > i_lo) load_tile(i - 1);
-      if constexpr (C::DS_OUT) {
-        if (i < i_hi) store_ds(i + 1);
-      }
-      if constexpr (C::BIAS) {
-        if (i < i_hi) store_dbias(i + 1);
-        if (i > i_lo) load_bias(i - 1, bnext);
-      }
-
-      if constexpr (C::G4) {
-        // GEMM4 of the previous q tile (dS in sST), deferred so its atomics / partial stores
-        // overlap this tile
-        if (i < i_hi) {
-          const bool add = C::MODE == DQ_RELAY && relay_rank(i + 1) > 0;
-          if constexpr (C::G4_16)
-            gemm4_16<C>(sST(i + 1), sK, dq_dst(i + 1), q0 + BR, mg.Lq, w, lane, rs, add);
-          else
-            gemm4<C>(sST(i + 1), sK, dq_dst(i + 1), q0 + BR, mg.Lq, w, lane, rs, add);
-          // single buffer: every wave is done reading it before this tile's dS overwrites it
-          // (the atomics / stores keep draining)
-          if constexpr (C::NSST == 1) lds_barrier();
-        }
-        // relay: once the key tile before this one has added into q tile i's sum, stage that sum
-        // (this wave's parts of it) for GEMM4 of tile i in the next iteration
-        if constexpr (C::MODE == DQ_RELAY) relay_stage(i);
-      }
-
-      // ---- the wave's 32 keys: GEMM1, GEMM2, softmax replay, dS, GEMM3, GEMM5 --------------------
-      const bool edge = tile_needs_mask(mg, q0, BR, k0, BC);
-      acc_t S = acc_t{}, dP = acc_t{};
-      // GEMM1 and GEMM2 are independent chains: alternate them so neither waits on the other's
-      // accumulator, and keep the operand reads a few MFMAs ahead of their use
+    if constexpr (C::PP) {
+      // ---- staggered wave groups ----------------------------------------------------------------
+      // Waves w and w + 4 share a SIMD.  Between two barriers, group A (waves 0-3) runs q tile i
+      // whole: GEMM1/GEMM2, the replay, GEMM3/GEMM5, then GEMM4 of tile i + 1; group B (waves 4-7)
+      // runs GEMM3/GEMM5 of tile i + 1 (its P / dS kept in registers across the barrier), then
+      // GEMM1/GEMM2 and the replay of tile i.  Each wave's replay then falls where the other wave
+      // of its SIMD issues MFMAs (A's after its GEMM1/GEMM2, B's beside A's GEMM3/GEMM5/GEMM4)
+      // instead of both replays leaving the matrix core idle at once.  Tiles i + 1, i and i - 1
+      // are live together (three q-tile buffers); group B issues the tile loads and is the only
+      // group that waits for them, so group A never waits on its atomics / stores.  GEMM4 of tile
+      // i + 1 reads a dS staging buffer whose both halves were complete at the last barrier.
+      const bool grpB = w >= C::NW / 2;  // wave-uniform
+      // q tile i by group B: fragments wb, wb + 4, ... of Q and of dO (the gather_frags layout),
+      // with the lane's row in the tile and its column offsets fixed for the whole loop (the four
+      // fragments of a wave share the fragment parity, hence the swizzled row)
+      constexpr int GB = C::NW / 2;
+      constexpr int NFQ = (C::N_KQ + GB - 1) / GB, NFO = (C::N_KV + GB - 1) / GB;
+      const int wb = w - GB;
+      const int ln = (lane & 48) | ((lane & 15) ^ (4 * kswz(lane >> 4, wb)));
+      const int row_l = ln & 31;
+      auto load_tile_b = [&](int i) {
+        char* t = tile(i);
+        const int row = min(i * BR + row_l, p.Sq - 1);
+        const uint32_t oq = (uint32_t)row * (uint32_t)p.sq.s, oo = (uint32_t)row * (uint32_t)p.sdo.s;
 #pragma unroll
-      for (int t = 0; t < (C::N_KQ > C::N_KV ? C::N_KQ : C::N_KV); ++t) {
-        if (t < C::N_KQ) {
-          const bf16x8 a = lds_read_b128(T + C::T_QA, t * 1024 + kofs[t & 1]);
-          if constexpr (C::KREG) {
-            S = M::mma(a, kreg[0][t], S);
-          } else {
-            S = M::mma(a, lds_read_b128(sK, (w * C::N_KQ + t) * 1024 + kofs[t & 1]), S);
+        for (int r = 0; r < NFQ; ++r) {
+          const int f = wb + GB * r;
+          const int col = 16 * f + 8 * (ln >> 5);  // one 32-row tile: fragment f is column block f
+          if (f < C::N_KQ)
+            dma16(rQ, (!C::PAD || col < dqk_act) ? (oq + col) * 2 : kOutOfRange, t + C::T_QA + f * 1024);
+        }
+#pragma unroll
+        for (int r = 0; r < NFO; ++r) {
+          const int f = wb + GB * r;
+          const int col = 16 * f + 8 * (ln >> 5);
+          if (f < C::N_KV)
+            dma16(rdO, (!C::PAD || col < dv_act) ? (oo + col) * 2 : kOutOfRange, t + C::T_OA + f * 1024);
+        }
+        if (wb == 0) dma4(rStat, (uint32_t)(i * BR * 2 + lane) * 4, t + C::T_ST);
+      };
+      auto store_ds_regs = [&](const uint32_t (&s)[8], int i_t) {  // as store_ds
+        char* wsb = reinterpret_cast<char*>(
+            p.ds_ws + (((int64_t)bh * p.n_kv_tiles + j) * n_q_tiles + i_t) * (BC * BR));
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          __builtin_nontemporal_store(u32x4{s[4 * h], s[4 * h + 1], s[4 * h + 2], s[4 * h + 3]},
+                                      reinterpret_cast<u32x4*>(wsb + w * 2048 + h * 1024 + lane * 16));
+      };
+      // GEMM1 / GEMM2 and the replay of q tile i for the wave's 32 keys: P / dS packed into pb /
+      // sb, invisible pairs cleared on edge tiles, dS staged in LDS for GEMM4
+      auto m1s = [&](int i, uint32_t (&pb)[8], uint32_t (&sb)[8]) __attribute__((always_inline)) {
+        const int q0 = i * BR;
+        const char* T = tile(i);
+        const float* sStat = reinterpret_cast<const float*>(T + C::T_ST);
+        acc_t S = acc_t{}, dP = acc_t{};
+#pragma unroll
+        for (int t = 0; t < (C::N_KQ > C::N_KV ? C::N_KQ : C::N_KV); ++t) {
+          if (t < C::N_KQ)
+            S = M::mma(lds_read_b128(T + C::T_QA, t * 1024 + kofs[t & 1]),
+                       lds_read_b128(sK, (w * C::N_KQ + t) * 1024 + kofs[t & 1]), S);
+          if (t < C::N_KV)
+            dP = M::mma(lds_read_b128(T + C::T_OA, t * 1024 + kofs[t & 1]), vreg[0][t], dP);
+        }
+        schedule_reads_ahead<2 * C::N_KQ + C::N_KV, C::N_KQ + C::N_KV, C::AHEAD>();
+        softmax_ds<C::F16, 0>(S, dP, sStat, g, p.scale_log2, pb, sb);
+        softmax_ds<C::F16, 2>(S, dP, sStat, g, p.scale_log2, pb, sb);
+        if (tile_needs_mask(mg, q0, BR, k0, BC)) {
+          const uint32_t vis_m = visible_rows(KeyRows(mg, q0 + g * 4, key_lane));
+          mask_pairs<0>(vis_m, pb, sb);
+          mask_pairs<2>(vis_m, pb, sb);
+        }
+        if constexpr (C::G4) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            *reinterpret_cast<u32x2*>(sST(i) + w * 2048 +
+                                      (C::G4_16 ? ds_store_off16(lane, x) : ds_store_off(lane, x))) =
+                u32x2{sb[2 * x], sb[2 * x + 1]};
+        }
+      };
+      // GEMM3 (dV^T += dO^T P) and GEMM5 (dK^T += Q^T dS) of q tile i
+      auto m2 = [&](int i, const uint32_t (&pb)[8], const uint32_t (&sb)[8]) __attribute__((always_inline)) {
+        const char* T = tile(i);
+        auto step = [&](auto tb_tag) __attribute__((always_inline)) {
+          constexpr int tb = decltype(tb_tag)::value;
+#pragma unroll
+          for (int dt = 0; dt < C::N_DVT; ++dt)
+            accV[dt][0] = M::mma(tra.read(T + C::T_OA, dt, tb),
+                                 __builtin_bit_cast(bf16x8, u32x4{pb[4 * tb], pb[4 * tb + 1],
+                                                                  pb[4 * tb + 2], pb[4 * tb + 3]}),
+                                 accV[dt][0]);
+#pragma unroll
+          for (int dt = 0; dt < C::N_DQT; ++dt)
+            accK[dt][0] = M::mma(tra.read(T + C::T_QA, dt, tb),
+                                 __builtin_bit_cast(bf16x8, u32x4{sb[4 * tb], sb[4 * tb + 1],
+                                                                  sb[4 * tb + 2], sb[4 * tb + 3]}),
+                                 accK[dt][0]);
+        };
+        __builtin_amdgcn_s_setprio(2);
+        step(IntTag<0>{});
+        step(IntTag<1>{});
+        schedule_reads_ahead<4 * (C::N_DVT + C::N_DQT), 2 * (C::N_DVT + C::N_DQT), C::AHEAD>();
+        __builtin_amdgcn_s_setprio(0);
+      };
+      auto g4 = [&](int i) __attribute__((always_inline)) {
+        if constexpr (C::G4_16)
+          gemm4_16<C>(sST(i), sK, dq_dst(i), i * BR, mg.Lq, w, lane);
+        else
+          gemm4<C>(sST(i), sK, dq_dst(i), i * BR, mg.Lq, w, lane);
+      };
+
+      wait_vmem();  // tile i_hi, K and V
+      lds_barrier();
+      // one loop per group (each keeps only its own values live); both pass the same barriers
+      if (grpB) {
+        uint32_t pb[8], sb[8];  // P / dS of the tile whose GEMM3/GEMM5 comes next
+        for (int i = i_hi; i >= i_lo; --i) {
+          if (i > i_lo) load_tile_b(i - 1);  // into tile i + 2's buffer (done with at the barrier)
+          if (i < i_hi) {
+            if constexpr (C::DS_OUT) store_ds_regs(sb, i + 1);
+            if constexpr (C::G4_B) g4(i + 1);
+            m2(i + 1, pb, sb);
+          }
+          m1s(i, pb, sb);
+          wait_vmem();    // tile i - 1 (and this group's dS stores / GEMM4 emission)
+          lds_barrier();  // tile i - 1 landed; dS of tile i complete in LDS
+        }
+        if constexpr (C::DS_OUT) store_ds_regs(sb, i_lo);
+        m2(i_lo, pb, sb);
+        if constexpr (C::G4_B) g4(i_lo);
+      } else {
+        for (int i = i_hi; i >= i_lo; --i) {
+          uint32_t pb[8], sb[8];
+          m1s(i, pb, sb);
+          if constexpr (C::DS_OUT) store_ds_regs(sb, i);
+          m2(i, pb, sb);
+          if constexpr (C::G4) {
+            if (i < i_hi) g4(i + 1);
+          }
+          lds_barrier();
+        }
+        if constexpr (C::G4) g4(i_lo);
+      }
+    } else {
+      for (int i = i_hi; i >= i_lo; --i) {
+        const int q0 = i * BR;
+        const char* T = tile(i);
+        const float* sStat = reinterpret_cast<const float*>(T + C::T_ST);
+        wait_vmem();      // this wave's loads of tile i (and its older atomics / stores) are done
+        lds_barrier();    // tile i landed everywhere; every wave is done with the previous tile
+        if constexpr (C::MODE == DQ_RELAY) {
+          // every wave's sums of q tile i + 2 (stored in the previous iteration) are complete
+          if (tid == 0 && i + 2 <= i_hi) relay_publish(relay_turn(i + 2), relay_rank(i + 2) + 1);
+        }
+        if (C::NBUF == 2 && i > i_lo) load_tile(i - 1);
+        if constexpr (C::DS_OUT) {
+          if (i < i_hi) store_ds(i + 1);
+        }
+        if constexpr (C::BIAS) {
+          if (i < i_hi) store_dbias(i + 1);
+          if (i > i_lo) load_bias(i - 1, bnext);
+        }
+
+        if constexpr (C::G4) {
+          // GEMM4 of the previous q tile (dS in sST), deferred so its atomics / partial stores
+          // overlap this tile
+          if (i < i_hi) {
+            const bool add = C::MODE == DQ_RELAY && relay_rank(i + 1) > 0;
+            if constexpr (C::G4_16)
+              gemm4_16<C>(sST(i + 1), sK, dq_dst(i + 1), q0 + BR, mg.Lq, w, lane, rs, add);
+            else
+              gemm4<C>(sST(i + 1), sK, dq_dst(i + 1), q0 + BR, mg.Lq, w, lane, rs, add);
+            // single buffer: every wave is done reading it before this tile's dS overwrites it
+            // (the atomics / stores keep draining)
+            if constexpr (C::NSST == 1) lds_barrier();
+          }
+          // relay: once the key tile before this one has added into q tile i's sum, stage that sum
+          // (this wave's parts of it) for GEMM4 of tile i in the next iteration
+          if constexpr (C::MODE == DQ_RELAY) relay_stage(i);
+        }
+
+        // ---- the wave's 32 keys: GEMM1, GEMM2, softmax replay, dS, GEMM3, GEMM5 --------------------
+        const bool edge = tile_needs_mask(mg, q0, BR, k0, BC);
+        acc_t S = acc_t{}, dP = acc_t{};
+        // GEMM1 and GEMM2 are independent chains: alternate them so neither waits on the other's
+        // accumulator, and keep the operand reads a few MFMAs ahead of their use
+  #pragma unroll
+        for (int t = 0; t < (C::N_KQ > C::N_KV ? C::N_KQ : C::N_KV); ++t) {
+          if (t < C::N_KQ) {
+            const bf16x8 a = lds_read_b128(T + C::T_QA, t * 1024 + kofs[t & 1]);
+            if constexpr (C::KREG) {
+              S = M::mma(a, kreg[0][t], S);
+            } else {
+              S = M::mma(a, lds_read_b128(sK, (w * C::N_KQ + t) * 1024 + kofs[t & 1]), S);
+            }
+          }
+          if (t < C::N_KV)
+            dP = M::mma(lds_read_b128(T + C::T_OA, t * 1024 + kofs[t & 1]), vreg[0][t], dP);
+        }
+        schedule_reads_ahead<(C::KREG ? 1 : 2) * C::N_KQ + C::N_KV, C::N_KQ + C::N_KV, C::AHEAD>();
+
+        // GEMM3 (dV^T += dO^T P) and GEMM5 (dK^T += Q^T dS), contraction step tb over q rows
+        // 16 tb .. 16 tb + 15, whose P / dS come from accumulator groups 2 tb and 2 tb + 1
+        // (the step index is a type so the P / dS register indices are constants)
+        uint32_t pb[8], sb[8];
+        auto gemm35_step = [&](auto tb_tag) __attribute__((always_inline)) {
+          constexpr int tb = decltype(tb_tag)::value;
+  #pragma unroll
+          for (int dt = 0; dt < C::N_DVT; ++dt)
+            accV[dt][0] = M::mma(tra.read(T + C::T_OA, dt, tb),
+                                 __builtin_bit_cast(bf16x8, u32x4{pb[4 * tb], pb[4 * tb + 1],
+                                                                  pb[4 * tb + 2], pb[4 * tb + 3]}),
+                                 accV[dt][0]);
+  #pragma unroll
+          for (int dt = 0; dt < C::N_DQT; ++dt)
+            accK[dt][0] = M::mma(tra.read(T + C::T_QA, dt, tb),
+                                 __builtin_bit_cast(bf16x8, u32x4{sb[4 * tb], sb[4 * tb + 1],
+                                                                  sb[4 * tb + 2], sb[4 * tb + 3]}),
+                                 accK[dt][0]);
+        };
+        // Softmax replay of all 32 rows, unmasked and branch-free; edge tiles then clear their
+        // invisible pairs in the packed words (keeping the masking out of the block the MFMA
+        // accumulators flow through avoids register copies at the join).
+        float bl[NBV];
+        bias_log2(bcur, bl);
+        softmax_ds<C::F16, 0, C::BIAS, C::QAT>(S, dP, sStat, g, p.scale_log2, pb, sb, bl, dsf, pf);
+        softmax_ds<C::F16, 2, C::BIAS, C::QAT>(S, dP, sStat, g, p.scale_log2, pb, sb, bl, dsf, pf);
+        if (edge) {
+          const uint32_t vis_m = visible_rows(KeyRows(mg, q0 + g * 4, key_lane));
+          mask_pairs<0>(vis_m, pb, sb);
+          mask_pairs<2>(vis_m, pb, sb);
+          if constexpr (C::BIAS == 2) {
+            // register 4x + e holds row offset 8x + e from the lane's first row
+  #pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (!((vis_m >> (8 * (r / 4) + (r % 4))) & 1u)) dsf[r] = 0.f;
+          }
+          if constexpr (C::QAT) {
+  #pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (!((vis_m >> (8 * (r / 4) + (r % 4))) & 1u)) pf[r] = 0.f;
           }
         }
-        if (t < C::N_KV)
-          dP = M::mma(lds_read_b128(T + C::T_OA, t * 1024 + kofs[t & 1]), vreg[0][t], dP);
-      }
-      schedule_reads_ahead<(C::KREG ? 1 : 2) * C::N_KQ + C::N_KV, C::N_KQ + C::N_KV, C::AHEAD>();
-
-      // GEMM3 (dV^T += dO^T P) and GEMM5 (dK^T += Q^T dS), contraction step tb over q rows
-      // 16 tb .. 16 tb + 15, whose P / dS come from accumulator groups 2 tb and 2 tb + 1
-      // (the step index is a type so the P / dS register indices are constants)
-      uint32_t pb[8], sb[8];
-      auto gemm35_step = [&](auto tb_tag) __attribute__((always_inline)) {
-        constexpr int tb = decltype(tb_tag)::value;
-#pragma unroll
-        for (int dt = 0; dt < C::N_DVT; ++dt)
-          accV[dt][0] = M::mma(tra.read(T + C::T_OA, dt, tb),
-                               __builtin_bit_cast(bf16x8, u32x4{pb[4 * tb], pb[4 * tb + 1],
-                                                                pb[4 * tb + 2], pb[4 * tb + 3]}),
-                               accV[dt][0]);
-#pragma unroll
-        for (int dt = 0; dt < C::N_DQT; ++dt)
-          accK[dt][0] = M::mma(tra.read(T + C::T_QA, dt, tb),
-                               __builtin_bit_cast(bf16x8, u32x4{sb[4 * tb], sb[4 * tb + 1],
-                                                                sb[4 * tb + 2], sb[4 * tb + 3]}),
-                               accK[dt][0]);
-      };
-      // Softmax replay of all 32 rows, unmasked and branch-free; edge tiles then clear their
-      // invisible pairs in the packed words (keeping the masking out of the block the MFMA
-      // accumulators flow through avoids register copies at the join).
-      float bl[NBV];
-      bias_log2(bcur, bl);
-      softmax_ds<C::F16, 0, C::BIAS, C::QAT>(S, dP, sStat, g, p.scale_log2, pb, sb, bl, dsf, pf);
-      softmax_ds<C::F16, 2, C::BIAS, C::QAT>(S, dP, sStat, g, p.scale_log2, pb, sb, bl, dsf, pf);
-      if (edge) {
-        const uint32_t vis_m = visible_rows(KeyRows(mg, q0 + g * 4, key_lane));
-        mask_pairs<0>(vis_m, pb, sb);
-        mask_pairs<2>(vis_m, pb, sb);
-        if constexpr (C::BIAS == 2) {
-          // register 4x + e holds row offset 8x + e from the lane's first row
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (!((vis_m >> (8 * (r / 4) + (r % 4))) & 1u)) dsf[r] = 0.f;
+        // QAT: GEMM3's P operand is the fake-quantised masked P (groups of 16 keys of a row)
+        if constexpr (C::QAT) nvfp4_p_pack_lds(pf, pb, smem + C::OFF_QS + w * C::QS_WAVE, lane);
+        if constexpr (C::BIAS) {
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) bcur[r] = bnext[r];
         }
-        if constexpr (C::QAT) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (!((vis_m >> (8 * (r / 4) + (r % 4))) & 1u)) pf[r] = 0.f;
+        if constexpr (C::DS_OUT) {
+  #pragma unroll
+          for (int x = 0; x < 8; ++x) sb_prev[x] = sb[x];
+        } else {
+          // dS of the wave's 32 keys to LDS as 2 KiB of quads (see ds_store_off / ds_store_off16)
+  #pragma unroll
+          for (int x = 0; x < 4; ++x)
+            *reinterpret_cast<u32x2*>(sST(i) + w * 2048 +
+                                      (C::G4_16 ? ds_store_off16(lane, x) : ds_store_off(lane, x))) =
+                u32x2{sb[2 * x], sb[2 * x + 1]};
+        }
+        // (raised wave priority: this MFMA-only phase issues ahead of the other wave's softmax)
+        __builtin_amdgcn_s_setprio(2);
+        gemm35_step(IntTag<0>{});
+        gemm35_step(IntTag<1>{});
+        schedule_reads_ahead<4 * (C::N_DVT + C::N_DQT), 2 * (C::N_DVT + C::N_DQT), C::AHEAD>();
+        __builtin_amdgcn_s_setprio(0);
+        if constexpr (C::NBUF == 1) {
+          lds_barrier();  // every wave is done with the single q-tile buffer
+          if (i > i_lo) load_tile(i - 1);
         }
       }
-      // QAT: GEMM3's P operand is the fake-quantised masked P (groups of 16 keys of a row)
-      if constexpr (C::QAT) nvfp4_p_pack_lds(pf, pb, smem + C::OFF_QS + w * C::QS_WAVE, lane);
-      if constexpr (C::BIAS) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) bcur[r] = bnext[r];
+      if constexpr (C::DS_OUT) store_ds(i_lo);
+      store_dbias(i_lo);
+      if constexpr (C::G4) {
+        if constexpr (C::MODE == DQ_RELAY) wait_vmem();  // the staged sum of q tile i_lo
+        lds_barrier();  // the last tile's dS is complete
+        const bool add = C::MODE == DQ_RELAY && relay_rank(i_lo) > 0;
+        if constexpr (C::G4_16)
+          gemm4_16<C>(sST(i_lo), sK, dq_dst(i_lo), i_lo * BR, mg.Lq, w, lane, rs, add);
+        else
+          gemm4<C>(sST(i_lo), sK, dq_dst(i_lo), i_lo * BR, mg.Lq, w, lane, rs, add);
       }
-      if constexpr (C::DS_OUT) {
-#pragma unroll
-        for (int x = 0; x < 8; ++x) sb_prev[x] = sb[x];
-      } else {
-        // dS of the wave's 32 keys to LDS as 2 KiB of quads (see ds_store_off / ds_store_off16)
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-          *reinterpret_cast<u32x2*>(sST(i) + w * 2048 +
-                                    (C::G4_16 ? ds_store_off16(lane, x) : ds_store_off(lane, x))) =
-              u32x2{sb[2 * x], sb[2 * x + 1]};
+      if constexpr (C::MODE == DQ_RELAY) {
+        wait_vmem();  // this wave's sums of q tiles i_lo + 1 and i_lo are stored
+        lds_barrier();
+        if (tid == 0) {
+          if (i_lo + 1 <= i_hi) relay_publish(relay_turn(i_lo + 1), relay_rank(i_lo + 1) + 1);
+          relay_publish(relay_turn(i_lo), relay_rank(i_lo) + 1);
+        }
       }
-      // (raised wave priority: this MFMA-only phase issues ahead of the other wave's softmax)
-      __builtin_amdgcn_s_setprio(2);
-      gemm35_step(IntTag<0>{});
-      gemm35_step(IntTag<1>{});
-      schedule_reads_ahead<4 * (C::N_DVT + C::N_DQT), 2 * (C::N_DVT + C::N_DQT), C::AHEAD>();
-      __builtin_amdgcn_s_setprio(0);
-      if constexpr (C::NBUF == 1) {
-        lds_barrier();  // every wave is done with the single q-tile buffer
-        if (i > i_lo) load_tile(i - 1);
-      }
-    }
-    if constexpr (C::DS_OUT) store_ds(i_lo);
-    store_dbias(i_lo);
-    if constexpr (C::G4) {
-      if constexpr (C::MODE == DQ_RELAY) wait_vmem();  // the staged sum of q tile i_lo
-      lds_barrier();  // the last tile's dS is complete
-      const bool add = C::MODE == DQ_RELAY && relay_rank(i_lo) > 0;
-      if constexpr (C::G4_16)
-        gemm4_16<C>(sST(i_lo), sK, dq_dst(i_lo), i_lo * BR, mg.Lq, w, lane, rs, add);
-      else
-        gemm4<C>(sST(i_lo), sK, dq_dst(i_lo), i_lo * BR, mg.Lq, w, lane, rs, add);
-    }
-    if constexpr (C::MODE == DQ_RELAY) {
-      wait_vmem();  // this wave's sums of q tiles i_lo + 1 and i_lo are stored
-      lds_barrier();
-      if (tid == 0) {
-        if (i_lo + 1 <= i_hi) relay_publish(relay_turn(i_lo + 1), relay_rank(i_lo + 1) + 1);
-        relay_publish(relay_turn(i_lo), relay_rank(i_lo) + 1);
-      }
-    }
+    }  // staggered groups / one group
   }
   if constexpr (C::MODE == DQ_RELAY) {
     if (tid == 0)
