@@ -47,7 +47,7 @@
 //     next iteration so its atomics (or partial stores) drain while that iteration computes.
 //   * The preprocess kernel supplies LSE * log2(e) per row (+inf for rows without keys), so the
 //     replay is one FMA and one v_exp_f32 per element.
-//   * 8-wave kernels without a bias: the two waves of each SIMD (w and w + 4) run half a q tile
+//   * Head dim 32 (8 waves, no bias): the two waves of each SIMD (w and w + 4) run half a q tile
 //     apart (staggered groups, see the q-tile loop), so that their softmax replays do not coincide.
 #pragma once
 #include "common.h"
@@ -164,7 +164,10 @@ struct MainCfg {
   // Staggered wave groups (8 waves, no bias, no QAT, not the relay): waves 0-3 and 4-7, which
   // share the four SIMDs pairwise, run half a q tile apart, so that one wave's softmax replay
   // (VALU) overlaps the other wave's MFMAs (see the q-tile loop).  Needs a third q-tile buffer.
-  static constexpr bool PP = NW == 8 && MODE != DQ_RELAY && BIAS_ == 0 && !QAT_ &&
+  // Measured on MI355X against the single-group loop (same box, causal GQA S=4096): head dim 32
+  // main kernel 178 -> 160 us (dQ partials) and 181 -> 170 us (fp32 atomics); head dim 64 2-8 %
+  // slower, head dim 128 neutral (dQ partials) to 3 % slower (dS panels).  Head dim 32 only.
+  static constexpr bool PP = NW == 8 && DQK_ == 32 && MODE != DQ_RELAY && BIAS_ == 0 && !QAT_ &&
                              SK_BYTES + 3 * TILE_BYTES + 2 * SST_BYTES <= 160 * 1024;
   static constexpr int NBUF = PP ? 3 : NBUF2;
   // dS staging for GEMM4, double-buffered by q-tile parity where LDS allows: GEMM4 of the previous
