@@ -29,6 +29,9 @@ CASES = {
                               window_left=100, len_lo=100),
     "d256_noncausal_s200": V(W["mha_det_s8192_d256"], Hq=2, Hkv=2, Sq=200, Skv=200),
     "d64_s128": W["mha_s128_d64"],
+    # head dim 32 (staggered wave groups): GQA, causal window, padding lengths
+    "d32_gqa_window_lens_s290": V(W["mla_window_padded_s4096"], B=2, Hq=4, Hkv=2, Sq=290, Skv=290,
+                                  window_left=70, len_lo=130, Dqk=32, Dv=32),
 }
 
 
