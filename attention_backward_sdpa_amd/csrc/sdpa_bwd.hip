@@ -15,6 +15,7 @@
 
 #include "../../include/sdpa_bwd.h"
 #include "dq2k.h"
+#include "dq2k_split.h"
 #include "dq_reduce.h"
 #include "main_launch.h"
 #include "small_kernels.h"
@@ -301,6 +302,21 @@ hipError_t dispatch_dq2k(const Dq2kParams& dp, int bc, hipStream_t s) {
   return launch_dq2k<C>(dp, (int)grid, s);
 }
 
+// head dim 256: the head dim split over wave pairs (dq2k_split.h).  Measured against dq2k_kernel
+// (same box, two passes): non-causal S=8192 D=256 319-320 -> 309 us; on the MLA workload's head
+// dim 192 it was 1-2 % slower, which keeps dq2k_kernel there.
+template <int DQK, int BC, bool F16>
+hipError_t dispatch_dq2k_split(const Dq2kParams& dp, int bc, hipStream_t s) {
+  using C = Dq2kSplitCfg<DQK, BC, F16>;
+  if (BC != bc) return hipErrorInvalidValue;  // must read the dS blocks the main kernel wrote
+  const int64_t grid = (int64_t)((dp.n_q_tiles + C::QT - 1) / C::QT) * dp.B * dp.Hq;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  const hipError_t e = lds_limit_once<C>(dq2k_split_kernel<C>, C::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dq2k_split_kernel<C>, dim3((unsigned)grid), dim3(C::NT), C::LDS_BYTES, s, dp);
+  return hipGetLastError();
+}
+
 template <bool F16>
 hipError_t run_dq2k_t(int Dqk, const Dq2kParams& dp, int bc, hipStream_t s) {
   if (bc == 256) {
@@ -313,7 +329,7 @@ hipError_t run_dq2k_t(int Dqk, const Dq2kParams& dp, int bc, hipStream_t s) {
   if (Dqk == 64) return dispatch_dq2k<64, 128, F16>(dp, bc, s);
   if (Dqk == 128) return dispatch_dq2k<128, 128, F16>(dp, bc, s);
   if (Dqk == 192) return dispatch_dq2k<192, 128, F16>(dp, bc, s);
-  return dispatch_dq2k<256, 128, F16>(dp, bc, s);
+  return dispatch_dq2k_split<256, 128, F16>(dp, bc, s);
 }
 
 hipError_t run_dq2k(int Dqk, bool f16, const Dq2kParams& dp, int bc, hipStream_t s) {
