@@ -120,9 +120,10 @@ def copy_probe(torch, dev):
     torch.cuda.synchronize()
 
 
-def atomic_probe():
+def atomic_rate():
     """fp32 atomic adds per second through torch's index_add_ (one atomic per element, consecutive
-    lanes on consecutive addresses): the ceiling that bounds a dQ built from fp32 atomics."""
+    lanes on consecutive addresses): the ceiling that bounds a dQ built from fp32 atomics.
+    Returns (adds per launch, ms per launch)."""
     import torch
     dev = torch.device("cuda:0")
     n_out, n = 16 << 20, 64 << 20
@@ -137,9 +138,44 @@ def atomic_probe():
         out.index_add_(0, idx, src)
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 10
+    return n, e0.elapsed_time(e1) / 10
+
+
+def atomic_probe():
+    n, ms = atomic_rate()
     print(json.dumps({"probe": "fp32 atomic add", "adds": n, "ms": round(ms, 4),
                       "g_adds_per_s": round(n / ms / 1e6, 1)}), flush=True)
+
+
+def kernel_tiles(w, bias=False, qat=False):
+    """The main kernel's head dim and key tile for the workload (32-row q tiles): the next native
+    head dim, 256-key tiles (8 waves) up to head dim 192 without a bias, else 128-key tiles."""
+    kq = next(d for d in (32, 64, 128, 192, 256) if w.Dqk <= d and w.Dv <= (128 if d == 192 else d))
+    return kq, (128 if kq == 256 or bias or qat else 256), 32
+
+
+def dq_atomic_adds(w, lens, bias=False, qat=False):
+    """fp32 atomic adds one main-kernel launch makes on the atomic route: every (key tile, q tile)
+    pair the mask leaves visible adds a 32-row x kernel-head-dim dQ block, rows past the batch
+    entry's query length skipped (the q-tile range rule of the kernel's mask geometry)."""
+    kq, bc, br = kernel_tiles(w, bias, qat)
+    total = 0
+    for b in range(w.B):
+        Lq = w.Sq if lens is None else int(lens[b])
+        Lkv = w.Skv if lens is None else int(lens[b])
+        rows = 0
+        for k0 in range(0, Lkv, bc):
+            kmax = min(k0 + bc, Lkv) - 1
+            qlo = max(k0, 0) if w.causal else 0       # top-left causal: q >= k
+            qhi = Lq - 1
+            if w.window_left >= 0:
+                qhi = min(kmax + w.window_left, qhi)  # window: q <= k + W
+            if Lq <= 0 or qlo > qhi:
+                continue
+            for i in range(qlo // br, qhi // br + 1):
+                rows += min(br, Lq - i * br)
+        total += rows * w.Hq * kq
+    return total
 
 
 def _pmc_means(directory, counter):
@@ -426,6 +462,17 @@ def main():
                      "unit": "TFLOP/s", "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
+    if route == lib.DQ_ATOMIC:
+        # the rate at which the main kernel's fp32 dQ atomics retire, next to the rate of a kernel
+        # that does nothing but fp32 atomic adds (torch's index_add_), measured now
+        adds = dq_atomic_adds(w, lens, args.bias != "none", args.qat)
+        n, ms = atomic_rate()
+        achieved = adds / (main_ms * 1e-3)
+        probe = n / (ms * 1e-3)
+        out["dq_atomics"] = {"adds_per_launch": adds, "main_us": round(main_ms * 1e3, 1),
+                             "achieved_g_adds_per_s": round(achieved / 1e9, 1),
+                             "probe_g_adds_per_s": round(probe / 1e9, 1),
+                             "achieved_over_probe": round(achieved / probe, 3)}
     if args.copy_probe:
         copy_probe(torch, dev)
     if not args.no_cpu_baseline:
