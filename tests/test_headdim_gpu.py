@@ -34,6 +34,11 @@ CASES = {
     "d160_s150": V(W["mha_det_s8192_d256"], Hq=2, Hkv=2, Sq=150, Skv=150, Dqk=160, Dv=160),
     "d248_causal_s130": V(W["mha_det_s8192_d256"], Hq=2, Hkv=1, Sq=130, Skv=130, causal=True,
                           Dqk=248, Dv=248),
+    # native head dim 32 with each key tile's q range split into 4 parts (a grid of 16 workgroups:
+    # 4 key tiles x 4 query heads), GQA: the staggered loop on partial ranges, the reduction over
+    # (query head, part) slots
+    "d32_gqa_split_causal_s1024": V(W["gqa_causal_s4096_d128"], B=1, Hq=4, Hkv=1, Sq=1024,
+                                    Skv=1024, Dqk=32, Dv=32),
 }
 
 
