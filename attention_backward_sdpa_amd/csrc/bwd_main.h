@@ -150,7 +150,11 @@ struct MainCfg {
   static constexpr int T_QA = 0;
   static constexpr int T_OA = T_QA + N_KQ * FRAG;
   static constexpr int T_ST = T_OA + N_KV * FRAG;
-  static constexpr int TILE_BYTES = T_ST + 2 * BR * 4;
+  // 8 waves with a bias: the tile's BR x BC bias elements (io type) travel with the q tile into
+  // LDS (LDS-DMA, row-major); the 4-wave layout prefetches each lane's 16 elements into registers
+  static constexpr bool BIAS_LDS = BIAS_ > 0 && NW_ == 8;
+  static constexpr int T_BIAS = T_ST + 2 * BR * 4;
+  static constexpr int TILE_BYTES = T_BIAS + (BIAS_LDS ? BR * BC * 2 : 0);
   static constexpr int SK_BYTES = KLDS ? BC * DQK * 2 : 0;
   static constexpr int SST_BYTES = G4 ? BC * BR * 2 : 0;
   // relay: the running sum of the next q tile, staged one iteration ahead (each wave stages the
@@ -766,6 +770,13 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
   const rsrc_t rQ = buf_rsrc(Qb, ((int64_t)(p.Sq - 1) * p.sq.s + dqk_act) * 2);
   const rsrc_t rdO = buf_rsrc(dOb, ((int64_t)(p.Sq - 1) * p.sdo.s + dv_act) * 2);
   const rsrc_t rStat = buf_rsrc(statb, (int64_t)p.sq_pad * 2 * 4);
+  // the head's bias for the LDS-staged layout: io-type elements, the host keeps the span below
+  // 2^31 bytes and Skv a multiple of 8 (16-byte chunks within a row)
+  const rsrc_t rBias = buf_rsrc(
+      C::BIAS_LDS ? reinterpret_cast<const bf16_t*>(p.bias) + (int64_t)b * p.bias_bstride +
+                        (int64_t)h * p.Sq * p.Skv
+                  : nullptr,
+      C::BIAS_LDS ? (int64_t)p.Sq * p.Skv * 2 : 0);
 
   acc_t accK[C::N_DQT][NKT], accV[C::N_DVT][NKT];
 #pragma unroll
@@ -795,6 +806,17 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
                                     dv_act);
       if (w == 0)  // 64 floats: [lse2, delta] x 32 rows, already padded to sq_pad rows
         dma4(rStat, (uint32_t)(i * BR * 2 + lane) * 4, t + C::T_ST);
+      if constexpr (C::BIAS_LDS) {
+        // bias rows i * BR .. + BR - 1, keys k0 .. k0 + BC - 1: 16-byte chunk c = 64 m + lane
+        // holds row c / (BC / 8), keys 8 (c % (BC / 8)) .. + 7 (rows past Sq read zeros; keys past
+        // Skv read the next row's values, which the masking clears)
+#pragma unroll
+        for (int m = w; m < C::BR * C::BC * 2 / 1024; m += C::NW) {
+          const int c = m * 64 + lane, row = c / (BC / 8), col = (c % (BC / 8)) * 8;
+          dma16(rBias, ((uint32_t)(i * BR + row) * (uint32_t)p.Skv + (uint32_t)(k0 + col)) * 2u,
+                t + C::T_BIAS + m * 1024);
+        }
+      }
     };
     load_tile(i_hi);
     // ---- K fragments into LDS (B operand of GEMM1 and/or GEMM4) -------------------------------
@@ -852,14 +874,15 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
     // touched until that tile's replay, so the loads complete under the previous tile's work.
     // dBias: the previous tile's masked fp32 dS, stored (or, for a batch-1 bias summed over the
     // batch, added with fp32 atomics) after the next tile's loads are issued.
-    constexpr int NBV = C::BIAS ? 16 : 1;
+    constexpr int NBV = C::BIAS && !C::BIAS_LDS ? 16 : 1;  // register-prefetched bias words
+    constexpr int NBL = C::BIAS ? 16 : 1;                     // the replay's bias * log2(e)
     uint32_t bcur[NBV], bnext[NBV];
     float dsf[C::BIAS == 2 ? 16 : 1];
     float pf[C::QAT ? 16 : 1];
     const int64_t bias_bh = (int64_t)b * p.bias_bstride + (int64_t)h * p.Sq * p.Skv;
     const int bias_key = min(key_lane, p.Skv - 1);
     auto load_bias = [&](int i_t, uint32_t (&dst)[NBV]) {
-      if constexpr (C::BIAS) {
+      if constexpr (C::BIAS && !C::BIAS_LDS) {
         int64_t x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -873,9 +896,16 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
         }
       }
     };
-    // the bias of the raw words, times log2(e), for the replay's exponent
-    auto bias_log2 = [&](const uint32_t (&raw)[NBV], float (&dst)[NBV]) {
-      if constexpr (C::BIAS) {
+    // the bias of the raw words (or of the LDS-staged tile T), times log2(e), for the replay's
+    // exponent
+    auto bias_log2 = [&](const uint32_t (&raw)[NBV], const char* T, float (&dst)[NBL]) {
+      if constexpr (C::BIAS_LDS) {
+        const char* row0 = T + C::T_BIAS + (w * KPW + lc) * 2;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          dst[r] = Elem<C::F16>::lo(*reinterpret_cast<const uint16_t*>(row0 + acc_row<32>(r, g) * (BC * 2))) *
+                   kLog2e;
+      } else if constexpr (C::BIAS) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           dst[r] = (p.bias_f32 ? __uint_as_float(raw[r]) : Elem<C::F16>::lo(raw[r])) * kLog2e;
@@ -1092,7 +1122,7 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
         if constexpr (C::DS_OUT) {
           if (i < i_hi) store_ds(i + 1);
         }
-        if constexpr (C::BIAS) {
+        if constexpr (C::BIAS && !C::BIAS_LDS) {
           if (i < i_hi) store_dbias(i + 1);
           if (i > i_lo) load_bias(i - 1, bnext);
         }
@@ -1120,7 +1150,7 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
         acc_t S = acc_t{}, dP = acc_t{};
         // GEMM1 and GEMM2 are independent chains: alternate them so neither waits on the other's
         // accumulator, and keep the operand reads a few MFMAs ahead of their use
-  #pragma unroll
+#pragma unroll
         for (int t = 0; t < (C::N_KQ > C::N_KV ? C::N_KQ : C::N_KV); ++t) {
           if (t < C::N_KQ) {
             const bf16x8 a = lds_read_b128(T + C::T_QA, t * 1024 + kofs[t & 1]);
@@ -1141,13 +1171,13 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
         uint32_t pb[8], sb[8];
         auto gemm35_step = [&](auto tb_tag) __attribute__((always_inline)) {
           constexpr int tb = decltype(tb_tag)::value;
-  #pragma unroll
+#pragma unroll
           for (int dt = 0; dt < C::N_DVT; ++dt)
             accV[dt][0] = M::mma(tra.read(T + C::T_OA, dt, tb),
                                  __builtin_bit_cast(bf16x8, u32x4{pb[4 * tb], pb[4 * tb + 1],
                                                                   pb[4 * tb + 2], pb[4 * tb + 3]}),
                                  accV[dt][0]);
-  #pragma unroll
+#pragma unroll
           for (int dt = 0; dt < C::N_DQT; ++dt)
             accK[dt][0] = M::mma(tra.read(T + C::T_QA, dt, tb),
                                  __builtin_bit_cast(bf16x8, u32x4{sb[4 * tb], sb[4 * tb + 1],
@@ -1157,8 +1187,8 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
         // Softmax replay of all 32 rows, unmasked and branch-free; edge tiles then clear their
         // invisible pairs in the packed words (keeping the masking out of the block the MFMA
         // accumulators flow through avoids register copies at the join).
-        float bl[NBV];
-        bias_log2(bcur, bl);
+        float bl[NBL];
+        bias_log2(bcur, T, bl);
         softmax_ds<C::F16, 0, C::BIAS, C::QAT>(S, dP, sStat, g, p.scale_log2, pb, sb, bl, dsf, pf);
         softmax_ds<C::F16, 2, C::BIAS, C::QAT>(S, dP, sStat, g, p.scale_log2, pb, sb, bl, dsf, pf);
         if (edge) {
@@ -1167,28 +1197,31 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
           mask_pairs<2>(vis_m, pb, sb);
           if constexpr (C::BIAS == 2) {
             // register 4x + e holds row offset 8x + e from the lane's first row
-  #pragma unroll
+#pragma unroll
             for (int r = 0; r < 16; ++r)
               if (!((vis_m >> (8 * (r / 4) + (r % 4))) & 1u)) dsf[r] = 0.f;
           }
           if constexpr (C::QAT) {
-  #pragma unroll
+#pragma unroll
             for (int r = 0; r < 16; ++r)
               if (!((vis_m >> (8 * (r / 4) + (r % 4))) & 1u)) pf[r] = 0.f;
           }
         }
+        // 8 waves: dBias of this tile leaves at once (the 4-wave layout defers it past the next
+        // tile's loads; here the registers to hold it are not there)
+        if constexpr (C::BIAS == 2 && C::BIAS_LDS) store_dbias(i);
         // QAT: GEMM3's P operand is the fake-quantised masked P (groups of 16 keys of a row)
         if constexpr (C::QAT) nvfp4_p_pack_lds(pf, pb, smem + C::OFF_QS + w * C::QS_WAVE, lane);
         if constexpr (C::BIAS) {
-  #pragma unroll
-          for (int r = 0; r < 16; ++r) bcur[r] = bnext[r];
+#pragma unroll
+          for (int r = 0; r < NBV; ++r) bcur[r] = bnext[r];
         }
         if constexpr (C::DS_OUT) {
-  #pragma unroll
+#pragma unroll
           for (int x = 0; x < 8; ++x) sb_prev[x] = sb[x];
         } else {
           // dS of the wave's 32 keys to LDS as 2 KiB of quads (see ds_store_off / ds_store_off16)
-  #pragma unroll
+#pragma unroll
           for (int x = 0; x < 4; ++x)
             *reinterpret_cast<u32x2*>(sST(i) + w * 2048 +
                                       (C::G4_16 ? ds_store_off16(lane, x) : ds_store_off(lane, x))) =
@@ -1206,7 +1239,7 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
         }
       }
       if constexpr (C::DS_OUT) store_ds(i_lo);
-      store_dbias(i_lo);
+      if constexpr (!C::BIAS_LDS) store_dbias(i_lo);
       if constexpr (C::G4) {
         if constexpr (C::MODE == DQ_RELAY) wait_vmem();  // the staged sum of q tile i_lo
         lds_barrier();  // the last tile's dS is complete

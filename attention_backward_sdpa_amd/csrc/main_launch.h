@@ -10,8 +10,9 @@
 namespace sdpa {
 
 // Tile geometry of the main kernel for a kernel head dim: 8 waves (256 registers each, 256-key
-// tiles) for DQK <= 192 without a bias; 4 waves (512 registers, 128-key tiles) for DQK = 256 and
-// for every head dim with a bias, whose next-tile values are held in registers.
+// tiles) for DQK <= 192 without a bias, and for DQK <= 128 with an io-type bias staged in LDS;
+// 4 waves (512 registers, 128-key tiles) for DQK = 256 and for the other biases, whose next-tile
+// values are held in registers.
 template <int DQK>
 struct MainShape {
   static constexpr int DV = DQK == 192 ? 128 : DQK;
@@ -51,7 +52,7 @@ hipError_t lds_limit_once(F* kernel, int bytes) {
 template <class C>
 struct IlpSched {
   static constexpr bool value =
-      C::KPW == 32 && C::DQK == C::DV &&
+      C::KPW == 32 && C::DQK == C::DV && !C::BIAS_LDS &&
       ((C::DQK == 256 && C::NW == 4 && C::BIAS == 0 && !C::QAT) ||
        (C::DQK == 128 && !(C::NW == 8 && C::MODE == DQ_PARTIAL)));
 };
@@ -77,8 +78,14 @@ hipError_t launch_main_mode(const MainParams& mp, DqMode mode, int grid, hipStre
     return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_DS, F16, BIAS, PAD, QAT>>(mp, grid, s);
   if (mode == DQ_PARTIAL)
     return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_PARTIAL, F16, BIAS, PAD, QAT>>(mp, grid, s);
-  if (mode == DQ_RELAY)
-    return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_RELAY, F16, BIAS, PAD, QAT>>(mp, grid, s);
+  if (mode == DQ_RELAY) {
+    // the relay keeps a bias on the 4-wave layout (its 8-wave bias kernel does not fit in 256
+    // registers); the host never asks for it
+    if constexpr (BIAS > 0 && NW == 8)
+      return hipErrorInvalidValue;
+    else
+      return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_RELAY, F16, BIAS, PAD, QAT>>(mp, grid, s);
+  }
   return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_ATOMIC, F16, BIAS, PAD, QAT>>(mp, grid, s);
 }
 
@@ -110,8 +117,17 @@ hipError_t launch_main_dqk(const MainParams& mp, DqMode mode, bool f16, int bias
       return hipErrorInvalidValue;
     }
   }
-  if (bias == 1) return launch_main_nw<DQK, NW1, 1>(mp, mode, f16, grid, bc, s);
-  if (bias == 2) return launch_main_nw<DQK, NW1, 2>(mp, mode, f16, grid, bc, s);
+  if (bias) {
+    // an io-type bias at head dims up to 128 may run the 8-wave layout with the bias tile staged
+    // in LDS (the host chose it through the key tile); otherwise the 4-wave layout
+    if constexpr (DQK <= 128 && NW0 == 8) {
+      if (bc == MainCfg<DQK, MainShape<DQK>::DV, 32, NW0, DQ_ATOMIC>::BC)
+        return bias == 1 ? launch_main_nw<DQK, NW0, 1>(mp, mode, f16, grid, bc, s)
+                         : launch_main_nw<DQK, NW0, 2>(mp, mode, f16, grid, bc, s);
+    }
+    return bias == 1 ? launch_main_nw<DQK, NW1, 1>(mp, mode, f16, grid, bc, s)
+                     : launch_main_nw<DQK, NW1, 2>(mp, mode, f16, grid, bc, s);
+  }
   return launch_main_nw<DQK, NW0, 0>(mp, mode, f16, grid, bc, s);
 }
 

@@ -122,6 +122,28 @@ Route route_for(int deterministic, int Dqk, const Geometry& g, int B, int Hq, in
   }
 }
 
+// A bias of the io type whose rows split into 16-byte chunks runs the 8-wave layout (256-key
+// tiles, the bias tile staged in LDS with its q tile) at kernel head dims up to 128; any other bias,
+// and every bias on the relay route (whose 8-wave bias kernel does not fit in 256 registers), the
+// 4-wave layout.  The chunks need Skv a multiple of 8 and a 16-byte-aligned tensor, and one head's
+// bias is addressed through 32-bit buffer offsets.
+bool bias_in_lds(const void* bias, int bias_dtype, int io_dtype, int kq, int Sq, int Skv) {
+  return bias != nullptr && bias_dtype == io_dtype && Skv % 8 == 0 &&
+         ((uintptr_t)bias & 15) == 0 && (int64_t)Sq * Skv * 2 < (int64_t{1} << 31) && kq <= 128;
+}
+
+// The main kernel's geometry and the dQ route of a call with kernel head dims (kq, kv).
+bool plan(int kq, int kv, int deterministic, int B, int Hq, int Sq, int Skv, bool bias,
+          bool bias_lds, Geometry* geo, Route* route) {
+  if (!geometry_for(kq, kv, geo, bias && !bias_lds)) return false;
+  *route = route_for(deterministic, kq, *geo, B, Hq, Sq, Skv);
+  if (bias && bias_lds && *route == R_RELAY) {
+    geometry_for(kq, kv, geo, true);
+    *route = route_for(deterministic, kq, *geo, B, Hq, Sq, Skv);
+  }
+  return true;
+}
+
 // Item queues of the relay: one per XCD of the current device (1..8), queried once per device.
 int relay_queues() {
   static std::atomic<int> cached[64];  // 0 until queried
@@ -436,8 +458,17 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
       L.t[x] = Strides{layouts[x].batch, layouts[x].head, layouts[x].seq};
   st = check_layouts(L, Sq, Skv, Dqk, Dv);
   if (st != SDPA_BWD_OK) return st;
-  const Route route = route_for(deterministic, KDqk, geo, B, Hq, Sq, Skv);
+  Route route = R_INVALID;
+  if (!qat)
+    plan(KDqk, KDv, deterministic, B, Hq, Sq, Skv, has_bias,
+         bias_in_lds(ba.bias, ba.dtype, dtype, KDqk, Sq, Skv), &geo, &route);
+  else
+    route = route_for(deterministic, KDqk, geo, B, Hq, Sq, Skv);
   if (route == R_INVALID) return SDPA_BWD_INVALID_ARG;
+  // the chosen key tile may be larger than validate() assumed: one head's rows (and its padded
+  // tiles) stay addressable through 32-bit buffer offsets
+  if (((int64_t)(Sq > Skv ? Sq : Skv) + geo.bc) * (KDqk > KDv ? KDqk : KDv) * 2 >= ((int64_t)1 << 31))
+    return SDPA_BWD_UNSUPPORTED;
   // dBias of a batch-1 bias sums over the batch with fp32 atomics: not reproducible ("Support
   // surface", bias), so the deterministic routes need a per-batch bias then
   const bool dbias_atomic = ba.dbias && ba.batch == 1 && B > 1;
@@ -928,10 +959,12 @@ size_t sdpa_bwd_run_workspace_size(const sdpa_bwd_args* a) {
   if (a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Sq < 0 || a->Skv < 0 || a->Hq % a->Hkv != 0)
     return 0;
   int kq, kv;
-  if (!kernel_dims(a->Dqk, a->Dv, &kq, &kv) || !geometry_for(kq, kv, &geo, a->bias != nullptr))
+  Route route = R_INVALID;
+  if (!kernel_dims(a->Dqk, a->Dv, &kq, &kv) ||
+      !plan(kq, kv, a->deterministic, a->B, a->Hq, a->Sq, a->Skv, a->bias != nullptr,
+            bias_in_lds(a->bias, a->bias_dtype, a->dtype, kq, a->Sq, a->Skv), &geo, &route))
     return 0;
   if (a->B == 0 || a->Sq == 0 || a->Skv == 0) return 0;
-  const Route route = route_for(a->deterministic, kq, geo, a->B, a->Hq, a->Sq, a->Skv);
   if (route == R_INVALID) return 0;
   const int64_t dbias_elems =
       a->dbias && a->bias && a->dbias_io ? (int64_t)a->bias_batch * a->Hq * a->Sq * a->Skv : 0;
@@ -944,9 +977,12 @@ int sdpa_bwd_run_dq_route(const sdpa_bwd_args* a) {
   if (a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Sq < 0 || a->Skv < 0 || a->Hq % a->Hkv != 0)
     return -1;
   int kq, kv;
-  if (!kernel_dims(a->Dqk, a->Dv, &kq, &kv) || !geometry_for(kq, kv, &geo, a->bias != nullptr))
+  Route route = R_INVALID;
+  if (!kernel_dims(a->Dqk, a->Dv, &kq, &kv) ||
+      !plan(kq, kv, a->deterministic, a->B, a->Hq, a->Sq, a->Skv, a->bias != nullptr,
+            bias_in_lds(a->bias, a->bias_dtype, a->dtype, kq, a->Sq, a->Skv), &geo, &route))
     return -1;
-  return route_code(route_for(a->deterministic, kq, geo, a->B, a->Hq, a->Sq, a->Skv));
+  return route_code(route);
 }
 
 int sdpa_bwd_preprocess(const void* o, const void* dO, const float* lse, float* stats,

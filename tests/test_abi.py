@@ -366,3 +366,24 @@ def test_nvfp4_qat_workspace_and_rejections(so):
     assert call(det=5) == lib.INVALID_ARG
     assert call() == lib.INVALID_ARG                                  # no workspace
     assert call(ws=p, ws_bytes=16) == lib.WORKSPACE_TOO_SMALL
+
+
+def test_bias_layout_choice(so):
+    # An io-type bias whose rows split into 16-byte chunks (Skv a multiple of 8, a 16-byte-aligned
+    # tensor) runs the 8-wave layout with 256-key tiles, any other bias the 4-wave layout with
+    # 128-key tiles. The dQ-partial route's workspace shows the key tile: one 32 x Dqk fp32 block
+    # per (head, key tile, q tile).
+    def size(Skv, bias, bias_dtype=lib.BF16, det=3):
+        a = lib.Args()
+        a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.Dqk, a.Dv = 1, 2, 2, 512, Skv, 128, 128
+        a.window_left, a.deterministic, a.dtype = -1, det, lib.BF16
+        a.bias, a.bias_batch, a.bias_dtype = bias, 1, bias_dtype
+        return so.sdpa_bwd_run_workspace_size(ctypes.byref(a))
+
+    blocks = lambda n_kv: 2 * n_kv * 512 * 128 * 4  # heads x key tiles x q rows x Dqk x fp32
+    assert size(512, 0) == size(512, 8192)                        # 8 waves, as without a bias
+    assert size(512, 8194) == size(512, 8192) + blocks(4) - blocks(2)    # misaligned: 4 waves
+    assert size(512, 8192, lib.FP32) == size(512, 8194)            # fp32 bias: 4 waves
+    assert size(516, 8192) == size(516, 8194)                      # Skv % 8 != 0: 4 waves
+    # the relay keeps the 4-wave layout; its workspace does not depend on the key tile
+    assert size(512, 8192, det=4) == size(512, 8194, det=4)

@@ -32,6 +32,13 @@ CASES = {
     "mha_d64_s200x330": (V(W["mha_s128_d64"], B=1, Hq=2, Hkv=2, Sq=200, Skv=330), "B"),
     # non-causal D = 256
     "det_d256_s200": (V(W["mha_det_s8192_d256"], Hq=2, Hkv=2, Sq=200, Skv=200), "B"),
+    # S_kv a multiple of 8 with an io-type bias: the 8-wave layout, the bias tile staged in LDS
+    # (the relay route keeps the 4-wave layout)
+    "gqa_causal_d128_s320": (V(W["gqa_causal_s4096_d128"], B=2, Hq=4, Hkv=2, Sq=320, Skv=320), "B"),
+    "gqa_causal_d128_s320_b1": (V(W["gqa_causal_s4096_d128"], B=2, Hq=4, Hkv=2, Sq=320, Skv=320), 1),
+    "window_padded_d128_s296": (V(W["mla_window_padded_s4096"], B=2, Hq=2, Hkv=2, Sq=296, Skv=296,
+                                  window_left=90, len_lo=100, Dqk=128, Dv=128), "B"),
+    "mha_d64_s200x328": (V(W["mha_s128_d64"], B=1, Hq=2, Hkv=2, Sq=200, Skv=328), "B"),
 }
 
 
@@ -139,7 +146,7 @@ def test_bias_deterministic_bitwise(det):
 
 @pytest.mark.parametrize("det", [0, 2, 3], ids=["atomic", "dspanels", "dqpartials"])
 @pytest.mark.parametrize("name", ["gqa_causal_d128_s333", "gqa_causal_d128_s333_b1", "mla_window_padded_s300",
-                                  "mha_d64_s200x330"])
+                                  "mha_d64_s200x330", "gqa_causal_d128_s320", "gqa_causal_d128_s320_b1"])
 def test_io_dtype_dbias(name, det):
     # "The kernel chain" dbias_cvt: a bf16 dBias output is the fp32 dBias rounded once; within the
     # parity tolerance of the oracle, masked pairs exactly 0, and the other gradients unchanged
