@@ -113,11 +113,11 @@ struct MainCfg {
   static constexpr bool PAD = PAD_;
   // NVFP4 attention QAT ("NVFP4 Attention QAT Backward", "Overview"): the inputs are already
   // fake-quantised; GEMM3 takes the fake-quantised P (dV = fake(P)^T dO) while dS, and so dQ and
-  // dK, use the unquantised P.  MHA, head dim 128, bf16, the 4-wave layout (the fp32 P is kept
-  // for the quantisation).
+  // dK, use the unquantised P.  MHA, head dim 128, bf16; the fp32 P goes through a wave-private
+  // LDS area for the group scales (8 waves, or 4 on the relay route).
   static constexpr bool QAT = QAT_;
-  static_assert(!QAT_ || (DQK_ == 128 && DV_ == 128 && !F16_ && BIAS_ == 0 && NW_ == 4),
-                "the QAT variant is bf16, head dim 128, no bias, 4 waves");
+  static_assert(!QAT_ || (DQK_ == 128 && DV_ == 128 && !F16_ && BIAS_ == 0),
+                "the QAT variant is bf16, head dim 128, no bias");
   // 0: no bias; 1: additive bias in the replayed scores; 2: bias and its gradient dBias = dS
   static constexpr int BIAS = BIAS_;
   static constexpr bool DS_OUT = MODE == DQ_DS;  // dS leaves the kernel, GEMM4 does not run here

@@ -52,7 +52,7 @@ hipError_t lds_limit_once(F* kernel, int bytes) {
 template <class C>
 struct IlpSched {
   static constexpr bool value =
-      C::KPW == 32 && C::DQK == C::DV && !C::BIAS_LDS &&
+      C::KPW == 32 && C::DQK == C::DV && !C::BIAS_LDS && !(C::QAT && C::NW == 8) &&
       ((C::DQK == 256 && C::NW == 4 && C::BIAS == 0 && !C::QAT) ||
        (C::DQK == 128 && !(C::NW == 8 && C::MODE == DQ_PARTIAL)));
 };
@@ -79,9 +79,9 @@ hipError_t launch_main_mode(const MainParams& mp, DqMode mode, int grid, hipStre
   if (mode == DQ_PARTIAL)
     return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_PARTIAL, F16, BIAS, PAD, QAT>>(mp, grid, s);
   if (mode == DQ_RELAY) {
-    // the relay keeps a bias on the 4-wave layout (its 8-wave bias kernel does not fit in 256
-    // registers); the host never asks for it
-    if constexpr (BIAS > 0 && NW == 8)
+    // the relay keeps a bias and the QAT variant on the 4-wave layout (their 8-wave kernels do
+    // not fit in 256 registers); the host never asks for them
+    if constexpr ((BIAS > 0 || QAT) && NW == 8)
       return hipErrorInvalidValue;
     else
       return launch_main_cfg<MainCfg<DQK, DV, KPW, NW, DQ_RELAY, F16, BIAS, PAD, QAT>>(mp, grid, s);
@@ -107,11 +107,12 @@ template <int DQK>
 hipError_t launch_main_dqk(const MainParams& mp, DqMode mode, bool f16, int bias, int grid, int bc,
                            hipStream_t s, bool qat) {
   constexpr int NW0 = MainShape<DQK>::nw(false), NW1 = MainShape<DQK>::nw(true);
-  if (qat) {  // NVFP4 QAT: head dim 128, bf16, no bias, the 4-wave layout, exact head dims
+  if (qat) {  // NVFP4 QAT: head dim 128, bf16, no bias, exact head dims; 8 waves but on the relay
     if constexpr (DQK == 128) {
-      if (f16 || bias || mp.dqk_act != 128 || mp.dv_act != 128 ||
-          MainCfg<128, 128, 32, NW1, DQ_ATOMIC>::BC != bc)
-        return hipErrorInvalidValue;
+      if (f16 || bias || mp.dqk_act != 128 || mp.dv_act != 128) return hipErrorInvalidValue;
+      if (MainCfg<128, 128, 32, NW0, DQ_ATOMIC>::BC == bc)
+        return launch_main_mode<128, 128, 32, NW0, false, 0, false, true>(mp, mode, grid, s);
+      if (MainCfg<128, 128, 32, NW1, DQ_ATOMIC>::BC != bc) return hipErrorInvalidValue;
       return launch_main_mode<128, 128, 32, NW1, false, 0, false, true>(mp, mode, grid, s);
     } else {
       return hipErrorInvalidValue;

@@ -132,16 +132,26 @@ bool bias_in_lds(const void* bias, int bias_dtype, int io_dtype, int kq, int Sq,
          ((uintptr_t)bias & 15) == 0 && (int64_t)Sq * Skv * 2 < (int64_t{1} << 31) && kq <= 128;
 }
 
+// Layout classes of a call: no per-element extra; an extra that rides on the 8-wave layout except
+// on the relay route (a bias staged in LDS, the NVFP4 QAT variant: their 8-wave relay kernels do
+// not fit in 256 registers); an extra that needs the 4-wave layout (any other bias).
+enum Extra { X_NONE = 0, X_WIDE = 1, X_NARROW = 2 };
+
 // The main kernel's geometry and the dQ route of a call with kernel head dims (kq, kv).
-bool plan(int kq, int kv, int deterministic, int B, int Hq, int Sq, int Skv, bool bias,
-          bool bias_lds, Geometry* geo, Route* route) {
-  if (!geometry_for(kq, kv, geo, bias && !bias_lds)) return false;
+bool plan(int kq, int kv, int deterministic, int B, int Hq, int Sq, int Skv, Extra x,
+          Geometry* geo, Route* route) {
+  if (!geometry_for(kq, kv, geo, x == X_NARROW)) return false;
   *route = route_for(deterministic, kq, *geo, B, Hq, Sq, Skv);
-  if (bias && bias_lds && *route == R_RELAY) {
+  if (x == X_WIDE && *route == R_RELAY) {
     geometry_for(kq, kv, geo, true);
     *route = route_for(deterministic, kq, *geo, B, Hq, Sq, Skv);
   }
   return true;
+}
+
+Extra bias_extra(const void* bias, int bias_dtype, int io_dtype, int kq, int Sq, int Skv) {
+  if (bias == nullptr) return X_NONE;
+  return bias_in_lds(bias, bias_dtype, io_dtype, kq, Sq, Skv) ? X_WIDE : X_NARROW;
 }
 
 // Item queues of the relay: one per XCD of the current device (1..8), queried once per device.
@@ -459,11 +469,8 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   st = check_layouts(L, Sq, Skv, Dqk, Dv);
   if (st != SDPA_BWD_OK) return st;
   Route route = R_INVALID;
-  if (!qat)
-    plan(KDqk, KDv, deterministic, B, Hq, Sq, Skv, has_bias,
-         bias_in_lds(ba.bias, ba.dtype, dtype, KDqk, Sq, Skv), &geo, &route);
-  else
-    route = route_for(deterministic, KDqk, geo, B, Hq, Sq, Skv);
+  plan(KDqk, KDv, deterministic, B, Hq, Sq, Skv,
+       qat ? X_WIDE : bias_extra(ba.bias, ba.dtype, dtype, KDqk, Sq, Skv), &geo, &route);
   if (route == R_INVALID) return SDPA_BWD_INVALID_ARG;
   // the chosen key tile may be larger than validate() assumed: one head's rows (and its padded
   // tiles) stay addressable through 32-bit buffer offsets
@@ -828,8 +835,8 @@ size_t sdpa_bwd_nvfp4_qat_workspace_size(int B, int H, int Sq, int Skv, int D, i
   if (B < 0 || H <= 0 || Sq < 0 || Skv < 0 || D != 128 || (causal && Sq != Skv)) return 0;
   if (B == 0 || Sq == 0 || Skv == 0) return 0;
   Geometry geo;
-  geometry_for(128, 128, &geo, true);
-  const Route route = route_for(deterministic, 128, geo, B, H, Sq, Skv);
+  Route route = R_INVALID;
+  plan(128, 128, deterministic, B, H, Sq, Skv, X_WIDE, &geo, &route);
   if (route == R_INVALID) return 0;
   return (size_t)(qat_hat_bytes(B, H, Sq, Skv) + carve(B, H, H, Sq, Skv, 128, 128, route, geo).total);
 }
@@ -961,8 +968,8 @@ size_t sdpa_bwd_run_workspace_size(const sdpa_bwd_args* a) {
   int kq, kv;
   Route route = R_INVALID;
   if (!kernel_dims(a->Dqk, a->Dv, &kq, &kv) ||
-      !plan(kq, kv, a->deterministic, a->B, a->Hq, a->Sq, a->Skv, a->bias != nullptr,
-            bias_in_lds(a->bias, a->bias_dtype, a->dtype, kq, a->Sq, a->Skv), &geo, &route))
+      !plan(kq, kv, a->deterministic, a->B, a->Hq, a->Sq, a->Skv,
+            bias_extra(a->bias, a->bias_dtype, a->dtype, kq, a->Sq, a->Skv), &geo, &route))
     return 0;
   if (a->B == 0 || a->Sq == 0 || a->Skv == 0) return 0;
   if (route == R_INVALID) return 0;
@@ -979,8 +986,8 @@ int sdpa_bwd_run_dq_route(const sdpa_bwd_args* a) {
   int kq, kv;
   Route route = R_INVALID;
   if (!kernel_dims(a->Dqk, a->Dv, &kq, &kv) ||
-      !plan(kq, kv, a->deterministic, a->B, a->Hq, a->Sq, a->Skv, a->bias != nullptr,
-            bias_in_lds(a->bias, a->bias_dtype, a->dtype, kq, a->Sq, a->Skv), &geo, &route))
+      !plan(kq, kv, a->deterministic, a->B, a->Hq, a->Sq, a->Skv,
+            bias_extra(a->bias, a->bias_dtype, a->dtype, kq, a->Sq, a->Skv), &geo, &route))
     return -1;
   return route_code(route);
 }

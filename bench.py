@@ -147,18 +147,21 @@ def atomic_probe():
                       "g_adds_per_s": round(n / ms / 1e6, 1)}), flush=True)
 
 
-def kernel_tiles(w, bias=False, qat=False):
-    """The main kernel's head dim and key tile for the workload (32-row q tiles): the next native
-    head dim, 256-key tiles (8 waves) up to head dim 192 without a bias, else 128-key tiles."""
+def kernel_tiles(w, bias=False):
+    """The main kernel's head dim and key tile for the workload (32-row q tiles) off the relay
+    route: the next native head dim; 256-key tiles (8 waves) up to head dim 192, with an io-type
+    bias (the only kind this script draws) up to head dim 128 when S_kv is a multiple of 8, and for
+    the QAT variant; else 128-key tiles (4 waves)."""
     kq = next(d for d in (32, 64, 128, 192, 256) if w.Dqk <= d and w.Dv <= (128 if d == 192 else d))
-    return kq, (128 if kq == 256 or bias or qat else 256), 32
+    narrow = kq == 256 or (bias and (kq > 128 or w.Skv % 8 != 0))
+    return kq, (128 if narrow else 256), 32
 
 
-def dq_atomic_adds(w, lens, bias=False, qat=False):
+def dq_atomic_adds(w, lens, bias=False):
     """fp32 atomic adds one main-kernel launch makes on the atomic route: every (key tile, q tile)
     pair the mask leaves visible adds a 32-row x kernel-head-dim dQ block, rows past the batch
     entry's query length skipped (the q-tile range rule of the kernel's mask geometry)."""
-    kq, bc, br = kernel_tiles(w, bias, qat)
+    kq, bc, br = kernel_tiles(w, bias)
     total = 0
     for b in range(w.B):
         Lq = w.Sq if lens is None else int(lens[b])
@@ -465,7 +468,7 @@ def main():
     if route == lib.DQ_ATOMIC:
         # the rate at which the main kernel's fp32 dQ atomics retire, next to the rate of a kernel
         # that does nothing but fp32 atomic adds (torch's index_add_), measured now
-        adds = dq_atomic_adds(w, lens, args.bias != "none", args.qat)
+        adds = dq_atomic_adds(w, lens, args.bias != "none")
         n, ms = atomic_rate()
         achieved = adds / (main_ms * 1e-3)
         probe = n / (ms * 1e-3)

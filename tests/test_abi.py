@@ -344,15 +344,16 @@ def test_io_dtype_dbias_workspace_and_rejections(so):
 
 
 def test_nvfp4_qat_workspace_and_rejections(so):
-    # the fake-quantised Q, K, V copies, then the chain's carve in the 4-wave layout (128-key
-    # tiles): statistics and, on the atomic route, the fp32 dQ accumulator
+    # the fake-quantised Q, K, V copies, then the chain's carve in the 8-wave layout (256-key
+    # tiles; the relay route keeps 4 waves): statistics and, on the atomic route, the fp32 dQ
+    # accumulator
     B, H, Sq, Skv = 1, 2, 200, 300
     hat = _al(B * H * Sq * 128 * 2) + 2 * _al(B * H * Skv * 128 * 2)
     assert lib.nvfp4_qat_workspace_size(B, H, Sq, Skv, 128, False, 0) == \
         hat + _al(B * H * 224 * 8) + _al(B * H * Sq * 128 * 4)
-    # dS panels over 128-key tiles (Skv padded to 384)
+    # dS panels over 256-key tiles (Skv padded to 512)
     assert lib.nvfp4_qat_workspace_size(B, H, Sq, Skv, 128, False, 2) == \
-        hat + _al(B * H * 224 * 8) + _al(B * H * 224 * 384 * 2)
+        hat + _al(B * H * 224 * 8) + _al(B * H * 224 * 512 * 2)
     assert lib.nvfp4_qat_workspace_size(B, H, Sq, Skv, 64, False, 0) == 0      # head dim 128 only
     assert lib.nvfp4_qat_workspace_size(B, H, Sq, Skv, 128, True, 0) == 0      # causal: Sq == Skv
     assert lib.nvfp4_qat_workspace_size(B, H, Sq, Skv, 128, False, 5) == 0
