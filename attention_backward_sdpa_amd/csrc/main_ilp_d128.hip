@@ -16,8 +16,6 @@ SDPA_ILP_PF(128, 4, DQ_ATOMIC, 2)
 SDPA_ILP_PF(128, 4, DQ_DS, 2)
 SDPA_ILP_PF(128, 4, DQ_PARTIAL, 2)
 SDPA_ILP_PF(128, 4, DQ_RELAY, 2)
-// NVFP4 QAT (bf16, exact head dims, no bias), every route
-SDPA_ILP(128, 4, DQ_ATOMIC, false, 0, false, true)
-SDPA_ILP(128, 4, DQ_DS, false, 0, false, true)
-SDPA_ILP(128, 4, DQ_PARTIAL, false, 0, false, true)
+// NVFP4 QAT (bf16, exact head dims, no bias) on the relay route, the one route where it keeps
+// 4 waves
 SDPA_ILP(128, 4, DQ_RELAY, false, 0, false, true)

@@ -112,8 +112,9 @@ hipError_t launch_main_dqk(const MainParams& mp, DqMode mode, bool f16, int bias
       if (f16 || bias || mp.dqk_act != 128 || mp.dv_act != 128) return hipErrorInvalidValue;
       if (MainCfg<128, 128, 32, NW0, DQ_ATOMIC>::BC == bc)
         return launch_main_mode<128, 128, 32, NW0, false, 0, false, true>(mp, mode, grid, s);
-      if (MainCfg<128, 128, 32, NW1, DQ_ATOMIC>::BC != bc) return hipErrorInvalidValue;
-      return launch_main_mode<128, 128, 32, NW1, false, 0, false, true>(mp, mode, grid, s);
+      if (MainCfg<128, 128, 32, NW1, DQ_ATOMIC>::BC != bc || mode != DQ_RELAY)
+        return hipErrorInvalidValue;
+      return launch_main_cfg<MainCfg<128, 128, 32, NW1, DQ_RELAY, false, 0, false, true>>(mp, grid, s);
     } else {
       return hipErrorInvalidValue;
     }

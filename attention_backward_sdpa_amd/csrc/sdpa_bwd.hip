@@ -28,9 +28,9 @@ constexpr int64_t kAlign = 256;
 inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 // Tile geometry per supported (Dqk, Dv): waves per workgroup NW, keys per wave KPW = 32, key
-// tile BC = NW * KPW, q tile BR = 32.  Head dims <= 128 run 8 waves (two per SIMD, 256 registers
-// each, 256-key tiles); larger head dims run 4 waves with 512 registers for the bigger dK/dV
-// accumulators (128-key tiles).
+// tile BC = NW * KPW, q tile BR = 32.  Kernel head dims up to 192 run 8 waves (two per SIMD, 256
+// registers each, 256-key tiles); head dim 256 runs 4 waves with 512 registers for the bigger
+// dK/dV accumulators (128-key tiles).
 struct Geometry {
   int nw, kpw, bc, br;
 };
@@ -50,16 +50,16 @@ bool kernel_dims(int Dqk, int Dv, int* kq, int* kv) {
   return false;
 }
 
-// With an additive bias every head dim runs the 4-wave layout (512 registers per wave): the
-// bias values of the next q tile are held in registers while the current one computes.
-bool geometry_for(int Dqk, int Dv, Geometry* g, bool bias = false) {
+// `narrow`: the 4-wave layout (512 registers per wave) at every head dim, for the extras that
+// need it (see plan): a bias held in registers a q tile ahead, the relay's bias and QAT kernels.
+bool geometry_for(int Dqk, int Dv, Geometry* g, bool narrow = false) {
   if (Dqk == 32 && Dv == 32) *g = {8, 32, 256, 32};
   else if (Dqk == 64 && Dv == 64) *g = {8, 32, 256, 32};
   else if (Dqk == 128 && Dv == 128) *g = {8, 32, 256, 32};
   else if (Dqk == 192 && Dv == 128) *g = {8, 32, 256, 32};
   else if (Dqk == 256 && Dv == 256) *g = {4, 32, 128, 32};
   else return false;
-  if (bias) *g = {4, 32, 128, 32};
+  if (narrow) *g = {4, 32, 128, 32};
   return true;
 }
 
@@ -256,12 +256,12 @@ int check_layouts(const Layouts& L, int Sq, int Skv, int Dqk, int Dv) {
 int validate(const void* q, const void* k, const void* v, const void* o, const void* dO,
              const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
              int Skv, int Dqk, int Dv, int window_left, int window_right, Geometry* geo,
-             bool bias = false) {
+             bool narrow = false) {
   if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0) return SDPA_BWD_INVALID_ARG;
   if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return SDPA_BWD_INVALID_ARG;
   if (window_left < -1 || window_right < 0) return SDPA_BWD_INVALID_ARG;
   int kq, kv;
-  if (!kernel_dims(Dqk, Dv, &kq, &kv) || !geometry_for(kq, kv, geo, bias))
+  if (!kernel_dims(Dqk, Dv, &kq, &kv) || !geometry_for(kq, kv, geo, narrow))
     return SDPA_BWD_UNSUPPORTED;
   // the kernels address one head's rows (and its padded tiles) through 32-bit buffer offsets
   const int64_t s_max = (Sq > Skv ? Sq : Skv) + geo->bc;
@@ -285,7 +285,7 @@ hipError_t launch_dq2k(const Dq2kParams& dp, int grid, hipStream_t s) {
 }
 
 // The main kernel of the route for kernel head dim Dqk (instantiated in main_d<Dqk>.hip).
-// bias: 0 none, 1 bias, 2 bias and dBias (the 4-wave layout of geometry_for).
+// bias: 0 none, 1 bias, 2 bias and dBias; `bc` is the key tile plan chose (it selects the layout).
 hipError_t run_main(int Dqk, const MainParams& mp, Route route, bool f16, int bias, int grid,
                     int bc, hipStream_t s, bool qat = false) {
   const DqMode mode = route == R_DS    ? DQ_DS
@@ -445,7 +445,8 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
         hipStream_t stream, void* const* events, bool qat = false) {
   Geometry geo;
   const bool has_bias = ba.bias != nullptr;
-  // a bias or the QAT variant runs the 4-wave layout
+  // checked here with the 4-wave geometry when an extra may need it; plan() below picks the
+  // layout, and the spans are checked again with its key tile
   int st = validate(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, Dqk, Dv, window_left,
                     window_right, &geo, has_bias || qat);
   if (st != SDPA_BWD_OK) return st;
