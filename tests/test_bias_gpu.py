@@ -173,3 +173,55 @@ def test_io_dtype_dbias(name, det):
                                               None if lens is None else lens[x])
                           for x in range(w.B)], axis=0)
         assert np.all(dbias[bb][:, ~vis] == 0)
+
+
+# fp16 io with a bias of the io type (S_kv a multiple of 8): the 8-wave layout with the bias tile
+# staged in LDS as fp16 (the relay keeps the 4-wave layout).  Tolerance as for the other fp16
+# cases: fp16 keeps 11 significant bits, so the error budget is 4 unit roundoffs (2e-3), which a
+# bias or operand read in the wrong 16-bit format would exceed by far.
+FP16_CASES = {
+    "fp16_gqa_causal_d128_s320": V(W["gqa_causal_s4096_d128"], B=2, Hq=4, Hkv=2, Sq=320, Skv=320),
+    "fp16_window_padded_d64_s264": V(W["mla_window_padded_s4096"], B=2, Hq=2, Hkv=2, Sq=264,
+                                     Skv=264, window_left=90, len_lo=100, Dqk=64, Dv=64),
+    "fp16_d32_s200x328": V(W["mha_s128_d64"], B=1, Hq=2, Hkv=2, Sq=200, Skv=328, Dqk=32, Dv=32),
+}
+FP16_TOL = 2e-3
+
+
+@pytest.mark.parametrize("det", [0, 2, 3, 4], ids=["atomic", "dspanels", "dqpartials", "relay"])
+@pytest.mark.parametrize("name", list(FP16_CASES))
+def test_fp16_io_bias_parity(name, det):
+    import attention_backward_sdpa_amd as lib
+    w = FP16_CASES[name]
+    C.log(f"fp16 io-type bias case {name} route {det}: {w}")
+    inp = synth.draw_inputs(w, dtype="fp16")
+    f = lambda x: synth.fp16_to_f32(x).astype(np.float64)
+    bias_bits = synth.fp16_bits(np.random.default_rng(23).standard_normal(
+        (w.B, w.Hq, w.Sq, w.Skv)).astype(np.float32))
+    bias64 = f(bias_bits)
+    lens = None if inp.seq_q_lens is None else [int(x) for x in inp.seq_q_lens]
+    kw = dict(causal=w.causal, window_left=w.window_left, seq_q_lens=lens, seq_kv_lens=lens)
+    o64, lse64 = oracle.forward(f(inp.q), f(inp.k), f(inp.v), w.softmax_scale, bias=bias64, **kw)
+    o_bits = synth.fp16_bits(o64.astype(np.float32))
+    lse = lse64.astype(np.float32)
+    ref = oracle.backward(f(inp.q), f(inp.k), f(inp.v), f(o_bits), f(inp.do),
+                          lse.astype(np.float64), w.softmax_scale, bias=bias64,
+                          return_dbias=True, **kw)
+    h = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.float16).cuda()
+    q, k, v, o, do = h(inp.q), h(inp.k), h(inp.v), h(o_bits), h(inp.do)
+    outs = [torch.full_like(x, float("nan")) for x in (q, k, v)]
+    dbias = torch.full((w.B, w.Hq, w.Sq, w.Skv), float("nan"), device="cuda")
+    tl = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
+    args = dict(scale=w.softmax_scale, causal=w.causal, window_left=w.window_left,
+                deterministic=det, seq_q_lens=tl, seq_kv_lens=tl, bias=h(bias_bits), dbias=dbias)
+    n = lib.run_workspace_size(q, k, v, **args)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    lib.sdpa_bwd_run(q, k, v, o, do, torch.from_numpy(lse).cuda(), *outs, workspace=ws, **args)
+    torch.cuda.synchronize()
+    got = [x.float().cpu().numpy() for x in outs + [dbias]]
+    for tname, g, r in zip(("dQ", "dK", "dV", "dBias"), got, ref):
+        C.assert_close(f"fp16 bias {name} route {det} {tname}", g, r, tol=FP16_TOL)
+    for bb in range(w.B):
+        L = None if lens is None else lens[bb]
+        vis = oracle.visible_mask(w.Sq, w.Skv, w.causal, w.window_left, L, L)
+        assert np.all(got[3][bb][:, ~vis] == 0)
