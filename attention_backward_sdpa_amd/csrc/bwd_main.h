@@ -22,10 +22,12 @@
 //
 // MI355X mapping (differs from the pages' SM120 warp-specialised design):
 //   * NW waves of 64 lanes; wave w owns KPW = 32 keys, so the key tile is BC = 32 * NW.  At head
-//     dim <= 128 there are 8 waves, two per SIMD, each within 256 registers: the hardware then
+//     dims up to 192 there are 8 waves, two per SIMD, each within 256 registers: the hardware then
 //     overlaps one wave's softmax VALU work and LDS latency with the other wave's MFMAs, and the
-//     256-key tile halves the dQ atomics and the Q/dO re-reads per key.  Above that, 4 waves with
-//     512 registers each hold the larger dK/dV accumulators.
+//     256-key tile halves the dQ atomics and the Q/dO re-reads per key.  At head dim 256, 4 waves
+//     with 512 registers each hold the larger dK/dV accumulators; so do the kernels whose extra
+//     per-element state does not fit 256 registers (a bias held in registers, the relay's bias
+//     and QAT variants).
 //   * S and dP are computed with q as the MFMA row index and keys as the column index
 //     (v_mfma_f32_32x32x16_bf16), so each wave's P and dS accumulators are already the B operand of
 //     GEMM3/GEMM5 (contraction over q) and its dK^T/dV^T partials complete inside the wave.
@@ -36,19 +38,20 @@
 //     operands of GEMM3/GEMM5 and the contraction-over-keys operand K of GEMM4:
 //       - Q and dO tiles (32 q rows), gathered straight from Q / dO with 16-byte LDS-DMA loads;
 //         read as A operands of GEMM1 / GEMM2 and, transposed, as Q^T / dO^T for GEMM5 / GEMM3;
-//       - the key tile K as B operands of GEMM1 (registers instead at head dim >= 192) and,
-//         transposed, of GEMM4.
+//       - the key tile K as B operands of GEMM1 (registers instead in the 4-wave kernels at head
+//         dims 192 and 256) and, transposed, of GEMM4.
 //     The q-tile buffers are double-buffered and filled one tile ahead of the compute.
 //   * The wave's V slice is held in registers as the B operand of GEMM2.
-//   * Deterministic route: each lane stores its bf16 dS values straight from registers as 8-byte
-//     quads (512 contiguous bytes per instruction, non-temporal); no LDS round trip.
+//   * dS-panel route: each lane stores its bf16 dS values straight from registers, 16 contiguous
+//     bytes per lane (1 KiB per instruction, non-temporal); no LDS round trip.
 //   * fp32-atomic and dQ-partial routes: dS is written to LDS in the same register order and
 //     GEMM4 reads it (and K) with ds_read_b64_tr_b16.  GEMM4 of q tile i runs at the start of the
 //     next iteration so its atomics (or partial stores) drain while that iteration computes.
 //   * The preprocess kernel supplies LSE * log2(e) per row (+inf for rows without keys), so the
 //     replay is one FMA and one v_exp_f32 per element.
-//   * Head dim 32 (8 waves, no bias): the two waves of each SIMD (w and w + 4) run half a q tile
-//     apart (staggered groups, see the q-tile loop), so that their softmax replays do not coincide.
+//   * Head dim 32 (8 waves, no bias, not the relay): the two waves of each SIMD (w and w + 4) run
+//     half a q tile apart (staggered groups, see the q-tile loop), so that their softmax replays do
+//     not coincide.
 #pragma once
 #include "common.h"
 #include "masks.h"
