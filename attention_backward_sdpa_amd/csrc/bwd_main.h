@@ -86,10 +86,11 @@ struct MainParams {
   float scale_log2;         // scale * log2(e)
   // additive bias ("API Usage" bias_tensor): (Bb, Hq, Sq, Skv) contiguous, Bb = 1 or B
   const void* bias;         // io-type or fp32 elements
-  float* dbias;             // (Bb, Hq, Sq, Skv) fp32 dBias = dS, or null
+  void* dbias;              // (Bb, Hq, Sq, Skv) dBias = dS (fp32, or the io type with dbias_io), or null
   int64_t bias_bstride;     // elements between batch entries of bias / dbias (0 for Bb = 1)
   int bias_f32;             // bias elements are fp32 (else the io type)
   int dbias_atomic;         // dBias accumulates over batch entries (Bb = 1, B > 1): fp32 atomics
+  int dbias_io;             // dBias elements of the io type, each written once (not with dbias_atomic)
   // ordered relay (DQ_RELAY)
   float* relay_acc;         // (B*Hq, sq_pad/32) blocks of 32 x Dqk fp32: the running dQ sums
   int* relay_turn;          // (B*Hq, sq_pad/32): KV tiles that have added into each sum (zeroed)
@@ -916,8 +917,24 @@ __global__ void __launch_bounds__(C::NT, 1) bwd_main_kernel(MainParams p) {
     };
     auto store_dbias = [&](int i_t) {
       if constexpr (C::BIAS == 2) {
-        float* base = p.dbias + bias_bh + key_lane;
         const int row0 = i_t * BR;
+        if (p.dbias_io) {
+          // an io-type output whose elements are each written once: rounded here, once
+          bf16_t* base = reinterpret_cast<bf16_t*>(p.dbias) + bias_bh + key_lane;
+          if (row0 + BR <= p.Sq && k0 + BC <= p.Skv) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              base[(int64_t)(row0 + acc_row<32>(r, g)) * p.Skv] = Elem<C::F16>::one(dsf[r]);
+          } else if (key_lane < p.Skv) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = row0 + acc_row<32>(r, g);
+              if (row < p.Sq) base[(int64_t)row * p.Skv] = Elem<C::F16>::one(dsf[r]);
+            }
+          }
+          return;
+        }
+        float* base = reinterpret_cast<float*>(p.dbias) + bias_bh + key_lane;
         if (row0 + BR <= p.Sq && k0 + BC <= p.Skv && !p.dbias_atomic) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) base[(int64_t)(row0 + acc_row<32>(r, g)) * p.Skv] = dsf[r];

@@ -69,7 +69,8 @@ struct BiasArgs {
   float* dbias = nullptr;
   int dtype = SDPA_BWD_BF16;  // SDPA_BWD_BF16 / SDPA_BWD_FP16 (the io type) or SDPA_BWD_FP32
   int batch = 1;              // 1 or B
-  bool dbias_io = false;      // dbias holds io-type elements: accumulate in fp32, then dbias_cvt
+  bool dbias_io = false;      // dbias holds io-type elements (see run(): written directly, or
+                              // accumulated in fp32 and converted by dbias_cvt)
 };
 
 // Number of parts the q-tile range of every key tile is split into (each part a workgroup of its
@@ -177,7 +178,8 @@ struct Carve {
   int64_t sq_pad = 0, skv_pad = 0;
 };
 
-// dbias_elems: elements of an fp32 dBias accumulator (an io-type dBias output), else 0.
+// dbias_elems: elements of an fp32 dBias accumulator (an io-type dBias summed over the batch),
+// else 0.
 Carve carve(int B, int Hq, int Hkv, int Sq, int Skv, int Dqk, int Dv, Route route,
             const Geometry& g, int64_t dbias_elems = 0) {
   Carve c;
@@ -481,12 +483,17 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   // surface", bias), so the deterministic routes need a per-batch bias then
   const bool dbias_atomic = ba.dbias && ba.batch == 1 && B > 1;
   if (dbias_atomic && route != R_ATOMIC) return SDPA_BWD_UNSUPPORTED;
+  // an io-type dBias: the main kernel writes each element once, rounded once, unless it sums over
+  // the batch; then it accumulates in an fp32 workspace copy that dbias_cvt rounds afterwards
+  // (the same single rounding of the same fp32 value either way)
+  const bool dbias_acc = ba.dbias && ba.dbias_io && dbias_atomic;
+  const bool dbias_direct_io = ba.dbias && ba.dbias_io && !dbias_atomic;
   // empty problems need no workspace (sdpa_bwd_workspace_size returns 0 for them)
   const bool empty = B == 0 || Sq == 0 || Skv == 0;
   const int64_t dbias_elems = (int64_t)ba.batch * Hq * Sq * Skv;
   const Carve c = empty ? Carve{}
                         : carve(B, Hq, Hkv, Sq, Skv, KDqk, KDv, route, geo,
-                                ba.dbias && ba.dbias_io ? dbias_elems : 0);
+                                dbias_acc ? dbias_elems : 0);
   if (c.total > 0 && workspace == nullptr) return SDPA_BWD_INVALID_ARG;
   if (check_ws && (uint64_t)c.total > (uint64_t)workspace_bytes) return SDPA_BWD_WORKSPACE_TOO_SMALL;
   if (c.total > 0 && ((uintptr_t)workspace % kAlign) != 0) return SDPA_BWD_UNSUPPORTED;
@@ -558,13 +565,14 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   pp.relay_ctl = route == R_RELAY ? (int*)(ws + c.relay_ctl) : nullptr;
   e = launch_preprocess(pp, KDv, f16, (int64_t)B * Hq * (c.sq_pad / geo.br), stream);
   if (e == hipSuccess) e = launch_dsink(stats, (int)c.sq_pad, false);
-  // the fp32 dBias the main kernel writes: the caller's output, or the workspace accumulator of
-  // an io-type output (converted once after the main kernel)
-  float* dbias32 = ba.dbias && ba.dbias_io ? (float*)(ws + c.dbias_f32) : (float*)ba.dbias;
+  // the dBias the main kernel writes: the caller's output (fp32 or, written directly, the io
+  // type), or the fp32 workspace accumulator of a batch-summed io-type output
+  void* dbias_main = dbias_acc ? (void*)(ws + c.dbias_f32) : ba.dbias;
   if (e == hipSuccess && ba.dbias) {
     // zero the dBias blocks the main kernel does not write (all of them when it accumulates)
     DbiasFillParams fp{};
-    fp.dbias = dbias32;
+    fp.dbias = dbias_main;
+    fp.io = dbias_direct_io ? 1 : 0;
     fp.seq_q_lens = seq_q_lens;
     fp.seq_kv_lens = seq_kv_lens;
     fp.Hq = Hq;
@@ -628,10 +636,11 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   mp.scale = scale;
   mp.scale_log2 = scale * kLog2e;
   mp.bias = ba.bias;
-  mp.dbias = dbias32;
+  mp.dbias = dbias_main;
   mp.bias_bstride = ba.batch == 1 ? 0 : (int64_t)Hq * Sq * Skv;
   mp.bias_f32 = ba.dtype == SDPA_BWD_FP32 ? 1 : 0;
   mp.dbias_atomic = dbias_atomic ? 1 : 0;
+  mp.dbias_io = dbias_direct_io ? 1 : 0;
   int64_t main_grid = (int64_t)mp.n_kv_tiles * split * B * Hq;
   const int64_t relay_items = main_grid;
   if (route == R_RELAY) {
@@ -645,8 +654,8 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
   e = run_main(KDqk, mp, route, f16, has_bias ? (ba.dbias ? 2 : 1) : 0, (int)main_grid, geo.bc,
                stream, qat);
   if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
-  if (ba.dbias && ba.dbias_io) {
-    e = launch_dbias_cvt(dbias32, ba.dbias, dbias_elems, f16, stream);
+  if (dbias_acc) {
+    e = launch_dbias_cvt((const float*)dbias_main, ba.dbias, dbias_elems, f16, stream);
     if (e != hipSuccess) return SDPA_BWD_LAUNCH_FAILED;
   }
   rec(2);
@@ -974,8 +983,10 @@ size_t sdpa_bwd_run_workspace_size(const sdpa_bwd_args* a) {
     return 0;
   if (a->B == 0 || a->Sq == 0 || a->Skv == 0) return 0;
   if (route == R_INVALID) return 0;
-  const int64_t dbias_elems =
-      a->dbias && a->bias && a->dbias_io ? (int64_t)a->bias_batch * a->Hq * a->Sq * a->Skv : 0;
+  // the fp32 accumulator of an io-type dBias summed over the batch (see run())
+  const int64_t dbias_elems = a->dbias && a->bias && a->dbias_io && a->bias_batch == 1 && a->B > 1
+                                  ? (int64_t)a->Hq * a->Sq * a->Skv
+                                  : 0;
   return (size_t)carve(a->B, a->Hq, a->Hkv, a->Sq, a->Skv, kq, kv, route, geo, dbias_elems).total;
 }
 

@@ -244,19 +244,20 @@ __global__ void __launch_bounds__(256) dsink_kernel(DsinkParams p) {
 }
 
 // ---- dBias fill -----------------------------------------------------------------------------------
-// dBias (Bb, Hq, Sq, Skv) fp32: the main kernel writes every element of the (q tile, key tile)
+// dBias (Bb, Hq, Sq, Skv), fp32 or the io type: the main kernel writes every element of the (q tile, key tile)
 // blocks it visits (masked pairs as 0); this kernel zeroes the elements of every other block, or
 // of every block when the main kernel accumulates dBias over the batch with atomics.  One
 // workgroup per (bias batch entry, query head, q tile); threads stride over the columns of the
 // tile's rows, a column's key tile deciding whether it is written here.
 struct DbiasFillParams {
-  float* dbias;
+  void* dbias;              // fp32 elements, or 16-bit io-type elements with `io`
   const int* seq_q_lens;
   const int* seq_kv_lens;
   int Hq, Sq, Skv;
   int bc, br;               // key tile and q tile of the main kernel
   int causal, window_left, window_right, bottom_right;
   int all;                  // zero every element
+  int io;                   // 16-bit io-type elements (zero is all bits clear for bf16 and fp16)
 };
 
 __global__ void __launch_bounds__(256) dbias_fill_kernel(DbiasFillParams p) {
@@ -271,7 +272,7 @@ __global__ void __launch_bounds__(256) dbias_fill_kernel(DbiasFillParams p) {
   mg.causal = p.causal;
   mg.W = p.window_left;
   mg.R = p.window_right;
-  float* base = p.dbias + (bh * p.Sq + (int64_t)i * p.br) * p.Skv;
+  const int64_t first = (bh * p.Sq + (int64_t)i * p.br) * p.Skv;
   const int rows = min(p.br, p.Sq - i * p.br);
   for (int c = threadIdx.x; c < p.Skv; c += 256) {
     bool visited = false;
@@ -280,8 +281,14 @@ __global__ void __launch_bounds__(256) dbias_fill_kernel(DbiasFillParams p) {
       q_tile_range(mg, (c / p.bc) * p.bc, p.bc, p.br, &lo, &hi);
       visited = lo <= i && i <= hi;
     }
-    if (!visited)
+    if (visited) continue;
+    if (p.io) {
+      bf16_t* base = reinterpret_cast<bf16_t*>(p.dbias) + first;
+      for (int r = 0; r < rows; ++r) base[(int64_t)r * p.Skv + c] = 0;
+    } else {
+      float* base = reinterpret_cast<float*>(p.dbias) + first;
       for (int r = 0; r < rows; ++r) base[(int64_t)r * p.Skv + c] = 0.f;
+    }
   }
 }
 

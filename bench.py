@@ -302,9 +302,10 @@ def main():
                          "3 dQ partials + ordered reduction, 4 ordered relay)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"],
                     help="io element type of Q, K, V, O, dO and the gradients")
-    ap.add_argument("--bias", default="none", choices=["none", "bias", "dbias"],
+    ap.add_argument("--bias", default="none", choices=["none", "bias", "dbias", "dbias_io"],
                     help="add a per-batch additive bias (B, Hq, Sq, Skv) of the io type, drawn "
-                         "N(0,1) (bias), and also produce its fp32 gradient (dbias)")
+                         "N(0,1) (bias), and also produce its gradient in fp32 (dbias) or in the "
+                         "io type (dbias_io)")
     ap.add_argument("--qat", action="store_true",
                     help="the NVFP4 attention-QAT backward (sdpa_bwd_nvfp4_qat) on the workload's "
                          "shape (MHA, head dim 128, no window or padding); O and LSE come from the "
@@ -356,8 +357,9 @@ def main():
     if args.bias != "none":
         gen = torch.Generator(device=dev).manual_seed(1000)
         bias = torch.randn(w.B, w.Hq, w.Sq, w.Skv, generator=gen, device=dev).to(io)
-        if args.bias == "dbias":
-            dbias = torch.empty(w.B, w.Hq, w.Sq, w.Skv, dtype=torch.float32, device=dev)
+        if args.bias in ("dbias", "dbias_io"):
+            dbias = torch.empty(w.B, w.Hq, w.Sq, w.Skv, device=dev,
+                                dtype=torch.float32 if args.bias == "dbias" else io)
     if args.qat and (w.Hq != w.Hkv or w.Dqk != 128 or w.Dv != 128 or w.window_left >= 0 or
                      lens is not None or args.bias != "none" or args.dtype != "bf16"):
         raise SystemExit("--qat: MHA, head dim 128, bf16, no window, padding or bias")
@@ -455,7 +457,8 @@ def main():
                    "dq_route": ROUTE_NAMES[route],
                    "nvfp4_qat": bool(args.qat),
                    "bias": {"none": "none", "bias": f"{args.dtype} (B, Hq, Sq, Skv)",
-                            "dbias": f"{args.dtype} (B, Hq, Sq, Skv) with fp32 dBias"}[args.bias],
+                            "dbias": f"{args.dtype} (B, Hq, Sq, Skv) with fp32 dBias",
+                            "dbias_io": f"{args.dtype} (B, Hq, Sq, Skv) with {args.dtype} dBias"}[args.bias],
                    "algorithmic_gflop": round(flops / 1e9, 3)},
         "stage_ms": {"preprocess": round(float(stage_avg[0]), 4), "main": round(float(stage_avg[1]), 4),
                      "gqa_reduce": round(float(stage_avg[2]), 4),

@@ -231,11 +231,14 @@ int sdpa_bwd_flex(const void* q, const void* k, const void* v, const void* o, co
  *               (use a per-batch bias).  Otherwise each element is written once (reproducible).
  *   dbias_io    0: dbias holds fp32 elements (above).  1: dbias holds elements of the io type
  *               (dtype), 2-byte aligned ("The kernel chain" dbias_cvt, "Support surface" bias: an
- *               io-dtype output adds a cast): dBias is accumulated in fp32 in the workspace
- *               (bias_batch*Hq*Sq*Skv floats, 256-byte aligned, after the other pieces) and rounded
- *               once to the io type by the dbias_cvt kernel right after the main kernel (inside the
- *               main kernel's event interval).  Read only when dbias is not NULL.
- * With a bias every head dim runs 128-key tiles, so the workspace can differ from the one
+ *               io-dtype output adds a cast).  Each element is the fp32 dBias rounded once to the
+ *               io type: written directly by the main kernel when it is written once (a per-batch
+ *               bias, or B == 1); for a bias summed over the batch (bias_batch == 1, B > 1) it is
+ *               accumulated in fp32 in the workspace (Hq*Sq*Skv floats, 256-byte aligned, after
+ *               the other pieces) and rounded by the dbias_cvt kernel right after the main kernel
+ *               (inside the main kernel's event interval).  Read only when dbias is not NULL.
+ * With a bias the key tile depends on the bias (256 keys with an io-type bias staged in LDS at
+ * kernel head dims up to 128, else 128), so the workspace can differ from the one
  * sdpa_bwd_workspace_size reports: size it with sdpa_bwd_run_workspace_size. */
 typedef struct sdpa_bwd_args {
   const void* q;

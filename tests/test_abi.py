@@ -307,9 +307,10 @@ def test_run_rejections_before_launch(so):
 
 
 def test_io_dtype_dbias_workspace_and_rejections(so):
-    # "The kernel chain" dbias_cvt: an io-type dBias output adds an fp32 accumulator of
-    # bias_batch * Hq * Sq * Skv floats (256-byte aligned) at the end of the carve (host tensors
-    # stand in for device ones: the size query reads only their shapes and whether they exist)
+    # "The kernel chain" dbias_cvt: an io-type dBias summed over the batch (a batch-1 bias with
+    # B > 1) adds an fp32 accumulator of Hq * Sq * Skv floats (256-byte aligned) at the end of the
+    # carve; a per-batch one is written directly and needs none (host tensors stand in for device
+    # ones: the size query reads only their shapes and whether they exist)
     torch = pytest.importorskip("torch")
     for Bb in (1, 2):
         q = torch.empty(2, 4, 200, 128, dtype=torch.bfloat16, device="cpu")
@@ -321,7 +322,7 @@ def test_io_dtype_dbias_workspace_and_rejections(so):
                                          dbias=torch.empty(Bb, 4, 200, 300, device="cpu"))
             io = lib.run_workspace_size(q, k, k, causal=True, deterministic=det, bias=bias,
                                         dbias=torch.empty(Bb, 4, 200, 300, dtype=torch.bfloat16))
-            assert f32 == base and io == base + _al(Bb * 4 * 200 * 300 * 4)
+            assert f32 == base and io == base + (_al(4 * 200 * 300 * 4) if Bb == 1 else 0)
         # an io-type dBias of another type than the inputs is refused by the binding
         with pytest.raises(ValueError):
             lib.run_workspace_size(q, k, k, bias=bias, dbias=torch.empty(

@@ -188,12 +188,13 @@ FP16_CASES = {
 FP16_TOL = 2e-3
 
 
+@pytest.mark.parametrize("dbias_io", [False, True], ids=["dbias_f32", "dbias_fp16"])
 @pytest.mark.parametrize("det", [0, 2, 3, 4], ids=["atomic", "dspanels", "dqpartials", "relay"])
 @pytest.mark.parametrize("name", list(FP16_CASES))
-def test_fp16_io_bias_parity(name, det):
+def test_fp16_io_bias_parity(name, det, dbias_io):
     import attention_backward_sdpa_amd as lib
     w = FP16_CASES[name]
-    C.log(f"fp16 io-type bias case {name} route {det}: {w}")
+    C.log(f"fp16 io-type bias case {name} route {det}, fp16 dBias {dbias_io}: {w}")
     inp = synth.draw_inputs(w, dtype="fp16")
     f = lambda x: synth.fp16_to_f32(x).astype(np.float64)
     bias_bits = synth.fp16_bits(np.random.default_rng(23).standard_normal(
@@ -210,7 +211,8 @@ def test_fp16_io_bias_parity(name, det):
     h = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.float16).cuda()
     q, k, v, o, do = h(inp.q), h(inp.k), h(inp.v), h(o_bits), h(inp.do)
     outs = [torch.full_like(x, float("nan")) for x in (q, k, v)]
-    dbias = torch.full((w.B, w.Hq, w.Sq, w.Skv), float("nan"), device="cuda")
+    dbias = torch.full((w.B, w.Hq, w.Sq, w.Skv), float("nan"), device="cuda",
+                       dtype=torch.float16 if dbias_io else torch.float32)
     tl = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
     args = dict(scale=w.softmax_scale, causal=w.causal, window_left=w.window_left,
                 deterministic=det, seq_q_lens=tl, seq_kv_lens=tl, bias=h(bias_bits), dbias=dbias)
