@@ -225,11 +225,14 @@ def dsink(o, do, lse, sink, seq_q_lens=None):
 
 
 def backward_dq_rows(q, k, v, o, do, lse, scale, b, h, rows, causal=False, window_left=-1,
-                     seq_q_lens=None, seq_kv_lens=None, bottom_right=False, window_right=0):
+                     seq_q_lens=None, seq_kv_lens=None, bottom_right=False, window_right=0,
+                     bias=None, return_ds=False):
     """dQ[b, h, rows, :] alone, from the same equations restricted to the listed query rows.
 
     dQ_i = scale * sum_j dS_ij K_j with dS_ij = P_ij (dO_i . V_j - O_i . dO_i): only the rows' own
-    scores are needed, so full-size tensors can be sampled row by row.
+    scores are needed, so full-size tensors can be sampled row by row.  With bias the scores gain
+    bias[b, h, rows] as in backward(); return_ds also returns the rows' dS, which is their dBias
+    for a per-batch bias.
     """
     B, Hq, Sq, _ = q.shape
     _, Hkv, Skv, _ = k.shape
@@ -241,18 +244,24 @@ def backward_dq_rows(q, k, v, o, do, lse, scale, b, h, rows, causal=False, windo
     kb = np.asarray(k[b, kh], dtype=np.float64)
     vb = np.asarray(v[b, kh], dtype=np.float64)
     dor = np.asarray(do[b, h, rows], dtype=np.float64)
-    p = _probabilities(scale * (qr @ kb.T), np.asarray(lse[b, h, rows], dtype=np.float64), vis)
+    s_rows = scale * (qr @ kb.T)
+    if bias is not None:
+        s_rows = s_rows + np.asarray(np.asarray(bias)[0 if np.asarray(bias).shape[0] == 1 else b, h, rows],
+                                     dtype=np.float64)
+    p = _probabilities(s_rows, np.asarray(lse[b, h, rows], dtype=np.float64), vis)
     delta = np.sum(np.asarray(o[b, h, rows], dtype=np.float64) * dor, axis=1)
     ds = p * (dor @ vb.T - delta[:, None])
-    return scale * (ds @ kb)
+    return (scale * (ds @ kb), ds) if return_ds else scale * (ds @ kb)
 
 
 def backward_dkdv_rows(q, k, v, o, do, lse, scale, b, kv_head, rows, causal=False, window_left=-1,
-                       seq_q_lens=None, seq_kv_lens=None, bottom_right=False, window_right=0):
+                       seq_q_lens=None, seq_kv_lens=None, bottom_right=False, window_right=0,
+                       bias=None):
     """(dK, dV)[b, kv_head, rows, :] alone: the listed key columns of P and dS over every query row.
 
     dV_j = sum_h sum_i P_ij dO_i and dK_j = scale * sum_h sum_i dS_ij Q_i, summed over the query
-    heads h of the KV head's group; only the listed key columns of the score matrix are formed.
+    heads h of the KV head's group; only the listed key columns of the score matrix are formed
+    (with bias, the listed columns of bias[b, h] join the scores as in backward()).
     """
     B, Hq, Sq, _ = q.shape
     _, Hkv, Skv, _ = k.shape
@@ -267,7 +276,11 @@ def backward_dkdv_rows(q, k, v, o, do, lse, scale, b, kv_head, rows, causal=Fals
     for h in range(kv_head * group, (kv_head + 1) * group):
         qh = np.asarray(q[b, h], dtype=np.float64)
         doh = np.asarray(do[b, h], dtype=np.float64)
-        p = _probabilities(scale * (qh @ kr.T), np.asarray(lse[b, h], dtype=np.float64), vis)
+        s_cols = scale * (qh @ kr.T)
+        if bias is not None:
+            s_cols = s_cols + np.asarray(
+                np.asarray(bias)[0 if np.asarray(bias).shape[0] == 1 else b, h][:, rows], dtype=np.float64)
+        p = _probabilities(s_cols, np.asarray(lse[b, h], dtype=np.float64), vis)
         delta = np.sum(np.asarray(o[b, h], dtype=np.float64) * doh, axis=1)
         ds = p * (doh @ vr.T - delta[:, None])
         dv += p.T @ doh

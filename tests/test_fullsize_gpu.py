@@ -168,3 +168,91 @@ def test_fullsize_deterministic_bitwise(name, det):
             h.update(np.ascontiguousarray(x).view(np.uint32).tobytes())
         digests.add(h.hexdigest())
     assert len(digests) == 1, f"{len(digests)} distinct results over 10 runs"
+
+
+# The additive bias at the headline's full size (causal GQA B=1 Hq=32 Hkv=8 S=4096 D=128): a
+# per-batch bf16 bias drawn N(0, 1) with its fp32 gradient ("API Usage" bias_tensor), on the fp32
+# atomic and dS-panel routes (the 8-wave kernels with the bias tile staged in LDS).  O and LSE come
+# from the fp64 oracle forward with that bias.  Sampled dQ rows, their dBias rows and dK/dV key
+# rows against the oracle; over whole heads: dBias exactly 0 on masked pairs, and every dBias row
+# sums to about 0 (sum_j dS_ij = sum_j P_ij dP_ij - delta_i, with sum_j P_ij = 1).
+_BIAS_PREP = {}
+
+
+def _prepare_bias():
+    if "c3" not in _BIAS_PREP:
+        w = W["gqa_causal_s4096_d128"]
+        t, host = prepared("gqa_causal_s4096_d128")
+        C.log("full-size bias case: drawing the bias")
+        rng = np.random.default_rng(77)
+        bias_bits = synth.bf16_bits(rng.standard_normal((w.B, w.Hq, w.Sq, w.Skv), dtype=np.float32))
+        bias32 = synth.bf16_to_f32(bias_bits)
+        C.log("full-size bias case: fp64 oracle forward with the bias")
+        o64, lse64 = oracle.forward(_f64(host["q"]), _f64(host["k"]), _f64(host["v"]),
+                                    w.softmax_scale, causal=True, bias=bias32)
+        o_bits = synth.bf16_bits(o64.astype(np.float32))
+        lse = lse64.astype(np.float32)
+        del o64, lse64
+        dev = torch.device("cuda:0")
+        tb = dict(t)
+        tb["o"] = torch.from_numpy(o_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        tb["lse"] = torch.from_numpy(lse).to(dev)
+        tb["bias"] = torch.from_numpy(bias_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        hb = dict(host, o=o_bits, lse=lse, bias=bias32)
+        torch.cuda.synchronize()
+        C.log("full-size bias case: inputs ready")
+        _BIAS_PREP["c3"] = (tb, hb)
+    return _BIAS_PREP["c3"]
+
+
+@pytest.mark.parametrize("det", [0, 2], ids=["atomic", "dspanels"])
+def test_fullsize_bias_sampled_rows(det):
+    import attention_backward_sdpa_amd as lib
+    w = W["gqa_causal_s4096_d128"]
+    t, host = _prepare_bias()
+    C.log(f"full-size bias case: GPU chain (deterministic={det})")
+    outs = [torch.empty_like(t[x]) for x in ("q", "k", "v")]
+    for x in outs:
+        x.view(torch.int16).fill_(0x7FC0)
+    dbias = torch.full(tuple(t["bias"].shape), float("nan"), device="cuda")
+    kw = dict(scale=w.softmax_scale, causal=True, deterministic=det, bias=t["bias"], dbias=dbias)
+    n = lib.run_workspace_size(t["q"], t["k"], t["v"], **kw)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    lib.sdpa_bwd_run(t["q"], t["k"], t["v"], t["o"], t["do"], t["lse"], *outs, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    dq, dk, dv = (C.bf16_tensor_to_f32(x) for x in outs)
+    heads = [0, 13, w.Hq - 1]
+    db = {h: dbias[0, h].cpu().numpy() for h in heads}
+    del dbias, ws
+    q, k, v, o, do = (_f64(host[x]) for x in ("q", "k", "v", "o", "do"))
+    lse = host["lse"].astype(np.float64)
+    okw = dict(causal=True, bias=host["bias"])
+    rng = np.random.default_rng(4321)
+    got_q, ref_q, got_b, ref_b = [], [], [], []
+    for h in heads:
+        rows = _edge_rows(w.Sq) + sorted(rng.choice(w.Sq, 4, replace=False).tolist())
+        r, ds = oracle.backward_dq_rows(q, k, v, o, do, lse, w.softmax_scale, 0, h, rows,
+                                        return_ds=True, **okw)
+        ref_q.append(r)
+        got_q.append(dq[0, h, rows])
+        ref_b.append(ds)
+        got_b.append(db[h][rows])
+    got_k, ref_k, got_v, ref_v = [], [], [], []
+    for kh in (0, w.Hkv - 1):
+        rows = _edge_rows(w.Skv) + sorted(rng.choice(w.Skv, 4, replace=False).tolist())
+        rk, rv = oracle.backward_dkdv_rows(q, k, v, o, do, lse, w.softmax_scale, 0, kh, rows, **okw)
+        ref_k.append(rk)
+        ref_v.append(rv)
+        got_k.append(dk[0, kh, rows])
+        got_v.append(dv[0, kh, rows])
+    tag = f"full-size bias (dQ route {ROUTE_NAMES[det]})"
+    C.assert_close(f"{tag} dQ sampled rows", np.concatenate(got_q), np.concatenate(ref_q))
+    C.assert_close(f"{tag} dBias sampled rows", np.concatenate(got_b), np.concatenate(ref_b))
+    C.assert_close(f"{tag} dK sampled rows", np.concatenate(got_k), np.concatenate(ref_k))
+    C.assert_close(f"{tag} dV sampled rows", np.concatenate(got_v), np.concatenate(ref_v))
+    vis = oracle.visible_mask(w.Sq, w.Skv, True)
+    for h in heads:
+        assert np.all(db[h][~vis] == 0), f"{tag}: dBias on masked pairs must be zero (head {h})"
+        rowsum = np.abs(db[h].astype(np.float64).sum(axis=1)).max()
+        assert rowsum <= 1e-2 * np.abs(db[h]).astype(np.float64).sum(axis=1).max(), \
+            f"{tag}: dBias rows do not sum to 0 (head {h})"

@@ -318,6 +318,29 @@ def test_sampled_rows_match_full(mask):
             np.testing.assert_allclose(gv, dv[b, kvh, [1, 4, 8]], atol=1e-13)
 
 
+@pytest.mark.parametrize("bias_batch", [1, 2])
+def test_sampled_rows_match_full_with_bias(bias_batch):
+    # the same with an additive bias: the rows' dQ, their dS (= dBias for a per-batch bias), and
+    # the key rows' dK/dV equal the full backward's
+    q, k, v, do, o, lse, scale, kw = _problem(23, B=2, Hq=4, Hkv=2, Sq=9, Skv=9, causal=True,
+                                              lens=[7, 9])
+    bias = np.random.default_rng(5).standard_normal((bias_batch, 4, 9, 9))
+    o, lse = oracle.forward(q, k, v, scale, bias=bias, **kw)
+    dq, dk, dv, dbias = oracle.backward(q, k, v, o, do, lse, scale, bias=bias, return_dbias=True, **kw)
+    for b in range(2):
+        for h in range(4):
+            r, ds = oracle.backward_dq_rows(q, k, v, o, do, lse, scale, b, h, [0, 3, 8], bias=bias,
+                                            return_ds=True, **kw)
+            np.testing.assert_allclose(r, dq[b, h, [0, 3, 8]], atol=1e-13)
+            if bias_batch == 2:
+                np.testing.assert_allclose(ds, dbias[b, h, [0, 3, 8]], atol=1e-13)
+        for kvh in range(2):
+            gk, gv = oracle.backward_dkdv_rows(q, k, v, o, do, lse, scale, b, kvh, [1, 4, 8],
+                                               bias=bias, **kw)
+            np.testing.assert_allclose(gk, dk[b, kvh, [1, 4, 8]], atol=1e-13)
+            np.testing.assert_allclose(gv, dv[b, kvh, [1, 4, 8]], atol=1e-13)
+
+
 # ----------------------------------------------------------------------------------------------
 # FLOP convention
 def test_flop_count():
