@@ -432,12 +432,6 @@ hipError_t launch_dbias_cvt(const float* src, void* dst, int64_t n, bool f16, hi
   return hipGetLastError();
 }
 
-int grid_stride_blocks(int64_t n) {
-  int64_t b = (n + 255) / 256;
-  if (b > 16384) b = 16384;
-  return (int)(b < 1 ? 1 : b);
-}
-
 int run(const void* q, const void* k, const void* v, const void* o, const void* dO,
         const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Skv,
         int Dqk, int Dv, float scale, int causal, int window_left, int deterministic,
@@ -531,7 +525,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const void* 
       e = launch_dbias_cvt(nullptr, ba.dbias, dbias_elems, f16, stream);
     } else if (e == hipSuccess && ba.dbias && (int64_t)ba.batch * Sq * Skv > 0) {
       // nothing attends: dBias is zero
-      DbiasFillParams fp{ba.dbias, nullptr, nullptr, Hq, Sq, Skv, geo.bc, geo.br, 0, -1, 0, 0, 1};
+      DbiasFillParams fp{ba.dbias, nullptr, nullptr, Hq, Sq, Skv, geo.bc, geo.br, 0, -1, 0, 0, 1, 0};
       hipLaunchKernelGGL(dbias_fill_kernel, dim3((unsigned)((int64_t)ba.batch * Hq * ((Sq + 31) / 32))),
                          dim3(256), 0, stream, fp);
       e = hipGetLastError();
