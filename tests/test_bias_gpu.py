@@ -227,3 +227,62 @@ def test_fp16_io_bias_parity(name, det, dbias_io):
         L = None if lens is None else lens[bb]
         vis = oracle.visible_mask(w.Sq, w.Skv, w.causal, w.window_left, L, L)
         assert np.all(got[3][bb][:, ~vis] == 0)
+
+
+# An additive bias under the other mask forms: bottom-right causal with S_q < S_kv, a right band,
+# and separate query / key lengths, with S_kv a multiple of 8 (the 8-wave layout with the bias tile
+# in LDS, whose last key tile runs past the keys and whose bottom q tile past the queries) and not
+# (the 4-wave layout).
+MASK_CASES = {
+    # name: (base workload, overrides, q lens, kv lens, bottom_right, window_right)
+    "bottom_right_sq_lt_skv_d128": ("gqa_causal_s4096_d128", dict(B=2, Hq=4, Hkv=2, Sq=300, Skv=520),
+                                    None, None, True, 0),
+    "bottom_right_band_lens_d64": ("mha_s128_d64", dict(B=2, Hq=2, Hkv=2, Sq=260, Skv=392, causal=True,
+                                                        window_left=100), [200, 260], [392, 300], True, 3),
+    "bottom_right_lens_d128_skv_odd": ("gqa_causal_s4096_d128", dict(B=2, Hq=4, Hkv=2, Sq=300, Skv=517),
+                                       [300, 211], [517, 400], True, 0),
+}
+
+
+@pytest.mark.parametrize("det", [0, 2, 3, 4], ids=["atomic", "dspanels", "dqpartials", "relay"])
+@pytest.mark.parametrize("name", list(MASK_CASES))
+def test_bias_mask_forms(name, det):
+    import attention_backward_sdpa_amd as lib
+    base, ov, lq, lkv, br, wr = MASK_CASES[name]
+    w = V(W[base], **ov)
+    C.log(f"bias mask case {name} route {det}: {w}, lens {lq} / {lkv}, bottom_right {br}, band {wr}")
+    inp = synth.draw_inputs(w)
+    f = C.f64
+    bias_bits = synth.bf16_bits(np.random.default_rng(31).standard_normal(
+        (w.B, w.Hq, w.Sq, w.Skv)).astype(np.float32))
+    bias64 = f(bias_bits)
+    kw = dict(causal=w.causal, window_left=w.window_left, seq_q_lens=lq, seq_kv_lens=lkv,
+              bottom_right=br, window_right=wr)
+    o64, lse64 = oracle.forward(f(inp.q), f(inp.k), f(inp.v), w.softmax_scale, bias=bias64, **kw)
+    o_bits = synth.bf16_bits(o64.astype(np.float32))
+    lse = lse64.astype(np.float32)
+    ref = oracle.backward(f(inp.q), f(inp.k), f(inp.v), f(o_bits), f(inp.do), lse.astype(np.float64),
+                          w.softmax_scale, bias=bias64, return_dbias=True, **kw)
+    dev = "cuda"
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v, o, do = bf(inp.q), bf(inp.k), bf(inp.v), bf(o_bits), bf(inp.do)
+    outs = [torch.empty_like(x) for x in (q, k, v)]
+    for x in outs:
+        x.view(torch.int16).fill_(0x7FC0)
+    dbias = torch.full((w.B, w.Hq, w.Sq, w.Skv), float("nan"), device=dev)
+    tl = lambda L: None if L is None else torch.tensor(L, dtype=torch.int32, device=dev)
+    args = dict(scale=w.softmax_scale, causal=w.causal, window_left=w.window_left, deterministic=det,
+                seq_q_lens=tl(lq), seq_kv_lens=tl(lkv), causal_bottom_right=br, window_right=wr,
+                bias=bf(bias_bits), dbias=dbias)
+    n = lib.run_workspace_size(q, k, v, **args)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    lib.sdpa_bwd_run(q, k, v, o, do, torch.from_numpy(lse).to(dev), *outs, workspace=ws, **args)
+    torch.cuda.synchronize()
+    got = [C.bf16_tensor_to_f32(x) for x in outs] + [dbias.cpu().numpy()]
+    for tname, g, r in zip(("dQ", "dK", "dV", "dBias"), got, ref):
+        C.assert_close(f"bias mask {name} route {det} {tname}", g, r)
+    for bb in range(w.B):
+        vis = oracle.visible_mask(w.Sq, w.Skv, w.causal, w.window_left,
+                                  None if lq is None else lq[bb], None if lkv is None else lkv[bb],
+                                  br, wr)
+        assert np.all(got[3][bb][:, ~vis] == 0)
