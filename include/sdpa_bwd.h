@@ -281,8 +281,9 @@ int sdpa_bwd_run(const sdpa_bwd_args* args);
 size_t sdpa_bwd_run_workspace_size(const sdpa_bwd_args* args);
 
 /* The dQ route sdpa_bwd_run takes for these arguments (values as for sdpa_bwd_dq_route; with a
- * bias the 128-key tiles can change the choice of `deterministic` = 1); -1 for arguments it
- * rejects by size or head dim, an unknown `deterministic` value, or args NULL.  Host only. */
+ * bias held in registers the 128-key tiles can change the choice of `deterministic` = 1); -1 for
+ * arguments it rejects by size or head dim, an unknown `deterministic` value, or args NULL.
+ * Host only. */
 int sdpa_bwd_run_dq_route(const sdpa_bwd_args* args);
 
 /* NVFP4 attention-QAT backward ("NVFP4 Attention QAT Backward", "Overview", "Tensor contract",
