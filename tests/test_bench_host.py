@@ -49,3 +49,29 @@ def test_against_brute_force():
     for w in cases:
         lens = synth.draw_inputs(w).seq_q_lens if w.padded else None
         assert bench.dq_atomic_adds(w, lens) == brute_force_adds(w, lens), w
+
+
+
+def test_kernel_tiles_match_the_library_plan():
+    """bench.py's model of the main kernel's key tile (which sets its atomic-add count) agrees with
+    the library's own layout choice, read from the dQ-partial workspace: statistics, then one
+    32 x Dqk fp32 block per (head, key tile, q tile).  MHA with 8 q tiles keeps the grid unsplit,
+    so there are no dK/dV partials in the carve."""
+    import ctypes
+    import attention_backward_sdpa_amd as lib
+    so = lib.library()
+    al = lambda n: (n + 255) // 256 * 256
+    B, H, Sq = 1, 2, 256
+    for D, Dv in ((32, 32), (64, 64), (128, 128), (192, 128), (256, 256)):
+        for Skv in (512, 520, 516):
+            for bias in (False, True):
+                w = V(W["mha_s128_d64"], B=B, Hq=H, Hkv=H, Sq=Sq, Skv=Skv, Dqk=D, Dv=Dv)
+                kq, bc, br = bench.kernel_tiles(w, bias)
+                a = lib.Args()
+                a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.Dqk, a.Dv = B, H, H, Sq, Skv, D, Dv
+                a.window_left, a.deterministic, a.dtype = -1, 3, lib.BF16
+                if bias:  # an io-type, 16-byte-aligned bias (the kind bench.py draws)
+                    a.bias, a.bias_batch, a.bias_dtype = 8192, B, lib.BF16
+                n_kv = -(-Skv // bc)
+                expected = al(B * H * Sq * 2 * 4) + al(B * H * n_kv * Sq * kq * 4)
+                assert so.sdpa_bwd_run_workspace_size(ctypes.byref(a)) == expected, (D, Skv, bias, bc)
