@@ -15,6 +15,7 @@
 
 #include "../../include/sdpa_bwd.h"
 #include "dq2k.h"
+#include "dq2k_half.h"
 #include "dq2k_split.h"
 #include "dq_reduce.h"
 #include "main_launch.h"
@@ -351,17 +352,43 @@ hipError_t dispatch_dq2k_split(const Dq2kParams& dp, int bc, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The keys of every chunk split over wave pairs (dq2k_half.h): 4 q tiles per workgroup, two
+// workgroups per CU.  Measured against dq2k_kernel (same box, two passes each): at head dim 64
+// (causal GQA S=4096) 128 -> 115 us; at head dim 128 faster only where dq2k_kernel's grid has
+// fewer than two workgroups per CU (causal MHA B2 H16 S=2048: 60-62 -> 57-58 us), slower on the
+// larger grids (causal GQA S=4096: 139-141 -> 160 us; non-causal MHA S=4096: 122 -> 138 us).
+bool dq2k_half_pays(int Dqk, const Dq2kParams& dp) {
+  if (Dqk == 64) return true;
+  const int64_t full_grid = (int64_t)((dp.n_q_tiles + 7) / 8) * dp.B * dp.Hq;
+  return Dqk == 128 && full_grid < 2 * kNumCUs;
+}
+
+template <int DQK, int BC, bool F16>
+hipError_t dispatch_dq2k_half(const Dq2kParams& dp, int bc, hipStream_t s) {
+  using C = Dq2kHalfCfg<DQK, BC, F16>;
+  if (BC != bc) return hipErrorInvalidValue;  // must read the dS blocks the main kernel wrote
+  const int64_t grid = (int64_t)((dp.n_q_tiles + C::QT - 1) / C::QT) * dp.B * dp.Hq;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  const hipError_t e = lds_limit_once<C>(dq2k_half_kernel<C>, C::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dq2k_half_kernel<C>, dim3((unsigned)grid), dim3(C::NT), C::LDS_BYTES, s, dp);
+  return hipGetLastError();
+}
+
 template <bool F16>
 hipError_t run_dq2k_t(int Dqk, const Dq2kParams& dp, int bc, hipStream_t s) {
+  const bool half = dq2k_half_pays(Dqk, dp);
   if (bc == 256) {
-    if (Dqk == 64) return dispatch_dq2k<64, 256, F16>(dp, bc, s);
-    if (Dqk == 128) return dispatch_dq2k<128, 256, F16>(dp, bc, s);
+    if (Dqk == 64) return dispatch_dq2k_half<64, 256, F16>(dp, bc, s);
+    if (Dqk == 128)
+      return half ? dispatch_dq2k_half<128, 256, F16>(dp, bc, s) : dispatch_dq2k<128, 256, F16>(dp, bc, s);
     if (Dqk == 192) return dispatch_dq2k<192, 256, F16>(dp, bc, s);
     return hipErrorInvalidValue;
   }
   // 128-key tiles: head dim 256, and every head dim under a bias
-  if (Dqk == 64) return dispatch_dq2k<64, 128, F16>(dp, bc, s);
-  if (Dqk == 128) return dispatch_dq2k<128, 128, F16>(dp, bc, s);
+  if (Dqk == 64) return dispatch_dq2k_half<64, 128, F16>(dp, bc, s);
+  if (Dqk == 128)
+    return half ? dispatch_dq2k_half<128, 128, F16>(dp, bc, s) : dispatch_dq2k<128, 128, F16>(dp, bc, s);
   if (Dqk == 192) return dispatch_dq2k<192, 128, F16>(dp, bc, s);
   return dispatch_dq2k_split<256, 128, F16>(dp, bc, s);
 }
