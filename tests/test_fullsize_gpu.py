@@ -256,3 +256,79 @@ def test_fullsize_bias_sampled_rows(det):
         rowsum = np.abs(db[h].astype(np.float64).sum(axis=1)).max()
         assert rowsum <= 1e-2 * np.abs(db[h]).astype(np.float64).sum(axis=1).max(), \
             f"{tag}: dBias rows do not sum to 0 (head {h})"
+
+
+# fp16 io at the headline's full size ("Support surface": FP16 / BF16): the inputs drawn as for
+# bf16 but rounded to binary16, O and LSE from the fp64 oracle forward rounded to fp16 / fp32, on
+# the fp32-atomic and dS-panel routes.  Sampled rows against the oracle at the fp16 tolerance
+# (4 unit roundoffs of binary16, as in tests/test_fp16_gpu.py), and the column-sum identities.
+FP16_TOL = 2e-3
+_FP16_PREP = {}
+
+
+def _prepare_fp16():
+    if "c3" not in _FP16_PREP:
+        w = W["gqa_causal_s4096_d128"]
+        C.log("full-size fp16 case: drawing inputs")
+        inp = synth.draw_inputs(w, dtype="fp16")
+        f = lambda bits: synth.fp16_to_f32(bits).astype(np.float64)
+        C.log("full-size fp16 case: fp64 oracle forward for O and LSE")
+        o64, lse64 = oracle.forward(f(inp.q), f(inp.k), f(inp.v), w.softmax_scale, causal=True)
+        o_bits = synth.fp16_bits(o64.astype(np.float32))
+        lse = lse64.astype(np.float32)
+        del o64, lse64
+        h = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.float16).cuda()
+        t = dict(q=h(inp.q), k=h(inp.k), v=h(inp.v), do=h(inp.do), o=h(o_bits),
+                 lse=torch.from_numpy(lse).cuda())
+        host = dict(q=f(inp.q), k=f(inp.k), v=f(inp.v), do=f(inp.do), o=f(o_bits),
+                    lse=lse.astype(np.float64))
+        torch.cuda.synchronize()
+        C.log("full-size fp16 case: inputs ready")
+        _FP16_PREP["c3"] = (t, host)
+    return _FP16_PREP["c3"]
+
+
+@pytest.mark.parametrize("det", [0, 2], ids=["atomic", "dspanels"])
+def test_fullsize_fp16_sampled_rows(det):
+    import attention_backward_sdpa_amd as lib
+    w = W["gqa_causal_s4096_d128"]
+    t, host = _prepare_fp16()
+    C.log(f"full-size fp16 case: GPU chain (deterministic={det})")
+    outs = [torch.empty_like(t[x]) for x in ("q", "k", "v")]
+    for x in outs:
+        x.view(torch.int16).fill_(0x7E00)  # fp16 NaN: every element must be written
+    n = lib.workspace_size(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.Dqk, w.Dv, True, -1, det, False)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    lib.sdpa_bwd_ex(t["q"], t["k"], t["v"], t["o"], t["do"], t["lse"], *outs,
+                    scale=w.softmax_scale, causal=True, deterministic=det, workspace=ws)
+    torch.cuda.synchronize()
+    dq, dk, dv = (x.float().cpu().numpy() for x in outs)
+    q, k, v, o, do, lse = (host[x] for x in ("q", "k", "v", "o", "do", "lse"))
+    rng = np.random.default_rng(99)
+    got_q, ref_q = [], []
+    for h in (0, 17, w.Hq - 1):
+        rows = _edge_rows(w.Sq) + sorted(rng.choice(w.Sq, 4, replace=False).tolist())
+        ref_q.append(oracle.backward_dq_rows(q, k, v, o, do, lse, w.softmax_scale, 0, h, rows, causal=True))
+        got_q.append(dq[0, h, rows])
+    got_k, ref_k, got_v, ref_v = [], [], [], []
+    for kh in (0, w.Hkv - 1):
+        rows = _edge_rows(w.Skv) + sorted(rng.choice(w.Skv, 4, replace=False).tolist())
+        rk, rv = oracle.backward_dkdv_rows(q, k, v, o, do, lse, w.softmax_scale, 0, kh, rows, causal=True)
+        ref_k.append(rk)
+        ref_v.append(rv)
+        got_k.append(dk[0, kh, rows])
+        got_v.append(dv[0, kh, rows])
+    tag = f"full-size fp16 (dQ route {ROUTE_NAMES[det]})"
+    C.assert_close(f"{tag} dQ sampled rows", np.concatenate(got_q), np.concatenate(ref_q), tol=FP16_TOL)
+    C.assert_close(f"{tag} dK sampled rows", np.concatenate(got_k), np.concatenate(ref_k), tol=FP16_TOL)
+    C.assert_close(f"{tag} dV sampled rows", np.concatenate(got_v), np.concatenate(ref_v), tol=FP16_TOL)
+    group = w.Hq // w.Hkv
+    for kh in range(w.Hkv):
+        hs = slice(kh * group, (kh + 1) * group)
+        lhs = dv[0, kh].astype(np.float64).sum(axis=0)
+        rhs = do[0, hs].sum(axis=(0, 1))
+        scale = max(float(np.abs(rhs).max()), float(np.abs(dv[0, kh]).max()))
+        assert np.abs(lhs - rhs).max() <= 1e-2 * scale, f"{tag}: sum_j dV != sum_i dO (kv head {kh})"
+        colsum = np.abs(dk[0, kh].astype(np.float64).sum(axis=0)).max()
+        assert colsum <= 1e-2 * np.abs(dk[0, kh]).astype(np.float64).sum(axis=0).max(), \
+            f"{tag}: sum_j dK != 0 (kv head {kh})"
