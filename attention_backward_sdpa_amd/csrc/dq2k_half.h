@@ -2,17 +2,19 @@
 // reduction of the deterministic two-kernel route ("SDPA Backward (SM120)", sections
 // "Determinism" and "Deterministic vs. non-deterministic dQ"), for head dims up to 128.
 //
-// dq2k_kernel gives each of its 8 waves one q tile, so a workgroup owns 8 q tiles (256 rows) and,
-// under a causal mask, the workgroups of a head differ in length by whole key tiles.  Here the
-// waves x and x + 4 share q tile x of a group of 4: wave x + 4 h contracts keys 32 h .. 32 h + 31
-// of every 64-key chunk (MFMA steps 2 h, 2 h + 1) and streams only that half of the chunk's dS.
-//   * The grid has twice as many workgroups, each half as long, and a workgroup needs about 64 KiB
-//     of LDS and at most 128 registers per lane, so two fit on a CU: more of the dS stream in
-//     flight per CU, and finer units for the longest-first order to balance.
+// dq2k_kernel gives each of its 8 waves one q tile and the whole of every 64-key chunk.  Here the
+// waves x and x + QT share q tile x of a group of QT: wave x + QT h contracts keys 32 h .. 32 h + 31
+// of every chunk (MFMA steps 2 h, 2 h + 1) and streams only that half of the chunk's dS.  A wave
+// then needs at most 128 registers, so a CU holds 16 waves, four per SIMD:
+//   * QT = 4: 8 waves and about 64 KiB of LDS per workgroup, two workgroups per CU.  The grid has
+//     twice as many workgroups as dq2k_kernel's, each half as long: finer units for the
+//     longest-first order to balance on small grids;
+//   * QT = 8: 16 waves per workgroup, one per CU, each K chunk in LDS serving 8 q tiles as in
+//     dq2k_kernel.
 //   * K is shared as in dq2k_kernel: every wave loads its share of each chunk's fragments KR
 //     chunks early and writes it to one of two LDS buffers; one barrier per chunk.
 //   * Each wave accumulates its half of the keys in registers, over the same ascending walk of its
-//     tile's chunks.  At the end wave x + 4 hands its sums to wave x through LDS, and wave x adds
+//     tile's chunks.  At the end wave x + QT hands its sums to wave x through LDS, and wave x adds
 //     them to its own (first half + second half, a fixed order) and stores the rows: the result is
 //     bitwise reproducible, though not bitwise equal to dq2k_kernel's single running sum.
 #pragma once
@@ -20,12 +22,13 @@
 
 namespace sdpa {
 
-template <int DQK_, int BC_, bool F16_ = false>
+template <int DQK_, int BC_, bool F16_ = false, int QT_ = 4>
 struct Dq2kHalfCfg {
-  static constexpr int DQK = DQK_, BC = BC_, NW = 8;
+  static constexpr int QT = QT_;                             // q tiles per workgroup
+  static constexpr int DQK = DQK_, BC = BC_, NW = 2 * QT;
   static constexpr bool F16 = F16_;  // fp16 io and dS instead of bf16
   static constexpr int BR = 32, NT = NW * 64, KC = 64;       // KC: keys per chunk
-  static constexpr int QT = NW / 2;                          // q tiles per workgroup
+  static constexpr int MIN_WG = QT == 4 ? 2 : 1;             // workgroups per CU
   static constexpr int N_DT = DQK / 32;                      // 32-column d tiles per wave
   static constexpr int STEPS = KC / 32;                      // MFMA key steps per wave and chunk
   static constexpr int DS_LOADS = KC * BR / 1024;            // 16-byte loads per lane and chunk
@@ -45,11 +48,11 @@ struct Dq2kHalfCfg {
   static_assert(DQK <= 128, "head dims up to 128");
   static_assert(BC % KC == 0, "whole chunks per KV tile");
   static_assert(K_FRAGS % NW == 0, "even K split over waves");
-  static_assert(2 * LDS_BYTES <= 160 * 1024, "two workgroups per CU");
+  static_assert(MIN_WG * LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
 template <class C>
-__global__ void __launch_bounds__(C::NT, 2) dq2k_half_kernel(Dq2kParams p) {
+__global__ void __launch_bounds__(C::NT, C::MIN_WG) dq2k_half_kernel(Dq2kParams p) {
   using M = Mfma32<C::F16>;
   using acc_t = typename M::acc_t;
   constexpr int BR = C::BR, BC = C::BC, DQK = C::DQK, KC = C::KC, QT = C::QT;

@@ -352,20 +352,23 @@ hipError_t dispatch_dq2k_split(const Dq2kParams& dp, int bc, hipStream_t s) {
   return hipGetLastError();
 }
 
-// The keys of every chunk split over wave pairs (dq2k_half.h): 4 q tiles per workgroup, two
-// workgroups per CU.  Measured against dq2k_kernel (same box, two passes each): at head dim 64
-// (causal GQA S=4096) 128 -> 115 us; at head dim 128 faster only where dq2k_kernel's grid has
-// fewer than two workgroups per CU (causal MHA B2 H16 S=2048: 60-62 -> 57-58 us), slower on the
-// larger grids (causal GQA S=4096: 139-141 -> 160 us; non-causal MHA S=4096: 122 -> 138 us).
-bool dq2k_half_pays(int Dqk, const Dq2kParams& dp) {
-  if (Dqk == 64) return true;
-  const int64_t full_grid = (int64_t)((dp.n_q_tiles + 7) / 8) * dp.B * dp.Hq;
-  return Dqk == 128 && full_grid < 2 * kNumCUs;
+// Head dims 64 and 128: the keys of every chunk split over wave pairs (dq2k_half.h).  Measured
+// against dq2k_kernel (one q tile per wave, 8 per workgroup; same box, two passes each):
+//   * 4 q tiles per workgroup (8 waves, two workgroups per CU): head dim 64 on causal GQA S=4096
+//     128 -> 112-115 us; head dim 128 where a grid of 8-q-tile groups has fewer than two
+//     workgroups per CU (causal MHA B2 H16 S=2048: 60-62 -> 56-57 us); on the larger head-dim-128
+//     grids slower (causal GQA S=4096 139-141 -> 160 us), twice the K traffic per q tile;
+//   * 8 q tiles per workgroup (16 waves, one workgroup per CU; K shared as in dq2k_kernel): head
+//     dim 128 on the larger grids, causal GQA S=4096 130-131 -> 124-126 us, non-causal MHA S=4096
+//     131 -> 105-106 us, fp16 133 -> 127-129 us.
+// Head dim 192 keeps dq2k_kernel (the 16-wave layout's LDS and registers do not fit there).
+bool dq2k_small_grid(const Dq2kParams& dp) {
+  return (int64_t)((dp.n_q_tiles + 7) / 8) * dp.B * dp.Hq < 2 * kNumCUs;
 }
 
-template <int DQK, int BC, bool F16>
+template <int DQK, int BC, bool F16, int QT>
 hipError_t dispatch_dq2k_half(const Dq2kParams& dp, int bc, hipStream_t s) {
-  using C = Dq2kHalfCfg<DQK, BC, F16>;
+  using C = Dq2kHalfCfg<DQK, BC, F16, QT>;
   if (BC != bc) return hipErrorInvalidValue;  // must read the dS blocks the main kernel wrote
   const int64_t grid = (int64_t)((dp.n_q_tiles + C::QT - 1) / C::QT) * dp.B * dp.Hq;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
@@ -375,20 +378,23 @@ hipError_t dispatch_dq2k_half(const Dq2kParams& dp, int bc, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BC, bool F16>
+hipError_t dispatch_dq2k_half_128(const Dq2kParams& dp, int bc, hipStream_t s) {
+  return dq2k_small_grid(dp) ? dispatch_dq2k_half<128, BC, F16, 4>(dp, bc, s)
+                             : dispatch_dq2k_half<128, BC, F16, 8>(dp, bc, s);
+}
+
 template <bool F16>
 hipError_t run_dq2k_t(int Dqk, const Dq2kParams& dp, int bc, hipStream_t s) {
-  const bool half = dq2k_half_pays(Dqk, dp);
   if (bc == 256) {
-    if (Dqk == 64) return dispatch_dq2k_half<64, 256, F16>(dp, bc, s);
-    if (Dqk == 128)
-      return half ? dispatch_dq2k_half<128, 256, F16>(dp, bc, s) : dispatch_dq2k<128, 256, F16>(dp, bc, s);
+    if (Dqk == 64) return dispatch_dq2k_half<64, 256, F16, 4>(dp, bc, s);
+    if (Dqk == 128) return dispatch_dq2k_half_128<256, F16>(dp, bc, s);
     if (Dqk == 192) return dispatch_dq2k<192, 256, F16>(dp, bc, s);
     return hipErrorInvalidValue;
   }
-  // 128-key tiles: head dim 256, and every head dim under a bias
-  if (Dqk == 64) return dispatch_dq2k_half<64, 128, F16>(dp, bc, s);
-  if (Dqk == 128)
-    return half ? dispatch_dq2k_half<128, 128, F16>(dp, bc, s) : dispatch_dq2k<128, 128, F16>(dp, bc, s);
+  // 128-key tiles: head dim 256, and every head dim under a bias held in registers
+  if (Dqk == 64) return dispatch_dq2k_half<64, 128, F16, 4>(dp, bc, s);
+  if (Dqk == 128) return dispatch_dq2k_half_128<128, F16>(dp, bc, s);
   if (Dqk == 192) return dispatch_dq2k<192, 128, F16>(dp, bc, s);
   return dispatch_dq2k_split<256, 128, F16>(dp, bc, s);
 }
