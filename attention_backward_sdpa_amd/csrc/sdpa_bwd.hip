@@ -355,15 +355,17 @@ hipError_t dispatch_dq2k_split(const Dq2kParams& dp, int bc, hipStream_t s) {
 // Head dims 64 and 128: the keys of every chunk split over wave pairs (dq2k_half.h).  Measured
 // against dq2k_kernel (one q tile per wave, 8 per workgroup; same box, two passes each):
 //   * 4 q tiles per workgroup (8 waves, two workgroups per CU): head dim 64 on causal GQA S=4096
-//     128 -> 112-115 us; head dim 128 where a grid of 8-q-tile groups has fewer than two
-//     workgroups per CU (causal MHA B2 H16 S=2048: 60-62 -> 56-57 us); on the larger head-dim-128
-//     grids slower (causal GQA S=4096 139-141 -> 160 us), twice the K traffic per q tile;
+//     128 -> 112-115 us; head dim 128 under a mask that makes the groups' lengths differ, where a
+//     grid of 8-q-tile groups has fewer than two workgroups per CU (causal MHA B2 H16 S=2048:
+//     60-62 -> 56-57 us); on the larger head-dim-128 grids slower (causal GQA S=4096 139-141 ->
+//     160 us), twice the K traffic per q tile;
 //   * 8 q tiles per workgroup (16 waves, one workgroup per CU; K shared as in dq2k_kernel): head
-//     dim 128 on the larger grids, causal GQA S=4096 130-131 -> 124-126 us, non-causal MHA S=4096
-//     131 -> 105-106 us, fp16 133 -> 127-129 us.
+//     dim 128 otherwise, causal GQA S=4096 130-131 -> 124-126 us, non-causal MHA B1 H16 S=4096
+//     (256 groups of equal length) 131 -> 105-106 us, fp16 133 -> 127-129 us.
 // Head dim 192 keeps dq2k_kernel (the 16-wave layout's LDS and registers do not fit there).
-bool dq2k_small_grid(const Dq2kParams& dp) {
-  return (int64_t)((dp.n_q_tiles + 7) / 8) * dp.B * dp.Hq < 2 * kNumCUs;
+bool dq2k_fine_groups(const Dq2kParams& dp) {
+  const bool uneven = dp.causal || dp.window_left >= 0 || dp.seq_q_lens || dp.seq_kv_lens;
+  return uneven && (int64_t)((dp.n_q_tiles + 7) / 8) * dp.B * dp.Hq < 2 * kNumCUs;
 }
 
 template <int DQK, int BC, bool F16, int QT>
@@ -380,8 +382,8 @@ hipError_t dispatch_dq2k_half(const Dq2kParams& dp, int bc, hipStream_t s) {
 
 template <int BC, bool F16>
 hipError_t dispatch_dq2k_half_128(const Dq2kParams& dp, int bc, hipStream_t s) {
-  return dq2k_small_grid(dp) ? dispatch_dq2k_half<128, BC, F16, 4>(dp, bc, s)
-                             : dispatch_dq2k_half<128, BC, F16, 8>(dp, bc, s);
+  return dq2k_fine_groups(dp) ? dispatch_dq2k_half<128, BC, F16, 4>(dp, bc, s)
+                              : dispatch_dq2k_half<128, BC, F16, 8>(dp, bc, s);
 }
 
 template <bool F16>
