@@ -39,8 +39,8 @@ class Workload:
         return self.scale if self.scale is not None else 1.0 / math.sqrt(self.Dqk)
 
 
-# The five workloads of the attention-backward study and the NVFP4-QAT example shape, seeded by
-# their index.
+# The five workloads of the attention-backward study, the NVFP4-QAT example shape and one GPU's
+# share of the causal GQA workload, seeded by their index.
 WORKLOADS = {
     "mha_s128_d64": Workload("mha_s128_d64", 1, 2, 2, 128, 128, 64, 64, causal=False, seed=1),
     "mha_causal_s2048_d128": Workload("mha_causal_s2048_d128", 2, 16, 16, 2048, 2048, 128, 128,
@@ -56,6 +56,10 @@ WORKLOADS = {
     # non-causal MHA, head dim 128
     "qat_mha_s4096_d128": Workload("qat_mha_s4096_d128", 1, 16, 16, 4096, 4096, 128, 128,
                                    causal=False, seed=6),
+    # one GPU's share of the causal GQA S=4096 workload split over 8 GPUs by KV-head group: one KV
+    # head and its 4 query heads
+    "gqa_causal_s4096_d128_1of8": Workload("gqa_causal_s4096_d128_1of8", 1, 4, 1, 4096, 4096, 128,
+                                           128, causal=True, seed=7),
 }
 
 

@@ -42,6 +42,8 @@ CASES = [
     ("gqa_causal_s4096_d128", 4),
     ("mha_det_s8192_d256", 4),
     ("mla_window_padded_s4096", 4),
+    ("gqa_causal_s4096_d128_1of8", 0),
+    ("gqa_causal_s4096_d128_1of8", 2),
 ]
 ROUTE_NAMES = {0: "atomic", 1: "det", 2: "dspanels", 3: "dqpartials", 4: "relay", None: "default"}
 
