@@ -44,6 +44,8 @@ CASES = [
     ("mla_window_padded_s4096", 4),
     ("gqa_causal_s4096_d128_1of8", 0),
     ("gqa_causal_s4096_d128_1of8", 2),
+    ("gqa_causal_s4096_d128_1of8", 3),
+    ("gqa_causal_s4096_d128_1of8", 4),
 ]
 ROUTE_NAMES = {0: "atomic", 1: "det", 2: "dspanels", 3: "dqpartials", 4: "relay", None: "default"}
 
